@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE FFN layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+One step = one full pass of the layer (routing, gate/up + SwiGLU, down +
+weighted combine) over one batch of synthetic tokens.  Default workload: the
+Qwen3-style decode layer (H=2048, E=128, k=8, I=768) at T=32 tokens.
+
+Decode steps cycle through `--layers` independent weight sets (like the
+layers of a model), so each step streams weights that the previous steps did
+not leave in the 256 MB last-level cache, and every step routes a fresh batch
+of tokens.  All inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line.  Besides the throughput it carries
+  roofline:     the dominant kernel's algorithmic HBM bytes per launch divided
+                by its average launch time, taken with HIP events recorded
+                around that kernel on the library's stream during the timed
+                steps, against the 8 TB/s HBM peak;
+  cpu_baseline: the FP64 CPU oracle, timed on this host on a bounded sample
+                of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE layer tokens/s; decode HBM TB/s % of peak; batched MFMA util %"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="qwen3-decode-T32")
+    p.add_argument("--layers", type=int, default=8, help="independent weight sets to cycle")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU time for the oracle baseline (0 = skip)")
+    p.add_argument("--extra", action="store_true",
+                   help="also time decode at T=1 and T=8 (reported under 'extra')")
+    return p.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def decode_algorithmic_bytes(cfg, U):
+    """HBM bytes the decode kernels must move at least, given U touched experts."""
+    T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
+    gate_up = U * 2 * I * H * 2 + T * H * 2 + T * k * I * 4          # weights, x, h hand-off
+    down = U * H * I * 2 + T * k * I * 4 + T * H * 2                  # weights, h, out
+    route = T * cfg.E * 4 + T * k * 8
+    return {"gate_up": gate_up, "down": down, "route": route}
+
+
+def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="decode_gate_up"):
+    from mixture_experts_ffn_07_amd.hip_events import HipEvent
+    dev = "cuda"
+    n_batches = steps + warmup
+    log(f"generating {layers} weight sets of {cfg.name} ({layers * W.expert_bytes(cfg) * cfg.E / 1e9:.1f} GB)")
+    weights = [W.make_weights(cfg, seed=seed + 1000 * l, device=dev) for l in range(layers)]
+    acts = [W.make_activations(cfg, seed=seed + 7919 * (b + 1), device=dev) for b in range(n_batches)]
+    T, k = cfg.T, cfg.k
+    out = torch.empty(T, cfg.H, dtype=torch.bfloat16, device=dev)
+    idx = torch.empty(n_batches, T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(n_batches, T, k, dtype=torch.float32, device=dev)
+    ws = M.workspace(M.moe_decode_workspace_bytes(T, cfg.H, cfg.I, cfg.E, k), dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        wl = weights[i % layers]
+        a = acts[i]
+        M.moe_decode_forward(a["x"], a["logits"], wl["w_gate_up"], wl["w_down"], k, out=out,
+                             topk_idx=idx[i], topk_w=wts[i], ws=ws, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        M.moe_profile_kernel(hook_kernel, evs[s][0].handle, evs[s][1].handle)
+        step(warmup + s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    M.moe_profile_kernel("none", None, None)
+    durs = [a.elapsed_ms(b) for a, b in evs]
+    U = [int(torch.unique(idx[warmup + s]).numel()) for s in range(steps)]
+    bytes_ = [decode_algorithmic_bytes(cfg, u) for u in U]
+    kern_bytes = sum(b["gate_up"] for b in bytes_)
+    layer_bytes = sum(sum(b.values()) for b in bytes_)
+    elapsed = t1 - t0
+    res = {
+        "elapsed_s": elapsed,
+        "ms_per_step": 1e3 * elapsed / steps,
+        "tokens_per_s": T * steps / elapsed,
+        "kernel_avg_us": 1e3 * sum(durs) / steps,
+        "kernel_gbs": kern_bytes / (sum(durs) * 1e-3) / 1e9,
+        "kernel_bytes_per_launch": kern_bytes / steps,
+        "layer_gbs": layer_bytes / elapsed / 1e9,
+        "avg_touched_experts": sum(U) / steps,
+        "first_batch": acts[warmup], "first_weights": weights[warmup % layers],
+    }
+    return res
+
+
+def cpu_baseline(W, cfg, act, weights, seconds):
+    """Time the FP64 oracle on this host (bounded sample of the same workload)."""
+    import numpy as np
+    from oracle import moe_forward
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    import torch
+    x = act["x"].cpu().view(torch.int16).numpy().view(np.uint16)
+    logits = act["logits"].cpu().numpy()
+    # copy only the experts this batch routes to; the copy is outside the timing
+    from oracle import route
+    ids = np.unique(route(logits, cfg.k)[0])
+    wgu = {int(e): weights["w_gate_up"][int(e)].cpu().view(torch.int16).numpy().view(np.uint16) for e in ids}
+    wd = {int(e): weights["w_down"][int(e)].cpu().view(torch.int16).numpy().view(np.uint16) for e in ids}
+    n, t0 = 0, time.perf_counter()
+    while True:
+        moe_forward(x, logits, wgu.__getitem__, wd.__getitem__, cfg.k)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": n * cfg.T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} pass(es) of the FP64 oracle over one {cfg.T}-token batch of "
+                      f"{cfg.name} ({len(ids)} routed experts), weights already in host memory, "
+                      f"{el:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported: this library has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    import mixture_experts_ffn_07_amd as M
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = W.get(args.workload)
+    if cfg.path != "decode":
+        raise SystemExit(f"workload {cfg.name} is a batched workload; not wired into bench.py yet")
+    log(f"device {torch.cuda.get_device_name(0)}; workload {cfg.name}")
+    r = run_decode(M, W, torch, cfg, args.steps, args.warmup, args.layers, args.seed)
+    roof = {"bound": "hbm", "kernel": "decode_gate_up", "achieved": round(r["kernel_gbs"], 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(r["kernel_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None, "avg_launch_us": round(r["kernel_avg_us"], 2),
+            "algorithmic_bytes_per_launch": int(r["kernel_bytes_per_launch"])}
+    line = {
+        "metric": METRIC, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
+                   "I": cfg.I, "weight_sets": args.layers, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "layer": {"hbm_gbs": round(r["layer_gbs"], 1),
+                  "hbm_frac": round(r["layer_gbs"] / HBM_PEAK_GBS, 4),
+                  "avg_touched_experts": round(r["avg_touched_experts"], 2),
+                  "latency_us": round(1e3 * r["ms_per_step"], 2)},
+    }
+    if args.extra:
+        ex = {}
+        for T in (1, 8):
+            c2 = W.get(f"qwen3-decode-T{T}")
+            r2 = run_decode(M, W, torch, c2, args.steps, args.warmup, args.layers, args.seed)
+            ex[c2.name] = {"tokens_per_s": round(r2["tokens_per_s"], 1),
+                           "latency_us": round(1e3 * r2["ms_per_step"], 2),
+                           "gate_up_us": round(r2["kernel_avg_us"], 2),
+                           "gate_up_gbs": round(r2["kernel_gbs"], 1),
+                           "layer_gbs": round(r2["layer_gbs"], 1)}
+        line["extra"] = ex
+    if args.cpu_seconds > 0:
+        log("timing the CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(W, cfg, r["first_batch"], r["first_weights"],
+                                            args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+/*
+ * moe_mi355x.h -- C ABI of the routed Mixture-of-Experts FFN layer for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (warp-decode article on picklee.vercel.app, sections "Background"
+ * and "Key points"; Mixture-of-Kittens summary on asapai.co.kr, sections
+ * "What is 2.37x measured against" and "Determinism on par with
+ * performance"): every token is routed to k experts chosen from its router
+ * logits; each routed expert applies its gate/up projection, the SwiGLU
+ * activation and its down projection; the routed experts' outputs are summed
+ * with the routing weights into the token's output, accumulating in FP32 in
+ * a fixed order so that the same inputs always give the same bytes.
+ *
+ * Conventions shared by every call
+ *   - Shapes: T tokens, H hidden size, I expert intermediate size, E experts,
+ *     k experts per token.  Row-major; the reduction dimension of every weight
+ *     matrix is contiguous.
+ *   - BF16 values are passed as uint16_t bit patterns.  FP8 E4M3 codes and
+ *     E8M0 scale codes are uint8_t.  MX blocks are 32 consecutive elements
+ *     along the reduction dimension.
+ *   - Every pointer argument is a device pointer unless stated otherwise; the
+ *     caller owns all memory.  The library allocates nothing and keeps no
+ *     state between calls except a cached device-property query.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on `stream` and returns; no call waits
+ *     for the device.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued.  A failure returns a negative moe_status and leaves a message
+ *     for moe_last_error() (per calling thread); nothing was enqueued.
+ *     A launch failure reported by the HIP runtime returns MOE_ERR_HIP.
+ *   - Device contents are not validated: expert ids must lie in [0, E) and
+ *     logits must be finite, otherwise results are undefined.
+ *   - Determinism: identical inputs, shapes and device give byte-identical
+ *     outputs.  No kernel accumulates floating point values with atomics.
+ *   - All device pointers must be 16-byte aligned.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  MOE_ERR_SHAPE = -2,       /* a size is out of range or not a multiple      */
+  MOE_ERR_ALIGN = -3,       /* a device pointer is not 16-byte aligned       */
+  MOE_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required       */
+  MOE_ERR_UNSUPPORTED = -5, /* a valid request this library does not serve   */
+  MOE_ERR_HIP = -6          /* the HIP runtime reported an error             */
+} moe_status;
+
+typedef enum {
+  MOE_BF16 = 0,   /* BF16 activations and weights                         */
+  MOE_MXFP8 = 1   /* E4M3 codes with one E8M0 scale per 32 along K          */
+} moe_dtype;
+
+/*
+ * moe_route_topk -- top-k expert routing with renormalised softmax weights
+ * (warp-decode article, "Background": expert routing picks each token's
+ * experts; "Key points": the routed experts).
+ *
+ *   logits   [T, E] float32, finite
+ *   topk_idx [T, k] int32 out: slot j holds the j-th expert in the order
+ *            (logit descending, expert index ascending); +0 and -0 tie, so the
+ *            lower index wins
+ *   topk_w   [T, k] float32 out: exp(l_j - l_0) / sum_i exp(l_i - l_0) over the
+ *            k selected logits (softmax over all E then renormalised over k)
+ * Limits: T >= 0 (T = 0 enqueues nothing), 1 <= k <= min(E, 32), E <= 1024.
+ * Index selection compares FP32 values exactly, so it is bit-exact.
+ */
+int moe_route_topk(const float* logits, int T, int E, int k,
+                   int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * moe_decode_forward -- the whole layer for a small decode batch
+ * (warp-decode article, "Key points": two kernels, gate_up and down, each
+ * output-centric, routed experts' contributions summed directly into FP32
+ * accumulators, no per-expert output buffer and no activation-gather buffer).
+ *
+ *   x           [T, H] BF16
+ *   logits      [T, E] float32
+ *   w_gate_up   [E, 2I, H] BF16: rows [0, I) gate, rows [I, 2I) up
+ *   w_down      [E, H, I] BF16
+ *   out         [T, H] BF16 out: FP32 sum, rounded to nearest even once
+ *   topk_idx    [T, k] int32 out, may be NULL (then kept in the workspace)
+ *   topk_w      [T, k] float32 out, may be NULL
+ *   workspace   >= moe_decode_workspace_bytes(T, H, I, E, k) bytes of device
+ *               memory, contents ignored on entry and overwritten
+ * Limits: 1 <= T <= 64 (larger T: MOE_ERR_UNSUPPORTED, use the batched calls),
+ * H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024.
+ * Only the weights of experts that some token routes to are read.
+ */
+int moe_decode_forward(const uint16_t* x, const float* logits,
+                       const uint16_t* w_gate_up, const uint16_t* w_down,
+                       int T, int H, int I, int E, int k,
+                       uint16_t* out, int32_t* topk_idx, float* topk_w,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+size_t moe_decode_workspace_bytes(int T, int H, int I, int E, int k);
+
+/*
+ * moe_quantize_mxfp8 -- MX block quantization of a BF16 matrix along its
+ * last dimension (the "MXFP8" forward of the Mixture-of-Kittens summary,
+ * "What is 2.37x measured against"; block rule of OCP Microscaling v1.0).
+ *
+ *   src    [rows, K] BF16
+ *   codes  [rows, K] uint8 E4M3 out
+ *   scales [rows, K/32] uint8 E8M0 out
+ * Per block of 32: s = floor(log2(max |v|)) - 8 clamped to [-127, 127]
+ * (an all-zero block takes s = -127); code = E4M3 of v / 2^s rounded to
+ * nearest even and saturated to +-448, sign bit copied from v.
+ * Limits: rows >= 0, K a positive multiple of 32.
+ */
+int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int K,
+                       uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * moe_gate_up_3d_batched -- gate/up projection and SwiGLU for every routed
+ * (token, slot) pair of a large batch, as one grouped GEMM over experts
+ * (warp-decode article, "Key points": kernel moe_gate_up_3d_batched;
+ * Mixture-of-Kittens summary: expert compute of the MoE layer forward at
+ * 2,048 tokens per GPU, BF16 and MXFP8).
+ *
+ *   x          [T, H]: BF16 (dtype MOE_BF16) or E4M3 codes (MOE_MXFP8)
+ *   x_scales   [T, H/32] E8M0 (MOE_MXFP8 only, else ignored)
+ *   w_gate_up  [E, 2I, H]: BF16 or E4M3 codes; rows [0, I) gate, [I, 2I) up
+ *   w_gate_up_scales [E, 2I, H/32] E8M0 (MOE_MXFP8 only)
+ *   topk_idx   [T, k] int32 from moe_route_topk
+ *   h          [T*k, I] out, rows in expert-grouped order (row r holds the
+ *              pair perm[r]; experts ascending, tokens ascending within an
+ *              expert): BF16 (MOE_BF16) or E4M3 codes (MOE_MXFP8), the
+ *              activation silu(g) * u computed in FP32 and rounded once
+ *   h_scales   [T*k, I/32] E8M0 out (MOE_MXFP8 only)
+ *   workspace  >= moe_workspace_bytes(T, H, I, E, k, dtype) bytes; this call
+ *              writes the expert grouping into it, and moe_down_3d_batched
+ *              must be given the same workspace and topk_idx, later on the
+ *              same stream
+ * Limits: T >= 1, H and I multiples of 128, 1 <= k <= min(E, 32), E <= 1024.
+ */
+int moe_gate_up_3d_batched(const void* x, const uint8_t* x_scales,
+                           const void* w_gate_up, const uint8_t* w_gate_up_scales,
+                           const int32_t* topk_idx,
+                           int T, int H, int I, int E, int k, int dtype,
+                           void* h, uint8_t* h_scales,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_down_3d_batched -- down projection of every routed pair and the
+ * routing-weighted combine into each token's output (warp-decode article,
+ * "Key points": kernel moe_down_3d_batched; Mixture-of-Kittens summary,
+ * "Determinism on par with performance": a fixed floating-point order).
+ *
+ *   h, h_scales      as written by moe_gate_up_3d_batched
+ *   w_down           [E, H, I]: BF16 or E4M3 codes
+ *   w_down_scales    [E, H, I/32] E8M0 (MOE_MXFP8 only)
+ *   topk_idx, topk_w [T, k] from moe_route_topk
+ *   out              [T, H] BF16 out: out[t] = sum over slots j = 0..k-1, in that
+ *                    order, of topk_w[t, j] * y[t, j], in FP32, rounded once
+ *   workspace        the workspace given to moe_gate_up_3d_batched
+ * Limits as for moe_gate_up_3d_batched.
+ */
+int moe_down_3d_batched(const void* h, const uint8_t* h_scales,
+                        const void* w_down, const uint8_t* w_down_scales,
+                        const int32_t* topk_idx, const float* topk_w,
+                        int T, int H, int I, int E, int k, int dtype,
+                        uint16_t* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+size_t moe_workspace_bytes(int T, int H, int I, int E, int k, int dtype);
+
+/*
+ * Kernel timing hook for benchmarks and profilers (not on any page).
+ * moe_profile_kernel(kernel, start, stop): from now on, the calling thread's
+ * launches of `kernel` are bracketed by hipEventRecord(start) and
+ * hipEventRecord(stop) on the launch stream; `start`/`stop` are hipEvent_t
+ * passed as void*, created by the caller.  kernel = MOE_KERNEL_NONE (or NULL
+ * events) switches the hook off.  Returns MOE_OK or MOE_ERR_SHAPE for an
+ * unknown kernel id.
+ */
+typedef enum {
+  MOE_KERNEL_NONE = 0,
+  MOE_KERNEL_ROUTE = 1,          /* moe_route_topk, and routing+plan in decode */
+  MOE_KERNEL_DECODE_GATE_UP = 2,
+  MOE_KERNEL_DECODE_DOWN = 3,
+  MOE_KERNEL_GROUP = 4,          /* expert grouping of the batched path        */
+  MOE_KERNEL_QUANT = 5,          /* moe_quantize_mxfp8                         */
+  MOE_KERNEL_GEMM_GATE_UP = 6,
+  MOE_KERNEL_GEMM_DOWN = 7,
+  MOE_KERNEL_COMBINE = 8,
+  MOE_KERNEL_COUNT = 9
+} moe_kernel_id;
+
+int moe_profile_kernel(int kernel, void* start_event, void* stop_event);
+
+/* Static text for a moe_status value. */
+const char* moe_status_string(int status);
+
+/* Detail of the calling thread's last failure ("" if none).  Host memory owned
+ * by the library, valid until the thread's next call. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

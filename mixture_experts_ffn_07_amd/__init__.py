@@ -1,0 +1,197 @@
+"""Python binding of libmoe_mi355x.so, the MI355X (gfx950) routed-MoE FFN library.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  The functions
+carry the names of the C entry points in include/moe_mi355x.h; importing this
+package raises ImportError when the library has not been built (there is no
+fallback of any kind).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN = 0, -1, -2, -3
+MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = -4, -5, -6
+MOE_BF16, MOE_MXFP8 = 0, 1
+KERNELS = {"none": 0, "route": 1, "decode_gate_up": 2, "decode_down": 3, "group": 4,
+           "quant": 5, "gemm_gate_up": 6, "gemm_down": 7, "combine": 8}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "moe_route_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_decode_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "moe_quantize_mxfp8": (_I, [_P, ctypes.c_int64, _I, _P, _P, _P]),
+    "moe_gate_up_3d_batched": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "moe_down_3d_batched": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "moe_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_profile_kernel": (_I, [_I, _P, _P]),
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_last_error": (ctypes.c_char_p, []),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m mixture_experts_ffn_07_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        detail = lib.moe_last_error().decode()
+        super().__init__(f"{fn}: {lib.moe_status_string(status).decode()} ({status}): {detail}")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _u16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"expected BF16 bits, got {t.dtype}")
+    return t
+
+
+def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: torch.Tensor = None,
+                   topk_w: torch.Tensor = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """logits [T, E] float32 -> (topk_idx [T, k] int32, topk_w [T, k] float32)."""
+    T, E = logits.shape
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be float32")
+    if topk_idx is None:
+        topk_idx = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _check("moe_route_topk", lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx),
+                                                _ptr(topk_w), _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_decode_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(lib.moe_decode_workspace_bytes(T, H, I, E, k))
+
+
+def moe_workspace_bytes(T: int, H: int, I: int, E: int, k: int, dtype: int) -> int:
+    return int(lib.moe_workspace_bytes(T, H, I, E, k, dtype))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A device buffer for the workspace argument (256-byte aligned by torch)."""
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def moe_decode_forward(x: torch.Tensor, logits: torch.Tensor, w_gate_up: torch.Tensor,
+                       w_down: torch.Tensor, k: int, out: torch.Tensor = None,
+                       topk_idx: torch.Tensor = None, topk_w: torch.Tensor = None,
+                       ws: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Whole layer for a decode batch (T <= 64); BF16 in and out."""
+    T, H = x.shape
+    E, I2, H2 = w_gate_up.shape
+    I = I2 // 2
+    if logits.shape != (T, E) or H2 != H or tuple(w_down.shape) != (E, H, I):
+        raise ValueError("inconsistent shapes")
+    _u16(x), _u16(w_gate_up), _u16(w_down)
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    need = moe_decode_workspace_bytes(T, H, I, E, k)
+    if ws is None:
+        ws = workspace(need, x.device)
+    _check("moe_decode_forward", lib.moe_decode_forward(
+        _ptr(x), _ptr(logits), _ptr(w_gate_up), _ptr(w_down), T, H, I, E, k, _ptr(out),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_quantize_mxfp8(src: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None,
+                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """src [rows, K] BF16 -> (E4M3 codes [rows, K] uint8, E8M0 scales [rows, K/32] uint8)."""
+    rows, K = src.shape
+    _u16(src)
+    if codes is None:
+        codes = torch.empty(rows, K, dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty(rows, K // 32, dtype=torch.uint8, device=src.device)
+    _check("moe_quantize_mxfp8", lib.moe_quantize_mxfp8(_ptr(src), rows, K, _ptr(codes),
+                                                        _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def moe_gate_up_3d_batched(x, w_gate_up, topk_idx, k: int, dtype: int = MOE_BF16, x_scales=None,
+                           w_gate_up_scales=None, h=None, h_scales=None, ws=None, stream=None):
+    """Grouped gate/up projection + SwiGLU; returns (h, h_scales, ws)."""
+    T, H = x.shape
+    E, I2, _ = w_gate_up.shape
+    I = I2 // 2
+    if h is None:
+        h = torch.empty(T * k, I, dtype=torch.bfloat16 if dtype == MOE_BF16 else torch.uint8,
+                        device=x.device)
+    if dtype == MOE_MXFP8 and h_scales is None:
+        h_scales = torch.empty(T * k, I // 32, dtype=torch.uint8, device=x.device)
+    if ws is None:
+        ws = workspace(moe_workspace_bytes(T, H, I, E, k, dtype), x.device)
+    _check("moe_gate_up_3d_batched", lib.moe_gate_up_3d_batched(
+        _ptr(x), _ptr(x_scales), _ptr(w_gate_up), _ptr(w_gate_up_scales), _ptr(topk_idx),
+        T, H, I, E, k, dtype, _ptr(h), _ptr(h_scales), _ptr(ws), ws.numel(), _stream(stream)))
+    return h, h_scales, ws
+
+
+def moe_down_3d_batched(h, w_down, topk_idx, topk_w, ws, k: int, dtype: int = MOE_BF16,
+                        h_scales=None, w_down_scales=None, out=None, stream=None):
+    """Grouped down projection + fixed-order weighted combine -> out [T, H] BF16."""
+    T = topk_idx.shape[0]
+    E, H, I = w_down.shape
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=h.device)
+    _check("moe_down_3d_batched", lib.moe_down_3d_batched(
+        _ptr(h), _ptr(h_scales), _ptr(w_down), _ptr(w_down_scales), _ptr(topk_idx),
+        _ptr(topk_w), T, H, I, E, k, dtype, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_profile_kernel(kernel, start_event: Optional[int], stop_event: Optional[int]) -> None:
+    """Bracket the named kernel's launches with the given hipEvent_t handles."""
+    kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    _check("moe_profile_kernel", lib.moe_profile_kernel(kid, start_event, stop_event))
+
+
+__all__ = ["lib", "LIB_PATH", "MoeError", "moe_route_topk", "moe_decode_forward",
+           "moe_decode_workspace_bytes", "moe_workspace_bytes", "moe_quantize_mxfp8",
+           "moe_gate_up_3d_batched", "moe_down_3d_batched", "moe_profile_kernel", "workspace",
+           "MOE_BF16", "MOE_MXFP8", "KERNELS"]

@@ -1,0 +1,63 @@
+// Launch wrappers between the C ABI (abi.cpp) and the kernels (*.hip).
+// Arguments have been validated by the caller; each returns hipGetLastError()
+// after its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Timing hook set by moe_profile_kernel (per calling thread): launches of
+// kernel `id` are bracketed by the two events when they are set.
+struct ProfileHook {
+  int kernel = 0;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfileHook& profile_hook();
+inline void prof_begin(int id, hipStream_t s) {
+  const ProfileHook& h = profile_hook();
+  if (h.kernel == id && h.start) (void)hipEventRecord(h.start, s);
+}
+inline void prof_end(int id, hipStream_t s) {
+  const ProfileHook& h = profile_hook();
+  if (h.kernel == id && h.stop) (void)hipEventRecord(h.stop, s);
+}
+enum KernelId { kRoute = 1, kDecGateUp = 2, kDecDown = 3, kGroup = 4, kQuant = 5,
+                kGemmGateUp = 6, kGemmDown = 7, kCombine = 8, kKernelCount = 9 };
+
+// Byte layout of the decode workspace.
+struct DecodeWs {
+  size_t plan_u, plan_e, plan_mask, idx, w, hw_hi, hw_lo, total;
+};
+DecodeWs decode_ws_layout(int T, int H, int I, int E, int k);
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                             hipStream_t s);
+
+hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t* wgu,
+                         const uint16_t* wd, int T, int H, int I, int E, int k, uint16_t* out,
+                         int32_t* idx, float* w, void* ws, hipStream_t s, int num_cus);
+
+// Byte layout of the batched workspace.
+struct BatchedWs {
+  size_t counts, offsets, perm, row_of, tiles, n_tiles, y, total;
+  int max_tiles;
+};
+BatchedWs batched_ws_layout(int T, int H, int I, int E, int k, int dtype);
+
+hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
+                           uint8_t* scales, hipStream_t s);
+
+hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* wgu,
+                                  const uint8_t* wgus, const int32_t* idx, int T, int H, int I,
+                                  int E, int k, int dtype, void* h, uint8_t* hs, void* ws,
+                                  hipStream_t s, int num_cus);
+
+hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
+                               const uint8_t* wds, const int32_t* idx, const float* w, int T,
+                               int H, int I, int E, int k, int dtype, uint16_t* out, void* ws,
+                               hipStream_t s, int num_cus);
+
+}  // namespace moe

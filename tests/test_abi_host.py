@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    from mixture_experts_ffn_07_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build()
+    import mixture_experts_ffn_07_amd as M
+    return M
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(m):
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(m.lib, n), n
+        assert ctypes.cast(getattr(m.lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings(m):
+    assert m.lib.moe_status_string(0) == b"ok"
+    for s in range(-6, 0):
+        assert m.lib.moe_status_string(s) not in (b"ok", b"unknown status")
+    assert m.lib.moe_status_string(5) == b"unknown status"
+
+
+FAKE = 0x10000        # a 16-byte aligned address that is never dereferenced
+
+
+def _dec(m, T=4, H=512, I=256, E=8, k=2, x=FAKE, lg=FAKE, wgu=FAKE, wd=FAKE, out=FAKE,
+         ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = m.lib.moe_decode_workspace_bytes(max(T, 1), H, I, E, k)
+    return m.lib.moe_decode_forward(x, lg, wgu, wd, T, H, I, E, k, out, None, None, ws, wsb, None)
+
+
+def test_decode_validation(m):
+    assert _dec(m, x=None) == m.MOE_ERR_NULL
+    assert _dec(m, out=None) == m.MOE_ERR_NULL
+    assert _dec(m, k=0) == m.MOE_ERR_SHAPE
+    assert _dec(m, k=9) == m.MOE_ERR_SHAPE                 # k > E
+    assert _dec(m, E=40, k=33) == m.MOE_ERR_SHAPE          # k > 32
+    assert _dec(m, E=1025, k=2) == m.MOE_ERR_SHAPE
+    assert _dec(m, H=384) == m.MOE_ERR_SHAPE               # not a multiple of 256
+    assert _dec(m, I=128) == m.MOE_ERR_SHAPE
+    assert _dec(m, T=0) == m.MOE_ERR_SHAPE
+    assert _dec(m, T=65, wsb=1 << 30) == m.MOE_ERR_UNSUPPORTED
+    assert _dec(m, ws=None) == m.MOE_ERR_WORKSPACE
+    need = m.lib.moe_decode_workspace_bytes(4, 512, 256, 8, 2)
+    assert _dec(m, wsb=need - 1) == m.MOE_ERR_WORKSPACE
+    assert _dec(m, x=FAKE + 2) == m.MOE_ERR_ALIGN
+    assert _dec(m, ws=FAKE + 8) == m.MOE_ERR_ALIGN
+    assert b"aligned" in m.lib.moe_last_error()
+
+
+def test_workspace_sizes(m):
+    assert m.lib.moe_decode_workspace_bytes(0, 512, 256, 8, 2) == 0
+    assert m.lib.moe_decode_workspace_bytes(65, 512, 256, 8, 2) == 0
+    a = m.lib.moe_decode_workspace_bytes(1, 2048, 768, 128, 8)
+    b = m.lib.moe_decode_workspace_bytes(32, 2048, 768, 128, 8)
+    assert 0 < a < b
+    # the activation hand-off (two BF16 arrays of T*k*I) dominates
+    assert b >= 32 * 8 * 768 * 4
+    assert m.lib.moe_workspace_bytes(2048, 7168, 2048, 384, 8, 0) > 0
+    assert m.lib.moe_workspace_bytes(2048, 7168, 2048, 384, 8, 7) == 0
+
+
+def test_route_validation(m):
+    r = m.lib.moe_route_topk
+    assert r(FAKE, 4, 8, 0, FAKE, FAKE, None) == m.MOE_ERR_SHAPE
+    assert r(FAKE, 4, 8, 9, FAKE, FAKE, None) == m.MOE_ERR_SHAPE
+    assert r(FAKE, -1, 8, 2, FAKE, FAKE, None) == m.MOE_ERR_SHAPE
+    assert r(None, 4, 8, 2, FAKE, FAKE, None) == m.MOE_ERR_NULL
+    assert r(None, 0, 8, 2, None, None, None) == m.MOE_OK        # T = 0 enqueues nothing
+
+
+def test_quant_validation(m):
+    q = m.lib.moe_quantize_mxfp8
+    assert q(FAKE, 4, 48, FAKE, FAKE, None) == m.MOE_ERR_SHAPE
+    assert q(FAKE, -1, 64, FAKE, FAKE, None) == m.MOE_ERR_SHAPE
+    assert q(None, 4, 64, FAKE, FAKE, None) == m.MOE_ERR_NULL
+    assert q(FAKE, 4, 64, FAKE + 1, FAKE, None) == m.MOE_ERR_ALIGN
+    assert q(None, 0, 64, None, None, None) == m.MOE_OK
+
+
+def test_batched_validation(m):
+    g = m.lib.moe_gate_up_3d_batched
+    need = m.lib.moe_workspace_bytes(64, 256, 256, 8, 2, 0)
+    args = dict(T=64, H=256, I=256, E=8, k=2, dt=0)
+
+    def call(x=FAKE, xs=None, w=FAKE, ws_=None, idx=FAKE, h=FAKE, hs=None, ws=FAKE, wsb=need, **kw):
+        a = dict(args, **kw)
+        return g(x, xs, w, ws_, idx, a["T"], a["H"], a["I"], a["E"], a["k"], a["dt"], h, hs, ws,
+                 wsb, None)
+    assert call(x=None) == m.MOE_ERR_NULL
+    assert call(H=200) == m.MOE_ERR_SHAPE
+    assert call(dt=3) == m.MOE_ERR_SHAPE
+    assert call(wsb=need - 1) == m.MOE_ERR_WORKSPACE
+    assert call(h=FAKE + 4) == m.MOE_ERR_ALIGN
+    assert call(dt=1, wsb=m.lib.moe_workspace_bytes(64, 256, 256, 8, 2, 1)) == m.MOE_ERR_NULL
+    d = m.lib.moe_down_3d_batched
+    assert d(FAKE, None, FAKE, None, FAKE, None, 64, 256, 256, 8, 2, 0, FAKE, FAKE, need,
+             None) == m.MOE_ERR_NULL
+
+
+def test_profile_hook_validation(m):
+    assert m.lib.moe_profile_kernel(99, None, None) == m.MOE_ERR_SHAPE
+    assert m.lib.moe_profile_kernel(2, None, None) == m.MOE_OK
+    assert m.lib.moe_profile_kernel(0, None, None) == m.MOE_OK
