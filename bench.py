@@ -30,6 +30,7 @@ import time
 
 METRIC = "MoE layer tokens/s; decode HBM TB/s % of peak; batched MFMA util %"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}   # dense, MI355X
 
 
 def parse():
@@ -112,6 +113,87 @@ def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="decod
     return res
 
 
+def batched_algorithmic(cfg, U):
+    """HBM bytes and MFMA flops the batched kernels must at least move / do."""
+    T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
+    P = T * k
+    eb = 1 if cfg.dtype == "mxfp8" else 2            # bytes per weight / activation code
+    sb = (1.0 / 32) if cfg.dtype == "mxfp8" else 0.0  # scale bytes per element
+    gate_up = U * 2 * I * H * (eb + sb) + T * H * (eb + sb) + P * I * (eb + sb)
+    down = U * H * I * (eb + sb) + P * I * (eb + sb)
+    down += (T * H * 2) if k == 1 else (P * H * 4 * 2 + T * H * 2)   # y round trip + out
+    return {"gate_up": gate_up, "down": down,
+            "flops_gate_up": 2.0 * P * 2 * I * H, "flops_down": 2.0 * P * H * I}
+
+
+def run_batched(M, W, torch, cfg, steps, warmup, seed, n_batches=4):
+    from mixture_experts_ffn_07_amd.hip_events import HipEvent
+    dev = "cuda"
+    log(f"generating weights of {cfg.name} ({W.expert_bytes(cfg) * cfg.E / 1e9:.1f} GB)")
+    wts = W.make_weights(cfg, seed=seed, device=dev)
+    acts = [W.make_activations(cfg, seed=seed + 7919 * (b + 1), device=dev) for b in range(n_batches)]
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    dt = M.MOE_MXFP8 if cfg.dtype == "mxfp8" else M.MOE_BF16
+    stream = torch.cuda.current_stream()
+    ws = M.workspace(M.moe_workspace_bytes(T, H, I, E, k, dt), dev)
+    idx = torch.empty(n_batches, T, k, dtype=torch.int32, device=dev)
+    tw = torch.empty(n_batches, T, k, dtype=torch.float32, device=dev)
+    hdt = torch.uint8 if dt == M.MOE_MXFP8 else torch.bfloat16
+    h = torch.empty(T * k, I, dtype=hdt, device=dev)
+    hs = torch.empty(T * k, I // 32, dtype=torch.uint8, device=dev) if dt == M.MOE_MXFP8 else None
+    xc = torch.empty(T, H, dtype=torch.uint8, device=dev) if dt == M.MOE_MXFP8 else None
+    xs = torch.empty(T, H // 32, dtype=torch.uint8, device=dev) if dt == M.MOE_MXFP8 else None
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        b = i % n_batches
+        a = acts[b]
+        M.moe_route_topk(a["logits"], k, topk_idx=idx[b], topk_w=tw[b], stream=stream)
+        if dt == M.MOE_MXFP8:
+            M.moe_quantize_mxfp8(a["x"], codes=xc, scales=xs, stream=stream)
+            M.moe_gate_up_3d_batched(xc, wts["w_gate_up"], idx[b], k, dt, x_scales=xs,
+                                     w_gate_up_scales=wts["w_gate_up_scales"], h=h, h_scales=hs,
+                                     ws=ws, stream=stream)
+            M.moe_down_3d_batched(h, wts["w_down"], idx[b], tw[b], ws, k, dt, h_scales=hs,
+                                  w_down_scales=wts["w_down_scales"], out=out, stream=stream)
+        else:
+            M.moe_gate_up_3d_batched(a["x"], wts["w_gate_up"], idx[b], k, dt, h=h, ws=ws,
+                                     stream=stream)
+            M.moe_down_3d_batched(h, wts["w_down"], idx[b], tw[b], ws, k, dt, out=out,
+                                  stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        M.moe_profile_kernel("gemm_gate_up", evs[s][0].handle, evs[s][1].handle)
+        step(warmup + s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    M.moe_profile_kernel("none", None, None)
+    durs = [a.elapsed_ms(b) for a, b in evs]
+    U = [int(torch.unique(idx[(warmup + s) % n_batches]).numel()) for s in range(steps)]
+    alg = [batched_algorithmic(cfg, u) for u in U]
+    elapsed = t1 - t0
+    kern_s = sum(durs) * 1e-3
+    return {
+        "elapsed_s": elapsed, "ms_per_step": 1e3 * elapsed / steps,
+        "tokens_per_s": T * steps / elapsed,
+        "kernel_avg_us": 1e3 * sum(durs) / steps,
+        "kernel_gbs": sum(a["gate_up"] for a in alg) / kern_s / 1e9,
+        "kernel_tflops": sum(a["flops_gate_up"] for a in alg) / kern_s / 1e12,
+        "kernel_bytes_per_launch": sum(a["gate_up"] for a in alg) / steps,
+        "kernel_flops_per_launch": sum(a["flops_gate_up"] for a in alg) / steps,
+        "layer_gbs": sum(a["gate_up"] + a["down"] for a in alg) / elapsed / 1e9,
+        "layer_tflops": sum(a["flops_gate_up"] + a["flops_down"] for a in alg) / elapsed / 1e12,
+        "avg_touched_experts": sum(U) / steps,
+        "first_batch": acts[warmup % n_batches], "first_weights": wts,
+    }
+
+
 def cpu_baseline(W, cfg, act, weights, seconds):
     """Time the FP64 oracle on this host (bounded sample of the same workload)."""
     import numpy as np
@@ -156,28 +238,48 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     cfg = W.get(args.workload)
-    if cfg.path != "decode":
-        raise SystemExit(f"workload {cfg.name} is a batched workload; not wired into bench.py yet")
     log(f"device {torch.cuda.get_device_name(0)}; workload {cfg.name}")
-    r = run_decode(M, W, torch, cfg, args.steps, args.warmup, args.layers, args.seed)
-    roof = {"bound": "hbm", "kernel": "decode_gate_up", "achieved": round(r["kernel_gbs"], 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(r["kernel_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None, "avg_launch_us": round(r["kernel_avg_us"], 2),
-            "algorithmic_bytes_per_launch": int(r["kernel_bytes_per_launch"])}
+    if cfg.path == "decode":
+        r = run_decode(M, W, torch, cfg, args.steps, args.warmup, args.layers, args.seed)
+        roof = {"bound": "hbm", "kernel": "decode_gate_up", "achieved": round(r["kernel_gbs"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(r["kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "avg_launch_us": round(r["kernel_avg_us"], 2),
+                "algorithmic_bytes_per_launch": int(r["kernel_bytes_per_launch"])}
+    else:
+        r = run_batched(M, W, torch, cfg, args.steps, args.warmup, args.seed)
+        peak_tf = MFMA_PEAK_TFLOPS[cfg.dtype]
+        rows_per_expert = cfg.T * cfg.k / cfg.E
+        if rows_per_expert >= 256:       # weight reuse high enough to be MFMA-bound
+            roof = {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": round(r["kernel_tflops"], 1),
+                    "peak": peak_tf, "unit": "TFLOP/s", "frac": round(r["kernel_tflops"] / peak_tf, 4),
+                    "traffic": None, "avg_launch_us": round(r["kernel_avg_us"], 2),
+                    "algorithmic_flops_per_launch": int(r["kernel_flops_per_launch"]),
+                    "hbm_gbs": round(r["kernel_gbs"], 1)}
+        else:
+            roof = {"bound": "hbm", "kernel": "gemm_gate_up", "achieved": round(r["kernel_gbs"], 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(r["kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_us": round(r["kernel_avg_us"], 2),
+                    "algorithmic_bytes_per_launch": int(r["kernel_bytes_per_launch"]),
+                    "mfma_tflops": round(r["kernel_tflops"], 1),
+                    "mfma_frac": round(r["kernel_tflops"] / peak_tf, 4)}
     line = {
         "metric": METRIC, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "mxfp8 (e4m3 + e8m0), fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
                    "I": cfg.I, "weight_sets": args.layers, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer": {"hbm_gbs": round(r["layer_gbs"], 1),
+                  **({"mfma_tflops": round(r["layer_tflops"], 1)} if "layer_tflops" in r else {}),
                   "hbm_frac": round(r["layer_gbs"] / HBM_PEAK_GBS, 4),
                   "avg_touched_experts": round(r["avg_touched_experts"], 2),
                   "latency_us": round(1e3 * r["ms_per_step"], 2)},
     }
-    if args.extra:
+    if args.extra and cfg.path == "decode":
         ex = {}
         for T in (1, 8):
             c2 = W.get(f"qwen3-decode-T{T}")
@@ -188,7 +290,7 @@ def main():
                            "gate_up_gbs": round(r2["kernel_gbs"], 1),
                            "layer_gbs": round(r2["layer_gbs"], 1)}
         line["extra"] = ex
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and cfg.path == "decode":
         log("timing the CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(W, cfg, r["first_batch"], r["first_weights"],
                                             args.cpu_seconds)

@@ -140,7 +140,8 @@ int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int K,
  *              writes the expert grouping into it, and moe_down_3d_batched
  *              must be given the same workspace and topk_idx, later on the
  *              same stream
- * Limits: T >= 1, H and I multiples of 128, 1 <= k <= min(E, 32), E <= 1024.
+ * Limits: T >= 1, H a multiple of 256, I a multiple of 128, 1 <= k <= min(E, 32),
+ * E <= 1024.
  */
 int moe_gate_up_3d_batched(const void* x, const uint8_t* x_scales,
                            const void* w_gate_up, const uint8_t* w_gate_up_scales,

@@ -183,7 +183,7 @@ int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
 
 static int check_batched(int T, int H, int I, int E, int k, int dtype, const void* ws,
                          size_t ws_bytes) {
-  if (int st = check_common(T, H, I, E, k, 128, 128)) return st;
+  if (int st = check_common(T, H, I, E, k, 256, 128)) return st;
   if (T < 1) return fail(MOE_ERR_SHAPE, "T=%d < 1", T);
   if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return fail(MOE_ERR_SHAPE, "dtype=%d", dtype);
   if (static_cast<long long>(T) * k > (1LL << 30)) return fail(MOE_ERR_SHAPE, "T*k too large");

@@ -50,4 +50,53 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Block-scaled FP8 (E4M3 x E4M3) MFMA, 16x16x128.  Operand lane layout: lane
+// (r, g) = (lane % 16, lane / 16) holds row r, K elements [16g, 16g+16) in
+// bytes 0..15 and [64+16g, 64+16g+16) in bytes 16..31; the E8M0 scale in the
+// low byte of lane (r, g)'s scale operand applies to K block [32g, 32g+32).
+__device__ __forceinline__ f32x4 mfma_mx16x16x128(i32x8 a, i32x8 b, int sa, int sb, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ i32x8 cat8(i32x4 lo, i32x4 hi) {
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// MX scale exponent of a block (OCP Microscaling v1.0 rule for E4M3):
+// s = floor(log2(amax)) - 8, clamped to [-127, 127]; amax = 0 gives -127.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  const uint32_t u = __float_as_uint(amax) & 0x7FFFFFFFu;
+  int fl;
+  if (u == 0) return -127;
+  if ((u >> 23) == 0) fl = (31 - __clz(u)) - 149;      // subnormal amax
+  else fl = static_cast<int>(u >> 23) - 127;
+  int s = fl - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// 2^-s as an exact FP32 value, s in [-127, 127].
+__device__ __forceinline__ float exp2_neg(int s) {
+  const int e = -s;                                      // in [-127, 127]
+  return e >= -126 ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23)
+                   : __uint_as_float(0x00400000u);       // 2^-127, subnormal
+}
+
+// FP32 -> E4M3 code: round to nearest even, saturate to +-448, sign copied.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __uint_as_float(u & 0x7FFFFFFFu);
+  uint32_t mag;
+  if (a >= 448.0f) {
+    mag = 0x7Eu;
+  } else if (a < 0.015625f) {                           // below 2^-6: step 2^-9
+    mag = static_cast<uint32_t>(rintf(a * 512.0f));     // 0..8, 8 = smallest normal
+  } else {
+    const uint32_t ab = __float_as_uint(a);
+    const uint32_t r = ab + 0x7FFFFu + ((ab >> 20) & 1u);   // RNE at the 3rd mantissa bit
+    mag = (r >> 20) - (120u << 3);                      // rebias 127 -> 7
+  }
+  return sign | mag;
+}
+
 }  // namespace moe

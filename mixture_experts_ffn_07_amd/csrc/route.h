@@ -25,15 +25,36 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
   return __uint_as_float(u);
 }
 
+// One DPP step of a 64-bit max: combine each lane with the lane CTRL names.
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, 0xF, 0xF, false));
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Wave-wide max of a 64-bit key, returned to every lane.  Within each row of
+// 16 lanes: quad swaps (xor 1, xor 2), then half-row and row mirrors; the four
+// row maxima are then read into scalar registers and combined.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, kWave);
-    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, kWave);
-    uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = max_dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = max_dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = max_dpp<0x141>(v);   // row_half_mirror
+  v = max_dpp<0x140>(v);   // row_mirror
+  uint64_t a = readlane_u64(v, 0), b = readlane_u64(v, 16);
+  uint64_t c = readlane_u64(v, 32), d = readlane_u64(v, 48);
+  a = a > b ? a : b;
+  c = c > d ? c : d;
+  return a > c ? a : c;
 }
 
 // Routes one token.  `lrow` points at its E logits.  On return lanes j < k hold

@@ -1,0 +1,146 @@
+"""GPU parity of the MXFP8 path: moe_quantize_mxfp8 bit-exact with the oracle's
+MX quantizer; the MXFP8 layer within relative L2 3e-2 of the
+quantization-aware FP64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import formats as F
+from oracle import route
+from oracle.moe import rel_l2
+from tests._gpu import MXFP8_REL_L2, W_ABS, bits, oracle, to_f64
+
+pytestmark = pytest.mark.gpu
+
+MX_TRIPWIRE = 1e-2     # expected ~2e-3 (BF16 output rounding); above this is a bug
+
+
+@pytest.fixture(scope="module")
+def M():
+    import mixture_experts_ffn_07_amd as M
+    return M
+
+
+def _quant_check(M, x: torch.Tensor, what: str):
+    print(f"[quant] {what}: {tuple(x.shape)}", flush=True)
+    codes, scales = M.moe_quantize_mxfp8(x.cuda().contiguous())
+    torch.cuda.synchronize()
+    want_c, want_s = F.mx_quantize(F.bf16_decode(bits(x)))
+    assert np.array_equal(scales.cpu().numpy(), want_s), what
+    got_c = codes.cpu().numpy()
+    bad = np.nonzero(got_c != want_c)
+    assert bad[0].size == 0, f"{what}: {bad[0].size} codes differ, first at {bad[0][0]},{bad[1][0]}"
+
+
+@pytest.mark.parametrize("rows,K,std", [(1, 32, 1.0), (7, 96, 0.02), (2048, 7168, 1.0),
+                                        (333, 256, 1e-3), (64, 4096, 50.0)])
+def test_quantize_random(M, rows, K, std):
+    g = torch.Generator().manual_seed(rows + K)
+    _quant_check(M, (torch.randn(rows, K, generator=g) * std).to(torch.bfloat16), f"std={std}")
+
+
+def test_quantize_edge_blocks(M):
+    x = torch.zeros(8, 64, dtype=torch.float32)
+    x[1, :32] = -0.0                                     # negative-zero block
+    x[2, 5] = 2.0 ** -130                                # subnormal-range max (bf16 keeps it)
+    x[3] = torch.linspace(-1, 1, 64) * 3.9999            # max just below 2^2
+    x[4, :32] = 2.0 ** 7                                 # exact power of two
+    x[4, 32:] = torch.linspace(-511, 511, 32) / 256      # values that saturate after scaling
+    x[5] = 1e-30                                         # tiny but normal
+    x[6, ::2] = 3.0e38                                   # near the BF16 maximum
+    x[7] = torch.arange(64) - 31.5
+    _quant_check(M, x.to(torch.bfloat16), "edge blocks")
+
+
+def test_quantize_empty(M):
+    c, s = M.moe_quantize_mxfp8(torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"))
+    assert c.shape == (0, 64) and s.shape == (0, 2)
+
+
+def run_mx(M, d):
+    cfg = d["cfg"]
+    idx, w = M.moe_route_topk(d["logits"], cfg.k)
+    xc, xs = M.moe_quantize_mxfp8(d["x"])
+    h, hs, ws = M.moe_gate_up_3d_batched(xc, d["w_gate_up"], idx, cfg.k, M.MOE_MXFP8,
+                                         x_scales=xs, w_gate_up_scales=d["w_gate_up_scales"])
+    out = M.moe_down_3d_batched(h, d["w_down"], idx, w, ws, cfg.k, M.MOE_MXFP8, h_scales=hs,
+                                w_down_scales=d["w_down_scales"])
+    torch.cuda.synchronize()
+    return out, idx, w, h, hs
+
+
+def _check(M, d, what, tokens=None):
+    cfg = d["cfg"]
+    print(f"[mxfp8] {what}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}", flush=True)
+    out, idx, w, h, hs = run_mx(M, d)
+    ridx, rw = route(d["logits"].cpu().numpy(), cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.max(np.abs(w.cpu().double().numpy() - rw)) <= W_ABS
+    ref = oracle(d, tokens=tokens)
+    got = out if tokens is None else out[torch.as_tensor(tokens, device=out.device)]
+    g = to_f64(got)
+    assert np.all(np.isfinite(g))
+    rl = rel_l2(g, ref)
+    print(f"[parity] {what}: rel_l2={rl:.3e}", flush=True)
+    assert rl <= MXFP8_REL_L2, f"{what}: rel_l2 {rl:.3e} > {MXFP8_REL_L2}"
+    assert rl <= MX_TRIPWIRE, f"{what}: rel_l2 {rl:.3e} above the expected level {MX_TRIPWIRE}"
+    return rl
+
+
+def _custom(T, H, I, E, k, seed=0):
+    cfg = W.Config(name=f"mx-T{T}-H{H}-I{I}-E{E}-k{k}", T=T, H=H, E=E, k=k, I=I, dtype="mxfp8",
+                   path="batched")
+    return W.make(cfg, seed=seed, device="cuda")
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (1, 256, 128, 4, 2),
+    (100, 512, 256, 8, 2),
+    (300, 256, 384, 6, 3),      # several M-tiles per expert
+    (257, 768, 128, 40, 8),
+    (500, 512, 256, 6, 1),      # k = 1: fused output
+])
+def test_mx_shapes(M, T, H, I, E, k):
+    _check(M, _custom(T, H, I, E, k, seed=T + 1), f"mx shape T={T} H={H} I={I} E={E} k={k}")
+
+
+def _sample(T, n, seed):
+    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
+
+
+def test_mx_dsv4_full_size(M):
+    d = W.make("dsv4-mxfp8-T2048", seed=0, device="cuda")
+    _check(M, d, "dsv4-mxfp8-T2048 (6 sampled tokens)", tokens=_sample(2048, 6, 2))
+
+
+def test_mx_dsv4_ep64_share(M):
+    d = W.make("dsv4-mxfp8-ep64share", seed=0, device="cuda")
+    _check(M, d, "dsv4-mxfp8-ep64share (48 sampled tokens)", tokens=_sample(16384, 48, 3))
+
+
+def test_mx_bit_identical_repeats(M):
+    d = _custom(1024, 512, 256, 32, 8, seed=5)
+    first = run_mx(M, d)
+    for _ in range(3):
+        again = run_mx(M, d)
+        assert torch.equal(again[0].view(torch.int16), first[0].view(torch.int16))
+        assert torch.equal(again[3], first[3]) and torch.equal(again[4], first[4])
+
+
+def test_mx_h_codes_match_oracle_quantizer(M):
+    # the h codes the GPU writes are the MX quantization of its own FP32
+    # activations; re-quantizing their decoded values must reproduce them, and
+    # they must be close to the oracle's unquantized activations
+    d = _custom(64, 256, 256, 4, 2, seed=6)
+    cfg = d["cfg"]
+    out, idx, w, h, hs = run_mx(M, d)
+    codes, scales = h.cpu().numpy(), hs.cpu().numpy()
+    deq = F.mx_dequantize(codes, scales)
+    c2, s2 = F.mx_quantize(deq)
+    assert np.array_equal(s2, scales) and np.array_equal(c2, codes)
+    _, inter = oracle(d, return_intermediates=True)
+    ridx, _ = route(d["logits"].cpu().numpy(), cfg.k)
+    pairs = sorted((int(ridx[t, j]), t, j) for t in range(cfg.T) for j in range(cfg.k))
+    want = np.stack([inter["a"][t, j] for (_, t, j) in pairs])
+    assert rel_l2(deq, want) < 1e-2
