@@ -32,6 +32,8 @@ constexpr int kBM = 64;            // rows (routed pairs) per M-tile
 constexpr int kGuNeurons = 128;    // neurons per gate_up workgroup (4 waves x 32)
 constexpr int kDnRows = 256;       // output dims per down workgroup (4 waves x 64)
 constexpr int kXcds = 8;
+constexpr int kStagesBf16 = 2;   // register pipeline depth of the BF16 GEMMs
+constexpr int kStagesMx = 2;     // and of the MXFP8 GEMMs
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 }  // namespace
@@ -146,6 +148,11 @@ __device__ __forceinline__ int xcd_item(int L, int n_items) {
 // gate_up, BF16: workgroup = (M-tile, 128 neurons); wave = 32 neurons (16
 // gate rows + 16 up rows in two groups) x 64 rows.  MFMA 16x16x32: A = weight
 // rows (lane: row col, K chunk grp), B = activation rows, D[row][token].
+// The K loop is double-buffered in registers: the loads of step ks + 1 are
+// issued before the MFMAs of step ks, so every wave keeps a step of weights
+// in flight while it computes.  Rows past the tile's end load the tile's first row;
+// their MFMA columns are computed and discarded (columns never mix).
+template <int D>
 __global__ __launch_bounds__(256) void gemm_gate_up_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
@@ -161,20 +168,18 @@ __global__ __launch_bounds__(256) void gemm_gate_up_bf16(
   const int rbase = offsets[e] + m0;
   const int wv = wave_id(), ln = lane_id(), col = ln & 15, grp = ln >> 4;
   const int nb = nb_i * kGuNeurons + wv * 32;
-  const bf16x8 zero8 = {};
 
-  const uint16_t* xr[4];
+  const uint16_t* __restrict__ wb = wgu + static_cast<size_t>(e) * 2 * I * H;
+  uint32_t og[2], ou[2], ox[4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    og[q] = static_cast<uint32_t>((nb + 16 * q + col) * H + grp * 8);
+    ou[q] = og[q] + static_cast<uint32_t>(I * H);
+  }
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
-    xr[g] = r < mcount ? x + static_cast<size_t>(perm[rbase + r] / k) * H + grp * 8 : nullptr;
-  }
-  const uint16_t* wg[2];
-  const uint16_t* wu[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    wg[q] = wgu + (static_cast<size_t>(e) * 2 * I + nb + 16 * q + col) * H + grp * 8;
-    wu[q] = wg[q] + static_cast<size_t>(I) * H;
+    ox[g] = static_cast<uint32_t>((perm[rbase + (r < mcount ? r : 0)] / k) * H + grp * 8);
   }
   f32x4 ag[2][4], au[2][4];
 #pragma unroll
@@ -182,26 +187,33 @@ __global__ __launch_bounds__(256) void gemm_gate_up_bf16(
 #pragma unroll
     for (int g = 0; g < 4; ++g) ag[q][g] = au[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ksteps = H / 32;
-#pragma unroll 2
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int ko = ks * 32;
-    bf16x8 a_g[2], a_u[2], b[4];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      a_g[q] = as_bf16x8(ld16(wg[q] + ko));
-      a_u[q] = as_bf16x8(ld16(wu[q] + ko));
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) b[g] = xr[g] ? as_bf16x8(ld16(xr[g] + ko)) : zero8;
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        ag[q][g] = mfma16x16x32(a_g[q], b[g], ag[q][g]);
-        au[q][g] = mfma16x16x32(a_u[q], b[g], au[q][g]);
-      }
+  bf16x8 bg[D][2], bu[D][2], bx[D][4];
+#define GU_LOAD(S, KO)                                                    \
+  {                                                                       \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                       \
+      bg[S][q] = as_bf16x8(ld16(wb + og[q] + (KO)));                      \
+      bu[S][q] = as_bf16x8(ld16(wb + ou[q] + (KO)));                      \
+    }                                                                     \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) bx[S][g] = as_bf16x8(ld16(x + ox[g] + (KO))); \
   }
+  const int ksteps = H / 32;
+#define GU_MMA(S)                                                             \
+  _Pragma("unroll") for (int q = 0; q < 2; ++q)                               \
+  _Pragma("unroll") for (int g = 0; g < 4; ++g) {                             \
+    ag[q][g] = mfma16x16x32(bg[S][q], bx[S][g], ag[q][g]);                    \
+    au[q][g] = mfma16x16x32(bu[S][q], bx[S][g], au[q][g]);                    \
+  }
+  GU_LOAD(0, 0)
+  const int kpairs = ksteps & ~1;
+  for (int ks = 0; ks < kpairs; ks += 2) {
+    GU_LOAD(1, (ks + 1) * 32)
+    GU_MMA(0)
+    GU_LOAD(0, min(ks + 2, ksteps - 1) * 32)
+    GU_MMA(1)
+  }
+  if (ksteps & 1) { GU_MMA(0) }
+#undef GU_MMA
+#undef GU_LOAD
   // SwiGLU epilogue: lane holds neurons nb+16q+4grp+{0..3} of row 16g+col
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -222,8 +234,9 @@ __global__ __launch_bounds__(256) void gemm_gate_up_bf16(
 }
 
 // down, BF16: workgroup = (M-tile, 256 output dims); wave = 64 dims (4 groups)
-// x 64 rows.  FUSED (k = 1): out[t] = bf16(w[t] * y) with t = perm[row].
-template <bool FUSED>
+// x 64 rows; the same double-buffered K loop.  FUSED (k = 1): out[t] = bf16(w[t] * y)
+// with t = perm[row].
+template <bool FUSED, int D>
 __global__ __launch_bounds__(256) void gemm_down_bf16(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ wd,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
@@ -239,38 +252,45 @@ __global__ __launch_bounds__(256) void gemm_down_bf16(
   const int rbase = offsets[e] + m0;
   const int wv = wave_id(), ln = lane_id(), col = ln & 15, grp = ln >> 4;
   const int db = db_i * kDnRows + wv * 64;
-  const bf16x8 zero8 = {};
 
-  const uint16_t* hr[4];
+  const uint16_t* __restrict__ wb = wd + static_cast<size_t>(e) * H * I;
+  const uint16_t* __restrict__ hb = h + static_cast<size_t>(rbase) * I;
+  uint32_t ow[4], oh[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ow[q] = static_cast<uint32_t>((db + 16 * q + col) * I + grp * 8);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
-    hr[g] = r < mcount ? h + static_cast<size_t>(rbase + r) * I + grp * 8 : nullptr;
+    oh[g] = static_cast<uint32_t>((r < mcount ? r : 0) * I + grp * 8);
   }
-  const uint16_t* wr[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    wr[q] = wd + (static_cast<size_t>(e) * H + db + 16 * q + col) * I + grp * 8;
   f32x4 acc[4][4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ksteps = I / 32;
-#pragma unroll 2
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int ko = ks * 32;
-    bf16x8 a[4], b[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) a[q] = as_bf16x8(ld16(wr[q] + ko));
-#pragma unroll
-    for (int g = 0; g < 4; ++g) b[g] = hr[g] ? as_bf16x8(ld16(hr[g] + ko)) : zero8;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) acc[q][g] = mfma16x16x32(a[q], b[g], acc[q][g]);
+  bf16x8 ba[D][4], bb[D][4];
+#define DN_LOAD(S, KO)                                                                   \
+  {                                                                                      \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) ba[S][q] = as_bf16x8(ld16(wb + ow[q] + (KO))); \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) bb[S][g] = as_bf16x8(ld16(hb + oh[g] + (KO))); \
   }
+  const int ksteps = I / 32;
+#define DN_MMA(S)                                                             \
+  _Pragma("unroll") for (int q = 0; q < 4; ++q)                               \
+  _Pragma("unroll") for (int g = 0; g < 4; ++g)                               \
+    acc[q][g] = mfma16x16x32(ba[S][q], bb[S][g], acc[q][g]);
+  DN_LOAD(0, 0)
+  const int kpairs = ksteps & ~1;
+  for (int ks = 0; ks < kpairs; ks += 2) {
+    DN_LOAD(1, (ks + 1) * 32)
+    DN_MMA(0)
+    DN_LOAD(0, min(ks + 2, ksteps - 1) * 32)
+    DN_MMA(1)
+  }
+  if (ksteps & 1) { DN_MMA(0) }
+#undef DN_MMA
+#undef DN_LOAD
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
@@ -365,7 +385,8 @@ __global__ __launch_bounds__(256) void quant_mx_rows(const uint16_t* __restrict_
 // gate_up, MXFP8: workgroup = (M-tile, 128 neurons); wave = 32 neurons (one
 // MX block of h) x 64 rows.  Per 128-wide K chunk a lane loads two 16-byte
 // pieces of its weight row and of its activation row, plus the row's scale
-// byte for block g of the chunk.
+// byte for block g of the chunk; double-buffered as the BF16 kernel.
+template <int D>
 __global__ __launch_bounds__(256) void gemm_gate_up_mx(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ wgu, const uint8_t* __restrict__ wgus,
@@ -384,27 +405,23 @@ __global__ __launch_bounds__(256) void gemm_gate_up_mx(
   const int nb = nb_i * kGuNeurons + wv * 32;
   const int KB = H / 32;                               // scale bytes per row
 
-  const uint8_t* xr[4];
-  const uint8_t* xsr[4];
+  const uint8_t* __restrict__ wb = wgu + static_cast<size_t>(e) * 2 * I * H;
+  const uint8_t* __restrict__ wsb = wgus + static_cast<size_t>(e) * 2 * I * KB;
+  uint32_t og[2], ou[2], osg[2], osu[2], ox[4], osx[4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int rg = nb + 16 * q + col, ru = rg + I;
+    og[q] = static_cast<uint32_t>(rg * H + 16 * grp);
+    ou[q] = static_cast<uint32_t>(ru * H + 16 * grp);
+    osg[q] = static_cast<uint32_t>(rg * KB + grp);
+    osu[q] = static_cast<uint32_t>(ru * KB + grp);
+  }
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
-    const int tok = r < mcount ? perm[rbase + r] / k : -1;
-    xr[g] = tok >= 0 ? x + static_cast<size_t>(tok) * H + 16 * grp : nullptr;
-    xsr[g] = tok >= 0 ? xs + static_cast<size_t>(tok) * KB + grp : nullptr;
-  }
-  const uint8_t* wg[2];
-  const uint8_t* wu[2];
-  const uint8_t* wgs[2];
-  const uint8_t* wus[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const size_t rg = static_cast<size_t>(e) * 2 * I + nb + 16 * q + col;
-    const size_t ru = rg + I;
-    wg[q] = wgu + rg * H + 16 * grp;
-    wu[q] = wgu + ru * H + 16 * grp;
-    wgs[q] = wgus + rg * KB + grp;
-    wus[q] = wgus + ru * KB + grp;
+    const int tok = perm[rbase + (r < mcount ? r : 0)] / k;
+    ox[g] = static_cast<uint32_t>(tok * H + 16 * grp);
+    osx[g] = static_cast<uint32_t>(tok * KB + grp);
   }
   f32x4 ag[2][4], au[2][4];
 #pragma unroll
@@ -412,36 +429,40 @@ __global__ __launch_bounds__(256) void gemm_gate_up_mx(
 #pragma unroll
     for (int g = 0; g < 4; ++g) ag[q][g] = au[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int chunks = H / 128;
-  for (int kc = 0; kc < chunks; ++kc) {
-    const int ko = kc * 128, so = kc * 4;
-    i32x8 a_g[2], a_u[2], b[4];
-    int sg[2], su[2], sx[4];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      a_g[q] = cat8(ld16(wg[q] + ko), ld16(wg[q] + ko + 64));
-      a_u[q] = cat8(ld16(wu[q] + ko), ld16(wu[q] + ko + 64));
-      sg[q] = wgs[q][so];
-      su[q] = wus[q][so];
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (xr[g]) {
-        b[g] = cat8(ld16(xr[g] + ko), ld16(xr[g] + ko + 64));
-        sx[g] = xsr[g][so];
-      } else {
-        b[g] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        sx[g] = 127;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        ag[q][g] = mfma_mx16x16x128(a_g[q], b[g], sg[q], sx[g], ag[q][g]);
-        au[q][g] = mfma_mx16x16x128(a_u[q], b[g], su[q], sx[g], au[q][g]);
-      }
+  i32x8 bg[D][2], bu[D][2], bx[D][4];
+  int sg[D][2], su[D][2], sx[D][4];
+#define GUM_LOAD(S, KC)                                                               \
+  {                                                                                   \
+    const int ko = (KC) * 128, so = (KC) * 4;                                         \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                   \
+      bg[S][q] = cat8(ld16(wb + og[q] + ko), ld16(wb + og[q] + ko + 64));             \
+      bu[S][q] = cat8(ld16(wb + ou[q] + ko), ld16(wb + ou[q] + ko + 64));             \
+      sg[S][q] = wsb[osg[q] + so];                                                    \
+      su[S][q] = wsb[osu[q] + so];                                                    \
+    }                                                                                 \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                   \
+      bx[S][g] = cat8(ld16(x + ox[g] + ko), ld16(x + ox[g] + ko + 64));               \
+      sx[S][g] = xs[osx[g] + so];                                                     \
+    }                                                                                 \
   }
+  const int chunks = H / 128;
+#define GUM_MMA(S)                                                                      \
+  _Pragma("unroll") for (int q = 0; q < 2; ++q)                                         \
+  _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                       \
+    ag[q][g] = mfma_mx16x16x128(bg[S][q], bx[S][g], sg[S][q], sx[S][g], ag[q][g]);      \
+    au[q][g] = mfma_mx16x16x128(bu[S][q], bx[S][g], su[S][q], sx[S][g], au[q][g]);      \
+  }
+  GUM_LOAD(0, 0)
+  const int kpairs = chunks & ~1;
+  for (int kc = 0; kc < kpairs; kc += 2) {
+    GUM_LOAD(1, kc + 1)
+    GUM_MMA(0)
+    GUM_LOAD(0, min(kc + 2, chunks - 1))
+    GUM_MMA(1)
+  }
+  if (chunks & 1) { GUM_MMA(0) }
+#undef GUM_MMA
+#undef GUM_LOAD
   // SwiGLU, then MX-quantize the 32 neurons [nb, nb+32) of each row: lanes
   // col + 16*grp (grp = 0..3) hold them (4 per q group each).
 #pragma unroll
@@ -464,17 +485,17 @@ __global__ __launch_bounds__(256) void gemm_gate_up_mx(
     uint8_t* hr = h + static_cast<size_t>(rbase + r) * I + nb + 4 * grp;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      uint32_t w = 0;
+      uint32_t wq = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w |= f32_to_e4m3(a[q][i] * inv) << (8 * i);
-      *reinterpret_cast<uint32_t*>(hr + 16 * q) = w;
+      for (int i = 0; i < 4; ++i) wq |= f32_to_e4m3(a[q][i] * inv) << (8 * i);
+      *reinterpret_cast<uint32_t*>(hr + 16 * q) = wq;
     }
     if (grp == 0) hs[static_cast<size_t>(rbase + r) * (I / 32) + nb / 32] = static_cast<uint8_t>(sexp + 127);
   }
 }
 
 // down, MXFP8: as the BF16 down kernel with 128-wide scaled K chunks.
-template <bool FUSED>
+template <bool FUSED, int D>
 __global__ __launch_bounds__(256) void gemm_down_mx(
     const uint8_t* __restrict__ h, const uint8_t* __restrict__ hs,
     const uint8_t* __restrict__ wd, const uint8_t* __restrict__ wds,
@@ -493,21 +514,23 @@ __global__ __launch_bounds__(256) void gemm_down_mx(
   const int db = db_i * kDnRows + wv * 64;
   const int KB = I / 32;
 
-  const uint8_t* hr[4];
-  const uint8_t* hsr[4];
+  const uint8_t* __restrict__ wb = wd + static_cast<size_t>(e) * H * I;
+  const uint8_t* __restrict__ wsb = wds + static_cast<size_t>(e) * H * KB;
+  const uint8_t* __restrict__ hb = h + static_cast<size_t>(rbase) * I;
+  const uint8_t* __restrict__ hsb = hs + static_cast<size_t>(rbase) * KB;
+  uint32_t ow[4], osw[4], oh[4], osh[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = db + 16 * q + col;
+    ow[q] = static_cast<uint32_t>(row * I + 16 * grp);
+    osw[q] = static_cast<uint32_t>(row * KB + grp);
+  }
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
-    hr[g] = r < mcount ? h + static_cast<size_t>(rbase + r) * I + 16 * grp : nullptr;
-    hsr[g] = r < mcount ? hs + static_cast<size_t>(rbase + r) * KB + grp : nullptr;
-  }
-  const uint8_t* wr[4];
-  const uint8_t* wsr[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const size_t row = static_cast<size_t>(e) * H + db + 16 * q + col;
-    wr[q] = wd + row * I + 16 * grp;
-    wsr[q] = wds + row * KB + grp;
+    const int rr = r < mcount ? r : 0;
+    oh[g] = static_cast<uint32_t>(rr * I + 16 * grp);
+    osh[g] = static_cast<uint32_t>(rr * KB + grp);
   }
   f32x4 acc[4][4];
 #pragma unroll
@@ -515,31 +538,36 @@ __global__ __launch_bounds__(256) void gemm_down_mx(
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int chunks = I / 128;
-  for (int kc = 0; kc < chunks; ++kc) {
-    const int ko = kc * 128, so = kc * 4;
-    i32x8 a[4], b[4];
-    int sa[4], sb[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      a[q] = cat8(ld16(wr[q] + ko), ld16(wr[q] + ko + 64));
-      sa[q] = wsr[q][so];
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (hr[g]) {
-        b[g] = cat8(ld16(hr[g] + ko), ld16(hr[g] + ko + 64));
-        sb[g] = hsr[g][so];
-      } else {
-        b[g] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        sb[g] = 127;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) acc[q][g] = mfma_mx16x16x128(a[q], b[g], sa[q], sb[g], acc[q][g]);
+  i32x8 ba[D][4], bb[D][4];
+  int sa[D][4], sb[D][4];
+#define DNM_LOAD(S, KC)                                                               \
+  {                                                                                   \
+    const int ko = (KC) * 128, so = (KC) * 4;                                         \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                   \
+      ba[S][q] = cat8(ld16(wb + ow[q] + ko), ld16(wb + ow[q] + ko + 64));             \
+      sa[S][q] = wsb[osw[q] + so];                                                    \
+    }                                                                                 \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                   \
+      bb[S][g] = cat8(ld16(hb + oh[g] + ko), ld16(hb + oh[g] + ko + 64));             \
+      sb[S][g] = hsb[osh[g] + so];                                                    \
+    }                                                                                 \
   }
+  const int chunks = I / 128;
+#define DNM_MMA(S)                                                                       \
+  _Pragma("unroll") for (int q = 0; q < 4; ++q)                                          \
+  _Pragma("unroll") for (int g = 0; g < 4; ++g)                                          \
+    acc[q][g] = mfma_mx16x16x128(ba[S][q], bb[S][g], sa[S][q], sb[S][g], acc[q][g]);
+  DNM_LOAD(0, 0)
+  const int kpairs = chunks & ~1;
+  for (int kc = 0; kc < kpairs; kc += 2) {
+    DNM_LOAD(1, kc + 1)
+    DNM_MMA(0)
+    DNM_LOAD(0, min(kc + 2, chunks - 1))
+    DNM_MMA(1)
+  }
+  if (chunks & 1) { DNM_MMA(0) }
+#undef DNM_MMA
+#undef DNM_LOAD
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
@@ -600,12 +628,12 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
   const int n_items = round_up((I / kGuNeurons) * L.max_tiles, kXcds);
   prof_begin(kGemmGateUp, s);
   if (dtype == 0)
-    hipLaunchKernelGGL(gemm_gate_up_bf16, dim3(n_items), dim3(256), 0, s,
+    hipLaunchKernelGGL(gemm_gate_up_bf16<kStagesBf16>, dim3(n_items), dim3(256), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, H, I, k, n_items,
                        static_cast<uint16_t*>(h));
   else
-    hipLaunchKernelGGL(gemm_gate_up_mx, dim3(n_items), dim3(256), 0, s,
+    hipLaunchKernelGGL(gemm_gate_up_mx<kStagesMx>, dim3(n_items), dim3(256), 0, s,
                        static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
                        p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, H, I, k, n_items,
                        static_cast<uint8_t*>(h), hs);
@@ -626,19 +654,19 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
     const uint8_t* hc = static_cast<const uint8_t*>(h);
     const uint8_t* wc = static_cast<const uint8_t*>(wd);
     if (k == 1)
-      hipLaunchKernelGGL(gemm_down_mx<true>, dim3(n_items), dim3(256), 0, s, hc, hs, wc, wds,
+      hipLaunchKernelGGL((gemm_down_mx<true, kStagesMx>), dim3(n_items), dim3(256), 0, s, hc, hs, wc, wds,
                          p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, n_items, p.y,
                          out);
     else
-      hipLaunchKernelGGL(gemm_down_mx<false>, dim3(n_items), dim3(256), 0, s, hc, hs, wc, wds,
+      hipLaunchKernelGGL((gemm_down_mx<false, kStagesMx>), dim3(n_items), dim3(256), 0, s, hc, hs, wc, wds,
                          p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, n_items, p.y,
                          out);
   } else if (k == 1)
-    hipLaunchKernelGGL(gemm_down_bf16<true>, dim3(n_items), dim3(256), 0, s,
+    hipLaunchKernelGGL((gemm_down_bf16<true, kStagesBf16>), dim3(n_items), dim3(256), 0, s,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, n_items, p.y, out);
   else
-    hipLaunchKernelGGL(gemm_down_bf16<false>, dim3(n_items), dim3(256), 0, s,
+    hipLaunchKernelGGL((gemm_down_bf16<false, kStagesBf16>), dim3(n_items), dim3(256), 0, s,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, n_items, p.y, out);
   prof_end(kGemmDown, s);

@@ -32,7 +32,6 @@ namespace moe {
 namespace {
 constexpr int kDecWaves = 8;          // waves per workgroup (split of K)
 constexpr int kDecThreads = kDecWaves * kWave;
-constexpr int kDownChunk = 4;         // K-steps per batch in down
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 }  // namespace
@@ -108,10 +107,33 @@ __global__ __launch_bounds__(1024) void decode_route_plan(
   }
 }
 
-// gate_up: work item = (touched expert u, block of 16 neurons).  Workgroups
-// stride over items.  Wave wv covers K range [wv*H/8, (wv+1)*H/8).
-// TM = token tiles of 16 the batch needs (1, 2 or 4); KC = K-steps whose
-// weights are loaded per batch.
+// Position of the n-th set bit of m (n < popcount(m)), by halving.
+__device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
+  int pos = 0;
+  int c = __popcll(m & 0xFFFFFFFFull);
+  if (n >= c) { n -= c; m >>= 32; pos += 32; }
+  c = __popc(static_cast<uint32_t>(m) & 0xFFFFu);
+  if (n >= c) { n -= c; m >>= 16; pos += 16; }
+  c = __popc(static_cast<uint32_t>(m) & 0xFFu);
+  if (n >= c) { n -= c; m >>= 8; pos += 8; }
+  c = __popc(static_cast<uint32_t>(m) & 0xFu);
+  if (n >= c) { n -= c; m >>= 4; pos += 4; }
+  c = __popc(static_cast<uint32_t>(m) & 0x3u);
+  if (n >= c) { n -= c; m >>= 2; pos += 2; }
+  c = static_cast<int>(m & 1u);
+  if (n >= c) pos += 1;
+  return pos;
+}
+
+// Largest plan a workgroup stages in LDS (touched experts <= E <= 1024).
+constexpr int kMaxPlan = 1024;
+
+// gate_up: work item = (touched expert u, block of 16 neurons); workgroups
+// stride over items.  Wave wv covers K range [wv*H/8, (wv+1)*H/8) in chunks
+// of KC steps of 32 (KC divides the steps).  The workgroup walks its flat
+// sequence of (item, chunk) tasks with the weights of the next task loaded
+// into a second register buffer while the current one is multiplied, so the
+// weight stream never waits on an epilogue.
 template <int TM, int KC>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_gate_up(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
@@ -120,102 +142,124 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
     const uint64_t* __restrict__ plan_mask, int H, int I, int k,
     uint16_t* __restrict__ hw_hi, uint16_t* __restrict__ hw_lo) {
   extern __shared__ float red[];                    // [8 waves][TM][gate/up][4][64]
-  __shared__ int tok_list[64];
+  __shared__ int s_e[kMaxPlan];
+  __shared__ uint64_t s_m[kMaxPlan];
   const int U = *plan_u;
+  for (int i = threadIdx.x; i < U; i += blockDim.x) {
+    s_e[i] = plan_e[i];
+    s_m[i] = plan_mask[i];
+  }
+  __syncthreads();
   const int nrb = I / 16;
   const int items = U * nrb;
   const int wv = wave_id(), ln = lane_id();
   const int col = ln & 15, grp = ln >> 4;
   const int kw = H / kDecWaves;
-  const int ksteps = kw / 32;
-  const size_t kb = static_cast<size_t>(wv) * kw + grp * 8;
-  const bf16x8 zero8 = {};
+  const int nch = kw / 32 / KC;                     // chunks per item
+  const int my_items = blockIdx.x < items ? (items - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int ntask = my_items * nch;
+  const uint32_t kb = static_cast<uint32_t>(wv * kw + grp * 8);
 
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+  // weight row offset (elements) of task t's gate row for this lane
+  auto task_w = [&](int t) -> const uint16_t* {
+    const int j = t / nch, c = t - j * nch;
+    const int item = blockIdx.x + j * gridDim.x;
     const int u = item / nrb, rb = item - u * nrb;
-    const int e = plan_e[u];
-    const uint64_t mask = plan_mask[u];
-    const int ntok = __popcll(mask);
-    const int tiles = (ntok + 15) >> 4;
-    if (wv == 0 && ((mask >> ln) & 1ull)) tok_list[__popcll(mask & ((1ull << ln) - 1))] = ln;
-    __syncthreads();
-    int tok[TM];
-#pragma unroll
-    for (int c = 0; c < TM; ++c) {
-      const int p = 16 * c + col;
-      tok[c] = p < ntok ? tok_list[p] : -1;
-    }
-    const uint16_t* pg = wgu + (static_cast<size_t>(e) * 2 * I + rb * 16 + col) * H + kb;
-    const uint16_t* pu = pg + static_cast<size_t>(I) * H;
-    f32x4 ag[TM], au[TM];
-#pragma unroll
-    for (int c = 0; c < TM; ++c) ag[c] = au[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    return wgu + (static_cast<size_t>(s_e[u]) * 2 * I + rb * 16 + col) * H + kb + c * KC * 32;
+  };
+  bf16x8 gA[KC], uA[KC], gB[KC], uB[KC];
+  const size_t up_off = static_cast<size_t>(I) * H;
+#define GU_ISSUE(G, UU, T)                                             \
+  {                                                                    \
+    const uint16_t* pg_ = task_w(T);                                   \
+    _Pragma("unroll") for (int s = 0; s < KC; ++s) {                   \
+      G[s] = as_bf16x8(ld16(pg_ + s * 32));                            \
+      UU[s] = as_bf16x8(ld16(pg_ + up_off + s * 32));                  \
+    }                                                                  \
+  }
+  f32x4 ag[TM], au[TM];
+  int tok[TM];
+  int ntok = 0, tiles = 0;
 
-    for (int s0 = 0; s0 < ksteps; s0 += KC) {
-      bf16x8 wg[KC], wu[KC];
+  auto run_task = [&](const bf16x8 (&G)[KC], const bf16x8 (&UU)[KC], int t) {
+    const int j = t / nch, c = t - j * nch;
+    const int item = blockIdx.x + j * gridDim.x;
+    const int u = item / nrb, rb = item - u * nrb;
+    const int e = s_e[u];
+    const uint64_t mask = s_m[u];
+    if (c == 0) {
+      ntok = __popcll(mask);
+      tiles = (ntok + 15) >> 4;
 #pragma unroll
-      for (int s = 0; s < KC; ++s) {
-        if (s0 + s < ksteps) {
-          wg[s] = as_bf16x8(ld16(pg + (s0 + s) * 32));
-          wu[s] = as_bf16x8(ld16(pu + (s0 + s) * 32));
-        }
+      for (int q = 0; q < TM; ++q) {
+        const int p = 16 * q + col;
+        tok[q] = nth_set_bit(mask, p < ntok ? p : 0);   // past the end: a valid token, column discarded
+        ag[q] = au[q] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    }
+    const uint32_t ko = kb + c * KC * 32;
 #pragma unroll
-      for (int c = 0; c < TM; ++c) {
-        if (c < tiles) {
-          bf16x8 xb[KC];
+    for (int q = 0; q < TM; ++q) {
+      if (q < tiles) {
+        bf16x8 xb[KC];
 #pragma unroll
-          for (int s = 0; s < KC; ++s)
-            xb[s] = (tok[c] >= 0 && s0 + s < ksteps)
-                        ? as_bf16x8(ld16(x + static_cast<size_t>(tok[c]) * H + kb + (s0 + s) * 32))
-                        : zero8;
+        for (int s = 0; s < KC; ++s) xb[s] = as_bf16x8(ld16(x + static_cast<size_t>(tok[q]) * H + ko + s * 32));
 #pragma unroll
-          for (int s = 0; s < KC; ++s) {
-            if (s0 + s < ksteps) {
-              ag[c] = mfma16x16x32(wg[s], xb[s], ag[c]);
-              au[c] = mfma16x16x32(wu[s], xb[s], au[c]);
-            }
-          }
+        for (int s = 0; s < KC; ++s) {
+          ag[q] = mfma16x16x32(G[s], xb[s], ag[q]);
+          au[q] = mfma16x16x32(UU[s], xb[s], au[q]);
         }
       }
     }
+    if (c != nch - 1) return;
+    // epilogue of the item: fixed-order sum over waves, SwiGLU, weight, split, store
 #pragma unroll
-    for (int c = 0; c < TM; ++c) {
-      if (c < tiles) {
+    for (int q = 0; q < TM; ++q) {
+      if (q < tiles) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          red[(((wv * TM + c) * 2 + 0) * 4 + r) * 64 + ln] = ag[c][r];
-          red[(((wv * TM + c) * 2 + 1) * 4 + r) * 64 + ln] = au[c][r];
+          red[(((wv * TM + q) * 2 + 0) * 4 + r) * 64 + ln] = ag[q][r];
+          red[(((wv * TM + q) * 2 + 1) * 4 + r) * 64 + ln] = au[q][r];
         }
       }
     }
     __syncthreads();
-    // Fixed-order sum over waves, SwiGLU, weight, split, store.
-    for (int q = threadIdx.x; q < tiles * 256; q += blockDim.x) {
-      const int c = q >> 8, within = q & 255;
+    for (int qq = threadIdx.x; qq < tiles * 256; qq += blockDim.x) {
+      const int q = qq >> 8, within = qq & 255;
       const int n = within >> 4, m = within & 15;    // token column n, weight row m
       const int src = 16 * (m >> 2) + n, r = m & 3;
       float g = 0.f, up = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < kDecWaves; ++w2) {
-        g += red[(((w2 * TM + c) * 2 + 0) * 4 + r) * 64 + src];
-        up += red[(((w2 * TM + c) * 2 + 1) * 4 + r) * 64 + src];
+        g += red[(((w2 * TM + q) * 2 + 0) * 4 + r) * 64 + src];
+        up += red[(((w2 * TM + q) * 2 + 1) * 4 + r) * 64 + src];
       }
-      const int p = c * 16 + n;
+      const int p = q * 16 + n;
       if (p < ntok) {
-        const int t = tok_list[p];
-        int j = 0;
-        while (j < k - 1 && idx[t * k + j] != e) ++j;
-        const float hv = wts[t * k + j] * swiglu(g, up);
+        const int tt = nth_set_bit(mask, p);
+        int js = 0;
+        while (js < k - 1 && idx[tt * k + js] != e) ++js;
+        const float hv = wts[tt * k + js] * swiglu(g, up);
         const uint32_t hi = f32_to_bf16_rne(hv);
         const uint32_t lo = f32_to_bf16_rne(hv - bf16_to_f32(hi));
-        const size_t o = static_cast<size_t>(t * k + j) * I + rb * 16 + m;
+        const size_t o = static_cast<size_t>(tt * k + js) * I + rb * 16 + m;
         hw_hi[o] = static_cast<uint16_t>(hi);
         hw_lo[o] = static_cast<uint16_t>(lo);
       }
     }
     __syncthreads();
+  };
+
+  if (ntask > 0) GU_ISSUE(gA, uA, 0)
+  for (int t = 0; t < ntask; t += 2) {
+    if (t + 1 < ntask) GU_ISSUE(gB, uB, t + 1)
+    run_task(gA, uA, t);
+    if (t + 1 < ntask) {
+      if (t + 2 < ntask) GU_ISSUE(gA, uA, t + 2)
+      run_task(gB, uB, t + 1);
+    }
   }
+#undef GU_ISSUE
 }
 
 // down: workgroup = 8 output dimensions d0..d0+7 of every touched expert (H/8
@@ -223,47 +267,12 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
 // across workgroups).  MFMA rows 0..7 carry those dimensions; lanes of rows
 // 8..15 issue no loads (the MFMA work they waste is free: the kernel is bound
 // by HBM).  Wave wv covers K range [wv*I/8, (wv+1)*I/8) of each touched expert
-// in ascending expert order, loading the weights of UE experts ahead of their
-// MFMAs; the eight wave partials are then added in LDS in wave order.
+// in ascending expert order, as a flat sequence of (expert, chunk of KD
+// steps) tasks whose weights are double-buffered in registers; the eight wave
+// partials are then added in LDS in wave order.
 constexpr int kDownRows = 8;
 
-template <int TM>
-__device__ __forceinline__ void down_expert(const bf16x8 (&a)[kDownChunk], int s0, int ksteps,
-                                            int e, uint64_t mask, int k, int col,
-                                            const int* s_idx, size_t kb, int I,
-                                            const uint16_t* __restrict__ hw_hi,
-                                            const uint16_t* __restrict__ hw_lo, f32x4 (&acc)[TM]) {
-  const bf16x8 zero8 = {};
-#pragma unroll
-  for (int c = 0; c < TM; ++c) {
-    const uint32_t bits = static_cast<uint32_t>(mask >> (16 * c)) & 0xFFFFu;
-    if (bits == 0) continue;
-    const int t = 16 * c + col;
-    const bool routed = (bits >> col) & 1u;
-    size_t row = 0;
-    if (routed) {
-      int j = 0;
-      while (j < k - 1 && s_idx[t * k + j] != e) ++j;
-      row = static_cast<size_t>(t * k + j) * I + kb;
-    }
-    bf16x8 bh[kDownChunk], bl[kDownChunk];
-#pragma unroll
-    for (int s = 0; s < kDownChunk; ++s) {
-      const bool ok = routed && s0 + s < ksteps;
-      bh[s] = ok ? as_bf16x8(ld16(hw_hi + row + (s0 + s) * 32)) : zero8;
-      bl[s] = ok ? as_bf16x8(ld16(hw_lo + row + (s0 + s) * 32)) : zero8;
-    }
-#pragma unroll
-    for (int s = 0; s < kDownChunk; ++s) {
-      if (s0 + s < ksteps) {
-        acc[c] = mfma16x16x32(a[s], bh[s], acc[c]);
-        acc[c] = mfma16x16x32(a[s], bl[s], acc[c]);
-      }
-    }
-  }
-}
-
-template <int TM, int UE>
+template <int TM, int KD>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_down(
     const uint16_t* __restrict__ wd, const int32_t* __restrict__ idx,
     const int* __restrict__ plan_u, const int32_t* __restrict__ plan_e,
@@ -271,46 +280,75 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
     const uint16_t* __restrict__ hw_lo, int T, int H, int I, int k, uint16_t* __restrict__ out) {
   extern __shared__ float red[];                    // [8 waves][TM][4][64]
   __shared__ int s_idx[64 * 32];
-  for (int i = threadIdx.x; i < T * k; i += blockDim.x) s_idx[i] = idx[i];
-  __syncthreads();
+  __shared__ int s_e[kMaxPlan];
+  __shared__ uint64_t s_m[kMaxPlan];
   const int U = *plan_u;
+  for (int i = threadIdx.x; i < T * k; i += blockDim.x) s_idx[i] = idx[i];
+  for (int i = threadIdx.x; i < U; i += blockDim.x) {
+    s_e[i] = plan_e[i];
+    s_m[i] = plan_mask[i];
+  }
+  __syncthreads();
   const int wv = wave_id(), ln = lane_id();
   const int col = ln & 15, grp = ln >> 4;
   const bool row_lane = col < kDownRows;
   const int d0 = blockIdx.x * kDownRows;
   const int kw = I / kDecWaves;
-  const int ksteps = kw / 32;
-  const size_t kb = static_cast<size_t>(wv) * kw + grp * 8;
+  const int nch = kw / 32 / KD;
+  const int ntask = U * nch;
+  const uint32_t kb = static_cast<uint32_t>(wv * kw + grp * 8);
   const uint16_t* pw = wd + (static_cast<size_t>(d0) + (row_lane ? col : 0)) * I + kb;
   const bf16x8 zero8 = {};
   f32x4 acc[TM];
 #pragma unroll
   for (int c = 0; c < TM; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int ub = 0; ub < U; ub += UE) {
-    int e[UE];
-    uint64_t m[UE];
+  bf16x8 aA[KD], aB[KD];
+#define DN_ISSUE(A, T)                                                                   \
+  {                                                                                      \
+    const int u_ = (T) / nch, c_ = (T) - u_ * nch;                                      \
+    const uint16_t* p_ = pw + static_cast<size_t>(s_e[u_]) * H * I + c_ * KD * 32;      \
+    _Pragma("unroll") for (int s = 0; s < KD; ++s)                                       \
+      A[s] = row_lane ? as_bf16x8(ld16(p_ + s * 32)) : zero8;                            \
+  }
+  auto run_task = [&](const bf16x8 (&A)[KD], int t) {
+    const int u = t / nch, c = t - u * nch;
+    const int e = s_e[u];
+    const uint64_t mask = s_m[u];
+    const uint32_t ko = kb + c * KD * 32;
 #pragma unroll
-    for (int q = 0; q < UE; ++q) {
-      const bool have = ub + q < U;
-      e[q] = have ? plan_e[ub + q] : 0;
-      m[q] = have ? plan_mask[ub + q] : 0ull;
+    for (int q = 0; q < TM; ++q) {
+      const uint32_t bits = static_cast<uint32_t>(mask >> (16 * q)) & 0xFFFFu;
+      if (bits == 0) continue;
+      const int tk = 16 * q + col;
+      const bool routed = (bits >> col) & 1u;
+      int js = 0;
+      if (routed)
+        while (js < k - 1 && s_idx[tk * k + js] != e) ++js;
+      const size_t row = static_cast<size_t>((routed ? tk : 0) * k + js) * I + ko;
+      bf16x8 bh[KD], bl[KD];
+#pragma unroll
+      for (int s = 0; s < KD; ++s) {
+        bh[s] = routed ? as_bf16x8(ld16(hw_hi + row + s * 32)) : zero8;
+        bl[s] = routed ? as_bf16x8(ld16(hw_lo + row + s * 32)) : zero8;
+      }
+#pragma unroll
+      for (int s = 0; s < KD; ++s) {
+        acc[q] = mfma16x16x32(A[s], bh[s], acc[q]);
+        acc[q] = mfma16x16x32(A[s], bl[s], acc[q]);
+      }
     }
-    for (int s0 = 0; s0 < ksteps; s0 += kDownChunk) {
-      bf16x8 a[UE][kDownChunk];
-#pragma unroll
-      for (int q = 0; q < UE; ++q)
-#pragma unroll
-        for (int s = 0; s < kDownChunk; ++s)
-          a[q][s] = (m[q] != 0 && row_lane && s0 + s < ksteps)
-                        ? as_bf16x8(ld16(pw + static_cast<size_t>(e[q]) * H * I + (s0 + s) * 32))
-                        : zero8;
-#pragma unroll
-      for (int q = 0; q < UE; ++q)
-        if (m[q] != 0)
-          down_expert<TM>(a[q], s0, ksteps, e[q], m[q], k, col, s_idx, kb, I, hw_hi, hw_lo, acc);
+  };
+  if (ntask > 0) DN_ISSUE(aA, 0)
+  for (int t = 0; t < ntask; t += 2) {
+    if (t + 1 < ntask) DN_ISSUE(aB, t + 1)
+    run_task(aA, t);
+    if (t + 1 < ntask) {
+      if (t + 2 < ntask) DN_ISSUE(aA, t + 2)
+      run_task(aB, t + 1);
     }
   }
+#undef DN_ISSUE
   // D rows 0..7 live in lanes with grp < 2
 #pragma unroll
   for (int c = 0; c < TM; ++c)
@@ -355,37 +393,55 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   const int grid1 = static_cast<int>(items_upper < grid_cap ? items_upper : grid_cap);
   const size_t lds_gu = sizeof(float) * kDecWaves * TM * 2 * 256;
   const size_t lds_dn = sizeof(float) * kDecWaves * TM * 256;
+  const int gsteps = H / kDecWaves / 32, dsteps = I / kDecWaves / 32;
+  int KC = gsteps % 4 == 0 ? 4 : (gsteps % 3 == 0 ? 3 : (gsteps % 2 == 0 ? 2 : 1));
+  if (TM == 4 && KC == 4) KC = 2;                   // keeps four token tiles within 128 VGPRs
+  const int KD = dsteps % 4 == 0 ? 4 : (dsteps % 3 == 0 ? 3 : (dsteps % 2 == 0 ? 2 : 1));
   const dim3 grid2(H / kDownRows);
   prof_begin(kDecGateUp, s);
-  if (TM == 1)
-    hipLaunchKernelGGL((decode_gate_up<1, 8>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x, wgu,
-                       idx_p, w_p, plan_u, plan_e, plan_mask, H, I, k, hw_hi, hw_lo);
-  else if (TM == 2)
-    hipLaunchKernelGGL((decode_gate_up<2, 4>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x, wgu,
-                       idx_p, w_p, plan_u, plan_e, plan_mask, H, I, k, hw_hi, hw_lo);
-  else
-    hipLaunchKernelGGL((decode_gate_up<4, 4>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x, wgu,
-                       idx_p, w_p, plan_u, plan_e, plan_mask, H, I, k, hw_hi, hw_lo);
+#define GU_LAUNCH(TMV, KCV)                                                                    \
+  hipLaunchKernelGGL((decode_gate_up<TMV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x,   \
+                     wgu, idx_p, w_p, plan_u, plan_e, plan_mask, H, I, k, hw_hi, hw_lo)
+#define GU_KC(TMV)                                        \
+  switch (KC) {                                           \
+    case 4: GU_LAUNCH(TMV, 4); break;                     \
+    case 3: GU_LAUNCH(TMV, 3); break;                     \
+    case 2: GU_LAUNCH(TMV, 2); break;                     \
+    default: GU_LAUNCH(TMV, 1); break;                    \
+  }
+  if (TM == 1) { GU_KC(1) } else if (TM == 2) { GU_KC(2) } else { GU_KC(4) }
+#undef GU_KC
+#undef GU_LAUNCH
   prof_end(kDecGateUp, s);
   prof_begin(kDecDown, s);
-  if (TM == 1)
-    hipLaunchKernelGGL((decode_down<1, 4>), grid2, dim3(kDecThreads), lds_dn, s, wd, idx_p, plan_u,
-                       plan_e, plan_mask, hw_hi, hw_lo, T, H, I, k, out);
-  else if (TM == 2)
-    hipLaunchKernelGGL((decode_down<2, 2>), grid2, dim3(kDecThreads), lds_dn, s, wd, idx_p, plan_u,
-                       plan_e, plan_mask, hw_hi, hw_lo, T, H, I, k, out);
-  else
-    hipLaunchKernelGGL((decode_down<4, 1>), grid2, dim3(kDecThreads), lds_dn, s, wd, idx_p, plan_u,
-                       plan_e, plan_mask, hw_hi, hw_lo, T, H, I, k, out);
+#define DN_LAUNCH(TMV, KDV)                                                                    \
+  hipLaunchKernelGGL((decode_down<TMV, KDV>), grid2, dim3(kDecThreads), lds_dn, s, wd, idx_p,    \
+                     plan_u, plan_e, plan_mask, hw_hi, hw_lo, T, H, I, k, out)
+#define DN_KD(TMV)                                        \
+  switch (KD) {                                           \
+    case 4: DN_LAUNCH(TMV, 4); break;                     \
+    case 3: DN_LAUNCH(TMV, 3); break;                     \
+    case 2: DN_LAUNCH(TMV, 2); break;                     \
+    default: DN_LAUNCH(TMV, 1); break;                    \
+  }
+  if (TM == 1) { DN_KD(1) } else if (TM == 2) { DN_KD(2) } else { DN_KD(4) }
+#undef DN_KD
+#undef DN_LAUNCH
   prof_end(kDecDown, s);
   return hipGetLastError();
 }
 
 hipError_t decode_set_attributes() {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_gate_up<4, 4>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     sizeof(float) * kDecWaves * 4 * 2 * 256 + 1024);
-  if (e != hipSuccess) return e;
+  const void* tm4[] = {reinterpret_cast<const void*>(decode_gate_up<4, 1>),
+                       reinterpret_cast<const void*>(decode_gate_up<4, 2>),
+                       reinterpret_cast<const void*>(decode_gate_up<4, 3>),
+                       reinterpret_cast<const void*>(decode_gate_up<4, 4>)};
+  hipError_t e = hipSuccess;
+  for (const void* f : tm4) {
+    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            sizeof(float) * kDecWaves * 4 * 2 * 256);
+    if (e != hipSuccess) return e;
+  }
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_route_plan),
                           hipFuncAttributeMaxDynamicSharedMemorySize,
                           sizeof(uint64_t) * 1024 + sizeof(int) * 16);
