@@ -45,6 +45,9 @@ def parse():
                    help="approximate CPU time for the oracle baseline (0 = skip)")
     p.add_argument("--extra", action="store_true",
                    help="also time decode at T=1 and T=8 (reported under 'extra')")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB three times (the "
+                        "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -237,6 +240,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+        return
     cfg = W.get(args.workload)
     log(f"device {torch.cuda.get_device_name(0)}; workload {cfg.name}")
     if cfg.path == "decode":

@@ -91,8 +91,8 @@ int moe_route_topk(const float* logits, int T, int E, int k,
  *   topk_w      [T, k] float32 out, may be NULL
  *   workspace   >= moe_decode_workspace_bytes(T, H, I, E, k) bytes of device
  *               memory, contents ignored on entry and overwritten
- * Limits: 1 <= T <= 64 (larger T: MOE_ERR_UNSUPPORTED, use the batched calls),
- * H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024.
+ * Limits: 1 <= T <= 64 and I <= 2048 (otherwise MOE_ERR_UNSUPPORTED: use the
+ * batched calls), H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024.
  * Only the weights of experts that some token routes to are read.
  */
 int moe_decode_forward(const uint16_t* x, const float* logits,
@@ -140,8 +140,7 @@ int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int K,
  *              writes the expert grouping into it, and moe_down_3d_batched
  *              must be given the same workspace and topk_idx, later on the
  *              same stream
- * Limits: T >= 1, H a multiple of 256, I a multiple of 128, 1 <= k <= min(E, 32),
- * E <= 1024.
+ * Limits: T >= 1, H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024.
  */
 int moe_gate_up_3d_batched(const void* x, const uint8_t* x_scales,
                            const void* w_gate_up, const uint8_t* w_gate_up_scales,

@@ -143,6 +143,7 @@ int moe_decode_forward(const uint16_t* x, const float* logits, const uint16_t* w
   if (int st = check_common(T, H, I, E, k, 256, 256)) return st;
   if (T == 0) return fail(MOE_ERR_SHAPE, "T=0: nothing to decode");
   if (T > 64) return fail(MOE_ERR_UNSUPPORTED, "T=%d > 64: use the batched calls", T);
+  if (I > 2048) return fail(MOE_ERR_UNSUPPORTED, "I=%d > 2048: use the batched calls", I);
   if (!x || !logits || !w_gate_up || !w_down || !out)
     return fail(MOE_ERR_NULL, "x, logits, w_gate_up, w_down and out are required");
   if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
@@ -183,7 +184,7 @@ int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
 
 static int check_batched(int T, int H, int I, int E, int k, int dtype, const void* ws,
                          size_t ws_bytes) {
-  if (int st = check_common(T, H, I, E, k, 256, 128)) return st;
+  if (int st = check_common(T, H, I, E, k, 256, 256)) return st;
   if (T < 1) return fail(MOE_ERR_SHAPE, "T=%d < 1", T);
   if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return fail(MOE_ERR_SHAPE, "dtype=%d", dtype);
   if (static_cast<long long>(T) * k > (1LL << 30)) return fail(MOE_ERR_SHAPE, "T*k too large");

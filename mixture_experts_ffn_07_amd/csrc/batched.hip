@@ -29,11 +29,7 @@ namespace moe {
 
 namespace {
 constexpr int kBM = 64;            // rows (routed pairs) per M-tile
-constexpr int kGuNeurons = 128;    // neurons per gate_up workgroup (4 waves x 32)
-constexpr int kDnRows = 256;       // output dims per down workgroup (4 waves x 64)
 constexpr int kXcds = 8;
-constexpr int kStagesBf16 = 2;   // register pipeline depth of the BF16 GEMMs
-constexpr int kStagesMx = 2;     // and of the MXFP8 GEMMs
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 }  // namespace
@@ -145,75 +141,136 @@ __device__ __forceinline__ int xcd_item(int L, int n_items) {
   return (L % kXcds) * (n_items / kXcds) + L / kXcds;
 }
 
-// gate_up, BF16: workgroup = (M-tile, 128 neurons); wave = 32 neurons (16
+// The grid is sized for the most M-tiles any routing can produce; the real
+// count is known on the device only.  Workgroups past the real items exit,
+// and the XCD remap runs over the real item space so every XCD gets an equal
+// share.  Returns -1 for a workgroup with nothing to do.
+__device__ __forceinline__ int real_item(int L, int nblk, int n_tiles) {
+  const int n_real = (nblk * n_tiles + kXcds - 1) / kXcds * kXcds;
+  if (L >= n_real) return -1;
+  const int item = xcd_item(L, n_real);
+  return item / nblk < n_tiles ? item : -1;
+}
+
+// gate_up, BF16: workgroup = (M-tile, NW*32 neurons); wave = 32 neurons (16
 // gate rows + 16 up rows in two groups) x 64 rows.  MFMA 16x16x32: A = weight
 // rows (lane: row col, K chunk grp), B = activation rows, D[row][token].
-// The K loop is double-buffered in registers: the loads of step ks + 1 are
-// issued before the MFMAs of step ks, so every wave keeps a step of weights
-// in flight while it computes.  Rows past the tile's end load the tile's first row;
-// their MFMA columns are computed and discarded (columns never mix).
-template <int D>
-__global__ __launch_bounds__(256) void gemm_gate_up_bf16(
+// The tile's 64 gathered activation rows are staged in LDS in chunks of 256
+// along K (double-buffered) and shared by all NW waves; each wave streams its
+// own weight rows from HBM into registers, double-buffered one K-step ahead.
+// Rows past the tile's end load the tile's first row; their MFMA columns are
+// computed and discarded (columns never mix).
+constexpr int kXC = 256;                 // K chunk of the staged activations
+constexpr int kXRS = kXC + 8;            // padded LDS row stride (elements)
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_gate_up_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, int H, int I, int k,
-    int n_items, uint16_t* __restrict__ h) {
-  const int nblk = I / kGuNeurons;
-  const int item = xcd_item(blockIdx.x, n_items);
+    uint16_t* __restrict__ h) {
+  __shared__ __align__(16) uint16_t xs[2][kBM * kXRS];
+  constexpr int NT = NW * 64;
+  constexpr int LPT = kBM * (kXC / 8) / NT;           // 16-byte activation loads per thread
+  const int nblk = I / (NW * 32);
+  const int item = real_item(blockIdx.x, nblk, *n_tiles);
+  if (item < 0) return;
   const int tile = item / nblk, nb_i = item - tile * nblk;
-  if (tile >= *n_tiles) return;
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
   const int mcount = min(kBM, counts[e] - m0);
   const int rbase = offsets[e] + m0;
-  const int wv = wave_id(), ln = lane_id(), col = ln & 15, grp = ln >> 4;
-  const int nb = nb_i * kGuNeurons + wv * 32;
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, col = ln & 15, grp = ln >> 4;
+  const int nb = nb_i * NW * 32 + wv * 32;
 
   const uint16_t* __restrict__ wb = wgu + static_cast<size_t>(e) * 2 * I * H;
-  uint32_t og[2], ou[2], ox[4];
+  uint32_t og[2], ou[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     og[q] = static_cast<uint32_t>((nb + 16 * q + col) * H + grp * 8);
     ou[q] = og[q] + static_cast<uint32_t>(I * H);
   }
+  // cooperative activation loader: chunk c = tid + i*NT -> (row c/32, 16-byte column c%32)
+  uint32_t oxl[LPT];
+  int lrow[LPT];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int r = 16 * g + col;
-    ox[g] = static_cast<uint32_t>((perm[rbase + (r < mcount ? r : 0)] / k) * H + grp * 8);
+  for (int i = 0; i < LPT; ++i) {
+    const int c = tid + i * NT, r = c >> 5;
+    lrow[i] = r * kXRS + (c & 31) * 8;
+    oxl[i] = static_cast<uint32_t>((perm[rbase + (r < mcount ? r : 0)] / k) * H + (c & 31) * 8);
   }
+  i32x4 xr[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) xr[i] = ld16(x + oxl[i]);
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xs[0][lrow[i]]) = xr[i];
+
   f32x4 ag[2][4], au[2][4];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int g = 0; g < 4; ++g) ag[q][g] = au[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  bf16x8 bg[D][2], bu[D][2], bx[D][4];
-#define GU_LOAD(S, KO)                                                    \
-  {                                                                       \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                       \
-      bg[S][q] = as_bf16x8(ld16(wb + og[q] + (KO)));                      \
-      bu[S][q] = as_bf16x8(ld16(wb + ou[q] + (KO)));                      \
-    }                                                                     \
-    _Pragma("unroll") for (int g = 0; g < 4; ++g) bx[S][g] = as_bf16x8(ld16(x + ox[g] + (KO))); \
+  bf16x8 wg0[2], wu0[2], wg1[2], wu1[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    wg0[q] = as_bf16x8(ld16(wb + og[q]));
+    wu0[q] = as_bf16x8(ld16(wb + ou[q]));
   }
-  const int ksteps = H / 32;
-#define GU_MMA(S)                                                             \
-  _Pragma("unroll") for (int q = 0; q < 2; ++q)                               \
-  _Pragma("unroll") for (int g = 0; g < 4; ++g) {                             \
-    ag[q][g] = mfma16x16x32(bg[S][q], bx[S][g], ag[q][g]);                    \
-    au[q][g] = mfma16x16x32(bu[S][q], bx[S][g], au[q][g]);                    \
+  __syncthreads();
+  const int nchunk = H / kXC;
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nchunk;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) xr[i] = ld16(x + oxl[i] + (c + 1) * kXC);
+    }
+    const uint16_t* xb = &xs[buf][(col) * kXRS + grp * 8];
+#pragma unroll
+    for (int s = 0; s < kXC / 32; s += 2) {
+      const int k0 = c * kXC + s * 32;
+      const int k1 = k0 + 32, k2 = min(k0 + 64, H - 32);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        wg1[q] = as_bf16x8(ld16(wb + og[q] + k1));
+        wu1[q] = as_bf16x8(ld16(wb + ou[q] + k1));
+      }
+      {
+        bf16x8 bx[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bx[g] = as_bf16x8(*reinterpret_cast<const i32x4*>(xb + 16 * g * kXRS + s * 32));
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            ag[q][g] = mfma16x16x32(wg0[q], bx[g], ag[q][g]);
+            au[q][g] = mfma16x16x32(wu0[q], bx[g], au[q][g]);
+          }
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        wg0[q] = as_bf16x8(ld16(wb + og[q] + k2));
+        wu0[q] = as_bf16x8(ld16(wb + ou[q] + k2));
+      }
+      {
+        bf16x8 bx[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bx[g] = as_bf16x8(*reinterpret_cast<const i32x4*>(xb + 16 * g * kXRS + (s + 1) * 32));
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            ag[q][g] = mfma16x16x32(wg1[q], bx[g], ag[q][g]);
+            au[q][g] = mfma16x16x32(wu1[q], bx[g], au[q][g]);
+          }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xs[buf ^ 1][lrow[i]]) = xr[i];
+    }
+    __syncthreads();
   }
-  GU_LOAD(0, 0)
-  const int kpairs = ksteps & ~1;
-  for (int ks = 0; ks < kpairs; ks += 2) {
-    GU_LOAD(1, (ks + 1) * 32)
-    GU_MMA(0)
-    GU_LOAD(0, min(ks + 2, ksteps - 1) * 32)
-    GU_MMA(1)
-  }
-  if (ksteps & 1) { GU_MMA(0) }
-#undef GU_MMA
-#undef GU_LOAD
   // SwiGLU epilogue: lane holds neurons nb+16q+4grp+{0..3} of row 16g+col
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -233,64 +290,100 @@ __global__ __launch_bounds__(256) void gemm_gate_up_bf16(
   }
 }
 
-// down, BF16: workgroup = (M-tile, 256 output dims); wave = 64 dims (4 groups)
-// x 64 rows; the same double-buffered K loop.  FUSED (k = 1): out[t] = bf16(w[t] * y)
-// with t = perm[row].
-template <bool FUSED, int D>
-__global__ __launch_bounds__(256) void gemm_down_bf16(
+// down, BF16: workgroup = (M-tile, NW*64 output dims); wave = 64 dims (4
+// groups) x 64 rows.  The tile's 64 activation rows (contiguous in h) are
+// staged in LDS as in gate_up.  FUSED (k = 1): out[t] = bf16(w[t] * y) with
+// t = perm[row].
+template <bool FUSED, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_down_bf16(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ wd,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
-    int H, int I, int n_items, float* __restrict__ y, uint16_t* __restrict__ out) {
-  const int nblk = H / kDnRows;
-  const int item = xcd_item(blockIdx.x, n_items);
+    int H, int I, float* __restrict__ y, uint16_t* __restrict__ out) {
+  __shared__ __align__(16) uint16_t hs_[2][kBM * kXRS];
+  constexpr int NT = NW * 64;
+  constexpr int LPT = kBM * (kXC / 8) / NT;
+  const int nblk = H / (NW * 64);
+  const int item = real_item(blockIdx.x, nblk, *n_tiles);
+  if (item < 0) return;
   const int tile = item / nblk, db_i = item - tile * nblk;
-  if (tile >= *n_tiles) return;
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
   const int mcount = min(kBM, counts[e] - m0);
   const int rbase = offsets[e] + m0;
-  const int wv = wave_id(), ln = lane_id(), col = ln & 15, grp = ln >> 4;
-  const int db = db_i * kDnRows + wv * 64;
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, col = ln & 15, grp = ln >> 4;
+  const int db = db_i * NW * 64 + wv * 64;
 
   const uint16_t* __restrict__ wb = wd + static_cast<size_t>(e) * H * I;
   const uint16_t* __restrict__ hb = h + static_cast<size_t>(rbase) * I;
-  uint32_t ow[4], oh[4];
+  uint32_t ow[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) ow[q] = static_cast<uint32_t>((db + 16 * q + col) * I + grp * 8);
+  uint32_t ohl[LPT];
+  int lrow[LPT];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int r = 16 * g + col;
-    oh[g] = static_cast<uint32_t>((r < mcount ? r : 0) * I + grp * 8);
+  for (int i = 0; i < LPT; ++i) {
+    const int c = tid + i * NT, r = c >> 5;
+    lrow[i] = r * kXRS + (c & 31) * 8;
+    ohl[i] = static_cast<uint32_t>((r < mcount ? r : 0) * I + (c & 31) * 8);
   }
+  i32x4 hr_[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) hr_[i] = ld16(hb + ohl[i]);
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&hs_[0][lrow[i]]) = hr_[i];
+
   f32x4 acc[4][4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  bf16x8 ba[D][4], bb[D][4];
-#define DN_LOAD(S, KO)                                                                   \
-  {                                                                                      \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) ba[S][q] = as_bf16x8(ld16(wb + ow[q] + (KO))); \
-    _Pragma("unroll") for (int g = 0; g < 4; ++g) bb[S][g] = as_bf16x8(ld16(hb + oh[g] + (KO))); \
+  bf16x8 a0[4], a1[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) a0[q] = as_bf16x8(ld16(wb + ow[q]));
+  __syncthreads();
+  const int nchunk = I / kXC;
+  for (int c = 0; c < nchunk; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nchunk;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) hr_[i] = ld16(hb + ohl[i] + (c + 1) * kXC);
+    }
+    const uint16_t* hbuf = &hs_[buf][col * kXRS + grp * 8];
+#pragma unroll
+    for (int s = 0; s < kXC / 32; s += 2) {
+      const int k0 = c * kXC + s * 32;
+      const int k1 = k0 + 32, k2 = min(k0 + 64, I - 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a1[q] = as_bf16x8(ld16(wb + ow[q] + k1));
+      {
+        bf16x8 bb[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bb[g] = as_bf16x8(*reinterpret_cast<const i32x4*>(hbuf + 16 * g * kXRS + s * 32));
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) acc[q][g] = mfma16x16x32(a0[q], bb[g], acc[q][g]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a0[q] = as_bf16x8(ld16(wb + ow[q] + k2));
+      {
+        bf16x8 bb[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bb[g] = as_bf16x8(*reinterpret_cast<const i32x4*>(hbuf + 16 * g * kXRS + (s + 1) * 32));
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) acc[q][g] = mfma16x16x32(a1[q], bb[g], acc[q][g]);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&hs_[buf ^ 1][lrow[i]]) = hr_[i];
+    }
+    __syncthreads();
   }
-  const int ksteps = I / 32;
-#define DN_MMA(S)                                                             \
-  _Pragma("unroll") for (int q = 0; q < 4; ++q)                               \
-  _Pragma("unroll") for (int g = 0; g < 4; ++g)                               \
-    acc[q][g] = mfma16x16x32(ba[S][q], bb[S][g], acc[q][g]);
-  DN_LOAD(0, 0)
-  const int kpairs = ksteps & ~1;
-  for (int ks = 0; ks < kpairs; ks += 2) {
-    DN_LOAD(1, (ks + 1) * 32)
-    DN_MMA(0)
-    DN_LOAD(0, min(ks + 2, ksteps - 1) * 32)
-    DN_MMA(1)
-  }
-  if (ksteps & 1) { DN_MMA(0) }
-#undef DN_MMA
-#undef DN_LOAD
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
@@ -382,32 +475,43 @@ __global__ __launch_bounds__(256) void quant_mx_rows(const uint16_t* __restrict_
   }
 }
 
-// gate_up, MXFP8: workgroup = (M-tile, 128 neurons); wave = 32 neurons (one
-// MX block of h) x 64 rows.  Per 128-wide K chunk a lane loads two 16-byte
-// pieces of its weight row and of its activation row, plus the row's scale
-// byte for block g of the chunk; double-buffered as the BF16 kernel.
-template <int D>
-__global__ __launch_bounds__(256) void gemm_gate_up_mx(
+// gate_up, MXFP8: workgroup = (M-tile, NW*32 neurons); wave = 32 neurons
+// (one MX block of h) x 64 rows.  The activation codes and scale bytes of
+// the tile are staged in LDS in stages of 256 along K (two 128-wide scaled
+// MFMA chunks), double-buffered; weights stream from HBM into registers one
+// chunk ahead.  Per chunk a lane feeds two 16-byte pieces of its row and the
+// row's scale byte for block grp of the chunk.
+constexpr int kMXC = 256;                // K stage of the staged MX codes (two chunks)
+constexpr int kMRS = kMXC + 16;          // padded LDS row stride (bytes)
+constexpr int kMSC = kMXC / 32;          // scale bytes per row per stage
+constexpr int kMCH = kMXC / 16;          // 16-byte code chunks per row per stage
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_gate_up_mx(
     const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ wgu, const uint8_t* __restrict__ wgus,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, int H, int I, int k,
-    int n_items, uint8_t* __restrict__ h, uint8_t* __restrict__ hs) {
-  const int nblk = I / kGuNeurons;
-  const int item = xcd_item(blockIdx.x, n_items);
+    uint8_t* __restrict__ h, uint8_t* __restrict__ hs) {
+  __shared__ __align__(16) uint8_t xl[2][kBM * kMRS];
+  __shared__ __align__(16) uint8_t sl[2][kBM * kMSC];
+  constexpr int NT = NW * 64;
+  constexpr int LPT = kBM * (kMXC / 16) / NT;
+  const int nblk = I / (NW * 32);
+  const int item = real_item(blockIdx.x, nblk, *n_tiles);
+  if (item < 0) return;
   const int tile = item / nblk, nb_i = item - tile * nblk;
-  if (tile >= *n_tiles) return;
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
   const int mcount = min(kBM, counts[e] - m0);
   const int rbase = offsets[e] + m0;
-  const int wv = wave_id(), ln = lane_id(), col = ln & 15, grp = ln >> 4;
-  const int nb = nb_i * kGuNeurons + wv * 32;
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, col = ln & 15, grp = ln >> 4;
+  const int nb = nb_i * NW * 32 + wv * 32;
   const int KB = H / 32;                               // scale bytes per row
 
   const uint8_t* __restrict__ wb = wgu + static_cast<size_t>(e) * 2 * I * H;
   const uint8_t* __restrict__ wsb = wgus + static_cast<size_t>(e) * 2 * I * KB;
-  uint32_t og[2], ou[2], osg[2], osu[2], ox[4], osx[4];
+  uint32_t og[2], ou[2], osg[2], osu[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int rg = nb + 16 * q + col, ru = rg + I;
@@ -416,53 +520,91 @@ __global__ __launch_bounds__(256) void gemm_gate_up_mx(
     osg[q] = static_cast<uint32_t>(rg * KB + grp);
     osu[q] = static_cast<uint32_t>(ru * KB + grp);
   }
+  // loaders: codes chunk c = tid + i*NT -> (row c/kMCH, 16-byte column c%kMCH);
+  // scales: thread tid < 64 loads row tid's kMSC scale bytes of the stage
+  uint32_t oxl[LPT];
+  int lrow[LPT];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int r = 16 * g + col;
-    const int tok = perm[rbase + (r < mcount ? r : 0)] / k;
-    ox[g] = static_cast<uint32_t>(tok * H + 16 * grp);
-    osx[g] = static_cast<uint32_t>(tok * KB + grp);
+  for (int i = 0; i < LPT; ++i) {
+    const int c = tid + i * NT, r = c / kMCH;
+    lrow[i] = r * kMRS + (c % kMCH) * 16;
+    oxl[i] = static_cast<uint32_t>((perm[rbase + (r < mcount ? r : 0)] / k) * H + (c % kMCH) * 16);
   }
+  const bool sload = tid < kBM;
+  const uint32_t osl = sload ? static_cast<uint32_t>((perm[rbase + (tid < mcount ? tid : 0)] / k) * KB) : 0u;
+  i32x4 xr[LPT];
+  uint2 sr = make_uint2(0u, 0u);
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) xr[i] = ld16(x + oxl[i]);
+  if (sload) sr = *reinterpret_cast<const uint2*>(xs + osl);
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xl[0][lrow[i]]) = xr[i];
+  if (sload) *reinterpret_cast<uint2*>(&sl[0][tid * kMSC]) = sr;
+
   f32x4 ag[2][4], au[2][4];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int g = 0; g < 4; ++g) ag[q][g] = au[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  i32x8 bg[D][2], bu[D][2], bx[D][4];
-  int sg[D][2], su[D][2], sx[D][4];
-#define GUM_LOAD(S, KC)                                                               \
-  {                                                                                   \
-    const int ko = (KC) * 128, so = (KC) * 4;                                         \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                   \
-      bg[S][q] = cat8(ld16(wb + og[q] + ko), ld16(wb + og[q] + ko + 64));             \
-      bu[S][q] = cat8(ld16(wb + ou[q] + ko), ld16(wb + ou[q] + ko + 64));             \
-      sg[S][q] = wsb[osg[q] + so];                                                    \
-      su[S][q] = wsb[osu[q] + so];                                                    \
-    }                                                                                 \
-    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                   \
-      bx[S][g] = cat8(ld16(x + ox[g] + ko), ld16(x + ox[g] + ko + 64));               \
-      sx[S][g] = xs[osx[g] + so];                                                     \
-    }                                                                                 \
+  i32x8 wg0[2], wu0[2], wg1[2], wu1[2];
+  int sg0[2], su0[2], sg1[2], su1[2];
+#define GUM_W(WG, WU, SG, SU, KC)                                                  \
+  {                                                                                \
+    const int ko_ = (KC) * 128, so_ = (KC) * 4;                                    \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                \
+      WG[q] = cat8(ld16(wb + og[q] + ko_), ld16(wb + og[q] + ko_ + 64));           \
+      WU[q] = cat8(ld16(wb + ou[q] + ko_), ld16(wb + ou[q] + ko_ + 64));           \
+      SG[q] = wsb[osg[q] + so_];                                                   \
+      SU[q] = wsb[osu[q] + so_];                                                   \
+    }                                                                              \
+  }
+#define GUM_MMA(WG, WU, SG, SU, CL)                                                \
+  {                                                                                \
+    i32x8 bx[4];                                                                   \
+    int sx[4];                                                                     \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                \
+      const uint8_t* p_ = xcur + (16 * g) * kMRS + (CL) * 128;                     \
+      bx[g] = cat8(*reinterpret_cast<const i32x4*>(p_),                            \
+                   *reinterpret_cast<const i32x4*>(p_ + 64));                      \
+      sx[g] = scur[(16 * g) * kMSC + (CL) * 4];                                    \
+    }                                                                              \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q)                                  \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                \
+      ag[q][g] = mfma_mx16x16x128(WG[q], bx[g], SG[q], sx[g], ag[q][g]);           \
+      au[q][g] = mfma_mx16x16x128(WU[q], bx[g], SU[q], sx[g], au[q][g]);           \
+    }                                                                              \
   }
   const int chunks = H / 128;
-#define GUM_MMA(S)                                                                      \
-  _Pragma("unroll") for (int q = 0; q < 2; ++q)                                         \
-  _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                       \
-    ag[q][g] = mfma_mx16x16x128(bg[S][q], bx[S][g], sg[S][q], sx[S][g], ag[q][g]);      \
-    au[q][g] = mfma_mx16x16x128(bu[S][q], bx[S][g], su[S][q], sx[S][g], au[q][g]);      \
+  GUM_W(wg0, wu0, sg0, su0, 0)
+  __syncthreads();
+  const int nstage = H / kMXC;
+  for (int st = 0; st < nstage; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nstage;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) xr[i] = ld16(x + oxl[i] + (st + 1) * kMXC);
+      if (sload) sr = *reinterpret_cast<const uint2*>(xs + osl + (st + 1) * kMSC);
+    }
+    const uint8_t* xcur = &xl[buf][col * kMRS + 16 * grp];
+    const uint8_t* scur = &sl[buf][col * kMSC + grp];
+#pragma unroll
+    for (int cl = 0; cl < kMXC / 128; cl += 2) {
+      const int kc = st * (kMXC / 128) + cl;
+      GUM_W(wg1, wu1, sg1, su1, kc + 1)
+      GUM_MMA(wg0, wu0, sg0, su0, cl)
+      GUM_W(wg0, wu0, sg0, su0, min(kc + 2, chunks - 1))
+      GUM_MMA(wg1, wu1, sg1, su1, cl + 1)
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xl[buf ^ 1][lrow[i]]) = xr[i];
+      if (sload) *reinterpret_cast<uint2*>(&sl[buf ^ 1][tid * kMSC]) = sr;
+    }
+    __syncthreads();
   }
-  GUM_LOAD(0, 0)
-  const int kpairs = chunks & ~1;
-  for (int kc = 0; kc < kpairs; kc += 2) {
-    GUM_LOAD(1, kc + 1)
-    GUM_MMA(0)
-    GUM_LOAD(0, min(kc + 2, chunks - 1))
-    GUM_MMA(1)
-  }
-  if (chunks & 1) { GUM_MMA(0) }
+#undef GUM_W
 #undef GUM_MMA
-#undef GUM_LOAD
   // SwiGLU, then MX-quantize the 32 neurons [nb, nb+32) of each row: lanes
   // col + 16*grp (grp = 0..3) hold them (4 per q group each).
 #pragma unroll
@@ -494,80 +636,121 @@ __global__ __launch_bounds__(256) void gemm_gate_up_mx(
   }
 }
 
-// down, MXFP8: as the BF16 down kernel with 128-wide scaled K chunks.
-template <bool FUSED, int D>
-__global__ __launch_bounds__(256) void gemm_down_mx(
+// down, MXFP8: as the BF16 down kernel, with the h codes and scale bytes of
+// the tile staged in LDS in stages of 256 along K.
+template <bool FUSED, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_down_mx(
     const uint8_t* __restrict__ h, const uint8_t* __restrict__ hs,
     const uint8_t* __restrict__ wd, const uint8_t* __restrict__ wds,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
-    int H, int I, int n_items, float* __restrict__ y, uint16_t* __restrict__ out) {
-  const int nblk = H / kDnRows;
-  const int item = xcd_item(blockIdx.x, n_items);
+    int H, int I, float* __restrict__ y, uint16_t* __restrict__ out) {
+  __shared__ __align__(16) uint8_t hl[2][kBM * kMRS];
+  __shared__ __align__(16) uint8_t sl[2][kBM * kMSC];
+  constexpr int NT = NW * 64;
+  constexpr int LPT = kBM * (kMXC / 16) / NT;
+  const int nblk = H / (NW * 64);
+  const int item = real_item(blockIdx.x, nblk, *n_tiles);
+  if (item < 0) return;
   const int tile = item / nblk, db_i = item - tile * nblk;
-  if (tile >= *n_tiles) return;
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
   const int mcount = min(kBM, counts[e] - m0);
   const int rbase = offsets[e] + m0;
-  const int wv = wave_id(), ln = lane_id(), col = ln & 15, grp = ln >> 4;
-  const int db = db_i * kDnRows + wv * 64;
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, col = ln & 15, grp = ln >> 4;
+  const int db = db_i * NW * 64 + wv * 64;
   const int KB = I / 32;
 
   const uint8_t* __restrict__ wb = wd + static_cast<size_t>(e) * H * I;
   const uint8_t* __restrict__ wsb = wds + static_cast<size_t>(e) * H * KB;
   const uint8_t* __restrict__ hb = h + static_cast<size_t>(rbase) * I;
   const uint8_t* __restrict__ hsb = hs + static_cast<size_t>(rbase) * KB;
-  uint32_t ow[4], osw[4], oh[4], osh[4];
+  uint32_t ow[4], osw[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = db + 16 * q + col;
     ow[q] = static_cast<uint32_t>(row * I + 16 * grp);
     osw[q] = static_cast<uint32_t>(row * KB + grp);
   }
+  uint32_t ohl[LPT];
+  int lrow[LPT];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int r = 16 * g + col;
-    const int rr = r < mcount ? r : 0;
-    oh[g] = static_cast<uint32_t>(rr * I + 16 * grp);
-    osh[g] = static_cast<uint32_t>(rr * KB + grp);
+  for (int i = 0; i < LPT; ++i) {
+    const int c = tid + i * NT, r = c / kMCH;
+    lrow[i] = r * kMRS + (c % kMCH) * 16;
+    ohl[i] = static_cast<uint32_t>((r < mcount ? r : 0) * I + (c % kMCH) * 16);
   }
+  const bool sload = tid < kBM;
+  const uint32_t osl = sload ? static_cast<uint32_t>((tid < mcount ? tid : 0) * KB) : 0u;
+  i32x4 hr_[LPT];
+  uint2 sr = make_uint2(0u, 0u);
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) hr_[i] = ld16(hb + ohl[i]);
+  if (sload) sr = *reinterpret_cast<const uint2*>(hsb + osl);
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&hl[0][lrow[i]]) = hr_[i];
+  if (sload) *reinterpret_cast<uint2*>(&sl[0][tid * kMSC]) = sr;
+
   f32x4 acc[4][4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  i32x8 ba[D][4], bb[D][4];
-  int sa[D][4], sb[D][4];
-#define DNM_LOAD(S, KC)                                                               \
-  {                                                                                   \
-    const int ko = (KC) * 128, so = (KC) * 4;                                         \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                   \
-      ba[S][q] = cat8(ld16(wb + ow[q] + ko), ld16(wb + ow[q] + ko + 64));             \
-      sa[S][q] = wsb[osw[q] + so];                                                    \
-    }                                                                                 \
-    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                   \
-      bb[S][g] = cat8(ld16(hb + oh[g] + ko), ld16(hb + oh[g] + ko + 64));             \
-      sb[S][g] = hsb[osh[g] + so];                                                    \
-    }                                                                                 \
+  i32x8 a0[4], a1[4];
+  int sa0[4], sa1[4];
+#define DNM_W(A, SA, KC)                                                           \
+  {                                                                                \
+    const int ko_ = (KC) * 128, so_ = (KC) * 4;                                    \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                \
+      A[q] = cat8(ld16(wb + ow[q] + ko_), ld16(wb + ow[q] + ko_ + 64));            \
+      SA[q] = wsb[osw[q] + so_];                                                   \
+    }                                                                              \
+  }
+#define DNM_MMA(A, SA, CL)                                                         \
+  {                                                                                \
+    i32x8 bb[4];                                                                   \
+    int sb[4];                                                                     \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                \
+      const uint8_t* p_ = hcur + (16 * g) * kMRS + (CL) * 128;                     \
+      bb[g] = cat8(*reinterpret_cast<const i32x4*>(p_),                            \
+                   *reinterpret_cast<const i32x4*>(p_ + 64));                      \
+      sb[g] = scur[(16 * g) * kMSC + (CL) * 4];                                    \
+    }                                                                              \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                  \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g)                                  \
+      acc[q][g] = mfma_mx16x16x128(A[q], bb[g], SA[q], sb[g], acc[q][g]);          \
   }
   const int chunks = I / 128;
-#define DNM_MMA(S)                                                                       \
-  _Pragma("unroll") for (int q = 0; q < 4; ++q)                                          \
-  _Pragma("unroll") for (int g = 0; g < 4; ++g)                                          \
-    acc[q][g] = mfma_mx16x16x128(ba[S][q], bb[S][g], sa[S][q], sb[S][g], acc[q][g]);
-  DNM_LOAD(0, 0)
-  const int kpairs = chunks & ~1;
-  for (int kc = 0; kc < kpairs; kc += 2) {
-    DNM_LOAD(1, kc + 1)
-    DNM_MMA(0)
-    DNM_LOAD(0, min(kc + 2, chunks - 1))
-    DNM_MMA(1)
+  DNM_W(a0, sa0, 0)
+  __syncthreads();
+  const int nstage = I / kMXC;
+  for (int st = 0; st < nstage; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nstage;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) hr_[i] = ld16(hb + ohl[i] + (st + 1) * kMXC);
+      if (sload) sr = *reinterpret_cast<const uint2*>(hsb + osl + (st + 1) * kMSC);
+    }
+    const uint8_t* hcur = &hl[buf][col * kMRS + 16 * grp];
+    const uint8_t* scur = &sl[buf][col * kMSC + grp];
+#pragma unroll
+    for (int cl = 0; cl < kMXC / 128; cl += 2) {
+      const int kc = st * (kMXC / 128) + cl;
+      DNM_W(a1, sa1, kc + 1)
+      DNM_MMA(a0, sa0, cl)
+      DNM_W(a0, sa0, min(kc + 2, chunks - 1))
+      DNM_MMA(a1, sa1, cl + 1)
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&hl[buf ^ 1][lrow[i]]) = hr_[i];
+      if (sload) *reinterpret_cast<uint2*>(&sl[buf ^ 1][tid * kMSC]) = sr;
+    }
+    __syncthreads();
   }
-  if (chunks & 1) { DNM_MMA(0) }
+#undef DNM_W
 #undef DNM_MMA
-#undef DNM_LOAD
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
@@ -625,17 +808,17 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
   hipLaunchKernelGGL(group_experts, dim3(E), dim3(1024), 0, s, idx, P, E, kBM, p.counts,
                      p.offsets, p.tiles, p.n_tiles, p.perm, p.row_of);
   prof_end(kGroup, s);
-  const int n_items = round_up((I / kGuNeurons) * L.max_tiles, kXcds);
+  constexpr int NW = 8;                              // 256 neurons per workgroup
+  const int n_items = round_up((I / (NW * 32)) * L.max_tiles, kXcds);
   prof_begin(kGemmGateUp, s);
   if (dtype == 0)
-    hipLaunchKernelGGL(gemm_gate_up_bf16<kStagesBf16>, dim3(n_items), dim3(256), 0, s,
+    hipLaunchKernelGGL(gemm_gate_up_bf16<NW>, dim3(n_items), dim3(NW * 64), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
-                       p.tiles, p.n_tiles, p.counts, p.offsets, H, I, k, n_items,
-                       static_cast<uint16_t*>(h));
+                       p.tiles, p.n_tiles, p.counts, p.offsets, H, I, k, static_cast<uint16_t*>(h));
   else
-    hipLaunchKernelGGL(gemm_gate_up_mx<kStagesMx>, dim3(n_items), dim3(256), 0, s,
+    hipLaunchKernelGGL(gemm_gate_up_mx<NW>, dim3(n_items), dim3(NW * 64), 0, s,
                        static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
-                       p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, H, I, k, n_items,
+                       p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, H, I, k,
                        static_cast<uint8_t*>(h), hs);
   prof_end(kGemmGateUp, s);
   return hipGetLastError();
@@ -648,27 +831,28 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   (void)idx; (void)num_cus;
   const BatchedWs L = batched_ws_layout(T, H, I, E, k, dtype);
   const BatchedPtrs p = batched_ptrs(ws, L);
-  const int n_items = round_up((H / kDnRows) * L.max_tiles, kXcds);
+  const bool wide = H % 512 == 0;                    // 8 waves x 64 dims, else 4 waves
+  const int nw = wide ? 8 : 4;
+  const int n_items = round_up((H / (nw * 64)) * L.max_tiles, kXcds);
+  const dim3 grid(n_items), block(nw * 64);
+#define DOWN_BF16(F, NWV)                                                                   \
+  hipLaunchKernelGGL((gemm_down_bf16<F, NWV>), grid, block, 0, s,                          \
+                     static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),       \
+                     p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, p.y, out)
+#define DOWN_MX(F, NWV)                                                                     \
+  hipLaunchKernelGGL((gemm_down_mx<F, NWV>), grid, block, 0, s,                            \
+                     static_cast<const uint8_t*>(h), hs, static_cast<const uint8_t*>(wd), wds, \
+                     p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, p.y, out)
   prof_begin(kGemmDown, s);
-  if (dtype != 0) {
-    const uint8_t* hc = static_cast<const uint8_t*>(h);
-    const uint8_t* wc = static_cast<const uint8_t*>(wd);
-    if (k == 1)
-      hipLaunchKernelGGL((gemm_down_mx<true, kStagesMx>), dim3(n_items), dim3(256), 0, s, hc, hs, wc, wds,
-                         p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, n_items, p.y,
-                         out);
-    else
-      hipLaunchKernelGGL((gemm_down_mx<false, kStagesMx>), dim3(n_items), dim3(256), 0, s, hc, hs, wc, wds,
-                         p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, n_items, p.y,
-                         out);
-  } else if (k == 1)
-    hipLaunchKernelGGL((gemm_down_bf16<true, kStagesBf16>), dim3(n_items), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd), p.perm,
-                       p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, n_items, p.y, out);
-  else
-    hipLaunchKernelGGL((gemm_down_bf16<false, kStagesBf16>), dim3(n_items), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd), p.perm,
-                       p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, n_items, p.y, out);
+  if (dtype == 0) {
+    if (k == 1) { if (wide) DOWN_BF16(true, 8); else DOWN_BF16(true, 4); }
+    else { if (wide) DOWN_BF16(false, 8); else DOWN_BF16(false, 4); }
+  } else {
+    if (k == 1) { if (wide) DOWN_MX(true, 8); else DOWN_MX(true, 4); }
+    else { if (wide) DOWN_MX(false, 8); else DOWN_MX(false, 4); }
+  }
+#undef DOWN_BF16
+#undef DOWN_MX
   prof_end(kGemmDown, s);
   if (k > 1) {
     prof_begin(kCombine, s);

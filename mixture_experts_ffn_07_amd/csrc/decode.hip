@@ -265,25 +265,47 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
 // down: workgroup = 8 output dimensions d0..d0+7 of every touched expert (H/8
 // workgroups, enough to occupy every CU without splitting the expert sum
 // across workgroups).  MFMA rows 0..7 carry those dimensions; lanes of rows
-// 8..15 issue no loads (the MFMA work they waste is free: the kernel is bound
-// by HBM).  Wave wv covers K range [wv*I/8, (wv+1)*I/8) of each touched expert
-// in ascending expert order, as a flat sequence of (expert, chunk of KD
-// steps) tasks whose weights are double-buffered in registers; the eight wave
-// partials are then added in LDS in wave order.
+// 8..15 issue no weight loads (the MFMA work they waste is free: the kernel
+// is bound by memory).  The 16 waves form EGW expert groups x KSW K-slices:
+// wave (eg, ks) takes experts u = eg, eg + EGW, ... in ascending order and
+// the K range [ks*I/KSW, (ks+1)*I/KSW) of each, loading the next expert's
+// weights while it multiplies the current one.  The 16 wave partials are
+// added in LDS in wave order, so the sum order is fixed.
 constexpr int kDownRows = 8;
+constexpr int kDownWaves = 16;
+constexpr int kDownThreads = kDownWaves * kWave;
+
+// Slot j of token t whose expert is e (the token routes to e exactly once):
+// a branch-free scan of the token's k expert ids, four at a time.
+__device__ __forceinline__ int slot_of(const int* s_idx_row, int k, int e) {
+  int js = 0;
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    const int4 v = *reinterpret_cast<const int4*>(s_idx_row + j0);
+    js = (v.x == e) ? j0 : js;
+    js = (j0 + 1 < k && v.y == e) ? j0 + 1 : js;
+    js = (j0 + 2 < k && v.z == e) ? j0 + 2 : js;
+    js = (j0 + 3 < k && v.w == e) ? j0 + 3 : js;
+  }
+  return js;
+}
 
 template <int TM, int KD>
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_down(
+__global__ __launch_bounds__(kDownThreads) void decode_down(
     const uint16_t* __restrict__ wd, const int32_t* __restrict__ idx,
     const int* __restrict__ plan_u, const int32_t* __restrict__ plan_e,
     const uint64_t* __restrict__ plan_mask, const uint16_t* __restrict__ hw_hi,
-    const uint16_t* __restrict__ hw_lo, int T, int H, int I, int k, uint16_t* __restrict__ out) {
-  extern __shared__ float red[];                    // [8 waves][TM][4][64]
-  __shared__ int s_idx[64 * 32];
+    const uint16_t* __restrict__ hw_lo, int T, int H, int I, int k, int KSW,
+    uint16_t* __restrict__ out) {
+  extern __shared__ float red[];                    // [16 waves][TM][4][64]
+  __shared__ __align__(16) int s_idx[64 * 32];      // token rows padded to a multiple of 4
   __shared__ int s_e[kMaxPlan];
   __shared__ uint64_t s_m[kMaxPlan];
   const int U = *plan_u;
-  for (int i = threadIdx.x; i < T * k; i += blockDim.x) s_idx[i] = idx[i];
+  const int kp = (k + 3) & ~3;                      // padded row length
+  for (int i = threadIdx.x; i < T * kp; i += blockDim.x) {
+    const int t = i / kp, j = i - t * kp;
+    s_idx[i] = j < k ? idx[t * k + j] : -1;
+  }
   for (int i = threadIdx.x; i < U; i += blockDim.x) {
     s_e[i] = plan_e[i];
     s_m[i] = plan_mask[i];
@@ -291,41 +313,38 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   __syncthreads();
   const int wv = wave_id(), ln = lane_id();
   const int col = ln & 15, grp = ln >> 4;
+  const int EGW = kDownWaves / KSW;
+  const int ks = wv % KSW, eg = wv / KSW;
   const bool row_lane = col < kDownRows;
   const int d0 = blockIdx.x * kDownRows;
-  const int kw = I / kDecWaves;
-  const int nch = kw / 32 / KD;
-  const int ntask = U * nch;
-  const uint32_t kb = static_cast<uint32_t>(wv * kw + grp * 8);
+  const int kw = I / KSW;                           // = KD * 32
+  const uint32_t kb = static_cast<uint32_t>(ks * kw + grp * 8);
   const uint16_t* pw = wd + (static_cast<size_t>(d0) + (row_lane ? col : 0)) * I + kb;
   const bf16x8 zero8 = {};
+  const int ntask = U > eg ? (U - 1 - eg) / EGW + 1 : 0;
   f32x4 acc[TM];
 #pragma unroll
   for (int c = 0; c < TM; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   bf16x8 aA[KD], aB[KD];
-#define DN_ISSUE(A, T)                                                                   \
-  {                                                                                      \
-    const int u_ = (T) / nch, c_ = (T) - u_ * nch;                                      \
-    const uint16_t* p_ = pw + static_cast<size_t>(s_e[u_]) * H * I + c_ * KD * 32;      \
-    _Pragma("unroll") for (int s = 0; s < KD; ++s)                                       \
-      A[s] = row_lane ? as_bf16x8(ld16(p_ + s * 32)) : zero8;                            \
+#define DN_ISSUE(A, TSK)                                                              \
+  {                                                                                   \
+    const uint16_t* p_ = pw + static_cast<size_t>(s_e[eg + (TSK) * EGW]) * H * I;    \
+    _Pragma("unroll") for (int s = 0; s < KD; ++s)                                    \
+      A[s] = row_lane ? as_bf16x8(ld16(p_ + s * 32)) : zero8;                         \
   }
-  auto run_task = [&](const bf16x8 (&A)[KD], int t) {
-    const int u = t / nch, c = t - u * nch;
+  auto run_task = [&](const bf16x8 (&A)[KD], int tsk) {
+    const int u = eg + tsk * EGW;
     const int e = s_e[u];
     const uint64_t mask = s_m[u];
-    const uint32_t ko = kb + c * KD * 32;
 #pragma unroll
     for (int q = 0; q < TM; ++q) {
       const uint32_t bits = static_cast<uint32_t>(mask >> (16 * q)) & 0xFFFFu;
       if (bits == 0) continue;
       const int tk = 16 * q + col;
       const bool routed = (bits >> col) & 1u;
-      int js = 0;
-      if (routed)
-        while (js < k - 1 && s_idx[tk * k + js] != e) ++js;
-      const size_t row = static_cast<size_t>((routed ? tk : 0) * k + js) * I + ko;
+      const int js = routed ? slot_of(s_idx + tk * kp, k, e) : 0;
+      const size_t row = static_cast<size_t>((routed ? tk : 0) * k + js) * I + kb;
       bf16x8 bh[KD], bl[KD];
 #pragma unroll
       for (int s = 0; s < KD; ++s) {
@@ -361,7 +380,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
     const int src = 16 * (mm >> 2) + n, r = mm & 3;
     float v = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kDecWaves; ++w2) v += red[((w2 * TM + c) * 4 + r) * 64 + src];
+    for (int w2 = 0; w2 < kDownWaves; ++w2) v += red[((w2 * TM + c) * 4 + r) * 64 + src];
     const int t = 16 * c + n;
     if (t < T) out[static_cast<size_t>(t) * H + d0 + mm] = static_cast<uint16_t>(f32_to_bf16_rne(v));
   }
@@ -392,11 +411,16 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   const long grid_cap = 2L * num_cus;
   const int grid1 = static_cast<int>(items_upper < grid_cap ? items_upper : grid_cap);
   const size_t lds_gu = sizeof(float) * kDecWaves * TM * 2 * 256;
-  const size_t lds_dn = sizeof(float) * kDecWaves * TM * 256;
-  const int gsteps = H / kDecWaves / 32, dsteps = I / kDecWaves / 32;
+  const size_t lds_dn = sizeof(float) * kDownWaves * TM * 256;
+  const int gsteps = H / kDecWaves / 32;
   int KC = gsteps % 4 == 0 ? 4 : (gsteps % 3 == 0 ? 3 : (gsteps % 2 == 0 ? 2 : 1));
   if (TM == 4 && KC == 4) KC = 2;                   // keeps four token tiles within 128 VGPRs
-  const int KD = dsteps % 4 == 0 ? 4 : (dsteps % 3 == 0 ? 3 : (dsteps % 2 == 0 ? 2 : 1));
+  // down: K-slices per workgroup so that each wave has at most 4 steps of 32
+  // (I is a multiple of 256, so I/32 is a multiple of 8 and KSW <= 16 works)
+  const int dtotal = I / 32;
+  int KSW = 1;
+  while (KSW < kDownWaves && (dtotal / KSW > 4 || dtotal % KSW)) KSW *= 2;
+  const int KD = dtotal / KSW;
   const dim3 grid2(H / kDownRows);
   prof_begin(kDecGateUp, s);
 #define GU_LAUNCH(TMV, KCV)                                                                    \
@@ -415,8 +439,8 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   prof_end(kDecGateUp, s);
   prof_begin(kDecDown, s);
 #define DN_LAUNCH(TMV, KDV)                                                                    \
-  hipLaunchKernelGGL((decode_down<TMV, KDV>), grid2, dim3(kDecThreads), lds_dn, s, wd, idx_p,    \
-                     plan_u, plan_e, plan_mask, hw_hi, hw_lo, T, H, I, k, out)
+  hipLaunchKernelGGL((decode_down<TMV, KDV>), grid2, dim3(kDownThreads), lds_dn, s, wd, idx_p,   \
+                     plan_u, plan_e, plan_mask, hw_hi, hw_lo, T, H, I, k, KSW, out)
 #define DN_KD(TMV)                                        \
   switch (KD) {                                           \
     case 4: DN_LAUNCH(TMV, 4); break;                     \

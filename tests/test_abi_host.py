@@ -111,7 +111,7 @@ def test_batched_validation(m):
     assert call(x=None) == m.MOE_ERR_NULL
     assert call(H=200) == m.MOE_ERR_SHAPE
     assert call(H=384) == m.MOE_ERR_SHAPE                  # not a multiple of 256
-    assert call(I=192) == m.MOE_ERR_SHAPE                  # not a multiple of 128
+    assert call(I=128) == m.MOE_ERR_SHAPE                  # not a multiple of 256
     assert call(dt=3) == m.MOE_ERR_SHAPE
     assert call(wsb=need - 1) == m.MOE_ERR_WORKSPACE
     assert call(h=FAKE + 4) == m.MOE_ERR_ALIGN

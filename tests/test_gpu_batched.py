@@ -49,10 +49,10 @@ def _custom(T, H, I, E, k, seed=0, x_std=1.0):
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [
-    (1, 256, 128, 4, 2),        # one token
+    (1, 256, 256, 4, 2),        # one token
     (100, 512, 256, 8, 2),      # ~25 rows per expert
-    (300, 256, 384, 6, 3),      # >64 rows per expert: several M-tiles, ragged last tile
-    (257, 768, 128, 40, 8),     # many small experts, some empty
+    (300, 256, 512, 6, 3),      # >64 rows per expert: several M-tiles, ragged last tile
+    (257, 768, 256, 40, 8),     # many small experts, some empty; 4-wave down
     (500, 512, 256, 6, 1),      # k = 1: down writes the output directly
     (64, 256, 256, 16, 16),     # k = E
 ])
@@ -92,7 +92,7 @@ def test_batched_bit_identical_repeats(M):
 
 def test_batched_grouping_is_stable(M):
     # the h rows come out grouped by expert, tokens ascending inside each expert
-    d = _custom(300, 256, 128, 10, 3, seed=4)
+    d = _custom(300, 256, 256, 10, 3, seed=4)
     cfg = d["cfg"]
     out, idx, w, h, ws = run_layer(M, d)
     ridx, _ = route(d["logits"].cpu().numpy(), cfg.k)

@@ -95,11 +95,11 @@ def _custom(T, H, I, E, k, seed=0):
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [
-    (1, 256, 128, 4, 2),
-    (100, 512, 256, 8, 2),
-    (300, 256, 384, 6, 3),      # several M-tiles per expert
-    (257, 768, 128, 40, 8),
-    (500, 512, 256, 6, 1),      # k = 1: fused output
+    (1, 256, 256, 4, 2),        # one token; 4-wave down
+    (100, 1024, 512, 8, 2),
+    (300, 512, 768, 6, 3),      # several M-tiles per expert, odd stage count
+    (257, 768, 256, 40, 8),     # many small experts, some empty; 4-wave down
+    (500, 512, 512, 6, 1),      # k = 1: fused output
 ])
 def test_mx_shapes(M, T, H, I, E, k):
     _check(M, _custom(T, H, I, E, k, seed=T + 1), f"mx shape T={T} H={H} I={I} E={E} k={k}")
@@ -120,7 +120,7 @@ def test_mx_dsv4_ep64_share(M):
 
 
 def test_mx_bit_identical_repeats(M):
-    d = _custom(1024, 512, 256, 32, 8, seed=5)
+    d = _custom(1024, 512, 512, 32, 8, seed=5)
     first = run_mx(M, d)
     for _ in range(3):
         again = run_mx(M, d)
@@ -132,7 +132,7 @@ def test_mx_h_codes_match_oracle_quantizer(M):
     # the h codes the GPU writes are the MX quantization of its own FP32
     # activations; re-quantizing their decoded values must reproduce them, and
     # they must be close to the oracle's unquantized activations
-    d = _custom(64, 256, 256, 4, 2, seed=6)
+    d = _custom(64, 512, 512, 4, 2, seed=6)
     cfg = d["cfg"]
     out, idx, w, h, hs = run_mx(M, d)
     codes, scales = h.cpu().numpy(), hs.cpu().numpy()
