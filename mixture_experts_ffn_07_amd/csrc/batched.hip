@@ -475,12 +475,14 @@ __global__ __launch_bounds__(256) void quant_mx_rows(const uint16_t* __restrict_
   }
 }
 
-// gate_up, MXFP8: workgroup = (M-tile, NW*32 neurons); wave = 32 neurons
-// (one MX block of h) x 64 rows.  The activation codes and scale bytes of
-// the tile are staged in LDS in stages of 256 along K (two 128-wide scaled
-// MFMA chunks), double-buffered; weights stream from HBM into registers one
-// chunk ahead.  Per chunk a lane feeds two 16-byte pieces of its row and the
-// row's scale byte for block grp of the chunk.
+// gate_up, MXFP8: workgroup = (M-tile, NW*16 neurons); wave = 16 neurons (16
+// gate rows + 16 up rows) x 64 rows, so the wide FP8 operands of a double-
+// buffered K loop fit the register file.  The activation codes and scale
+// bytes of the tile are staged in LDS in stages of 256 along K (two 128-wide
+// scaled MFMA chunks), double-buffered and shared by all NW waves.  Per chunk
+// a lane feeds two 16-byte pieces of its row and the row's scale byte for
+// block grp of the chunk.  An MX block of h (32 neurons) spans the wave pair
+// (2m, 2m+1); their per-row maxima meet in LDS.
 constexpr int kMXC = 256;                // K stage of the staged MX codes (two chunks)
 constexpr int kMRS = kMXC + 16;          // padded LDS row stride (bytes)
 constexpr int kMSC = kMXC / 32;          // scale bytes per row per stage
@@ -495,9 +497,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_gate_up_mx(
     uint8_t* __restrict__ h, uint8_t* __restrict__ hs) {
   __shared__ __align__(16) uint8_t xl[2][kBM * kMRS];
   __shared__ __align__(16) uint8_t sl[2][kBM * kMSC];
+  __shared__ float s_amax[NW][kBM];
   constexpr int NT = NW * 64;
-  constexpr int LPT = kBM * (kMXC / 16) / NT;
-  const int nblk = I / (NW * 32);
+  constexpr int LPT = (kBM * kMCH + NT - 1) / NT;
+  const int nblk = I / (NW * 16);
   const int item = real_item(blockIdx.x, nblk, *n_tiles);
   if (item < 0) return;
   const int tile = item / nblk, nb_i = item - tile * nblk;
@@ -506,29 +509,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_gate_up_mx(
   const int mcount = min(kBM, counts[e] - m0);
   const int rbase = offsets[e] + m0;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, col = ln & 15, grp = ln >> 4;
-  const int nb = nb_i * NW * 32 + wv * 32;
+  const int nb = nb_i * NW * 16 + wv * 16;
   const int KB = H / 32;                               // scale bytes per row
 
   const uint8_t* __restrict__ wb = wgu + static_cast<size_t>(e) * 2 * I * H;
   const uint8_t* __restrict__ wsb = wgus + static_cast<size_t>(e) * 2 * I * KB;
-  uint32_t og[2], ou[2], osg[2], osu[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int rg = nb + 16 * q + col, ru = rg + I;
-    og[q] = static_cast<uint32_t>(rg * H + 16 * grp);
-    ou[q] = static_cast<uint32_t>(ru * H + 16 * grp);
-    osg[q] = static_cast<uint32_t>(rg * KB + grp);
-    osu[q] = static_cast<uint32_t>(ru * KB + grp);
-  }
+  const int rg = nb + col, ru = rg + I;
+  const uint32_t og = static_cast<uint32_t>(rg * H + 16 * grp);
+  const uint32_t ou = static_cast<uint32_t>(ru * H + 16 * grp);
+  const uint32_t osg = static_cast<uint32_t>(rg * KB + grp);
+  const uint32_t osu = static_cast<uint32_t>(ru * KB + grp);
   // loaders: codes chunk c = tid + i*NT -> (row c/kMCH, 16-byte column c%kMCH);
   // scales: thread tid < 64 loads row tid's kMSC scale bytes of the stage
   uint32_t oxl[LPT];
   int lrow[LPT];
+  bool lact[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int c = tid + i * NT, r = c / kMCH;
-    lrow[i] = r * kMRS + (c % kMCH) * 16;
-    oxl[i] = static_cast<uint32_t>((perm[rbase + (r < mcount ? r : 0)] / k) * H + (c % kMCH) * 16);
+    lact[i] = c < kBM * kMCH;
+    const int rr = lact[i] && r < mcount ? r : 0;
+    lrow[i] = lact[i] ? r * kMRS + (c % kMCH) * 16 : 0;
+    oxl[i] = static_cast<uint32_t>((perm[rbase + rr] / k) * H + (c % kMCH) * 16);
   }
   const bool sload = tid < kBM;
   const uint32_t osl = sload ? static_cast<uint32_t>((perm[rbase + (tid < mcount ? tid : 0)] / k) * KB) : 0u;
@@ -538,41 +540,31 @@ __global__ __launch_bounds__(NW * 64) void gemm_gate_up_mx(
   for (int i = 0; i < LPT; ++i) xr[i] = ld16(x + oxl[i]);
   if (sload) sr = *reinterpret_cast<const uint2*>(xs + osl);
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xl[0][lrow[i]]) = xr[i];
+  for (int i = 0; i < LPT; ++i)
+    if (lact[i]) *reinterpret_cast<i32x4*>(&xl[0][lrow[i]]) = xr[i];
   if (sload) *reinterpret_cast<uint2*>(&sl[0][tid * kMSC]) = sr;
 
-  f32x4 ag[2][4], au[2][4];
+  f32x4 ag[4], au[4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) ag[q][g] = au[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  i32x8 wg0[2], wu0[2], wg1[2], wu1[2];
-  int sg0[2], su0[2], sg1[2], su1[2];
+  for (int g = 0; g < 4; ++g) ag[g] = au[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  i32x8 wg0, wu0, wg1, wu1;
+  int sg0, su0, sg1, su1;
 #define GUM_W(WG, WU, SG, SU, KC)                                                  \
   {                                                                                \
     const int ko_ = (KC) * 128, so_ = (KC) * 4;                                    \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                \
-      WG[q] = cat8(ld16(wb + og[q] + ko_), ld16(wb + og[q] + ko_ + 64));           \
-      WU[q] = cat8(ld16(wb + ou[q] + ko_), ld16(wb + ou[q] + ko_ + 64));           \
-      SG[q] = wsb[osg[q] + so_];                                                   \
-      SU[q] = wsb[osu[q] + so_];                                                   \
-    }                                                                              \
+    WG = cat8(ld16(wb + og + ko_), ld16(wb + og + ko_ + 64));                      \
+    WU = cat8(ld16(wb + ou + ko_), ld16(wb + ou + ko_ + 64));                      \
+    SG = wsb[osg + so_];                                                           \
+    SU = wsb[osu + so_];                                                           \
   }
 #define GUM_MMA(WG, WU, SG, SU, CL)                                                \
-  {                                                                                \
-    i32x8 bx[4];                                                                   \
-    int sx[4];                                                                     \
-    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                \
-      const uint8_t* p_ = xcur + (16 * g) * kMRS + (CL) * 128;                     \
-      bx[g] = cat8(*reinterpret_cast<const i32x4*>(p_),                            \
-                   *reinterpret_cast<const i32x4*>(p_ + 64));                      \
-      sx[g] = scur[(16 * g) * kMSC + (CL) * 4];                                    \
-    }                                                                              \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q)                                  \
-    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                \
-      ag[q][g] = mfma_mx16x16x128(WG[q], bx[g], SG[q], sx[g], ag[q][g]);           \
-      au[q][g] = mfma_mx16x16x128(WU[q], bx[g], SU[q], sx[g], au[q][g]);           \
-    }                                                                              \
+  _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                  \
+    const uint8_t* p_ = xcur + (16 * g) * kMRS + (CL) * 128;                       \
+    const i32x8 bx = cat8(*reinterpret_cast<const i32x4*>(p_),                     \
+                          *reinterpret_cast<const i32x4*>(p_ + 64));               \
+    const int sx = scur[(16 * g) * kMSC + (CL) * 4];                               \
+    ag[g] = mfma_mx16x16x128(WG, bx, SG, sx, ag[g]);                               \
+    au[g] = mfma_mx16x16x128(WU, bx, SU, sx, au[g]);                               \
   }
   const int chunks = H / 128;
   GUM_W(wg0, wu0, sg0, su0, 0)
@@ -588,56 +580,57 @@ __global__ __launch_bounds__(NW * 64) void gemm_gate_up_mx(
     }
     const uint8_t* xcur = &xl[buf][col * kMRS + 16 * grp];
     const uint8_t* scur = &sl[buf][col * kMSC + grp];
-#pragma unroll
-    for (int cl = 0; cl < kMXC / 128; cl += 2) {
-      const int kc = st * (kMXC / 128) + cl;
-      GUM_W(wg1, wu1, sg1, su1, kc + 1)
-      GUM_MMA(wg0, wu0, sg0, su0, cl)
-      GUM_W(wg0, wu0, sg0, su0, min(kc + 2, chunks - 1))
-      GUM_MMA(wg1, wu1, sg1, su1, cl + 1)
-    }
+    const int kc = st * 2;
+    GUM_W(wg1, wu1, sg1, su1, kc + 1)
+    GUM_MMA(wg0, wu0, sg0, su0, 0)
+    GUM_W(wg0, wu0, sg0, su0, min(kc + 2, chunks - 1))
+    GUM_MMA(wg1, wu1, sg1, su1, 1)
     if (more) {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xl[buf ^ 1][lrow[i]]) = xr[i];
+      for (int i = 0; i < LPT; ++i)
+        if (lact[i]) *reinterpret_cast<i32x4*>(&xl[buf ^ 1][lrow[i]]) = xr[i];
       if (sload) *reinterpret_cast<uint2*>(&sl[buf ^ 1][tid * kMSC]) = sr;
     }
     __syncthreads();
   }
 #undef GUM_W
 #undef GUM_MMA
-  // SwiGLU, then MX-quantize the 32 neurons [nb, nb+32) of each row: lanes
-  // col + 16*grp (grp = 0..3) hold them (4 per q group each).
+  // SwiGLU; per-row maximum over this wave's 16 neurons (lanes col + 16*grp),
+  // combined with the partner wave's through LDS, gives the MX scale of the
+  // 32-neuron block; then each wave encodes its own 16 neurons.
+  float a[4][4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[g][i] = swiglu(ag[g][i], au[g][i]);
+      amax = fmaxf(amax, fabsf(a[g][i]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+    if (grp == 0) s_amax[wv][16 * g + col] = amax;
+  }
+  __syncthreads();
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
-    float a[2][4];
-    float amax = 0.f;
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[q][i] = swiglu(ag[q][g][i], au[q][g][i]);
-        amax = fmaxf(amax, fabsf(a[q][i]));
-      }
-    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
     if (r >= mcount) continue;
+    const float amax = fmaxf(s_amax[wv][r], s_amax[wv ^ 1][r]);
     const int sexp = mx_scale_exp(amax);
     const float inv = exp2_neg(sexp);
-    uint8_t* hr = h + static_cast<size_t>(rbase + r) * I + nb + 4 * grp;
+    uint32_t wq = 0;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      uint32_t wq = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wq |= f32_to_e4m3(a[q][i] * inv) << (8 * i);
-      *reinterpret_cast<uint32_t*>(hr + 16 * q) = wq;
-    }
-    if (grp == 0) hs[static_cast<size_t>(rbase + r) * (I / 32) + nb / 32] = static_cast<uint8_t>(sexp + 127);
+    for (int i = 0; i < 4; ++i) wq |= f32_to_e4m3(a[g][i] * inv) << (8 * i);
+    *reinterpret_cast<uint32_t*>(h + static_cast<size_t>(rbase + r) * I + nb + 4 * grp) = wq;
+    if (grp == 0 && (wv & 1) == 0)
+      hs[static_cast<size_t>(rbase + r) * (I / 32) + nb / 32] = static_cast<uint8_t>(sexp + 127);
   }
 }
 
-// down, MXFP8: as the BF16 down kernel, with the h codes and scale bytes of
-// the tile staged in LDS in stages of 256 along K.
+// down, MXFP8: workgroup = (M-tile, NW*32 output dims); wave = 32 dims (2
+// groups) x 64 rows; the h codes and scale bytes of the tile are staged in
+// LDS in stages of 256 along K, as in gate_up.
 template <bool FUSED, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_down_mx(
     const uint8_t* __restrict__ h, const uint8_t* __restrict__ hs,
@@ -648,8 +641,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_down_mx(
   __shared__ __align__(16) uint8_t hl[2][kBM * kMRS];
   __shared__ __align__(16) uint8_t sl[2][kBM * kMSC];
   constexpr int NT = NW * 64;
-  constexpr int LPT = kBM * (kMXC / 16) / NT;
-  const int nblk = H / (NW * 64);
+  constexpr int LPT = (kBM * kMCH + NT - 1) / NT;
+  const int nblk = H / (NW * 32);
   const int item = real_item(blockIdx.x, nblk, *n_tiles);
   if (item < 0) return;
   const int tile = item / nblk, db_i = item - tile * nblk;
@@ -658,27 +651,29 @@ __global__ __launch_bounds__(NW * 64) void gemm_down_mx(
   const int mcount = min(kBM, counts[e] - m0);
   const int rbase = offsets[e] + m0;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, col = ln & 15, grp = ln >> 4;
-  const int db = db_i * NW * 64 + wv * 64;
+  const int db = db_i * NW * 32 + wv * 32;
   const int KB = I / 32;
 
   const uint8_t* __restrict__ wb = wd + static_cast<size_t>(e) * H * I;
   const uint8_t* __restrict__ wsb = wds + static_cast<size_t>(e) * H * KB;
   const uint8_t* __restrict__ hb = h + static_cast<size_t>(rbase) * I;
   const uint8_t* __restrict__ hsb = hs + static_cast<size_t>(rbase) * KB;
-  uint32_t ow[4], osw[4];
+  uint32_t ow[2], osw[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < 2; ++q) {
     const int row = db + 16 * q + col;
     ow[q] = static_cast<uint32_t>(row * I + 16 * grp);
     osw[q] = static_cast<uint32_t>(row * KB + grp);
   }
   uint32_t ohl[LPT];
   int lrow[LPT];
+  bool lact[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int c = tid + i * NT, r = c / kMCH;
-    lrow[i] = r * kMRS + (c % kMCH) * 16;
-    ohl[i] = static_cast<uint32_t>((r < mcount ? r : 0) * I + (c % kMCH) * 16);
+    lact[i] = c < kBM * kMCH;
+    lrow[i] = lact[i] ? r * kMRS + (c % kMCH) * 16 : 0;
+    ohl[i] = static_cast<uint32_t>((lact[i] && r < mcount ? r : 0) * I + (c % kMCH) * 16);
   }
   const bool sload = tid < kBM;
   const uint32_t osl = sload ? static_cast<uint32_t>((tid < mcount ? tid : 0) * KB) : 0u;
@@ -688,37 +683,33 @@ __global__ __launch_bounds__(NW * 64) void gemm_down_mx(
   for (int i = 0; i < LPT; ++i) hr_[i] = ld16(hb + ohl[i]);
   if (sload) sr = *reinterpret_cast<const uint2*>(hsb + osl);
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&hl[0][lrow[i]]) = hr_[i];
+  for (int i = 0; i < LPT; ++i)
+    if (lact[i]) *reinterpret_cast<i32x4*>(&hl[0][lrow[i]]) = hr_[i];
   if (sload) *reinterpret_cast<uint2*>(&sl[0][tid * kMSC]) = sr;
 
-  f32x4 acc[4][4];
+  f32x4 acc[2][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  i32x8 a0[4], a1[4];
-  int sa0[4], sa1[4];
+  i32x8 a0[2], a1[2];
+  int sa0[2], sa1[2];
 #define DNM_W(A, SA, KC)                                                           \
   {                                                                                \
     const int ko_ = (KC) * 128, so_ = (KC) * 4;                                    \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                \
       A[q] = cat8(ld16(wb + ow[q] + ko_), ld16(wb + ow[q] + ko_ + 64));            \
       SA[q] = wsb[osw[q] + so_];                                                   \
     }                                                                              \
   }
 #define DNM_MMA(A, SA, CL)                                                         \
-  {                                                                                \
-    i32x8 bb[4];                                                                   \
-    int sb[4];                                                                     \
-    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                \
-      const uint8_t* p_ = hcur + (16 * g) * kMRS + (CL) * 128;                     \
-      bb[g] = cat8(*reinterpret_cast<const i32x4*>(p_),                            \
-                   *reinterpret_cast<const i32x4*>(p_ + 64));                      \
-      sb[g] = scur[(16 * g) * kMSC + (CL) * 4];                                    \
-    }                                                                              \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                  \
-    _Pragma("unroll") for (int g = 0; g < 4; ++g)                                  \
-      acc[q][g] = mfma_mx16x16x128(A[q], bb[g], SA[q], sb[g], acc[q][g]);          \
+  _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                  \
+    const uint8_t* p_ = hcur + (16 * g) * kMRS + (CL) * 128;                       \
+    const i32x8 bb = cat8(*reinterpret_cast<const i32x4*>(p_),                     \
+                          *reinterpret_cast<const i32x4*>(p_ + 64));               \
+    const int sb = scur[(16 * g) * kMSC + (CL) * 4];                               \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q)                                  \
+      acc[q][g] = mfma_mx16x16x128(A[q], bb, SA[q], sb, acc[q][g]);                \
   }
   const int chunks = I / 128;
   DNM_W(a0, sa0, 0)
@@ -734,17 +725,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_down_mx(
     }
     const uint8_t* hcur = &hl[buf][col * kMRS + 16 * grp];
     const uint8_t* scur = &sl[buf][col * kMSC + grp];
-#pragma unroll
-    for (int cl = 0; cl < kMXC / 128; cl += 2) {
-      const int kc = st * (kMXC / 128) + cl;
-      DNM_W(a1, sa1, kc + 1)
-      DNM_MMA(a0, sa0, cl)
-      DNM_W(a0, sa0, min(kc + 2, chunks - 1))
-      DNM_MMA(a1, sa1, cl + 1)
-    }
+    const int kc = st * 2;
+    DNM_W(a1, sa1, kc + 1)
+    DNM_MMA(a0, sa0, 0)
+    DNM_W(a0, sa0, min(kc + 2, chunks - 1))
+    DNM_MMA(a1, sa1, 1)
     if (more) {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&hl[buf ^ 1][lrow[i]]) = hr_[i];
+      for (int i = 0; i < LPT; ++i)
+        if (lact[i]) *reinterpret_cast<i32x4*>(&hl[buf ^ 1][lrow[i]]) = hr_[i];
       if (sload) *reinterpret_cast<uint2*>(&sl[buf ^ 1][tid * kMSC]) = sr;
     }
     __syncthreads();
@@ -760,7 +749,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_down_mx(
       const float wt = w[t];
       uint16_t* orow = out + static_cast<size_t>(t) * H + db + 4 * grp;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 2; ++q) {
         uint2 v;
         v.x = f32_to_bf16_rne(wt * acc[q][g][0]) | (f32_to_bf16_rne(wt * acc[q][g][1]) << 16);
         v.y = f32_to_bf16_rne(wt * acc[q][g][2]) | (f32_to_bf16_rne(wt * acc[q][g][3]) << 16);
@@ -769,7 +758,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_down_mx(
     } else {
       float* yr = y + static_cast<size_t>(rbase + r) * H + db + 4 * grp;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(yr + 16 * q) = acc[q][g];
+      for (int q = 0; q < 2; ++q) *reinterpret_cast<f32x4*>(yr + 16 * q) = acc[q][g];
     }
   }
 }
@@ -808,8 +797,8 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
   hipLaunchKernelGGL(group_experts, dim3(E), dim3(1024), 0, s, idx, P, E, kBM, p.counts,
                      p.offsets, p.tiles, p.n_tiles, p.perm, p.row_of);
   prof_end(kGroup, s);
-  constexpr int NW = 8;                              // 256 neurons per workgroup
-  const int n_items = round_up((I / (NW * 32)) * L.max_tiles, kXcds);
+  constexpr int NW = 8;          // BF16: 8 waves x 32 neurons; MXFP8: 8 waves x 16 neurons
+  const int n_items = round_up((I / (dtype == 0 ? NW * 32 : NW * 16)) * L.max_tiles, kXcds);
   prof_begin(kGemmGateUp, s);
   if (dtype == 0)
     hipLaunchKernelGGL(gemm_gate_up_bf16<NW>, dim3(n_items), dim3(NW * 64), 0, s,
@@ -831,10 +820,12 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   (void)idx; (void)num_cus;
   const BatchedWs L = batched_ws_layout(T, H, I, E, k, dtype);
   const BatchedPtrs p = batched_ptrs(ws, L);
-  const bool wide = H % 512 == 0;                    // 8 waves x 64 dims, else 4 waves
-  const int nw = wide ? 8 : 4;
-  const int n_items = round_up((H / (nw * 64)) * L.max_tiles, kXcds);
-  const dim3 grid(n_items), block(nw * 64);
+  // output dims per workgroup: BF16 8 waves x 64 (4 x 64 when H is not a
+  // multiple of 512); MXFP8 8 waves x 32
+  const bool wide = dtype == 0 && H % 512 == 0;
+  const int dims = dtype == 0 ? (wide ? 512 : 256) : 256;
+  const int n_items = round_up((H / dims) * L.max_tiles, kXcds);
+  const dim3 grid(n_items), block(dtype == 0 ? dims : 512);
 #define DOWN_BF16(F, NWV)                                                                   \
   hipLaunchKernelGGL((gemm_down_bf16<F, NWV>), grid, block, 0, s,                          \
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),       \
@@ -848,8 +839,8 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
     if (k == 1) { if (wide) DOWN_BF16(true, 8); else DOWN_BF16(true, 4); }
     else { if (wide) DOWN_BF16(false, 8); else DOWN_BF16(false, 4); }
   } else {
-    if (k == 1) { if (wide) DOWN_MX(true, 8); else DOWN_MX(true, 4); }
-    else { if (wide) DOWN_MX(false, 8); else DOWN_MX(false, 4); }
+    if (k == 1) DOWN_MX(true, 8);
+    else DOWN_MX(false, 8);
   }
 #undef DOWN_BF16
 #undef DOWN_MX
