@@ -24,22 +24,26 @@
 // L2): workgroups are dispatched to the 8 XCDs round-robin by linear id.
 #include "common.h"
 #include "internal.h"
+#include "tiles.h"
 
 namespace moe {
 
 namespace {
 constexpr int kBM = 64;            // rows (routed pairs) per M-tile
-constexpr int kXcds = 8;
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 }  // namespace
 
+bool use_large_tiles(int T, int H, int I, int E, int k, int dtype) {
+  const int64_t P = static_cast<int64_t>(T) * k;
+  return dtype == 0 && P >= static_cast<int64_t>(kLargeBM) * E && H % 256 == 0 && I % 128 == 0;
+}
+
 BatchedWs batched_ws_layout(int T, int H, int I, int E, int k, int dtype) {
-  (void)I;
-  (void)dtype;
   BatchedWs L{};
   const size_t P = static_cast<size_t>(T) * k;
-  L.max_tiles = static_cast<int>(E + (P + kBM - 1) / kBM);
+  L.bm = use_large_tiles(T, H, I, E, k, dtype) ? kLargeBM : kBM;
+  L.max_tiles = static_cast<int>(E + (P + L.bm - 1) / L.bm);
   size_t o = 0;
   L.n_tiles = o;   o += 256;
   L.counts = o;    o = align256(o + sizeof(int) * E);
@@ -131,25 +135,6 @@ __global__ __launch_bounds__(1024) void group_experts(
     running += total;
     __syncthreads();
   }
-}
-
-// ---------------------------------------------------------------------------
-// Work-item order: item L of a 1-D grid (dispatched to XCD L % 8) takes the
-// (L % 8)-th eighth of the item space, so consecutive items - the N-blocks of
-// one M-tile - share an XCD.  n_items must be a multiple of 8.
-__device__ __forceinline__ int xcd_item(int L, int n_items) {
-  return (L % kXcds) * (n_items / kXcds) + L / kXcds;
-}
-
-// The grid is sized for the most M-tiles any routing can produce; the real
-// count is known on the device only.  Workgroups past the real items exit,
-// and the XCD remap runs over the real item space so every XCD gets an equal
-// share.  Returns -1 for a workgroup with nothing to do.
-__device__ __forceinline__ int real_item(int L, int nblk, int n_tiles) {
-  const int n_real = (nblk * n_tiles + kXcds - 1) / kXcds * kXcds;
-  if (L >= n_real) return -1;
-  const int item = xcd_item(L, n_real);
-  return item / nblk < n_tiles ? item : -1;
 }
 
 // gate_up, BF16: workgroup = (M-tile, NW*32 neurons); wave = 32 neurons (16
@@ -794,9 +779,17 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
   const BatchedPtrs p = batched_ptrs(ws, L);
   const int P = T * k;
   prof_begin(kGroup, s);
-  hipLaunchKernelGGL(group_experts, dim3(E), dim3(1024), 0, s, idx, P, E, kBM, p.counts,
+  hipLaunchKernelGGL(group_experts, dim3(E), dim3(1024), 0, s, idx, P, E, L.bm, p.counts,
                      p.offsets, p.tiles, p.n_tiles, p.perm, p.row_of);
   prof_end(kGroup, s);
+  if (L.bm == kLargeBM) {
+    prof_begin(kGemmGateUp, s);
+    const hipError_t e = launch_gate_up_large_bf16(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm, p.tiles,
+        p.n_tiles, p.counts, p.offsets, H, I, k, static_cast<uint16_t*>(h), L.max_tiles, s);
+    prof_end(kGemmGateUp, s);
+    return e;
+  }
   constexpr int NW = 8;          // BF16: 8 waves x 32 neurons; MXFP8: 8 waves x 16 neurons
   const int n_items = round_up((I / (dtype == 0 ? NW * 32 : NW * 16)) * L.max_tiles, kXcds);
   prof_begin(kGemmGateUp, s);
@@ -820,6 +813,21 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   (void)idx; (void)num_cus;
   const BatchedWs L = batched_ws_layout(T, H, I, E, k, dtype);
   const BatchedPtrs p = batched_ptrs(ws, L);
+  if (L.bm == kLargeBM) {
+    prof_begin(kGemmDown, s);
+    hipError_t e = launch_down_large_bf16(static_cast<const uint16_t*>(h),
+                                          static_cast<const uint16_t*>(wd), p.perm, p.tiles,
+                                          p.n_tiles, p.counts, p.offsets, w, H, I, k, p.y, out,
+                                          L.max_tiles, s);
+    prof_end(kGemmDown, s);
+    if (e == hipSuccess && k > 1) {
+      prof_begin(kCombine, s);
+      hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out);
+      prof_end(kCombine, s);
+      e = hipGetLastError();
+    }
+    return e;
+  }
   // output dims per workgroup: BF16 8 waves x 64 (4 x 64 when H is not a
   // multiple of 512); MXFP8 8 waves x 32
   const bool wide = dtype == 0 && H % 512 == 0;
@@ -865,6 +873,6 @@ hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* co
   return hipGetLastError();
 }
 
-hipError_t batched_set_attributes() { return hipSuccess; }
+hipError_t batched_set_attributes() { return large_set_attributes(); }
 
 }  // namespace moe
