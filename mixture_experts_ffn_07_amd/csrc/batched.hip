@@ -53,6 +53,8 @@ BatchedWs batched_ws_layout(int T, int H, int I, int E, int k, int dtype) {
   L.row_of = o;    o = align256(o + sizeof(int) * P);
   L.y = o;
   if (k > 1) o = align256(o + sizeof(float) * P * H);
+  L.partial = o;
+  if (L.bm == kLargeBM) o = align256(o + sizeof(float) * kLargeMaxSlices * kLargeBM * 256);
   L.total = o;
   return L;
 }
@@ -753,7 +755,7 @@ namespace {
 struct BatchedPtrs {
   int *n_tiles, *counts, *offsets, *perm, *row_of;
   int2* tiles;
-  float* y;
+  float *y, *partial;
 };
 BatchedPtrs batched_ptrs(void* ws, const BatchedWs& L) {
   char* b = static_cast<char*>(ws);
@@ -765,6 +767,7 @@ BatchedPtrs batched_ptrs(void* ws, const BatchedWs& L) {
   p.perm = reinterpret_cast<int*>(b + L.perm);
   p.row_of = reinterpret_cast<int*>(b + L.row_of);
   p.y = reinterpret_cast<float*>(b + L.y);
+  p.partial = reinterpret_cast<float*>(b + L.partial);
   return p;
 }
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
@@ -774,7 +777,6 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
                                   const uint8_t* wgus, const int32_t* idx, int T, int H, int I,
                                   int E, int k, int dtype, void* h, uint8_t* hs, void* ws,
                                   hipStream_t s, int num_cus) {
-  (void)num_cus;
   const BatchedWs L = batched_ws_layout(T, H, I, E, k, dtype);
   const BatchedPtrs p = batched_ptrs(ws, L);
   const int P = T * k;
@@ -786,7 +788,8 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
     prof_begin(kGemmGateUp, s);
     const hipError_t e = launch_gate_up_large_bf16(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm, p.tiles,
-        p.n_tiles, p.counts, p.offsets, H, I, k, static_cast<uint16_t*>(h), L.max_tiles, s);
+        p.n_tiles, p.counts, p.offsets, H, I, k, static_cast<uint16_t*>(h), p.partial,
+        L.max_tiles, num_cus, s);
     prof_end(kGemmGateUp, s);
     return e;
   }
@@ -810,7 +813,7 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
                                const uint8_t* wds, const int32_t* idx, const float* w, int T,
                                int H, int I, int E, int k, int dtype, uint16_t* out, void* ws,
                                hipStream_t s, int num_cus) {
-  (void)idx; (void)num_cus;
+  (void)idx;
   const BatchedWs L = batched_ws_layout(T, H, I, E, k, dtype);
   const BatchedPtrs p = batched_ptrs(ws, L);
   if (L.bm == kLargeBM) {
@@ -818,7 +821,7 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
     hipError_t e = launch_down_large_bf16(static_cast<const uint16_t*>(h),
                                           static_cast<const uint16_t*>(wd), p.perm, p.tiles,
                                           p.n_tiles, p.counts, p.offsets, w, H, I, k, p.y, out,
-                                          L.max_tiles, s);
+                                          p.partial, L.max_tiles, num_cus, s);
     prof_end(kGemmDown, s);
     if (e == hipSuccess && k > 1) {
       prof_begin(kCombine, s);

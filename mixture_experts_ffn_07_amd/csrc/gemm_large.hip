@@ -35,12 +35,80 @@ constexpr int kLTile = kLargeBM * kLBK;      // elements per operand stage (256 
 constexpr size_t kLLds = 2 * 2 * kLTile * sizeof(uint16_t);   // 128 KB
 enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2 };
 
+// Tail split.  One workgroup fills a CU, so n items run in ceil(n / ncu)
+// rounds; when the last round would leave more than half of the CUs idle, its
+// items are cut along K into S slices that run side by side.  Each slice
+// writes its FP32 partial tile to the workspace and gemm_large_fixup adds the
+// S partials of an item in slice order (fixed, so results stay bit-identical
+// run to run) before the usual epilogue.  Items before `full` run whole.
+struct TailPlan {
+  int full, rem, S;
+};
+__device__ __forceinline__ TailPlan tail_plan(int n_real, int ncu, int nk) {
+  TailPlan p;
+  const int rounds = n_real / ncu;
+  p.rem = n_real - rounds * ncu;
+  p.S = 1;
+  if (p.rem > 0 && 2 * p.rem <= ncu && ncu % kXcds == 0)
+    p.S = max(1, min(min(8, ncu / p.rem), min(nk / 2, kLargeMaxSlices / p.rem)));
+  p.full = p.S > 1 ? rounds * ncu : n_real;
+  return p;
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 // s_waitcnt with only the LDS/scalar counter constrained to 0
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 }  // namespace
+
+// Epilogue of a 256 x 256 tile (see gemm_large_bf16 for the register layout).
+template <int KIND>
+__device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const int* __restrict__ perm,
+                                               const float* __restrict__ w, int H, int I, int rbase,
+                                               int mcount, int nb, int wm, int wn, int l32, int hi,
+                                               uint16_t* __restrict__ hout, float* __restrict__ y,
+                                               uint16_t* __restrict__ out) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wm * 128 + 32 * j + l32;
+    if (r >= mcount) continue;
+    if (KIND == kGateUp) {
+      uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb * 128 + wn * 64 + 4 * hi;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t p[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            p[t] = f32_to_bf16_rne(swiglu(acc[i][j][4 * q + t], acc[i + 2][j][4 * q + t]));
+          *reinterpret_cast<uint2*>(hr + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+        }
+    } else if (KIND == kDownFused) {
+      const int t = perm[rbase + r];        // k = 1: pair id == token
+      const float wt_t = w[t];
+      uint16_t* orow = out + static_cast<size_t>(t) * H + nb * 256 + wn * 128 + 4 * hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t p[4];
+#pragma unroll
+          for (int t4 = 0; t4 < 4; ++t4) p[t4] = f32_to_bf16_rne(wt_t * acc[i][j][4 * q + t4]);
+          *reinterpret_cast<uint2*>(orow + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+        }
+    } else {
+      float* yr = y + static_cast<size_t>(rbase + r) * H + nb * 256 + wn * 128 + 4 * hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(yr + 32 * i + 8 * q) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    }
+  }
+}
 
 // KIND kGateUp:    act = x [T,H], wt = W_gate_up [E,2I,H]; writes h [P,I] (sorted rows, BF16).
 // KIND kDown*:     act = h [P,I] (sorted rows), wt = W_down [E,H,I]; kDownFused (k = 1)
@@ -55,13 +123,30 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint16_t* __restrict__ hout, float* __restrict__ y,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, float* __restrict__ partial, int ncu) {
   extern __shared__ __align__(16) uint16_t lds[];   // [stage][A, B][256 x 64]
   constexpr bool kGU = KIND == kGateUp;
   const int K = kGU ? H : I;
   const int nblk = kGU ? I / 128 : H / 256;
-  const int item = real_item(blockIdx.x, nblk, *n_tiles);
-  if (item < 0) return;
+  const int nk = K / kLBK;
+  const int n_real = nblk * *n_tiles;
+  const TailPlan plan = tail_plan(n_real, ncu, nk);
+  const int L = blockIdx.x;
+  int item, kb = 0, ke = nk, slot = -1;
+  if (plan.S > 1 && L < plan.full) {
+    item = xcd_item(L, plan.full);
+  } else if (plan.S > 1) {
+    const int t = L - plan.full;
+    if (t >= plan.rem * plan.S) return;
+    item = plan.full + t % plan.rem;
+    const int sl = t / plan.rem;
+    kb = sl * nk / plan.S;
+    ke = (sl + 1) * nk / plan.S;
+    slot = t;
+  } else {
+    item = real_item(L, nblk, *n_tiles);
+    if (item < 0) return;
+  }
   const int tile = item / nblk, nb = item - tile * nblk;
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
@@ -95,7 +180,6 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
   }
   // LDS: row r, 16-byte chunk c at r*64 + ((c ^ (r & 7)) * 8); here r & 7 == lrow
   const int lw = (wv * 64 + lrow) * kLBK + ((lc ^ lrow) * 8);
-  const int nk = K / kLBK;
   // fragment rows of this wave
   int fa[4];
 #pragma unroll
@@ -106,7 +190,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
 
   i32x4 stg[16];   // [0..7] weight rows, [8..15] activation rows
 #define GLOAD(Q, KT) do {                                                               \
-    const uint32_t kk_ = static_cast<uint32_t>(min((KT), nk - 1) * kLBK);               \
+    const uint32_t kk_ = static_cast<uint32_t>(min((KT), ke - 1) * kLBK);               \
     if ((Q) < 8) stg[Q] = ld16(abase + ao + static_cast<uint32_t>((Q) * 8) * K + kk_);  \
     else stg[Q] = ld16(act + bo[(Q) - 8] + kk_);                                        \
   } while (0)
@@ -145,21 +229,22 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
   // prologue: stage 0 into LDS buffer 0, stage 1 into the staging registers
 #pragma unroll
-  for (int q = 0; q < 16; ++q) GLOAD(q, 0);
+  for (int q = 0; q < 16; ++q) GLOAD(q, kb);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) LWRITE(q, 0);
+  for (int q = 0; q < 16; ++q) LWRITE(q, kb);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) GLOAD(q, 1);
+  for (int q = 0; q < 16; ++q) GLOAD(q, kb + 1);
   __syncthreads();
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   {
+    const uint16_t* at = lds + (kb & 1) * 2 * kLTile;
     const int so = (hi ^ swz) * 8;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) a0[g] = RDF(&lds[fa[g] + so]);
+    for (int g = 0; g < 4; ++g) a0[g] = RDF(&at[fa[g] + so]);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) b0[g] = RDF(&lds[kLTile + fb + 32 * g * kLBK + so]);
+    for (int g = 0; g < 4; ++g) b0[g] = RDF(&at[kLTile + fb + 32 * g * kLBK + so]);
   }
-  for (int kt = 0; kt < nk; ++kt) {
+  for (int kt = kb; kt < ke; ++kt) {
     PHASE(a0, b0, a1, b1, kt, 1, kt, 0, 6);
     PHASE(a1, b1, a0, b0, kt, 2, kt, 6, 5);
     PHASE(a0, b0, a1, b1, kt, 3, kt, 11, 5);
@@ -173,69 +258,114 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
 #undef RDF
 #undef PHASE
 
-  // epilogue
+  if (slot >= 0) {
+    // tail slice: FP32 partial tile in register order, [64 x f32x4][256 threads]
+    f32x4* pp = reinterpret_cast<f32x4*>(partial) + static_cast<size_t>(slot) * 64 * 256 + tid;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = wm * 128 + 32 * j + l32;
-    if (r >= mcount) continue;
-    if (kGU) {
-      uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb * 128 + wn * 64 + 4 * hi;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t p[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            p[t] = f32_to_bf16_rne(swiglu(acc[i][j][4 * q + t], acc[i + 2][j][4 * q + t]));
-          *reinterpret_cast<uint2*>(hr + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
-        }
-    } else if (KIND == kDownFused) {
-      const int t = perm[rbase + r];        // k = 1: pair id == token
-      const float wt_t = w[t];
-      uint16_t* orow = out + static_cast<size_t>(t) * H + nb * 256 + wn * 128 + 4 * hi;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t p[4];
-#pragma unroll
-          for (int t4 = 0; t4 < 4; ++t4) p[t4] = f32_to_bf16_rne(wt_t * acc[i][j][4 * q + t4]);
-          *reinterpret_cast<uint2*>(orow + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
-        }
-    } else {
-      float* yr = y + static_cast<size_t>(rbase + r) * H + nb * 256 + wn * 128 + 4 * hi;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4*>(yr + 32 * i + 8 * q) =
+          pp[((i * 4 + j) * 4 + q) * 256] =
               f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-    }
+    return;
+  }
+  large_epilogue<KIND>(acc, perm, w, H, I, rbase, mcount, nb, wm, wn, l32, hi, hout, y, out);
+}
+
+// Tail fix-up, element-parallel: thread g of the grid takes one f32x4 of the
+// partial tile (register order: f32x4 index ((i*4 + j)*4 + q)*256 + tid of the
+// GEMM's thread tid) of tail item full + g / per_item, adds it over the S
+// slices in slice order and applies that piece of the epilogue.  gate_up pairs
+// gate block i with up block i + 2, so one thread takes both (i < 2).
+template <int KIND>
+__global__ __launch_bounds__(256) void gemm_large_fixup(
+    const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
+    const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
+    int H, int I, uint16_t* __restrict__ hout, float* __restrict__ y, uint16_t* __restrict__ out,
+    const float* __restrict__ partial, int ncu) {
+  constexpr bool kGU = KIND == kGateUp;
+  constexpr int kPerItem = kGU ? 32 * 256 : 64 * 256;   // threads per tail item
+  const int nblk = kGU ? I / 128 : H / 256;
+  const int nk = (kGU ? H : I) / kLBK;
+  const TailPlan plan = tail_plan(nblk * *n_tiles, ncu, nk);
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  const int b = g / kPerItem;
+  if (plan.S == 1 || b >= plan.rem) return;
+  const int f = g - b * kPerItem;            // f32x4 index within the tile (gate half for gate_up)
+  const int tid = f & 255, ijq = f >> 8;     // GEMM thread and register block
+  const int i = ijq >> 4, j = (ijq >> 2) & 3, q = ijq & 3;
+  const int item = plan.full + b;
+  const int tile = item / nblk, nb = item - tile * nblk;
+  const int2 te = tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int mcount = min(kLargeBM, counts[e] - m0);
+  const int rbase = offsets[e] + m0;
+  const int wv = tid >> 6, ln = tid & 63, l32 = ln & 31, hi = ln >> 5;
+  const int wm = wv & 1, wn = wv >> 1;
+  const int r = wm * 128 + 32 * j + l32;
+  if (r >= mcount) return;
+  const f32x4* pp = reinterpret_cast<const f32x4*>(partial) + f;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+  for (int sl = 0; sl < plan.S; ++sl) {
+    const size_t base = static_cast<size_t>(sl * plan.rem + b) * 64 * 256;
+    a += pp[base];
+    if (kGU) u += pp[base + 2 * 16 * 256];   // up block i + 2
+  }
+  if (kGU) {
+    uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb * 128 + wn * 64 + 32 * i + 8 * q + 4 * hi;
+    uint32_t p[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) p[t] = f32_to_bf16_rne(swiglu(a[t], u[t]));
+    *reinterpret_cast<uint2*>(hr) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+  } else if (KIND == kDownFused) {
+    const int t = perm[rbase + r];
+    const float wt_t = w[t];
+    uint16_t* o = out + static_cast<size_t>(t) * H + nb * 256 + wn * 128 + 32 * i + 8 * q + 4 * hi;
+    uint32_t p[4];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) p[t4] = f32_to_bf16_rne(wt_t * a[t4]);
+    *reinterpret_cast<uint2*>(o) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+  } else {
+    *reinterpret_cast<f32x4*>(y + static_cast<size_t>(rbase + r) * H + nb * 256 + wn * 128 + 32 * i +
+                              8 * q + 4 * hi) = a;
   }
 }
+
+namespace {
+// grid: every item whole, plus room for the tail slices (rem * S - rem < ncu)
+int large_grid(int nblk, int max_tiles, int ncu) {
+  return (nblk * max_tiles + ncu + kXcds - 1) / kXcds * kXcds;
+}
+}  // namespace
 
 hipError_t launch_gate_up_large_bf16(const uint16_t* x, const uint16_t* wgu, const int* perm,
                                      const int2* tiles, const int* n_tiles, const int* counts,
                                      const int* offsets, int H, int I, int k, uint16_t* h,
-                                     int max_tiles, hipStream_t s) {
-  const int n_items = ((I / 128) * max_tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(gemm_large_bf16<kGateUp>, dim3(n_items), dim3(256), kLLds, s, x, wgu, perm,
-                     tiles, n_tiles, counts, offsets, nullptr, H, I, k, h, nullptr, nullptr);
+                                     float* partial, int max_tiles, int ncu, hipStream_t s) {
+  const int grid = large_grid(I / 128, max_tiles, ncu);
+  hipLaunchKernelGGL(gemm_large_bf16<kGateUp>, dim3(grid), dim3(256), kLLds, s, x, wgu, perm,
+                     tiles, n_tiles, counts, offsets, nullptr, H, I, k, h, nullptr, nullptr,
+                     partial, ncu);
+  hipLaunchKernelGGL(gemm_large_fixup<kGateUp>, dim3(ncu / 2 * 32), dim3(256), 0, s, perm, tiles,
+                     n_tiles, counts, offsets, nullptr, H, I, h, nullptr, nullptr, partial, ncu);
   return hipGetLastError();
 }
 
 hipError_t launch_down_large_bf16(const uint16_t* h, const uint16_t* wd, const int* perm,
                                   const int2* tiles, const int* n_tiles, const int* counts,
                                   const int* offsets, const float* w, int H, int I, int k,
-                                  float* y, uint16_t* out, int max_tiles, hipStream_t s) {
-  const int n_items = ((H / 256) * max_tiles + kXcds - 1) / kXcds * kXcds;
-  if (k == 1)
-    hipLaunchKernelGGL(gemm_large_bf16<kDownFused>, dim3(n_items), dim3(256), kLLds, s, h, wd,
-                       perm, tiles, n_tiles, counts, offsets, w, H, I, k, nullptr, y, out);
-  else
-    hipLaunchKernelGGL(gemm_large_bf16<kDownSlots>, dim3(n_items), dim3(256), kLLds, s, h, wd,
-                       perm, tiles, n_tiles, counts, offsets, w, H, I, k, nullptr, y, out);
+                                  float* y, uint16_t* out, float* partial, int max_tiles, int ncu,
+                                  hipStream_t s) {
+  const int grid = large_grid(H / 256, max_tiles, ncu);
+#define LARGE_DOWN(KD)                                                                        \
+  hipLaunchKernelGGL(gemm_large_bf16<KD>, dim3(grid), dim3(256), kLLds, s, h, wd, perm, tiles, \
+                     n_tiles, counts, offsets, w, H, I, k, nullptr, y, out, partial, ncu);    \
+  hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
+                     n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu)
+  if (k == 1) { LARGE_DOWN(kDownFused); } else { LARGE_DOWN(kDownSlots); }
+#undef LARGE_DOWN
   return hipGetLastError();
 }
 

@@ -43,23 +43,27 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
 // Byte layout of the batched workspace.  bm = rows per M-tile (64, or
 // kLargeBM when the large-group GEMMs run).
 struct BatchedWs {
-  size_t counts, offsets, perm, row_of, tiles, n_tiles, y, total;
+  size_t counts, offsets, perm, row_of, tiles, n_tiles, y, partial, total;
   int max_tiles, bm;
 };
 BatchedWs batched_ws_layout(int T, int H, int I, int E, int k, int dtype);
 
 // Large-group GEMMs (gemm_large.hip): chosen when the routed rows per expert
 // average at least kLargeBM, i.e. when the projections are MFMA-bound.
+// Tail items may be split along K into at most kLargeMaxSlices FP32 partial
+// tiles of 256 x 256 (the `partial` workspace region).
 constexpr int kLargeBM = 256;
+constexpr int kLargeMaxSlices = 256;
 bool use_large_tiles(int T, int H, int I, int E, int k, int dtype);
 hipError_t launch_gate_up_large_bf16(const uint16_t* x, const uint16_t* wgu, const int* perm,
                                      const int2* tiles, const int* n_tiles, const int* counts,
                                      const int* offsets, int H, int I, int k, uint16_t* h,
-                                     int max_tiles, hipStream_t s);
+                                     float* partial, int max_tiles, int ncu, hipStream_t s);
 hipError_t launch_down_large_bf16(const uint16_t* h, const uint16_t* wd, const int* perm,
                                   const int2* tiles, const int* n_tiles, const int* counts,
                                   const int* offsets, const float* w, int H, int I, int k,
-                                  float* y, uint16_t* out, int max_tiles, hipStream_t s);
+                                  float* y, uint16_t* out, float* partial, int max_tiles, int ncu,
+                                  hipStream_t s);
 hipError_t large_set_attributes();
 
 hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* codes,

@@ -73,3 +73,15 @@ def test_large_h_rows_grouped(M):
     got = h.float().cpu().double().numpy()
     rel = np.linalg.norm(got - want) / np.linalg.norm(want)
     assert rel < 5e-3, rel
+
+
+def test_large_whole_rounds_without_split(M):
+    # tokens dealt round-robin to 4 experts: 1,024 rows each = 4 tiles, so gate_up has
+    # exactly 16 tiles x 16 N-blocks = 256 items (no tail to split), down 16 items (split)
+    T, E = 4096, 4
+    d = _custom(T, 256, 2048, E, 1, seed=21)
+    lg = torch.full((T, E), -4.0, device="cuda")
+    lg[torch.arange(T), torch.arange(T) % E] = 4.0
+    d["logits"] = lg.contiguous()
+    tokens = np.sort(np.random.default_rng(2).choice(T, size=192, replace=False))
+    _check(M, d, "large: whole rounds (no tail split)", tokens=tokens)
