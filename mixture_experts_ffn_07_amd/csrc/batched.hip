@@ -36,7 +36,8 @@ inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255);
 
 bool use_large_tiles(int T, int H, int I, int E, int k, int dtype) {
   const int64_t P = static_cast<int64_t>(T) * k;
-  return dtype == 0 && P >= static_cast<int64_t>(kLargeBM) * E && H % 256 == 0 && I % 128 == 0;
+  return (dtype == 0 || dtype == 1) && P >= static_cast<int64_t>(kLargeBM) * E && H % 256 == 0 &&
+         I % 128 == 0;
 }
 
 BatchedWs batched_ws_layout(int T, int H, int I, int E, int k, int dtype) {
@@ -786,10 +787,17 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
   prof_end(kGroup, s);
   if (L.bm == kLargeBM) {
     prof_begin(kGemmGateUp, s);
-    const hipError_t e = launch_gate_up_large_bf16(
-        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm, p.tiles,
-        p.n_tiles, p.counts, p.offsets, H, I, k, static_cast<uint16_t*>(h), p.partial,
-        L.max_tiles, num_cus, s);
+    const hipError_t e =
+        dtype == 0
+            ? launch_gate_up_large_bf16(static_cast<const uint16_t*>(x),
+                                        static_cast<const uint16_t*>(wgu), p.perm, p.tiles,
+                                        p.n_tiles, p.counts, p.offsets, H, I, k,
+                                        static_cast<uint16_t*>(h), p.partial, L.max_tiles, num_cus, s)
+            : launch_gate_up_large_mx(static_cast<const uint8_t*>(x), xs,
+                                      static_cast<const uint8_t*>(wgu), wgus, p.perm, p.tiles,
+                                      p.n_tiles, p.counts, p.offsets, H, I, k,
+                                      static_cast<uint8_t*>(h), hs, p.partial, L.max_tiles,
+                                      num_cus, s);
     prof_end(kGemmGateUp, s);
     return e;
   }
@@ -818,10 +826,16 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   const BatchedPtrs p = batched_ptrs(ws, L);
   if (L.bm == kLargeBM) {
     prof_begin(kGemmDown, s);
-    hipError_t e = launch_down_large_bf16(static_cast<const uint16_t*>(h),
-                                          static_cast<const uint16_t*>(wd), p.perm, p.tiles,
-                                          p.n_tiles, p.counts, p.offsets, w, H, I, k, p.y, out,
-                                          p.partial, L.max_tiles, num_cus, s);
+    hipError_t e =
+        dtype == 0
+            ? launch_down_large_bf16(static_cast<const uint16_t*>(h),
+                                     static_cast<const uint16_t*>(wd), p.perm, p.tiles, p.n_tiles,
+                                     p.counts, p.offsets, w, H, I, k, p.y, out, p.partial,
+                                     L.max_tiles, num_cus, s)
+            : launch_down_large_mx(static_cast<const uint8_t*>(h), hs,
+                                   static_cast<const uint8_t*>(wd), wds, p.perm, p.tiles,
+                                   p.n_tiles, p.counts, p.offsets, w, H, I, k, p.y, out,
+                                   p.partial, L.max_tiles, num_cus, s);
     prof_end(kGemmDown, s);
     if (e == hipSuccess && k > 1) {
       prof_begin(kCombine, s);

@@ -284,11 +284,10 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, uint16_t* __restrict__ hout, float* __restrict__ y, uint16_t* __restrict__ out,
-    const float* __restrict__ partial, int ncu) {
+    const float* __restrict__ partial, int ncu, int nk) {
   constexpr bool kGU = KIND == kGateUp;
   constexpr int kPerItem = kGU ? 32 * 256 : 64 * 256;   // threads per tail item
   const int nblk = kGU ? I / 128 : H / 256;
-  const int nk = (kGU ? H : I) / kLBK;
   const TailPlan plan = tail_plan(nblk * *n_tiles, ncu, nk);
   const int g = blockIdx.x * 256 + threadIdx.x;
   const int b = g / kPerItem;
@@ -333,6 +332,296 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
   }
 }
 
+
+// SwiGLU + MX quantization of one 32-neuron block of one token row: the lane
+// pair (l32, hi = 0/1) holds neurons 8q + 4hi + t (register 4q + t) of gate
+// block g and up block u.  Scale from the block's amax (OCP Microscaling v1.0
+// rule), codes E4M3 of v * 2^-s; the hi = 0 lane writes the scale byte.  Both
+// lanes of a pair always take the same branch (same row).
+__device__ __forceinline__ void mx_store_block(const f32x16& g, const f32x16& u, int r, int mcount,
+                                               int rbase, int n, int hi, int I,
+                                               uint8_t* __restrict__ hq, uint8_t* __restrict__ hs) {
+  if (r >= mcount) return;
+  float v[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    v[x] = swiglu(g[x], u[x]);
+    amax = fmaxf(amax, fabsf(v[x]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+  const int sx = mx_scale_exp(amax);
+  const float inv = exp2_neg(sx);
+  uint8_t* hr = hq + static_cast<size_t>(rbase + r) * I + n + 4 * hi;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c |= f32_to_e4m3(v[4 * q + t] * inv) << (8 * t);
+    *reinterpret_cast<uint32_t*>(hr + 8 * q) = c;
+  }
+  if (hi == 0) hs[static_cast<size_t>(rbase + r) * (I / 32) + n / 32] = static_cast<uint8_t>(sx + 127);
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 (E4M3 codes, one E8M0 scale per 32 along K).  Same tile, waves and
+// pipeline as the BF16 kernel, in bytes: a stage is 128 K (128-byte row
+// segments, the same LDS layout), plus the stage's 4 scale bytes of each of the
+// 256 rows of both operands (one dword per row).  MFMA
+// v_mfma_scale_f32_32x32x64_f8f6f4: lane (l32, hi) holds bytes [16hi, +16) of
+// K block 0 and of K block 1 of the 64-wide K step, and supplies the scale of
+// block hi of its row; so at K step ks of a stage, lane hi takes 16-byte
+// chunks 4ks + hi and 4ks + 2 + hi, and scale byte 2ks + hi of its row's dword
+// (shifted down by 8 hi, then selected with opsel 2ks).
+namespace {
+constexpr int kMBK = 128;                                  // K per stage
+constexpr int kMTile = kLargeBM * kMBK;                    // bytes per operand stage
+constexpr size_t kMLds = 2 * 2 * kMTile + 2 * 2 * kLargeBM * 4;   // data + scales: 132 KB
+
+template <int OPSEL>
+__device__ __forceinline__ f32x16 mfma_mx32(i32x8 a, i32x8 b, int sa, int sb, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, sa, OPSEL, sb);
+}
+}  // namespace
+
+// KIND kGateUp:  act = x codes [T,H] + scales [T,H/32]; wt = W_gate_up codes [E,2I,H] +
+//                scales [E,2I,H/32]; writes h codes [P,I] + scales [P,I/32] (sorted rows),
+//                quantized from the FP32 SwiGLU values.
+// KIND kDown*:   act = h codes + scales; wt = W_down codes [E,H,I] + scales [E,H,I/32].
+template <int KIND>
+__global__ __launch_bounds__(256) void gemm_large_mx(
+    const uint8_t* __restrict__ act, const uint8_t* __restrict__ act_s,
+    const uint8_t* __restrict__ wt, const uint8_t* __restrict__ wt_s,
+    const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
+    const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
+    int H, int I, int k, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
+    float* __restrict__ y, uint16_t* __restrict__ out, float* __restrict__ partial, int ncu) {
+  extern __shared__ __align__(16) uint8_t ldm[];   // [stage][A, B][256 x 128] then [stage][A, B][256] dwords
+  uint32_t* lsc = reinterpret_cast<uint32_t*>(ldm + 2 * 2 * kMTile);
+  constexpr bool kGU = KIND == kGateUp;
+  const int K = kGU ? H : I;
+  const int KSB = K / 32;                          // scale bytes per row
+  const int nblk = kGU ? I / 128 : H / 256;
+  const int nk = K / kMBK;
+  const int n_real = nblk * *n_tiles;
+  const TailPlan plan = tail_plan(n_real, ncu, nk);
+  const int L = blockIdx.x;
+  int item, kb = 0, ke = nk, slot = -1;
+  if (plan.S > 1 && L < plan.full) {
+    item = xcd_item(L, plan.full);
+  } else if (plan.S > 1) {
+    const int t = L - plan.full;
+    if (t >= plan.rem * plan.S) return;
+    item = plan.full + t % plan.rem;
+    const int sl = t / plan.rem;
+    kb = sl * nk / plan.S;
+    ke = (sl + 1) * nk / plan.S;
+    slot = t;
+  } else {
+    item = real_item(L, nblk, *n_tiles);
+    if (item < 0) return;
+  }
+  const int tile = item / nblk, nb = item - tile * nblk;
+  const int2 te = tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int mcount = min(kLargeBM, counts[e] - m0);
+  const int rbase = offsets[e] + m0;
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, l32 = ln & 31, hi = ln >> 5;
+  const int wm = wv & 1, wn = wv >> 1;
+
+  // data loader as in the BF16 kernel (16-byte chunk ln & 7 of rows wv*64 + 8j + (ln >> 3))
+  const int lrow = ln >> 3, lc = ln & 7;
+  const uint8_t* __restrict__ abase;
+  const uint8_t* __restrict__ asb;
+  uint32_t ao, so_a, so_b;
+  const int n0 = nb * 128;
+  if (kGU) {
+    abase = wt + static_cast<size_t>(e) * 2 * I * H;
+    asb = wt_s + static_cast<size_t>(e) * 2 * I * KSB;
+    ao = static_cast<uint32_t>(((wv < 2 ? n0 + wv * 64 : I + n0 + (wv - 2) * 64) + lrow) * H + lc * 16);
+    so_a = static_cast<uint32_t>((tid < 128 ? n0 + tid : I + n0 + tid - 128) * KSB);
+  } else {
+    abase = wt + static_cast<size_t>(e) * H * I;
+    asb = wt_s + static_cast<size_t>(e) * H * KSB;
+    ao = static_cast<uint32_t>((nb * 256 + wv * 64 + lrow) * I + lc * 16);
+    so_a = static_cast<uint32_t>((nb * 256 + tid) * KSB);
+  }
+  uint32_t bo[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = wv * 64 + 8 * j + lrow;
+    const int rr = r < mcount ? r : 0;
+    bo[j] = kGU ? static_cast<uint32_t>((perm[rbase + rr] / k) * H + lc * 16)
+                : static_cast<uint32_t>((rbase + rr) * I + lc * 16);
+  }
+  {
+    const int rr = tid < mcount ? tid : 0;         // scale loader: thread = tile row
+    so_b = static_cast<uint32_t>((kGU ? perm[rbase + rr] / k : rbase + rr) * KSB);
+  }
+  const int lw = (wv * 64 + lrow) * kMBK + ((lc ^ lrow) * 16);
+  int fa[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = (kGU ? (i >> 1) * 128 + wn * 64 + (i & 1) * 32 : wn * 128 + 32 * i) + l32;
+  const int fb = wm * 128 + l32;
+  const int swz = l32 & 7;
+
+  i32x4 stg[16];
+  uint32_t sst[2];
+#define GLOAD(Q, KT) do {                                                               \
+    const uint32_t kk_ = static_cast<uint32_t>(min((KT), ke - 1) * kMBK);               \
+    if ((Q) < 8) stg[Q] = ld16(abase + ao + static_cast<uint32_t>((Q) * 8) * K + kk_);  \
+    else stg[Q] = ld16(act + bo[(Q) - 8] + kk_);                                        \
+  } while (0)
+#define SLOAD(KT) do {                                                                  \
+    const uint32_t ks_ = static_cast<uint32_t>(min((KT), ke - 1) * 4);                 \
+    sst[0] = *reinterpret_cast<const uint32_t*>(asb + so_a + ks_);                      \
+    sst[1] = *reinterpret_cast<const uint32_t*>(act_s + so_b + ks_);                    \
+  } while (0)
+#define LWRITE(Q, KT) do {                                                              \
+    uint8_t* st_ = ldm + ((KT) & 1) * 2 * kMTile;                                       \
+    if ((Q) < 8) *reinterpret_cast<i32x4*>(&st_[lw + (Q) * 8 * kMBK]) = stg[Q];         \
+    else *reinterpret_cast<i32x4*>(&st_[kMTile + lw + ((Q) - 8) * 8 * kMBK]) = stg[Q];  \
+  } while (0)
+#define SWRITE(KT) do {                                                                 \
+    uint32_t* sc_ = lsc + ((KT) & 1) * 2 * kLargeBM;                                    \
+    sc_[tid] = sst[0];                                                                  \
+    sc_[kLargeBM + tid] = sst[1];                                                       \
+  } while (0)
+  // fragment piece P (0..15) of stage RKT, K step RKS: fragment P >> 1 (A 0..3, B 4..7), half P & 1
+#define RDP(F, P, RKT, RKS) do {                                                        \
+    const uint8_t* at_ = ldm + ((RKT) & 1) * 2 * kMTile;                                \
+    const int fr_ = (P) >> 1, h_ = (P) & 1;                                             \
+    const int row_ = fr_ < 4 ? fa[fr_] : fb + 32 * (fr_ - 4);                           \
+    const uint8_t* src_ = (fr_ < 4 ? at_ : at_ + kMTile) + row_ * kMBK +               \
+                          (((4 * (RKS) + 2 * h_ + hi) ^ swz) * 16);                     \
+    const i32x4 v_ = *reinterpret_cast<const i32x4*>(src_);                             \
+    _Pragma("unroll") for (int u_ = 0; u_ < 4; ++u_) F[fr_][4 * h_ + u_] = v_[u_];      \
+  } while (0)
+#define RDS(SC, RKT) do {                                                               \
+    const uint32_t* sc_ = lsc + ((RKT) & 1) * 2 * kLargeBM;                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) SC[i_] = sc_[fa[i_]] >> (8 * hi);  \
+    _Pragma("unroll") for (int j_ = 0; j_ < 4; ++j_)                                    \
+      SC[4 + j_] = sc_[kLargeBM + fb + 32 * j_] >> (8 * hi);                            \
+  } while (0)
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) GLOAD(q, kb);
+  SLOAD(kb);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) LWRITE(q, kb);
+  SWRITE(kb);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) GLOAD(q, kb + 1);
+  SLOAD(kb + 1);
+  __syncthreads();
+  i32x8 f0[8], f1[8];          // fragments: [0..3] A, [4..7] B
+  uint32_t sc[8], scn[8];      // scales of the current / next stage
+#pragma unroll
+  for (int p = 0; p < 16; ++p) RDP(f0, p, kb, 0);
+  RDS(sc, kb);
+  for (int kt = kb; kt < ke; ++kt) {
+    // K step 0: MFMAs on f0; read K step 1 into f1; stage kt+1 to LDS, stage kt+2 loads
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const int i = g >> 2, j = g & 3;
+      acc[i][j] = mfma_mx32<0>(f0[i], f0[4 + j], static_cast<int>(sc[i]), static_cast<int>(sc[4 + j]), acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      RDP(f1, g, kt, 1);
+      LWRITE(g, kt + 1);
+      GLOAD(g, kt + 2);
+      if (g == 15) { SWRITE(kt + 1); SLOAD(kt + 2); }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    // K step 1: MFMAs on f1; read K step 0 of stage kt+1 into f0, and its scales
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const int i = g >> 2, j = g & 3;
+      acc[i][j] = mfma_mx32<2>(f1[i], f1[4 + j], static_cast<int>(sc[i]), static_cast<int>(sc[4 + j]), acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+      RDP(f0, g, kt + 1, 0);
+      if (g == 0) RDS(scn, kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sc[q] = scn[q];
+  }
+#undef GLOAD
+#undef SLOAD
+#undef LWRITE
+#undef SWRITE
+#undef RDP
+#undef RDS
+
+  if (slot >= 0) {
+    f32x4* pp = reinterpret_cast<f32x4*>(partial) + static_cast<size_t>(slot) * 64 * 256 + tid;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          pp[((i * 4 + j) * 4 + q) * 256] =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    return;
+  }
+  if (kGU) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) mx_store_block(acc[i][j], acc[i + 2][j], wm * 128 + 32 * j + l32, mcount,
+                                                 rbase, n0 + wn * 64 + 32 * i, hi, I, hq, hs);
+  } else {
+    large_epilogue<KIND>(acc, perm, w, H, I, rbase, mcount, nb, wm, wn, l32, hi, nullptr, y, out);
+  }
+}
+
+// Tail fix-up of the MXFP8 gate_up: workgroup (item b, block i, token group j) -
+// 8 per tail item - sums the slices of gate block i and up block i + 2 for its
+// 32 x 32 piece and quantizes it as the GEMM epilogue does.
+__global__ __launch_bounds__(256) void gemm_large_mx_fixup_gate_up(
+    const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
+    const int* __restrict__ counts, const int* __restrict__ offsets, int H, int I,
+    uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, const float* __restrict__ partial, int ncu,
+    int nk) {
+  const int nblk = I / 128;
+  const TailPlan plan = tail_plan(nblk * *n_tiles, ncu, nk);
+  const int b = blockIdx.x >> 3, i = (blockIdx.x >> 2) & 1, j = blockIdx.x & 3;
+  if (plan.S == 1 || b >= plan.rem) return;
+  const int item = plan.full + b;
+  const int tile = item / nblk, nb = item - tile * nblk;
+  const int2 te = tiles[tile];
+  const int e = te.x, m0 = te.y;
+  const int mcount = min(kLargeBM, counts[e] - m0);
+  const int rbase = offsets[e] + m0;
+  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, l32 = ln & 31, hi = ln >> 5;
+  f32x16 g = {}, u = {};
+  for (int sl = 0; sl < plan.S; ++sl) {
+    const f32x4* pp = reinterpret_cast<const f32x4*>(partial) +
+                      static_cast<size_t>(sl * plan.rem + b) * 64 * 256 + tid;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 vg = pp[((i * 4 + j) * 4 + q) * 256];
+      const f32x4 vu = pp[(((i + 2) * 4 + j) * 4 + q) * 256];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        g[4 * q + t] += vg[t];
+        u[4 * q + t] += vu[t];
+      }
+    }
+  }
+  mx_store_block(g, u, (wv & 1) * 128 + 32 * j + l32, mcount, rbase,
+                 nb * 128 + (wv >> 1) * 64 + 32 * i, hi, I, hq, hs);
+}
+
 namespace {
 // grid: every item whole, plus room for the tail slices (rem * S - rem < ncu)
 int large_grid(int nblk, int max_tiles, int ncu) {
@@ -349,7 +638,8 @@ hipError_t launch_gate_up_large_bf16(const uint16_t* x, const uint16_t* wgu, con
                      tiles, n_tiles, counts, offsets, nullptr, H, I, k, h, nullptr, nullptr,
                      partial, ncu);
   hipLaunchKernelGGL(gemm_large_fixup<kGateUp>, dim3(ncu / 2 * 32), dim3(256), 0, s, perm, tiles,
-                     n_tiles, counts, offsets, nullptr, H, I, h, nullptr, nullptr, partial, ncu);
+                     n_tiles, counts, offsets, nullptr, H, I, h, nullptr, nullptr, partial, ncu,
+                     H / kLBK);
   return hipGetLastError();
 }
 
@@ -363,9 +653,40 @@ hipError_t launch_down_large_bf16(const uint16_t* h, const uint16_t* wd, const i
   hipLaunchKernelGGL(gemm_large_bf16<KD>, dim3(grid), dim3(256), kLLds, s, h, wd, perm, tiles, \
                      n_tiles, counts, offsets, w, H, I, k, nullptr, y, out, partial, ncu);    \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
-                     n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu)
+                     n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kLBK)
   if (k == 1) { LARGE_DOWN(kDownFused); } else { LARGE_DOWN(kDownSlots); }
 #undef LARGE_DOWN
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up_large_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* wgu,
+                                   const uint8_t* wgus, const int* perm, const int2* tiles,
+                                   const int* n_tiles, const int* counts, const int* offsets, int H,
+                                   int I, int k, uint8_t* hq, uint8_t* hs, float* partial,
+                                   int max_tiles, int ncu, hipStream_t s) {
+  const int grid = large_grid(I / 128, max_tiles, ncu);
+  hipLaunchKernelGGL(gemm_large_mx<kGateUp>, dim3(grid), dim3(256), kMLds, s, x, xs, wgu, wgus,
+                     perm, tiles, n_tiles, counts, offsets, nullptr, H, I, k, hq, hs, nullptr,
+                     nullptr, partial, ncu);
+  hipLaunchKernelGGL(gemm_large_mx_fixup_gate_up, dim3(ncu / 2 * 8), dim3(256), 0, s, tiles,
+                     n_tiles, counts, offsets, H, I, hq, hs, partial, ncu, H / kMBK);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* wd,
+                                const uint8_t* wds, const int* perm, const int2* tiles,
+                                const int* n_tiles, const int* counts, const int* offsets,
+                                const float* w, int H, int I, int k, float* y, uint16_t* out,
+                                float* partial, int max_tiles, int ncu, hipStream_t s) {
+  const int grid = large_grid(H / 256, max_tiles, ncu);
+#define LARGE_DOWN_MX(KD)                                                                     \
+  hipLaunchKernelGGL(gemm_large_mx<KD>, dim3(grid), dim3(256), kMLds, s, hq, hs, wd, wds,      \
+                     perm, tiles, n_tiles, counts, offsets, w, H, I, k, nullptr, nullptr, y,  \
+                     out, partial, ncu);                                                      \
+  hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
+                     n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kMBK)
+  if (k == 1) { LARGE_DOWN_MX(kDownFused); } else { LARGE_DOWN_MX(kDownSlots); }
+#undef LARGE_DOWN_MX
   return hipGetLastError();
 }
 
@@ -379,6 +700,16 @@ hipError_t large_set_attributes() {
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kDownSlots>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  const int mbytes = static_cast<int>(kMLds);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_mx<kGateUp>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_mx<kDownFused>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_mx<kDownSlots>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
   return e;
 }
 

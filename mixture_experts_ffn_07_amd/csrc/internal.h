@@ -64,6 +64,16 @@ hipError_t launch_down_large_bf16(const uint16_t* h, const uint16_t* wd, const i
                                   const int* offsets, const float* w, int H, int I, int k,
                                   float* y, uint16_t* out, float* partial, int max_tiles, int ncu,
                                   hipStream_t s);
+hipError_t launch_gate_up_large_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* wgu,
+                                   const uint8_t* wgus, const int* perm, const int2* tiles,
+                                   const int* n_tiles, const int* counts, const int* offsets, int H,
+                                   int I, int k, uint8_t* hq, uint8_t* hs, float* partial,
+                                   int max_tiles, int ncu, hipStream_t s);
+hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* wd,
+                                const uint8_t* wds, const int* perm, const int2* tiles,
+                                const int* n_tiles, const int* counts, const int* offsets,
+                                const float* w, int H, int I, int k, float* y, uint16_t* out,
+                                float* partial, int max_tiles, int ncu, hipStream_t s);
 hipError_t large_set_attributes();
 
 hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
