@@ -13,12 +13,10 @@
 // HBM traffic.  The eight waves of a workgroup split the reduction dimension
 // and their partial sums are added in LDS in a fixed wave order.
 //
-// The activation handed from gate_up to down is w_j * silu(g) * u in FP32,
-// stored as an exact-sum pair of BF16 values (hi = rne(v), lo = rne(v - hi)),
-// so the down projection's MFMA sees ~16 significant bits of the FP32 value
-// rather than BF16's 8; the FP32 accumulation is untouched.  Pre-multiplying
-// by the routing weight lets all routed experts of a token accumulate into
-// one MFMA accumulator.
+// The activation handed from gate_up to down is w_j * silu(g) * u, computed in
+// FP32 and rounded once to BF16 (the MFMA operand type; the batched path does
+// the same); the FP32 accumulation is untouched.  Pre-multiplying by the
+// routing weight lets all routed experts of a token add into one sum.
 //
 // Determinism: expert order (ascending id), token order, the MFMA sequence
 // and the cross-wave sum order are all fixed; nothing accumulates through
@@ -46,8 +44,7 @@ DecodeWs decode_ws_layout(int T, int H, int I, int E, int k) {
   L.plan_mask = o;   o = align256(o + sizeof(uint64_t) * E);
   L.idx = o;         o = align256(o + sizeof(int32_t) * pairs);
   L.w = o;           o = align256(o + sizeof(float) * pairs);
-  L.hw_hi = o;       o = align256(o + 2 * pairs * I);
-  L.hw_lo = o;       o = align256(o + 2 * pairs * I);
+  L.hw = o;          o = align256(o + 2 * pairs * I);
   L.total = o;
   return L;
 }
@@ -139,8 +136,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
     const int32_t* __restrict__ idx, const float* __restrict__ wts,
     const int* __restrict__ plan_u, const int32_t* __restrict__ plan_e,
-    const uint64_t* __restrict__ plan_mask, int H, int I, int k,
-    uint16_t* __restrict__ hw_hi, uint16_t* __restrict__ hw_lo) {
+    const uint64_t* __restrict__ plan_mask, int H, int I, int k, uint16_t* __restrict__ hw) {
   extern __shared__ float red[];                    // [8 waves][TM][gate/up][4][64]
   __shared__ int s_e[kMaxPlan];
   __shared__ uint64_t s_m[kMaxPlan];
@@ -240,11 +236,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
         int js = 0;
         while (js < k - 1 && idx[tt * k + js] != e) ++js;
         const float hv = wts[tt * k + js] * swiglu(g, up);
-        const uint32_t hi = f32_to_bf16_rne(hv);
-        const uint32_t lo = f32_to_bf16_rne(hv - bf16_to_f32(hi));
-        const size_t o = static_cast<size_t>(tt * k + js) * I + rb * 16 + m;
-        hw_hi[o] = static_cast<uint16_t>(hi);
-        hw_lo[o] = static_cast<uint16_t>(lo);
+        hw[static_cast<size_t>(tt * k + js) * I + rb * 16 + m] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
       }
     }
     __syncthreads();
@@ -266,11 +258,16 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
 // workgroups, enough to occupy every CU without splitting the expert sum
 // across workgroups).  MFMA rows 0..7 carry those dimensions; lanes of rows
 // 8..15 issue no weight loads (the MFMA work they waste is free: the kernel
-// is bound by memory).  The 16 waves form EGW expert groups x KSW K-slices:
-// wave (eg, ks) takes experts u = eg, eg + EGW, ... in ascending order and
-// the K range [ks*I/KSW, (ks+1)*I/KSW) of each, loading the next expert's
-// weights while it multiplies the current one.  The 16 wave partials are
-// added in LDS in wave order, so the sum order is fixed.
+// is bound by memory).  MFMA columns are the tokens routed to the current
+// expert, compacted (16 per tile), so every activation load is a routed
+// token's row and each expert costs one tile of loads and MFMAs (more only
+// for the rare expert with over 16 tokens).  Each wave adds an expert's
+// results into its own FP32 accumulator rows in LDS ([token][8 dims]), in
+// ascending expert order; the 16 waves' accumulators are added in wave order
+// at the end, so the sum order is fixed.  The 16 waves form EGW expert groups
+// x KSW K-slices: wave (eg, ks) takes experts u = eg, eg + EGW, ... and the K
+// range [ks*I/KSW, (ks+1)*I/KSW) of each, loading the next expert's weights
+// and first activation tile while it multiplies the current one.
 constexpr int kDownRows = 8;
 constexpr int kDownWaves = 16;
 constexpr int kDownThreads = kDownWaves * kWave;
@@ -289,14 +286,13 @@ __device__ __forceinline__ int slot_of(const int* s_idx_row, int k, int e) {
   return js;
 }
 
-template <int TM, int KD>
+template <int KD>
 __global__ __launch_bounds__(kDownThreads) void decode_down(
     const uint16_t* __restrict__ wd, const int32_t* __restrict__ idx,
     const int* __restrict__ plan_u, const int32_t* __restrict__ plan_e,
-    const uint64_t* __restrict__ plan_mask, const uint16_t* __restrict__ hw_hi,
-    const uint16_t* __restrict__ hw_lo, int T, int H, int I, int k, int KSW,
-    uint16_t* __restrict__ out) {
-  extern __shared__ float red[];                    // [16 waves][TM][4][64]
+    const uint64_t* __restrict__ plan_mask, const uint16_t* __restrict__ hw, int T, int H, int I,
+    int k, int KSW, uint16_t* __restrict__ out) {
+  extern __shared__ float accl[];                   // [16 waves][T][8 dims]
   __shared__ __align__(16) int s_idx[64 * 32];      // token rows padded to a multiple of 4
   __shared__ int s_e[kMaxPlan];
   __shared__ uint64_t s_m[kMaxPlan];
@@ -310,6 +306,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     s_e[i] = plan_e[i];
     s_m[i] = plan_mask[i];
   }
+  for (int i = threadIdx.x; i < kDownWaves * T * kDownRows; i += blockDim.x) accl[i] = 0.f;
   __syncthreads();
   const int wv = wave_id(), ln = lane_id();
   const int col = ln & 15, grp = ln >> 4;
@@ -320,69 +317,75 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
   const int kw = I / KSW;                           // = KD * 32
   const uint32_t kb = static_cast<uint32_t>(ks * kw + grp * 8);
   const uint16_t* pw = wd + (static_cast<size_t>(d0) + (row_lane ? col : 0)) * I + kb;
+  float* myacc = accl + wv * T * kDownRows;
   const bf16x8 zero8 = {};
   const int ntask = U > eg ? (U - 1 - eg) / EGW + 1 : 0;
-  f32x4 acc[TM];
-#pragma unroll
-  for (int c = 0; c < TM; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 aA[KD], aB[KD];
-#define DN_ISSUE(A, TSK)                                                              \
-  {                                                                                   \
-    const uint16_t* p_ = pw + static_cast<size_t>(s_e[eg + (TSK) * EGW]) * H * I;    \
-    _Pragma("unroll") for (int s = 0; s < KD; ++s)                                    \
-      A[s] = row_lane ? as_bf16x8(ld16(p_ + s * 32)) : zero8;                         \
-  }
-  auto run_task = [&](const bf16x8 (&A)[KD], int tsk) {
-    const int u = eg + tsk * EGW;
-    const int e = s_e[u];
-    const uint64_t mask = s_m[u];
-#pragma unroll
-    for (int q = 0; q < TM; ++q) {
-      const uint32_t bits = static_cast<uint32_t>(mask >> (16 * q)) & 0xFFFFu;
-      if (bits == 0) continue;
-      const int tk = 16 * q + col;
-      const bool routed = (bits >> col) & 1u;
-      const int js = routed ? slot_of(s_idx + tk * kp, k, e) : 0;
-      const size_t row = static_cast<size_t>((routed ? tk : 0) * k + js) * I + kb;
-      bf16x8 bh[KD], bl[KD];
-#pragma unroll
-      for (int s = 0; s < KD; ++s) {
-        bh[s] = routed ? as_bf16x8(ld16(hw_hi + row + s * 32)) : zero8;
-        bl[s] = routed ? as_bf16x8(ld16(hw_lo + row + s * 32)) : zero8;
-      }
-#pragma unroll
-      for (int s = 0; s < KD; ++s) {
-        acc[q] = mfma16x16x32(A[s], bh[s], acc[q]);
-        acc[q] = mfma16x16x32(A[s], bl[s], acc[q]);
-      }
+  // activation row (element offset) of compact column c of expert e with token mask m
+  auto act_row = [&](uint64_t m, int e, int c, bool on) -> size_t {
+    const int t = on ? nth_set_bit(m, c) : 0;
+    const int js = on ? slot_of(s_idx + t * kp, k, e) : 0;
+    return static_cast<size_t>(t * k + js) * I + kb;
+  };
+  // add the tile's D rows 0..7 (lanes grp < 2) into the wave's accumulator rows
+  auto accumulate = [&](const f32x4& d, uint64_t m, int c, bool on) {
+    if (on && grp < 2) {
+      f32x4* a = reinterpret_cast<f32x4*>(myacc + nth_set_bit(m, c) * kDownRows + 4 * grp);
+      *a = *a + d;
     }
   };
-  if (ntask > 0) DN_ISSUE(aA, 0)
+  bf16x8 aA[KD], aB[KD], bA[KD], bB[KD];
+#define DN_ISSUE(A, B, TSK)                                                                \
+  {                                                                                        \
+    const int u_ = eg + (TSK) * EGW;                                                       \
+    const int e_ = s_e[u_];                                                                \
+    const uint64_t m_ = s_m[u_];                                                           \
+    const uint16_t* p_ = pw + static_cast<size_t>(e_) * H * I;                             \
+    _Pragma("unroll") for (int s = 0; s < KD; ++s)                                         \
+      A[s] = row_lane ? as_bf16x8(ld16(p_ + s * 32)) : zero8;                              \
+    const bool on_ = col < __popcll(m_);                                                   \
+    const size_t r_ = act_row(m_, e_, col, on_);                                           \
+    _Pragma("unroll") for (int s = 0; s < KD; ++s)                                         \
+      B[s] = on_ ? as_bf16x8(ld16(hw + r_ + s * 32)) : zero8;                              \
+  }
+#define DN_RUN(A, B, TSK)                                                                  \
+  {                                                                                        \
+    const int u_ = eg + (TSK) * EGW;                                                       \
+    const int e_ = s_e[u_];                                                                \
+    const uint64_t m_ = s_m[u_];                                                           \
+    const int nt_ = __popcll(m_);                                                          \
+    f32x4 d_ = {0.f, 0.f, 0.f, 0.f};                                                       \
+    _Pragma("unroll") for (int s = 0; s < KD; ++s) d_ = mfma16x16x32(A[s], B[s], d_);      \
+    accumulate(d_, m_, col, col < nt_);                                                    \
+    for (int c0 = 16; c0 < nt_; c0 += 16) {           /* experts with over 16 tokens */    \
+      const bool on_ = c0 + col < nt_;                                                     \
+      const size_t r_ = act_row(m_, e_, c0 + col, on_);                                    \
+      bf16x8 bx_[KD];                                                                      \
+      _Pragma("unroll") for (int s = 0; s < KD; ++s)                                       \
+        bx_[s] = on_ ? as_bf16x8(ld16(hw + r_ + s * 32)) : zero8;                          \
+      f32x4 dx_ = {0.f, 0.f, 0.f, 0.f};                                                    \
+      _Pragma("unroll") for (int s = 0; s < KD; ++s) dx_ = mfma16x16x32(A[s], bx_[s], dx_); \
+      accumulate(dx_, m_, c0 + col, on_);                                                  \
+    }                                                                                      \
+  }
+  if (ntask > 0) DN_ISSUE(aA, bA, 0)
   for (int t = 0; t < ntask; t += 2) {
-    if (t + 1 < ntask) DN_ISSUE(aB, t + 1)
-    run_task(aA, t);
+    if (t + 1 < ntask) DN_ISSUE(aB, bB, t + 1)
+    DN_RUN(aA, bA, t)
     if (t + 1 < ntask) {
-      if (t + 2 < ntask) DN_ISSUE(aA, t + 2)
-      run_task(aB, t + 1);
+      if (t + 2 < ntask) DN_ISSUE(aA, bA, t + 2)
+      DN_RUN(aB, bB, t + 1)
     }
   }
 #undef DN_ISSUE
-  // D rows 0..7 live in lanes with grp < 2
-#pragma unroll
-  for (int c = 0; c < TM; ++c)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) red[((wv * TM + c) * 4 + r) * 64 + ln] = acc[c][r];
+#undef DN_RUN
   __syncthreads();
-  for (int q = threadIdx.x; q < TM * 16 * kDownRows; q += blockDim.x) {
-    const int c = q / (16 * kDownRows), within = q % (16 * kDownRows);
-    const int n = within / kDownRows, mm = within % kDownRows;   // token column n, output row mm
-    const int src = 16 * (mm >> 2) + n, r = mm & 3;
+  for (int i = threadIdx.x; i < T * kDownRows; i += blockDim.x) {
     float v = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kDownWaves; ++w2) v += red[((w2 * TM + c) * 4 + r) * 64 + src];
-    const int t = 16 * c + n;
-    if (t < T) out[static_cast<size_t>(t) * H + d0 + mm] = static_cast<uint16_t>(f32_to_bf16_rne(v));
+    for (int w2 = 0; w2 < kDownWaves; ++w2) v += accl[w2 * T * kDownRows + i];
+    const int t = i / kDownRows, mm = i - t * kDownRows;
+    out[static_cast<size_t>(t) * H + d0 + mm] = static_cast<uint16_t>(f32_to_bf16_rne(v));
   }
 }
 
@@ -396,8 +399,7 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   uint64_t* plan_mask = reinterpret_cast<uint64_t*>(base + L.plan_mask);
   int32_t* idx_p = idx ? idx : reinterpret_cast<int32_t*>(base + L.idx);
   float* w_p = w ? w : reinterpret_cast<float*>(base + L.w);
-  uint16_t* hw_hi = reinterpret_cast<uint16_t*>(base + L.hw_hi);
-  uint16_t* hw_lo = reinterpret_cast<uint16_t*>(base + L.hw_lo);
+  uint16_t* hw = reinterpret_cast<uint16_t*>(base + L.hw);
 
   const int nchunks = (E + kWave - 1) / kWave;
   const size_t lds_plan = sizeof(uint64_t) * E + sizeof(int) * nchunks;
@@ -411,7 +413,7 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   const long grid_cap = 2L * num_cus;
   const int grid1 = static_cast<int>(items_upper < grid_cap ? items_upper : grid_cap);
   const size_t lds_gu = sizeof(float) * kDecWaves * TM * 2 * 256;
-  const size_t lds_dn = sizeof(float) * kDownWaves * TM * 256;
+  const size_t lds_dn = sizeof(float) * kDownWaves * T * kDownRows;
   const int gsteps = H / kDecWaves / 32;
   int KC = gsteps % 4 == 0 ? 4 : (gsteps % 3 == 0 ? 3 : (gsteps % 2 == 0 ? 2 : 1));
   if (TM == 4 && KC == 4) KC = 2;                   // keeps four token tiles within 128 VGPRs
@@ -425,7 +427,7 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   prof_begin(kDecGateUp, s);
 #define GU_LAUNCH(TMV, KCV)                                                                    \
   hipLaunchKernelGGL((decode_gate_up<TMV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x,   \
-                     wgu, idx_p, w_p, plan_u, plan_e, plan_mask, H, I, k, hw_hi, hw_lo)
+                     wgu, idx_p, w_p, plan_u, plan_e, plan_mask, H, I, k, hw)
 #define GU_KC(TMV)                                        \
   switch (KC) {                                           \
     case 4: GU_LAUNCH(TMV, 4); break;                     \
@@ -438,18 +440,15 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
 #undef GU_LAUNCH
   prof_end(kDecGateUp, s);
   prof_begin(kDecDown, s);
-#define DN_LAUNCH(TMV, KDV)                                                                    \
-  hipLaunchKernelGGL((decode_down<TMV, KDV>), grid2, dim3(kDownThreads), lds_dn, s, wd, idx_p,   \
-                     plan_u, plan_e, plan_mask, hw_hi, hw_lo, T, H, I, k, KSW, out)
-#define DN_KD(TMV)                                        \
-  switch (KD) {                                           \
-    case 4: DN_LAUNCH(TMV, 4); break;                     \
-    case 3: DN_LAUNCH(TMV, 3); break;                     \
-    case 2: DN_LAUNCH(TMV, 2); break;                     \
-    default: DN_LAUNCH(TMV, 1); break;                    \
+#define DN_LAUNCH(KDV)                                                                         \
+  hipLaunchKernelGGL((decode_down<KDV>), grid2, dim3(kDownThreads), lds_dn, s, wd, idx_p, plan_u, \
+                     plan_e, plan_mask, hw, T, H, I, k, KSW, out)
+  switch (KD) {
+    case 4: DN_LAUNCH(4); break;
+    case 3: DN_LAUNCH(3); break;
+    case 2: DN_LAUNCH(2); break;
+    default: DN_LAUNCH(1); break;
   }
-  if (TM == 1) { DN_KD(1) } else if (TM == 2) { DN_KD(2) } else { DN_KD(4) }
-#undef DN_KD
 #undef DN_LAUNCH
   prof_end(kDecDown, s);
   return hipGetLastError();
