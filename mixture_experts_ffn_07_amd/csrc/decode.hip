@@ -49,61 +49,6 @@ DecodeWs decode_ws_layout(int T, int H, int I, int E, int k) {
   return L;
 }
 
-// One workgroup: route every token, then list the touched experts in
-// ascending order with a 64-bit mask of the tokens routed to each.
-__global__ __launch_bounds__(1024) void decode_route_plan(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx,
-    float* __restrict__ wts, int* __restrict__ plan_u, int32_t* __restrict__ plan_e,
-    uint64_t* __restrict__ plan_mask) {
-  extern __shared__ uint64_t dyn_masks[];          // [E] token masks, then chunk counts
-  __shared__ int s_idx[64 * 32];
-  const int nchunks = (E + kWave - 1) / kWave;
-  int* chunk_off = reinterpret_cast<int*>(dyn_masks + E);
-  const int nw = blockDim.x / kWave, wv = wave_id(), lane = lane_id();
-
-  for (int t = wv; t < T; t += nw) {
-    int e;
-    float wt;
-    route_token_any(logits + static_cast<size_t>(t) * E, E, k, &e, &wt);
-    if (lane < k) {
-      idx[t * k + lane] = e;
-      wts[t * k + lane] = wt;
-      s_idx[t * k + lane] = e;
-    }
-  }
-  for (int i = threadIdx.x; i < E; i += blockDim.x) dyn_masks[i] = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i < T * k; i += blockDim.x)
-    atomicOr(reinterpret_cast<unsigned long long*>(&dyn_masks[s_idx[i]]), 1ull << (i / k));
-  __syncthreads();
-  for (int c = wv; c < nchunks; c += nw) {
-    const int e = c * kWave + lane;
-    const uint64_t on = __ballot(e < E && dyn_masks[e] != 0);
-    if (lane == 0) chunk_off[c] = __popcll(on);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int s = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = chunk_off[c];
-      chunk_off[c] = s;
-      s += v;
-    }
-    *plan_u = s;
-  }
-  __syncthreads();
-  for (int c = wv; c < nchunks; c += nw) {
-    const int e = c * kWave + lane;
-    const bool on = e < E && dyn_masks[e] != 0;
-    const uint64_t b = __ballot(on);
-    if (on) {
-      const int r = chunk_off[c] + __popcll(b & ((1ull << lane) - 1));
-      plan_e[r] = e;
-      plan_mask[r] = dyn_masks[e];
-    }
-  }
-}
-
 // Position of the n-th set bit of m (n < popcount(m)), by halving.
 __device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
   int pos = 0;
@@ -125,6 +70,53 @@ __device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
 // Largest plan a workgroup stages in LDS (touched experts <= E <= 1024).
 constexpr int kMaxPlan = 1024;
 
+// Touched-expert plan, built by every gate_up workgroup from the routing
+// result (T*k expert ids, L2-resident): s_e[u] = the u-th touched expert in
+// ascending order, s_m[u] = the mask of the tokens routed to it; returns the
+// count U.  `masks` (E words) and `coff` ((E + 63) / 64 ints) are LDS scratch.
+// The 64-bit masks are built with integer atomics (the result does not depend
+// on their order); the list is compacted with wave ballots, in expert order.
+__device__ int build_plan(const int32_t* __restrict__ idx, int T, int E, int k,
+                          uint64_t* masks, int* coff, int* s_e, uint64_t* s_m) {
+  const int nchunks = (E + kWave - 1) / kWave;
+  const int nw = blockDim.x / kWave, wv = wave_id(), lane = lane_id();
+  for (int i = threadIdx.x; i < E; i += blockDim.x) masks[i] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * k; i += blockDim.x)
+    atomicOr(reinterpret_cast<unsigned long long*>(&masks[idx[i]]), 1ull << (i / k));
+  __syncthreads();
+  for (int c = wv; c < nchunks; c += nw) {
+    const int e = c * kWave + lane;
+    const uint64_t on = __ballot(e < E && masks[e] != 0);
+    if (lane == 0) coff[c] = __popcll(on);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int sum = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = coff[c];
+      coff[c] = sum;
+      sum += v;
+    }
+    coff[nchunks] = sum;
+  }
+  __syncthreads();
+  for (int c = wv; c < nchunks; c += nw) {
+    const int e = c * kWave + lane;
+    const bool on = e < E && masks[e] != 0;
+    const uint64_t b = __ballot(on);
+    if (on) {
+      const int r = coff[c] + __popcll(b & ((1ull << lane) - 1));
+      s_e[r] = e;
+      s_m[r] = masks[e];
+    }
+  }
+  const int U = coff[nchunks];
+  __syncthreads();
+  return U;
+}
+
+
 // gate_up: work item = (touched expert u, block of 16 neurons); workgroups
 // stride over items.  Wave wv covers K range [wv*H/8, (wv+1)*H/8) in chunks
 // of KC steps of 32 (KC divides the steps).  The workgroup walks its flat
@@ -134,18 +126,22 @@ constexpr int kMaxPlan = 1024;
 template <int TM, int KC>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_gate_up(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
-    const int32_t* __restrict__ idx, const float* __restrict__ wts,
-    const int* __restrict__ plan_u, const int32_t* __restrict__ plan_e,
-    const uint64_t* __restrict__ plan_mask, int H, int I, int k, uint16_t* __restrict__ hw) {
+    const int32_t* __restrict__ idx, const float* __restrict__ wts, int T, int E,
+    int* __restrict__ plan_u, int32_t* __restrict__ plan_e, uint64_t* __restrict__ plan_mask,
+    int H, int I, int k, uint16_t* __restrict__ hw) {
   extern __shared__ float red[];                    // [8 waves][TM][gate/up][4][64]
   __shared__ int s_e[kMaxPlan];
   __shared__ uint64_t s_m[kMaxPlan];
-  const int U = *plan_u;
-  for (int i = threadIdx.x; i < U; i += blockDim.x) {
-    s_e[i] = plan_e[i];
-    s_m[i] = plan_mask[i];
+  // the plan's scratch (E masks + chunk offsets) borrows the reduction buffer
+  const int U = build_plan(idx, T, E, k, reinterpret_cast<uint64_t*>(red),
+                           reinterpret_cast<int*>(reinterpret_cast<uint64_t*>(red) + E), s_e, s_m);
+  if (blockIdx.x == 0) {                            // the plan for the down kernel
+    for (int i = threadIdx.x; i < U; i += blockDim.x) {
+      plan_e[i] = s_e[i];
+      plan_mask[i] = s_m[i];
+    }
+    if (threadIdx.x == 0) *plan_u = U;
   }
-  __syncthreads();
   const int nrb = I / 16;
   const int items = U * nrb;
   const int wv = wave_id(), ln = lane_id();
@@ -401,18 +397,17 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   float* w_p = w ? w : reinterpret_cast<float*>(base + L.w);
   uint16_t* hw = reinterpret_cast<uint16_t*>(base + L.hw);
 
-  const int nchunks = (E + kWave - 1) / kWave;
-  const size_t lds_plan = sizeof(uint64_t) * E + sizeof(int) * nchunks;
-  prof_begin(kRoute, s);
-  hipLaunchKernelGGL(decode_route_plan, dim3(1), dim3(1024), lds_plan, s, logits, T, E, k, idx_p,
-                     w_p, plan_u, plan_e, plan_mask);
-  prof_end(kRoute, s);
+  hipError_t err = launch_route_topk(logits, T, E, k, idx_p, w_p, s);   // brackets kRoute
+  if (err != hipSuccess) return err;
 
   const int TM = T <= 16 ? 1 : (T <= 32 ? 2 : 4);   // token tiles the kernels carry
   const long items_upper = static_cast<long>(T * k < E ? T * k : E) * (I / 16);
   const long grid_cap = 2L * num_cus;
   const int grid1 = static_cast<int>(items_upper < grid_cap ? items_upper : grid_cap);
-  const size_t lds_gu = sizeof(float) * kDecWaves * TM * 2 * 256;
+  // reduction buffer; the plan scratch (E masks + chunk offsets) must fit in it too
+  size_t lds_gu = sizeof(float) * kDecWaves * TM * 2 * 256;
+  const size_t lds_plan = sizeof(uint64_t) * E + sizeof(int) * ((E + kWave - 1) / kWave + 1);
+  if (lds_plan > lds_gu) lds_gu = lds_plan;
   const size_t lds_dn = sizeof(float) * kDownWaves * T * kDownRows;
   const int gsteps = H / kDecWaves / 32;
   int KC = gsteps % 4 == 0 ? 4 : (gsteps % 3 == 0 ? 3 : (gsteps % 2 == 0 ? 2 : 1));
@@ -427,7 +422,7 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   prof_begin(kDecGateUp, s);
 #define GU_LAUNCH(TMV, KCV)                                                                    \
   hipLaunchKernelGGL((decode_gate_up<TMV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x,   \
-                     wgu, idx_p, w_p, plan_u, plan_e, plan_mask, H, I, k, hw)
+                     wgu, idx_p, w_p, T, E, plan_u, plan_e, plan_mask, H, I, k, hw)
 #define GU_KC(TMV)                                        \
   switch (KC) {                                           \
     case 4: GU_LAUNCH(TMV, 4); break;                     \
@@ -465,9 +460,6 @@ hipError_t decode_set_attributes() {
                             sizeof(float) * kDecWaves * 4 * 2 * 256);
     if (e != hipSuccess) return e;
   }
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_route_plan),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          sizeof(uint64_t) * 1024 + sizeof(int) * 16);
   return e;
 }
 

@@ -4,10 +4,11 @@
 // logit descending, then expert index ascending, and the first k are kept; the weights are the softmax of the k selected logits
 // (softmax over all E renormalised over the selection).
 //
-// Each logit becomes a 64-bit key: high word = FP32 bits mapped to an
-// unsigned order (-0 folded onto +0), low word = ~expert, so the largest key
-// is the largest logit and, among equal logits, the lowest index.  k rounds
-// of a wave-wide max pick the experts in slot order.
+// Each logit becomes a 32-bit key: its FP32 bits mapped to an unsigned order
+// (-0 folded onto +0; every finite logit maps above 0, which marks "taken").
+// Each of k rounds takes the wave-wide maximum key (DPP), then the lowest
+// expert index holding it (wave ballots, experts lane + 64*i scanned by i
+// first), so slots come out by logit descending, index ascending.
 #pragma once
 
 #include "common.h"
@@ -25,65 +26,60 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
   return __uint_as_float(u);
 }
 
-// One DPP step of a 64-bit max: combine each lane with the lane CTRL names.
+// One DPP step of a 32-bit max: combine each lane with the lane CTRL names.
 template <int CTRL>
-__device__ __forceinline__ uint64_t max_dpp(uint64_t v) {
-  const uint32_t lo = static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL, 0xF, 0xF, false));
-  const uint32_t hi = static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), CTRL, 0xF, 0xF, false));
-  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+__device__ __forceinline__ uint32_t max_dpp_u32(uint32_t v) {
+  const uint32_t o = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF, 0xF, false));
   return o > v ? o : v;
 }
 
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), lane);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// Wave-wide max of a 64-bit key, returned to every lane.  Within each row of
+// Wave-wide max of a 32-bit key, returned to every lane.  Within each row of
 // 16 lanes: quad swaps (xor 1, xor 2), then half-row and row mirrors; the four
 // row maxima are then read into scalar registers and combined.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_dpp<0xB1>(v);    // quad_perm [1,0,3,2]
-  v = max_dpp<0x4E>(v);    // quad_perm [2,3,0,1]
-  v = max_dpp<0x141>(v);   // row_half_mirror
-  v = max_dpp<0x140>(v);   // row_mirror
-  uint64_t a = readlane_u64(v, 0), b = readlane_u64(v, 16);
-  uint64_t c = readlane_u64(v, 32), d = readlane_u64(v, 48);
-  a = a > b ? a : b;
-  c = c > d ? c : d;
-  return a > c ? a : c;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max_dpp_u32<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = max_dpp_u32<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = max_dpp_u32<0x141>(v);   // row_half_mirror
+  v = max_dpp_u32<0x140>(v);   // row_mirror
+  const uint32_t a = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
+  const uint32_t b = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
+  const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
+  const uint32_t d = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
 }
 
-// Routes one token.  `lrow` points at its E logits.  On return lanes j < k hold
-// (expert of slot j, weight of slot j); other lanes hold (-1, 0).
-// R = candidate logits per lane (E <= 64 * R).
+// Routes one token from its logits already in registers: lane l holds the
+// logits of experts l + 64*i in v[i] (any value where l + 64*i >= E).  On
+// return lanes j < k hold (expert of slot j, weight of slot j); other lanes
+// hold (-1, 0).  R = candidate logits per lane (E <= 64 * R).
 template <int R>
-__device__ __forceinline__ void route_token(const float* __restrict__ lrow, int E, int k,
-                                            int* out_e, float* out_w) {
+__device__ __forceinline__ void route_token_regs(const float (&v)[R], int E, int k, int* out_e,
+                                                 float* out_w) {
   const int lane = lane_id();
-  uint64_t keys[R];
+  uint32_t keys[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int e = lane + kWave * i;
-    keys[i] = e < E ? (static_cast<uint64_t>(ordered_key(lrow[e])) << 32) |
-                          static_cast<uint64_t>(0xFFFFFFFFu - static_cast<uint32_t>(e))
-                    : 0ull;
-  }
+  for (int i = 0; i < R; ++i) keys[i] = lane + kWave * i < E ? ordered_key(v[i]) : 0u;
   int my_e = -1;
   float my_v = 0.0f;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
+    uint32_t best = 0;
 #pragma unroll
     for (int i = 0; i < R; ++i) best = keys[i] > best ? keys[i] : best;
-    best = wave_max_u64(best);
+    best = wave_max_u32(best);
+    // lowest expert holding the maximum: first i with a match, then its lowest lane
+    int sel = 0;
 #pragma unroll
-    for (int i = 0; i < R; ++i) keys[i] = keys[i] == best ? 0ull : keys[i];   // keys are unique
+    for (int i = R - 1; i >= 0; --i) {
+      const uint64_t b = __ballot(keys[i] == best);
+      sel = b ? kWave * i + __builtin_ctzll(b) : sel;
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) keys[i] = (lane + kWave * i == sel) ? 0u : keys[i];
     if (lane == r) {
-      my_e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best));
-      my_v = key_to_float(static_cast<uint32_t>(best >> 32));
+      my_e = sel;
+      my_v = key_to_float(best);
     }
   }
   const float v0 = __shfl(my_v, 0, kWave);
@@ -91,6 +87,26 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lrow, int 
   const float den = wave_sum(ex);
   *out_e = my_e;
   *out_w = lane < k ? ex / den : 0.0f;
+}
+
+// Loads the E logits of one token (lane l: experts l + 64*i).
+template <int R>
+__device__ __forceinline__ void load_logits(const float* __restrict__ lrow, int E, float (&v)[R]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int e = lane + kWave * i;
+    v[i] = e < E ? lrow[e] : 0.0f;
+  }
+}
+
+// Routes one token.  `lrow` points at its E logits.
+template <int R>
+__device__ __forceinline__ void route_token(const float* __restrict__ lrow, int E, int k,
+                                            int* out_e, float* out_w) {
+  float v[R];
+  load_logits<R>(lrow, E, v);
+  route_token_regs<R>(v, E, k, out_e, out_w);
 }
 
 // Dispatch on the number of candidates per lane (E <= 1024).
