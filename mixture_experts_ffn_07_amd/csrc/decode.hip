@@ -41,7 +41,8 @@ DecodeWs decode_ws_layout(int T, int H, int I, int E, int k) {
   (void)H;
   L.plan_u = o;      o += 256;
   L.plan_e = o;      o = align256(o + sizeof(int32_t) * E);
-  L.plan_mask = o;   o = align256(o + sizeof(uint64_t) * E);
+  L.plan_off = o;    o = align256(o + sizeof(int32_t) * (E + 1));
+  L.plan_pr = o;     o = align256(o + sizeof(uint16_t) * pairs);
   L.idx = o;         o = align256(o + sizeof(int32_t) * pairs);
   L.w = o;           o = align256(o + sizeof(float) * pairs);
   L.hw = o;          o = align256(o + 2 * pairs * I);
@@ -49,37 +50,24 @@ DecodeWs decode_ws_layout(int T, int H, int I, int E, int k) {
   return L;
 }
 
-// Position of the n-th set bit of m (n < popcount(m)), by halving.
-__device__ __forceinline__ int nth_set_bit(uint64_t m, int n) {
-  int pos = 0;
-  int c = __popcll(m & 0xFFFFFFFFull);
-  if (n >= c) { n -= c; m >>= 32; pos += 32; }
-  c = __popc(static_cast<uint32_t>(m) & 0xFFFFu);
-  if (n >= c) { n -= c; m >>= 16; pos += 16; }
-  c = __popc(static_cast<uint32_t>(m) & 0xFFu);
-  if (n >= c) { n -= c; m >>= 8; pos += 8; }
-  c = __popc(static_cast<uint32_t>(m) & 0xFu);
-  if (n >= c) { n -= c; m >>= 4; pos += 4; }
-  c = __popc(static_cast<uint32_t>(m) & 0x3u);
-  if (n >= c) { n -= c; m >>= 2; pos += 2; }
-  c = static_cast<int>(m & 1u);
-  if (n >= c) pos += 1;
-  return pos;
-}
-
-// Largest plan a workgroup stages in LDS (touched experts <= E <= 1024).
+// Largest plan a workgroup stages in LDS: touched experts <= E <= 1024,
+// routed pairs <= T*k <= 64*32.
 constexpr int kMaxPlan = 1024;
+constexpr int kMaxPairs = 64 * 32;
 
 // Touched-expert plan, built by every gate_up workgroup from the routing
-// result (T*k expert ids, L2-resident): s_e[u] = the u-th touched expert in
-// ascending order, s_m[u] = the mask of the tokens routed to it; returns the
-// count U.  `masks` (E words) and `coff` ((E + 63) / 64 ints) are LDS scratch.
-// The 64-bit masks are built with integer atomics (the result does not depend
-// on their order); the list is compacted with wave ballots, in expert order.
-__device__ int build_plan(const int32_t* __restrict__ idx, int T, int E, int k,
-                          uint64_t* masks, int* coff, int* s_e, uint64_t* s_m) {
-  const int nchunks = (E + kWave - 1) / kWave;
+// result (T*k expert ids, L2-resident), in compressed-row form:
+//   s_e[u]                  the u-th touched expert, ascending
+//   s_pr[s_off[u] .. s_off[u+1])  the pairs p = t*k + j routed to it, tokens ascending
+// Returns U.  `masks` (E words) and `scr` (E + 33 ints) are LDS scratch.  The
+// 64-bit token masks are built with integer atomics (the result does not
+// depend on their order); everything after is ordered compaction and scans.
+__device__ int build_plan(const int32_t* __restrict__ idx, int T, int E, int k, uint64_t* masks,
+                          int* scr, int* s_e, int* s_off, uint16_t* s_pr) {
+  const int nchunks = (E + kWave - 1) / kWave;      // <= 16
   const int nw = blockDim.x / kWave, wv = wave_id(), lane = lane_id();
+  int* map = scr;                                   // [E] expert -> plan position
+  int* coff = scr + E;                              // [17] chunk offsets, then per-chunk pair sums
   for (int i = threadIdx.x; i < E; i += blockDim.x) masks[i] = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < T * k; i += blockDim.x)
@@ -98,24 +86,57 @@ __device__ int build_plan(const int32_t* __restrict__ idx, int T, int E, int k,
       coff[c] = sum;
       sum += v;
     }
-    coff[nchunks] = sum;
+    coff[16] = sum;
   }
   __syncthreads();
+  const int U = coff[16];
+  // compaction: expert list and map; each chunk's token counts scanned within the wave
   for (int c = wv; c < nchunks; c += nw) {
     const int e = c * kWave + lane;
     const bool on = e < E && masks[e] != 0;
     const uint64_t b = __ballot(on);
+    const int cnt = on ? __popcll(masks[e]) : 0;
+    int incl = cnt;                                 // inclusive scan of counts over the chunk's lanes
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int v = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += v;
+    }
     if (on) {
       const int r = coff[c] + __popcll(b & ((1ull << lane) - 1));
       s_e[r] = e;
-      s_m[r] = masks[e];
+      map[e] = r;
+      s_off[r + 1] = incl;                          // chunk-local inclusive sum, fixed up below
     }
   }
-  const int U = coff[nchunks];
+  __syncthreads();
+  // pair totals of the chunks, scanned, added to the chunk-local sums
+  if (threadIdx.x == 0) {
+    int sum = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int last = (c + 1 < nchunks ? coff[c + 1] : U) - 1;   // last plan slot of chunk c
+      const int tot = last >= coff[c] ? s_off[last + 1] : 0;
+      scr[E + 17 + c] = sum;                         // (scratch past coff) chunk base
+      sum += tot;
+    }
+    s_off[0] = 0;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < U; r += blockDim.x) {
+    // chunk of plan slot r: largest c with coff[c] <= r
+    int c = 0;
+    while (c + 1 < nchunks && coff[c + 1] <= r) ++c;
+    s_off[r + 1] += scr[E + 17 + c];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
+    const int e = idx[i], t = i / k;
+    const int pos = s_off[map[e]] + __popcll(masks[e] & ((1ull << t) - 1));
+    s_pr[pos] = static_cast<uint16_t>(i);
+  }
   __syncthreads();
   return U;
 }
-
 
 // gate_up: work item = (touched expert u, block of 16 neurons); workgroups
 // stride over items.  Wave wv covers K range [wv*H/8, (wv+1)*H/8) in chunks
@@ -127,20 +148,26 @@ template <int TM, int KC>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_gate_up(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
     const int32_t* __restrict__ idx, const float* __restrict__ wts, int T, int E,
-    int* __restrict__ plan_u, int32_t* __restrict__ plan_e, uint64_t* __restrict__ plan_mask,
-    int H, int I, int k, uint16_t* __restrict__ hw) {
+    int* __restrict__ plan_u, int32_t* __restrict__ plan_e, int32_t* __restrict__ plan_off,
+    uint16_t* __restrict__ plan_pr, int H, int I, int k, uint16_t* __restrict__ hw) {
   extern __shared__ float red[];                    // [8 waves][TM][gate/up][4][64]
   __shared__ int s_e[kMaxPlan];
-  __shared__ uint64_t s_m[kMaxPlan];
-  // the plan's scratch (E masks + chunk offsets) borrows the reduction buffer
+  __shared__ int s_off[kMaxPlan + 1];
+  __shared__ uint16_t s_pr[kMaxPairs];
+  // the plan's scratch (E masks, E + 33 ints) borrows the reduction buffer
   const int U = build_plan(idx, T, E, k, reinterpret_cast<uint64_t*>(red),
-                           reinterpret_cast<int*>(reinterpret_cast<uint64_t*>(red) + E), s_e, s_m);
+                           reinterpret_cast<int*>(reinterpret_cast<uint64_t*>(red) + E), s_e,
+                           s_off, s_pr);
   if (blockIdx.x == 0) {                            // the plan for the down kernel
     for (int i = threadIdx.x; i < U; i += blockDim.x) {
       plan_e[i] = s_e[i];
-      plan_mask[i] = s_m[i];
+      plan_off[i + 1] = s_off[i + 1];
     }
-    if (threadIdx.x == 0) *plan_u = U;
+    for (int i = threadIdx.x; i < T * k; i += blockDim.x) plan_pr[i] = s_pr[i];
+    if (threadIdx.x == 0) {
+      plan_off[0] = 0;
+      *plan_u = U;
+    }
   }
   const int nrb = I / 16;
   const int items = U * nrb;
@@ -177,15 +204,14 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
     const int j = t / nch, c = t - j * nch;
     const int item = blockIdx.x + j * gridDim.x;
     const int u = item / nrb, rb = item - u * nrb;
-    const int e = s_e[u];
-    const uint64_t mask = s_m[u];
+    const int base = s_off[u];
     if (c == 0) {
-      ntok = __popcll(mask);
+      ntok = s_off[u + 1] - base;
       tiles = (ntok + 15) >> 4;
 #pragma unroll
       for (int q = 0; q < TM; ++q) {
         const int p = 16 * q + col;
-        tok[q] = nth_set_bit(mask, p < ntok ? p : 0);   // past the end: a valid token, column discarded
+        tok[q] = s_pr[base + (p < ntok ? p : 0)] / k;   // past the end: a valid token, column discarded
         ag[q] = au[q] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
@@ -228,11 +254,9 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
       }
       const int p = q * 16 + n;
       if (p < ntok) {
-        const int tt = nth_set_bit(mask, p);
-        int js = 0;
-        while (js < k - 1 && idx[tt * k + js] != e) ++js;
-        const float hv = wts[tt * k + js] * swiglu(g, up);
-        hw[static_cast<size_t>(tt * k + js) * I + rb * 16 + m] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+        const int pr = s_pr[base + p];               // pair t*k + j of this token and expert
+        const float hv = wts[pr] * swiglu(g, up);
+        hw[static_cast<size_t>(pr) * I + rb * 16 + m] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
       }
     }
     __syncthreads();
@@ -268,40 +292,20 @@ constexpr int kDownRows = 8;
 constexpr int kDownWaves = 16;
 constexpr int kDownThreads = kDownWaves * kWave;
 
-// Slot j of token t whose expert is e (the token routes to e exactly once):
-// a branch-free scan of the token's k expert ids, four at a time.
-__device__ __forceinline__ int slot_of(const int* s_idx_row, int k, int e) {
-  int js = 0;
-  for (int j0 = 0; j0 < k; j0 += 4) {
-    const int4 v = *reinterpret_cast<const int4*>(s_idx_row + j0);
-    js = (v.x == e) ? j0 : js;
-    js = (j0 + 1 < k && v.y == e) ? j0 + 1 : js;
-    js = (j0 + 2 < k && v.z == e) ? j0 + 2 : js;
-    js = (j0 + 3 < k && v.w == e) ? j0 + 3 : js;
-  }
-  return js;
-}
-
 template <int KD>
 __global__ __launch_bounds__(kDownThreads) void decode_down(
-    const uint16_t* __restrict__ wd, const int32_t* __restrict__ idx,
-    const int* __restrict__ plan_u, const int32_t* __restrict__ plan_e,
-    const uint64_t* __restrict__ plan_mask, const uint16_t* __restrict__ hw, int T, int H, int I,
+    const uint16_t* __restrict__ wd, const int* __restrict__ plan_u,
+    const int32_t* __restrict__ plan_e, const int32_t* __restrict__ plan_off,
+    const uint16_t* __restrict__ plan_pr, const uint16_t* __restrict__ hw, int T, int H, int I,
     int k, int KSW, uint16_t* __restrict__ out) {
   extern __shared__ float accl[];                   // [16 waves][T][8 dims]
-  __shared__ __align__(16) int s_idx[64 * 32];      // token rows padded to a multiple of 4
   __shared__ int s_e[kMaxPlan];
-  __shared__ uint64_t s_m[kMaxPlan];
+  __shared__ int s_off[kMaxPlan + 1];
+  __shared__ uint16_t s_pr[kMaxPairs];
   const int U = *plan_u;
-  const int kp = (k + 3) & ~3;                      // padded row length
-  for (int i = threadIdx.x; i < T * kp; i += blockDim.x) {
-    const int t = i / kp, j = i - t * kp;
-    s_idx[i] = j < k ? idx[t * k + j] : -1;
-  }
-  for (int i = threadIdx.x; i < U; i += blockDim.x) {
-    s_e[i] = plan_e[i];
-    s_m[i] = plan_mask[i];
-  }
+  for (int i = threadIdx.x; i < U; i += blockDim.x) s_e[i] = plan_e[i];
+  for (int i = threadIdx.x; i <= U; i += blockDim.x) s_off[i] = plan_off[i];
+  for (int i = threadIdx.x; i < T * k; i += blockDim.x) s_pr[i] = plan_pr[i];
   for (int i = threadIdx.x; i < kDownWaves * T * kDownRows; i += blockDim.x) accl[i] = 0.f;
   __syncthreads();
   const int wv = wave_id(), ln = lane_id();
@@ -317,60 +321,55 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
   const bf16x8 zero8 = {};
   const int ntask = U > eg ? (U - 1 - eg) / EGW + 1 : 0;
 
-  // activation row (element offset) of compact column c of expert e with token mask m
-  auto act_row = [&](uint64_t m, int e, int c, bool on) -> size_t {
-    const int t = on ? nth_set_bit(m, c) : 0;
-    const int js = on ? slot_of(s_idx + t * kp, k, e) : 0;
-    return static_cast<size_t>(t * k + js) * I + kb;
-  };
-  // add the tile's D rows 0..7 (lanes grp < 2) into the wave's accumulator rows
-  auto accumulate = [&](const f32x4& d, uint64_t m, int c, bool on) {
+  // add the tile's D rows 0..7 (lanes grp < 2) into token t's accumulator row
+  auto accumulate = [&](const f32x4& d, int t, bool on) {
     if (on && grp < 2) {
-      f32x4* a = reinterpret_cast<f32x4*>(myacc + nth_set_bit(m, c) * kDownRows + 4 * grp);
+      f32x4* a = reinterpret_cast<f32x4*>(myacc + t * kDownRows + 4 * grp);
       *a = *a + d;
     }
   };
   bf16x8 aA[KD], aB[KD], bA[KD], bB[KD];
-#define DN_ISSUE(A, B, TSK)                                                                \
+  int pA = 0, pB = 0;                               // pair of this lane's column in the first tile
+#define DN_ISSUE(A, B, P, TSK)                                                             \
   {                                                                                        \
     const int u_ = eg + (TSK) * EGW;                                                       \
-    const int e_ = s_e[u_];                                                                \
-    const uint64_t m_ = s_m[u_];                                                           \
-    const uint16_t* p_ = pw + static_cast<size_t>(e_) * H * I;                             \
+    const int base_ = s_off[u_];                                                           \
+    const uint16_t* p_ = pw + static_cast<size_t>(s_e[u_]) * H * I;                        \
     _Pragma("unroll") for (int s = 0; s < KD; ++s)                                         \
       A[s] = row_lane ? as_bf16x8(ld16(p_ + s * 32)) : zero8;                              \
-    const bool on_ = col < __popcll(m_);                                                   \
-    const size_t r_ = act_row(m_, e_, col, on_);                                           \
+    const bool on_ = col < s_off[u_ + 1] - base_;                                          \
+    P = on_ ? s_pr[base_ + col] : 0;                                                       \
+    const size_t r_ = static_cast<size_t>(P) * I + kb;                                     \
     _Pragma("unroll") for (int s = 0; s < KD; ++s)                                         \
       B[s] = on_ ? as_bf16x8(ld16(hw + r_ + s * 32)) : zero8;                              \
   }
-#define DN_RUN(A, B, TSK)                                                                  \
+#define DN_RUN(A, B, P, TSK)                                                               \
   {                                                                                        \
     const int u_ = eg + (TSK) * EGW;                                                       \
-    const int e_ = s_e[u_];                                                                \
-    const uint64_t m_ = s_m[u_];                                                           \
-    const int nt_ = __popcll(m_);                                                          \
+    const int base_ = s_off[u_];                                                           \
+    const int nt_ = s_off[u_ + 1] - base_;                                                 \
     f32x4 d_ = {0.f, 0.f, 0.f, 0.f};                                                       \
     _Pragma("unroll") for (int s = 0; s < KD; ++s) d_ = mfma16x16x32(A[s], B[s], d_);      \
-    accumulate(d_, m_, col, col < nt_);                                                    \
+    accumulate(d_, P / k, col < nt_);                                                      \
     for (int c0 = 16; c0 < nt_; c0 += 16) {           /* experts with over 16 tokens */    \
       const bool on_ = c0 + col < nt_;                                                     \
-      const size_t r_ = act_row(m_, e_, c0 + col, on_);                                    \
+      const int pr_ = on_ ? s_pr[base_ + c0 + col] : 0;                                    \
+      const size_t r_ = static_cast<size_t>(pr_) * I + kb;                                 \
       bf16x8 bx_[KD];                                                                      \
       _Pragma("unroll") for (int s = 0; s < KD; ++s)                                       \
         bx_[s] = on_ ? as_bf16x8(ld16(hw + r_ + s * 32)) : zero8;                          \
       f32x4 dx_ = {0.f, 0.f, 0.f, 0.f};                                                    \
       _Pragma("unroll") for (int s = 0; s < KD; ++s) dx_ = mfma16x16x32(A[s], bx_[s], dx_); \
-      accumulate(dx_, m_, c0 + col, on_);                                                  \
+      accumulate(dx_, pr_ / k, on_);                                                       \
     }                                                                                      \
   }
-  if (ntask > 0) DN_ISSUE(aA, bA, 0)
+  if (ntask > 0) DN_ISSUE(aA, bA, pA, 0)
   for (int t = 0; t < ntask; t += 2) {
-    if (t + 1 < ntask) DN_ISSUE(aB, bB, t + 1)
-    DN_RUN(aA, bA, t)
+    if (t + 1 < ntask) DN_ISSUE(aB, bB, pB, t + 1)
+    DN_RUN(aA, bA, pA, t)
     if (t + 1 < ntask) {
-      if (t + 2 < ntask) DN_ISSUE(aA, bA, t + 2)
-      DN_RUN(aB, bB, t + 1)
+      if (t + 2 < ntask) DN_ISSUE(aA, bA, pA, t + 2)
+      DN_RUN(aB, bB, pB, t + 1)
     }
   }
 #undef DN_ISSUE
@@ -392,7 +391,8 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   char* base = static_cast<char*>(ws);
   int* plan_u = reinterpret_cast<int*>(base + L.plan_u);
   int32_t* plan_e = reinterpret_cast<int32_t*>(base + L.plan_e);
-  uint64_t* plan_mask = reinterpret_cast<uint64_t*>(base + L.plan_mask);
+  int32_t* plan_off = reinterpret_cast<int32_t*>(base + L.plan_off);
+  uint16_t* plan_pr = reinterpret_cast<uint16_t*>(base + L.plan_pr);
   int32_t* idx_p = idx ? idx : reinterpret_cast<int32_t*>(base + L.idx);
   float* w_p = w ? w : reinterpret_cast<float*>(base + L.w);
   uint16_t* hw = reinterpret_cast<uint16_t*>(base + L.hw);
@@ -406,7 +406,7 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   const int grid1 = static_cast<int>(items_upper < grid_cap ? items_upper : grid_cap);
   // reduction buffer; the plan scratch (E masks + chunk offsets) must fit in it too
   size_t lds_gu = sizeof(float) * kDecWaves * TM * 2 * 256;
-  const size_t lds_plan = sizeof(uint64_t) * E + sizeof(int) * ((E + kWave - 1) / kWave + 1);
+  const size_t lds_plan = sizeof(uint64_t) * E + sizeof(int) * (E + 33);
   if (lds_plan > lds_gu) lds_gu = lds_plan;
   const size_t lds_dn = sizeof(float) * kDownWaves * T * kDownRows;
   const int gsteps = H / kDecWaves / 32;
@@ -422,7 +422,7 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   prof_begin(kDecGateUp, s);
 #define GU_LAUNCH(TMV, KCV)                                                                    \
   hipLaunchKernelGGL((decode_gate_up<TMV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x,   \
-                     wgu, idx_p, w_p, T, E, plan_u, plan_e, plan_mask, H, I, k, hw)
+                     wgu, idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw)
 #define GU_KC(TMV)                                        \
   switch (KC) {                                           \
     case 4: GU_LAUNCH(TMV, 4); break;                     \
@@ -436,8 +436,8 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   prof_end(kDecGateUp, s);
   prof_begin(kDecDown, s);
 #define DN_LAUNCH(KDV)                                                                         \
-  hipLaunchKernelGGL((decode_down<KDV>), grid2, dim3(kDownThreads), lds_dn, s, wd, idx_p, plan_u, \
-                     plan_e, plan_mask, hw, T, H, I, k, KSW, out)
+  hipLaunchKernelGGL((decode_down<KDV>), grid2, dim3(kDownThreads), lds_dn, s, wd, plan_u, plan_e, \
+                     plan_off, plan_pr, hw, T, H, I, k, KSW, out)
   switch (KD) {
     case 4: DN_LAUNCH(4); break;
     case 3: DN_LAUNCH(3); break;

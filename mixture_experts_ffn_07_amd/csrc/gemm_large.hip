@@ -202,9 +202,9 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
 #define RDF(PTR) as_bf16x8(*reinterpret_cast<const i32x4*>(PTR))
   // One MFMA K step on fragments (A, B): 8 groups of 2 MFMAs; group g then
   // reads fragment g of the next K step (stage RKT, step RKS) and, for g < NQ,
-  // writes staged chunk Q0+g of stage KT+1 to LDS and reloads that chunk from
-  // stage KT+2.  sched_barrier keeps this order.
-#define PHASE(A, B, NA, NB, RKT, RKS, KT, Q0, NQ) do {                                  \
+  // writes staged chunk Q0+g of stage WKT to LDS and reloads that chunk from
+  // stage WKT+1.  sched_barrier keeps this order.
+#define PHASE(A, B, NA, NB, RKT, RKS, WKT, Q0, NQ) do {                                 \
     const uint16_t* at_ = lds + ((RKT) & 1) * 2 * kLTile;                               \
     const uint16_t* bt_ = at_ + kLTile;                                                 \
     const int so_ = (((2 * (RKS) + hi) ^ swz) * 8);                                     \
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
       __builtin_amdgcn_sched_barrier(0);                                                \
       if (g < 4) NA[g] = RDF(&at_[fa[g] + so_]);                                        \
       else NB[g - 4] = RDF(&bt_[fb + 32 * (g - 4) * kLBK + so_]);                       \
-      if (g < (NQ)) { LWRITE((Q0) + g, (KT) + 1); GLOAD((Q0) + g, (KT) + 2); }          \
+      if (g < (NQ)) { LWRITE((Q0) + g, WKT); GLOAD((Q0) + g, (WKT) + 1); }              \
       __builtin_amdgcn_sched_barrier(0);                                                \
     }                                                                                   \
   } while (0)
@@ -227,13 +227,20 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  // prologue: stage 0 into LDS buffer 0, stage 1 into the staging registers
+  // The LDS writes of stage s+1 are spread over the four K steps that may
+  // write its buffer: the last step of stage s-1 (chunks 12..15, after the
+  // barrier that ends the reads of stage s-1) and the first three of stage s
+  // (chunks 0..11, before the barrier that publishes stage s+1).  Prologue:
+  // stage kb in LDS, chunks 12..15 of stage kb+1 in LDS, the staging registers
+  // holding chunks 0..11 of stage kb+1 and 12..15 of stage kb+2.
 #pragma unroll
   for (int q = 0; q < 16; ++q) GLOAD(q, kb);
 #pragma unroll
   for (int q = 0; q < 16; ++q) LWRITE(q, kb);
 #pragma unroll
   for (int q = 0; q < 16; ++q) GLOAD(q, kb + 1);
+#pragma unroll
+  for (int q = 12; q < 16; ++q) { LWRITE(q, kb + 1); GLOAD(q, kb + 2); }
   __syncthreads();
   bf16x8 a0[4], b0[4], a1[4], b1[4];
   {
@@ -245,13 +252,13 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     for (int g = 0; g < 4; ++g) b0[g] = RDF(&at[kLTile + fb + 32 * g * kLBK + so]);
   }
   for (int kt = kb; kt < ke; ++kt) {
-    PHASE(a0, b0, a1, b1, kt, 1, kt, 0, 6);
-    PHASE(a1, b1, a0, b0, kt, 2, kt, 6, 5);
-    PHASE(a0, b0, a1, b1, kt, 3, kt, 11, 5);
+    PHASE(a0, b0, a1, b1, kt, 1, kt + 1, 0, 4);
+    PHASE(a1, b1, a0, b0, kt, 2, kt + 1, 4, 4);
+    PHASE(a0, b0, a1, b1, kt, 3, kt + 1, 8, 4);
     // stage kt+1 is in LDS for every wave, and every wave is done reading stage kt
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
-    PHASE(a1, b1, a0, b0, kt + 1, 0, kt, 0, 0);
+    PHASE(a1, b1, a0, b0, kt + 1, 0, kt + 2, 12, 4);
   }
 #undef GLOAD
 #undef LWRITE
@@ -511,6 +518,11 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  // LDS writes of stage s+1 are split between the second K step of stage s-1
+  // (chunks 0..7) and the first of stage s (chunks 8..15 and the scales), as in
+  // the BF16 kernel.  Prologue: stage kb and chunks 0..7 of stage kb+1 in LDS;
+  // registers holding chunks 8..15 and the scales of stage kb+1 and chunks 0..7
+  // of stage kb+2.
 #pragma unroll
   for (int q = 0; q < 16; ++q) GLOAD(q, kb);
   SLOAD(kb);
@@ -520,6 +532,8 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
 #pragma unroll
   for (int q = 0; q < 16; ++q) GLOAD(q, kb + 1);
   SLOAD(kb + 1);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) { LWRITE(q, kb + 1); GLOAD(q, kb + 2); }
   __syncthreads();
   i32x8 f0[8], f1[8];          // fragments: [0..3] A, [4..7] B
   uint32_t sc[8], scn[8];      // scales of the current / next stage
@@ -527,21 +541,22 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
   for (int p = 0; p < 16; ++p) RDP(f0, p, kb, 0);
   RDS(sc, kb);
   for (int kt = kb; kt < ke; ++kt) {
-    // K step 0: MFMAs on f0; read K step 1 into f1; stage kt+1 to LDS, stage kt+2 loads
+    // K step 0: MFMAs on f0; read K step 1 into f1; chunks 8..15 and scales of
+    // stage kt+1 to LDS, each chunk reloaded from stage kt+2
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       const int i = g >> 2, j = g & 3;
       acc[i][j] = mfma_mx32<0>(f0[i], f0[4 + j], static_cast<int>(sc[i]), static_cast<int>(sc[4 + j]), acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
       RDP(f1, g, kt, 1);
-      LWRITE(g, kt + 1);
-      GLOAD(g, kt + 2);
-      if (g == 15) { SWRITE(kt + 1); SLOAD(kt + 2); }
+      if (g & 1) { LWRITE(8 + (g >> 1), kt + 1); GLOAD(8 + (g >> 1), kt + 2); }
+      if (g == 14) { SWRITE(kt + 1); SLOAD(kt + 2); }
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
-    // K step 1: MFMAs on f1; read K step 0 of stage kt+1 into f0, and its scales
+    // K step 1: MFMAs on f1; read K step 0 of stage kt+1 into f0, and its
+    // scales; chunks 0..7 of stage kt+2 to LDS, each reloaded from stage kt+3
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       const int i = g >> 2, j = g & 3;
@@ -549,6 +564,7 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
       __builtin_amdgcn_sched_barrier(0);
       RDP(f0, g, kt + 1, 0);
       if (g == 0) RDS(scn, kt + 1);
+      if (g & 1) { LWRITE(g >> 1, kt + 2); GLOAD(g >> 1, kt + 3); }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll

@@ -29,7 +29,7 @@ enum KernelId { kRoute = 1, kDecGateUp = 2, kDecDown = 3, kGroup = 4, kQuant = 5
 
 // Byte layout of the decode workspace.
 struct DecodeWs {
-  size_t plan_u, plan_e, plan_mask, idx, w, hw, total;
+  size_t plan_u, plan_e, plan_off, plan_pr, idx, w, hw, total;
 };
 DecodeWs decode_ws_layout(int T, int H, int I, int E, int k);
 
