@@ -41,11 +41,14 @@ CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 # as null until the counters are taken again.
 TRAFFIC = {
     ("decode_gate_up", "qwen3-decode-T32"): (
-        709.8e6, ("decode.hip", "common.h", "route.h"), "6314d70b7fa1f954",
+        709.3e6, ('decode.hip', 'common.h', 'internal.h'), "fe71f57aeb281214",
         "profiles/decode_gate_up_qwen3-decode-T32.md"),
     ("gemm_gate_up", "kimi-bf16-T2048"): (
-        24.770e9, ("batched.hip", "common.h"), "6e25d430d57455a6",
+        24685.2e6, ('batched.hip', 'common.h', 'tiles.h'), "32e32395354f7707",
         "profiles/gemm_gate_up_kimi-bf16-T2048.md"),
+    ("gemm_gate_up", "kimi-bf16-ep64share"): (
+        2485.7e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "8ae64901ab3f19cd",
+        "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
 }
 
 

@@ -23,7 +23,6 @@
 // atomics (the only atomic is an integer OR that builds expert token masks).
 #include "common.h"
 #include "internal.h"
-#include "route.h"
 
 namespace moe {
 
