@@ -275,21 +275,36 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
 // down: workgroup = 8 output dimensions d0..d0+7 of every touched expert (H/8
 // workgroups, enough to occupy every CU without splitting the expert sum
-// across workgroups).  MFMA rows 0..7 carry those dimensions; lanes of rows
-// 8..15 issue no weight loads (the MFMA work they waste is free: the kernel
-// is bound by memory).  MFMA columns are the tokens routed to the current
-// expert, compacted (16 per tile), so every activation load is a routed
-// token's row and each expert costs one tile of loads and MFMAs (more only
-// for the rare expert with over 16 tokens).  Each wave adds an expert's
-// results into its own FP32 accumulator rows in LDS ([token][8 dims]), in
-// ascending expert order; the 16 waves' accumulators are added in wave order
+// across workgroups).  The 16x16x32 MFMA is used as two 8x8 products side by
+// side: rows 0..7 and 8..15 both carry the dimensions d0..d0+7, rows 0..7
+// with the first 32 of each 64 K positions and rows 8..15 with the second,
+// and columns 0..7 / 8..15 carry the same tokens' matching K halves.  The two
+// diagonal 8x8 blocks of D are the wanted partial sums (the off-diagonal
+// blocks are discarded), so every lane's weight load is useful: per step a
+// wave reads 8 rows x 128 contiguous bytes.  The tokens are those routed to
+// the current expert (compacted plan columns).  A dense load (64 lanes, 16
+// bytes each) brings the wave's K range of several tokens at once into a
+// small wave-private LDS tile, from which the lanes read the MFMA layout.
+// Each wave adds an expert's results into its own FP32 accumulator rows in
+// LDS ([token][8 dims]), in ascending expert order, first the half-0 block
+// then the half-1 block; the 16 waves' accumulators are added in wave order
 // at the end, so the sum order is fixed.  The 16 waves form EGW expert groups
 // x KSW K-slices: wave (eg, ks) takes experts u = eg, eg + EGW, ... and the K
-// range [ks*I/KSW, (ks+1)*I/KSW) of each, loading the next expert's weights
-// and first activation tile while it multiplies the current one.
+// range [ks*I/KSW, (ks+1)*I/KSW) of each (64*KD positions), loading the next
+// expert's weights and activations while it multiplies the current one.
 constexpr int kDownRows = 8;
 constexpr int kDownWaves = 16;
 constexpr int kDownThreads = kDownWaves * kWave;
+
+// per-KD geometry of the activation staging tile
+template <int KD>
+struct DownGeom {
+  static constexpr int kCh = 8 * KD;                // 16-byte chunks of one token's K range
+  static constexpr int kPerLoad = kWave / kCh;      // tokens one dense load covers
+  static constexpr int kTW = 2 * kPerLoad < 8 ? 2 * kPerLoad : 8;   // tokens per MFMA tile
+  static constexpr int kRow = kCh + 1;              // padded tile row (chunks): no bank conflicts
+  static constexpr int kStage = kTW * kRow;         // chunks per wave
+};
 
 template <int KD>
 __global__ __launch_bounds__(kDownThreads) void decode_down(
@@ -297,82 +312,129 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     const int32_t* __restrict__ plan_e, const int32_t* __restrict__ plan_off,
     const uint16_t* __restrict__ plan_pr, const uint16_t* __restrict__ hw, int T, int H, int I,
     int k, int KSW, uint16_t* __restrict__ out) {
-  extern __shared__ float accl[];                   // [16 waves][T][8 dims]
-  __shared__ int s_e[kMaxPlan];
-  __shared__ int s_off[kMaxPlan + 1];
+  using G = DownGeom<KD>;
+  // dynamic LDS: [16 waves][T][8 dims] FP32 accumulators, then [16 waves][kStage] chunks
+  extern __shared__ float accl[];
+  __shared__ uint16_t s_e[kMaxPlan];                // E <= 1024
+  __shared__ uint16_t s_off[kMaxPlan + 1];          // <= T*k <= 2048
   __shared__ uint16_t s_pr[kMaxPairs];
+  __shared__ uint8_t s_tk[kMaxPairs];               // token of each plan entry (T <= 64)
   const int U = *plan_u;
-  for (int i = threadIdx.x; i < U; i += blockDim.x) s_e[i] = plan_e[i];
-  for (int i = threadIdx.x; i <= U; i += blockDim.x) s_off[i] = plan_off[i];
-  for (int i = threadIdx.x; i < T * k; i += blockDim.x) s_pr[i] = plan_pr[i];
+  for (int i = threadIdx.x; i < U; i += blockDim.x) s_e[i] = static_cast<uint16_t>(plan_e[i]);
+  for (int i = threadIdx.x; i <= U; i += blockDim.x) s_off[i] = static_cast<uint16_t>(plan_off[i]);
+  for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
+    const int pr = plan_pr[i];
+    s_pr[i] = static_cast<uint16_t>(pr);
+    s_tk[i] = static_cast<uint8_t>(pr / k);
+  }
   for (int i = threadIdx.x; i < kDownWaves * T * kDownRows; i += blockDim.x) accl[i] = 0.f;
   __syncthreads();
-  const int wv = wave_id(), ln = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
   const int col = ln & 15, grp = ln >> 4;
+  const int hf = col >> 3, c8 = col & 7;            // K half and row / token within it
   const int EGW = kDownWaves / KSW;
   const int ks = wv % KSW, eg = wv / KSW;
-  const bool row_lane = col < kDownRows;
   const int d0 = blockIdx.x * kDownRows;
-  const int kw = I / KSW;                           // = KD * 32
-  const uint32_t kb = static_cast<uint32_t>(ks * kw + grp * 8);
-  const uint16_t* pw = wd + (static_cast<size_t>(d0) + (row_lane ? col : 0)) * I + kb;
+  const int kw = I / KSW;                           // = 64 * KD
+  // weights: lane (row c8, half hf, group grp), step s -> K offset 64s + 32hf + 8grp
+  const uint32_t woff = static_cast<uint32_t>((d0 + c8) * I + ks * kw + hf * 32 + grp * 8);
   float* myacc = accl + wv * T * kDownRows;
-  const bf16x8 zero8 = {};
+  i32x4* stage = reinterpret_cast<i32x4*>(accl + kDownWaves * T * kDownRows) + wv * G::kStage;
+  // dense activation loads: lane = token slot dc, chunk dq of the wave's K range
+  const int dc = ln / G::kCh, dq = ln - dc * G::kCh;
+  const bool ld_lane = dc < G::kPerLoad;
+  const uint32_t kd = static_cast<uint32_t>(ks * kw + dq * 8);
+  i32x4* st0 = stage + dc * G::kRow + dq;           // this lane's slot for the first load
+  i32x4* st1 = st0 + G::kPerLoad * G::kRow;         // and for the second
+  // MFMA B lane (token c8, half hf, group grp): chunk 8s + 4hf + grp; tokens past the
+  // tile read a valid row whose columns are discarded
+  const i32x4* bsrc = stage + (c8 < G::kTW ? c8 : G::kTW - 1) * G::kRow + 4 * hf + grp;
+  // D: lane (column col, group grp) holds rows 4grp..4grp+3; the wanted block is
+  // group half == column half, token c8, dims 4*(grp&1)..+3
+  const bool d_lane = (grp >> 1) == hf;
+  const int dofs = 4 * (grp & 1);
   const int ntask = U > eg ? (U - 1 - eg) / EGW + 1 : 0;
 
-  // add the tile's D rows 0..7 (lanes grp < 2) into token t's accumulator row
-  auto accumulate = [&](const f32x4& d, int t, bool on) {
-    if (on && grp < 2) {
-      f32x4* a = reinterpret_cast<f32x4*>(myacc + t * kDownRows + 4 * grp);
-      *a = *a + d;
+  bf16x8 aA[KD], aB[KD];
+  i32x4 hA0 = {}, hA1 = {}, hB0 = {}, hB1 = {};
+  // activations of tokens [c0, c0 + kPerLoad) of the plan entries at `base` (nt of them):
+  // every lane loads (lanes past the tokens repeat token c0), so the load count is fixed
+  auto load_h0 = [&](int base, int c0, int nt) {
+    const int slot = ld_lane && c0 + dc < nt ? c0 + dc : c0;
+    return ld16(hw + static_cast<uint32_t>(s_pr[base + slot] * I + kd));
+  };
+  // tokens [c0 + kPerLoad, c0 + kTW), loaded only when some exist
+  auto load_h1 = [&](int base, int c0, int nt, i32x4& h1) {
+    if (G::kTW > G::kPerLoad && nt - c0 > G::kPerLoad) {
+      const int c1 = c0 + G::kPerLoad;
+      const int slot = ld_lane && c1 + dc < nt ? c1 + dc : c1;
+      h1 = ld16(hw + static_cast<uint32_t>(s_pr[base + slot] * I + kd));
     }
   };
-  bf16x8 aA[KD], aB[KD], bA[KD], bB[KD];
-  int pA = 0, pB = 0;                               // pair of this lane's column in the first tile
-#define DN_ISSUE(A, B, P, TSK)                                                             \
-  {                                                                                        \
-    const int u_ = eg + (TSK) * EGW;                                                       \
-    const int base_ = s_off[u_];                                                           \
-    const uint16_t* p_ = pw + static_cast<size_t>(s_e[u_]) * H * I;                        \
-    _Pragma("unroll") for (int s = 0; s < KD; ++s)                                         \
-      A[s] = row_lane ? as_bf16x8(ld16(p_ + s * 32)) : zero8;                              \
-    const bool on_ = col < s_off[u_ + 1] - base_;                                          \
-    P = on_ ? s_pr[base_ + col] : 0;                                                       \
-    const size_t r_ = static_cast<size_t>(P) * I + kb;                                     \
-    _Pragma("unroll") for (int s = 0; s < KD; ++s)                                         \
-      B[s] = on_ ? as_bf16x8(ld16(hw + r_ + s * 32)) : zero8;                              \
-  }
-#define DN_RUN(A, B, P, TSK)                                                               \
-  {                                                                                        \
-    const int u_ = eg + (TSK) * EGW;                                                       \
-    const int base_ = s_off[u_];                                                           \
-    const int nt_ = s_off[u_ + 1] - base_;                                                 \
-    f32x4 d_ = {0.f, 0.f, 0.f, 0.f};                                                       \
-    _Pragma("unroll") for (int s = 0; s < KD; ++s) d_ = mfma16x16x32(A[s], B[s], d_);      \
-    accumulate(d_, P / k, col < nt_);                                                      \
-    for (int c0 = 16; c0 < nt_; c0 += 16) {           /* experts with over 16 tokens */    \
-      const bool on_ = c0 + col < nt_;                                                     \
-      const int pr_ = on_ ? s_pr[base_ + c0 + col] : 0;                                    \
-      const size_t r_ = static_cast<size_t>(pr_) * I + kb;                                 \
-      bf16x8 bx_[KD];                                                                      \
-      _Pragma("unroll") for (int s = 0; s < KD; ++s)                                       \
-        bx_[s] = on_ ? as_bf16x8(ld16(hw + r_ + s * 32)) : zero8;                          \
-      f32x4 dx_ = {0.f, 0.f, 0.f, 0.f};                                                    \
-      _Pragma("unroll") for (int s = 0; s < KD; ++s) dx_ = mfma16x16x32(A[s], bx_[s], dx_); \
-      accumulate(dx_, pr_ / k, on_);                                                       \
-    }                                                                                      \
-  }
-  if (ntask > 0) DN_ISSUE(aA, bA, pA, 0)
-  for (int t = 0; t < ntask; t += 2) {
-    if (t + 1 < ntask) DN_ISSUE(aB, bB, pB, t + 1)
-    DN_RUN(aA, bA, pA, t)
+  auto task_plan = [&](int tsk, int& base, int& nt, int& e) {
+    const int u = eg + tsk * EGW;
+    base = __builtin_amdgcn_readfirstlane(s_off[u]);
+    nt = __builtin_amdgcn_readfirstlane(s_off[u + 1]) - base;
+    e = __builtin_amdgcn_readfirstlane(s_e[u]);
+  };
+  // loads of one task in a fixed order: first activations, weights, optional activations
+  auto issue = [&](int tsk, bf16x8 (&A)[KD], i32x4& h0, i32x4& h1) {
+    int base, nt, e;
+    task_plan(tsk, base, nt, e);
+    h0 = load_h0(base, 0, nt);
+    const uint16_t* pe = wd + static_cast<size_t>(e) * H * I;
+#pragma unroll
+    for (int s = 0; s < KD; ++s) A[s] = as_bf16x8(ld16(pe + woff + s * 64));
+    load_h1(base, 0, nt, h1);
+  };
+  // stage tokens [c0, c0 + kTW) (already loaded into h0, h1), multiply, accumulate
+  auto tile = [&](const bf16x8 (&A)[KD], int base, int c0, int nt, const i32x4& h0,
+                  const i32x4& h1) {
+    if (ld_lane) {
+      *st0 = h0;
+      if (G::kTW > G::kPerLoad) *st1 = h1;
+    }
+    __builtin_amdgcn_wave_barrier();
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KD; ++s) d = mfma16x16x32(A[s], as_bf16x8(bsrc[8 * s]), d);
+    const bool on = d_lane && c8 < G::kTW && c0 + c8 < nt;
+    const int t = on ? s_tk[base + c0 + c8] : 0;
+    f32x4* acc = reinterpret_cast<f32x4*>(myacc + t * kDownRows + dofs);
+    if (on && hf == 0) *acc = *acc + d;             // half-0 block, then half-1 block
+    __builtin_amdgcn_wave_barrier();
+    if (on && hf == 1) *acc = *acc + d;
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto run = [&](int tsk, const bf16x8 (&A)[KD], const i32x4& h0, const i32x4& h1) {
+    int base, nt, e;
+    task_plan(tsk, base, nt, e);
+    tile(A, base, 0, nt, h0, h1);                   // every touched expert has a token
+    for (int c0 = G::kTW; c0 < nt; c0 += G::kTW) {  // experts with more than kTW tokens
+      i32x4 r1 = {};
+      const i32x4 r0 = load_h0(base, c0, nt);
+      load_h1(base, c0, nt, r1);
+      tile(A, base, c0, nt, r0, r1);
+    }
+  };
+  // one task ahead: the loads of task t+1 are in flight while task t multiplies
+  if (ntask > 0) {
+    issue(0, aA, hA0, hA1);
+    int t = 0;
+    for (; t + 2 < ntask; t += 2) {
+      issue(t + 1, aB, hB0, hB1);
+      run(t, aA, hA0, hA1);
+      issue(t + 2, aA, hA0, hA1);
+      run(t + 1, aB, hB0, hB1);
+    }
     if (t + 1 < ntask) {
-      if (t + 2 < ntask) DN_ISSUE(aA, bA, pA, t + 2)
-      DN_RUN(aB, bB, pB, t + 1)
+      issue(t + 1, aB, hB0, hB1);
+      run(t, aA, hA0, hA1);
+      run(t + 1, aB, hB0, hB1);
+    } else {
+      run(t, aA, hA0, hA1);
     }
   }
-#undef DN_ISSUE
-#undef DN_RUN
   __syncthreads();
   for (int i = threadIdx.x; i < T * kDownRows; i += blockDim.x) {
     float v = 0.f;
@@ -381,6 +443,14 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     const int t = i / kDownRows, mm = i - t * kDownRows;
     out[static_cast<size_t>(t) * H + d0 + mm] = static_cast<uint16_t>(f32_to_bf16_rne(v));
   }
+}
+
+// dynamic LDS of decode_down<KD>
+inline size_t down_lds_bytes(int T, int KD) {
+  const int stage = KD == 3 ? DownGeom<3>::kStage
+                  : KD == 4 ? DownGeom<4>::kStage
+                  : KD == 5 ? DownGeom<5>::kStage : DownGeom<7>::kStage;
+  return sizeof(float) * kDownWaves * T * kDownRows + sizeof(i32x4) * kDownWaves * stage;
 }
 
 hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t* wgu,
@@ -407,16 +477,19 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   size_t lds_gu = sizeof(float) * kDecWaves * TM * 2 * 256;
   const size_t lds_plan = sizeof(uint64_t) * E + sizeof(int) * (E + 33);
   if (lds_plan > lds_gu) lds_gu = lds_plan;
-  const size_t lds_dn = sizeof(float) * kDownWaves * T * kDownRows;
   const int gsteps = H / kDecWaves / 32;
   int KC = gsteps % 4 == 0 ? 4 : (gsteps % 3 == 0 ? 3 : (gsteps % 2 == 0 ? 2 : 1));
   if (TM == 4 && KC == 4) KC = 2;                   // keeps four token tiles within 128 VGPRs
-  // down: K-slices per workgroup so that each wave has at most 4 steps of 32
-  // (I is a multiple of 256, so I/32 is a multiple of 8 and KSW <= 16 works)
-  const int dtotal = I / 32;
+  // down: K-slices per workgroup (a power of two, so that the 16 waves split into
+  // expert groups), the fewest that leave each wave at most 4 steps of 64; I is a
+  // multiple of 256 up to 2048, so I/64 is 4, 8, ..., 32, and the two sizes with no
+  // such split (I = 1280, 1792) take 4 slices of 5 or 7 steps
+  const int dtotal = I / 64;
   int KSW = 1;
-  while (KSW < kDownWaves && (dtotal / KSW > 4 || dtotal % KSW)) KSW *= 2;
+  while (KSW < 8 && (dtotal / KSW > 4 || dtotal % KSW)) KSW *= 2;
+  if (dtotal % KSW) KSW = 4;
   const int KD = dtotal / KSW;
+  const size_t lds_dn = down_lds_bytes(T, KD);
   const dim3 grid2(H / kDownRows);
   prof_begin(kDecGateUp, s);
 #define GU_LAUNCH(TMV, KCV)                                                                    \
@@ -438,10 +511,11 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   hipLaunchKernelGGL((decode_down<KDV>), grid2, dim3(kDownThreads), lds_dn, s, wd, plan_u, plan_e, \
                      plan_off, plan_pr, hw, T, H, I, k, KSW, out)
   switch (KD) {
-    case 4: DN_LAUNCH(4); break;
     case 3: DN_LAUNCH(3); break;
-    case 2: DN_LAUNCH(2); break;
-    default: DN_LAUNCH(1); break;
+    case 4: DN_LAUNCH(4); break;
+    case 5: DN_LAUNCH(5); break;
+    case 7: DN_LAUNCH(7); break;
+    default: return hipErrorInvalidValue;            // not reachable for valid I
   }
 #undef DN_LAUNCH
   prof_end(kDecDown, s);
@@ -457,6 +531,17 @@ hipError_t decode_set_attributes() {
   for (const void* f : tm4) {
     e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                             sizeof(float) * kDecWaves * 4 * 2 * 256);
+    if (e != hipSuccess) return e;
+  }
+  // down at T = 64: accumulators plus the staging tiles exceed 64 KB
+  const void* dn[] = {reinterpret_cast<const void*>(decode_down<3>),
+                      reinterpret_cast<const void*>(decode_down<4>),
+                      reinterpret_cast<const void*>(decode_down<5>),
+                      reinterpret_cast<const void*>(decode_down<7>)};
+  const int kds[] = {3, 4, 5, 7};
+  for (int i = 0; i < 4; ++i) {
+    e = hipFuncSetAttribute(dn[i], hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(down_lds_bytes(64, kds[i])));
     if (e != hipSuccess) return e;
   }
   return e;
