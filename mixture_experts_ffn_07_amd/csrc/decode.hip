@@ -137,26 +137,44 @@ __device__ int build_plan(const int32_t* __restrict__ idx, int T, int E, int k, 
   return U;
 }
 
-// gate_up: work item = (touched expert u, block of 16 neurons); workgroups
-// stride over items.  Wave wv covers K range [wv*H/8, (wv+1)*H/8) in chunks
-// of KC steps of 32 (KC divides the steps).  The workgroup walks its flat
-// sequence of (item, chunk) tasks with the weights of the next task loaded
-// into a second register buffer while the current one is multiplied, so the
-// weight stream never waits on an epilogue.
-template <int TM, int KC>
+// gate_up: work item = (touched expert u, block of NB = 8*NG neurons);
+// workgroups stride over items.  The K dimension H is cut into steps of 64
+// positions and the eight waves share them (wave wv takes steps
+// [wv*S/8, (wv+1)*S/8), S = H/64), walking them in chunks of KC steps.
+//
+// MFMA layout (two 8x8 products per 16x16x32 instruction): A rows 0..7 are
+// the 8 neurons of a neuron group with the first 32 positions of a step, rows
+// 8..15 the same neurons with the second 32; B columns 0..7 / 8..15 are up to
+// 8 tokens with the same two halves.  The diagonal 8x8 blocks of D are the
+// wanted partial sums, added together once per item.  With this layout every
+// weight load instruction reads 8 rows x 128 contiguous bytes (whole cache
+// lines, streamed with the non-temporal hint) and every activation load 8
+// tokens x 128 bytes.
+//
+// The workgroup walks its flat sequence of (item, chunk) tasks with the
+// weights of the next task loaded into a second register buffer while the
+// current one is multiplied, so the weight stream never waits on an epilogue.
+template <int TM8, int NG, int KC>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_gate_up(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
     const int32_t* __restrict__ idx, const float* __restrict__ wts, int T, int E,
     int* __restrict__ plan_u, int32_t* __restrict__ plan_e, int32_t* __restrict__ plan_off,
     uint16_t* __restrict__ plan_pr, int H, int I, int k, uint16_t* __restrict__ hw) {
-  extern __shared__ float red[];                    // [8 waves][TM][gate/up][4][64]
+  constexpr int NB = 8 * NG;                        // neurons per item
+  constexpr bool kPx = TM8 < 8;                     // prefetch the first tile's activations
+  // two buffers (alternate items) of [8 waves][TM8 tiles][NG groups][gate/up][4 regs]
+  // [16 lanes] FP32 per-wave sums
+  extern __shared__ float red[];
   __shared__ int s_e[kMaxPlan];
   __shared__ int s_off[kMaxPlan + 1];
   __shared__ uint16_t s_pr[kMaxPairs];
+  __shared__ float s_w[kMaxPairs];                  // routing weight of each plan entry
   // the plan's scratch (E masks, E + 33 ints) borrows the reduction buffer
   const int U = build_plan(idx, T, E, k, reinterpret_cast<uint64_t*>(red),
                            reinterpret_cast<int*>(reinterpret_cast<uint64_t*>(red) + E), s_e,
                            s_off, s_pr);
+  // (the epilogues then issue no global loads, which would wait on the weight stream)
+  for (int i = threadIdx.x; i < T * k; i += kDecThreads) s_w[i] = wts[s_pr[i]];
   if (blockIdx.x == 0) {                            // the plan for the down kernel
     for (int i = threadIdx.x; i < U; i += blockDim.x) {
       plan_e[i] = s_e[i];
@@ -168,109 +186,207 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
       *plan_u = U;
     }
   }
-  const int nrb = I / 16;
+  const int nrb = I / NB;
   const int items = U * nrb;
-  const int wv = wave_id(), ln = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
   const int col = ln & 15, grp = ln >> 4;
-  const int kw = H / kDecWaves;
-  const int nch = kw / 32 / KC;                     // chunks per item
+  const int hf = col >> 3, c8 = col & 7;
+  const int S = H / 64;                             // steps of 64 positions
+  const int s0 = wv * S / kDecWaves, s1 = (wv + 1) * S / kDecWaves;
+  const int nch = (s1 - s0) / KC;                   // chunks per item (KC divides s1 - s0)
   const int my_items = blockIdx.x < items ? (items - 1 - blockIdx.x) / gridDim.x + 1 : 0;
-  const int ntask = my_items * nch;
-  const uint32_t kb = static_cast<uint32_t>(wv * kw + grp * 8);
+  // lane's K offset within a step: half hf, 16-byte group grp
+  const uint32_t kl = static_cast<uint32_t>(s0 * 64 + hf * 32 + grp * 8);
+  const size_t up_off = static_cast<size_t>(I) * H;
 
-  // weight row offset (elements) of task t's gate row for this lane
+  auto item_of = [&](int j, int& u, int& rb) {
+    const int item = blockIdx.x + j * gridDim.x;
+    u = item / nrb;
+    rb = item - u * nrb;
+  };
+  // first weight element of task t (item j, chunk c) for this lane: gate row of group 0
   auto task_w = [&](int t) -> const uint16_t* {
     const int j = t / nch, c = t - j * nch;
-    const int item = blockIdx.x + j * gridDim.x;
-    const int u = item / nrb, rb = item - u * nrb;
-    return wgu + (static_cast<size_t>(s_e[u]) * 2 * I + rb * 16 + col) * H + kb + c * KC * 32;
+    int u, rb;
+    item_of(j, u, rb);
+    const int e = __builtin_amdgcn_readfirstlane(s_e[u]);
+    return wgu + (static_cast<size_t>(e) * 2 * I + rb * NB + c8) * H + kl + c * KC * 64;
   };
-  bf16x8 gA[KC], uA[KC], gB[KC], uB[KC];
-  const size_t up_off = static_cast<size_t>(I) * H;
-#define GU_ISSUE(G, UU, T)                                             \
-  {                                                                    \
-    const uint16_t* pg_ = task_w(T);                                   \
-    _Pragma("unroll") for (int s = 0; s < KC; ++s) {                   \
-      G[s] = as_bf16x8(ld16(pg_ + s * 32));                            \
-      UU[s] = as_bf16x8(ld16(pg_ + up_off + s * 32));                  \
-    }                                                                  \
-  }
-  f32x4 ag[TM], au[TM];
-  int tok[TM];
-  int ntok = 0, tiles = 0;
-
-  auto run_task = [&](const bf16x8 (&G)[KC], const bf16x8 (&UU)[KC], int t) {
+  bf16x8 gA[KC][NG], uA[KC][NG], gB[KC][NG], uB[KC][NG];
+  bf16x8 xA[KC], xB[KC];                            // first token tile's activations
+  uint32_t itk = 0;                                 // this lane's first-tile token, issue side
+  // loads of task t: weights, then the first token tile's activations
+  auto issue = [&](int t, bf16x8 (&G)[KC][NG], bf16x8 (&UU)[KC][NG], bf16x8 (&XT)[KC]) {
     const int j = t / nch, c = t - j * nch;
-    const int item = blockIdx.x + j * gridDim.x;
-    const int u = item / nrb, rb = item - u * nrb;
-    const int base = s_off[u];
-    if (c == 0) {
-      ntok = s_off[u + 1] - base;
-      tiles = (ntok + 15) >> 4;
+    if (kPx && c == 0) {                            // a new item: its first tile's tokens
+      int u, rb;
+      item_of(j, u, rb);
+      const int b = __builtin_amdgcn_readfirstlane(s_off[u]);
+      const int n = __builtin_amdgcn_readfirstlane(s_off[u + 1]) - b;
+      itk = static_cast<uint32_t>(s_pr[b + (c8 < n ? c8 : 0)] / k);
+    }
+    const uint16_t* pg = task_w(t);
 #pragma unroll
-      for (int q = 0; q < TM; ++q) {
-        const int p = 16 * q + col;
-        tok[q] = s_pr[base + (p < ntok ? p : 0)] / k;   // past the end: a valid token, column discarded
-        ag[q] = au[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < KC; ++s) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        G[s][g] = as_bf16x8(ld16_stream(pg + static_cast<size_t>(g * 8) * H + s * 64));
+        UU[s][g] = as_bf16x8(ld16_stream(pg + up_off + static_cast<size_t>(g * 8) * H + s * 64));
       }
     }
-    const uint32_t ko = kb + c * KC * 32;
+    if (kPx) {
+      const uint32_t xo = itk * static_cast<uint32_t>(H) + kl + c * KC * 64;
 #pragma unroll
-    for (int q = 0; q < TM; ++q) {
-      if (q < tiles) {
-        bf16x8 xb[KC];
-#pragma unroll
-        for (int s = 0; s < KC; ++s) xb[s] = as_bf16x8(ld16(x + static_cast<size_t>(tok[q]) * H + ko + s * 32));
-#pragma unroll
-        for (int s = 0; s < KC; ++s) {
-          ag[q] = mfma16x16x32(G[s], xb[s], ag[q]);
-          au[q] = mfma16x16x32(UU[s], xb[s], au[q]);
-        }
-      }
+      for (int s = 0; s < KC; ++s) XT[s] = as_bf16x8(ld16(x + xo + s * 64));
     }
-    if (c != nch - 1) return;
-    // epilogue of the item: fixed-order sum over waves, SwiGLU, weight, split, store
+  };
+  f32x4 ag[TM8][NG], au[TM8][NG];
+  uint32_t tkp[(TM8 + 3) / 4];                      // lane's token per tile, packed bytes (T <= 64)
+  int ntok = 0, tiles = 0, base = 0;
+
+  // item epilogue: add the two half blocks, then the waves in order; SwiGLU,
+  // routing weight, BF16 store.  `have` = this wave holds sums (else zeros).
+  // One barrier per item: the buffer alternates, and a wave passes item j+1's
+  // barrier only after every wave has finished reading item j's sums.
+  auto epilogue = [&](int j, bool have) {
+    int u, rb;
+    item_of(j, u, rb);
+    const int b0 = __builtin_amdgcn_readfirstlane(s_off[u]);
+    const int nt = __builtin_amdgcn_readfirstlane(s_off[u + 1]) - b0, nq = (nt + 7) >> 3;
+    float* rbuf = red + (j & 1) * (kDecWaves * TM8 * NG * 128);
+    const bool wl = col < 8 && grp < 2;             // lanes holding the half-0 block
+    const int li = c8 + 8 * grp;
 #pragma unroll
-    for (int q = 0; q < TM; ++q) {
-      if (q < tiles) {
+    for (int q = 0; q < TM8; ++q) {
+      if (q < nq) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          red[(((wv * TM + q) * 2 + 0) * 4 + r) * 64 + ln] = ag[q][r];
-          red[(((wv * TM + q) * 2 + 1) * 4 + r) * 64 + ln] = au[q][r];
+        for (int g = 0; g < NG; ++g) {
+          f32x4 vg = have ? ag[q][g] : f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 vu = have ? au[q][g] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {           // half-1 block sits 40 lanes up
+            vg[r] += __shfl_down(vg[r], 40, kWave);
+            vu[r] += __shfl_down(vu[r], 40, kWave);
+          }
+          if (wl) {
+            float* dst = rbuf + (((wv * TM8 + q) * NG + g) * 2) * 64 + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              dst[r * 16] = vg[r];
+              dst[64 + r * 16] = vu[r];
+            }
+          }
         }
       }
     }
     __syncthreads();
-    for (int qq = threadIdx.x; qq < tiles * 256; qq += blockDim.x) {
-      const int q = qq >> 8, within = qq & 255;
-      const int n = within >> 4, m = within & 15;    // token column n, weight row m
-      const int src = 16 * (m >> 2) + n, r = m & 3;
-      float g = 0.f, up = 0.f;
+    // one element per thread (TM8 * 8 * NB <= 512): straight-line code, so the
+    // compiler has no store loop to drain the weight loads in flight before
+    static_assert(TM8 * 8 * NB <= kDecThreads, "one reduction element per thread");
+    const int qq = threadIdx.x;
+    if (qq < nq * 8 * NB) {
+      const int q = qq / (8 * NB), within = qq - q * (8 * NB);
+      const int n = within / NB, m = within - n * NB;   // token n of the tile, neuron m
+      const int g = m >> 3, mm = m & 7;
+      const int r = mm & 3, lsrc = n + 8 * (mm >> 2);
+      float gs = 0.f, us = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < kDecWaves; ++w2) {
-        g += red[(((w2 * TM + q) * 2 + 0) * 4 + r) * 64 + src];
-        up += red[(((w2 * TM + q) * 2 + 1) * 4 + r) * 64 + src];
+        const float* src = rbuf + (((w2 * TM8 + q) * NG + g) * 2) * 64 + r * 16 + lsrc;
+        gs += src[0];
+        us += src[64];
       }
-      const int p = q * 16 + n;
-      if (p < ntok) {
-        const int pr = s_pr[base + p];               // pair t*k + j of this token and expert
-        const float hv = wts[pr] * swiglu(g, up);
-        hw[static_cast<size_t>(pr) * I + rb * 16 + m] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+      const int p = q * 8 + n;
+      if (p < nt) {
+        const int pr = s_pr[b0 + p];                 // pair t*k + j of this token and expert
+        const float hv = s_w[b0 + p] * swiglu(gs, us);
+        hw[static_cast<size_t>(pr) * I + rb * NB + m] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
       }
     }
-    __syncthreads();
   };
 
-  if (ntask > 0) GU_ISSUE(gA, uA, 0)
-  for (int t = 0; t < ntask; t += 2) {
-    if (t + 1 < ntask) GU_ISSUE(gB, uB, t + 1)
-    run_task(gA, uA, t);
+  auto run_task = [&](const bf16x8 (&G)[KC][NG], const bf16x8 (&UU)[KC][NG],
+                      const bf16x8 (&XT)[KC], int t) {
+    const int j = t / nch, c = t - j * nch;
+    if (c == 0) {
+      int u, rb;
+      item_of(j, u, rb);
+      base = __builtin_amdgcn_readfirstlane(s_off[u]);
+      ntok = __builtin_amdgcn_readfirstlane(s_off[u + 1]) - base;
+      tiles = (ntok + 7) >> 3;
+#pragma unroll
+      for (int q = 0; q < (TM8 + 3) / 4; ++q) tkp[q] = 0;
+#pragma unroll
+      for (int q = 0; q < TM8; ++q) {
+        const int p = 8 * q + c8;                   // past the end: a valid token, column discarded
+        const uint32_t tk = static_cast<uint32_t>(s_pr[base + (p < ntok ? p : 0)] / k);
+        tkp[q >> 2] |= tk << (8 * (q & 3));
+#pragma unroll
+        for (int g = 0; g < NG; ++g) ag[q][g] = au[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < TM8; ++q) {
+      if (q < tiles) {
+        bf16x8 xb[KC];
+        if (kPx && q == 0) {
+#pragma unroll
+          for (int s = 0; s < KC; ++s) xb[s] = XT[s];
+        } else {                                    // later tiles: experts with over 8 tokens
+          const uint32_t tk = (tkp[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+          const uint32_t xo = tk * static_cast<uint32_t>(H) + kl + c * KC * 64;
+#pragma unroll
+          for (int s = 0; s < KC; ++s) xb[s] = as_bf16x8(ld16(x + xo + s * 64));
+        }
+#pragma unroll
+        for (int s = 0; s < KC; ++s) {
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            ag[q][g] = mfma16x16x32(G[s][g], xb[s], ag[q][g]);
+            au[q][g] = mfma16x16x32(UU[s][g], xb[s], au[q][g]);
+          }
+        }
+      }
+    }
+    if (c == nch - 1) epilogue(j, true);
+  };
+
+  if (nch == 0) {                                   // no K steps for this wave (H < 512)
+    for (int j = 0; j < my_items; ++j) epilogue(j, false);
+    return;
+  }
+  // one task ahead: the loads of task t+1 are in flight while task t multiplies.
+  // The steady-state loop issues unconditionally, so the compiler's waits leave
+  // the next task's loads in flight; the 8-tile variant, whose accumulators take
+  // half the registers, uses the compact loop (one copy of each task body).
+  const int ntask = my_items * nch;
+  if constexpr (TM8 == 8) {
+    if (ntask > 0) issue(0, gA, uA, xA);
+    for (int t = 0; t < ntask; t += 2) {
+      if (t + 1 < ntask) issue(t + 1, gB, uB, xB);
+      run_task(gA, uA, xA, t);
+      if (t + 1 < ntask) {
+        if (t + 2 < ntask) issue(t + 2, gA, uA, xA);
+        run_task(gB, uB, xB, t + 1);
+      }
+    }
+  } else if (ntask > 0) {
+    issue(0, gA, uA, xA);
+    int t = 0;
+    for (; t + 2 < ntask; t += 2) {
+      issue(t + 1, gB, uB, xB);
+      run_task(gA, uA, xA, t);
+      issue(t + 2, gA, uA, xA);
+      run_task(gB, uB, xB, t + 1);
+    }
     if (t + 1 < ntask) {
-      if (t + 2 < ntask) GU_ISSUE(gA, uA, t + 2)
-      run_task(gB, uB, t + 1);
+      issue(t + 1, gB, uB, xB);
+      run_task(gA, uA, xA, t);
+      run_task(gB, uB, xB, t + 1);
+    } else {
+      run_task(gA, uA, xA, t);
     }
   }
-#undef GU_ISSUE
 }
 
 // down: workgroup = 8 output dimensions d0..d0+7 of every touched expert (H/8
@@ -384,7 +500,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     h0 = load_h0(base, 0, nt);
     const uint16_t* pe = wd + static_cast<size_t>(e) * H * I;
 #pragma unroll
-    for (int s = 0; s < KD; ++s) A[s] = as_bf16x8(ld16(pe + woff + s * 64));
+    for (int s = 0; s < KD; ++s) A[s] = as_bf16x8(ld16_stream(pe + woff + s * 64));
     load_h1(base, 0, nt, h1);
   };
   // stage tokens [c0, c0 + kTW) (already loaded into h0, h1), multiply, accumulate
@@ -453,6 +569,11 @@ inline size_t down_lds_bytes(int T, int KD) {
   return sizeof(float) * kDownWaves * T * kDownRows + sizeof(i32x4) * kDownWaves * stage;
 }
 
+// dynamic LDS of decode_gate_up<TM8, NG, KC>: the per-wave reduction sums
+inline size_t gate_up_lds_bytes(int TM8, int NG) {
+  return 2 * sizeof(float) * kDecWaves * TM8 * NG * 2 * 4 * 16;
+}
+
 hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t* wgu,
                          const uint16_t* wd, int T, int H, int I, int E, int k, uint16_t* out,
                          int32_t* idx, float* w, void* ws, hipStream_t s, int num_cus) {
@@ -469,17 +590,20 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   hipError_t err = launch_route_topk(logits, T, E, k, idx_p, w_p, s);   // brackets kRoute
   if (err != hipSuccess) return err;
 
-  const int TM = T <= 16 ? 1 : (T <= 32 ? 2 : 4);   // token tiles the kernels carry
-  const long items_upper = static_cast<long>(T * k < E ? T * k : E) * (I / 16);
+  // gate_up: 8-token tiles the kernel carries, neuron groups per item, steps per chunk
+  const int TM8 = T <= 8 ? 1 : (T <= 16 ? 2 : (T <= 32 ? 4 : 8));
+  // register budget (128 per lane): weights of two tasks + 16*NG accumulators per tile
+  const int NG = TM8 <= 2 ? 2 : 1;
+  const int S = H / 64;                             // a multiple of 4
+  // two steps per chunk when every wave's step count is even and registers allow
+  const int KC = (S % 16 == 0 && (TM8 == 1 || TM8 == 4)) ? 2 : 1;
+  const long items_upper = static_cast<long>(T * k < E ? T * k : E) * (I / (8 * NG));
   const long grid_cap = 2L * num_cus;
   const int grid1 = static_cast<int>(items_upper < grid_cap ? items_upper : grid_cap);
   // reduction buffer; the plan scratch (E masks + chunk offsets) must fit in it too
-  size_t lds_gu = sizeof(float) * kDecWaves * TM * 2 * 256;
+  size_t lds_gu = gate_up_lds_bytes(TM8, NG);
   const size_t lds_plan = sizeof(uint64_t) * E + sizeof(int) * (E + 33);
   if (lds_plan > lds_gu) lds_gu = lds_plan;
-  const int gsteps = H / kDecWaves / 32;
-  int KC = gsteps % 4 == 0 ? 4 : (gsteps % 3 == 0 ? 3 : (gsteps % 2 == 0 ? 2 : 1));
-  if (TM == 4 && KC == 4) KC = 2;                   // keeps four token tiles within 128 VGPRs
   // down: K-slices per workgroup (a power of two, so that the 16 waves split into
   // expert groups), the fewest that leave each wave at most 4 steps of 64; I is a
   // multiple of 256 up to 2048, so I/64 is 4, 8, ..., 32, and the two sizes with no
@@ -492,18 +616,18 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   const size_t lds_dn = down_lds_bytes(T, KD);
   const dim3 grid2(H / kDownRows);
   prof_begin(kDecGateUp, s);
-#define GU_LAUNCH(TMV, KCV)                                                                    \
-  hipLaunchKernelGGL((decode_gate_up<TMV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x,   \
-                     wgu, idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw)
-#define GU_KC(TMV)                                        \
-  switch (KC) {                                           \
-    case 4: GU_LAUNCH(TMV, 4); break;                     \
-    case 3: GU_LAUNCH(TMV, 3); break;                     \
-    case 2: GU_LAUNCH(TMV, 2); break;                     \
-    default: GU_LAUNCH(TMV, 1); break;                    \
+#define GU_LAUNCH(TMV, NGV, KCV)                                                               \
+  hipLaunchKernelGGL((decode_gate_up<TMV, NGV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, \
+                     x, wgu, idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw)
+  if (TM8 == 1) {
+    if (KC == 2) GU_LAUNCH(1, 2, 2); else GU_LAUNCH(1, 2, 1);
+  } else if (TM8 == 2) {
+    GU_LAUNCH(2, 2, 1);
+  } else if (TM8 == 4) {
+    if (KC == 2) GU_LAUNCH(4, 1, 2); else GU_LAUNCH(4, 1, 1);
+  } else {
+    GU_LAUNCH(8, 1, 1);
   }
-  if (TM == 1) { GU_KC(1) } else if (TM == 2) { GU_KC(2) } else { GU_KC(4) }
-#undef GU_KC
 #undef GU_LAUNCH
   prof_end(kDecGateUp, s);
   prof_begin(kDecDown, s);
@@ -523,16 +647,7 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
 }
 
 hipError_t decode_set_attributes() {
-  const void* tm4[] = {reinterpret_cast<const void*>(decode_gate_up<4, 1>),
-                       reinterpret_cast<const void*>(decode_gate_up<4, 2>),
-                       reinterpret_cast<const void*>(decode_gate_up<4, 3>),
-                       reinterpret_cast<const void*>(decode_gate_up<4, 4>)};
   hipError_t e = hipSuccess;
-  for (const void* f : tm4) {
-    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            sizeof(float) * kDecWaves * 4 * 2 * 256);
-    if (e != hipSuccess) return e;
-  }
   // down at T = 64: accumulators plus the staging tiles exceed 64 KB
   const void* dn[] = {reinterpret_cast<const void*>(decode_down<3>),
                       reinterpret_cast<const void*>(decode_down<4>),
