@@ -137,6 +137,20 @@ __device__ int build_plan(const int32_t* __restrict__ idx, int T, int E, int k, 
   return U;
 }
 
+// Workgroup 0 of gate_up writes the plan to global memory for the down kernel.
+__device__ void publish_plan(int U, int P, const int* s_e, const int* s_off, const uint16_t* s_pr,
+                             int* plan_u, int32_t* plan_e, int32_t* plan_off, uint16_t* plan_pr) {
+  for (int i = threadIdx.x; i < U; i += blockDim.x) {
+    plan_e[i] = s_e[i];
+    plan_off[i + 1] = s_off[i + 1];
+  }
+  for (int i = threadIdx.x; i < P; i += blockDim.x) plan_pr[i] = s_pr[i];
+  if (threadIdx.x == 0) {
+    plan_off[0] = 0;
+    *plan_u = U;
+  }
+}
+
 // gate_up: work item = (touched expert u, block of NB = 8*NG neurons);
 // workgroups stride over items.  The K dimension H is cut into steps of 64
 // positions and the eight waves share them (wave wv takes steps
@@ -154,14 +168,13 @@ __device__ int build_plan(const int32_t* __restrict__ idx, int T, int E, int k, 
 // The workgroup walks its flat sequence of (item, chunk) tasks with the
 // weights of the next task loaded into a second register buffer while the
 // current one is multiplied, so the weight stream never waits on an epilogue.
-template <int TM8, int NG, int KC>
+template <int TM8, int NG, int KC>   // TM8 <= 4: T <= 32
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_gate_up(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
     const int32_t* __restrict__ idx, const float* __restrict__ wts, int T, int E,
     int* __restrict__ plan_u, int32_t* __restrict__ plan_e, int32_t* __restrict__ plan_off,
     uint16_t* __restrict__ plan_pr, int H, int I, int k, uint16_t* __restrict__ hw) {
   constexpr int NB = 8 * NG;                        // neurons per item
-  constexpr bool kPx = TM8 < 8;                     // prefetch the first tile's activations
   // two buffers (alternate items) of [8 waves][TM8 tiles][NG groups][gate/up][4 regs]
   // [16 lanes] FP32 per-wave sums
   extern __shared__ float red[];
@@ -175,17 +188,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
                            s_off, s_pr);
   // (the epilogues then issue no global loads, which would wait on the weight stream)
   for (int i = threadIdx.x; i < T * k; i += kDecThreads) s_w[i] = wts[s_pr[i]];
-  if (blockIdx.x == 0) {                            // the plan for the down kernel
-    for (int i = threadIdx.x; i < U; i += blockDim.x) {
-      plan_e[i] = s_e[i];
-      plan_off[i + 1] = s_off[i + 1];
-    }
-    for (int i = threadIdx.x; i < T * k; i += blockDim.x) plan_pr[i] = s_pr[i];
-    if (threadIdx.x == 0) {
-      plan_off[0] = 0;
-      *plan_u = U;
-    }
-  }
+  if (blockIdx.x == 0) publish_plan(U, T * k, s_e, s_off, s_pr, plan_u, plan_e, plan_off, plan_pr);
   const int nrb = I / NB;
   const int items = U * nrb;
   const int wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   // loads of task t: weights, then the first token tile's activations
   auto issue = [&](int t, bf16x8 (&G)[KC][NG], bf16x8 (&UU)[KC][NG], bf16x8 (&XT)[KC]) {
     const int j = t / nch, c = t - j * nch;
-    if (kPx && c == 0) {                            // a new item: its first tile's tokens
+    if (c == 0) {                                   // a new item: its first tile's tokens
       int u, rb;
       item_of(j, u, rb);
       const int b = __builtin_amdgcn_readfirstlane(s_off[u]);
@@ -234,11 +237,9 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
         UU[s][g] = as_bf16x8(ld16_stream(pg + up_off + static_cast<size_t>(g * 8) * H + s * 64));
       }
     }
-    if (kPx) {
-      const uint32_t xo = itk * static_cast<uint32_t>(H) + kl + c * KC * 64;
+    const uint32_t xo = itk * static_cast<uint32_t>(H) + kl + c * KC * 64;
 #pragma unroll
-      for (int s = 0; s < KC; ++s) XT[s] = as_bf16x8(ld16(x + xo + s * 64));
-    }
+    for (int s = 0; s < KC; ++s) XT[s] = as_bf16x8(ld16(x + xo + s * 64));
   };
   f32x4 ag[TM8][NG], au[TM8][NG];
   uint32_t tkp[(TM8 + 3) / 4];                      // lane's token per tile, packed bytes (T <= 64)
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
     for (int q = 0; q < TM8; ++q) {
       if (q < tiles) {
         bf16x8 xb[KC];
-        if (kPx && q == 0) {
+        if (q == 0) {
 #pragma unroll
           for (int s = 0; s < KC; ++s) xb[s] = XT[s];
         } else {                                    // later tiles: experts with over 8 tokens
@@ -357,20 +358,9 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   }
   // one task ahead: the loads of task t+1 are in flight while task t multiplies.
   // The steady-state loop issues unconditionally, so the compiler's waits leave
-  // the next task's loads in flight; the 8-tile variant, whose accumulators take
-  // half the registers, uses the compact loop (one copy of each task body).
+  // the next task's loads in flight.
   const int ntask = my_items * nch;
-  if constexpr (TM8 == 8) {
-    if (ntask > 0) issue(0, gA, uA, xA);
-    for (int t = 0; t < ntask; t += 2) {
-      if (t + 1 < ntask) issue(t + 1, gB, uB, xB);
-      run_task(gA, uA, xA, t);
-      if (t + 1 < ntask) {
-        if (t + 2 < ntask) issue(t + 2, gA, uA, xA);
-        run_task(gB, uB, xB, t + 1);
-      }
-    }
-  } else if (ntask > 0) {
+  if (ntask > 0) {
     issue(0, gA, uA, xA);
     int t = 0;
     for (; t + 2 < ntask; t += 2) {
@@ -385,6 +375,148 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
       run_task(gB, uB, xB, t + 1);
     } else {
       run_task(gA, uA, xA, t);
+    }
+  }
+}
+
+// gate_up for batches with many tokens per expert (T > 32): work item =
+// (touched expert u, 16 neurons), MFMA rows = 16 neurons (gate and up
+// separately), columns = 16 tokens, so an expert with up to 64 tokens takes
+// four column tiles and each weight load serves 16 tokens per MFMA.  Each
+// weight load reads 16 rows x 64 bytes, so the loads stay plain (the second
+// half of each 128-byte line comes with the next step, from the cache).  Wave
+// wv covers K range [wv*H/8, (wv+1)*H/8) in chunks of KC steps of 32; tasks
+// and the one-ahead weight buffer as in the narrow kernel.
+template <int KC>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_gate_up_wide(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
+    const int32_t* __restrict__ idx, const float* __restrict__ wts, int T, int E,
+    int* __restrict__ plan_u, int32_t* __restrict__ plan_e, int32_t* __restrict__ plan_off,
+    uint16_t* __restrict__ plan_pr, int H, int I, int k, uint16_t* __restrict__ hw) {
+  constexpr int TM = 4;                             // 16-token tiles (T <= 64)
+  extern __shared__ float red[];                    // [8 waves][TM][gate/up][4][64]
+  __shared__ int s_e[kMaxPlan];
+  __shared__ int s_off[kMaxPlan + 1];
+  __shared__ uint16_t s_pr[kMaxPairs];
+  const int U = build_plan(idx, T, E, k, reinterpret_cast<uint64_t*>(red),
+                           reinterpret_cast<int*>(reinterpret_cast<uint64_t*>(red) + E), s_e,
+                           s_off, s_pr);
+  if (blockIdx.x == 0) publish_plan(U, T * k, s_e, s_off, s_pr, plan_u, plan_e, plan_off, plan_pr);
+  const int nrb = I / 16;
+  const int items = U * nrb;
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
+  const int col = ln & 15, grp = ln >> 4;
+  const int kw = H / kDecWaves;
+  const int nch = kw / 32 / KC;                     // chunks per item
+  const int my_items = blockIdx.x < items ? (items - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int ntask = my_items * nch;
+  const uint32_t kb = static_cast<uint32_t>(wv * kw + grp * 8);
+
+  auto task_w = [&](int t) -> const uint16_t* {
+    const int j = t / nch, c = t - j * nch;
+    const int item = blockIdx.x + j * gridDim.x;
+    const int u = item / nrb, rb = item - u * nrb;
+    const int e = __builtin_amdgcn_readfirstlane(s_e[u]);
+    return wgu + (static_cast<size_t>(e) * 2 * I + rb * 16 + col) * H + kb + c * KC * 32;
+  };
+  bf16x8 gA[KC], uA[KC], gB[KC], uB[KC];
+  const size_t up_off = static_cast<size_t>(I) * H;
+  auto issue = [&](int t, bf16x8 (&G)[KC], bf16x8 (&UU)[KC]) {
+    const uint16_t* pg = task_w(t);
+#pragma unroll
+    for (int s = 0; s < KC; ++s) {
+      G[s] = as_bf16x8(ld16(pg + s * 32));
+      UU[s] = as_bf16x8(ld16(pg + up_off + s * 32));
+    }
+  };
+  f32x4 ag[TM], au[TM];
+  int tok[TM];
+  int ntok = 0, tiles = 0;
+  float wl[2];                                      // routing weights of this thread's two epilogue elements
+
+  auto run_task = [&](const bf16x8 (&G)[KC], const bf16x8 (&UU)[KC], int t) {
+    const int j = t / nch, c = t - j * nch;
+    const int item = blockIdx.x + j * gridDim.x;
+    const int u = item / nrb, rb = item - u * nrb;
+    const int base = __builtin_amdgcn_readfirstlane(s_off[u]);
+    if (c == 0) {
+      ntok = __builtin_amdgcn_readfirstlane(s_off[u + 1]) - base;
+      tiles = (ntok + 15) >> 4;
+#pragma unroll
+      for (int q = 0; q < TM; ++q) {
+        const int p = 16 * q + col;
+        tok[q] = s_pr[base + (p < ntok ? p : 0)] / k;   // past the end: a valid token, column discarded
+        ag[q] = au[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      // loaded here, long before the epilogue needs them, so that waiting for them
+      // does not wait for the weight loads issued in between
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int qq = threadIdx.x + h * kDecThreads;
+        const int p = (qq >> 8) * 16 + ((qq & 255) >> 4);
+        wl[h] = qq < tiles * 256 && p < ntok ? wts[s_pr[base + p]] : 0.f;
+      }
+    }
+    const uint32_t ko = kb + c * KC * 32;
+#pragma unroll
+    for (int q = 0; q < TM; ++q) {
+      if (q < tiles) {
+        bf16x8 xb[KC];
+#pragma unroll
+        for (int s = 0; s < KC; ++s)
+          xb[s] = as_bf16x8(ld16(x + static_cast<uint32_t>(tok[q] * H) + ko + s * 32));
+#pragma unroll
+        for (int s = 0; s < KC; ++s) {
+          ag[q] = mfma16x16x32(G[s], xb[s], ag[q]);
+          au[q] = mfma16x16x32(UU[s], xb[s], au[q]);
+        }
+      }
+    }
+    if (c != nch - 1) return;
+    // epilogue of the item: fixed-order sum over waves, SwiGLU, weight, store
+#pragma unroll
+    for (int q = 0; q < TM; ++q) {
+      if (q < tiles) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          red[(((wv * TM + q) * 2 + 0) * 4 + r) * 64 + ln] = ag[q][r];
+          red[(((wv * TM + q) * 2 + 1) * 4 + r) * 64 + ln] = au[q][r];
+        }
+      }
+    }
+    __syncthreads();
+    // at most TM*256 = 1024 elements: two per thread, unrolled (no store loop)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int qq = threadIdx.x + h * kDecThreads;
+      if (qq < tiles * 256) {
+        const int q = qq >> 8, within = qq & 255;
+        const int n = within >> 4, m = within & 15;  // token column n, weight row m
+        const int src = 16 * (m >> 2) + n, r = m & 3;
+        float g = 0.f, up = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kDecWaves; ++w2) {
+          g += red[(((w2 * TM + q) * 2 + 0) * 4 + r) * 64 + src];
+          up += red[(((w2 * TM + q) * 2 + 1) * 4 + r) * 64 + src];
+        }
+        const int p = q * 16 + n;
+        if (p < ntok) {
+          const int pr = s_pr[base + p];
+          const float hv = wl[h] * swiglu(g, up);
+          hw[static_cast<size_t>(pr) * I + rb * 16 + m] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+        }
+      }
+    }
+    __syncthreads();
+  };
+
+  if (ntask > 0) issue(0, gA, uA);
+  for (int t = 0; t < ntask; t += 2) {
+    if (t + 1 < ntask) issue(t + 1, gB, uB);
+    run_task(gA, uA, t);
+    if (t + 1 < ntask) {
+      if (t + 2 < ntask) issue(t + 2, gA, uA);
+      run_task(gB, uB, t + 1);
     }
   }
 }
@@ -590,18 +722,22 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   hipError_t err = launch_route_topk(logits, T, E, k, idx_p, w_p, s);   // brackets kRoute
   if (err != hipSuccess) return err;
 
-  // gate_up: 8-token tiles the kernel carries, neuron groups per item, steps per chunk
-  const int TM8 = T <= 8 ? 1 : (T <= 16 ? 2 : (T <= 32 ? 4 : 8));
+  // gate_up: T <= 32 takes the narrow kernel (8-token tiles, full-line streamed
+  // weights); T > 32 the wide one (16-token tiles)
+  const bool wide = T > 32;
+  const int TM8 = T <= 8 ? 1 : (T <= 16 ? 2 : 4);
   // register budget (128 per lane): weights of two tasks + 16*NG accumulators per tile
   const int NG = TM8 <= 2 ? 2 : 1;
   const int S = H / 64;                             // a multiple of 4
   // two steps per chunk when every wave's step count is even and registers allow
   const int KC = (S % 16 == 0 && (TM8 == 1 || TM8 == 4)) ? 2 : 1;
-  const long items_upper = static_cast<long>(T * k < E ? T * k : E) * (I / (8 * NG));
+  const int gsteps = H / kDecWaves / 32;            // wide kernel: steps of 32 per wave
+  const int KCW = gsteps % 2 == 0 ? 2 : 1;
+  const long items_upper = static_cast<long>(T * k < E ? T * k : E) * (I / (wide ? 16 : 8 * NG));
   const long grid_cap = 2L * num_cus;
   const int grid1 = static_cast<int>(items_upper < grid_cap ? items_upper : grid_cap);
   // reduction buffer; the plan scratch (E masks + chunk offsets) must fit in it too
-  size_t lds_gu = gate_up_lds_bytes(TM8, NG);
+  size_t lds_gu = wide ? sizeof(float) * kDecWaves * 4 * 2 * 256 : gate_up_lds_bytes(TM8, NG);
   const size_t lds_plan = sizeof(uint64_t) * E + sizeof(int) * (E + 33);
   if (lds_plan > lds_gu) lds_gu = lds_plan;
   // down: K-slices per workgroup (a power of two, so that the 16 waves split into
@@ -619,15 +755,19 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
 #define GU_LAUNCH(TMV, NGV, KCV)                                                               \
   hipLaunchKernelGGL((decode_gate_up<TMV, NGV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, \
                      x, wgu, idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw)
-  if (TM8 == 1) {
+#define GU_WIDE(KCV)                                                                            \
+  hipLaunchKernelGGL((decode_gate_up_wide<KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x, wgu, \
+                     idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw)
+  if (wide) {
+    if (KCW == 2) GU_WIDE(2); else GU_WIDE(1);
+  } else if (TM8 == 1) {
     if (KC == 2) GU_LAUNCH(1, 2, 2); else GU_LAUNCH(1, 2, 1);
   } else if (TM8 == 2) {
     GU_LAUNCH(2, 2, 1);
-  } else if (TM8 == 4) {
-    if (KC == 2) GU_LAUNCH(4, 1, 2); else GU_LAUNCH(4, 1, 1);
   } else {
-    GU_LAUNCH(8, 1, 1);
+    if (KC == 2) GU_LAUNCH(4, 1, 2); else GU_LAUNCH(4, 1, 1);
   }
+#undef GU_WIDE
 #undef GU_LAUNCH
   prof_end(kDecGateUp, s);
   prof_begin(kDecDown, s);
