@@ -521,25 +521,28 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   }
 }
 
-// down: workgroup = 8 output dimensions d0..d0+7 of every touched expert (H/8
-// workgroups, enough to occupy every CU without splitting the expert sum
-// across workgroups).  The 16x16x32 MFMA is used as two 8x8 products side by
-// side: rows 0..7 and 8..15 both carry the dimensions d0..d0+7, rows 0..7
-// with the first 32 of each 64 K positions and rows 8..15 with the second,
-// and columns 0..7 / 8..15 carry the same tokens' matching K halves.  The two
-// diagonal 8x8 blocks of D are the wanted partial sums (the off-diagonal
-// blocks are discarded), so every lane's weight load is useful: per step a
-// wave reads 8 rows x 128 contiguous bytes.  The tokens are those routed to
-// the current expert (compacted plan columns).  A dense load (64 lanes, 16
-// bytes each) brings the wave's K range of several tokens at once into a
-// small wave-private LDS tile, from which the lanes read the MFMA layout.
-// Each wave adds an expert's results into its own FP32 accumulator rows in
-// LDS ([token][8 dims]), in ascending expert order, first the half-0 block
-// then the half-1 block; the 16 waves' accumulators are added in wave order
-// at the end, so the sum order is fixed.  The 16 waves form EGW expert groups
-// x KSW K-slices: wave (eg, ks) takes experts u = eg, eg + EGW, ... and the K
-// range [ks*I/KSW, (ks+1)*I/KSW) of each (64*KD positions), loading the next
-// expert's weights and activations while it multiplies the current one.
+// down: workgroup = 8*NR output dimensions of every touched expert (NR = 1 or
+// 2 groups of 8; H/(8*NR) workgroups, enough to occupy every CU without
+// splitting the expert sum across workgroups).  The 16x16x32 MFMA is used as
+// two 8x8 products side by side: rows 0..7 and 8..15 both carry the 8
+// dimensions of a group, rows 0..7 with the first 32 of each 64 K positions
+// and rows 8..15 with the second, and columns 0..7 / 8..15 carry the same
+// tokens' matching K halves.  The two diagonal 8x8 blocks of D are the wanted
+// partial sums (the off-diagonal blocks are discarded), so every lane's weight
+// load is useful: per step a wave reads 8 rows x 128 contiguous bytes per
+// group.  The tokens are those routed to the current expert (compacted plan
+// columns).  A dense load (64 lanes, 16 bytes each) brings the wave's K range
+// of several tokens at once into a small wave-private LDS tile, from which
+// the lanes read the MFMA layout; with two groups one activation load serves
+// both (the activations are re-read by every workgroup, so wider workgroups
+// halve that traffic where H leaves enough of them).  Each wave adds an
+// expert's results into its own FP32 accumulator rows in LDS ([token][8*NR
+// dims]), in ascending expert order, first the half-0 block then the half-1
+// block; the 16 waves' accumulators are added in wave order at the end, so the
+// sum order is fixed.  The 16 waves form EGW expert groups x KSW K-slices:
+// wave (eg, ks) takes experts u = eg, eg + EGW, ... and the K range
+// [ks*I/KSW, (ks+1)*I/KSW) of each (64*KD positions), loading the next
+// expert's weights and first activations while it multiplies the current one.
 constexpr int kDownRows = 8;
 constexpr int kDownWaves = 16;
 constexpr int kDownThreads = kDownWaves * kWave;
@@ -554,40 +557,42 @@ struct DownGeom {
   static constexpr int kStage = kTW * kRow;         // chunks per wave
 };
 
-template <int KD>
+template <int KD, int NR>
 __global__ __launch_bounds__(kDownThreads) void decode_down(
     const uint16_t* __restrict__ wd, const int* __restrict__ plan_u,
     const int32_t* __restrict__ plan_e, const int32_t* __restrict__ plan_off,
     const uint16_t* __restrict__ plan_pr, const uint16_t* __restrict__ hw, int T, int H, int I,
     int k, int KSW, uint16_t* __restrict__ out) {
   using G = DownGeom<KD>;
-  // dynamic LDS: [16 waves][T][8 dims] FP32 accumulators, then [16 waves][kStage] chunks
+  constexpr int RW = kDownRows * NR;                // output dimensions per workgroup
+  // dynamic LDS: [16 waves][T][RW dims] FP32 accumulators, then [16 waves][kStage] chunks
   extern __shared__ float accl[];
   __shared__ uint16_t s_e[kMaxPlan];                // E <= 1024
   __shared__ uint16_t s_off[kMaxPlan + 1];          // <= T*k <= 2048
   __shared__ uint16_t s_pr[kMaxPairs];
   __shared__ uint8_t s_tk[kMaxPairs];               // token of each plan entry (T <= 64)
   const int U = *plan_u;
-  for (int i = threadIdx.x; i < U; i += blockDim.x) s_e[i] = static_cast<uint16_t>(plan_e[i]);
-  for (int i = threadIdx.x; i <= U; i += blockDim.x) s_off[i] = static_cast<uint16_t>(plan_off[i]);
-  for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
+  for (int i = threadIdx.x; i < U; i += kDownThreads) s_e[i] = static_cast<uint16_t>(plan_e[i]);
+  for (int i = threadIdx.x; i <= U; i += kDownThreads) s_off[i] = static_cast<uint16_t>(plan_off[i]);
+  for (int i = threadIdx.x; i < T * k; i += kDownThreads) {
     const int pr = plan_pr[i];
     s_pr[i] = static_cast<uint16_t>(pr);
     s_tk[i] = static_cast<uint8_t>(pr / k);
   }
-  for (int i = threadIdx.x; i < kDownWaves * T * kDownRows; i += blockDim.x) accl[i] = 0.f;
+  for (int i = threadIdx.x; i < kDownWaves * T * RW; i += kDownThreads) accl[i] = 0.f;
   __syncthreads();
   const int wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
   const int col = ln & 15, grp = ln >> 4;
   const int hf = col >> 3, c8 = col & 7;            // K half and row / token within it
   const int EGW = kDownWaves / KSW;
   const int ks = wv % KSW, eg = wv / KSW;
-  const int d0 = blockIdx.x * kDownRows;
+  const int d0 = blockIdx.x * RW;
   const int kw = I / KSW;                           // = 64 * KD
-  // weights: lane (row c8, half hf, group grp), step s -> K offset 64s + 32hf + 8grp
+  // weights: lane (row c8, half hf, group grp), step s -> K offset 64s + 32hf + 8grp;
+  // dimension group r adds 8r rows
   const uint32_t woff = static_cast<uint32_t>((d0 + c8) * I + ks * kw + hf * 32 + grp * 8);
-  float* myacc = accl + wv * T * kDownRows;
-  i32x4* stage = reinterpret_cast<i32x4*>(accl + kDownWaves * T * kDownRows) + wv * G::kStage;
+  float* myacc = accl + wv * T * RW;
+  i32x4* stage = reinterpret_cast<i32x4*>(accl + kDownWaves * T * RW) + wv * G::kStage;
   // dense activation loads: lane = token slot dc, chunk dq of the wave's K range
   const int dc = ln / G::kCh, dq = ln - dc * G::kCh;
   const bool ld_lane = dc < G::kPerLoad;
@@ -603,21 +608,15 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
   const int dofs = 4 * (grp & 1);
   const int ntask = U > eg ? (U - 1 - eg) / EGW + 1 : 0;
 
-  bf16x8 aA[KD], aB[KD];
+  bf16x8 aA[NR][KD], aB[NR][KD];
   i32x4 hA0 = {}, hA1 = {}, hB0 = {}, hB1 = {};
-  // activations of tokens [c0, c0 + kPerLoad) of the plan entries at `base` (nt of them):
-  // every lane loads (lanes past the tokens repeat token c0), so the load count is fixed
-  auto load_h0 = [&](int base, int c0, int nt) {
-    const int slot = ld_lane && c0 + dc < nt ? c0 + dc : c0;
+  // activations of tokens [c0, c0 + kPerLoad) of the plan entries at `base` (nt of
+  // them): every lane loads (lanes past the tokens repeat the last valid one), so
+  // the load count is fixed
+  auto load_at = [&](int base, int c0, int nt) {
+    const int last = nt - 1;
+    const int slot = ld_lane && c0 + dc <= last ? c0 + dc : (c0 < last ? c0 : last);
     return ld16(hw + static_cast<uint32_t>(s_pr[base + slot] * I + kd));
-  };
-  // tokens [c0 + kPerLoad, c0 + kTW), loaded only when some exist
-  auto load_h1 = [&](int base, int c0, int nt, i32x4& h1) {
-    if (G::kTW > G::kPerLoad && nt - c0 > G::kPerLoad) {
-      const int c1 = c0 + G::kPerLoad;
-      const int slot = ld_lane && c1 + dc < nt ? c1 + dc : c1;
-      h1 = ld16(hw + static_cast<uint32_t>(s_pr[base + slot] * I + kd));
-    }
   };
   auto task_plan = [&](int tsk, int& base, int& nt, int& e) {
     const int u = eg + tsk * EGW;
@@ -626,43 +625,59 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     e = __builtin_amdgcn_readfirstlane(s_e[u]);
   };
   // loads of one task in a fixed order: first activations, weights, optional activations
-  auto issue = [&](int tsk, bf16x8 (&A)[KD], i32x4& h0, i32x4& h1) {
+  auto issue = [&](int tsk, bf16x8 (&A)[NR][KD], i32x4& h0, i32x4& h1) {
     int base, nt, e;
     task_plan(tsk, base, nt, e);
-    h0 = load_h0(base, 0, nt);
+    h0 = load_at(base, 0, nt);
     const uint16_t* pe = wd + static_cast<size_t>(e) * H * I;
 #pragma unroll
-    for (int s = 0; s < KD; ++s) A[s] = as_bf16x8(ld16_stream(pe + woff + s * 64));
-    load_h1(base, 0, nt, h1);
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int s = 0; s < KD; ++s)
+        A[r][s] = as_bf16x8(ld16_stream(pe + woff + r * kDownRows * I + s * 64));
+    if (G::kTW > G::kPerLoad && nt > G::kPerLoad) h1 = load_at(base, G::kPerLoad, nt);
   };
   // stage tokens [c0, c0 + kTW) (already loaded into h0, h1), multiply, accumulate
-  auto tile = [&](const bf16x8 (&A)[KD], int base, int c0, int nt, const i32x4& h0,
+  auto tile = [&](const bf16x8 (&A)[NR][KD], int base, int c0, int nt, const i32x4& h0,
                   const i32x4& h1) {
     if (ld_lane) {
       *st0 = h0;
       if (G::kTW > G::kPerLoad) *st1 = h1;
     }
     __builtin_amdgcn_wave_barrier();
-    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 b[KD];
 #pragma unroll
-    for (int s = 0; s < KD; ++s) d = mfma16x16x32(A[s], as_bf16x8(bsrc[8 * s]), d);
+    for (int s = 0; s < KD; ++s) b[s] = as_bf16x8(bsrc[8 * s]);
     const bool on = d_lane && c8 < G::kTW && c0 + c8 < nt;
     const int t = on ? s_tk[base + c0 + c8] : 0;
-    f32x4* acc = reinterpret_cast<f32x4*>(myacc + t * kDownRows + dofs);
-    if (on && hf == 0) *acc = *acc + d;             // half-0 block, then half-1 block
-    __builtin_amdgcn_wave_barrier();
-    if (on && hf == 1) *acc = *acc + d;
-    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KD; ++s) d = mfma16x16x32(A[r][s], b[s], d);
+      f32x4* acc = reinterpret_cast<f32x4*>(myacc + t * RW + r * kDownRows + dofs);
+      if (on && hf == 0) *acc = *acc + d;           // half-0 block, then half-1 block
+      __builtin_amdgcn_wave_barrier();
+      if (on && hf == 1) *acc = *acc + d;
+      __builtin_amdgcn_wave_barrier();
+    }
   };
-  auto run = [&](int tsk, const bf16x8 (&A)[KD], const i32x4& h0, const i32x4& h1) {
+  auto run = [&](int tsk, const bf16x8 (&A)[NR][KD], const i32x4& h0, const i32x4& h1) {
     int base, nt, e;
     task_plan(tsk, base, nt, e);
     tile(A, base, 0, nt, h0, h1);                   // every touched expert has a token
-    for (int c0 = G::kTW; c0 < nt; c0 += G::kTW) {  // experts with more than kTW tokens
-      i32x4 r1 = {};
-      const i32x4 r0 = load_h0(base, c0, nt);
-      load_h1(base, c0, nt, r1);
-      tile(A, base, c0, nt, r0, r1);
+    if (nt > G::kTW) {                              // experts with more than kTW tokens:
+      // the next tile's loads are issued before the current tile waits (fixed count,
+      // clamped rows), so their latency overlaps
+      i32x4 r0 = load_at(base, G::kTW, nt);
+      i32x4 r1 = G::kTW > G::kPerLoad ? load_at(base, G::kTW + G::kPerLoad, nt) : r0;
+      for (int c0 = G::kTW; c0 < nt; c0 += G::kTW) {
+        const i32x4 n0 = load_at(base, c0 + G::kTW, nt);
+        const i32x4 n1 = G::kTW > G::kPerLoad ? load_at(base, c0 + G::kTW + G::kPerLoad, nt) : n0;
+        tile(A, base, c0, nt, r0, r1);
+        r0 = n0;
+        r1 = n1;
+      }
     }
   };
   // one task ahead: the loads of task t+1 are in flight while task t multiplies
@@ -684,24 +699,24 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < T * kDownRows; i += blockDim.x) {
+  for (int i = threadIdx.x; i < T * RW; i += kDownThreads) {
     float v = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kDownWaves; ++w2) v += accl[w2 * T * kDownRows + i];
-    const int t = i / kDownRows, mm = i - t * kDownRows;
+    for (int w2 = 0; w2 < kDownWaves; ++w2) v += accl[w2 * T * RW + i];
+    const int t = i / RW, mm = i - t * RW;
     out[static_cast<size_t>(t) * H + d0 + mm] = static_cast<uint16_t>(f32_to_bf16_rne(v));
   }
 }
 
-// dynamic LDS of decode_down<KD>
-inline size_t down_lds_bytes(int T, int KD) {
+// dynamic LDS of decode_down<KD, NR>
+inline size_t down_lds_bytes(int T, int KD, int NR) {
   const int stage = KD == 3 ? DownGeom<3>::kStage
                   : KD == 4 ? DownGeom<4>::kStage
                   : KD == 5 ? DownGeom<5>::kStage : DownGeom<7>::kStage;
-  return sizeof(float) * kDownWaves * T * kDownRows + sizeof(i32x4) * kDownWaves * stage;
+  return sizeof(float) * kDownWaves * T * kDownRows * NR + sizeof(i32x4) * kDownWaves * stage;
 }
 
-// dynamic LDS of decode_gate_up<TM8, NG, KC>: the per-wave reduction sums
+// dynamic LDS of decode_gate_up<TM8, NG, KC>: two buffers of per-wave reduction sums
 inline size_t gate_up_lds_bytes(int TM8, int NG) {
   return 2 * sizeof(float) * kDecWaves * TM8 * NG * 2 * 4 * 16;
 }
@@ -749,8 +764,11 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   while (KSW < 8 && (dtotal / KSW > 4 || dtotal % KSW)) KSW *= 2;
   if (dtotal % KSW) KSW = 4;
   const int KD = dtotal / KSW;
-  const size_t lds_dn = down_lds_bytes(T, KD);
-  const dim3 grid2(H / kDownRows);
+  // 16 dimensions per workgroup when that still leaves a workgroup per CU (the
+  // activations are re-read by every workgroup)
+  // (the 5- and 7-step slices keep one group: two would not fit 128 registers)
+  const int NR = H / (2 * kDownRows) >= num_cus && KD <= 4 ? 2 : 1;
+  const size_t lds_dn = down_lds_bytes(T, KD, NR);
   prof_begin(kDecGateUp, s);
 #define GU_LAUNCH(TMV, NGV, KCV)                                                               \
   hipLaunchKernelGGL((decode_gate_up<TMV, NGV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, \
@@ -771,16 +789,19 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
 #undef GU_LAUNCH
   prof_end(kDecGateUp, s);
   prof_begin(kDecDown, s);
-#define DN_LAUNCH(KDV)                                                                         \
-  hipLaunchKernelGGL((decode_down<KDV>), grid2, dim3(kDownThreads), lds_dn, s, wd, plan_u, plan_e, \
-                     plan_off, plan_pr, hw, T, H, I, k, KSW, out)
+#define DN_LAUNCH(KDV, NRV)                                                                    \
+  hipLaunchKernelGGL((decode_down<KDV, NRV>), dim3(H / (kDownRows * NRV)), dim3(kDownThreads),    \
+                     lds_dn, s, wd, plan_u, plan_e, plan_off, plan_pr, hw, T, H, I, k, KSW, out)
+#define DN_NR(KDV) \
+  if (NR == 2) DN_LAUNCH(KDV, 2); else DN_LAUNCH(KDV, 1);
   switch (KD) {
-    case 3: DN_LAUNCH(3); break;
-    case 4: DN_LAUNCH(4); break;
-    case 5: DN_LAUNCH(5); break;
-    case 7: DN_LAUNCH(7); break;
+    case 3: DN_NR(3) break;
+    case 4: DN_NR(4) break;
+    case 5: DN_LAUNCH(5, 1); break;
+    case 7: DN_LAUNCH(7, 1); break;
     default: return hipErrorInvalidValue;            // not reachable for valid I
   }
+#undef DN_NR
 #undef DN_LAUNCH
   prof_end(kDecDown, s);
   return hipGetLastError();
@@ -789,14 +810,16 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
 hipError_t decode_set_attributes() {
   hipError_t e = hipSuccess;
   // down at T = 64: accumulators plus the staging tiles exceed 64 KB
-  const void* dn[] = {reinterpret_cast<const void*>(decode_down<3>),
-                      reinterpret_cast<const void*>(decode_down<4>),
-                      reinterpret_cast<const void*>(decode_down<5>),
-                      reinterpret_cast<const void*>(decode_down<7>)};
-  const int kds[] = {3, 4, 5, 7};
-  for (int i = 0; i < 4; ++i) {
+  const void* dn[] = {reinterpret_cast<const void*>(decode_down<3, 1>),
+                      reinterpret_cast<const void*>(decode_down<4, 1>),
+                      reinterpret_cast<const void*>(decode_down<5, 1>),
+                      reinterpret_cast<const void*>(decode_down<7, 1>),
+                      reinterpret_cast<const void*>(decode_down<3, 2>),
+                      reinterpret_cast<const void*>(decode_down<4, 2>)};
+  const int kds[] = {3, 4, 5, 7, 3, 4}, nrs[] = {1, 1, 1, 1, 2, 2};
+  for (int i = 0; i < 6; ++i) {
     e = hipFuncSetAttribute(dn[i], hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(down_lds_bytes(64, kds[i])));
+                            static_cast<int>(down_lds_bytes(64, kds[i], nrs[i])));
     if (e != hipSuccess) return e;
   }
   return e;
