@@ -521,6 +521,203 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   }
 }
 
+// gate_up for T > 32 with whole-line weight loads (H a multiple of 512): the
+// same items, MFMA layout (16 neurons x 16 tokens), tiles and epilogue as
+// decode_gate_up_wide, but each task is one 64-position step of the wave's K
+// range, and its 16 gate and 16 up rows are read with four loads of 8 rows x
+// 128 contiguous bytes (non-temporal), written to a wave-private LDS tile and
+// read back in the MFMA layout.  The tile lives in the wave's own slice of the
+// reduction buffer: a wave writes that slice only for its own tasks or its own
+// partial sums, and the other waves read it only between the epilogue's two
+// barriers.  16-byte chunks are XOR-swizzled by row, so the column reads (one
+// row per lane) hit distinct banks.
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_gate_up_wide_stream(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
+    const int32_t* __restrict__ idx, const float* __restrict__ wts, int T, int E,
+    int* __restrict__ plan_u, int32_t* __restrict__ plan_e, int32_t* __restrict__ plan_off,
+    uint16_t* __restrict__ plan_pr, int H, int I, int k, uint16_t* __restrict__ hw) {
+  constexpr int TM = 4;                             // 16-token tiles (T <= 64)
+  constexpr int kSlice = TM * 2 * 4 * 64;           // floats per wave in the reduction buffer
+  extern __shared__ float red[];                    // [8 waves][TM][gate/up][4][64]
+  __shared__ int s_e[kMaxPlan];
+  __shared__ int s_off[kMaxPlan + 1];
+  __shared__ uint16_t s_pr[kMaxPairs];
+  const int U = build_plan(idx, T, E, k, reinterpret_cast<uint64_t*>(red),
+                           reinterpret_cast<int*>(reinterpret_cast<uint64_t*>(red) + E), s_e,
+                           s_off, s_pr);
+  if (blockIdx.x == 0) publish_plan(U, T * k, s_e, s_off, s_pr, plan_u, plan_e, plan_off, plan_pr);
+  const int nrb = I / 16;
+  const int items = U * nrb;
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
+  const int col = ln & 15, grp = ln >> 4;
+  const int kw = H / kDecWaves;                     // a multiple of 64
+  const int nch = kw / 64;                          // tasks (steps of 64) per item
+  const int my_items = blockIdx.x < items ? (items - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int ntask = my_items * nch;
+  // whole-line loads: lane = (row ln/8 of an 8-row group, 16-byte chunk ln%8)
+  const int lr = ln >> 3, lc = ln & 7;
+  const uint32_t wl_off = static_cast<uint32_t>(lr * H + wv * kw + lc * 8);
+  i32x4* tilep = reinterpret_cast<i32x4*>(red + wv * kSlice);   // [gate/up][16 rows][8 chunks]
+  i32x4* wdst = tilep + lr * 8 + (lc ^ lr);        // + (mat*16 + 8*half) * 8
+  // MFMA A lane (row col, group grp), 32-step s2: chunk 4*s2 + grp of row col
+  const i32x4* asrc = tilep + col * 8;
+  const size_t up_off = static_cast<size_t>(I) * H;
+  const uint32_t kb = static_cast<uint32_t>(wv * kw + grp * 8);  // activation lane offset
+
+  i32x4 wA[4], wB[4];                               // [gate/up][row half] whole-line loads
+  uint32_t itk = 0;                                 // this lane's first-tile token, load side
+  // weights of task t
+  auto issue = [&](int t, i32x4 (&W)[4]) {
+    const int j = t / nch, c = t - j * nch;
+    const int item = blockIdx.x + j * gridDim.x;
+    const int u = item / nrb, rb = item - u * nrb;
+    const int e = __builtin_amdgcn_readfirstlane(s_e[u]);
+    const uint16_t* pw = wgu + (static_cast<size_t>(e) * 2 * I + rb * 16) * H + wl_off + c * 64;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        W[2 * m + hh] = ld16_stream(pw + m * up_off + static_cast<size_t>(8 * hh) * H);
+  };
+  float wl[2];                                       // routing weights of this thread's two epilogue elements
+  // first token tile's activations of task t (both 32-steps), and at an item's
+  // first task the routing weights its epilogue needs; issued before the next
+  // task's weights, so that waiting for them leaves those in flight
+  auto load_x0 = [&](int t, bf16x8 (&XT)[2]) {
+    const int j = t / nch, c = t - j * nch;
+    if (c == 0) {
+      const int item = blockIdx.x + j * gridDim.x;
+      const int u = item / nrb;
+      const int b = __builtin_amdgcn_readfirstlane(s_off[u]);
+      const int n = __builtin_amdgcn_readfirstlane(s_off[u + 1]) - b;
+      itk = static_cast<uint32_t>(s_pr[b + (col < n ? col : 0)] / k);
+      const int nq = (n + 15) >> 4;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int qq = threadIdx.x + h * kDecThreads;
+        const int p = (qq >> 8) * 16 + ((qq & 255) >> 4);
+        wl[h] = qq < nq * 256 && p < n ? wts[s_pr[b + p]] : 0.f;
+      }
+    }
+    const uint32_t xo = itk * static_cast<uint32_t>(H) + kb + c * 64;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) XT[s2] = as_bf16x8(ld16(x + xo + s2 * 32));
+  };
+  f32x4 ag[TM], au[TM];
+  uint32_t tkp = 0;                                 // this lane's token per tile, packed bytes
+  int ntok = 0, tiles = 0;
+
+  auto run_task = [&](const i32x4 (&W)[4], const bf16x8 (&XT)[2], int t) {
+    const int j = t / nch, c = t - j * nch;
+    const int item = blockIdx.x + j * gridDim.x;
+    const int u = item / nrb, rb = item - u * nrb;
+    const int base = __builtin_amdgcn_readfirstlane(s_off[u]);
+    if (c == 0) {
+      ntok = __builtin_amdgcn_readfirstlane(s_off[u + 1]) - base;
+      tiles = (ntok + 15) >> 4;
+      tkp = 0;
+#pragma unroll
+      for (int q = 0; q < TM; ++q) {
+        const int p = 16 * q + col;                 // past the end: a valid token, column discarded
+        tkp |= static_cast<uint32_t>(s_pr[base + (p < ntok ? p : 0)] / k) << (8 * q);
+        ag[q] = au[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    // whole-line weights -> LDS tile -> MFMA layout
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wdst[i * 64] = W[i];   // (mat*16 + 8*half) rows = 8i rows
+    __builtin_amdgcn_wave_barrier();
+    bf16x8 ga[2], ua[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int ch = (4 * s2 + grp) ^ (col & 7);
+      ga[s2] = as_bf16x8(asrc[ch]);
+      ua[s2] = as_bf16x8(asrc[16 * 8 + ch]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t ko = kb + c * 64;
+#pragma unroll
+    for (int q = 0; q < TM; ++q) {
+      if (q < tiles) {
+        bf16x8 xb[2];
+        if (q == 0) {
+          xb[0] = XT[0];
+          xb[1] = XT[1];
+        } else {                                    // later tiles: experts with over 16 tokens
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+            xb[s2] = as_bf16x8(ld16(x + ((tkp >> (8 * q)) & 0xFFu) * static_cast<uint32_t>(H) + ko + s2 * 32));
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          ag[q] = mfma16x16x32(ga[s2], xb[s2], ag[q]);
+          au[q] = mfma16x16x32(ua[s2], xb[s2], au[q]);
+        }
+      }
+    }
+    if (c != nch - 1) return;
+    // epilogue of the item: fixed-order sum over waves, SwiGLU, weight, store
+#pragma unroll
+    for (int q = 0; q < TM; ++q) {
+      if (q < tiles) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          red[(((wv * TM + q) * 2 + 0) * 4 + r) * 64 + ln] = ag[q][r];
+          red[(((wv * TM + q) * 2 + 1) * 4 + r) * 64 + ln] = au[q][r];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int qq = threadIdx.x + h * kDecThreads;
+      if (qq < tiles * 256) {
+        const int q = qq >> 8, within = qq & 255;
+        const int n = within >> 4, m = within & 15;  // token column n, weight row m
+        const int src = 16 * (m >> 2) + n, r = m & 3;
+        float g = 0.f, up = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kDecWaves; ++w2) {
+          g += red[(((w2 * TM + q) * 2 + 0) * 4 + r) * 64 + src];
+          up += red[(((w2 * TM + q) * 2 + 1) * 4 + r) * 64 + src];
+        }
+        const int p = q * 16 + n;
+        if (p < ntok) {
+          const int pr = s_pr[base + p];
+          const float hv = wl[h] * swiglu(g, up);
+          hw[static_cast<size_t>(pr) * I + rb * 16 + m] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+        }
+      }
+    }
+    __syncthreads();
+  };
+
+  // one task ahead; the steady-state loop issues unconditionally, so the
+  // compiler's waits leave the next task's weights in flight
+  bf16x8 x0[2];
+  if (ntask > 0) {
+    issue(0, wA);
+    int t = 0;
+    for (; t + 2 < ntask; t += 2) {
+      load_x0(t, x0);
+      issue(t + 1, wB);
+      run_task(wA, x0, t);
+      load_x0(t + 1, x0);
+      issue(t + 2, wA);
+      run_task(wB, x0, t + 1);
+    }
+    load_x0(t, x0);
+    if (t + 1 < ntask) {
+      issue(t + 1, wB);
+      run_task(wA, x0, t);
+      load_x0(t + 1, x0);
+      run_task(wB, x0, t + 1);
+    } else {
+      run_task(wA, x0, t);
+    }
+  }
+}
+
 // down: workgroup = 8*NR output dimensions of every touched expert (NR = 1 or
 // 2 groups of 8; H/(8*NR) workgroups, enough to occupy every CU without
 // splitting the expert sum across workgroups).  The 16x16x32 MFMA is used as
@@ -776,7 +973,10 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
 #define GU_WIDE(KCV)                                                                            \
   hipLaunchKernelGGL((decode_gate_up_wide<KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x, wgu, \
                      idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw)
-  if (wide) {
+  if (wide && H % 512 == 0) {
+    hipLaunchKernelGGL(decode_gate_up_wide_stream, dim3(grid1), dim3(kDecThreads), lds_gu, s, x, wgu,
+                       idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw);
+  } else if (wide) {
     if (KCW == 2) GU_WIDE(2); else GU_WIDE(1);
   } else if (TM8 == 1) {
     if (KC == 2) GU_LAUNCH(1, 2, 2); else GU_LAUNCH(1, 2, 1);

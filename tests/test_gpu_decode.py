@@ -58,6 +58,7 @@ def _custom(T, H, I, E, k, seed=0, x_std=1.0):
     (37, 768, 512, 40, 5),     # odd sizes, three token tiles
     (64, 256, 512, 1000, 32),  # k = 32, E near the limit
     (5, 1024, 2048, 16, 3),    # I = 2048: eight K-slices of 256 in down
+    (48, 1024, 512, 24, 6),    # T > 32 with H % 512 == 0: whole-line gate_up, two steps per wave
     (3, 512, 1280, 8, 2),      # I = 1280: four K-slices of 320 in down
     (9, 256, 1792, 12, 3),     # I = 1792: four K-slices of 448 in down
 ])
