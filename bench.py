@@ -34,20 +34,21 @@ METRIC = "MoE layer tokens/s; decode HBM TB/s % of peak; batched MFMA util %"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 
-# HBM bytes per launch of the dominant kernel, from two rocprofv3 counter passes
-# (FETCH_SIZE, WRITE_SIZE) scaled by a 1 GiB copy (profiles/copy_calibration_1GiB.md).
+# HBM bytes per launch of the dominant kernel (read + written), from two rocprofv3
+# counter passes (FETCH_SIZE, WRITE_SIZE) scaled by a 1 GiB copy
+# (profiles/copy_calibration_1GiB.md).
 # Each record holds a fingerprint of the kernel sources it was measured on; when
 # the sources change the figure no longer describes the kernel and is reported
 # as null until the counters are taken again.
 TRAFFIC = {
     ("decode_gate_up", "qwen3-decode-T32"): (
-        709.3e6, ('decode.hip', 'common.h', 'internal.h'), "fe71f57aeb281214",
+        705.7e6, ('decode.hip', 'common.h', 'internal.h'), "a97635611fd0fc62",
         "profiles/decode_gate_up_qwen3-decode-T32.md"),
     ("gemm_gate_up", "kimi-bf16-T2048"): (
-        24685.2e6, ('batched.hip', 'common.h', 'tiles.h'), "32e32395354f7707",
+        24769.7e6, ('batched.hip', 'common.h', 'tiles.h'), "9d5ea23d5da2c32f",
         "profiles/gemm_gate_up_kimi-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
-        2485.7e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "8ae64901ab3f19cd",
+        2618.0e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "70d9b3c6a25bfac1",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
 }
 
