@@ -140,27 +140,43 @@ __global__ __launch_bounds__(1024) void group_experts(
   }
 }
 
-// gate_up, BF16: workgroup = (M-tile, NW*32 neurons); wave = 32 neurons (16
-// gate rows + 16 up rows in two groups) x 64 rows.  MFMA 16x16x32: A = weight
-// rows (lane: row col, K chunk grp), B = activation rows, D[row][token].
-// The tile's 64 gathered activation rows are staged in LDS in chunks of 256
-// along K (double-buffered) and shared by all NW waves; each wave streams its
-// own weight rows from HBM into registers, double-buffered one K-step ahead.
+// Batched BF16 projections with a whole-line weight stream (both gate_up and
+// down): workgroup = (M-tile of 64 routed rows, NW waves); each wave owns two
+// groups of 16 weight rows - gate_up (KIND 0): 16 neurons' gate rows and their
+// up rows; down (KIND 1, 2): 32 output dimensions - and all 64 rows of the
+// tile.  Each 64-position K step of a wave reads its 32 weight rows as four
+// loads of 8 rows x 128 contiguous bytes (whole cache lines, non-temporal: the
+// weights are read once per M-tile); a plain 16x16x32 A operand would take 16
+// rows x 64 bytes per load, half lines, which stream markedly slower.  Each
+// 8-row load goes through a wave-private 2 KB LDS tile (16-byte chunks
+// XOR-swizzled by row, so the one-row-per-lane reads hit distinct banks) and is
+// read back in the A layout, one 16-row group at a time.  The tile's 64
+// activation rows (gathered through perm for gate_up, contiguous in h for
+// down) are staged in LDS in 128-wide K chunks, double-buffered and shared by
+// the waves; the next step's weights are in flight while a step multiplies.
 // Rows past the tile's end load the tile's first row; their MFMA columns are
 // computed and discarded (columns never mix).
-constexpr int kXC = 256;                 // K chunk of the staged activations
-constexpr int kXRS = kXC + 8;            // padded LDS row stride (elements)
+// Epilogues: KIND 0 SwiGLU -> h (BF16); KIND 1 FP32 y per slot; KIND 2 (k = 1)
+// out[t] = bf16(w[t] * y) with t = perm[row].
+constexpr int kSXC = 128;                // K chunk of the staged activations
+constexpr int kSXRS = kSXC + 8;          // padded LDS row stride (elements)
+enum { kProjGateUp = 0, kProjDown = 1, kProjDownFused = 2 };
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void gemm_gate_up_bf16(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
+template <int KIND, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_bf16s(
+    const uint16_t* __restrict__ act, const uint16_t* __restrict__ wt,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
-    const int* __restrict__ counts, const int* __restrict__ offsets, int H, int I, int k,
-    uint16_t* __restrict__ h) {
-  __shared__ __align__(16) uint16_t xs[2][kBM * kXRS];
+    const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
+    int H, int I, int k, uint16_t* __restrict__ hout, float* __restrict__ y,
+    uint16_t* __restrict__ out) {
   constexpr int NT = NW * 64;
-  constexpr int LPT = kBM * (kXC / 8) / NT;           // 16-byte activation loads per thread
-  const int nblk = I / (NW * 32);
+  constexpr int RPW = KIND == kProjGateUp ? 16 : 32;      // outputs per wave
+  constexpr int LPT = kBM * (kSXC / 8) / NT;              // 16-byte activation loads per thread
+  __shared__ __align__(16) uint16_t xs[2][kBM * kSXRS];
+  __shared__ __align__(16) i32x4 wtl[NW][16 * 8];         // per wave: [16 rows][8 chunks]
+  const int K = KIND == kProjGateUp ? H : I;              // reduction length
+  const int N = KIND == kProjGateUp ? I : H;              // outputs
+  const int nblk = N / (NW * RPW);
   const int item = real_item(blockIdx.x, nblk, *n_tiles);
   if (item < 0) return;
   const int tile = item / nblk, nb_i = item - tile * nblk;
@@ -168,229 +184,133 @@ __global__ __launch_bounds__(NW * 64) void gemm_gate_up_bf16(
   const int e = te.x, m0 = te.y;
   const int mcount = min(kBM, counts[e] - m0);
   const int rbase = offsets[e] + m0;
-  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, col = ln & 15, grp = ln >> 4;
-  const int nb = nb_i * NW * 32 + wv * 32;
+  const int tid = threadIdx.x, ln = tid & 63, col = ln & 15, grp = ln >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb = nb_i * NW * RPW + wv * RPW;              // the wave's first output
+  // the wave's two 16-row weight groups
+  const int row0 = nb, row1 = KIND == kProjGateUp ? I + nb : nb + 16;
 
-  const uint16_t* __restrict__ wb = wgu + static_cast<size_t>(e) * 2 * I * H;
-  uint32_t og[2], ou[2];
+  // whole-line loads: lane = (row lr of an 8-row group, 16-byte chunk lc)
+  const int lr = ln >> 3, lc = ln & 7;
+  const uint16_t* __restrict__ wb = wt + static_cast<size_t>(e) * (KIND == kProjGateUp ? 2 * I : H) * K;
+  uint32_t ow[4];                                         // group 0 rows 0-7, 8-15, group 1 rows 0-7, 8-15
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    og[q] = static_cast<uint32_t>((nb + 16 * q + col) * H + grp * 8);
-    ou[q] = og[q] + static_cast<uint32_t>(I * H);
-  }
-  // cooperative activation loader: chunk c = tid + i*NT -> (row c/32, 16-byte column c%32)
+  for (int i = 0; i < 4; ++i)
+    ow[i] = static_cast<uint32_t>(((i < 2 ? row0 : row1) + 8 * (i & 1) + lr) * K + lc * 8);
+  i32x4* tw = wtl[wv];
+  i32x4* wdst = tw + lr * 8 + (lc ^ lr);                  // + 64 for rows 8-15
+  // A lane (row col, group grp), 32-half hh: chunk 4*hh + grp of row col
+  const i32x4* asrc = tw + col * 8;
+  const int sw = col & 7;
+
+  // cooperative activation loader: chunk c = tid + i*NT -> (row c/16, 16-byte column c%16)
   uint32_t oxl[LPT];
   int lrow[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
-    const int c = tid + i * NT, r = c >> 5;
-    lrow[i] = r * kXRS + (c & 31) * 8;
-    oxl[i] = static_cast<uint32_t>((perm[rbase + (r < mcount ? r : 0)] / k) * H + (c & 31) * 8);
+    const int c = tid + i * NT, r = c >> 4, rr = r < mcount ? r : 0;
+    lrow[i] = r * kSXRS + (c & 15) * 8;
+    const int arow = KIND == kProjGateUp ? perm[rbase + rr] / k : rbase + rr;
+    oxl[i] = static_cast<uint32_t>(arow * K + (c & 15) * 8);
   }
   i32x4 xr[LPT];
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) xr[i] = ld16(x + oxl[i]);
+  for (int i = 0; i < LPT; ++i) xr[i] = ld16(act + oxl[i]);
 #pragma unroll
   for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xs[0][lrow[i]]) = xr[i];
 
-  f32x4 ag[2][4], au[2][4];
+  f32x4 acc0[4], acc1[4];                                 // [row group g of the tile]
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int g = 0; g < 4; ++g) acc0[g] = acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nsteps = K / 64;
+  i32x4 wA[4], wB[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) ag[q][g] = au[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 wg0[2], wu0[2], wg1[2], wu1[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    wg0[q] = as_bf16x8(ld16(wb + og[q]));
-    wu0[q] = as_bf16x8(ld16(wb + ou[q]));
-  }
+  for (int i = 0; i < 4; ++i) wA[i] = ld16_stream(wb + ow[i]);
   __syncthreads();
-  const int nchunk = H / kXC;
+
+  // one 64-position step: weights W (already loaded), activations from xs[buf] at
+  // chunk offset st*64
+  auto step = [&](const i32x4 (&W)[4], int buf, int st) {
+    const uint16_t* xb = &xs[buf][col * kSXRS + st * 64 + grp * 8];
+    bf16x8 bx[4][2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        bx[g][hh] = as_bf16x8(*reinterpret_cast<const i32x4*>(xb + 16 * g * kSXRS + hh * 32));
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {                         // row group 0, then 1
+      wdst[0] = W[2 * m];
+      wdst[64] = W[2 * m + 1];
+      __builtin_amdgcn_wave_barrier();
+      bf16x8 a[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) a[hh] = as_bf16x8(asrc[(4 * hh + grp) ^ sw]);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          if (m == 0) acc0[g] = mfma16x16x32(a[hh], bx[g][hh], acc0[g]);
+          else acc1[g] = mfma16x16x32(a[hh], bx[g][hh], acc1[g]);
+        }
+    }
+  };
+  const int nchunk = K / kSXC;
   for (int c = 0; c < nchunk; ++c) {
     const int buf = c & 1;
     const bool more = c + 1 < nchunk;
     if (more) {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) xr[i] = ld16(x + oxl[i] + (c + 1) * kXC);
+      for (int i = 0; i < LPT; ++i) xr[i] = ld16(act + oxl[i] + (c + 1) * kSXC);
     }
-    const uint16_t* xb = &xs[buf][(col) * kXRS + grp * 8];
+    // steps 2c (weights in wA) and 2c+1 (wB); the step after each is loaded first
+    // (clamped to the last step, a harmless repeat, so the load count is fixed)
+    const uint32_t k1 = static_cast<uint32_t>((2 * c + 1) * 64);
+    const uint32_t k2 = static_cast<uint32_t>(min(2 * c + 2, nsteps - 1) * 64);
 #pragma unroll
-    for (int s = 0; s < kXC / 32; s += 2) {
-      const int k0 = c * kXC + s * 32;
-      const int k1 = k0 + 32, k2 = min(k0 + 64, H - 32);
+    for (int i = 0; i < 4; ++i) wB[i] = ld16_stream(wb + ow[i] + k1);
+    step(wA, buf, 0);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        wg1[q] = as_bf16x8(ld16(wb + og[q] + k1));
-        wu1[q] = as_bf16x8(ld16(wb + ou[q] + k1));
-      }
-      {
-        bf16x8 bx[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) bx[g] = as_bf16x8(*reinterpret_cast<const i32x4*>(xb + 16 * g * kXRS + s * 32));
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            ag[q][g] = mfma16x16x32(wg0[q], bx[g], ag[q][g]);
-            au[q][g] = mfma16x16x32(wu0[q], bx[g], au[q][g]);
-          }
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        wg0[q] = as_bf16x8(ld16(wb + og[q] + k2));
-        wu0[q] = as_bf16x8(ld16(wb + ou[q] + k2));
-      }
-      {
-        bf16x8 bx[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) bx[g] = as_bf16x8(*reinterpret_cast<const i32x4*>(xb + 16 * g * kXRS + (s + 1) * 32));
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            ag[q][g] = mfma16x16x32(wg1[q], bx[g], ag[q][g]);
-            au[q][g] = mfma16x16x32(wu1[q], bx[g], au[q][g]);
-          }
-      }
-    }
+    for (int i = 0; i < 4; ++i) wA[i] = ld16_stream(wb + ow[i] + k2);
+    step(wB, buf, 1);
     if (more) {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xs[buf ^ 1][lrow[i]]) = xr[i];
     }
     __syncthreads();
   }
-  // SwiGLU epilogue: lane holds neurons nb+16q+4grp+{0..3} of row 16g+col
+  // epilogue: lane holds outputs nb+4grp+{0..3} (group 0) and row1+4grp+{0..3}
+  // (group 1) of tile row 16g+col
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
     if (r >= mcount) continue;
-    uint16_t* hr = h + static_cast<size_t>(rbase + r) * I + nb + 4 * grp;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    if (KIND == kProjGateUp) {
+      uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb + 4 * grp;
       uint32_t p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = f32_to_bf16_rne(swiglu(ag[q][g][i], au[q][g][i]));
+      for (int i = 0; i < 4; ++i) p[i] = f32_to_bf16_rne(swiglu(acc0[g][i], acc1[g][i]));
       uint2 v;
       v.x = p[0] | (p[1] << 16);
       v.y = p[2] | (p[3] << 16);
-      *reinterpret_cast<uint2*>(hr + 16 * q) = v;
-    }
-  }
-}
-
-// down, BF16: workgroup = (M-tile, NW*64 output dims); wave = 64 dims (4
-// groups) x 64 rows.  The tile's 64 activation rows (contiguous in h) are
-// staged in LDS as in gate_up.  FUSED (k = 1): out[t] = bf16(w[t] * y) with
-// t = perm[row].
-template <bool FUSED, int NW>
-__global__ __launch_bounds__(NW * 64) void gemm_down_bf16(
-    const uint16_t* __restrict__ h, const uint16_t* __restrict__ wd,
-    const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
-    const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
-    int H, int I, float* __restrict__ y, uint16_t* __restrict__ out) {
-  __shared__ __align__(16) uint16_t hs_[2][kBM * kXRS];
-  constexpr int NT = NW * 64;
-  constexpr int LPT = kBM * (kXC / 8) / NT;
-  const int nblk = H / (NW * 64);
-  const int item = real_item(blockIdx.x, nblk, *n_tiles);
-  if (item < 0) return;
-  const int tile = item / nblk, db_i = item - tile * nblk;
-  const int2 te = tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int mcount = min(kBM, counts[e] - m0);
-  const int rbase = offsets[e] + m0;
-  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, col = ln & 15, grp = ln >> 4;
-  const int db = db_i * NW * 64 + wv * 64;
-
-  const uint16_t* __restrict__ wb = wd + static_cast<size_t>(e) * H * I;
-  const uint16_t* __restrict__ hb = h + static_cast<size_t>(rbase) * I;
-  uint32_t ow[4];
+      *reinterpret_cast<uint2*>(hr) = v;
+    } else if (KIND == kProjDownFused) {
+      const int t = perm[rbase + r];                      // k = 1: pair id == token
+      const float wt_ = w[t];
+      uint16_t* orow = out + static_cast<size_t>(t) * H + nb + 4 * grp;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ow[q] = static_cast<uint32_t>((db + 16 * q + col) * I + grp * 8);
-  uint32_t ohl[LPT];
-  int lrow[LPT];
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int c = tid + i * NT, r = c >> 5;
-    lrow[i] = r * kXRS + (c & 31) * 8;
-    ohl[i] = static_cast<uint32_t>((r < mcount ? r : 0) * I + (c & 31) * 8);
-  }
-  i32x4 hr_[LPT];
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) hr_[i] = ld16(hb + ohl[i]);
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&hs_[0][lrow[i]]) = hr_[i];
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) acc[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 a0[4], a1[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) a0[q] = as_bf16x8(ld16(wb + ow[q]));
-  __syncthreads();
-  const int nchunk = I / kXC;
-  for (int c = 0; c < nchunk; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < nchunk;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) hr_[i] = ld16(hb + ohl[i] + (c + 1) * kXC);
-    }
-    const uint16_t* hbuf = &hs_[buf][col * kXRS + grp * 8];
-#pragma unroll
-    for (int s = 0; s < kXC / 32; s += 2) {
-      const int k0 = c * kXC + s * 32;
-      const int k1 = k0 + 32, k2 = min(k0 + 64, I - 32);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) a1[q] = as_bf16x8(ld16(wb + ow[q] + k1));
-      {
-        bf16x8 bb[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) bb[g] = as_bf16x8(*reinterpret_cast<const i32x4*>(hbuf + 16 * g * kXRS + s * 32));
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) acc[q][g] = mfma16x16x32(a0[q], bb[g], acc[q][g]);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) a0[q] = as_bf16x8(ld16(wb + ow[q] + k2));
-      {
-        bf16x8 bb[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) bb[g] = as_bf16x8(*reinterpret_cast<const i32x4*>(hbuf + 16 * g * kXRS + (s + 1) * 32));
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) acc[q][g] = mfma16x16x32(a1[q], bb[g], acc[q][g]);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&hs_[buf ^ 1][lrow[i]]) = hr_[i];
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int r = 16 * g + col;
-    if (r >= mcount) continue;
-    if (FUSED) {
-      const int t = perm[rbase + r];         // k = 1: pair id == token
-      const float wt = w[t];
-      uint16_t* orow = out + static_cast<size_t>(t) * H + db + 4 * grp;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int m = 0; m < 2; ++m) {
+        const f32x4 a = m == 0 ? acc0[g] : acc1[g];
         uint2 v;
-        v.x = f32_to_bf16_rne(wt * acc[q][g][0]) | (f32_to_bf16_rne(wt * acc[q][g][1]) << 16);
-        v.y = f32_to_bf16_rne(wt * acc[q][g][2]) | (f32_to_bf16_rne(wt * acc[q][g][3]) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * q) = v;
+        v.x = f32_to_bf16_rne(wt_ * a[0]) | (f32_to_bf16_rne(wt_ * a[1]) << 16);
+        v.y = f32_to_bf16_rne(wt_ * a[2]) | (f32_to_bf16_rne(wt_ * a[3]) << 16);
+        *reinterpret_cast<uint2*>(orow + 16 * m) = v;
       }
     } else {
-      float* yr = y + static_cast<size_t>(rbase + r) * H + db + 4 * grp;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) *reinterpret_cast<f32x4*>(yr + 16 * q) = acc[q][g];
+      float* yr = y + static_cast<size_t>(rbase + r) * H + nb + 4 * grp;
+      *reinterpret_cast<f32x4*>(yr) = acc0[g];
+      *reinterpret_cast<f32x4*>(yr + 16) = acc1[g];
     }
   }
 }
@@ -804,10 +724,11 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
   constexpr int NW = 8;          // BF16: 8 waves x 32 neurons; MXFP8: 8 waves x 16 neurons
   const int n_items = round_up((I / (dtype == 0 ? NW * 32 : NW * 16)) * L.max_tiles, kXcds);
   prof_begin(kGemmGateUp, s);
-  if (dtype == 0)
-    hipLaunchKernelGGL(gemm_gate_up_bf16<NW>, dim3(n_items), dim3(NW * 64), 0, s,
+  if (dtype == 0)   // 16 waves x 16 neurons = 256 neurons per workgroup, as NW * 32 above
+    hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
-                       p.tiles, p.n_tiles, p.counts, p.offsets, H, I, k, static_cast<uint16_t*>(h));
+                       p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
+                       static_cast<uint16_t*>(h), nullptr, nullptr);
   else
     hipLaunchKernelGGL(gemm_gate_up_mx<NW>, dim3(n_items), dim3(NW * 64), 0, s,
                        static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
@@ -845,24 +766,25 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
     }
     return e;
   }
-  // output dims per workgroup: BF16 8 waves x 64 (4 x 64 when H is not a
+  // output dims per workgroup: BF16 16 waves x 32 (8 x 32 when H is not a
   // multiple of 512); MXFP8 8 waves x 32
   const bool wide = dtype == 0 && H % 512 == 0;
   const int dims = dtype == 0 ? (wide ? 512 : 256) : 256;
   const int n_items = round_up((H / dims) * L.max_tiles, kXcds);
-  const dim3 grid(n_items), block(dtype == 0 ? dims : 512);
-#define DOWN_BF16(F, NWV)                                                                   \
-  hipLaunchKernelGGL((gemm_down_bf16<F, NWV>), grid, block, 0, s,                          \
+  const dim3 grid(n_items), block(dtype == 0 ? 2 * dims : 512);
+#define DOWN_BF16(KINDV, NWV)                                                               \
+  hipLaunchKernelGGL((gemm_bf16s<KINDV, NWV>), grid, block, 0, s,                          \
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),       \
-                     p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, p.y, out)
+                     p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr,   \
+                     p.y, out)
 #define DOWN_MX(F, NWV)                                                                     \
   hipLaunchKernelGGL((gemm_down_mx<F, NWV>), grid, block, 0, s,                            \
                      static_cast<const uint8_t*>(h), hs, static_cast<const uint8_t*>(wd), wds, \
                      p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, p.y, out)
   prof_begin(kGemmDown, s);
   if (dtype == 0) {
-    if (k == 1) { if (wide) DOWN_BF16(true, 8); else DOWN_BF16(true, 4); }
-    else { if (wide) DOWN_BF16(false, 8); else DOWN_BF16(false, 4); }
+    if (k == 1) { if (wide) DOWN_BF16(kProjDownFused, 16); else DOWN_BF16(kProjDownFused, 8); }
+    else { if (wide) DOWN_BF16(kProjDown, 16); else DOWN_BF16(kProjDown, 8); }
   } else {
     if (k == 1) DOWN_MX(true, 8);
     else DOWN_MX(false, 8);
