@@ -383,32 +383,43 @@ __global__ __launch_bounds__(256) void quant_mx_rows(const uint16_t* __restrict_
   }
 }
 
-// gate_up, MXFP8: workgroup = (M-tile, NW*16 neurons); wave = 16 neurons (16
-// gate rows + 16 up rows) x 64 rows, so the wide FP8 operands of a double-
-// buffered K loop fit the register file.  The activation codes and scale
-// bytes of the tile are staged in LDS in stages of 256 along K (two 128-wide
-// scaled MFMA chunks), double-buffered and shared by all NW waves.  Per chunk
-// a lane feeds two 16-byte pieces of its row and the row's scale byte for
-// block grp of the chunk.  An MX block of h (32 neurons) spans the wave pair
-// (2m, 2m+1); their per-row maxima meet in LDS.
+// Batched MXFP8 projections with a whole-line weight stream, the layout of
+// gemm_bf16s for FP8 codes: workgroup = (M-tile of 64 routed rows, NW waves),
+// each wave owning two groups of 16 weight rows (gate_up, KIND 0: 16 neurons'
+// gate and up rows; down, KIND 1 / 2: 32 output dimensions).  A 128-position
+// chunk of a row is 128 bytes: the wave reads its 32 rows as four loads of 8
+// rows x 128 contiguous bytes (non-temporal), passes them through a
+// wave-private 2 KB LDS tile (16-byte chunks XOR-swizzled by row) and reads
+// back the 32-byte A operand of the block-scaled 16x16x128 MFMA.  The rows'
+// E8M0 scale bytes come 8 per row per 256-position stage (two chunks) in one
+// load per 16-row group.  The tile's activation codes and scale bytes are
+// staged in LDS in 256-position stages, double-buffered and shared by the
+// waves.  The gate_up epilogue quantizes h to MX: a 32-neuron block spans the
+// wave pair (2m, 2m+1), whose per-row maxima meet in LDS.
 constexpr int kMXC = 256;                // K stage of the staged MX codes (two chunks)
 constexpr int kMRS = kMXC + 16;          // padded LDS row stride (bytes)
 constexpr int kMSC = kMXC / 32;          // scale bytes per row per stage
 constexpr int kMCH = kMXC / 16;          // 16-byte code chunks per row per stage
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void gemm_gate_up_mx(
-    const uint8_t* __restrict__ x, const uint8_t* __restrict__ xs,
-    const uint8_t* __restrict__ wgu, const uint8_t* __restrict__ wgus,
+template <int KIND, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_mx_s(
+    const uint8_t* __restrict__ act, const uint8_t* __restrict__ acts,
+    const uint8_t* __restrict__ wt, const uint8_t* __restrict__ wts,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
-    const int* __restrict__ counts, const int* __restrict__ offsets, int H, int I, int k,
-    uint8_t* __restrict__ h, uint8_t* __restrict__ hs) {
+    const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
+    int H, int I, int k, uint8_t* __restrict__ hout, uint8_t* __restrict__ hsout,
+    float* __restrict__ y, uint16_t* __restrict__ out) {
+  constexpr int NT = NW * 64;
+  constexpr int RPW = KIND == kProjGateUp ? 16 : 32;      // outputs per wave
+  constexpr int LPT = kBM * kMCH / NT;                    // 16-byte code loads per thread
   __shared__ __align__(16) uint8_t xl[2][kBM * kMRS];
   __shared__ __align__(16) uint8_t sl[2][kBM * kMSC];
-  __shared__ float s_amax[NW][kBM];
-  constexpr int NT = NW * 64;
-  constexpr int LPT = (kBM * kMCH + NT - 1) / NT;
-  const int nblk = I / (NW * 16);
+  __shared__ __align__(16) i32x4 wtl[NW][16 * 8];         // per wave: [16 rows][8 chunks]
+  __shared__ float s_amax[KIND == kProjGateUp ? NW : 1][kBM];
+  const int K = KIND == kProjGateUp ? H : I;              // reduction length
+  const int N = KIND == kProjGateUp ? I : H;              // outputs
+  const int KB = K / 32;                                  // scale bytes per row
+  const int nblk = N / (NW * RPW);
   const int item = real_item(blockIdx.x, nblk, *n_tiles);
   if (item < 0) return;
   const int tile = item / nblk, nb_i = item - tile * nblk;
@@ -416,257 +427,177 @@ __global__ __launch_bounds__(NW * 64) void gemm_gate_up_mx(
   const int e = te.x, m0 = te.y;
   const int mcount = min(kBM, counts[e] - m0);
   const int rbase = offsets[e] + m0;
-  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, col = ln & 15, grp = ln >> 4;
-  const int nb = nb_i * NW * 16 + wv * 16;
-  const int KB = H / 32;                               // scale bytes per row
+  const int tid = threadIdx.x, ln = tid & 63, col = ln & 15, grp = ln >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb = nb_i * NW * RPW + wv * RPW;              // the wave's first output
+  const int row0 = nb, row1 = KIND == kProjGateUp ? I + nb : nb + 16;
+  const size_t wrows = KIND == kProjGateUp ? 2 * static_cast<size_t>(I) : H;
 
-  const uint8_t* __restrict__ wb = wgu + static_cast<size_t>(e) * 2 * I * H;
-  const uint8_t* __restrict__ wsb = wgus + static_cast<size_t>(e) * 2 * I * KB;
-  const int rg = nb + col, ru = rg + I;
-  const uint32_t og = static_cast<uint32_t>(rg * H + 16 * grp);
-  const uint32_t ou = static_cast<uint32_t>(ru * H + 16 * grp);
-  const uint32_t osg = static_cast<uint32_t>(rg * KB + grp);
-  const uint32_t osu = static_cast<uint32_t>(ru * KB + grp);
+  // whole-line loads: lane = (row lr of an 8-row group, 16-byte chunk lc)
+  const int lr = ln >> 3, lc = ln & 7;
+  const uint8_t* __restrict__ wb = wt + static_cast<size_t>(e) * wrows * K;
+  const uint8_t* __restrict__ wsb = wts + static_cast<size_t>(e) * wrows * KB;
+  uint32_t ow[4];                                         // group 0 rows 0-7, 8-15, group 1 rows 0-7, 8-15
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    ow[i] = static_cast<uint32_t>(((i < 2 ? row0 : row1) + 8 * (i & 1) + lr) * K + lc * 16);
+  // scale bytes: lane (row col, group grp) of each 16-row group
+  const uint32_t osw0 = static_cast<uint32_t>((row0 + col) * KB);
+  const uint32_t osw1 = static_cast<uint32_t>((row1 + col) * KB);
+  i32x4* tw = wtl[wv];
+  i32x4* wdst = tw + lr * 8 + (lc ^ lr);                  // + 64 for rows 8-15
+  const i32x4* asrc = tw + col * 8;
+  const int sw = col & 7;
+
   // loaders: codes chunk c = tid + i*NT -> (row c/kMCH, 16-byte column c%kMCH);
   // scales: thread tid < 64 loads row tid's kMSC scale bytes of the stage
   uint32_t oxl[LPT];
   int lrow[LPT];
-  bool lact[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
-    const int c = tid + i * NT, r = c / kMCH;
-    lact[i] = c < kBM * kMCH;
-    const int rr = lact[i] && r < mcount ? r : 0;
-    lrow[i] = lact[i] ? r * kMRS + (c % kMCH) * 16 : 0;
-    oxl[i] = static_cast<uint32_t>((perm[rbase + rr] / k) * H + (c % kMCH) * 16);
+    const int c = tid + i * NT, r = c / kMCH, rr = r < mcount ? r : 0;
+    lrow[i] = r * kMRS + (c % kMCH) * 16;
+    const int arow = KIND == kProjGateUp ? perm[rbase + rr] / k : rbase + rr;
+    oxl[i] = static_cast<uint32_t>(arow * K + (c % kMCH) * 16);
   }
   const bool sload = tid < kBM;
-  const uint32_t osl = sload ? static_cast<uint32_t>((perm[rbase + (tid < mcount ? tid : 0)] / k) * KB) : 0u;
+  const int srow = tid < mcount ? tid : 0;
+  const uint32_t osl =
+      sload ? static_cast<uint32_t>((KIND == kProjGateUp ? perm[rbase + srow] / k : rbase + srow) * KB)
+            : 0u;
   i32x4 xr[LPT];
   uint2 sr = make_uint2(0u, 0u);
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) xr[i] = ld16(x + oxl[i]);
-  if (sload) sr = *reinterpret_cast<const uint2*>(xs + osl);
+  for (int i = 0; i < LPT; ++i) xr[i] = ld16(act + oxl[i]);
+  if (sload) sr = *reinterpret_cast<const uint2*>(acts + osl);
 #pragma unroll
-  for (int i = 0; i < LPT; ++i)
-    if (lact[i]) *reinterpret_cast<i32x4*>(&xl[0][lrow[i]]) = xr[i];
+  for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xl[0][lrow[i]]) = xr[i];
   if (sload) *reinterpret_cast<uint2*>(&sl[0][tid * kMSC]) = sr;
 
-  f32x4 ag[4], au[4];
+  f32x4 acc0[4], acc1[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) ag[g] = au[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  i32x8 wg0, wu0, wg1, wu1;
-  int sg0, su0, sg1, su1;
-#define GUM_W(WG, WU, SG, SU, KC)                                                  \
-  {                                                                                \
-    const int ko_ = (KC) * 128, so_ = (KC) * 4;                                    \
-    WG = cat8(ld16(wb + og + ko_), ld16(wb + og + ko_ + 64));                      \
-    WU = cat8(ld16(wb + ou + ko_), ld16(wb + ou + ko_ + 64));                      \
-    SG = wsb[osg + so_];                                                           \
-    SU = wsb[osu + so_];                                                           \
-  }
-#define GUM_MMA(WG, WU, SG, SU, CL)                                                \
-  _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                  \
-    const uint8_t* p_ = xcur + (16 * g) * kMRS + (CL) * 128;                       \
-    const i32x8 bx = cat8(*reinterpret_cast<const i32x4*>(p_),                     \
-                          *reinterpret_cast<const i32x4*>(p_ + 64));               \
-    const int sx = scur[(16 * g) * kMSC + (CL) * 4];                               \
-    ag[g] = mfma_mx16x16x128(WG, bx, SG, sx, ag[g]);                               \
-    au[g] = mfma_mx16x16x128(WU, bx, SU, sx, au[g]);                               \
-  }
-  const int chunks = H / 128;
-  GUM_W(wg0, wu0, sg0, su0, 0)
+  for (int g = 0; g < 4; ++g) acc0[g] = acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nchunk = K / 128;
+  i32x4 wA[4], wB[4];
+  uint2 scA0, scA1;                                       // this stage's scale bytes, groups 0 / 1
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wA[i] = ld16_stream(wb + ow[i]);
+  scA0 = *reinterpret_cast<const uint2*>(wsb + osw0);
+  scA1 = *reinterpret_cast<const uint2*>(wsb + osw1);
   __syncthreads();
-  const int nstage = H / kMXC;
+
+  // one 128-position chunk cc (0 or 1) of stage buffer buf: weights W, scale words
+  // s0 / s1 (byte grp of the word is this lane's block scale)
+  auto chunk = [&](const i32x4 (&W)[4], int buf, int cc, uint32_t s0, uint32_t s1) {
+    // both row groups' A operands through the tile, then each B fragment feeds both
+    i32x8 a[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      wdst[0] = W[2 * m];
+      wdst[64] = W[2 * m + 1];
+      __builtin_amdgcn_wave_barrier();
+      a[m] = cat8(asrc[grp ^ sw], asrc[(4 + grp) ^ sw]);
+      __builtin_amdgcn_wave_barrier();
+    }
+    const int sa0 = static_cast<int>((s0 >> (8 * grp)) & 0xFFu);
+    const int sa1 = static_cast<int>((s1 >> (8 * grp)) & 0xFFu);
+    const uint8_t* xcur = &xl[buf][col * kMRS + cc * 128 + 16 * grp];
+    const uint8_t* scur = &sl[buf][col * kMSC + cc * 4 + grp];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint8_t* p_ = xcur + (16 * g) * kMRS;
+      const i32x8 bx = cat8(*reinterpret_cast<const i32x4*>(p_), *reinterpret_cast<const i32x4*>(p_ + 64));
+      const int sx = scur[(16 * g) * kMSC];
+      acc0[g] = mfma_mx16x16x128(a[0], bx, sa0, sx, acc0[g]);
+      acc1[g] = mfma_mx16x16x128(a[1], bx, sa1, sx, acc1[g]);
+    }
+  };
+  const int nstage = K / kMXC;
   for (int st = 0; st < nstage; ++st) {
     const int buf = st & 1;
     const bool more = st + 1 < nstage;
     if (more) {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) xr[i] = ld16(x + oxl[i] + (st + 1) * kMXC);
-      if (sload) sr = *reinterpret_cast<const uint2*>(xs + osl + (st + 1) * kMSC);
+      for (int i = 0; i < LPT; ++i) xr[i] = ld16(act + oxl[i] + (st + 1) * kMXC);
+      if (sload) sr = *reinterpret_cast<const uint2*>(acts + osl + (st + 1) * kMSC);
     }
-    const uint8_t* xcur = &xl[buf][col * kMRS + 16 * grp];
-    const uint8_t* scur = &sl[buf][col * kMSC + grp];
-    const int kc = st * 2;
-    GUM_W(wg1, wu1, sg1, su1, kc + 1)
-    GUM_MMA(wg0, wu0, sg0, su0, 0)
-    GUM_W(wg0, wu0, sg0, su0, min(kc + 2, chunks - 1))
-    GUM_MMA(wg1, wu1, sg1, su1, 1)
+    // chunks 2st (weights in wA) and 2st+1 (wB); the chunk after each is loaded
+    // first (clamped to the last chunk / stage, a harmless repeat: fixed load count)
+    const uint32_t k1 = static_cast<uint32_t>((2 * st + 1) * 128);
+    const uint32_t k2 = static_cast<uint32_t>(min(2 * st + 2, nchunk - 1) * 128);
+    const uint32_t s2 = static_cast<uint32_t>(min(st + 1, nstage - 1) * kMSC);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wB[i] = ld16_stream(wb + ow[i] + k1);
+    chunk(wA, buf, 0, scA0.x, scA1.x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wA[i] = ld16_stream(wb + ow[i] + k2);
+    const uint2 scN0 = *reinterpret_cast<const uint2*>(wsb + osw0 + s2);
+    const uint2 scN1 = *reinterpret_cast<const uint2*>(wsb + osw1 + s2);
+    chunk(wB, buf, 1, scA0.y, scA1.y);
+    scA0 = scN0;
+    scA1 = scN1;
     if (more) {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i)
-        if (lact[i]) *reinterpret_cast<i32x4*>(&xl[buf ^ 1][lrow[i]]) = xr[i];
+      for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xl[buf ^ 1][lrow[i]]) = xr[i];
       if (sload) *reinterpret_cast<uint2*>(&sl[buf ^ 1][tid * kMSC]) = sr;
     }
     __syncthreads();
   }
-#undef GUM_W
-#undef GUM_MMA
-  // SwiGLU; per-row maximum over this wave's 16 neurons (lanes col + 16*grp),
-  // combined with the partner wave's through LDS, gives the MX scale of the
-  // 32-neuron block; then each wave encodes its own 16 neurons.
-  float a[4][4];
+  if (KIND == kProjGateUp) {
+    // SwiGLU; per-row maximum over this wave's 16 neurons (lanes col + 16*grp),
+    // combined with the partner wave's through LDS, gives the MX scale of the
+    // 32-neuron block; then each wave encodes its own 16 neurons.
+    float a[4][4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float amax = 0.f;
+    for (int g = 0; g < 4; ++g) {
+      float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[g][i] = swiglu(ag[g][i], au[g][i]);
-      amax = fmaxf(amax, fabsf(a[g][i]));
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-    if (grp == 0) s_amax[wv][16 * g + col] = amax;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int r = 16 * g + col;
-    if (r >= mcount) continue;
-    const float amax = fmaxf(s_amax[wv][r], s_amax[wv ^ 1][r]);
-    const int sexp = mx_scale_exp(amax);
-    const float inv = exp2_neg(sexp);
-    uint32_t wq = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wq |= f32_to_e4m3(a[g][i] * inv) << (8 * i);
-    *reinterpret_cast<uint32_t*>(h + static_cast<size_t>(rbase + r) * I + nb + 4 * grp) = wq;
-    if (grp == 0 && (wv & 1) == 0)
-      hs[static_cast<size_t>(rbase + r) * (I / 32) + nb / 32] = static_cast<uint8_t>(sexp + 127);
-  }
-}
-
-// down, MXFP8: workgroup = (M-tile, NW*32 output dims); wave = 32 dims (2
-// groups) x 64 rows; the h codes and scale bytes of the tile are staged in
-// LDS in stages of 256 along K, as in gate_up.
-template <bool FUSED, int NW>
-__global__ __launch_bounds__(NW * 64) void gemm_down_mx(
-    const uint8_t* __restrict__ h, const uint8_t* __restrict__ hs,
-    const uint8_t* __restrict__ wd, const uint8_t* __restrict__ wds,
-    const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
-    const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
-    int H, int I, float* __restrict__ y, uint16_t* __restrict__ out) {
-  __shared__ __align__(16) uint8_t hl[2][kBM * kMRS];
-  __shared__ __align__(16) uint8_t sl[2][kBM * kMSC];
-  constexpr int NT = NW * 64;
-  constexpr int LPT = (kBM * kMCH + NT - 1) / NT;
-  const int nblk = H / (NW * 32);
-  const int item = real_item(blockIdx.x, nblk, *n_tiles);
-  if (item < 0) return;
-  const int tile = item / nblk, db_i = item - tile * nblk;
-  const int2 te = tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int mcount = min(kBM, counts[e] - m0);
-  const int rbase = offsets[e] + m0;
-  const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, col = ln & 15, grp = ln >> 4;
-  const int db = db_i * NW * 32 + wv * 32;
-  const int KB = I / 32;
-
-  const uint8_t* __restrict__ wb = wd + static_cast<size_t>(e) * H * I;
-  const uint8_t* __restrict__ wsb = wds + static_cast<size_t>(e) * H * KB;
-  const uint8_t* __restrict__ hb = h + static_cast<size_t>(rbase) * I;
-  const uint8_t* __restrict__ hsb = hs + static_cast<size_t>(rbase) * KB;
-  uint32_t ow[2], osw[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = db + 16 * q + col;
-    ow[q] = static_cast<uint32_t>(row * I + 16 * grp);
-    osw[q] = static_cast<uint32_t>(row * KB + grp);
-  }
-  uint32_t ohl[LPT];
-  int lrow[LPT];
-  bool lact[LPT];
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int c = tid + i * NT, r = c / kMCH;
-    lact[i] = c < kBM * kMCH;
-    lrow[i] = lact[i] ? r * kMRS + (c % kMCH) * 16 : 0;
-    ohl[i] = static_cast<uint32_t>((lact[i] && r < mcount ? r : 0) * I + (c % kMCH) * 16);
-  }
-  const bool sload = tid < kBM;
-  const uint32_t osl = sload ? static_cast<uint32_t>((tid < mcount ? tid : 0) * KB) : 0u;
-  i32x4 hr_[LPT];
-  uint2 sr = make_uint2(0u, 0u);
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) hr_[i] = ld16(hb + ohl[i]);
-  if (sload) sr = *reinterpret_cast<const uint2*>(hsb + osl);
-#pragma unroll
-  for (int i = 0; i < LPT; ++i)
-    if (lact[i]) *reinterpret_cast<i32x4*>(&hl[0][lrow[i]]) = hr_[i];
-  if (sload) *reinterpret_cast<uint2*>(&sl[0][tid * kMSC]) = sr;
-
-  f32x4 acc[2][4];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) acc[q][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  i32x8 a0[2], a1[2];
-  int sa0[2], sa1[2];
-#define DNM_W(A, SA, KC)                                                           \
-  {                                                                                \
-    const int ko_ = (KC) * 128, so_ = (KC) * 4;                                    \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                \
-      A[q] = cat8(ld16(wb + ow[q] + ko_), ld16(wb + ow[q] + ko_ + 64));            \
-      SA[q] = wsb[osw[q] + so_];                                                   \
-    }                                                                              \
-  }
-#define DNM_MMA(A, SA, CL)                                                         \
-  _Pragma("unroll") for (int g = 0; g < 4; ++g) {                                  \
-    const uint8_t* p_ = hcur + (16 * g) * kMRS + (CL) * 128;                       \
-    const i32x8 bb = cat8(*reinterpret_cast<const i32x4*>(p_),                     \
-                          *reinterpret_cast<const i32x4*>(p_ + 64));               \
-    const int sb = scur[(16 * g) * kMSC + (CL) * 4];                               \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q)                                  \
-      acc[q][g] = mfma_mx16x16x128(A[q], bb, SA[q], sb, acc[q][g]);                \
-  }
-  const int chunks = I / 128;
-  DNM_W(a0, sa0, 0)
-  __syncthreads();
-  const int nstage = I / kMXC;
-  for (int st = 0; st < nstage; ++st) {
-    const int buf = st & 1;
-    const bool more = st + 1 < nstage;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) hr_[i] = ld16(hb + ohl[i] + (st + 1) * kMXC);
-      if (sload) sr = *reinterpret_cast<const uint2*>(hsb + osl + (st + 1) * kMSC);
-    }
-    const uint8_t* hcur = &hl[buf][col * kMRS + 16 * grp];
-    const uint8_t* scur = &sl[buf][col * kMSC + grp];
-    const int kc = st * 2;
-    DNM_W(a1, sa1, kc + 1)
-    DNM_MMA(a0, sa0, 0)
-    DNM_W(a0, sa0, min(kc + 2, chunks - 1))
-    DNM_MMA(a1, sa1, 1)
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < LPT; ++i)
-        if (lact[i]) *reinterpret_cast<i32x4*>(&hl[buf ^ 1][lrow[i]]) = hr_[i];
-      if (sload) *reinterpret_cast<uint2*>(&sl[buf ^ 1][tid * kMSC]) = sr;
-    }
-    __syncthreads();
-  }
-#undef DNM_W
-#undef DNM_MMA
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int r = 16 * g + col;
-    if (r >= mcount) continue;
-    if (FUSED) {
-      const int t = perm[rbase + r];
-      const float wt = w[t];
-      uint16_t* orow = out + static_cast<size_t>(t) * H + db + 4 * grp;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        uint2 v;
-        v.x = f32_to_bf16_rne(wt * acc[q][g][0]) | (f32_to_bf16_rne(wt * acc[q][g][1]) << 16);
-        v.y = f32_to_bf16_rne(wt * acc[q][g][2]) | (f32_to_bf16_rne(wt * acc[q][g][3]) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * q) = v;
+      for (int i = 0; i < 4; ++i) {
+        a[g][i] = swiglu(acc0[g][i], acc1[g][i]);
+        amax = fmaxf(amax, fabsf(a[g][i]));
       }
-    } else {
-      float* yr = y + static_cast<size_t>(rbase + r) * H + db + 4 * grp;
+      amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      if (grp == 0) s_amax[KIND == kProjGateUp ? wv : 0][16 * g + col] = amax;
+    }
+    __syncthreads();
 #pragma unroll
-      for (int q = 0; q < 2; ++q) *reinterpret_cast<f32x4*>(yr + 16 * q) = acc[q][g];
+    for (int g = 0; g < 4; ++g) {
+      const int r = 16 * g + col;
+      if (r >= mcount) continue;
+      const float amax = fmaxf(s_amax[KIND == kProjGateUp ? wv : 0][r],
+                               s_amax[KIND == kProjGateUp ? (wv ^ 1) : 0][r]);
+      const int sexp = mx_scale_exp(amax);
+      const float inv = exp2_neg(sexp);
+      uint32_t wq = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wq |= f32_to_e4m3(a[g][i] * inv) << (8 * i);
+      *reinterpret_cast<uint32_t*>(hout + static_cast<size_t>(rbase + r) * I + nb + 4 * grp) = wq;
+      if (grp == 0 && (wv & 1) == 0)
+        hsout[static_cast<size_t>(rbase + r) * (I / 32) + nb / 32] = static_cast<uint8_t>(sexp + 127);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r = 16 * g + col;
+      if (r >= mcount) continue;
+      if (KIND == kProjDownFused) {
+        const int t = perm[rbase + r];                    // k = 1: pair id == token
+        const float wt_ = w[t];
+        uint16_t* orow = out + static_cast<size_t>(t) * H + nb + 4 * grp;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const f32x4 a = m == 0 ? acc0[g] : acc1[g];
+          uint2 v;
+          v.x = f32_to_bf16_rne(wt_ * a[0]) | (f32_to_bf16_rne(wt_ * a[1]) << 16);
+          v.y = f32_to_bf16_rne(wt_ * a[2]) | (f32_to_bf16_rne(wt_ * a[3]) << 16);
+          *reinterpret_cast<uint2*>(orow + 16 * m) = v;
+        }
+      } else {
+        float* yr = y + static_cast<size_t>(rbase + r) * H + nb + 4 * grp;
+        *reinterpret_cast<f32x4*>(yr) = acc0[g];
+        *reinterpret_cast<f32x4*>(yr + 16) = acc1[g];
+      }
     }
   }
 }
@@ -721,19 +652,20 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
     prof_end(kGemmGateUp, s);
     return e;
   }
-  constexpr int NW = 8;          // BF16: 8 waves x 32 neurons; MXFP8: 8 waves x 16 neurons
-  const int n_items = round_up((I / (dtype == 0 ? NW * 32 : NW * 16)) * L.max_tiles, kXcds);
+  // BF16: 16 waves x 16 neurons = 256 neurons per workgroup (I is a multiple of
+  // 256); MXFP8: 8 waves x 16 (its wide operands take ~200 registers per lane)
+  const int n_items = round_up((I / (dtype == 0 ? 256 : 128)) * L.max_tiles, kXcds);
   prof_begin(kGemmGateUp, s);
-  if (dtype == 0)   // 16 waves x 16 neurons = 256 neurons per workgroup, as NW * 32 above
+  if (dtype == 0)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
                        static_cast<uint16_t*>(h), nullptr, nullptr);
   else
-    hipLaunchKernelGGL(gemm_gate_up_mx<NW>, dim3(n_items), dim3(NW * 64), 0, s,
+    hipLaunchKernelGGL((gemm_mx_s<kProjGateUp, 8>), dim3(n_items), dim3(512), 0, s,
                        static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
-                       p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, H, I, k,
-                       static_cast<uint8_t*>(h), hs);
+                       p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
+                       static_cast<uint8_t*>(h), hs, nullptr, nullptr);
   prof_end(kGemmGateUp, s);
   return hipGetLastError();
 }
@@ -766,28 +698,29 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
     }
     return e;
   }
-  // output dims per workgroup: BF16 16 waves x 32 (8 x 32 when H is not a
-  // multiple of 512); MXFP8 8 waves x 32
+  // output dims per workgroup: BF16 16 waves x 32 (8 x 32 when H is not a multiple
+  // of 512); MXFP8 8 x 32
   const bool wide = dtype == 0 && H % 512 == 0;
-  const int dims = dtype == 0 ? (wide ? 512 : 256) : 256;
+  const int dims = wide ? 512 : 256;
   const int n_items = round_up((H / dims) * L.max_tiles, kXcds);
-  const dim3 grid(n_items), block(dtype == 0 ? 2 * dims : 512);
+  const dim3 grid(n_items), block(2 * dims);
 #define DOWN_BF16(KINDV, NWV)                                                               \
   hipLaunchKernelGGL((gemm_bf16s<KINDV, NWV>), grid, block, 0, s,                          \
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),       \
                      p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr,   \
                      p.y, out)
-#define DOWN_MX(F, NWV)                                                                     \
-  hipLaunchKernelGGL((gemm_down_mx<F, NWV>), grid, block, 0, s,                            \
+#define DOWN_MX(KINDV, NWV)                                                                 \
+  hipLaunchKernelGGL((gemm_mx_s<KINDV, NWV>), grid, block, 0, s,                           \
                      static_cast<const uint8_t*>(h), hs, static_cast<const uint8_t*>(wd), wds, \
-                     p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, p.y, out)
+                     p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr,   \
+                     nullptr, p.y, out)
   prof_begin(kGemmDown, s);
   if (dtype == 0) {
     if (k == 1) { if (wide) DOWN_BF16(kProjDownFused, 16); else DOWN_BF16(kProjDownFused, 8); }
     else { if (wide) DOWN_BF16(kProjDown, 16); else DOWN_BF16(kProjDown, 8); }
   } else {
-    if (k == 1) DOWN_MX(true, 8);
-    else DOWN_MX(false, 8);
+    if (k == 1) DOWN_MX(kProjDownFused, 8);
+    else DOWN_MX(kProjDown, 8);
   }
 #undef DOWN_BF16
 #undef DOWN_MX
