@@ -486,30 +486,34 @@ __global__ __launch_bounds__(NW * 64) void gemm_mx_s(
   scA1 = *reinterpret_cast<const uint2*>(wsb + osw1);
   __syncthreads();
 
-  // one 128-position chunk cc (0 or 1) of stage buffer buf: weights W, scale words
-  // s0 / s1 (byte grp of the word is this lane's block scale)
-  auto chunk = [&](const i32x4 (&W)[4], int buf, int cc, uint32_t s0, uint32_t s1) {
-    // both row groups' A operands through the tile, then each B fragment feeds both
-    i32x8 a[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      wdst[0] = W[2 * m];
-      wdst[64] = W[2 * m + 1];
-      __builtin_amdgcn_wave_barrier();
-      a[m] = cat8(asrc[grp ^ sw], asrc[(4 + grp) ^ sw]);
-      __builtin_amdgcn_wave_barrier();
-    }
-    const int sa0 = static_cast<int>((s0 >> (8 * grp)) & 0xFFu);
-    const int sa1 = static_cast<int>((s1 >> (8 * grp)) & 0xFFu);
+  // one 128-position chunk cc (0 or 1) of stage buffer buf: weights W, block scales
+  // sa0 / sa1 of this lane's rows.  One row group at a time (its A operand, then
+  // the four B fragments); the empty asm statements keep each MFMA at its place,
+  // where the compiler would otherwise sink them all to the end of the stage and
+  // hold every operand live (beyond the 128 registers of 16 waves per CU).
+  auto chunk = [&](const i32x4 (&W)[4], int buf, int cc, int sa0, int sa1) {
     const uint8_t* xcur = &xl[buf][col * kMRS + cc * 128 + 16 * grp];
     const uint8_t* scur = &sl[buf][col * kMSC + cc * 4 + grp];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint8_t* p_ = xcur + (16 * g) * kMRS;
-      const i32x8 bx = cat8(*reinterpret_cast<const i32x4*>(p_), *reinterpret_cast<const i32x4*>(p_ + 64));
-      const int sx = scur[(16 * g) * kMSC];
-      acc0[g] = mfma_mx16x16x128(a[0], bx, sa0, sx, acc0[g]);
-      acc1[g] = mfma_mx16x16x128(a[1], bx, sa1, sx, acc1[g]);
+    for (int m = 0; m < 2; ++m) {                         // row group 0, then 1
+      wdst[0] = W[2 * m];
+      wdst[64] = W[2 * m + 1];
+      __builtin_amdgcn_wave_barrier();
+      const i32x8 a = cat8(asrc[grp ^ sw], asrc[(4 + grp) ^ sw]);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint8_t* p_ = xcur + (16 * g) * kMRS;
+        const i32x8 bx = cat8(*reinterpret_cast<const i32x4*>(p_), *reinterpret_cast<const i32x4*>(p_ + 64));
+        const int sx = scur[(16 * g) * kMSC];
+        if (m == 0) {
+          acc0[g] = mfma_mx16x16x128(a, bx, sa0, sx, acc0[g]);
+          asm volatile("" : "+v"(acc0[g]));
+        } else {
+          acc1[g] = mfma_mx16x16x128(a, bx, sa1, sx, acc1[g]);
+          asm volatile("" : "+v"(acc1[g]));
+        }
+      }
     }
   };
   const int nstage = K / kMXC;
@@ -528,14 +532,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_mx_s(
     const uint32_t s2 = static_cast<uint32_t>(min(st + 1, nstage - 1) * kMSC);
 #pragma unroll
     for (int i = 0; i < 4; ++i) wB[i] = ld16_stream(wb + ow[i] + k1);
-    chunk(wA, buf, 0, scA0.x, scA1.x);
+    const int b1_0 = static_cast<int>((scA0.y >> (8 * grp)) & 0xFFu);   // chunk 1's scale bytes
+    const int b1_1 = static_cast<int>((scA1.y >> (8 * grp)) & 0xFFu);
+    chunk(wA, buf, 0, static_cast<int>((scA0.x >> (8 * grp)) & 0xFFu),
+          static_cast<int>((scA1.x >> (8 * grp)) & 0xFFu));
 #pragma unroll
     for (int i = 0; i < 4; ++i) wA[i] = ld16_stream(wb + ow[i] + k2);
-    const uint2 scN0 = *reinterpret_cast<const uint2*>(wsb + osw0 + s2);
-    const uint2 scN1 = *reinterpret_cast<const uint2*>(wsb + osw1 + s2);
-    chunk(wB, buf, 1, scA0.y, scA1.y);
-    scA0 = scN0;
-    scA1 = scN1;
+    scA0 = *reinterpret_cast<const uint2*>(wsb + osw0 + s2);
+    scA1 = *reinterpret_cast<const uint2*>(wsb + osw1 + s2);
+    chunk(wB, buf, 1, b1_0, b1_1);
     if (more) {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xl[buf ^ 1][lrow[i]]) = xr[i];
@@ -652,9 +657,8 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
     prof_end(kGemmGateUp, s);
     return e;
   }
-  // BF16: 16 waves x 16 neurons = 256 neurons per workgroup (I is a multiple of
-  // 256); MXFP8: 8 waves x 16 (its wide operands take ~200 registers per lane)
-  const int n_items = round_up((I / (dtype == 0 ? 256 : 128)) * L.max_tiles, kXcds);
+  // 16 waves x 16 neurons = 256 neurons per workgroup (I is a multiple of 256)
+  const int n_items = round_up((I / 256) * L.max_tiles, kXcds);
   prof_begin(kGemmGateUp, s);
   if (dtype == 0)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 16>), dim3(n_items), dim3(1024), 0, s,
@@ -662,7 +666,7 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
                        static_cast<uint16_t*>(h), nullptr, nullptr);
   else
-    hipLaunchKernelGGL((gemm_mx_s<kProjGateUp, 8>), dim3(n_items), dim3(512), 0, s,
+    hipLaunchKernelGGL((gemm_mx_s<kProjGateUp, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
                        p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
                        static_cast<uint8_t*>(h), hs, nullptr, nullptr);
@@ -698,9 +702,8 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
     }
     return e;
   }
-  // output dims per workgroup: BF16 16 waves x 32 (8 x 32 when H is not a multiple
-  // of 512); MXFP8 8 x 32
-  const bool wide = dtype == 0 && H % 512 == 0;
+  // output dims per workgroup: 16 waves x 32 (8 x 32 when H is not a multiple of 512)
+  const bool wide = H % 512 == 0;
   const int dims = wide ? 512 : 256;
   const int n_items = round_up((H / dims) * L.max_tiles, kXcds);
   const dim3 grid(n_items), block(2 * dims);
@@ -719,8 +722,8 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
     if (k == 1) { if (wide) DOWN_BF16(kProjDownFused, 16); else DOWN_BF16(kProjDownFused, 8); }
     else { if (wide) DOWN_BF16(kProjDown, 16); else DOWN_BF16(kProjDown, 8); }
   } else {
-    if (k == 1) DOWN_MX(kProjDownFused, 8);
-    else DOWN_MX(kProjDown, 8);
+    if (k == 1) { if (wide) DOWN_MX(kProjDownFused, 16); else DOWN_MX(kProjDownFused, 8); }
+    else { if (wide) DOWN_MX(kProjDown, 16); else DOWN_MX(kProjDown, 8); }
   }
 #undef DOWN_BF16
 #undef DOWN_MX
