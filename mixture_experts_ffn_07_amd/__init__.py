@@ -43,7 +43,7 @@ _SIGS = {
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m mixture_experts_ffn_07_amd.build`")
+                          "`python mixture_experts_ffn_07_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)

@@ -1,6 +1,9 @@
 """Build the gfx950 shared library libmoe_mi355x.so in-tree with hipcc.
 
-    python -m mixture_experts_ffn_07_amd.build [-v]
+    python mixture_experts_ffn_07_amd/build.py [-v]
+
+(run as a file: importing the package loads the built library, so it cannot
+come first.)
 
 Every HIP source is compiled for gfx950 only, with packed-FP32 instruction
 selection switched off, then linked into one shared object next to this file.

@@ -12,7 +12,12 @@ HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
 
 @pytest.fixture(scope="module")
 def m():
-    from mixture_experts_ffn_07_amd import build as B
+    # the build script by path: importing the package needs the built library
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "moe_mi355x_build", os.path.join(ROOT, "mixture_experts_ffn_07_amd", "build.py"))
+    B = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(B)
     if not os.path.exists(B.LIB):
         B.build()
     import mixture_experts_ffn_07_amd as M
