@@ -23,6 +23,7 @@
 // atomics (the only atomic is an integer OR that builds expert token masks).
 #include "common.h"
 #include "internal.h"
+#include "route.h"
 
 namespace moe {
 
@@ -168,26 +169,58 @@ __device__ void publish_plan(int U, int P, const int* s_e, const int* s_off, con
 // The workgroup walks its flat sequence of (item, chunk) tasks with the
 // weights of the next task loaded into a second register buffer while the
 // current one is multiplied, so the weight stream never waits on an epilogue.
+//
+// At T <= 16 (route != 0) the routing runs here too: a separate launch and its
+// gap before this kernel cost more than routing two tokens per wave.  Every
+// workgroup routes all T tokens (the same routine as moe_route_topk, so the
+// result is bit-identical) into LDS past the plan scratch, and workgroup 0
+// writes topk_idx / topk_w out.  Otherwise the routing launch has written them
+// and each workgroup copies them into the same LDS area.
 template <int TM8, int NG, int KC>   // TM8 <= 4: T <= 32
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_gate_up(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
-    const int32_t* __restrict__ idx, const float* __restrict__ wts, int T, int E,
-    int* __restrict__ plan_u, int32_t* __restrict__ plan_e, int32_t* __restrict__ plan_off,
-    uint16_t* __restrict__ plan_pr, int H, int I, int k, uint16_t* __restrict__ hw) {
+    const float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ wts,
+    int T, int E, int* __restrict__ plan_u, int32_t* __restrict__ plan_e,
+    int32_t* __restrict__ plan_off, uint16_t* __restrict__ plan_pr, int H, int I, int k,
+    uint16_t* __restrict__ hw, int route_off, int route) {
   constexpr int NB = 8 * NG;                        // neurons per item
-  // two buffers (alternate items) of [8 waves][TM8 tiles][NG groups][gate/up][4 regs]
-  // [16 lanes] FP32 per-wave sums
+  // dynamic LDS: two buffers (alternate items) of [8 waves][TM8 tiles][NG groups]
+  // [gate/up][4 regs][16 lanes] FP32 per-wave sums, which the plan scratch (E masks,
+  // E + 33 ints) borrows first; at byte route_off the routing result [T*k] ids, weights
   extern __shared__ float red[];
   __shared__ int s_e[kMaxPlan];
   __shared__ int s_off[kMaxPlan + 1];
   __shared__ uint16_t s_pr[kMaxPairs];
   __shared__ float s_w[kMaxPairs];                  // routing weight of each plan entry
-  // the plan's scratch (E masks, E + 33 ints) borrows the reduction buffer
-  const int U = build_plan(idx, T, E, k, reinterpret_cast<uint64_t*>(red),
+  int32_t* r_idx = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(red) + route_off);
+  float* r_w = reinterpret_cast<float*>(r_idx + T * k);
+  if (route) {
+    // wave w routes tokens w and w + 8 (T <= 16)
+    const int w0 = wave_id();
+    if (E <= 64) route_tokens_wave<1, 2>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
+    else if (E <= 128) route_tokens_wave<2, 2>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
+    else if (E <= 256) route_tokens_wave<4, 2>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
+    else if (E <= 512) route_tokens_wave<8, 2>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
+    else route_tokens_wave<16, 2>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int i = threadIdx.x; i < T * k; i += kDecThreads) {
+        idx[i] = r_idx[i];
+        wts[i] = r_w[i];
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < T * k; i += kDecThreads) {
+      r_idx[i] = idx[i];
+      r_w[i] = wts[i];
+    }
+    __syncthreads();
+  }
+  const int U = build_plan(r_idx, T, E, k, reinterpret_cast<uint64_t*>(red),
                            reinterpret_cast<int*>(reinterpret_cast<uint64_t*>(red) + E), s_e,
                            s_off, s_pr);
   // (the epilogues then issue no global loads, which would wait on the weight stream)
-  for (int i = threadIdx.x; i < T * k; i += kDecThreads) s_w[i] = wts[s_pr[i]];
+  for (int i = threadIdx.x; i < T * k; i += kDecThreads) s_w[i] = r_w[s_pr[i]];
   if (blockIdx.x == 0) publish_plan(U, T * k, s_e, s_off, s_pr, plan_u, plan_e, plan_off, plan_pr);
   const int nrb = I / NB;
   const int items = U * nrb;
@@ -931,12 +964,16 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   float* w_p = w ? w : reinterpret_cast<float*>(base + L.w);
   uint16_t* hw = reinterpret_cast<uint16_t*>(base + L.hw);
 
-  hipError_t err = launch_route_topk(logits, T, E, k, idx_p, w_p, s);   // brackets kRoute
-  if (err != hipSuccess) return err;
+  // T <= 16: the gate_up kernel routes the tokens itself; otherwise a routing launch first
+  const bool wide = T > 32;
+  const int fuse_route = T <= 16;
+  if (!fuse_route) {
+    const hipError_t err = launch_route_topk(logits, T, E, k, idx_p, w_p, s);   // brackets kRoute
+    if (err != hipSuccess) return err;
+  }
 
   // gate_up: T <= 32 takes the narrow kernel (8-token tiles, full-line streamed
   // weights); T > 32 the wide one (16-token tiles)
-  const bool wide = T > 32;
   const int TM8 = T <= 8 ? 1 : (T <= 16 ? 2 : 4);
   // register budget (128 per lane): weights of two tasks + 16*NG accumulators per tile
   const int NG = TM8 <= 2 ? 2 : 1;
@@ -948,10 +985,13 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   const long items_upper = static_cast<long>(T * k < E ? T * k : E) * (I / (wide ? 16 : 8 * NG));
   const long grid_cap = 2L * num_cus;
   const int grid1 = static_cast<int>(items_upper < grid_cap ? items_upper : grid_cap);
-  // reduction buffer; the plan scratch (E masks + chunk offsets) must fit in it too
+  // reduction buffer; the plan scratch (E masks + chunk offsets) must fit in it too;
+  // the narrow kernel keeps its routing result past both
   size_t lds_gu = wide ? sizeof(float) * kDecWaves * 4 * 2 * 256 : gate_up_lds_bytes(TM8, NG);
   const size_t lds_plan = sizeof(uint64_t) * E + sizeof(int) * (E + 33);
   if (lds_plan > lds_gu) lds_gu = lds_plan;
+  const int route_off = static_cast<int>((lds_gu + 15) / 16 * 16);
+  if (!wide) lds_gu = route_off + static_cast<size_t>(T) * k * (sizeof(int32_t) + sizeof(float));
   // down: K-slices per workgroup (a power of two, so that the 16 waves split into
   // expert groups), the fewest that leave each wave at most 4 steps of 64; I is a
   // multiple of 256 up to 2048, so I/64 is 4, 8, ..., 32, and the two sizes with no
@@ -969,7 +1009,8 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   prof_begin(kDecGateUp, s);
 #define GU_LAUNCH(TMV, NGV, KCV)                                                               \
   hipLaunchKernelGGL((decode_gate_up<TMV, NGV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, \
-                     x, wgu, idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw)
+                     x, wgu, logits, idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, \
+                     k, hw, route_off, fuse_route)
 #define GU_WIDE(KCV)                                                                            \
   hipLaunchKernelGGL((decode_gate_up_wide<KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x, wgu, \
                      idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw)

@@ -109,6 +109,34 @@ __device__ __forceinline__ void route_token(const float* __restrict__ lrow, int 
   route_token_regs<R>(v, E, k, out_e, out_w);
 }
 
+// Routes tokens t = t0, t0 + step, ... (at most NT of them, t < T) with one wave:
+// every token's logits are loaded before the first is routed, so the load
+// latencies overlap.  Lanes j < k of token t write (expert, weight) of slot j to
+// idx[t*k + j], w[t*k + j].
+template <int R, int NT>
+__device__ __forceinline__ void route_tokens_wave(const float* __restrict__ logits, int T, int E,
+                                                  int k, int t0, int step, int32_t* idx, float* w) {
+  float v[NT][R];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int t = t0 + j * step;
+    if (t < T) load_logits<R>(logits + static_cast<size_t>(t) * E, E, v[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int t = t0 + j * step;
+    if (t < T) {
+      int e;
+      float wt;
+      route_token_regs<R>(v[j], E, k, &e, &wt);
+      if (lane_id() < k) {
+        idx[t * k + lane_id()] = e;
+        w[t * k + lane_id()] = wt;
+      }
+    }
+  }
+}
+
 // Dispatch on the number of candidates per lane (E <= 1024).
 __device__ __forceinline__ void route_token_any(const float* __restrict__ lrow, int E, int k,
                                                 int* out_e, float* out_w) {
