@@ -32,6 +32,16 @@ def bf16_decode(bits) -> np.ndarray:
         return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def bf16_round(v) -> np.ndarray:
+    """float64 -> the nearest BF16 value (8 significant bits, float32's
+    exponent range), ties to even, returned as float64.  Finite inputs whose
+    rounded magnitude stays below 2^128."""
+    v = np.asarray(v, dtype=np.float64)
+    _, ex = np.frexp(v)                           # v = m * 2^ex, 0.5 <= |m| < 1
+    q = np.exp2(np.maximum(ex - 8, -133).astype(np.float64))   # one unit in the 8th bit
+    return np.rint(v / q) * q                     # exact: q is a power of two
+
+
 def e4m3_decode(codes) -> np.ndarray:
     """uint8 E4M3 codes -> float64 (exact); 0x7F / 0xFF decode to NaN."""
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)

@@ -33,7 +33,7 @@ from typing import Optional, Sequence, Union
 
 import numpy as np
 
-from .formats import bf16_decode, mx_dequantize, mx_quantize
+from .formats import bf16_decode, bf16_round, mx_dequantize, mx_quantize
 
 ArrayLike = Union[np.ndarray, Sequence]
 
@@ -89,7 +89,7 @@ def _expert_matrix(w, e: int, dtype: str, scales=None) -> np.ndarray:
 def moe_forward(x, logits, w_gate_up, w_down, k: int, dtype: str = "bf16",
                 w_gate_up_scales=None, w_down_scales=None,
                 tokens: Optional[ArrayLike] = None,
-                return_intermediates: bool = False):
+                return_intermediates: bool = False, h_round: str = "exact"):
     """The whole layer in float64.
 
     x           [T, H] uint16 BF16 bit patterns
@@ -100,10 +100,18 @@ def moe_forward(x, logits, w_gate_up, w_down, k: int, dtype: str = "bf16",
     w_down      [E, H, I] likewise (scales [E, H, I/32])
     tokens      optional subset of token ids: only those rows are computed
                 (every token's output depends on that token alone)
+    h_round     rounding of the gated activations a before the down projection,
+                for the accuracy comparison the warp-decode article draws
+                ("Comparison": no quantized intermediate activations): "exact"
+                (none, the default), "bf16" (round to nearest even), "mxfp8"
+                (E4M3 + E8M0 blocks of 32 along I, the MXFP8 mode's rule).  In
+                MXFP8 mode a is always MX-quantized and h_round must be "exact".
     Returns out [n_tokens, H] float64, or (out, dict) with the routing, the
     per-slot activations a [n, k, I] and expert outputs y [n, k, H]."""
     if dtype not in ("bf16", "mxfp8"):
         raise ValueError(dtype)
+    if h_round not in ("exact", "bf16", "mxfp8") or (dtype == "mxfp8" and h_round != "exact"):
+        raise ValueError(h_round)
     x = np.asarray(x, dtype=np.uint16)
     logits = np.asarray(logits, dtype=np.float32)
     if tokens is not None:
@@ -130,8 +138,10 @@ def moe_forward(x, logits, w_gate_up, w_down, k: int, dtype: str = "bf16",
         g = xe @ wgu[:I].T                           # gate projection
         u = xe @ wgu[I:].T                           # up projection
         a = silu(g) * u                              # SwiGLU
-        if dtype == "mxfp8":
+        if dtype == "mxfp8" or h_round == "mxfp8":
             a = mx_dequantize(*mx_quantize(a))
+        elif h_round == "bf16":
+            a = bf16_round(a)
         y[rows, slots] = a @ wd.T                    # down projection
         if return_intermediates:
             if a_all is None:

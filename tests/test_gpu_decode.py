@@ -118,3 +118,25 @@ def test_decode_rejects_large_batch(M):
     with pytest.raises(M.MoeError) as e:
         M.moe_decode_forward(d["x"], d["logits"], d["w_gate_up"], d["w_down"], 2)
     assert e.value.status == -5
+
+
+def test_decode_accuracy_study(M):
+    # the GPU decode (BF16 hand-off) against the FP64 oracle, beside the oracle's
+    # own BF16-hand-off and FP8-hand-off variants (tests/test_accuracy_study.py)
+    from oracle import moe_forward
+    from oracle.formats import bf16_round
+    from oracle.moe import rel_l2
+    from tests._gpu import Fetch, bits
+    d = W.make("qwen3-decode-T8", seed=0, device="cuda")
+    cfg = d["cfg"]
+    print(f"[decode] accuracy study: qwen3-decode-T8", flush=True)
+    out, _, _ = _run(M, d)
+    args = (bits(d["x"]), d["logits"].cpu().numpy(), Fetch(d["w_gate_up"]), Fetch(d["w_down"]), cfg.k)
+    exact = moe_forward(*args)
+    d_gpu = rel_l2(out.cpu().double().numpy(), exact)
+    d_bf16 = rel_l2(bf16_round(moe_forward(*args, h_round="bf16")), exact)
+    d_fp8 = rel_l2(bf16_round(moe_forward(*args, h_round="mxfp8")), exact)
+    print(f"[accuracy] GPU decode {d_gpu:.3e}; oracle with BF16 h {d_bf16:.3e}, with MXFP8 h "
+          f"{d_fp8:.3e}; FP8 / GPU = {d_fp8 / d_gpu:.2f}", flush=True)
+    assert d_gpu < 1.2 * d_bf16
+    assert d_fp8 > 3 * d_gpu

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import formats as F
 from oracle import moe_forward, route
 from tests._exact import bf16_bits_to_float, mx_block_exact
 
@@ -182,3 +183,53 @@ def test_shape_mismatch_rejected():
     x, logits, wgu, wd = _rand_layer(rng, 2, 32, 16, 4)
     with pytest.raises(ValueError):
         moe_forward(x, logits, wgu, wd[:, :, :8], 2)
+
+
+def _mx_exact(rng, shape):
+    """Values whose MX quantization is exact: E4M3 codes times one power of two
+    per block of 32 along the last axis, each block holding a +-256 (so the
+    block rule recovers the same scale).  Returns (codes, scales, float64)."""
+    *lead, K = shape
+    codes = rng.integers(0, 0x7F, size=shape).astype(np.uint8)     # finite, positive
+    codes |= (rng.integers(0, 2, size=shape).astype(np.uint8) << 7)  # random sign
+    blk = codes.reshape(*lead, K // 32, 32)
+    blk[..., 0] = 0x78 | (blk[..., 0] & 0x80)                       # +-256 = 1.0 * 2^8
+    blk[..., 1:] = np.where((blk[..., 1:] & 0x7F) > 0x78, blk[..., 1:] & 0x80, blk[..., 1:])
+    codes = blk.reshape(shape)
+    scales = rng.integers(118, 126, size=(*lead, K // 32)).astype(np.uint8)
+    vals = F.mx_dequantize(codes, scales)
+    return codes, scales, vals
+
+
+def test_h_round_mxfp8_equals_mxfp8_mode_on_mx_exact_inputs():
+    # with x and the weights already exactly MX-representable, the MXFP8 mode
+    # (which re-quantizes x and a) and the BF16 mode with a quantized by h_round
+    # perform the same float64 arithmetic
+    rng = np.random.default_rng(21)
+    T, H, I, E, k = 5, 64, 64, 4, 2
+    _, _, xv = _mx_exact(rng, (T, H))
+    gc, gs, gv = _mx_exact(rng, (E, 2 * I, H))
+    dc, ds, dv = _mx_exact(rng, (E, H, I))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    a = moe_forward(_bf16_bits(xv), logits, gc, dc, k, dtype="mxfp8",
+                    w_gate_up_scales=gs, w_down_scales=ds)
+    b = moe_forward(_bf16_bits(xv), logits, _bf16_bits(gv), _bf16_bits(dv), k, h_round="mxfp8")
+    assert np.array_equal(a, b)
+
+
+def test_h_round_bf16_rounds_the_activations_once():
+    rng = np.random.default_rng(22)
+    x, logits, wgu, wd = _rand_layer(rng, 4, 64, 32, 6)
+    exact, ie = moe_forward(x, logits, wgu, wd, 3, return_intermediates=True)
+    rounded, ir = moe_forward(x, logits, wgu, wd, 3, h_round="bf16", return_intermediates=True)
+    assert np.array_equal(ir["a"], F.bf16_round(ie["a"]))
+    # the output moves by at most the rounding of a, carried through the down projection
+    dv = F.bf16_decode(wd)
+    bound = np.zeros_like(exact)
+    for t in range(4):
+        for j in range(3):
+            e = ie["idx"][t, j]
+            bound[t] += ie["w"][t, j] * (np.abs(dv[e]) @ (np.abs(ie["a"][t, j]) * 2.0 ** -8))
+    assert np.all(np.abs(rounded - exact) <= bound * (1 + 1e-9) + 1e-300)
+    with pytest.raises(ValueError):
+        moe_forward(x, logits, wgu, wd, 3, h_round="fp8")

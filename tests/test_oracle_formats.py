@@ -117,3 +117,30 @@ def test_mx_quantize_invariants():
     c2, s2 = F.mx_quantize(v * 2.0 ** 5)
     assert np.array_equal(c2, codes)
     assert np.array_equal(s2.astype(int) - scales.astype(int), np.full(scales.shape, 5))
+
+
+def test_bf16_round_matches_torch_on_float32_inputs():
+    # torch's float32 -> bfloat16 cast (round to nearest even) is an independent
+    # routine; on float32 inputs one rounding from float64 equals it
+    rng = np.random.default_rng(11)
+    mag = rng.standard_normal(40000) * np.exp2(rng.integers(-140, 120, 40000).astype(np.float64))
+    ties = (rng.integers(0, 1 << 16, 2000).astype(np.uint32) << 16 | 0x8000).view(np.float32)
+    subn = (rng.integers(1, 1 << 23, 2000).astype(np.uint32)).view(np.float32)   # float32 subnormals
+    v = np.concatenate([mag.astype(np.float32), ties, subn, -ties, np.float32([0.0, -0.0])])
+    v = v[np.isfinite(v)]
+    ours = F.bf16_round(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_round_fixes_bf16_values_and_bounds_error():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = F.bf16_decode(bits)
+    vals = vals[np.isfinite(vals)]
+    assert np.array_equal(F.bf16_round(vals), vals)            # BF16 values are fixed points
+    rng = np.random.default_rng(12)
+    v = rng.standard_normal(100000) * np.exp2(rng.integers(-100, 100, 100000).astype(np.float64))
+    r = F.bf16_round(v)
+    # unit roundoff of an 8-bit significand: |r - v| <= 2^-8 |v|
+    assert np.all(np.abs(r - v) <= np.abs(v) * 2.0 ** -8 * (1 + 1e-15))
+    assert np.array_equal(F.bf16_round(r), r)
