@@ -52,8 +52,9 @@ def _custom(T, H, I, E, k, seed=0, x_std=1.0):
     (1, 256, 256, 4, 2),        # one token
     (100, 512, 256, 8, 2),      # ~25 rows per expert
     (300, 256, 512, 6, 3),      # >64 rows per expert: several M-tiles, ragged last tile
-    (257, 768, 256, 40, 8),     # many small experts, some empty; 4-wave down
+    (257, 768, 256, 40, 8),     # many small experts, some empty; 8-wave down (H % 512 != 0)
     (500, 512, 256, 6, 1),      # k = 1: down writes the output directly
+    (200, 768, 512, 5, 1),      # k = 1 with the 8-wave down
     (64, 256, 256, 16, 16),     # k = E
 ])
 def test_batched_shapes(M, T, H, I, E, k):

@@ -95,11 +95,12 @@ def _custom(T, H, I, E, k, seed=0):
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [
-    (1, 256, 256, 4, 2),        # one token; 4-wave down
+    (1, 256, 256, 4, 2),        # one token; 8-wave down (H % 512 != 0)
     (100, 1024, 512, 8, 2),
     (300, 512, 768, 6, 3),      # several M-tiles per expert, odd stage count
-    (257, 768, 256, 40, 8),     # many small experts, some empty; 4-wave down
+    (257, 768, 256, 40, 8),     # many small experts, some empty; 8-wave down
     (500, 512, 512, 6, 1),      # k = 1: fused output
+    (200, 768, 512, 5, 1),      # k = 1 with the 8-wave down
 ])
 def test_mx_shapes(M, T, H, I, E, k):
     _check(M, _custom(T, H, I, E, k, seed=T + 1), f"mx shape T={T} H={H} I={I} E={E} k={k}")
