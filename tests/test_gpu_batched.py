@@ -77,6 +77,11 @@ def test_batched_kimi_full_size(M):
     _check(M, d, "kimi-bf16-T2048 (8 sampled tokens)", tokens=_sample(2048, 8, 0))
 
 
+def test_batched_glm_full_size(M):
+    d = W.make("glm-bf16-T2048", seed=0, device="cuda")
+    _check(M, d, "glm-bf16-T2048 (8 sampled tokens)", tokens=_sample(2048, 8, 4))
+
+
 def test_batched_kimi_ep64_share(M):
     d = W.make("kimi-bf16-ep64share", seed=0, device="cuda")
     _check(M, d, "kimi-bf16-ep64share (48 sampled tokens)", tokens=_sample(16384, 48, 1))

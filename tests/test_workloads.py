@@ -23,7 +23,9 @@ def test_shapes_follow_the_pages():
     assert (q35.E, q35.k) == (g["qwen35_397b_a17b"]["E"], g["qwen35_397b_a17b"]["k"])
     ds = W.get("dsv4-mxfp8-T2048")
     assert (ds.E, ds.I) == (g["deepseek_v4_pro"]["E"], g["deepseek_v4_pro"]["I"])
-    for c in (kimi, ds):
+    glm = W.get("glm-bf16-T2048")
+    assert (glm.E, glm.H) == (g["glm_52"]["E"], g["glm_52"]["H"])
+    for c in (kimi, ds, glm):
         assert c.T == g["tokens_per_gpu"]["value"]
     # one GPU's share under EP 64: all 2048*k received rows over E/64 local experts
     for share, full in (("kimi-bf16-ep64share", kimi), ("dsv4-mxfp8-ep64share", ds)):

@@ -80,6 +80,8 @@ CONFIGS: Dict[str, Config] = {c.name: c for c in [
        note="Kimi-K2.7-Code-shaped batched layer, all 384 experts resident"),
     _c(name="dsv4-mxfp8-T2048", T=2048, H=7168, E=384, k=8, I=3072, dtype="mxfp8",
        path="batched", note="DeepSeek-V4-Pro-shaped batched layer, MXFP8"),
+    _c(name="glm-bf16-T2048", T=2048, H=6144, E=256, k=8, I=2048, path="batched",
+       note="GLM-5.2-shaped batched layer (E and H from the pages; k = 8 and I = 2048 assumed)"),
     _c(name="kimi-bf16-ep64share", T=16384, H=7168, E=6, k=1, I=2048, path="batched",
        note="one GPU's share under expert parallelism 64 at 2048 tokens/GPU: "
             "16384 received rows over 384/64 = 6 local experts"),
