@@ -80,6 +80,8 @@ def _expert_matrix(w, e: int, dtype: str, scales=None) -> np.ndarray:
     ``w`` is either an array [E, R, K] or a callable e -> array [R, K] (lets a
     caller fetch only the experts it needs)."""
     we = w(e) if callable(w) else np.asarray(w[e])
+    if dtype == "f64":
+        return np.asarray(we, dtype=np.float64)
     if dtype == "bf16":
         return bf16_decode(we)
     se = scales(e) if callable(scales) else np.asarray(scales[e])
@@ -106,13 +108,16 @@ def moe_forward(x, logits, w_gate_up, w_down, k: int, dtype: str = "bf16",
                 (none, the default), "bf16" (round to nearest even), "mxfp8"
                 (E4M3 + E8M0 blocks of 32 along I, the MXFP8 mode's rule).  In
                 MXFP8 mode a is always MX-quantized and h_round must be "exact".
+    dtype "f64" takes x and the weights as float64 values (no decoding): the
+    real-valued layer, for derivative checks by finite differences.
     Returns out [n_tokens, H] float64, or (out, dict) with the routing, the
-    per-slot activations a [n, k, I] and expert outputs y [n, k, H]."""
-    if dtype not in ("bf16", "mxfp8"):
+    per-slot pre-activations gu [n, k, 2I] (gate then up), activations
+    a [n, k, I] and expert outputs y [n, k, H]."""
+    if dtype not in ("bf16", "mxfp8", "f64"):
         raise ValueError(dtype)
     if h_round not in ("exact", "bf16", "mxfp8") or (dtype == "mxfp8" and h_round != "exact"):
         raise ValueError(h_round)
-    x = np.asarray(x, dtype=np.uint16)
+    x = np.asarray(x, dtype=np.float64 if dtype == "f64" else np.uint16)
     logits = np.asarray(logits, dtype=np.float32)
     if tokens is not None:
         tokens = np.asarray(tokens, dtype=np.int64)
@@ -121,11 +126,12 @@ def moe_forward(x, logits, w_gate_up, w_down, k: int, dtype: str = "bf16",
     T, H = x.shape
     idx, w = route(logits, k)
 
-    xf = bf16_decode(x)
+    xf = x if dtype == "f64" else bf16_decode(x)
     if dtype == "mxfp8":
         xf = mx_dequantize(*mx_quantize(xf))
 
     a_all: Optional[np.ndarray] = None
+    gu_all: Optional[np.ndarray] = None
     y = np.zeros((T, k, H), dtype=np.float64)
     for e in np.unique(idx):
         rows, slots = np.nonzero(idx == e)           # every (t, j) routed to e
@@ -146,13 +152,16 @@ def moe_forward(x, logits, w_gate_up, w_down, k: int, dtype: str = "bf16",
         if return_intermediates:
             if a_all is None:
                 a_all = np.zeros((T, k, I), dtype=np.float64)
+                gu_all = np.zeros((T, k, 2 * I), dtype=np.float64)
             a_all[rows, slots] = a
+            gu_all[rows, slots, :I] = g
+            gu_all[rows, slots, I:] = u
 
     out = np.zeros((T, H), dtype=np.float64)
     for j in range(k):                               # combine in slot order
         out += w[:, j:j + 1] * y[:, j, :]
     if return_intermediates:
-        return out, {"idx": idx, "w": w, "a": a_all, "y": y}
+        return out, {"idx": idx, "w": w, "gu": gu_all, "a": a_all, "y": y}
     return out
 
 
