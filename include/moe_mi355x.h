@@ -174,6 +174,46 @@ int moe_down_3d_batched(const void* h, const uint8_t* h_scales,
 size_t moe_workspace_bytes(int T, int H, int I, int E, int k, int dtype);
 
 /*
+ * moe_backward_batched -- backward pass of the whole layer for a large batch,
+ * BF16 (Mixture-of-Kittens summary, "What is 2.37x measured against": the
+ * MoE layer's backward pass, measured beside its forward pass at 2,048 tokens
+ * per GPU).  The gradient is that of the exact layer for the scalar
+ * sum(dout * out), with the top-k selection held fixed: for each routed pair
+ * (t, j) -> e, with g, u = gate/up pre-activations of x[t], a = silu(g) * u,
+ * y = W_down[e] a and w = topk_w[t, j],
+ *   d_topk_w[t, j] = dout[t] . y
+ *   dg = w (W_down[e]^T dout[t]) * u * silu'(g),  du = w (W_down[e]^T dout[t]) * silu(g)
+ *   dx[t]          = sum over j of W_gate[e]^T dg + W_up[e]^T du
+ *   dw_down[e]     = sum over e's pairs of (w dout[t]) a^T
+ *   dw_gate_up[e]  = sum over e's pairs of [dg; du] x[t]^T
+ *   dlogits[t, m]  = w_m (d_topk_w[t, m's slot] - sum_j w_j d_topk_w[t, j]) for
+ *                    the k selected experts m (softmax renormalised over them),
+ *                    0 for every other expert.
+ * The gate/up pre-activations are recomputed from x (nothing is kept from the
+ * forward call).  All sums accumulate in FP32 in a fixed order; dx and both
+ * weight gradients are rounded once to BF16.
+ *
+ *   x [T, H], w_gate_up [E, 2I, H], w_down [E, H, I]  BF16, as for the forward
+ *   topk_idx, topk_w [T, k]   from moe_route_topk
+ *   dout       [T, H] BF16    gradient of the layer output
+ *   dx         [T, H] BF16 out
+ *   dw_gate_up [E, 2I, H] BF16 out (zero for experts no token routes to)
+ *   dw_down    [E, H, I] BF16 out (likewise)
+ *   d_topk_w   [T, k] FP32 out
+ *   dlogits    [T, E] FP32 out
+ *   workspace  >= moe_backward_workspace_bytes(T, H, I, E, k) bytes
+ * Limits: T >= 1, H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024.
+ */
+int moe_backward_batched(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
+                         const int32_t* topk_idx, const float* topk_w, const uint16_t* dout,
+                         int T, int H, int I, int E, int k,
+                         uint16_t* dx, uint16_t* dw_gate_up, uint16_t* dw_down,
+                         float* d_topk_w, float* dlogits,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+size_t moe_backward_workspace_bytes(int T, int H, int I, int E, int k);
+
+/*
  * Kernel timing hook for benchmarks and profilers (not on any page).
  * moe_profile_kernel(kernel, start, stop): from now on, the calling thread's
  * launches of `kernel` are bracketed by hipEventRecord(start) and
@@ -192,7 +232,12 @@ typedef enum {
   MOE_KERNEL_GEMM_GATE_UP = 6,
   MOE_KERNEL_GEMM_DOWN = 7,
   MOE_KERNEL_COMBINE = 8,
-  MOE_KERNEL_COUNT = 9
+  MOE_KERNEL_BWD_GATE_UP = 9,    /* backward: recomputed gate/up pre-activations */
+  MOE_KERNEL_BWD_DOWN = 10,      /* backward: W_down^T dout and the SwiGLU step  */
+  MOE_KERNEL_BWD_INPUT = 11,     /* backward: dx (and the slot sum)              */
+  MOE_KERNEL_BWD_WDOWN = 12,     /* backward: dw_down                            */
+  MOE_KERNEL_BWD_WGATE_UP = 13,  /* backward: dw_gate_up                         */
+  MOE_KERNEL_COUNT = 14
 } moe_kernel_id;
 
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event);

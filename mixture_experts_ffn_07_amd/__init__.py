@@ -21,7 +21,8 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN = 0, -1, -2, -3
 MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = -4, -5, -6
 MOE_BF16, MOE_MXFP8 = 0, 1
 KERNELS = {"none": 0, "route": 1, "decode_gate_up": 2, "decode_down": 3, "group": 4,
-           "quant": 5, "gemm_gate_up": 6, "gemm_down": 7, "combine": 8}
+           "quant": 5, "gemm_gate_up": 6, "gemm_down": 7, "combine": 8, "bwd_gate_up": 9,
+           "bwd_down": 10, "bwd_input": 11, "bwd_wdown": 12, "bwd_wgate_up": 13}
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -34,6 +35,9 @@ _SIGS = {
     "moe_gate_up_3d_batched": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "moe_down_3d_batched": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "moe_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "moe_backward_batched": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
+                                  _P, _SZ, _P]),
+    "moe_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_profile_kernel": (_I, [_I, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
@@ -185,6 +189,37 @@ def moe_down_3d_batched(h, w_down, topk_idx, topk_w, ws, k: int, dtype: int = MO
     return out
 
 
+def moe_backward_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(lib.moe_backward_workspace_bytes(T, H, I, E, k))
+
+
+def moe_backward_batched(x, w_gate_up, w_down, topk_idx, topk_w, dout, k: int, dx=None,
+                         dw_gate_up=None, dw_down=None, d_topk_w=None, dlogits=None, ws=None,
+                         stream=None):
+    """Backward pass of the layer (BF16); returns (dx, dw_gate_up, dw_down, d_topk_w, dlogits)."""
+    T, H = x.shape
+    E, I2, _ = w_gate_up.shape
+    I = I2 // 2
+    dev = x.device
+    if dx is None:
+        dx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    if dw_gate_up is None:
+        dw_gate_up = torch.empty(E, I2, H, dtype=torch.bfloat16, device=dev)
+    if dw_down is None:
+        dw_down = torch.empty(E, H, I, dtype=torch.bfloat16, device=dev)
+    if d_topk_w is None:
+        d_topk_w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    if dlogits is None:
+        dlogits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(moe_backward_workspace_bytes(T, H, I, E, k), dev)
+    _check("moe_backward_batched", lib.moe_backward_batched(
+        _ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(topk_idx), _ptr(topk_w), _ptr(dout),
+        T, H, I, E, k, _ptr(dx), _ptr(dw_gate_up), _ptr(dw_down), _ptr(d_topk_w), _ptr(dlogits),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return dx, dw_gate_up, dw_down, d_topk_w, dlogits
+
+
 def moe_profile_kernel(kernel, start_event: Optional[int], stop_event: Optional[int]) -> None:
     """Bracket the named kernel's launches with the given hipEvent_t handles."""
     kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
@@ -193,5 +228,6 @@ def moe_profile_kernel(kernel, start_event: Optional[int], stop_event: Optional[
 
 __all__ = ["lib", "LIB_PATH", "MoeError", "moe_route_topk", "moe_decode_forward",
            "moe_decode_workspace_bytes", "moe_workspace_bytes", "moe_quantize_mxfp8",
-           "moe_gate_up_3d_batched", "moe_down_3d_batched", "moe_profile_kernel", "workspace",
+           "moe_gate_up_3d_batched", "moe_down_3d_batched", "moe_backward_batched",
+           "moe_backward_workspace_bytes", "moe_profile_kernel", "workspace",
            "MOE_BF16", "MOE_MXFP8", "KERNELS"]

@@ -237,4 +237,41 @@ int moe_down_3d_batched(const void* h, const uint8_t* h_scales, const void* w_do
                     "moe_down_3d_batched launch");
 }
 
+size_t moe_backward_workspace_bytes(int T, int H, int I, int E, int k) {
+  if (T < 1 || H <= 0 || I <= 0 || E < 1 || k < 1) return 0;
+  return moe::backward_ws_layout(T, H, I, E, k).total;
+}
+
+int moe_backward_batched(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
+                         const int32_t* topk_idx, const float* topk_w, const uint16_t* dout, int T,
+                         int H, int I, int E, int k, uint16_t* dx, uint16_t* dw_gate_up,
+                         uint16_t* dw_down, float* d_topk_w, float* dlogits, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (int st = check_common(T, H, I, E, k, 256, 256)) return st;
+  if (T < 1) return fail(MOE_ERR_SHAPE, "T=%d < 1", T);
+  if (static_cast<long long>(T) * k > (1LL << 24))
+    return fail(MOE_ERR_SHAPE, "T*k=%lld > 2^24", static_cast<long long>(T) * k);
+  if (static_cast<long long>(T) * k * H >= (1LL << 31) ||
+      static_cast<long long>(T) * k * 2 * I >= (1LL << 31) ||
+      2LL * I * H >= (1LL << 31))
+    return fail(MOE_ERR_SHAPE, "T*k*H, T*k*2I or 2I*H reaches 2^31");
+  if (!x || !w_gate_up || !w_down || !topk_idx || !topk_w || !dout || !dx || !dw_gate_up ||
+      !dw_down || !d_topk_w || !dlogits)
+    return fail(MOE_ERR_NULL, "every input and output pointer is required");
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  const size_t need = moe::backward_ws_layout(T, H, I, E, k).total;
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(topk_idx) ||
+      !aligned16(topk_w) || !aligned16(dout) || !aligned16(dx) || !aligned16(dw_gate_up) ||
+      !aligned16(dw_down) || !aligned16(d_topk_w) || !aligned16(dlogits) || !aligned16(workspace))
+    return fail(MOE_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  return hip_status(moe::launch_backward(x, w_gate_up, w_down, topk_idx, topk_w, dout, T, H, I, E,
+                                         k, dx, dw_gate_up, dw_down, d_topk_w, dlogits, workspace,
+                                         static_cast<hipStream_t>(stream)),
+                    "moe_backward_batched launch");
+}
+
 }  // extern "C"

@@ -739,6 +739,15 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   return hipGetLastError();
 }
 
+hipError_t launch_group_experts(const int32_t* idx, int P, int E, int BM, int* counts, int* offsets,
+                                int2* tiles, int* n_tiles, int* perm, int* row_of, hipStream_t s) {
+  prof_begin(kGroup, s);
+  hipLaunchKernelGGL(group_experts, dim3(E), dim3(1024), 0, s, idx, P, E, BM, counts, offsets,
+                     tiles, n_tiles, perm, row_of);
+  prof_end(kGroup, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
                            uint8_t* scales, hipStream_t s) {
   const int64_t n_blocks = rows * (K / 32);

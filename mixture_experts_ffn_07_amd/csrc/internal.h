@@ -25,7 +25,8 @@ inline void prof_end(int id, hipStream_t s) {
   if (h.kernel == id && h.stop) (void)hipEventRecord(h.stop, s);
 }
 enum KernelId { kRoute = 1, kDecGateUp = 2, kDecDown = 3, kGroup = 4, kQuant = 5,
-                kGemmGateUp = 6, kGemmDown = 7, kCombine = 8, kKernelCount = 9 };
+                kGemmGateUp = 6, kGemmDown = 7, kCombine = 8, kBwdGateUp = 9, kBwdDown = 10,
+                kBwdInput = 11, kBwdWDown = 12, kBwdWGateUp = 13, kKernelCount = 14 };
 
 // Byte layout of the decode workspace.
 struct DecodeWs {
@@ -75,6 +76,22 @@ hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint
                                 const float* w, int H, int I, int k, float* y, uint16_t* out,
                                 float* partial, int max_tiles, int ncu, hipStream_t s);
 hipError_t large_set_attributes();
+
+// Stable expert grouping of the T*k routed pairs into M-tiles of BM rows
+// (batched.hip); used by the forward and the backward.
+hipError_t launch_group_experts(const int32_t* idx, int P, int E, int BM, int* counts, int* offsets,
+                                int2* tiles, int* n_tiles, int* perm, int* row_of, hipStream_t s);
+
+// Byte layout of the backward workspace (backward.hip).
+struct BackwardWs {
+  size_t counts, offsets, tiles, n_tiles, perm, row_of, gu, dgu, dwp, dxs, total;
+  int max_tiles;
+};
+BackwardWs backward_ws_layout(int T, int H, int I, int E, int k);
+hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_t* wd,
+                           const int32_t* idx, const float* w, const uint16_t* dout, int T, int H,
+                           int I, int E, int k, uint16_t* dx, uint16_t* dwgu, uint16_t* dwd,
+                           float* dtw, float* dlogits, void* ws, hipStream_t s);
 
 hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
                            uint8_t* scales, hipStream_t s);

@@ -130,3 +130,28 @@ def test_profile_hook_validation(m):
     assert m.lib.moe_profile_kernel(99, None, None) == m.MOE_ERR_SHAPE
     assert m.lib.moe_profile_kernel(2, None, None) == m.MOE_OK
     assert m.lib.moe_profile_kernel(0, None, None) == m.MOE_OK
+
+
+def test_backward_validation(m):
+    b = m.lib.moe_backward_batched
+    need = m.lib.moe_backward_workspace_bytes(64, 256, 256, 8, 2)
+    assert need > 0
+    assert m.lib.moe_backward_workspace_bytes(0, 256, 256, 8, 2) == 0
+
+    def call(x=FAKE, dout=FAKE, dx=FAKE, dwgu=FAKE, ws=FAKE, wsb=need, T=64, H=256, I=256, E=8,
+             k=2):
+        return b(x, FAKE, FAKE, FAKE, FAKE, dout, T, H, I, E, k, dx, dwgu, FAKE, FAKE, FAKE, ws,
+                 wsb, None)
+    assert call(x=None) == m.MOE_ERR_NULL
+    assert call(dout=None) == m.MOE_ERR_NULL
+    assert call(dwgu=None) == m.MOE_ERR_NULL
+    assert call(H=384) == m.MOE_ERR_SHAPE
+    assert call(I=128) == m.MOE_ERR_SHAPE
+    assert call(T=0) == m.MOE_ERR_SHAPE
+    assert call(k=9) == m.MOE_ERR_SHAPE
+    assert call(ws=None) == m.MOE_ERR_WORKSPACE
+    assert call(wsb=need - 1) == m.MOE_ERR_WORKSPACE
+    assert call(dx=FAKE + 2) == m.MOE_ERR_ALIGN
+    # the workspace holds the recomputed FP32 pre-activations and the BF16 gradients
+    # of [g; u] for every routed pair
+    assert need >= 64 * 2 * 2 * 256 * (4 + 2)

@@ -90,7 +90,7 @@ CONFIGS: Dict[str, Config] = {c.name: c for c in [
 ]}
 
 # stream tags: each tensor kind draws from its own stream
-_TAG = {"x": 1, "logits": 2, "zipf": 3, "w_gate_up": 4, "w_down": 5}
+_TAG = {"x": 1, "logits": 2, "zipf": 3, "w_gate_up": 4, "w_down": 5, "dout": 6}
 
 
 def get(name: str) -> Config:
@@ -173,6 +173,12 @@ def make_activations(cfg: Config, seed: int = 0, device="cpu") -> Dict[str, torc
         bias = (-cfg.zipf_s * torch.log(rank)).to(torch.float32).to(device)
         logits = logits + bias
     return {"x": x.contiguous(), "logits": logits.contiguous()}
+
+
+def make_output_grad(cfg: Config, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Gradient of the layer output for the backward pass: dout [T, H] BF16,
+    N(0, 1) (the scale of a loss gradient does not change relative errors)."""
+    return _normal((cfg.T, cfg.H), 1.0, device, seed, "dout").to(torch.bfloat16).contiguous()
 
 
 def make(name_or_cfg, seed: int = 0, device="cpu", T: Optional[int] = None) -> Dict[str, object]:
