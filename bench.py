@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the routed MoE FFN layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1] [--pass backward]
 
 One step = one full pass of the layer (routing, gate/up + SwiGLU, down +
 weighted combine) over one batch of synthetic tokens.  Default workload: the
@@ -11,6 +11,10 @@ Decode steps cycle through `--layers` independent weight sets (like the
 layers of a model), so each step streams weights that the previous steps did
 not leave in the 256 MB last-level cache, and every step routes a fresh batch
 of tokens.  All inputs are resident in HBM before the timed region starts.
+
+With --pass backward (batched BF16 workloads) a step is routing plus the
+layer's backward pass instead (dx, both weight gradients, the routing-weight
+and logit gradients for a seeded output gradient).
 
 Prints ONE JSON line.  Besides the throughput it carries
   roofline:     the dominant kernel's algorithmic HBM bytes per launch divided
@@ -42,14 +46,17 @@ CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 # as null until the counters are taken again.
 TRAFFIC = {
     ("decode_gate_up", "qwen3-decode-T32"): (
-        705.8e6, ('decode.hip', 'common.h', 'internal.h'), "927c44f2d9a4493f",
+        705.8e6, ('decode.hip', 'common.h', 'internal.h'), "edd61e3d43a019b8",
         "profiles/decode_gate_up_qwen3-decode-T32.md"),
     ("gemm_gate_up", "kimi-bf16-T2048"): (
-        22998.9e6, ('batched.hip', 'common.h', 'tiles.h'), "4056ba65bb7cf8e8",
+        22998.9e6, ('batched.hip', 'common.h', 'tiles.h'), "aaa3c811e47a61e4",
         "profiles/gemm_gate_up_kimi-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
         2576.2e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "70d9b3c6a25bfac1",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
+    ("bwd_wgate_up", "kimi-bf16-T2048"): (
+        23708.6e6, ('backward.hip', 'common.h', 'tiles.h'), "933da455364ed6ec",
+        "profiles/bwd_wgate_up_kimi-bf16-T2048.md"),
 }
 
 
@@ -85,6 +92,10 @@ def parse():
                    help="approximate CPU time for the oracle baseline (0 = skip)")
     p.add_argument("--extra", action="store_true",
                    help="also time decode at T=1 and T=8 (reported under 'extra')")
+    p.add_argument("--pass", dest="pass_", choices=("forward", "backward"), default="forward",
+                   help="backward: time the layer's backward pass (batched BF16 workloads)")
+    p.add_argument("--calibrate-fill-mib", type=int, default=0,
+                   help="only time a plain device fill of this many MiB (HBM write rate)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB three times (the "
                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -237,6 +248,83 @@ def run_batched(M, W, torch, cfg, steps, warmup, seed, n_batches=4):
     }
 
 
+BWD_KERNELS = ("bwd_gate_up", "bwd_down", "bwd_input", "bwd_wdown", "bwd_wgate_up")
+
+
+def backward_algorithmic(cfg, U):
+    """Bytes each backward kernel must at least move, and its MFMA flops."""
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    P = T * k
+    wgu, wd = U * 2 * I * H * 2, U * H * I * 2
+    slots = (P * H * 4 * 2 + T * H * 2) if k > 1 else T * H * 2
+    return {
+        "bwd_gate_up": (wgu + T * H * 2 + P * 2 * I * 4, 2.0 * P * 2 * I * H),
+        "bwd_down": (wd + T * H * 2 + P * 2 * I * 4 + P * 2 * I * 2, 2.0 * P * H * I),
+        "bwd_input": (wgu + P * 2 * I * 2 + slots, 2.0 * P * 2 * I * H),
+        "bwd_wdown": (T * H * 2 + P * 2 * I * 4 + E * H * I * 2, 2.0 * P * H * I),
+        "bwd_wgate_up": (P * 2 * I * 2 + T * H * 2 + E * 2 * I * H * 2, 2.0 * P * 2 * I * H),
+    }
+
+
+def run_backward(M, W, torch, cfg, steps, warmup, seed, n_batches=2):
+    """One step = routing + the whole backward pass of one batch.  The timed
+    steps bracket the five backward kernels in turn with HIP events."""
+    from mixture_experts_ffn_07_amd.hip_events import HipEvent
+    dev = "cuda"
+    log(f"generating weights of {cfg.name} ({W.expert_bytes(cfg) * cfg.E / 1e9:.1f} GB)")
+    wts = W.make_weights(cfg, seed=seed, device=dev)
+    acts = [W.make_activations(cfg, seed=seed + 7919 * (b + 1), device=dev) for b in range(n_batches)]
+    douts = [W.make_output_grad(cfg, seed=seed + 104729 * (b + 1), device=dev)
+             for b in range(n_batches)]
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    stream = torch.cuda.current_stream()
+    ws = M.workspace(M.moe_backward_workspace_bytes(T, H, I, E, k), dev)
+    idx = torch.empty(n_batches, T, k, dtype=torch.int32, device=dev)
+    tw = torch.empty(n_batches, T, k, dtype=torch.float32, device=dev)
+    dx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    dwgu = torch.empty(E, 2 * I, H, dtype=torch.bfloat16, device=dev)
+    dwd = torch.empty(E, H, I, dtype=torch.bfloat16, device=dev)
+    dtw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    dl = torch.empty(T, E, dtype=torch.float32, device=dev)
+
+    def step(i):
+        b = i % n_batches
+        a = acts[b]
+        M.moe_route_topk(a["logits"], k, topk_idx=idx[b], topk_w=tw[b], stream=stream)
+        M.moe_backward_batched(a["x"], wts["w_gate_up"], wts["w_down"], idx[b], tw[b], douts[b],
+                               k, dx=dx, dw_gate_up=dwgu, dw_down=dwd, d_topk_w=dtw, dlogits=dl,
+                               ws=ws, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        M.moe_profile_kernel(BWD_KERNELS[s % len(BWD_KERNELS)], evs[s][0].handle, evs[s][1].handle)
+        step(warmup + s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    M.moe_profile_kernel("none", None, None)
+    U = [int(torch.unique(idx[(warmup + s) % n_batches]).numel()) for s in range(steps)]
+    per = {}
+    for q, name in enumerate(BWD_KERNELS):
+        ss = [s for s in range(steps) if s % len(BWD_KERNELS) == q]
+        if not ss:
+            continue
+        dur = sum(evs[s][0].elapsed_ms(evs[s][1]) for s in ss) * 1e-3
+        nbytes = sum(backward_algorithmic(cfg, U[s])[name][0] for s in ss)
+        flops = sum(backward_algorithmic(cfg, U[s])[name][1] for s in ss)
+        per[name] = {"avg_us": 1e6 * dur / len(ss), "gbs": nbytes / dur / 1e9,
+                     "tflops": flops / dur / 1e12, "bytes_per_launch": nbytes / len(ss)}
+    elapsed = t1 - t0
+    tot_bytes = sum(sum(v[0] for v in backward_algorithmic(cfg, u).values()) for u in U)
+    return {"elapsed_s": elapsed, "ms_per_step": 1e3 * elapsed / steps,
+            "tokens_per_s": T * steps / elapsed, "per_kernel": per,
+            "layer_gbs": tot_bytes / elapsed / 1e9, "avg_touched_experts": sum(U) / steps}
+
+
 def cpu_baseline(W, cfg, act, weights, seconds):
     """Time the FP64 oracle on this host (bounded sample of the same workload)."""
     import numpy as np
@@ -290,8 +378,54 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
         return
+    if args.calibrate_fill_mib:
+        n = args.calibrate_fill_mib << 20
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst.fill_(1)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dst.fill_(0)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        print(json.dumps({"fill_bytes": n, "best_gbs": round(n / min(ts) / 1e9, 1),
+                          "median_gbs": round(n / sorted(ts)[2] / 1e9, 1)}), flush=True)
+        return
     cfg = W.get(args.workload)
     log(f"device {torch.cuda.get_device_name(0)}; workload {cfg.name}")
+    if args.pass_ == "backward":
+        if cfg.path != "batched" or cfg.dtype != "bf16":
+            print(f"--pass backward needs a batched BF16 workload, not {cfg.name}", file=sys.stderr)
+            sys.exit(2)
+        r = run_backward(M, W, torch, cfg, args.steps, args.warmup, args.seed)
+        name, k = max(r["per_kernel"].items(), key=lambda kv: kv[1]["avg_us"])
+        traffic, tprof = traffic_for(name, cfg.name)
+        roof = {"bound": "hbm", "kernel": name, "achieved": round(k["gbs"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k["gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": tprof,
+                "avg_launch_us": round(k["avg_us"], 2),
+                "algorithmic_bytes_per_launch": int(k["bytes_per_launch"])}
+        line = {
+            "metric": "MoE layer backward tokens/s", "value": round(r["tokens_per_s"], 1),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": cfg.name + " backward", "T": cfg.T, "H": cfg.H, "E": cfg.E,
+                       "k": cfg.k, "I": cfg.I, "parallelism": "none (1 GPU)"},
+            "roofline": roof,
+            "kernels": {n: {"avg_us": round(v["avg_us"], 1), "gbs": round(v["gbs"], 1),
+                            "tflops": round(v["tflops"], 1)} for n, v in r["per_kernel"].items()},
+            "layer": {"hbm_gbs": round(r["layer_gbs"], 1),
+                      "hbm_frac": round(r["layer_gbs"] / HBM_PEAK_GBS, 4),
+                      "avg_touched_experts": round(r["avg_touched_experts"], 2),
+                      "latency_us": round(1e3 * r["ms_per_step"], 2)},
+            "cpu_baseline": None,
+        }
+        print(json.dumps(line), flush=True)
+        return
     if cfg.path == "decode":
         r = run_decode(M, W, torch, cfg, args.steps, args.warmup, args.layers, args.seed)
         traffic, tprof = traffic_for("decode_gate_up", cfg.name)

@@ -17,20 +17,24 @@
 //   group_experts   the forward's grouping (64-row M-tiles, stable order)
 //   kGU   gu[row]  = [W_gate; W_up][e] x[t]                FP32, recomputed (not stored
 //                   by the forward)
-//   kDD   dh tile  = W_down[e]^T dout[t]; epilogue: dgu[row] = [dg; du] (BF16) and
-//                   one partial dot a . dh per 128 columns
+//   kDD   dh tile  = W_down[e]^T dout[t]; epilogue: dgu[row] = [dg; du] (BF16), the
+//                   weighted activation wa[row] = w a (BF16) and one partial dot
+//                   a . dh per 128 columns
 //   kDG   dxs[row] = W_gate_up[e]^T dgu[row]               FP32 per pair (k = 1: dx)
 //   sum_pairs       dx[t] = sum_j dxs[row of (t, j)] in slot order, rounded once
-//   kWD   dW_down[e]    = sum over the expert's rows of (w dout[t]) a^T     -> BF16
+//   kWD   dW_down[e]    = sum over the expert's rows of dout[t] (w a)^T     -> BF16
 //   kWG   dW_gate_up[e] = sum over the expert's rows of [dg; du] x[t]^T     -> BF16
 //   route_bwd       d_topk_w = the partial dots summed in column order; dlogits
 //
 // Every sum runs in a fixed order (MFMA K order, rows ascending within an
 // expert, slots ascending), so repeated runs are bit-identical.
 //
-// The GEMMs share one LDS-tiled kernel: a workgroup of 4 waves computes an
-// MT x 128 tile (MT = 64 routed rows for the three activation-gradient kinds,
-// 128 for the weight gradients) in K chunks of 64, double-buffered in LDS.
+// The three activation-gradient GEMMs share one LDS-tiled kernel (bwd_gemm):
+// a workgroup of 4 waves computes a 64-row x 128-column tile in K chunks of
+// 64, double-buffered in LDS.  The two weight gradients (bwd_wgrad) reduce
+// over an expert's routed rows: a workgroup keeps one 128-column block of its
+// n-side operand in LDS and walks 8 blocks of 128 output rows, prefetching the
+// next block's operand while the current one multiplies and stores.
 // Operands whose reduction index is the contiguous one ("rows": x, dout, dgu
 // rows, W_gate_up rows) are copied 16 bytes at a time; the others ("cols":
 // W_down and W_gate_up read along their output dimension, and every operand
@@ -53,7 +57,7 @@ constexpr int kBB = 64;          // routed rows per M-tile
 constexpr int kKC = 64;          // K chunk (elements)
 constexpr int kNT = 128;         // output columns per workgroup
 constexpr int kCS32 = kNT + 4;   // FP32 C-tile row stride (elements)
-constexpr int kCS16 = kNT + 8;   // BF16 C-tile row stride (elements)
+constexpr int kMB = 8;           // 128-row output blocks per weight-gradient workgroup
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -70,6 +74,7 @@ struct BwdArgs {
   const int* offsets;       // first grouped row per expert
   float* gu;                // [P, 2I] grouped rows
   uint16_t* dgu;            // [P, 2I] grouped rows
+  uint16_t* wa;             // [P, I] grouped rows: w * silu(g) * u
   float* dwp;               // [P, I/128] partial dots
   float* dxs;               // [P, H] grouped rows (k > 1)
   uint16_t* dx;             // [T, H]
@@ -93,39 +98,9 @@ __device__ __forceinline__ void pack_pairs(const i32x4& v0, const i32x4& v1, uin
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
-// BF16 x8 (16 bytes) times a scalar, rounded back to BF16.
-__device__ __forceinline__ i32x4 scale_bf16x8(i32x4 v, float s) {
-  i32x4 r;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t a = static_cast<uint32_t>(v[d]);
-    const uint32_t lo = f32_to_bf16_rne(s * bf16_to_f32(a & 0xFFFFu));
-    const uint32_t hi = f32_to_bf16_rne(s * bf16_to_f32(a >> 16));
-    r[d] = static_cast<int>(lo | (hi << 16));
-  }
-  return r;
-}
-
-// silu(g) * u of 8 FP32 pairs, rounded to BF16 (16 bytes).
-__device__ __forceinline__ i32x4 swiglu_bf16x8(const f32x4& g0, const f32x4& g1, const f32x4& u0,
-                                               const f32x4& u1) {
-  i32x4 r;
-#pragma unroll
-  for (int d = 0; d < 2; ++d) {
-    const uint32_t lo = f32_to_bf16_rne(swiglu(g0[2 * d], u0[2 * d]));
-    const uint32_t hi = f32_to_bf16_rne(swiglu(g0[2 * d + 1], u0[2 * d + 1]));
-    r[d] = static_cast<int>(lo | (hi << 16));
-    const uint32_t lo1 = f32_to_bf16_rne(swiglu(g1[2 * d], u1[2 * d]));
-    const uint32_t hi1 = f32_to_bf16_rne(swiglu(g1[2 * d + 1], u1[2 * d + 1]));
-    r[2 + d] = static_cast<int>(lo1 | (hi1 << 16));
-  }
-  return r;
-}
-
-template <int KIND>
+template <int KIND>   // kGU, kDD, kDG
 __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
-  constexpr bool WGRAD = KIND == kWD || KIND == kWG;
-  constexpr int MT = WGRAD ? 128 : kBB;
+  constexpr int MT = kBB;
   constexpr int MI = MT / 32;                         // 16-row A blocks per wave
   constexpr int AROW_U = MT * 8 / 256;                // "rows" A units per thread
   constexpr int BROW_U = kNT * 8 / 256;               // "rows" B units per thread (kGU)
@@ -137,51 +112,31 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, I = a.I, k = a.k;
 
-  // ---- work item ----
-  int e, n0, m0 = 0, mcount = 0, rbase = 0, nchunks;
-  if constexpr (!WGRAD) {
-    const int N = KIND == kGU ? 2 * I : (KIND == kDD ? I : H);
-    const int nblk = N / kNT;
-    const int item = real_item(blockIdx.x, nblk, *a.n_tiles);
-    if (item < 0) return;
-    const int tile = item / nblk;
-    n0 = (item - tile * nblk) * kNT;
-    const int2 te = a.tiles[tile];
-    e = te.x;
-    mcount = min(kBB, a.counts[e] - te.y);
-    rbase = a.offsets[e] + te.y;
-    nchunks = (KIND == kDG ? 2 * I : H) / kKC;
-  } else {
-    const int M = KIND == kWD ? H : 2 * I;
-    const int N = KIND == kWD ? I : H;
-    const int mb = M / MT, nb = N / kNT;
-    const int n_items = a.E * mb * nb;
-    const int item = xcd_item(blockIdx.x, gridDim.x);
-    if (item >= n_items) return;
-    e = item / (mb * nb);
-    const int rem = item - e * (mb * nb);
-    m0 = (rem / nb) * MT;
-    n0 = (rem % nb) * kNT;
-    rbase = a.offsets[e];
-    mcount = a.counts[e];                            // the expert's rows = the K range
-    nchunks = (mcount + kKC - 1) / kKC;
-  }
+  // ---- work item: (M-tile of 64 routed rows, 128 output columns) ----
+  const int N = KIND == kGU ? 2 * I : (KIND == kDD ? I : H);
+  const int nblk = N / kNT;
+  const int item = real_item(blockIdx.x, nblk, *a.n_tiles);
+  if (item < 0) return;
+  const int tile = item / nblk;
+  const int n0 = (item - tile * nblk) * kNT;
+  const int2 te = a.tiles[tile];
+  const int e = te.x;
+  const int mcount = min(kBB, a.counts[e] - te.y);
+  const int rbase = a.offsets[e] + te.y;
+  const int nchunks = (KIND == kDG ? 2 * I : H) / kKC;
 
   // ---- operand sources ----
   // "rows" A (kGU, kDD, kDG): unit u -> (row r = u / 8, chunk u % 8); rows past the
   // tile's end read its first row (their results are never stored)
-  const uint16_t* abase = nullptr;
-  uint32_t aoff[AROW_U > 0 ? AROW_U : 1] = {};
-  if constexpr (!WGRAD) {
-    abase = KIND == kGU ? a.x : (KIND == kDD ? a.dout : a.dgu);
+  const uint16_t* const abase = KIND == kGU ? a.x : (KIND == kDD ? a.dout : a.dgu);
+  uint32_t aoff[AROW_U];
 #pragma unroll
-    for (int i = 0; i < AROW_U; ++i) {
-      const int u = tid + 256 * i, r = u >> 3, c = u & 7;
-      const int rr = r < mcount ? r : 0;
-      const uint32_t row = KIND == kDG ? static_cast<uint32_t>(rbase + rr) * (2 * I)
-                                       : static_cast<uint32_t>(a.perm[rbase + rr] / k) * H;
-      aoff[i] = row + 8 * c;
-    }
+  for (int i = 0; i < AROW_U; ++i) {
+    const int u = tid + 256 * i, r = u >> 3, c = u & 7;
+    const int rr = r < mcount ? r : 0;
+    const uint32_t row = KIND == kDG ? static_cast<uint32_t>(rbase + rr) * (2 * I)
+                                     : static_cast<uint32_t>(a.perm[rbase + rr] / k) * H;
+    aoff[i] = row + 8 * c;
   }
   // "rows" B (kGU): W_gate_up[e] rows n0 .. n0+127
   const uint16_t* bbase = nullptr;
@@ -208,52 +163,21 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
   }
 
   // ---- staging registers and their LDS placement ----
-  i32x4 ra[WGRAD ? 4 : AROW_U];                      // A: rows units, or 2 cols units x 2 K rows
+  i32x4 ra[AROW_U];
   i32x4 rb[4];                                        // B: 4 rows units, or 2 cols units x 2 K rows
-  f32x4 rg[KIND == kWD ? 16 : 1];                     // kWD B: g and u of 2 units x 2 rows (FP32)
-  float rsc[WGRAD ? 4 : 1];                           // kWD A: routing weight per K row
-  bool rv[WGRAD ? 4 : 1];                             // K row inside the expert
 
   auto load_chunk = [&](int ch) {
-    if constexpr (!WGRAD) {
 #pragma unroll
-      for (int i = 0; i < AROW_U; ++i) ra[i] = ld16(abase + aoff[i] + ch * kKC);
-      if constexpr (KIND == kGU) {
+    for (int i = 0; i < AROW_U; ++i) ra[i] = ld16(abase + aoff[i] + ch * kKC);
+    if constexpr (KIND == kGU) {
 #pragma unroll
-        for (int i = 0; i < BROW_U; ++i) rb[i] = ld16_stream(bbase + boff[i] + ch * kKC);
-      } else {
-        const uint32_t kof = static_cast<uint32_t>(ch * kKC) * bld;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          rb[2 * i] = ld16_stream(bbase + boff[i] + kof);
-          rb[2 * i + 1] = ld16_stream(bbase + boff[i] + kof + bld);
-        }
-      }
+      for (int i = 0; i < BROW_U; ++i) rb[i] = ld16_stream(bbase + boff[i] + ch * kKC);
     } else {
-      // K rows are the expert's grouped rows rbase + ch*64 + 2p (+1); rows past
-      // the expert's end are loaded from its last row and zeroed when packed
+      const uint32_t kof = static_cast<uint32_t>(ch * kKC) * bld;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int u = tid + 256 * i, q = u & 15, p = u >> 4;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kr = ch * kKC + 2 * p + h;
-          const int row = rbase + (kr < mcount ? kr : mcount - 1);
-          rv[2 * i + h] = kr < mcount;
-          if constexpr (KIND == kWD) {
-            const int pair = a.perm[row];
-            rsc[2 * i + h] = a.w[pair];
-            ra[2 * i + h] = ld16(a.dout + static_cast<size_t>(pair / k) * H + m0 + 8 * q);
-            const float* gp = a.gu + static_cast<size_t>(row) * (2 * I) + n0 + 8 * q;
-            rg[8 * i + 4 * h + 0] = *reinterpret_cast<const f32x4*>(gp);
-            rg[8 * i + 4 * h + 1] = *reinterpret_cast<const f32x4*>(gp + 4);
-            rg[8 * i + 4 * h + 2] = *reinterpret_cast<const f32x4*>(gp + I);
-            rg[8 * i + 4 * h + 3] = *reinterpret_cast<const f32x4*>(gp + I + 4);
-          } else {
-            ra[2 * i + h] = ld16(a.dgu + static_cast<size_t>(row) * (2 * I) + m0 + 8 * q);
-            rb[2 * i + h] = ld16(a.x + static_cast<size_t>(a.perm[row] / k) * H + n0 + 8 * q);
-          }
-        }
+        rb[2 * i] = ld16_stream(bbase + boff[i] + kof);
+        rb[2 * i + 1] = ld16_stream(bbase + boff[i] + kof + bld);
       }
     }
   };
@@ -261,12 +185,10 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
   auto store_chunk = [&](int buf) {
     uint16_t* ab = As + buf * MT * kKC;
     uint16_t* bb = Bs + buf * kNT * kKC;
-    if constexpr (!WGRAD) {
 #pragma unroll
-      for (int i = 0; i < AROW_U; ++i) {
-        const int u = tid + 256 * i;
-        *reinterpret_cast<i32x4*>(ab + swz(u >> 3, u & 7)) = ra[i];
-      }
+    for (int i = 0; i < AROW_U; ++i) {
+      const int u = tid + 256 * i;
+      *reinterpret_cast<i32x4*>(ab + swz(u >> 3, u & 7)) = ra[i];
     }
     if constexpr (KIND == kGU) {
 #pragma unroll
@@ -275,38 +197,16 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
         *reinterpret_cast<i32x4*>(bb + swz(u >> 3, u & 7)) = rb[i];
       }
     } else {
-      // "cols" B (and A for the weight gradients): unit (p, q) holds K rows 2p, 2p+1
-      // of columns 8q .. 8q+7; column 8q+j becomes LDS row 8q+j
+      // "cols" B: unit (p, q) holds K rows 2p, 2p+1 of columns 8q .. 8q+7;
+      // column 8q+j becomes LDS row 8q+j
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int u = tid + 256 * i, q = u & 15, p = u >> 4;
-        const int co = (2 * p) & 7, ch = p >> 2;
-        uint32_t wb_[8], wa_[8];
-        if constexpr (WGRAD) {
-          // K rows past the expert's end contribute zero on both sides
-          const i32x4 zero = {0, 0, 0, 0};
-          i32x4 a0 = ra[2 * i], a1 = ra[2 * i + 1], b0, b1;
-          if constexpr (KIND == kWD) {
-            a0 = scale_bf16x8(a0, rsc[2 * i]);
-            a1 = scale_bf16x8(a1, rsc[2 * i + 1]);
-            b0 = swiglu_bf16x8(rg[8 * i + 0], rg[8 * i + 1], rg[8 * i + 2], rg[8 * i + 3]);
-            b1 = swiglu_bf16x8(rg[8 * i + 4], rg[8 * i + 5], rg[8 * i + 6], rg[8 * i + 7]);
-          } else {
-            b0 = rb[2 * i];
-            b1 = rb[2 * i + 1];
-          }
-          if (!rv[2 * i]) a0 = b0 = zero;
-          if (!rv[2 * i + 1]) a1 = b1 = zero;
-          pack_pairs(a0, a1, wa_);
-          pack_pairs(b0, b1, wb_);
-        } else {
-          pack_pairs(rb[2 * i], rb[2 * i + 1], wb_);
-        }
+        uint32_t wb_[8];
+        pack_pairs(rb[2 * i], rb[2 * i + 1], wb_);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          *reinterpret_cast<uint32_t*>(bb + swz(8 * q + j, ch) + co) = wb_[j];
-          if constexpr (WGRAD) *reinterpret_cast<uint32_t*>(ab + swz(8 * q + j, ch) + co) = wa_[j];
-        }
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint32_t*>(bb + swz(8 * q + j, p >> 2) + ((2 * p) & 7)) = wb_[j];
       }
     }
   };
@@ -320,10 +220,8 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nchunks > 0) {
-    load_chunk(0);
-    store_chunk(0);
-  }
+  load_chunk(0);
+  store_chunk(0);
   __syncthreads();
   for (int ch = 0; ch < nchunks; ++ch) {
     const int buf = ch & 1;
@@ -354,7 +252,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
 
   // ---- C tile through LDS (the operand buffers are free after the last barrier) ----
   // lane: tile row wm*MT/2 + 16i + fr, columns wn*64 + 16j + 4fg .. +3
-  if constexpr (!WGRAD) {
+  {
     float* Cs = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -362,18 +260,6 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
       for (int j = 0; j < 4; ++j)
         *reinterpret_cast<f32x4*>(Cs + (wm * (MT / 2) + 16 * i + fr) * kCS32 + wn * 64 + 16 * j + 4 * fg) =
             acc[i][j];
-  } else {
-    uint16_t* Cs = lds;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 v = acc[i][j];
-        uint2 p;
-        p.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-        p.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-        *reinterpret_cast<uint2*>(Cs + (wm * (MT / 2) + 16 * i + fr) * kCS16 + wn * 64 + 16 * j + 4 * fg) = p;
-      }
   }
   __syncthreads();
 
@@ -381,14 +267,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
   const int sg = tid & 15;
 #pragma unroll 1
   for (int r = tid >> 4; r < MT; r += 16) {
-    if constexpr (WGRAD) {
-      const uint16_t* Cs = lds;
-      const i32x4 v = *reinterpret_cast<const i32x4*>(Cs + r * kCS16 + 8 * sg);
-      uint16_t* dst = KIND == kWD
-                          ? a.dwd + (static_cast<size_t>(e) * H + m0 + r) * I + n0 + 8 * sg
-                          : a.dwgu + (static_cast<size_t>(e) * 2 * I + m0 + r) * H + n0 + 8 * sg;
-      st16(dst, v);
-    } else {
+    {
       const float* Cs = reinterpret_cast<const float*>(lds);
       const f32x4 c0 = *reinterpret_cast<const f32x4*>(Cs + r * kCS32 + 8 * sg);
       const f32x4 c1 = *reinterpret_cast<const f32x4*>(Cs + r * kCS32 + 8 * sg + 4);
@@ -410,7 +289,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
         const f32x4 u0 = *reinterpret_cast<const f32x4*>(gp + I);
         const f32x4 u1 = *reinterpret_cast<const f32x4*>(gp + I + 4);
         float part = 0.0f;
-        uint32_t pg[4], pu[4];
+        uint32_t pg[4], pu[4], pa[4];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const float g = q < 4 ? g0[q] : g1[q - 4];
@@ -422,12 +301,15 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
           const float da = wt * dh;
           const uint32_t bg = f32_to_bf16_rne(da * u * (sg_ * (1.0f + g * (1.0f - sg_))));
           const uint32_t bu = f32_to_bf16_rne(da * si);
+          const uint32_t ba = f32_to_bf16_rne(wt * (si * u));
           if (q & 1) {
             pg[q >> 1] |= bg << 16;
             pu[q >> 1] |= bu << 16;
+            pa[q >> 1] |= ba << 16;
           } else {
             pg[q >> 1] = bg;
             pu[q >> 1] = bu;
+            pa[q >> 1] = ba;
           }
         }
         // partial dot over the 128 columns: the 16 lanes of this row, fixed butterfly
@@ -439,6 +321,9 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
                           static_cast<int>(pg[3])});
           st16(dst + I, i32x4{static_cast<int>(pu[0]), static_cast<int>(pu[1]),
                               static_cast<int>(pu[2]), static_cast<int>(pu[3])});
+          st16(a.wa + grow * I + n0 + 8 * sg,
+               i32x4{static_cast<int>(pa[0]), static_cast<int>(pa[1]), static_cast<int>(pa[2]),
+                     static_cast<int>(pa[3])});
           if (sg == 0) a.dwp[grow * (I / kNT) + n0 / kNT] = part;
         }
       } else {   // kDG
@@ -458,6 +343,177 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
           }
         }
       }
+    }
+  }
+}
+
+// Weight gradients, reduced over an expert's grouped rows r (K, in chunks of
+// 64; rows past the expert's end count as zero):
+//   kWD: dW_down[e][h][i]    = sum_r dout[t_r][h] * wa[r][i]   (A = dout rows
+//        gathered through perm, output rows h; B = wa rows, output columns i)
+//   kWG: dW_gate_up[e][c][h] = sum_r dgu[r][c] * x[t_r][h]     (A = dgu rows,
+//        output rows c; B = x rows gathered through perm, output columns h)
+// Workgroup = (expert, 128 output columns, kMB blocks of 128 output rows).
+// With one chunk (at most 64 rows: the common case at 40-60 routed rows per
+// expert) the B tile is staged once and stays in LDS for every row block;
+// each row block's A tile is loaded while the previous block multiplies, and
+// the finished block is written straight from the accumulators (4 BF16 per
+// lane, a full 128-byte line per row across a wave's four stores).
+template <int KIND>   // kWD, kWG (at most 256 registers: two workgroups per CU)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_wgrad(
+    BwdArgs a) {
+  __shared__ __align__(16) uint16_t lds[4 * 128 * kKC];
+  uint16_t* const As = lds;                           // [2][128 rows][64 K]
+  uint16_t* const Bs = lds + 2 * 128 * kKC;           // [2][128 columns][64 K]
+  const int tid = threadIdx.x, ln = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.H, I = a.I, k = a.k;
+  const int M = KIND == kWD ? H : 2 * I, N = KIND == kWD ? I : H;
+  const int mb = M / 128, nb = N / kNT, mgs = (mb + kMB - 1) / kMB;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
+  if (item >= a.E * nb * mgs) return;
+  const int e = item / (nb * mgs);
+  const int rem = item - e * (nb * mgs);
+  const int n0 = (rem / mgs) * kNT;
+  const int mfirst = (rem % mgs) * kMB, mend = min(mb, mfirst + kMB);
+  const int cnt = a.counts[e], rbase = a.offsets[e];
+  const int nchunks = (cnt + kKC - 1) / kKC;
+  const bool bres = nchunks == 1;
+  uint16_t* const out = KIND == kWD ? a.dwd + static_cast<size_t>(e) * H * I
+                                    : a.dwgu + static_cast<size_t>(e) * 2 * I * H;
+  const uint16_t* const Ab = KIND == kWD ? a.dout : a.dgu;
+  const uint16_t* const Bb = KIND == kWD ? a.wa : a.x;
+
+  // unit i of this thread: u = tid + 256 i -> (K-row pair p = u / 16, 8 columns
+  // from 8q, q = u % 16); element offsets of its two K rows in A and in B
+  uint32_t aro[4], bro[4];
+  bool vld[4];
+  auto rows_for = [&](int ch) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = (tid + 256 * i) >> 4;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kr = ch * kKC + 2 * p + h;
+        vld[2 * i + h] = kr < cnt;
+        const int row = rbase + (kr < cnt ? kr : cnt - 1);
+        const uint32_t tok = static_cast<uint32_t>(a.perm[row] / k) * H;
+        aro[2 * i + h] = KIND == kWD ? tok : static_cast<uint32_t>(row) * (2 * I);
+        bro[2 * i + h] = KIND == kWD ? static_cast<uint32_t>(row) * I : tok;
+      }
+    }
+  };
+  i32x4 ra[4], rb[4];
+  auto load = [&](int mi, bool with_b) {
+    const int m0 = mi * 128;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = (tid + 256 * i) & 15;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        ra[2 * i + h] = ld16(Ab + aro[2 * i + h] + m0 + 8 * q);
+        if (with_b) rb[2 * i + h] = ld16(Bb + bro[2 * i + h] + n0 + 8 * q);
+      }
+    }
+  };
+  auto stage = [&](int buf, bool with_b) {
+    uint16_t* ab = As + buf * 128 * kKC;
+    uint16_t* bb = Bs + buf * 128 * kKC;
+    const i32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = tid + 256 * i, q = u & 15, p = u >> 4;
+      uint32_t w_[8];
+      pack_pairs(vld[2 * i] ? ra[2 * i] : zero, vld[2 * i + 1] ? ra[2 * i + 1] : zero, w_);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint32_t*>(ab + swz(8 * q + j, p >> 2) + ((2 * p) & 7)) = w_[j];
+      if (with_b) {
+        pack_pairs(vld[2 * i] ? rb[2 * i] : zero, vld[2 * i + 1] ? rb[2 * i + 1] : zero, w_);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint32_t*>(bb + swz(8 * q + j, p >> 2) + ((2 * p) & 7)) = w_[j];
+      }
+    }
+  };
+
+  const int wm = wv & 1, wn = wv >> 1;
+  const int fr = ln & 15, fg = ln >> 4;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // lane: output row mi*128 + wm*64 + 16i + fr, columns n0 + wn*64 + 16j + 4fg .. +3.
+  // Lanes fg and fg^1 (lane ^ 16) trade halves so that each stores 8 consecutive
+  // columns: the even one those of block j, the odd one those of block j+1.
+  auto store_tile = [&](int mi) {
+    const bool odd = fg & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t* orow = out + static_cast<size_t>(mi * 128 + wm * 64 + 16 * i + fr) * N + n0 + wn * 64;
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        uint32_t lo[2], hi[2];
+        lo[0] = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
+        lo[1] = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
+        hi[0] = f32_to_bf16_rne(acc[i][j + 1][0]) | (f32_to_bf16_rne(acc[i][j + 1][1]) << 16);
+        hi[1] = f32_to_bf16_rne(acc[i][j + 1][2]) | (f32_to_bf16_rne(acc[i][j + 1][3]) << 16);
+        const uint32_t s0 = odd ? lo[0] : hi[0], s1 = odd ? lo[1] : hi[1];
+        const uint32_t r0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(s0), 16, kWave));
+        const uint32_t r1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(s1), 16, kWave));
+        const i32x4 v = odd ? i32x4{static_cast<int>(r0), static_cast<int>(r1), static_cast<int>(hi[0]),
+                                    static_cast<int>(hi[1])}
+                            : i32x4{static_cast<int>(lo[0]), static_cast<int>(lo[1]),
+                                    static_cast<int>(r0), static_cast<int>(r1)};
+        const int col = odd ? 16 * (j + 1) + 4 * (fg - 1) : 16 * j + 4 * fg;
+        st16(orow + col, v);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  const int total = (mend - mfirst) * nchunks;
+  if (total == 0) {                                   // no routed rows: zero gradient
+    for (int mi = mfirst; mi < mend; ++mi) store_tile(mi);
+    return;
+  }
+  rows_for(0);
+  load(mfirst, true);
+  stage(0, true);
+  __syncthreads();
+  for (int it = 0; it < total; ++it) {
+    const int mq = it / nchunks;
+    const int mi = mfirst + mq, ch = it - mq * nchunks;
+    const int buf = it & 1;
+    const bool more = it + 1 < total;
+    if (more) {
+      const int mq1 = (it + 1) / nchunks;
+      if (!bres) rows_for(it + 1 - mq1 * nchunks);
+      load(mfirst + mq1, !bres);
+    }
+    const uint16_t* ab = As + buf * 128 * kKC;
+    const uint16_t* bb = Bs + (bres ? 0 : buf) * 128 * kKC;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int c = 4 * s2 + fg;
+      bf16x8 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const i32x4*>(ab + swz(wm * 64 + 16 * i + fr, c)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = as_bf16x8(*reinterpret_cast<const i32x4*>(bb + swz(wn * 64 + 16 * j + fr, c)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(bfr[j], af[i], acc[i][j]);
+    }
+    if (ch == nchunks - 1) store_tile(mi);
+    if (more) {
+      stage(buf ^ 1, !bres);
+      __syncthreads();
     }
   }
 }
@@ -533,6 +589,7 @@ BackwardWs backward_ws_layout(int T, int H, int I, int E, int k) {
   L.row_of = o;   o = align256(o + sizeof(int) * P);
   L.gu = o;       o = align256(o + sizeof(float) * P * 2 * I);
   L.dgu = o;      o = align256(o + sizeof(uint16_t) * P * 2 * I);
+  L.wa = o;       o = align256(o + sizeof(uint16_t) * P * I);
   L.dwp = o;      o = align256(o + sizeof(float) * P * (I / kNT));
   L.dxs = o;
   if (k > 1) o = align256(o + sizeof(float) * P * H);
@@ -559,6 +616,7 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   a.offsets = reinterpret_cast<int*>(b + L.offsets);
   a.gu = reinterpret_cast<float*>(b + L.gu);
   a.dgu = reinterpret_cast<uint16_t*>(b + L.dgu);
+  a.wa = reinterpret_cast<uint16_t*>(b + L.wa);
   a.dwp = reinterpret_cast<float*>(b + L.dwp);
   a.dxs = reinterpret_cast<float*>(b + L.dxs);
   a.dx = dx;
@@ -580,7 +638,7 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
     return dim3(static_cast<unsigned>((n / kNT * L.max_tiles + kXcds - 1) / kXcds * kXcds));
   };
   auto grid_w = [&](int M, int N) {
-    const long long n = static_cast<long long>(E) * (M / 128) * (N / kNT);
+    const long long n = static_cast<long long>(E) * ((M / 128 + kMB - 1) / kMB) * (N / kNT);
     return dim3(static_cast<unsigned>((n + kXcds - 1) / kXcds * kXcds));
   };
   prof_begin(kBwdGateUp, s);
@@ -594,10 +652,10 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   if (k > 1) hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, a.dxs, row_of, T, H, k, dx);
   prof_end(kBwdInput, s);
   prof_begin(kBwdWDown, s);
-  hipLaunchKernelGGL(bwd_gemm<kWD>, grid_w(H, I), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_wgrad<kWD>, grid_w(H, I), dim3(256), 0, s, a);
   prof_end(kBwdWDown, s);
   prof_begin(kBwdWGateUp, s);
-  hipLaunchKernelGGL(bwd_gemm<kWG>, grid_w(2 * I, H), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_wgrad<kWG>, grid_w(2 * I, H), dim3(256), 0, s, a);
   prof_end(kBwdWGateUp, s);
   hipLaunchKernelGGL(route_bwd, dim3(T), dim3(64), 0, s, a.dwp, row_of, idx, w, T, E, k, I / kNT,
                      dtw, dlogits);

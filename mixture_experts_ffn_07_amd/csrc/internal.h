@@ -84,7 +84,7 @@ hipError_t launch_group_experts(const int32_t* idx, int P, int E, int BM, int* c
 
 // Byte layout of the backward workspace (backward.hip).
 struct BackwardWs {
-  size_t counts, offsets, tiles, n_tiles, perm, row_of, gu, dgu, dwp, dxs, total;
+  size_t counts, offsets, tiles, n_tiles, perm, row_of, gu, dgu, wa, dwp, dxs, total;
   int max_tiles;
 };
 BackwardWs backward_ws_layout(int T, int H, int I, int E, int k);
