@@ -92,8 +92,13 @@ def parse():
                    help="approximate CPU time for the oracle baseline (0 = skip)")
     p.add_argument("--extra", action="store_true",
                    help="also time decode at T=1 and T=8 (reported under 'extra')")
-    p.add_argument("--pass", dest="pass_", choices=("forward", "backward"), default="forward",
-                   help="backward: time the layer's backward pass (batched BF16 workloads)")
+    p.add_argument("--pass", dest="pass_", choices=("forward", "backward", "train"),
+                   default="forward",
+                   help="backward: the layer's backward pass; train: forward + backward "
+                        "(batched BF16 workloads)")
+    p.add_argument("--recompute", action="store_true",
+                   help="backward recomputes the gate/up pre-activations instead of reading "
+                        "those the training forward kept")
     p.add_argument("--calibrate-fill-mib", type=int, default=0,
                    help="only time a plain device fill of this many MiB (HBM write rate)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -266,9 +271,13 @@ def backward_algorithmic(cfg, U):
     }
 
 
-def run_backward(M, W, torch, cfg, steps, warmup, seed, n_batches=2):
-    """One step = routing + the whole backward pass of one batch.  The timed
-    steps bracket the five backward kernels in turn with HIP events."""
+def run_backward(M, W, torch, cfg, steps, warmup, seed, n_batches=2, recompute=False,
+                 train=False):
+    """One step = routing + the backward pass of one batch (train: routing, the
+    training forward, then the backward).  Without recompute the backward reads
+    the gate/up pre-activations that moe_gate_up_3d_batched_train kept (made
+    before the timed region for the backward-only step).  The timed steps
+    bracket the step's kernels in turn with HIP events."""
     from mixture_experts_ffn_07_amd.hip_events import HipEvent
     dev = "cuda"
     log(f"generating weights of {cfg.name} ({W.expert_bytes(cfg) * cfg.E / 1e9:.1f} GB)")
@@ -286,40 +295,67 @@ def run_backward(M, W, torch, cfg, steps, warmup, seed, n_batches=2):
     dwd = torch.empty(E, H, I, dtype=torch.bfloat16, device=dev)
     dtw = torch.empty(T, k, dtype=torch.float32, device=dev)
     dl = torch.empty(T, E, dtype=torch.float32, device=dev)
+    fws = M.workspace(M.moe_workspace_bytes(T, H, I, E, k, M.MOE_BF16), dev)
+    h = torch.empty(T * k, I, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    gus = [None] * n_batches
+    if not recompute:
+        for b in range(n_batches):
+            gus[b] = torch.empty(T * k, 2 * I, dtype=torch.float32, device=dev)
+            M.moe_route_topk(acts[b]["logits"], k, topk_idx=idx[b], topk_w=tw[b], stream=stream)
+            M.moe_gate_up_3d_batched_train(acts[b]["x"], wts["w_gate_up"], idx[b], k, h=h,
+                                           gu=gus[b], ws=fws, stream=stream)
 
     def step(i):
         b = i % n_batches
         a = acts[b]
         M.moe_route_topk(a["logits"], k, topk_idx=idx[b], topk_w=tw[b], stream=stream)
+        if train:
+            M.moe_gate_up_3d_batched_train(a["x"], wts["w_gate_up"], idx[b], k, h=h, gu=gus[b],
+                                           ws=fws, stream=stream)
+            M.moe_down_3d_batched(h, wts["w_down"], idx[b], tw[b], fws, k, out=out, stream=stream)
         M.moe_backward_batched(a["x"], wts["w_gate_up"], wts["w_down"], idx[b], tw[b], douts[b],
-                               k, dx=dx, dw_gate_up=dwgu, dw_down=dwd, d_topk_w=dtw, dlogits=dl,
-                               ws=ws, stream=stream)
+                               k, gu_saved=gus[b], dx=dx, dw_gate_up=dwgu, dw_down=dwd,
+                               d_topk_w=dtw, dlogits=dl, ws=ws, stream=stream)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
     torch.cuda.synchronize()
+    kernels = [n for n in BWD_KERNELS if recompute or n != "bwd_gate_up"]
+    if train:
+        kernels = ["gemm_gate_up", "gemm_down"] + kernels
     t0 = time.perf_counter()
     for s in range(steps):
-        M.moe_profile_kernel(BWD_KERNELS[s % len(BWD_KERNELS)], evs[s][0].handle, evs[s][1].handle)
+        M.moe_profile_kernel(kernels[s % len(kernels)], evs[s][0].handle, evs[s][1].handle)
         step(warmup + s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     M.moe_profile_kernel("none", None, None)
     U = [int(torch.unique(idx[(warmup + s) % n_batches]).numel()) for s in range(steps)]
+
+    def alg(u):
+        d = dict(backward_algorithmic(cfg, u))
+        if not recompute:
+            del d["bwd_gate_up"]
+        if train:
+            f = batched_algorithmic(cfg, u)
+            d["gemm_gate_up"] = (f["gate_up"] + T * k * 2 * I * 4, f["flops_gate_up"])
+            d["gemm_down"] = (f["down"], f["flops_down"])
+        return d
     per = {}
-    for q, name in enumerate(BWD_KERNELS):
-        ss = [s for s in range(steps) if s % len(BWD_KERNELS) == q]
+    for q, name in enumerate(kernels):
+        ss = [s for s in range(steps) if s % len(kernels) == q]
         if not ss:
             continue
         dur = sum(evs[s][0].elapsed_ms(evs[s][1]) for s in ss) * 1e-3
-        nbytes = sum(backward_algorithmic(cfg, U[s])[name][0] for s in ss)
-        flops = sum(backward_algorithmic(cfg, U[s])[name][1] for s in ss)
+        nbytes = sum(alg(U[s])[name][0] for s in ss)
+        flops = sum(alg(U[s])[name][1] for s in ss)
         per[name] = {"avg_us": 1e6 * dur / len(ss), "gbs": nbytes / dur / 1e9,
                      "tflops": flops / dur / 1e12, "bytes_per_launch": nbytes / len(ss)}
     elapsed = t1 - t0
-    tot_bytes = sum(sum(v[0] for v in backward_algorithmic(cfg, u).values()) for u in U)
+    tot_bytes = sum(sum(v[0] for v in alg(u).values()) for u in U)
     return {"elapsed_s": elapsed, "ms_per_step": 1e3 * elapsed / steps,
             "tokens_per_s": T * steps / elapsed, "per_kernel": per,
             "layer_gbs": tot_bytes / elapsed / 1e9, "avg_touched_experts": sum(U) / steps}
@@ -396,11 +432,15 @@ def main():
         return
     cfg = W.get(args.workload)
     log(f"device {torch.cuda.get_device_name(0)}; workload {cfg.name}")
-    if args.pass_ == "backward":
+    if args.pass_ in ("backward", "train"):
         if cfg.path != "batched" or cfg.dtype != "bf16":
-            print(f"--pass backward needs a batched BF16 workload, not {cfg.name}", file=sys.stderr)
+            print(f"--pass {args.pass_} needs a batched BF16 workload, not {cfg.name}",
+                  file=sys.stderr)
             sys.exit(2)
-        r = run_backward(M, W, torch, cfg, args.steps, args.warmup, args.seed)
+        # the large-group forward GEMMs (>= 256 routed rows per expert) keep no pre-activations
+        recompute = args.recompute or cfg.T * cfg.k >= 256 * cfg.E
+        r = run_backward(M, W, torch, cfg, args.steps, args.warmup, args.seed,
+                         recompute=recompute, train=args.pass_ == "train")
         name, k = max(r["per_kernel"].items(), key=lambda kv: kv[1]["avg_us"])
         traffic, tprof = traffic_for(name, cfg.name)
         roof = {"bound": "hbm", "kernel": name, "achieved": round(k["gbs"], 1),
@@ -409,12 +449,16 @@ def main():
                 "avg_launch_us": round(k["avg_us"], 2),
                 "algorithmic_bytes_per_launch": int(k["bytes_per_launch"])}
         line = {
-            "metric": "MoE layer backward tokens/s", "value": round(r["tokens_per_s"], 1),
+            "metric": ("MoE layer backward tokens/s" if args.pass_ == "backward"
+                       else "MoE layer forward+backward tokens/s"),
+            "value": round(r["tokens_per_s"], 1),
             "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": cfg.name + " backward", "T": cfg.T, "H": cfg.H, "E": cfg.E,
-                       "k": cfg.k, "I": cfg.I, "parallelism": "none (1 GPU)"},
+            "config": {"workload": f"{cfg.name} {args.pass_}", "T": cfg.T, "H": cfg.H,
+                       "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                       "preactivations": "recomputed" if recompute else "kept by the forward",
+                       "parallelism": "none (1 GPU)"},
             "roofline": roof,
             "kernels": {n: {"avg_us": round(v["avg_us"], 1), "gbs": round(v["gbs"], 1),
                             "tflops": round(v["tflops"], 1)} for n, v in r["per_kernel"].items()},

@@ -174,6 +174,27 @@ int moe_down_3d_batched(const void* h, const uint8_t* h_scales,
 size_t moe_workspace_bytes(int T, int H, int I, int E, int k, int dtype);
 
 /*
+ * moe_gate_up_3d_batched_train -- moe_gate_up_3d_batched (BF16) that also keeps
+ * what the backward pass needs: the FP32 gate/up pre-activations of every
+ * routed pair (Mixture-of-Kittens summary, "Where pull was faster than push":
+ * the backward reuses forward activations rather than recomputing them).
+ *
+ *   x, w_gate_up, topk_idx, h, workspace   as for moe_gate_up_3d_batched with
+ *              dtype MOE_BF16
+ *   gu         [T*k, 2I] FP32 out, row t*k + j (slot order): [g; u] of pair
+ *              (t, j), g = W_gate[e] x[t], u = W_up[e] x[t] summed in FP32
+ *              (the values h was computed from); pass it to moe_backward_batched
+ * moe_down_3d_batched follows with the same workspace, as after
+ * moe_gate_up_3d_batched.  Limits as for moe_gate_up_3d_batched; shapes with
+ * 256 or more routed rows per expert on average (the large-group GEMMs) return
+ * MOE_ERR_UNSUPPORTED.
+ */
+int moe_gate_up_3d_batched_train(const uint16_t* x, const uint16_t* w_gate_up,
+                                 const int32_t* topk_idx, int T, int H, int I, int E, int k,
+                                 uint16_t* h, float* gu,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_backward_batched -- backward pass of the whole layer for a large batch,
  * BF16 (Mixture-of-Kittens summary, "What is 2.37x measured against": the
  * MoE layer's backward pass, measured beside its forward pass at 2,048 tokens
@@ -189,13 +210,15 @@ size_t moe_workspace_bytes(int T, int H, int I, int E, int k, int dtype);
  *   dlogits[t, m]  = w_m (d_topk_w[t, m's slot] - sum_j w_j d_topk_w[t, j]) for
  *                    the k selected experts m (softmax renormalised over them),
  *                    0 for every other expert.
- * The gate/up pre-activations are recomputed from x (nothing is kept from the
- * forward call).  All sums accumulate in FP32 in a fixed order; dx and both
- * weight gradients are rounded once to BF16.
+ * The gate/up pre-activations come from gu_saved (as written by
+ * moe_gate_up_3d_batched_train) or, when it is NULL, are recomputed from x.
+ * All sums accumulate in FP32 in a fixed order; dx and both weight gradients
+ * are rounded once to BF16.
  *
  *   x [T, H], w_gate_up [E, 2I, H], w_down [E, H, I]  BF16, as for the forward
  *   topk_idx, topk_w [T, k]   from moe_route_topk
  *   dout       [T, H] BF16    gradient of the layer output
+ *   gu_saved   [T*k, 2I] FP32 from moe_gate_up_3d_batched_train, or NULL
  *   dx         [T, H] BF16 out
  *   dw_gate_up [E, 2I, H] BF16 out (zero for experts no token routes to)
  *   dw_down    [E, H, I] BF16 out (likewise)
@@ -206,7 +229,7 @@ size_t moe_workspace_bytes(int T, int H, int I, int E, int k, int dtype);
  */
 int moe_backward_batched(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
                          const int32_t* topk_idx, const float* topk_w, const uint16_t* dout,
-                         int T, int H, int I, int E, int k,
+                         const float* gu_saved, int T, int H, int I, int E, int k,
                          uint16_t* dx, uint16_t* dw_gate_up, uint16_t* dw_down,
                          float* d_topk_w, float* dlogits,
                          void* workspace, size_t workspace_bytes, void* stream);

@@ -35,8 +35,9 @@ _SIGS = {
     "moe_gate_up_3d_batched": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "moe_down_3d_batched": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "moe_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
-    "moe_backward_batched": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P,
-                                  _P, _SZ, _P]),
+    "moe_backward_batched": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                                  _P, _P, _SZ, _P]),
+    "moe_gate_up_3d_batched_train": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "moe_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_profile_kernel": (_I, [_I, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
@@ -193,9 +194,28 @@ def moe_backward_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
     return int(lib.moe_backward_workspace_bytes(T, H, I, E, k))
 
 
-def moe_backward_batched(x, w_gate_up, w_down, topk_idx, topk_w, dout, k: int, dx=None,
-                         dw_gate_up=None, dw_down=None, d_topk_w=None, dlogits=None, ws=None,
-                         stream=None):
+def moe_gate_up_3d_batched_train(x, w_gate_up, topk_idx, k: int, h=None, gu=None, ws=None,
+                                 stream=None):
+    """moe_gate_up_3d_batched (BF16) that also returns the FP32 pre-activations;
+    returns (h, gu, ws)."""
+    T, H = x.shape
+    E, I2, _ = w_gate_up.shape
+    I = I2 // 2
+    if h is None:
+        h = torch.empty(T * k, I, dtype=torch.bfloat16, device=x.device)
+    if gu is None:
+        gu = torch.empty(T * k, I2, dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(moe_workspace_bytes(T, H, I, E, k, MOE_BF16), x.device)
+    _check("moe_gate_up_3d_batched_train", lib.moe_gate_up_3d_batched_train(
+        _ptr(x), _ptr(w_gate_up), _ptr(topk_idx), T, H, I, E, k, _ptr(h), _ptr(gu), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return h, gu, ws
+
+
+def moe_backward_batched(x, w_gate_up, w_down, topk_idx, topk_w, dout, k: int, gu_saved=None,
+                         dx=None, dw_gate_up=None, dw_down=None, d_topk_w=None, dlogits=None,
+                         ws=None, stream=None):
     """Backward pass of the layer (BF16); returns (dx, dw_gate_up, dw_down, d_topk_w, dlogits)."""
     T, H = x.shape
     E, I2, _ = w_gate_up.shape
@@ -215,7 +235,7 @@ def moe_backward_batched(x, w_gate_up, w_down, topk_idx, topk_w, dout, k: int, d
         ws = workspace(moe_backward_workspace_bytes(T, H, I, E, k), dev)
     _check("moe_backward_batched", lib.moe_backward_batched(
         _ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(topk_idx), _ptr(topk_w), _ptr(dout),
-        T, H, I, E, k, _ptr(dx), _ptr(dw_gate_up), _ptr(dw_down), _ptr(d_topk_w), _ptr(dlogits),
+        _ptr(gu_saved), T, H, I, E, k, _ptr(dx), _ptr(dw_gate_up), _ptr(dw_down), _ptr(d_topk_w), _ptr(dlogits),
         _ptr(ws), ws.numel(), _stream(stream)))
     return dx, dw_gate_up, dw_down, d_topk_w, dlogits
 
@@ -228,6 +248,7 @@ def moe_profile_kernel(kernel, start_event: Optional[int], stop_event: Optional[
 
 __all__ = ["lib", "LIB_PATH", "MoeError", "moe_route_topk", "moe_decode_forward",
            "moe_decode_workspace_bytes", "moe_workspace_bytes", "moe_quantize_mxfp8",
-           "moe_gate_up_3d_batched", "moe_down_3d_batched", "moe_backward_batched",
+           "moe_gate_up_3d_batched", "moe_down_3d_batched", "moe_gate_up_3d_batched_train",
+           "moe_backward_batched",
            "moe_backward_workspace_bytes", "moe_profile_kernel", "workspace",
            "MOE_BF16", "MOE_MXFP8", "KERNELS"]

@@ -243,8 +243,9 @@ size_t moe_backward_workspace_bytes(int T, int H, int I, int E, int k) {
 }
 
 int moe_backward_batched(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,
-                         const int32_t* topk_idx, const float* topk_w, const uint16_t* dout, int T,
-                         int H, int I, int E, int k, uint16_t* dx, uint16_t* dw_gate_up,
+                         const int32_t* topk_idx, const float* topk_w, const uint16_t* dout,
+                         const float* gu_saved, int T, int H, int I, int E, int k,
+                         uint16_t* dx, uint16_t* dw_gate_up,
                          uint16_t* dw_down, float* d_topk_w, float* dlogits, void* workspace,
                          size_t workspace_bytes, void* stream) {
   if (int st = check_common(T, H, I, E, k, 256, 256)) return st;
@@ -264,14 +265,40 @@ int moe_backward_batched(const uint16_t* x, const uint16_t* w_gate_up, const uin
     return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(topk_idx) ||
       !aligned16(topk_w) || !aligned16(dout) || !aligned16(dx) || !aligned16(dw_gate_up) ||
-      !aligned16(dw_down) || !aligned16(d_topk_w) || !aligned16(dlogits) || !aligned16(workspace))
+      !aligned16(dw_down) || !aligned16(d_topk_w) || !aligned16(dlogits) ||
+      !aligned16(workspace) || (gu_saved && !aligned16(gu_saved)))
     return fail(MOE_ERR_ALIGN, "device pointers must be 16-byte aligned");
   int cus = 0;
   if (int st = device_info(&cus)) return st;
-  return hip_status(moe::launch_backward(x, w_gate_up, w_down, topk_idx, topk_w, dout, T, H, I, E,
-                                         k, dx, dw_gate_up, dw_down, d_topk_w, dlogits, workspace,
-                                         static_cast<hipStream_t>(stream)),
+  return hip_status(moe::launch_backward(x, w_gate_up, w_down, topk_idx, topk_w, dout, gu_saved,
+                                         T, H, I, E, k, dx, dw_gate_up, dw_down, d_topk_w,
+                                         dlogits, workspace, static_cast<hipStream_t>(stream)),
                     "moe_backward_batched launch");
+}
+
+int moe_gate_up_3d_batched_train(const uint16_t* x, const uint16_t* w_gate_up,
+                                 const int32_t* topk_idx, int T, int H, int I, int E, int k,
+                                 uint16_t* h, float* gu, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (int st = check_batched(T, H, I, E, k, MOE_BF16, workspace, workspace_bytes)) return st;
+  if (!x || !w_gate_up || !topk_idx || !h || !gu)
+    return fail(MOE_ERR_NULL, "x, w_gate_up, topk_idx, h and gu are required");
+  if (moe::use_large_tiles(T, H, I, E, k, MOE_BF16))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "T*k=%lld routed rows over E=%d experts: the large-group GEMMs do not keep "
+                "the pre-activations",
+                static_cast<long long>(T) * k, E);
+  if (static_cast<long long>(T) * k * 2 * I >= (1LL << 31))
+    return fail(MOE_ERR_SHAPE, "T*k*2I reaches 2^31");
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(topk_idx) || !aligned16(h) ||
+      !aligned16(gu))
+    return fail(MOE_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  return hip_status(moe::launch_gate_up_batched(x, nullptr, w_gate_up, nullptr, topk_idx, T, H, I,
+                                                E, k, MOE_BF16, h, nullptr, workspace,
+                                                static_cast<hipStream_t>(stream), cus, gu),
+                    "moe_gate_up_3d_batched_train launch");
 }
 
 }  // extern "C"

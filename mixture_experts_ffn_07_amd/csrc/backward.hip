@@ -15,8 +15,8 @@
 //
 // Launches, all on the caller's stream, in this order:
 //   group_experts   the forward's grouping (64-row M-tiles, stable order)
-//   kGU   gu[row]  = [W_gate; W_up][e] x[t]                FP32, recomputed (not stored
-//                   by the forward)
+//   kGU   gu[row]  = [W_gate; W_up][e] x[t]                FP32, recomputed when the
+//                   caller has not kept the forward's pre-activations
 //   kDD   dh tile  = W_down[e]^T dout[t]; epilogue: dgu[row] = [dg; du] (BF16), the
 //                   weighted activation wa[row] = w a (BF16) and one partial dot
 //                   a . dh per 128 columns
@@ -72,7 +72,8 @@ struct BwdArgs {
   const int* n_tiles;
   const int* counts;        // rows per expert
   const int* offsets;       // first grouped row per expert
-  float* gu;                // [P, 2I] grouped rows
+  float* gu;                // [P, 2I] grouped rows (recomputed pre-activations)
+  const float* gus;         // or NULL: [P, 2I] pair (slot) order, saved by the forward
   uint16_t* dgu;            // [P, 2I] grouped rows
   uint16_t* wa;             // [P, I] grouped rows: w * silu(g) * u
   float* dwp;               // [P, I/128] partial dots
@@ -283,7 +284,8 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
         // columns n0 + 8sg .. +7 of the intermediate dimension
         const int pair = a.perm[grow];
         const float wt = a.w[pair];
-        const float* gp = a.gu + grow * (2 * I) + n0 + 8 * sg;
+        const float* gp = (a.gus ? a.gus + static_cast<size_t>(pair) * (2 * I) : a.gu + grow * (2 * I)) +
+                          n0 + 8 * sg;
         const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp);
         const f32x4 g1 = *reinterpret_cast<const f32x4*>(gp + 4);
         const f32x4 u0 = *reinterpret_cast<const f32x4*>(gp + I);
@@ -598,9 +600,10 @@ BackwardWs backward_ws_layout(int T, int H, int I, int E, int k) {
 }
 
 hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_t* wd,
-                           const int32_t* idx, const float* w, const uint16_t* dout, int T, int H,
-                           int I, int E, int k, uint16_t* dx, uint16_t* dwgu, uint16_t* dwd,
-                           float* dtw, float* dlogits, void* ws, hipStream_t s) {
+                           const int32_t* idx, const float* w, const uint16_t* dout,
+                           const float* gu_saved, int T, int H, int I, int E, int k,
+                           uint16_t* dx, uint16_t* dwgu, uint16_t* dwd, float* dtw,
+                           float* dlogits, void* ws, hipStream_t s) {
   const BackwardWs L = backward_ws_layout(T, H, I, E, k);
   char* b = static_cast<char*>(ws);
   BwdArgs a{};
@@ -615,6 +618,7 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   a.counts = reinterpret_cast<int*>(b + L.counts);
   a.offsets = reinterpret_cast<int*>(b + L.offsets);
   a.gu = reinterpret_cast<float*>(b + L.gu);
+  a.gus = gu_saved;
   a.dgu = reinterpret_cast<uint16_t*>(b + L.dgu);
   a.wa = reinterpret_cast<uint16_t*>(b + L.wa);
   a.dwp = reinterpret_cast<float*>(b + L.dwp);
@@ -641,9 +645,11 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
     const long long n = static_cast<long long>(E) * ((M / 128 + kMB - 1) / kMB) * (N / kNT);
     return dim3(static_cast<unsigned>((n + kXcds - 1) / kXcds * kXcds));
   };
-  prof_begin(kBwdGateUp, s);
-  hipLaunchKernelGGL(bwd_gemm<kGU>, grid_tiles(2 * I), dim3(256), 0, s, a);
-  prof_end(kBwdGateUp, s);
+  if (!gu_saved) {
+    prof_begin(kBwdGateUp, s);
+    hipLaunchKernelGGL(bwd_gemm<kGU>, grid_tiles(2 * I), dim3(256), 0, s, a);
+    prof_end(kBwdGateUp, s);
+  }
   prof_begin(kBwdDown, s);
   hipLaunchKernelGGL(bwd_gemm<kDD>, grid_tiles(I), dim3(256), 0, s, a);
   prof_end(kBwdDown, s);

@@ -156,11 +156,12 @@ __global__ __launch_bounds__(1024) void group_experts(
 // the waves; the next step's weights are in flight while a step multiplies.
 // Rows past the tile's end load the tile's first row; their MFMA columns are
 // computed and discarded (columns never mix).
-// Epilogues: KIND 0 SwiGLU -> h (BF16); KIND 1 FP32 y per slot; KIND 2 (k = 1)
-// out[t] = bf16(w[t] * y) with t = perm[row].
+// Epilogues: KIND 0 SwiGLU -> h (BF16); KIND 3 the same, and also the FP32
+// pre-activations g and u of each pair in slot order (for the backward pass);
+// KIND 1 FP32 y per slot; KIND 2 (k = 1) out[t] = bf16(w[t] * y) with t = perm[row].
 constexpr int kSXC = 128;                // K chunk of the staged activations
 constexpr int kSXRS = kSXC + 8;          // padded LDS row stride (elements)
-enum { kProjGateUp = 0, kProjDown = 1, kProjDownFused = 2 };
+enum { kProjGateUp = 0, kProjDown = 1, kProjDownFused = 2, kProjGateUpSave = 3 };
 
 template <int KIND, int NW>   // (128 registers: with NW = 8, two workgroups share a CU)
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_bf16s(
@@ -168,14 +169,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint16_t* __restrict__ hout, float* __restrict__ y,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, float* __restrict__ gu) {
+  constexpr bool GU = KIND == kProjGateUp || KIND == kProjGateUpSave;
   constexpr int NT = NW * 64;
-  constexpr int RPW = KIND == kProjGateUp ? 16 : 32;      // outputs per wave
+  constexpr int RPW = GU ? 16 : 32;      // outputs per wave
   constexpr int LPT = kBM * (kSXC / 8) / NT;              // 16-byte activation loads per thread
   __shared__ __align__(16) uint16_t xs[2][kBM * kSXRS];
   __shared__ __align__(16) i32x4 wtl[NW][16 * 8];         // per wave: [16 rows][8 chunks]
-  const int K = KIND == kProjGateUp ? H : I;              // reduction length
-  const int N = KIND == kProjGateUp ? I : H;              // outputs
+  const int K = GU ? H : I;              // reduction length
+  const int N = GU ? I : H;              // outputs
   const int nblk = N / (NW * RPW);
   const int item = real_item(blockIdx.x, nblk, *n_tiles);
   if (item < 0) return;
@@ -188,11 +190,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = nb_i * NW * RPW + wv * RPW;              // the wave's first output
   // the wave's two 16-row weight groups
-  const int row0 = nb, row1 = KIND == kProjGateUp ? I + nb : nb + 16;
+  const int row0 = nb, row1 = GU ? I + nb : nb + 16;
 
   // whole-line loads: lane = (row lr of an 8-row group, 16-byte chunk lc)
   const int lr = ln >> 3, lc = ln & 7;
-  const uint16_t* __restrict__ wb = wt + static_cast<size_t>(e) * (KIND == kProjGateUp ? 2 * I : H) * K;
+  const uint16_t* __restrict__ wb = wt + static_cast<size_t>(e) * (GU ? 2 * I : H) * K;
   uint32_t ow[4];                                         // group 0 rows 0-7, 8-15, group 1 rows 0-7, 8-15
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   for (int i = 0; i < LPT; ++i) {
     const int c = tid + i * NT, r = c >> 4, rr = r < mcount ? r : 0;
     lrow[i] = r * kSXRS + (c & 15) * 8;
-    const int arow = KIND == kProjGateUp ? perm[rbase + rr] / k : rbase + rr;
+    const int arow = GU ? perm[rbase + rr] / k : rbase + rr;
     oxl[i] = static_cast<uint32_t>(arow * K + (c & 15) * 8);
   }
   i32x4 xr[LPT];
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   for (int g = 0; g < 4; ++g) {
     const int r = 16 * g + col;
     if (r >= mcount) continue;
-    if (KIND == kProjGateUp) {
+    if (GU) {
       uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb + 4 * grp;
       uint32_t p[4];
 #pragma unroll
@@ -295,6 +297,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
       v.x = p[0] | (p[1] << 16);
       v.y = p[2] | (p[3] << 16);
       *reinterpret_cast<uint2*>(hr) = v;
+      if (KIND == kProjGateUpSave) {                      // FP32 g and u of the pair, slot order
+        float* gp = gu + static_cast<size_t>(perm[rbase + r]) * (2 * I) + nb + 4 * grp;
+        *reinterpret_cast<f32x4*>(gp) = acc0[g];
+        *reinterpret_cast<f32x4*>(gp + I) = acc1[g];
+      }
     } else if (KIND == kProjDownFused) {
       const int t = perm[rbase + r];                      // k = 1: pair id == token
       const float wt_ = w[t];
@@ -633,7 +640,7 @@ int round_up(int v, int m) { return (v + m - 1) / m * m; }
 hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* wgu,
                                   const uint8_t* wgus, const int32_t* idx, int T, int H, int I,
                                   int E, int k, int dtype, void* h, uint8_t* hs, void* ws,
-                                  hipStream_t s, int num_cus) {
+                                  hipStream_t s, int num_cus, float* gu) {
   const BatchedWs L = batched_ws_layout(T, H, I, E, k, dtype);
   const BatchedPtrs p = batched_ptrs(ws, L);
   const int P = T * k;
@@ -660,11 +667,16 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
   // 16 waves x 16 neurons = 256 neurons per workgroup (I is a multiple of 256)
   const int n_items = round_up((I / 256) * L.max_tiles, kXcds);
   prof_begin(kGemmGateUp, s);
-  if (dtype == 0)
+  if (dtype == 0 && gu)
+    hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 16>), dim3(n_items), dim3(1024), 0, s,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
+                       p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
+                       static_cast<uint16_t*>(h), nullptr, nullptr, gu);
+  else if (dtype == 0)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint16_t*>(h), nullptr, nullptr);
+                       static_cast<uint16_t*>(h), nullptr, nullptr, nullptr);
   else
     hipLaunchKernelGGL((gemm_mx_s<kProjGateUp, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
@@ -714,7 +726,7 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   hipLaunchKernelGGL((gemm_bf16s<KINDV, NWV>), grid, block, 0, s,                          \
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),       \
                      p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr,   \
-                     p.y, out)
+                     p.y, out, nullptr)
 #define DOWN_MX(KINDV, NWV)                                                                 \
   hipLaunchKernelGGL((gemm_mx_s<KINDV, NWV>), grid, block, 0, s,                           \
                      static_cast<const uint8_t*>(h), hs, static_cast<const uint8_t*>(wd), wds, \

@@ -88,18 +88,21 @@ struct BackwardWs {
   int max_tiles;
 };
 BackwardWs backward_ws_layout(int T, int H, int I, int E, int k);
+// gu_saved: NULL (the pre-activations are recomputed) or [T*k, 2I] FP32, slot order
 hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_t* wd,
-                           const int32_t* idx, const float* w, const uint16_t* dout, int T, int H,
-                           int I, int E, int k, uint16_t* dx, uint16_t* dwgu, uint16_t* dwd,
-                           float* dtw, float* dlogits, void* ws, hipStream_t s);
+                           const int32_t* idx, const float* w, const uint16_t* dout,
+                           const float* gu_saved, int T, int H, int I, int E, int k,
+                           uint16_t* dx, uint16_t* dwgu, uint16_t* dwd, float* dtw,
+                           float* dlogits, void* ws, hipStream_t s);
 
 hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
                            uint8_t* scales, hipStream_t s);
 
+// gu: NULL, or (BF16, small groups only) [T*k, 2I] FP32 pre-activations out, slot order
 hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* wgu,
                                   const uint8_t* wgus, const int32_t* idx, int T, int H, int I,
                                   int E, int k, int dtype, void* h, uint8_t* hs, void* ws,
-                                  hipStream_t s, int num_cus);
+                                  hipStream_t s, int num_cus, float* gu = nullptr);
 
 hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
                                const uint8_t* wds, const int32_t* idx, const float* w, int T,

@@ -140,8 +140,8 @@ def test_backward_validation(m):
 
     def call(x=FAKE, dout=FAKE, dx=FAKE, dwgu=FAKE, ws=FAKE, wsb=need, T=64, H=256, I=256, E=8,
              k=2):
-        return b(x, FAKE, FAKE, FAKE, FAKE, dout, T, H, I, E, k, dx, dwgu, FAKE, FAKE, FAKE, ws,
-                 wsb, None)
+        return b(x, FAKE, FAKE, FAKE, FAKE, dout, None, T, H, I, E, k, dx, dwgu, FAKE, FAKE, FAKE,
+                 ws, wsb, None)
     assert call(x=None) == m.MOE_ERR_NULL
     assert call(dout=None) == m.MOE_ERR_NULL
     assert call(dwgu=None) == m.MOE_ERR_NULL
@@ -155,3 +155,19 @@ def test_backward_validation(m):
     # the workspace holds the recomputed FP32 pre-activations and the BF16 gradients
     # of [g; u] for every routed pair
     assert need >= 64 * 2 * 2 * 256 * (4 + 2)
+
+
+def test_train_forward_validation(m):
+    g = m.lib.moe_gate_up_3d_batched_train
+    need = m.lib.moe_workspace_bytes(64, 256, 256, 8, 2, 0)
+
+    def call(x=FAKE, gu=FAKE, T=64, H=256, I=256, E=8, k=2, wsb=need):
+        return g(x, FAKE, FAKE, T, H, I, E, k, FAKE, gu, FAKE, wsb, None)
+    assert call(x=None) == m.MOE_ERR_NULL
+    assert call(gu=None) == m.MOE_ERR_NULL
+    assert call(I=128) == m.MOE_ERR_SHAPE
+    assert call(wsb=need - 1) == m.MOE_ERR_WORKSPACE
+    assert call(gu=FAKE + 4) == m.MOE_ERR_ALIGN
+    # >= 256 routed rows per expert on average: the large-group GEMMs keep nothing
+    big = m.lib.moe_workspace_bytes(4096, 256, 256, 2, 1, 0)
+    assert call(T=4096, E=2, k=1, wsb=big) == m.MOE_ERR_UNSUPPORTED

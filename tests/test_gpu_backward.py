@@ -32,10 +32,14 @@ def M():
     return M
 
 
-def run_bwd(M, d, dout):
+def run_bwd(M, d, dout, saved=False):
+    """Routing, then the backward pass; with saved=True the gate/up pre-activations
+    come from moe_gate_up_3d_batched_train instead of being recomputed."""
     cfg = d["cfg"]
     idx, w = M.moe_route_topk(d["logits"], cfg.k)
-    res = M.moe_backward_batched(d["x"], d["w_gate_up"], d["w_down"], idx, w, dout, cfg.k)
+    gu = M.moe_gate_up_3d_batched_train(d["x"], d["w_gate_up"], idx, cfg.k)[1] if saved else None
+    res = M.moe_backward_batched(d["x"], d["w_gate_up"], d["w_down"], idx, w, dout, cfg.k,
+                                 gu_saved=gu)
     torch.cuda.synchronize()
     return res, idx
 
@@ -48,11 +52,12 @@ def _fp32(got, ref, bound, what):
     assert rl <= bound, f"{what}: {rl:.3e} > {bound}"
 
 
-def _check(M, d, what, tokens=None, experts=None, seed=0):
+def _check(M, d, what, tokens=None, experts=None, seed=0, saved=False):
     cfg = d["cfg"]
-    print(f"[backward] {what}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}", flush=True)
+    print(f"[backward] {what}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} saved={saved}",
+          flush=True)
     dout = W.make_output_grad(cfg, seed=seed, device="cuda")
-    (dx, dwgu, dwd, dtw, dl), idx = run_bwd(M, d, dout)
+    (dx, dwgu, dwd, dtw, dl), idx = run_bwd(M, d, dout, saved=saved)
     if experts == "sample":                           # experts that some token routes to
         used = np.unique(idx.cpu().numpy())
         rng = np.random.default_rng(7)
@@ -93,6 +98,43 @@ def test_backward_shapes(M, T, H, I, E, k):
     _check(M, _custom(T, H, I, E, k, seed=T + E), f"bwd T={T} k={k}")
 
 
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (100, 512, 256, 8, 2),
+    (300, 256, 512, 6, 3),
+    (257, 768, 256, 40, 8),
+    (200, 512, 256, 5, 1),
+])
+def test_backward_with_saved_preactivations(M, T, H, I, E, k):
+    _check(M, _custom(T, H, I, E, k, seed=T + E + 1), f"bwd saved T={T} k={k}", saved=True)
+
+
+def test_train_forward_matches_forward_and_oracle(M):
+    # same h as the inference call (same kernel arithmetic), the same output after
+    # the down projection, and FP32 pre-activations close to the oracle's
+    d = _custom(300, 512, 256, 6, 3, seed=12)
+    cfg = d["cfg"]
+    idx, w = M.moe_route_topk(d["logits"], cfg.k)
+    h0, _, ws0 = M.moe_gate_up_3d_batched(d["x"], d["w_gate_up"], idx, cfg.k)
+    out0 = M.moe_down_3d_batched(h0, d["w_down"], idx, w, ws0, cfg.k)
+    h1, gu, ws1 = M.moe_gate_up_3d_batched_train(d["x"], d["w_gate_up"], idx, cfg.k)
+    out1 = M.moe_down_3d_batched(h1, d["w_down"], idx, w, ws1, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    from tests._gpu import oracle
+    _, inter = oracle(d, return_intermediates=True)
+    ref = inter["gu"].reshape(cfg.T * cfg.k, 2 * cfg.I)
+    _fp32(gu, ref, 1e-5, "train forward gu")
+
+
+def test_train_forward_rejects_large_groups(M):
+    d = _custom(4096, 256, 256, 2, 1, seed=2)
+    idx, _ = M.moe_route_topk(d["logits"], 1)
+    with pytest.raises(M.MoeError) as ei:
+        M.moe_gate_up_3d_batched_train(d["x"], d["w_gate_up"], idx, 1)
+    assert ei.value.status == M.MOE_ERR_UNSUPPORTED
+
+
 def test_backward_bit_identical_repeats(M):
     d = _custom(600, 512, 256, 12, 4, seed=5)
     dout = W.make_output_grad(d["cfg"], seed=1, device="cuda")
@@ -109,10 +151,11 @@ def _sample(T, n, seed):
     return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
 
 
-def test_backward_kimi_full_size(M):
+@pytest.mark.parametrize("saved", [False, True])
+def test_backward_kimi_full_size(M, saved):
     d = W.make("kimi-bf16-T2048", seed=0, device="cuda")
     _check(M, d, "kimi-bf16-T2048 (8 tokens, 3 experts)", tokens=_sample(2048, 8, 2),
-           experts="sample")
+           experts="sample", saved=saved)
 
 
 def test_backward_ep64_share_full_size(M):
