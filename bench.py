@@ -185,11 +185,16 @@ def batched_algorithmic(cfg, U):
             "flops_gate_up": 2.0 * P * 2 * I * H, "flops_down": 2.0 * P * H * I}
 
 
-def run_batched(M, W, torch, cfg, steps, warmup, seed, n_batches=4):
+def run_batched(M, W, torch, cfg, steps, warmup, seed, n_batches=4, layers=1):
+    """Steps cycle through `layers` weight sets when they fit in 16 GB (decode-sized
+    layers: each step then streams weights the last-level cache does not hold)."""
     from mixture_experts_ffn_07_amd.hip_events import HipEvent
     dev = "cuda"
-    log(f"generating weights of {cfg.name} ({W.expert_bytes(cfg) * cfg.E / 1e9:.1f} GB)")
-    wts = W.make_weights(cfg, seed=seed, device=dev)
+    gb = W.expert_bytes(cfg) * cfg.E / 1e9
+    n_sets = layers if gb * layers <= 16.0 else 1
+    log(f"generating {n_sets} weight set(s) of {cfg.name} ({gb:.1f} GB each)")
+    sets = [W.make_weights(cfg, seed=seed + 1000003 * l, device=dev) for l in range(n_sets)]
+    wts = sets[0]
     acts = [W.make_activations(cfg, seed=seed + 7919 * (b + 1), device=dev) for b in range(n_batches)]
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     dt = M.MOE_MXFP8 if cfg.dtype == "mxfp8" else M.MOE_BF16
@@ -207,6 +212,7 @@ def run_batched(M, W, torch, cfg, steps, warmup, seed, n_batches=4):
     def step(i):
         b = i % n_batches
         a = acts[b]
+        wts = sets[i % n_sets]
         M.moe_route_topk(a["logits"], k, topk_idx=idx[b], topk_w=tw[b], stream=stream)
         if dt == M.MOE_MXFP8:
             M.moe_quantize_mxfp8(a["x"], codes=xc, scales=xs, stream=stream)
@@ -248,7 +254,7 @@ def run_batched(M, W, torch, cfg, steps, warmup, seed, n_batches=4):
         "kernel_flops_per_launch": sum(a["flops_gate_up"] for a in alg) / steps,
         "layer_gbs": sum(a["gate_up"] + a["down"] for a in alg) / elapsed / 1e9,
         "layer_tflops": sum(a["flops_gate_up"] + a["flops_down"] for a in alg) / elapsed / 1e12,
-        "avg_touched_experts": sum(U) / steps,
+        "avg_touched_experts": sum(U) / steps, "weight_sets": n_sets,
         "first_batch": acts[warmup % n_batches], "first_weights": wts,
     }
 
@@ -480,7 +486,7 @@ def main():
                 "avg_launch_us": round(r["kernel_avg_us"], 2),
                 "algorithmic_bytes_per_launch": int(r["kernel_bytes_per_launch"])}
     else:
-        r = run_batched(M, W, torch, cfg, args.steps, args.warmup, args.seed)
+        r = run_batched(M, W, torch, cfg, args.steps, args.warmup, args.seed, layers=args.layers)
         peak_tf = MFMA_PEAK_TFLOPS[cfg.dtype]
         rows_per_expert = cfg.T * cfg.k / cfg.E
         if rows_per_expert >= 256:       # weight reuse high enough to be MFMA-bound
@@ -506,7 +512,8 @@ def main():
         "dtype": "bf16" if cfg.dtype == "bf16" else "mxfp8 (e4m3 + e8m0), fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
-                   "I": cfg.I, "weight_sets": args.layers, "parallelism": "none (1 GPU)"},
+                   "I": cfg.I, "weight_sets": r.get("weight_sets", args.layers),
+                   "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "layer": {"hbm_gbs": round(r["layer_gbs"], 1),
                   **({"mfma_tflops": round(r["layer_tflops"], 1)} if "layer_tflops" in r else {}),

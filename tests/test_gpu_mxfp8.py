@@ -145,3 +145,10 @@ def test_mx_h_codes_match_oracle_quantizer(M):
     pairs = sorted((int(ridx[t, j]), t, j) for t in range(cfg.T) for j in range(cfg.k))
     want = np.stack([inter["a"][t, j] for (_, t, j) in pairs])
     assert rel_l2(deq, want) < 1e-2
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_mxfp8_decode_shapes(M, T):
+    # the Qwen3-style decode layer with MXFP8 weights, every token checked
+    d = W.make("qwen3-mxfp8-decode-T32", seed=3, device="cuda", T=T)
+    _check(M, d, f"qwen3-mxfp8-decode T={T}")

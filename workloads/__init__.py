@@ -74,6 +74,9 @@ CONFIGS: Dict[str, Config] = {c.name: c for c in [
        note="Qwen3-style decode, near-uniform routing"),
     _c(name="qwen3-decode-T32", T=32, H=2048, E=128, k=8, I=768,
        note="Qwen3-style decode, near-uniform routing"),
+    _c(name="qwen3-mxfp8-decode-T32", T=32, H=2048, E=128, k=8, I=768, dtype="mxfp8",
+       path="batched", note="Qwen3-style decode with MXFP8 weights (x and h MX-quantized), "
+                            "served by the batched MXFP8 calls"),
     _c(name="q35-zipf-T64", T=64, H=4096, E=512, k=10, I=1024, zipf_s=1.1,
        note="Qwen3.5-397B-A17B-shaped decode, Zipf(1.1) expert skew"),
     _c(name="kimi-bf16-T2048", T=2048, H=7168, E=384, k=8, I=2048, path="batched",
