@@ -53,7 +53,7 @@ namespace moe {
 namespace {
 
 enum { kGU = 0, kDD = 1, kDG = 2, kWD = 3, kWG = 4 };
-constexpr int kBB = 64;          // routed rows per M-tile
+constexpr int kBB = 64;          // routed rows per M-tile (128 when experts average >= 48 rows)
 constexpr int kKC = 64;          // K chunk (elements)
 constexpr int kNT = 128;         // output columns per workgroup
 constexpr int kCS32 = kNT + 4;   // FP32 C-tile row stride (elements)
@@ -99,9 +99,8 @@ __device__ __forceinline__ void pack_pairs(const i32x4& v0, const i32x4& v1, uin
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
-template <int KIND>   // kGU, kDD, kDG
+template <int KIND, int MT>   // kGU, kDD, kDG; MT = routed rows per M-tile (64 or 128)
 __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
-  constexpr int MT = kBB;
   constexpr int MI = MT / 32;                         // 16-row A blocks per wave
   constexpr int AROW_U = MT * 8 / 256;                // "rows" A units per thread
   constexpr int BROW_U = kNT * 8 / 256;               // "rows" B units per thread (kGU)
@@ -113,7 +112,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, I = a.I, k = a.k;
 
-  // ---- work item: (M-tile of 64 routed rows, 128 output columns) ----
+  // ---- work item: (M-tile of MT routed rows, 128 output columns) ----
   const int N = KIND == kGU ? 2 * I : (KIND == kDD ? I : H);
   const int nblk = N / kNT;
   const int item = real_item(blockIdx.x, nblk, *a.n_tiles);
@@ -122,7 +121,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
   const int n0 = (item - tile * nblk) * kNT;
   const int2 te = a.tiles[tile];
   const int e = te.x;
-  const int mcount = min(kBB, a.counts[e] - te.y);
+  const int mcount = min(MT, a.counts[e] - te.y);
   const int rbase = a.offsets[e] + te.y;
   const int nchunks = (KIND == kDG ? 2 * I : H) / kKC;
 
@@ -251,27 +250,30 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
     __syncthreads();
   }
 
-  // ---- C tile through LDS (the operand buffers are free after the last barrier) ----
-  // lane: tile row wm*MT/2 + 16i + fr, columns wn*64 + 16j + 4fg .. +3
-  {
-    float* Cs = reinterpret_cast<float*>(lds);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<f32x4*>(Cs + (wm * (MT / 2) + 16 * i + fr) * kCS32 + wn * 64 + 16 * j + 4 * fg) =
-            acc[i][j];
-  }
-  __syncthreads();
-
-  // ---- epilogue: thread = (tile row r, 8 consecutive columns 8*sg) ----
+  // ---- C tile through LDS, 64 rows at a time (the operand buffers are free after
+  // the last barrier); lane: tile row wm*MT/2 + 16i + fr, columns wn*64 + 16j + 4fg .. +3
   const int sg = tid & 15;
 #pragma unroll 1
-  for (int r = tid >> 4; r < MT; r += 16) {
+  for (int half = 0; half < MT / 64; ++half) {
+    if (MT == 64 || wm == half) {
+      float* Cs = reinterpret_cast<float*>(lds);
+      const int rl = MT == 64 ? wm * 32 : 0;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4*>(Cs + (rl + 16 * i + fr) * kCS32 + wn * 64 + 16 * j + 4 * fg) =
+              acc[i][j];
+    }
+    __syncthreads();
+  // ---- epilogue: thread = (tile row r, 8 consecutive columns 8*sg) ----
+#pragma unroll 1
+  for (int rc = tid >> 4; rc < 64; rc += 16) {
+    const int r = half * 64 + rc;
     {
       const float* Cs = reinterpret_cast<const float*>(lds);
-      const f32x4 c0 = *reinterpret_cast<const f32x4*>(Cs + r * kCS32 + 8 * sg);
-      const f32x4 c1 = *reinterpret_cast<const f32x4*>(Cs + r * kCS32 + 8 * sg + 4);
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(Cs + rc * kCS32 + 8 * sg);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(Cs + rc * kCS32 + 8 * sg + 4);
       const bool live = r < mcount;
       const size_t grow = static_cast<size_t>(rbase + (live ? r : 0));
       if constexpr (KIND == kGU) {
@@ -347,6 +349,8 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
       }
     }
   }
+    __syncthreads();                                  // before the next half reuses Cs
+  }
 }
 
 // Weight gradients, reduced over an expert's grouped rows r (K, in chunks of
@@ -356,11 +360,12 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
 //   kWG: dW_gate_up[e][c][h] = sum_r dgu[r][c] * x[t_r][h]     (A = dgu rows,
 //        output rows c; B = x rows gathered through perm, output columns h)
 // Workgroup = (expert, 128 output columns, kMB blocks of 128 output rows).
-// With one chunk (at most 64 rows: the common case at 40-60 routed rows per
-// expert) the B tile is staged once and stays in LDS for every row block;
+// With at most two chunks (up to 128 rows: the common case at 40-70 routed
+// rows per expert) the B tiles are staged during the first row block and stay
+// in LDS (one slot per chunk) for every later row block;
 // each row block's A tile is loaded while the previous block multiplies, and
-// the finished block is written straight from the accumulators (4 BF16 per
-// lane, a full 128-byte line per row across a wave's four stores).
+// the finished block is written from the accumulators, 16 bytes per lane after
+// neighbouring lanes trade halves (64 contiguous bytes per row per store).
 template <int KIND>   // kWD, kWG (at most 256 registers: two workgroups per CU)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_wgrad(
     BwdArgs a) {
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int mfirst = (rem % mgs) * kMB, mend = min(mb, mfirst + kMB);
   const int cnt = a.counts[e], rbase = a.offsets[e];
   const int nchunks = (cnt + kKC - 1) / kKC;
-  const bool bres = nchunks == 1;
+  const bool bres = nchunks <= 2;                     // B chunk ch stays in LDS slot ch
   uint16_t* const out = KIND == kWD ? a.dwd + static_cast<size_t>(e) * H * I
                                     : a.dwgu + static_cast<size_t>(e) * 2 * I * H;
   const uint16_t* const Ab = KIND == kWD ? a.dout : a.dgu;
@@ -418,9 +423,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  auto stage = [&](int buf, bool with_b) {
+  auto stage = [&](int buf, int bslot, bool with_b) {
     uint16_t* ab = As + buf * 128 * kKC;
-    uint16_t* bb = Bs + buf * 128 * kKC;
+    uint16_t* bb = Bs + bslot * 128 * kKC;
     const i32x4 zero = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -483,20 +488,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   rows_for(0);
   load(mfirst, true);
-  stage(0, true);
+  stage(0, 0, true);
   __syncthreads();
   for (int it = 0; it < total; ++it) {
     const int mq = it / nchunks;
     const int mi = mfirst + mq, ch = it - mq * nchunks;
     const int buf = it & 1;
     const bool more = it + 1 < total;
+    const int mq1 = (it + 1) / nchunks, ch1 = it + 1 - mq1 * nchunks;
+    // B is loaded for every chunk, or (resident) only during the first row block
+    const bool nb_load = !bres || mq1 == 0;
     if (more) {
-      const int mq1 = (it + 1) / nchunks;
-      if (!bres) rows_for(it + 1 - mq1 * nchunks);
-      load(mfirst + mq1, !bres);
+      if (nchunks > 1) rows_for(ch1);
+      load(mfirst + mq1, nb_load);
     }
     const uint16_t* ab = As + buf * 128 * kKC;
-    const uint16_t* bb = Bs + (bres ? 0 : buf) * 128 * kKC;
+    const uint16_t* bb = Bs + (bres ? ch : buf) * 128 * kKC;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int c = 4 * s2 + fg;
@@ -514,7 +521,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (ch == nchunks - 1) store_tile(mi);
     if (more) {
-      stage(buf ^ 1, !bres);
+      stage(buf ^ 1, bres ? ch1 : buf ^ 1, nb_load);
       __syncthreads();
     }
   }
@@ -633,7 +640,12 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   const int P = T * k;
   int* row_of = reinterpret_cast<int*>(b + L.row_of);
 
-  hipError_t err = launch_group_experts(idx, P, E, kBB, const_cast<int*>(a.counts),
+  // 128-row M-tiles once experts average 48 routed rows or more: an expert's
+  // weights are then streamed once per tile for up to 128 rows (fewer second
+  // tiles); below that most experts fit one 64-row tile, and the taller tile only
+  // adds staging (measured: slower at ~43 rows per expert)
+  const bool tall = P >= 48LL * E;
+  hipError_t err = launch_group_experts(idx, P, E, tall ? 128 : kBB, const_cast<int*>(a.counts),
                                         const_cast<int*>(a.offsets), const_cast<int2*>(a.tiles),
                                         const_cast<int*>(a.n_tiles), const_cast<int*>(a.perm),
                                         row_of, s);
@@ -647,14 +659,17 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   };
   if (!gu_saved) {
     prof_begin(kBwdGateUp, s);
-    hipLaunchKernelGGL(bwd_gemm<kGU>, grid_tiles(2 * I), dim3(256), 0, s, a);
+    if (tall) hipLaunchKernelGGL((bwd_gemm<kGU, 128>), grid_tiles(2 * I), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((bwd_gemm<kGU, 64>), grid_tiles(2 * I), dim3(256), 0, s, a);
     prof_end(kBwdGateUp, s);
   }
   prof_begin(kBwdDown, s);
-  hipLaunchKernelGGL(bwd_gemm<kDD>, grid_tiles(I), dim3(256), 0, s, a);
+  if (tall) hipLaunchKernelGGL((bwd_gemm<kDD, 128>), grid_tiles(I), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((bwd_gemm<kDD, 64>), grid_tiles(I), dim3(256), 0, s, a);
   prof_end(kBwdDown, s);
   prof_begin(kBwdInput, s);
-  hipLaunchKernelGGL(bwd_gemm<kDG>, grid_tiles(H), dim3(256), 0, s, a);
+  if (tall) hipLaunchKernelGGL((bwd_gemm<kDG, 128>), grid_tiles(H), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((bwd_gemm<kDG, 64>), grid_tiles(H), dim3(256), 0, s, a);
   if (k > 1) hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, a.dxs, row_of, T, H, k, dx);
   prof_end(kBwdInput, s);
   prof_begin(kBwdWDown, s);
