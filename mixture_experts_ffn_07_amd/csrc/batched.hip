@@ -664,10 +664,29 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
     prof_end(kGemmGateUp, s);
     return e;
   }
-  // 16 waves x 16 neurons = 256 neurons per workgroup (I is a multiple of 256)
+  // 16 waves x 16 neurons = 256 neurons per workgroup (I is a multiple of 256);
+  // when that gives fewer than four workgroups per CU (decode-sized batches: about
+  // one M-tile per touched expert) 8 waves x 16 neurons instead, twice the items
+  const bool narrow = (I / 256) * L.max_tiles < 4 * num_cus;
   const int n_items = round_up((I / 256) * L.max_tiles, kXcds);
+  const int n_items8 = round_up((I / 128) * L.max_tiles, kXcds);
   prof_begin(kGemmGateUp, s);
-  if (dtype == 0 && gu)
+  if (narrow && dtype == 0 && gu)
+    hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 8>), dim3(n_items8), dim3(512), 0, s,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
+                       p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
+                       static_cast<uint16_t*>(h), nullptr, nullptr, gu);
+  else if (narrow && dtype == 0)
+    hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 8>), dim3(n_items8), dim3(512), 0, s,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
+                       p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
+                       static_cast<uint16_t*>(h), nullptr, nullptr, nullptr);
+  else if (narrow)
+    hipLaunchKernelGGL((gemm_mx_s<kProjGateUp, 8>), dim3(n_items8), dim3(512), 0, s,
+                       static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
+                       p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
+                       static_cast<uint8_t*>(h), hs, nullptr, nullptr);
+  else if (dtype == 0 && gu)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
@@ -716,9 +735,10 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   }
   // output dims per workgroup: BF16 8 waves x 32, two workgroups per CU (a CU stays
   // busy while one of them starts its next item: measured ~4% faster than one
-  // 16-wave workgroup); MXFP8 16 waves x 32 (8 x 32 when H is not a multiple of
-  // 512), where the 8-wave form measured slower
-  const bool wide = dtype == 1 && H % 512 == 0;
+  // 16-wave workgroup); MXFP8 16 waves x 32, where the 8-wave form measured slower
+  // on large batches (8 x 32 when H is not a multiple of 512, or when 16-wave
+  // items would leave fewer than four workgroups per CU)
+  const bool wide = dtype == 1 && H % 512 == 0 && (H / 512) * L.max_tiles >= 4 * num_cus;
   const int dims = wide ? 512 : 256;
   const int n_items = round_up((H / dims) * L.max_tiles, kXcds);
   const dim3 grid(n_items), block(2 * dims);
