@@ -46,16 +46,16 @@ CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 # as null until the counters are taken again.
 TRAFFIC = {
     ("decode_gate_up", "qwen3-decode-T32"): (
-        705.8e6, ('decode.hip', 'common.h', 'internal.h'), "edd61e3d43a019b8",
+        705.8e6, ('decode.hip', 'common.h', 'internal.h'), "679afa22cc65e07f",
         "profiles/decode_gate_up_qwen3-decode-T32.md"),
     ("gemm_gate_up", "kimi-bf16-T2048"): (
-        22998.9e6, ('batched.hip', 'common.h', 'tiles.h'), "aaa3c811e47a61e4",
+        22995.8e6, ('batched.hip', 'common.h', 'tiles.h'), "cce191cd9049f4c3",
         "profiles/gemm_gate_up_kimi-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
-        2576.2e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "70d9b3c6a25bfac1",
+        2580.2e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "70d9b3c6a25bfac1",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
-        23708.6e6, ('backward.hip', 'common.h', 'tiles.h'), "933da455364ed6ec",
+        23710.1e6, ('backward.hip', 'common.h', 'tiles.h'), "63d2f0301b2be2dd",
         "profiles/bwd_wgate_up_kimi-bf16-T2048.md"),
 }
 
@@ -270,9 +270,10 @@ def backward_algorithmic(cfg, U):
     slots = (P * H * 4 * 2 + T * H * 2) if k > 1 else T * H * 2
     return {
         "bwd_gate_up": (wgu + T * H * 2 + P * 2 * I * 4, 2.0 * P * 2 * I * H),
-        "bwd_down": (wd + T * H * 2 + P * 2 * I * 4 + P * 2 * I * 2, 2.0 * P * H * I),
+        # reads W_down, dout, [g; u]; writes [dg; du] and w * a (both BF16)
+        "bwd_down": (wd + T * H * 2 + P * 2 * I * 4 + P * 2 * I * 2 + P * I * 2, 2.0 * P * H * I),
         "bwd_input": (wgu + P * 2 * I * 2 + slots, 2.0 * P * 2 * I * H),
-        "bwd_wdown": (T * H * 2 + P * 2 * I * 4 + E * H * I * 2, 2.0 * P * H * I),
+        "bwd_wdown": (T * H * 2 + P * I * 2 + E * H * I * 2, 2.0 * P * H * I),
         "bwd_wgate_up": (P * 2 * I * 2 + T * H * 2 + E * 2 * I * H * 2, 2.0 * P * 2 * I * H),
     }
 
