@@ -46,7 +46,7 @@ CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 # as null until the counters are taken again.
 TRAFFIC = {
     ("decode_gate_up", "qwen3-decode-T32"): (
-        705.8e6, ('decode.hip', 'common.h', 'internal.h'), "679afa22cc65e07f",
+        705.8e6, ('decode.hip', 'common.h', 'internal.h'), "3b4fe63a63b2ee54",
         "profiles/decode_gate_up_qwen3-decode-T32.md"),
     ("gemm_gate_up", "kimi-bf16-T2048"): (
         22995.8e6, ('batched.hip', 'common.h', 'tiles.h'), "cce191cd9049f4c3",

@@ -975,14 +975,17 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   // gate_up: T <= 32 takes the narrow kernel (8-token tiles, full-line streamed
   // weights); T > 32 the wide one (16-token tiles)
   const int TM8 = T <= 8 ? 1 : (T <= 16 ? 2 : 4);
-  // register budget (128 per lane): weights of two tasks + 16*NG accumulators per tile
-  const int NG = TM8 <= 2 ? 2 : 1;
+  // register budget (128 per lane): weights of two tasks + 16*NG accumulators per tile;
+  // one 8-neuron group per item when 16-neuron items would number fewer than two per
+  // CU (T = 1: 8 experts x 48 items): the finer items even out the last round
+  const long pairs_u = T * k < E ? T * k : E;
+  const int NG = TM8 <= 2 && pairs_u * (I / 16) >= 2L * num_cus ? 2 : 1;
   const int S = H / 64;                             // a multiple of 4
   // two steps per chunk when every wave's step count is even and registers allow
   const int KC = (S % 16 == 0 && (TM8 == 1 || TM8 == 4)) ? 2 : 1;
   const int gsteps = H / kDecWaves / 32;            // wide kernel: steps of 32 per wave
   const int KCW = gsteps % 2 == 0 ? 2 : 1;
-  const long items_upper = static_cast<long>(T * k < E ? T * k : E) * (I / (wide ? 16 : 8 * NG));
+  const long items_upper = pairs_u * (I / (wide ? 16 : 8 * NG));
   const long grid_cap = 2L * num_cus;
   const int grid1 = static_cast<int>(items_upper < grid_cap ? items_upper : grid_cap);
   // reduction buffer; the plan scratch (E masks + chunk offsets) must fit in it too;
@@ -1019,10 +1022,14 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
                        idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw);
   } else if (wide) {
     if (KCW == 2) GU_WIDE(2); else GU_WIDE(1);
-  } else if (TM8 == 1) {
+  } else if (TM8 == 1 && NG == 2) {
     if (KC == 2) GU_LAUNCH(1, 2, 2); else GU_LAUNCH(1, 2, 1);
-  } else if (TM8 == 2) {
+  } else if (TM8 == 1) {
+    if (KC == 2) GU_LAUNCH(1, 1, 2); else GU_LAUNCH(1, 1, 1);
+  } else if (TM8 == 2 && NG == 2) {
     GU_LAUNCH(2, 2, 1);
+  } else if (TM8 == 2) {
+    GU_LAUNCH(2, 1, 1);
   } else {
     if (KC == 2) GU_LAUNCH(4, 1, 2); else GU_LAUNCH(4, 1, 1);
   }
