@@ -52,7 +52,7 @@ TRAFFIC = {
         22995.8e6, ('batched.hip', 'common.h', 'tiles.h'), "cce191cd9049f4c3",
         "profiles/gemm_gate_up_kimi-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
-        2580.2e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "70d9b3c6a25bfac1",
+        1958.4e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "616261e8e59703ae",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
         23710.1e6, ('backward.hip', 'common.h', 'tiles.h'), "63d2f0301b2be2dd",

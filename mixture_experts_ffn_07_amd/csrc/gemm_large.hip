@@ -55,6 +55,22 @@ __device__ __forceinline__ TailPlan tail_plan(int n_real, int ncu, int nk) {
   return p;
 }
 
+// Item order.  Items are (M-tile, N-block) pairs; an XCD runs a contiguous run
+// of item numbers, 32 at a time.  Numbering N-blocks fastest would make those
+// 32 one or two M-tiles against ~32 different weight blocks (about 34 distinct
+// operand blocks per K stage in the XCD's L2); numbering groups of
+// kLargeGroupM M-tiles with the M-tile fastest makes them 4 M-tiles x 8
+// N-blocks (12 distinct blocks), so each staged block is shared by more CUs.
+constexpr int kLargeGroupM = 4;
+__device__ __forceinline__ void large_coords(int item, int nblk, int n_tiles, int& tile, int& nb) {
+  const int grp = item / (kLargeGroupM * nblk);
+  const int r = item - grp * kLargeGroupM * nblk;
+  const int t0 = grp * kLargeGroupM;
+  const int gm = min(kLargeGroupM, n_tiles - t0);
+  nb = r / gm;
+  tile = t0 + (r - nb * gm);
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -147,7 +163,8 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     item = real_item(L, nblk, *n_tiles);
     if (item < 0) return;
   }
-  const int tile = item / nblk, nb = item - tile * nblk;
+  int tile, nb;
+  large_coords(item, nblk, *n_tiles, tile, nb);
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
   const int mcount = min(kLargeBM, counts[e] - m0);
@@ -303,7 +320,8 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
   const int tid = f & 255, ijq = f >> 8;     // GEMM thread and register block
   const int i = ijq >> 4, j = (ijq >> 2) & 3, q = ijq & 3;
   const int item = plan.full + b;
-  const int tile = item / nblk, nb = item - tile * nblk;
+  int tile, nb;
+  large_coords(item, nblk, *n_tiles, tile, nb);
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
   const int mcount = min(kLargeBM, counts[e] - m0);
@@ -428,7 +446,8 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
     item = real_item(L, nblk, *n_tiles);
     if (item < 0) return;
   }
-  const int tile = item / nblk, nb = item - tile * nblk;
+  int tile, nb;
+  large_coords(item, nblk, *n_tiles, tile, nb);
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
   const int mcount = min(kLargeBM, counts[e] - m0);
@@ -613,7 +632,8 @@ __global__ __launch_bounds__(256) void gemm_large_mx_fixup_gate_up(
   const int b = blockIdx.x >> 3, i = (blockIdx.x >> 2) & 1, j = blockIdx.x & 3;
   if (plan.S == 1 || b >= plan.rem) return;
   const int item = plan.full + b;
-  const int tile = item / nblk, nb = item - tile * nblk;
+  int tile, nb;
+  large_coords(item, nblk, *n_tiles, tile, nb);
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
   const int mcount = min(kLargeBM, counts[e] - m0);
