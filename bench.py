@@ -51,6 +51,9 @@ TRAFFIC = {
     ("gemm_gate_up", "kimi-bf16-T2048"): (
         22995.8e6, ('batched.hip', 'common.h', 'tiles.h'), "cce191cd9049f4c3",
         "profiles/gemm_gate_up_kimi-bf16-T2048.md"),
+    ("gemm_gate_up", "glm-bf16-T2048"): (
+        13213.0e6, ('batched.hip', 'common.h', 'tiles.h'), "6c6a697ae8f717b2",
+        "profiles/gemm_gate_up_glm-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
         1958.4e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "616261e8e59703ae",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),

@@ -30,6 +30,7 @@ namespace moe {
 
 namespace {
 constexpr int kBM = 64;            // rows (routed pairs) per M-tile
+constexpr int kTallBM = 128;       // BF16, experts averaging 48+ rows
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 }  // namespace
@@ -43,7 +44,10 @@ bool use_large_tiles(int T, int H, int I, int E, int k, int dtype) {
 BatchedWs batched_ws_layout(int T, int H, int I, int E, int k, int dtype) {
   BatchedWs L{};
   const size_t P = static_cast<size_t>(T) * k;
-  L.bm = use_large_tiles(T, H, I, E, k, dtype) ? kLargeBM : kBM;
+  // BF16 takes 128-row tiles when experts average 48 routed rows or more (with
+  // 64-row tiles about half of them would stream their weights twice)
+  L.bm = use_large_tiles(T, H, I, E, k, dtype) ? kLargeBM
+         : dtype == 0 && P >= 48 * static_cast<size_t>(E) ? kTallBM : kBM;
   L.max_tiles = static_cast<int>(E + (P + L.bm - 1) / L.bm);
   size_t o = 0;
   L.n_tiles = o;   o += 256;
@@ -163,18 +167,26 @@ constexpr int kSXC = 128;                // K chunk of the staged activations
 constexpr int kSXRS = kSXC + 8;          // padded LDS row stride (elements)
 enum { kProjGateUp = 0, kProjDown = 1, kProjDownFused = 2, kProjGateUpSave = 3 };
 
-template <int KIND, int NW>   // (128 registers: with NW = 8, two workgroups share a CU)
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemm_bf16s(
+// BM = 128 (experts averaging 48 routed rows or more, where 64-row tiles would
+// stream about half the experts' weights twice): the tile's 128 rows in eight
+// 16-row groups, and each wave owns ONE group of 16 weight rows - gate_up: 8
+// neurons' gate rows then their up rows, so a lane pairs its gate values with
+// the up values of lane + 32; down: 16 output dimensions - which keeps the
+// accumulators (and registers) of the 64-row form.
+template <int KIND, int NW, int BM = 64, int NGW = 2>   // (128 registers: with NW = 8, two workgroups share a CU)
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 128 && NGW == 2 ? 2 : 4, 8))) void gemm_bf16s(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ wt,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint16_t* __restrict__ hout, float* __restrict__ y,
     uint16_t* __restrict__ out, float* __restrict__ gu) {
   constexpr bool GU = KIND == kProjGateUp || KIND == kProjGateUpSave;
+  constexpr bool ONE = NGW == 1;         // one 16-row weight group per wave
   constexpr int NT = NW * 64;
-  constexpr int RPW = GU ? 16 : 32;      // outputs per wave
-  constexpr int LPT = kBM * (kSXC / 8) / NT;              // 16-byte activation loads per thread
-  __shared__ __align__(16) uint16_t xs[2][kBM * kSXRS];
+  constexpr int G = BM / 16;             // 16-row groups of the tile
+  constexpr int RPW = (GU ? 16 : 32) * NGW / 2;           // outputs per wave
+  constexpr int LPT = BM * (kSXC / 8) / NT;               // 16-byte activation loads per thread
+  __shared__ __align__(16) uint16_t xs[2][BM * kSXRS];
   __shared__ __align__(16) i32x4 wtl[NW][16 * 8];         // per wave: [16 rows][8 chunks]
   const int K = GU ? H : I;              // reduction length
   const int N = GU ? I : H;              // outputs
@@ -184,21 +196,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const int tile = item / nblk, nb_i = item - tile * nblk;
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
-  const int mcount = min(kBM, counts[e] - m0);
+  const int mcount = min(BM, counts[e] - m0);
   const int rbase = offsets[e] + m0;
   const int tid = threadIdx.x, ln = tid & 63, col = ln & 15, grp = ln >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = nb_i * NW * RPW + wv * RPW;              // the wave's first output
-  // the wave's two 16-row weight groups
-  const int row0 = nb, row1 = GU ? I + nb : nb + 16;
+  // the wave's 16-row weight groups (BM 64: two; BM 128: one, rows 0-7 from row0
+  // and rows 8-15 from row1)
+  const int row0 = nb, row1 = GU ? I + nb : nb + (ONE ? 8 : 16);
 
   // whole-line loads: lane = (row lr of an 8-row group, 16-byte chunk lc)
   const int lr = ln >> 3, lc = ln & 7;
   const uint16_t* __restrict__ wb = wt + static_cast<size_t>(e) * (GU ? 2 * I : H) * K;
-  uint32_t ow[4];                                         // group 0 rows 0-7, 8-15, group 1 rows 0-7, 8-15
+  constexpr int NWL = 2 * NGW;                            // 8-row weight loads per step
+  uint32_t ow[NWL];                                       // BM 64: group 0 rows 0-7, 8-15, group 1 rows 0-7, 8-15
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    ow[i] = static_cast<uint32_t>(((i < 2 ? row0 : row1) + 8 * (i & 1) + lr) * K + lc * 8);
+  for (int i = 0; i < NWL; ++i)
+    ow[i] = ONE ? static_cast<uint32_t>(((i == 0 ? row0 : row1) + lr) * K + lc * 8)
+                 : static_cast<uint32_t>(((i < 2 ? row0 : row1) + 8 * (i & 1) + lr) * K + lc * 8);
   i32x4* tw = wtl[wv];
   i32x4* wdst = tw + lr * 8 + (lc ^ lr);                  // + 64 for rows 8-15
   // A lane (row col, group grp), 32-half hh: chunk 4*hh + grp of row col
@@ -221,41 +236,62 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 #pragma unroll
   for (int i = 0; i < LPT; ++i) *reinterpret_cast<i32x4*>(&xs[0][lrow[i]]) = xr[i];
 
-  f32x4 acc0[4], acc1[4];                                 // [row group g of the tile]
+  f32x4 acc0[G], acc1[ONE ? 1 : G];                       // [row group g of the tile]
 #pragma unroll
-  for (int g = 0; g < 4; ++g) acc0[g] = acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < G; ++g) acc0[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < (ONE ? 1 : G); ++g) acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nsteps = K / 64;
-  i32x4 wA[4], wB[4];
+  i32x4 wA[NWL], wB[NWL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) wA[i] = ld16_stream(wb + ow[i]);
+  for (int i = 0; i < NWL; ++i) wA[i] = ld16_stream(wb + ow[i]);
   __syncthreads();
 
   // one 64-position step: weights W (already loaded), activations from xs[buf] at
   // chunk offset st*64
-  auto step = [&](const i32x4 (&W)[4], int buf, int st) {
+  auto step = [&](const i32x4 (&W)[NWL], int buf, int st) {
     const uint16_t* xb = &xs[buf][col * kSXRS + st * 64 + grp * 8];
-    bf16x8 bx[4][2];
+    if (!ONE) {
+      bf16x8 bx[G][2];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        bx[g][hh] = as_bf16x8(*reinterpret_cast<const i32x4*>(xb + 16 * g * kSXRS + hh * 32));
+        for (int hh = 0; hh < 2; ++hh)
+          bx[g][hh] = as_bf16x8(*reinterpret_cast<const i32x4*>(xb + 16 * g * kSXRS + hh * 32));
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {                         // row group 0, then 1
-      wdst[0] = W[2 * m];
-      wdst[64] = W[2 * m + 1];
+      for (int m = 0; m < 2; ++m) {                       // row group 0, then 1
+        wdst[0] = W[2 * m];
+        wdst[64] = W[2 * m + 1];
+        __builtin_amdgcn_wave_barrier();
+        bf16x8 a[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) a[hh] = as_bf16x8(asrc[(4 * hh + grp) ^ sw]);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            if (m == 0) acc0[g] = mfma16x16x32(a[hh], bx[g][hh], acc0[g]);
+            else acc1[(ONE ? 0 : g)] = mfma16x16x32(a[hh], bx[g][hh], acc1[(ONE ? 0 : g)]);
+          }
+      }
+    } else {
+      wdst[0] = W[0];
+      wdst[64] = W[1];
       __builtin_amdgcn_wave_barrier();
       bf16x8 a[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) a[hh] = as_bf16x8(asrc[(4 * hh + grp) ^ sw]);
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < G; ++g) {
+        bf16x8 bx[2];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          if (m == 0) acc0[g] = mfma16x16x32(a[hh], bx[g][hh], acc0[g]);
-          else acc1[g] = mfma16x16x32(a[hh], bx[g][hh], acc1[g]);
-        }
+        for (int hh = 0; hh < 2; ++hh)
+          bx[hh] = as_bf16x8(*reinterpret_cast<const i32x4*>(xb + 16 * g * kSXRS + hh * 32));
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) acc0[g] = mfma16x16x32(a[hh], bx[hh], acc0[g]);
+      }
     }
   };
   const int nchunk = K / kSXC;
@@ -271,10 +307,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
     const uint32_t k1 = static_cast<uint32_t>((2 * c + 1) * 64);
     const uint32_t k2 = static_cast<uint32_t>(min(2 * c + 2, nsteps - 1) * 64);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wB[i] = ld16_stream(wb + ow[i] + k1);
+    for (int i = 0; i < NWL; ++i) wB[i] = ld16_stream(wb + ow[i] + k1);
     step(wA, buf, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wA[i] = ld16_stream(wb + ow[i] + k2);
+    for (int i = 0; i < NWL; ++i) wA[i] = ld16_stream(wb + ow[i] + k2);
     step(wB, buf, 1);
     if (more) {
 #pragma unroll
@@ -282,17 +318,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
     }
     __syncthreads();
   }
-  // epilogue: lane holds outputs nb+4grp+{0..3} (group 0) and row1+4grp+{0..3}
-  // (group 1) of tile row 16g+col
+  // epilogue.  BM 64: lane holds outputs nb+4grp+{0..3} (group 0) and
+  // row1+4grp+{0..3} (group 1) of tile row 16g+col.  BM 128: lane holds weight
+  // rows 4grp+{0..3} of the wave's group - gate_up: gate of neurons nb+4grp+i for
+  // grp < 2, up of neurons nb+4(grp-2)+i for grp >= 2; down: outputs nb+4grp+i.
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < G; ++g) {
     const int r = 16 * g + col;
-    if (r >= mcount) continue;
+    f32x4 up;
+    if (ONE && GU) {                                      // up values of lane + 32 (all lanes take part)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc0[g][i], 32, kWave);
+    } else {
+      up = acc1[ONE ? 0 : g];
+    }
+    if (r >= mcount || (ONE && GU && grp >= 2)) continue;
     if (GU) {
       uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb + 4 * grp;
       uint32_t p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = f32_to_bf16_rne(swiglu(acc0[g][i], acc1[g][i]));
+      for (int i = 0; i < 4; ++i) p[i] = f32_to_bf16_rne(swiglu(acc0[g][i], up[i]));
       uint2 v;
       v.x = p[0] | (p[1] << 16);
       v.y = p[2] | (p[3] << 16);
@@ -300,15 +345,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
       if (KIND == kProjGateUpSave) {                      // FP32 g and u of the pair, slot order
         float* gp = gu + static_cast<size_t>(perm[rbase + r]) * (2 * I) + nb + 4 * grp;
         *reinterpret_cast<f32x4*>(gp) = acc0[g];
-        *reinterpret_cast<f32x4*>(gp + I) = acc1[g];
+        *reinterpret_cast<f32x4*>(gp + I) = up;
       }
     } else if (KIND == kProjDownFused) {
       const int t = perm[rbase + r];                      // k = 1: pair id == token
       const float wt_ = w[t];
       uint16_t* orow = out + static_cast<size_t>(t) * H + nb + 4 * grp;
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const f32x4 a = m == 0 ? acc0[g] : acc1[g];
+      for (int m = 0; m < NGW; ++m) {
+        const f32x4 a = m == 0 ? acc0[g] : up;
         uint2 v;
         v.x = f32_to_bf16_rne(wt_ * a[0]) | (f32_to_bf16_rne(wt_ * a[1]) << 16);
         v.y = f32_to_bf16_rne(wt_ * a[2]) | (f32_to_bf16_rne(wt_ * a[3]) << 16);
@@ -317,7 +362,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
     } else {
       float* yr = y + static_cast<size_t>(rbase + r) * H + nb + 4 * grp;
       *reinterpret_cast<f32x4*>(yr) = acc0[g];
-      *reinterpret_cast<f32x4*>(yr + 16) = acc1[g];
+      if (!ONE) *reinterpret_cast<f32x4*>(yr + 16) = up;
     }
   }
 }
@@ -664,13 +709,29 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
     prof_end(kGemmGateUp, s);
     return e;
   }
+  prof_begin(kGemmGateUp, s);
+  if (L.bm == kTallBM) {
+    // 8 waves x 16 neurons = 128 neurons per workgroup, 128-row tiles
+    const int n_tall = round_up((I / 128) * L.max_tiles, kXcds);
+    if (gu)
+      hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 8, kTallBM>), dim3(n_tall), dim3(512), 0, s,
+                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
+                         p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
+                         static_cast<uint16_t*>(h), nullptr, nullptr, gu);
+    else
+      hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 8, kTallBM>), dim3(n_tall), dim3(512), 0, s,
+                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
+                         p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
+                         static_cast<uint16_t*>(h), nullptr, nullptr, nullptr);
+    prof_end(kGemmGateUp, s);
+    return hipGetLastError();
+  }
   // 16 waves x 16 neurons = 256 neurons per workgroup (I is a multiple of 256);
   // when that gives fewer than four workgroups per CU (decode-sized batches: about
   // one M-tile per touched expert) 8 waves x 16 neurons instead, twice the items
   const bool narrow = (I / 256) * L.max_tiles < 4 * num_cus;
   const int n_items = round_up((I / 256) * L.max_tiles, kXcds);
   const int n_items8 = round_up((I / 128) * L.max_tiles, kXcds);
-  prof_begin(kGemmGateUp, s);
   if (narrow && dtype == 0 && gu)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 8>), dim3(n_items8), dim3(512), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
@@ -753,7 +814,18 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
                      p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr,   \
                      nullptr, p.y, out)
   prof_begin(kGemmDown, s);
-  if (dtype == 0) {
+  if (L.bm == kTallBM) {
+    // 8 waves x 32 dimensions = 256 output dimensions per workgroup, 128-row tiles
+    const dim3 grid_t(round_up((H / 256) * L.max_tiles, kXcds)), block_t(512);
+#define DOWN_TALL(KINDV)                                                                    \
+    hipLaunchKernelGGL((gemm_bf16s<KINDV, 8, kTallBM>), grid_t, block_t, 0, s,              \
+                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),     \
+                       p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr, \
+                       p.y, out, nullptr)
+    if (k == 1) DOWN_TALL(kProjDownFused);
+    else DOWN_TALL(kProjDown);
+#undef DOWN_TALL
+  } else if (dtype == 0) {
     if (k == 1) DOWN_BF16(kProjDownFused, 8);
     else DOWN_BF16(kProjDown, 8);
   } else {

@@ -51,9 +51,11 @@ def _custom(T, H, I, E, k, seed=0, x_std=1.0):
 @pytest.mark.parametrize("T,H,I,E,k", [
     (1, 256, 256, 4, 2),        # one token
     (100, 512, 256, 8, 2),      # ~25 rows per expert
-    (300, 256, 512, 6, 3),      # >64 rows per expert: several M-tiles, ragged last tile
-    (257, 768, 256, 40, 8),     # many small experts, some empty; 8-wave down (H % 512 != 0)
-    (500, 512, 256, 6, 1),      # k = 1: down writes the output directly
+    (160, 256, 512, 8, 2),      # ~40 rows per expert: 64-row tiles, some experts take two
+    (300, 256, 512, 6, 3),      # ~150 rows per expert: 128-row tiles, ragged last tile
+    (700, 512, 256, 8, 2),      # ~175 rows per expert: 128-row tiles, two per expert
+    (257, 768, 256, 40, 8),     # many small experts, some empty; 128-row tiles (~51 rows avg)
+    (500, 512, 256, 6, 1),      # k = 1, 128-row tiles: down writes the output directly
     (200, 768, 512, 5, 1),      # k = 1 with the 8-wave down
     (64, 256, 256, 16, 16),     # k = E
 ])
