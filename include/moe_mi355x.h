@@ -185,9 +185,8 @@ size_t moe_workspace_bytes(int T, int H, int I, int E, int k, int dtype);
  *              (t, j), g = W_gate[e] x[t], u = W_up[e] x[t] summed in FP32
  *              (the values h was computed from); pass it to moe_backward_batched
  * moe_down_3d_batched follows with the same workspace, as after
- * moe_gate_up_3d_batched.  Limits as for moe_gate_up_3d_batched; shapes with
- * 256 or more routed rows per expert on average (the large-group GEMMs) return
- * MOE_ERR_UNSUPPORTED.
+ * moe_gate_up_3d_batched.  Limits as for moe_gate_up_3d_batched, and
+ * T*k*2I < 2^31 (MOE_ERR_SHAPE otherwise).
  */
 int moe_gate_up_3d_batched_train(const uint16_t* x, const uint16_t* w_gate_up,
                                  const int32_t* topk_idx, int T, int H, int I, int E, int k,

@@ -283,11 +283,6 @@ int moe_gate_up_3d_batched_train(const uint16_t* x, const uint16_t* w_gate_up,
   if (int st = check_batched(T, H, I, E, k, MOE_BF16, workspace, workspace_bytes)) return st;
   if (!x || !w_gate_up || !topk_idx || !h || !gu)
     return fail(MOE_ERR_NULL, "x, w_gate_up, topk_idx, h and gu are required");
-  if (moe::use_large_tiles(T, H, I, E, k, MOE_BF16))
-    return fail(MOE_ERR_UNSUPPORTED,
-                "T*k=%lld routed rows over E=%d experts: the large-group GEMMs do not keep "
-                "the pre-activations",
-                static_cast<long long>(T) * k, E);
   if (static_cast<long long>(T) * k * 2 * I >= (1LL << 31))
     return fail(MOE_ERR_SHAPE, "T*k*2I reaches 2^31");
   if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(topk_idx) || !aligned16(h) ||

@@ -700,7 +700,8 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
             ? launch_gate_up_large_bf16(static_cast<const uint16_t*>(x),
                                         static_cast<const uint16_t*>(wgu), p.perm, p.tiles,
                                         p.n_tiles, p.counts, p.offsets, H, I, k,
-                                        static_cast<uint16_t*>(h), p.partial, L.max_tiles, num_cus, s)
+                                        static_cast<uint16_t*>(h), p.partial, L.max_tiles, num_cus, s,
+                                        gu)
             : launch_gate_up_large_mx(static_cast<const uint8_t*>(x), xs,
                                       static_cast<const uint8_t*>(wgu), wgus, p.perm, p.tiles,
                                       p.n_tiles, p.counts, p.offsets, H, I, k,

@@ -33,7 +33,7 @@ namespace {
 constexpr int kLBK = 64;                     // K per stage
 constexpr int kLTile = kLargeBM * kLBK;      // elements per operand stage (256 rows x 64)
 constexpr size_t kLLds = 2 * 2 * kLTile * sizeof(uint16_t);   // 128 KB
-enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2 };
+enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2, kGateUpSave = 3 };
 
 // Tail split.  One workgroup fills a CU, so n items run in ceil(n / ncu)
 // rounds; when the last round would leave more than half of the CUs idle, its
@@ -84,13 +84,26 @@ __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const 
                                                const float* __restrict__ w, int H, int I, int rbase,
                                                int mcount, int nb, int wm, int wn, int l32, int hi,
                                                uint16_t* __restrict__ hout, float* __restrict__ y,
-                                               uint16_t* __restrict__ out) {
+                                               uint16_t* __restrict__ out, float* __restrict__ gu) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = wm * 128 + 32 * j + l32;
     if (r >= mcount) continue;
-    if (KIND == kGateUp) {
+    if (KIND == kGateUp || KIND == kGateUpSave) {
       uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb * 128 + wn * 64 + 4 * hi;
+      if (KIND == kGateUpSave) {                 // FP32 g and u of the pair, slot order
+        float* gp = gu + static_cast<size_t>(perm[rbase + r]) * (2 * I) + nb * 128 + wn * 64 + 4 * hi;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<f32x4*>(gp + 32 * i + 8 * q) =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            *reinterpret_cast<f32x4*>(gp + I + 32 * i + 8 * q) =
+                f32x4{acc[i + 2][j][4 * q], acc[i + 2][j][4 * q + 1], acc[i + 2][j][4 * q + 2],
+                      acc[i + 2][j][4 * q + 3]};
+          }
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -139,9 +152,9 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint16_t* __restrict__ hout, float* __restrict__ y,
-    uint16_t* __restrict__ out, float* __restrict__ partial, int ncu) {
+    uint16_t* __restrict__ out, float* __restrict__ partial, int ncu, float* __restrict__ gu) {
   extern __shared__ __align__(16) uint16_t lds[];   // [stage][A, B][256 x 64]
-  constexpr bool kGU = KIND == kGateUp;
+  constexpr bool kGU = KIND == kGateUp || KIND == kGateUpSave;
   const int K = kGU ? H : I;
   const int nblk = kGU ? I / 128 : H / 256;
   const int nk = K / kLBK;
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
               f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     return;
   }
-  large_epilogue<KIND>(acc, perm, w, H, I, rbase, mcount, nb, wm, wn, l32, hi, hout, y, out);
+  large_epilogue<KIND>(acc, perm, w, H, I, rbase, mcount, nb, wm, wn, l32, hi, hout, y, out, gu);
 }
 
 // Tail fix-up, element-parallel: thread g of the grid takes one f32x4 of the
@@ -308,8 +321,8 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, uint16_t* __restrict__ hout, float* __restrict__ y, uint16_t* __restrict__ out,
-    const float* __restrict__ partial, int ncu, int nk) {
-  constexpr bool kGU = KIND == kGateUp;
+    const float* __restrict__ partial, int ncu, int nk, float* __restrict__ gu) {
+  constexpr bool kGU = KIND == kGateUp || KIND == kGateUpSave;
   constexpr int kPerItem = kGU ? 32 * 256 : 64 * 256;   // threads per tail item
   const int nblk = kGU ? I / 128 : H / 256;
   const TailPlan plan = tail_plan(nblk * *n_tiles, ncu, nk);
@@ -339,6 +352,12 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
   }
   if (kGU) {
     uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb * 128 + wn * 64 + 32 * i + 8 * q + 4 * hi;
+    if (KIND == kGateUpSave) {                   // FP32 g and u of the pair, slot order
+      float* gp = gu + static_cast<size_t>(perm[rbase + r]) * (2 * I) + nb * 128 + wn * 64 + 32 * i +
+                  8 * q + 4 * hi;
+      *reinterpret_cast<f32x4*>(gp) = a;
+      *reinterpret_cast<f32x4*>(gp + I) = u;
+    }
     uint32_t p[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) p[t] = f32_to_bf16_rne(swiglu(a[t], u[t]));
@@ -615,7 +634,7 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
       for (int i = 0; i < 2; ++i) mx_store_block(acc[i][j], acc[i + 2][j], wm * 128 + 32 * j + l32, mcount,
                                                  rbase, n0 + wn * 64 + 32 * i, hi, I, hq, hs);
   } else {
-    large_epilogue<KIND>(acc, perm, w, H, I, rbase, mcount, nb, wm, wn, l32, hi, nullptr, y, out);
+    large_epilogue<KIND>(acc, perm, w, H, I, rbase, mcount, nb, wm, wn, l32, hi, nullptr, y, out, nullptr);
   }
 }
 
@@ -668,14 +687,18 @@ int large_grid(int nblk, int max_tiles, int ncu) {
 hipError_t launch_gate_up_large_bf16(const uint16_t* x, const uint16_t* wgu, const int* perm,
                                      const int2* tiles, const int* n_tiles, const int* counts,
                                      const int* offsets, int H, int I, int k, uint16_t* h,
-                                     float* partial, int max_tiles, int ncu, hipStream_t s) {
+                                     float* partial, int max_tiles, int ncu, hipStream_t s,
+                                     float* gu) {
   const int grid = large_grid(I / 128, max_tiles, ncu);
-  hipLaunchKernelGGL(gemm_large_bf16<kGateUp>, dim3(grid), dim3(256), kLLds, s, x, wgu, perm,
-                     tiles, n_tiles, counts, offsets, nullptr, H, I, k, h, nullptr, nullptr,
-                     partial, ncu);
-  hipLaunchKernelGGL(gemm_large_fixup<kGateUp>, dim3(ncu / 2 * 32), dim3(256), 0, s, perm, tiles,
-                     n_tiles, counts, offsets, nullptr, H, I, h, nullptr, nullptr, partial, ncu,
-                     H / kLBK);
+#define LARGE_GU(KG)                                                                          \
+  hipLaunchKernelGGL(gemm_large_bf16<KG>, dim3(grid), dim3(256), kLLds, s, x, wgu, perm,       \
+                     tiles, n_tiles, counts, offsets, nullptr, H, I, k, h, nullptr, nullptr,  \
+                     partial, ncu, gu);                                                       \
+  hipLaunchKernelGGL(gemm_large_fixup<KG>, dim3(ncu / 2 * 32), dim3(256), 0, s, perm, tiles,   \
+                     n_tiles, counts, offsets, nullptr, H, I, h, nullptr, nullptr, partial, ncu, \
+                     H / kLBK, gu)
+  if (gu) { LARGE_GU(kGateUpSave); } else { LARGE_GU(kGateUp); }
+#undef LARGE_GU
   return hipGetLastError();
 }
 
@@ -687,9 +710,11 @@ hipError_t launch_down_large_bf16(const uint16_t* h, const uint16_t* wd, const i
   const int grid = large_grid(H / 256, max_tiles, ncu);
 #define LARGE_DOWN(KD)                                                                        \
   hipLaunchKernelGGL(gemm_large_bf16<KD>, dim3(grid), dim3(256), kLLds, s, h, wd, perm, tiles, \
-                     n_tiles, counts, offsets, w, H, I, k, nullptr, y, out, partial, ncu);    \
+                     n_tiles, counts, offsets, w, H, I, k, nullptr, y, out, partial, ncu,     \
+                     nullptr);                                                                \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
-                     n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kLBK)
+                     n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kLBK, \
+                     nullptr)
   if (k == 1) { LARGE_DOWN(kDownFused); } else { LARGE_DOWN(kDownSlots); }
 #undef LARGE_DOWN
   return hipGetLastError();
@@ -720,7 +745,8 @@ hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint
                      perm, tiles, n_tiles, counts, offsets, w, H, I, k, nullptr, nullptr, y,  \
                      out, partial, ncu);                                                      \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
-                     n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kMBK)
+                     n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kMBK, \
+                     nullptr)
   if (k == 1) { LARGE_DOWN_MX(kDownFused); } else { LARGE_DOWN_MX(kDownSlots); }
 #undef LARGE_DOWN_MX
   return hipGetLastError();
@@ -730,6 +756,9 @@ hipError_t large_set_attributes() {
   const int bytes = static_cast<int>(kLLds);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kGateUp>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kGateUpSave>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kDownFused>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);

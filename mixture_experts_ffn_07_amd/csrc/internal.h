@@ -59,7 +59,8 @@ bool use_large_tiles(int T, int H, int I, int E, int k, int dtype);
 hipError_t launch_gate_up_large_bf16(const uint16_t* x, const uint16_t* wgu, const int* perm,
                                      const int2* tiles, const int* n_tiles, const int* counts,
                                      const int* offsets, int H, int I, int k, uint16_t* h,
-                                     float* partial, int max_tiles, int ncu, hipStream_t s);
+                                     float* partial, int max_tiles, int ncu, hipStream_t s,
+                                     float* gu);   // gu: also keep the FP32 pre-activations
 hipError_t launch_down_large_bf16(const uint16_t* h, const uint16_t* wd, const int* perm,
                                   const int2* tiles, const int* n_tiles, const int* counts,
                                   const int* offsets, const float* w, int H, int I, int k,

@@ -168,6 +168,6 @@ def test_train_forward_validation(m):
     assert call(I=128) == m.MOE_ERR_SHAPE
     assert call(wsb=need - 1) == m.MOE_ERR_WORKSPACE
     assert call(gu=FAKE + 4) == m.MOE_ERR_ALIGN
-    # >= 256 routed rows per expert on average: the large-group GEMMs keep nothing
-    big = m.lib.moe_workspace_bytes(4096, 256, 256, 2, 1, 0)
-    assert call(T=4096, E=2, k=1, wsb=big) == m.MOE_ERR_UNSUPPORTED
+    # T*k*2I must stay below 2^31 (pair-row offsets of gu are 32-bit)
+    huge = m.lib.moe_workspace_bytes(1 << 20, 256, 1024, 8, 1, 0)
+    assert call(T=1 << 20, I=1024, k=1, wsb=huge) == m.MOE_ERR_SHAPE

@@ -127,12 +127,25 @@ def test_train_forward_matches_forward_and_oracle(M):
     _fp32(gu, ref, 1e-5, "train forward gu")
 
 
-def test_train_forward_rejects_large_groups(M):
-    d = _custom(4096, 256, 256, 2, 1, seed=2)
-    idx, _ = M.moe_route_topk(d["logits"], 1)
-    with pytest.raises(M.MoeError) as ei:
-        M.moe_gate_up_3d_batched_train(d["x"], d["w_gate_up"], idx, 1)
-    assert ei.value.status == M.MOE_ERR_UNSUPPORTED
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (1100, 512, 256, 4, 1),     # large-group GEMMs, last round cut along K (fix-up epilogue)
+    (600, 256, 512, 2, 2),      # k = 2, ragged last tile
+])
+def test_train_forward_large_groups(M, T, H, I, E, k):
+    # >= 256 routed rows per expert: the large-group gate_up keeps the pre-activations
+    # too, in its own epilogue and in the fix-up of the K-split tail
+    d = _custom(T, H, I, E, k, seed=T + 3)
+    cfg = d["cfg"]
+    idx, w = M.moe_route_topk(d["logits"], cfg.k)
+    h0, _, ws0 = M.moe_gate_up_3d_batched(d["x"], d["w_gate_up"], idx, cfg.k)
+    h1, gu, ws1 = M.moe_gate_up_3d_batched_train(d["x"], d["w_gate_up"], idx, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(h0.view(torch.int16), h1.view(torch.int16))
+    from tests._gpu import oracle
+    _, inter = oracle(d, return_intermediates=True)
+    ref = inter["gu"].reshape(cfg.T * cfg.k, 2 * cfg.I)
+    _fp32(gu, ref, 1e-5, "train forward gu (large groups)")
+    _check(M, d, f"bwd saved, large groups T={T} k={k}", saved=True)
 
 
 def test_backward_bit_identical_repeats(M):
