@@ -602,6 +602,18 @@ BackwardWs backward_ws_layout(int T, int H, int I, int E, int k) {
   L.dwp = o;      o = align256(o + sizeof(float) * P * (I / kNT));
   L.dxs = o;
   if (k > 1) o = align256(o + sizeof(float) * P * H);
+  // >= 256 routed rows per expert on average: the weight gradients run on the
+  // large-group GEMM over transposed operands (32-bit element offsets into them)
+  const size_t cols = wgrad_large_cols(static_cast<int>(P), E);
+  const size_t rows_max = static_cast<size_t>(H > 2 * I ? H : 2 * I);
+  L.large_w = P >= static_cast<size_t>(256) * E && rows_max * cols < (static_cast<size_t>(1) << 31);
+  if (L.large_w) {
+    L.koff = o;   o = align256(o + sizeof(int) * (E + 1));
+    L.xT = o;     o = align256(o + sizeof(uint16_t) * H * cols);
+    L.doutT = o;  o = align256(o + sizeof(uint16_t) * H * cols);
+    L.dguT = o;   o = align256(o + sizeof(uint16_t) * 2 * I * cols);
+    L.waT = o;    o = align256(o + sizeof(uint16_t) * I * cols);
+  }
   L.total = o;
   return L;
 }
@@ -672,12 +684,21 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   else hipLaunchKernelGGL((bwd_gemm<kDG, 64>), grid_tiles(H), dim3(256), 0, s, a);
   if (k > 1) hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, a.dxs, row_of, T, H, k, dx);
   prof_end(kBwdInput, s);
-  prof_begin(kBwdWDown, s);
-  hipLaunchKernelGGL(bwd_wgrad<kWD>, grid_w(H, I), dim3(256), 0, s, a);
-  prof_end(kBwdWDown, s);
-  prof_begin(kBwdWGateUp, s);
-  hipLaunchKernelGGL(bwd_wgrad<kWG>, grid_w(2 * I, H), dim3(256), 0, s, a);
-  prof_end(kBwdWGateUp, s);
+  if (L.large_w) {
+    err = launch_wgrad_large(x, dout, a.dgu, a.wa, a.perm, a.counts, a.offsets, P, H, I, E, k,
+                             reinterpret_cast<int*>(b + L.koff), reinterpret_cast<uint16_t*>(b + L.xT),
+                             reinterpret_cast<uint16_t*>(b + L.doutT),
+                             reinterpret_cast<uint16_t*>(b + L.dguT),
+                             reinterpret_cast<uint16_t*>(b + L.waT), dwgu, dwd, s);
+    if (err != hipSuccess) return err;
+  } else {
+    prof_begin(kBwdWDown, s);
+    hipLaunchKernelGGL(bwd_wgrad<kWD>, grid_w(H, I), dim3(256), 0, s, a);
+    prof_end(kBwdWDown, s);
+    prof_begin(kBwdWGateUp, s);
+    hipLaunchKernelGGL(bwd_wgrad<kWG>, grid_w(2 * I, H), dim3(256), 0, s, a);
+    prof_end(kBwdWGateUp, s);
+  }
   hipLaunchKernelGGL(route_bwd, dim3(T), dim3(64), 0, s, a.dwp, row_of, idx, w, T, E, k, I / kNT,
                      dtw, dlogits);
   return hipGetLastError();

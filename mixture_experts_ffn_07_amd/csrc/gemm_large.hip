@@ -33,7 +33,7 @@ namespace {
 constexpr int kLBK = 64;                     // K per stage
 constexpr int kLTile = kLargeBM * kLBK;      // elements per operand stage (256 rows x 64)
 constexpr size_t kLLds = 2 * 2 * kLTile * sizeof(uint16_t);   // 128 KB
-enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2, kGateUpSave = 3 };
+enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2, kGateUpSave = 3, kWgradGateUp = 4, kWgradDown = 5 };
 
 // Tail split.  One workgroup fills a CU, so n items run in ceil(n / ncu)
 // rounds; when the last round would leave more than half of the CUs idle, its
@@ -146,42 +146,67 @@ __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const 
 // 32x32x16 result puts, in lane (l32, hi) register 4q+t, weight row 8q + 4hi + t
 // and activation row l32 of the 32 x 32 block.  Within each stage of 64, lane
 // half hi takes K chunks 2*ks + hi at MFMA K step ks (the same for A and B).
+// KIND kWgradGateUp / kWgradDown (weight gradients of the backward pass): A and
+// B are transposed copies [rows][KPT] whose columns hold the routed rows of
+// expert e in offsets[e] .. offsets[e+1] (zero-padded to multiples of 64; KPT =
+// offsets[E]): kWgradGateUp A = x^T (rows h), B = [dg; du]^T (rows c), writes
+// dW_gate_up[e][c][h]; kWgradDown A = (w a)^T (rows i), B = dout^T (rows h),
+// writes dW_down[e][h][i].  A workgroup takes expert e, 256 A rows and 256 B rows
+// and reduces over the expert's columns only (no K split).
 template <int KIND>
 __global__ __launch_bounds__(256) void gemm_large_bf16(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ wt,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint16_t* __restrict__ hout, float* __restrict__ y,
-    uint16_t* __restrict__ out, float* __restrict__ partial, int ncu, float* __restrict__ gu) {
+    uint16_t* __restrict__ out, float* __restrict__ partial, int ncu, float* __restrict__ gu,
+    int E) {
   extern __shared__ __align__(16) uint16_t lds[];   // [stage][A, B][256 x 64]
   constexpr bool kGU = KIND == kGateUp || KIND == kGateUpSave;
-  const int K = kGU ? H : I;
+  constexpr bool kWG = KIND == kWgradGateUp || KIND == kWgradDown;
+  const int K = kWG ? offsets[E] : (kGU ? H : I);    // row stride of both operands
+  const int nA = KIND == kWgradGateUp ? H / 256 : I / 256;       // (weight gradients)
+  const int nB = KIND == kWgradGateUp ? 2 * I / 256 : H / 256;
   const int nblk = kGU ? I / 128 : H / 256;
   const int nk = K / kLBK;
-  const int n_real = nblk * *n_tiles;
-  const TailPlan plan = tail_plan(n_real, ncu, nk);
   const int L = blockIdx.x;
   int item, kb = 0, ke = nk, slot = -1;
-  if (plan.S > 1 && L < plan.full) {
-    item = xcd_item(L, plan.full);
-  } else if (plan.S > 1) {
-    const int t = L - plan.full;
-    if (t >= plan.rem * plan.S) return;
-    item = plan.full + t % plan.rem;
-    const int sl = t / plan.rem;
-    kb = sl * nk / plan.S;
-    ke = (sl + 1) * nk / plan.S;
-    slot = t;
+  int e, nb, bb = 0, mcount = kLargeBM, rbase = 0;
+  if (kWG) {
+    const int per = nA * nB, n_w = E * per;
+    const int n_pad = (n_w + kXcds - 1) / kXcds * kXcds;
+    if (L >= n_pad) return;
+    item = xcd_item(L, n_pad);
+    if (item >= n_w) return;
+    e = item / per;
+    large_coords(item - e * per, nA, nB, bb, nb);
+    kb = offsets[e] / kLBK;
+    ke = offsets[e + 1] / kLBK;
   } else {
-    item = real_item(L, nblk, *n_tiles);
-    if (item < 0) return;
+    const int n_real = nblk * *n_tiles;
+    const TailPlan plan = tail_plan(n_real, ncu, nk);
+    if (plan.S > 1 && L < plan.full) {
+      item = xcd_item(L, plan.full);
+    } else if (plan.S > 1) {
+      const int t = L - plan.full;
+      if (t >= plan.rem * plan.S) return;
+      item = plan.full + t % plan.rem;
+      const int sl = t / plan.rem;
+      kb = sl * nk / plan.S;
+      ke = (sl + 1) * nk / plan.S;
+      slot = t;
+    } else {
+      item = real_item(L, nblk, *n_tiles);
+      if (item < 0) return;
+    }
+    int tile;
+    large_coords(item, nblk, *n_tiles, tile, nb);
+    const int2 te = tiles[tile];
+    e = te.x;
+    const int m0 = te.y;
+    mcount = min(kLargeBM, counts[e] - m0);
+    rbase = offsets[e] + m0;
   }
-  int tile, nb;
-  large_coords(item, nblk, *n_tiles, tile, nb);
-  const int2 te = tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int mcount = min(kLargeBM, counts[e] - m0);
-  const int rbase = offsets[e] + m0;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, l32 = ln & 31, hi = ln >> 5;
   const int wm = wv & 1, wn = wv >> 1;
 
@@ -191,7 +216,10 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
   const int lrow = ln >> 3, lc = ln & 7;
   const uint16_t* __restrict__ abase;
   uint32_t ao;
-  if (kGU) {
+  if (kWG) {
+    abase = wt;
+    ao = static_cast<uint32_t>((nb * 256 + wv * 64 + lrow) * K + lc * 8);
+  } else if (kGU) {
     const int n0 = nb * 128;
     abase = wt + static_cast<size_t>(e) * 2 * I * H;
     // tile rows 0..127: gate neurons n0.., rows 128..255: up neurons n0..
@@ -205,7 +233,8 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
   for (int j = 0; j < 8; ++j) {
     const int r = wv * 64 + 8 * j + lrow;
     const int rr = r < mcount ? r : 0;
-    bo[j] = kGU ? static_cast<uint32_t>((perm[rbase + rr] / k) * H + lc * 8)
+    bo[j] = kWG ? static_cast<uint32_t>((bb * 256 + r) * K + lc * 8)
+          : kGU ? static_cast<uint32_t>((perm[rbase + rr] / k) * H + lc * 8)
                 : static_cast<uint32_t>((rbase + rr) * I + lc * 8);
   }
   // LDS: row r, 16-byte chunk c at r*64 + ((c ^ (r & 7)) * 8); here r & 7 == lrow
@@ -262,7 +291,9 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
   // barrier that ends the reads of stage s-1) and the first three of stage s
   // (chunks 0..11, before the barrier that publishes stage s+1).  Prologue:
   // stage kb in LDS, chunks 12..15 of stage kb+1 in LDS, the staging registers
-  // holding chunks 0..11 of stage kb+1 and 12..15 of stage kb+2.
+  // holding chunks 0..11 of stage kb+1 and 12..15 of stage kb+2.  (An expert
+  // with no routed rows has an empty range: its weight gradient is zero.)
+  if (ke > kb) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) GLOAD(q, kb);
 #pragma unroll
@@ -290,11 +321,33 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     __builtin_amdgcn_s_barrier();
     PHASE(a1, b1, a0, b0, kt + 1, 0, kt + 2, 12, 4);
   }
+  }
 #undef GLOAD
 #undef LWRITE
 #undef RDF
 #undef PHASE
 
+  if (kWG) {
+    // dW[e][B row][A row], BF16: lane (l32, hi) holds A rows 32i + 8q + 4hi + t of
+    // the wave's 128 and B row 32j + l32 of its 128
+    const int colsA = nA * 256;
+    uint16_t* base = out + static_cast<size_t>(e) * (nB * 256) * colsA;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint16_t* orow = base + static_cast<size_t>(bb * 256 + wm * 128 + 32 * j + l32) * colsA +
+                       nb * 256 + wn * 128 + 4 * hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t p[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) p[t] = f32_to_bf16_rne(acc[i][j][4 * q + t]);
+          *reinterpret_cast<uint2*>(orow + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+        }
+    }
+    return;
+  }
   if (slot >= 0) {
     // tail slice: FP32 partial tile in register order, [64 x f32x4][256 threads]
     f32x4* pp = reinterpret_cast<f32x4*>(partial) + static_cast<size_t>(slot) * 64 * 256 + tid;
@@ -693,7 +746,7 @@ hipError_t launch_gate_up_large_bf16(const uint16_t* x, const uint16_t* wgu, con
 #define LARGE_GU(KG)                                                                          \
   hipLaunchKernelGGL(gemm_large_bf16<KG>, dim3(grid), dim3(256), kLLds, s, x, wgu, perm,       \
                      tiles, n_tiles, counts, offsets, nullptr, H, I, k, h, nullptr, nullptr,  \
-                     partial, ncu, gu);                                                       \
+                     partial, ncu, gu, 0);                                                    \
   hipLaunchKernelGGL(gemm_large_fixup<KG>, dim3(ncu / 2 * 32), dim3(256), 0, s, perm, tiles,   \
                      n_tiles, counts, offsets, nullptr, H, I, h, nullptr, nullptr, partial, ncu, \
                      H / kLBK, gu)
@@ -711,7 +764,7 @@ hipError_t launch_down_large_bf16(const uint16_t* h, const uint16_t* wd, const i
 #define LARGE_DOWN(KD)                                                                        \
   hipLaunchKernelGGL(gemm_large_bf16<KD>, dim3(grid), dim3(256), kLLds, s, h, wd, perm, tiles, \
                      n_tiles, counts, offsets, w, H, I, k, nullptr, y, out, partial, ncu,     \
-                     nullptr);                                                                \
+                     nullptr, 0);                                                             \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
                      n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kLBK, \
                      nullptr)
@@ -752,12 +805,124 @@ hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint
   return hipGetLastError();
 }
 
+namespace {
+// Column offsets of the weight-gradient operands: koff[e] = sum over e' < e of
+// counts[e'] rounded up to 64, koff[E] = KPT.  One wave: each lane sums a run of
+// experts, then an exclusive scan over the lanes.
+__global__ __launch_bounds__(64) void wgrad_koff(const int* __restrict__ counts, int E,
+                                                 int* __restrict__ koff) {
+  const int ln = threadIdx.x;
+  const int per = (E + 63) / 64, e0 = ln * per, e1 = min(E, e0 + per);
+  int sum = 0;
+  for (int e = e0; e < e1; ++e) sum += (counts[e] + kLBK - 1) / kLBK * kLBK;
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, kWave);
+    if (ln >= d) incl += v;
+  }
+  int run = incl - sum;
+  for (int e = e0; e < e1; ++e) {
+    koff[e] = run;
+    run += (counts[e] + kLBK - 1) / kLBK * kLBK;
+  }
+  if (ln == 63) koff[E] = incl;
+}
+
+// Gather-transpose for the weight gradients: dst[c][koff[e] + r] = element c of
+// expert e's r-th routed row, 0 for r in [counts[e], padded end).  TOKEN: the row
+// is token perm[offsets[e] + r] / k of src (x, dout); otherwise grouped row
+// offsets[e] + r (dgu, w a).  Workgroup = 64 routed rows x 64 columns, through
+// an LDS tile; 16-byte loads along the source rows, 16-byte stores along dst rows.
+template <bool TOKEN>
+__global__ __launch_bounds__(256) void wgrad_transpose(
+    const uint16_t* __restrict__ src, int C, const int* __restrict__ perm, int k,
+    const int* __restrict__ counts, const int* __restrict__ offsets,
+    const int* __restrict__ koff, int E, uint16_t* __restrict__ dst) {
+  __shared__ __align__(16) uint16_t tl[64][64 + 8];
+  const int KPT = koff[E];
+  const int g0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  if (g0 >= KPT) return;
+  int lo = 0, hi = E - 1;                         // last e with koff[e] <= g0 (ranges non-empty)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (koff[mid] <= g0) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo, r0 = g0 - koff[e], cnt = counts[e], goff = offsets[e];
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ch = tid + 256 * u, r = ch >> 3, cc = ch & 7;
+    i32x4 v = {0, 0, 0, 0};
+    if (r0 + r < cnt) {
+      const int gr = goff + r0 + r;
+      const int row = TOKEN ? perm[gr] / k : gr;
+      v = ld16(src + static_cast<size_t>(row) * C + c0 + cc * 8);
+    }
+    *reinterpret_cast<i32x4*>(&tl[r][cc * 8]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ch = tid + 256 * u, c = ch >> 3, rc = ch & 7;
+    uint32_t p[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      p[t] = static_cast<uint32_t>(tl[rc * 8 + 2 * t][c]) | (static_cast<uint32_t>(tl[rc * 8 + 2 * t + 1][c]) << 16);
+    *reinterpret_cast<uint4*>(dst + static_cast<size_t>(c0 + c) * KPT + g0 + rc * 8) =
+        make_uint4(p[0], p[1], p[2], p[3]);
+  }
+}
+
+}  // namespace
+
+size_t wgrad_large_cols(int P, int E) {
+  return static_cast<size_t>(P) + static_cast<size_t>(kLBK - 1) * E;
+}
+
+hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uint16_t* dgu,
+                              const uint16_t* wa, const int* perm, const int* counts,
+                              const int* offsets, int P, int H, int I, int E, int k, int* koff,
+                              uint16_t* xT, uint16_t* doutT, uint16_t* dguT, uint16_t* waT,
+                              uint16_t* dwgu, uint16_t* dwd, hipStream_t s) {
+  const unsigned gtiles = static_cast<unsigned>((wgrad_large_cols(P, E) + 63) / 64);
+  hipLaunchKernelGGL(wgrad_koff, dim3(1), dim3(64), 0, s, counts, E, koff);
+  auto grid_w = [&](int nA, int nB) {
+    return dim3(static_cast<unsigned>((E * nA * nB + kXcds - 1) / kXcds * kXcds));
+  };
+  prof_begin(kBwdWDown, s);
+  hipLaunchKernelGGL(wgrad_transpose<false>, dim3(gtiles, I / 64), dim3(256), 0, s, wa, I, perm, k,
+                     counts, offsets, koff, E, waT);
+  hipLaunchKernelGGL(wgrad_transpose<true>, dim3(gtiles, H / 64), dim3(256), 0, s, dout, H, perm, k,
+                     counts, offsets, koff, E, doutT);
+  hipLaunchKernelGGL(gemm_large_bf16<kWgradDown>, grid_w(I / 256, H / 256), dim3(256), kLLds, s,
+                     doutT, waT, perm, nullptr, nullptr, counts, koff, nullptr, H, I, k, nullptr,
+                     nullptr, dwd, nullptr, 0, nullptr, E);
+  prof_end(kBwdWDown, s);
+  prof_begin(kBwdWGateUp, s);
+  hipLaunchKernelGGL(wgrad_transpose<true>, dim3(gtiles, H / 64), dim3(256), 0, s, x, H, perm, k,
+                     counts, offsets, koff, E, xT);
+  hipLaunchKernelGGL(wgrad_transpose<false>, dim3(gtiles, 2 * I / 64), dim3(256), 0, s, dgu, 2 * I,
+                     perm, k, counts, offsets, koff, E, dguT);
+  hipLaunchKernelGGL(gemm_large_bf16<kWgradGateUp>, grid_w(H / 256, 2 * I / 256), dim3(256), kLLds,
+                     s, dguT, xT, perm, nullptr, nullptr, counts, koff, nullptr, H, I, k, nullptr,
+                     nullptr, dwgu, nullptr, 0, nullptr, E);
+  prof_end(kBwdWGateUp, s);
+  return hipGetLastError();
+}
+
 hipError_t large_set_attributes() {
   const int bytes = static_cast<int>(kLLds);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kGateUp>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kGateUpSave>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kWgradGateUp>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kWgradDown>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kDownFused>),

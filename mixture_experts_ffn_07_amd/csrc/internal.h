@@ -76,6 +76,15 @@ hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint
                                 const int* n_tiles, const int* counts, const int* offsets,
                                 const float* w, int H, int I, int k, float* y, uint16_t* out,
                                 float* partial, int max_tiles, int ncu, hipStream_t s);
+// Weight gradients of the backward pass for large groups (>= 256 routed rows
+// per expert): koff [E+1] ints, and transposed operands of wgrad_large_cols(P, E)
+// columns each - xT, doutT [H][cols], dguT [2I][cols], waT [I][cols].
+size_t wgrad_large_cols(int P, int E);
+hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uint16_t* dgu,
+                              const uint16_t* wa, const int* perm, const int* counts,
+                              const int* offsets, int P, int H, int I, int E, int k, int* koff,
+                              uint16_t* xT, uint16_t* doutT, uint16_t* dguT, uint16_t* waT,
+                              uint16_t* dwgu, uint16_t* dwd, hipStream_t s);
 hipError_t large_set_attributes();
 
 // Stable expert grouping of the T*k routed pairs into M-tiles of BM rows
@@ -86,7 +95,9 @@ hipError_t launch_group_experts(const int32_t* idx, int P, int E, int BM, int* c
 // Byte layout of the backward workspace (backward.hip).
 struct BackwardWs {
   size_t counts, offsets, tiles, n_tiles, perm, row_of, gu, dgu, wa, dwp, dxs, total;
+  size_t koff, xT, doutT, dguT, waT;   // large groups: the weight gradients' operands
   int max_tiles;
+  bool large_w;                        // weight gradients on the large-group GEMM
 };
 BackwardWs backward_ws_layout(int T, int H, int I, int E, int k);
 // gu_saved: NULL (the pre-activations are recomputed) or [T*k, 2I] FP32, slot order

@@ -148,6 +148,19 @@ def test_train_forward_large_groups(M, T, H, I, E, k):
     _check(M, d, f"bwd saved, large groups T={T} k={k}", saved=True)
 
 
+def test_backward_large_groups_with_empty_expert(M):
+    # >= 256 routed rows per expert on average: the weight gradients run on the
+    # large-group GEMM over transposed, zero-padded operands; expert 3 gets no rows
+    # (its gradients must be exactly zero) and the others ragged counts
+    T, E = 1500, 4
+    d = _custom(T, 256, 256, E, 2, seed=31)
+    lg = d["logits"].clone()
+    lg[:, 3] = -30.0
+    d["logits"] = lg.contiguous()
+    _check(M, d, "bwd large groups, one empty expert")
+    _check(M, d, "bwd large groups, one empty expert, saved", saved=True)
+
+
 def test_backward_bit_identical_repeats(M):
     d = _custom(600, 512, 256, 12, 4, seed=5)
     dout = W.make_output_grad(d["cfg"], seed=1, device="cuda")
