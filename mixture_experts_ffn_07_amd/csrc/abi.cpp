@@ -272,7 +272,7 @@ int moe_backward_batched(const uint16_t* x, const uint16_t* w_gate_up, const uin
   if (int st = device_info(&cus)) return st;
   return hip_status(moe::launch_backward(x, w_gate_up, w_down, topk_idx, topk_w, dout, gu_saved,
                                          T, H, I, E, k, dx, dw_gate_up, dw_down, d_topk_w,
-                                         dlogits, workspace, static_cast<hipStream_t>(stream)),
+                                         dlogits, workspace, static_cast<hipStream_t>(stream), cus),
                     "moe_backward_batched launch");
 }
 

@@ -613,6 +613,11 @@ BackwardWs backward_ws_layout(int T, int H, int I, int E, int k) {
     L.doutT = o;  o = align256(o + sizeof(uint16_t) * H * cols);
     L.dguT = o;   o = align256(o + sizeof(uint16_t) * 2 * I * cols);
     L.waT = o;    o = align256(o + sizeof(uint16_t) * I * cols);
+    L.max_tiles256 = static_cast<int>(E + (P + kLargeBM - 1) / kLargeBM);
+    L.n_tiles256 = o; o += 256;
+    L.tiles256 = o;   o = align256(o + sizeof(int) * 2 * L.max_tiles256);
+    L.wguT = o;       o = align256(o + sizeof(uint16_t) * E * 2 * I * H);
+    L.partial = o;    o = align256(o + sizeof(float) * kLargeMaxSlices * kLargeBM * 256);
   }
   L.total = o;
   return L;
@@ -622,7 +627,7 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
                            const int32_t* idx, const float* w, const uint16_t* dout,
                            const float* gu_saved, int T, int H, int I, int E, int k,
                            uint16_t* dx, uint16_t* dwgu, uint16_t* dwd, float* dtw,
-                           float* dlogits, void* ws, hipStream_t s) {
+                           float* dlogits, void* ws, hipStream_t s, int num_cus) {
   const BackwardWs L = backward_ws_layout(T, H, I, E, k);
   char* b = static_cast<char*>(ws);
   BwdArgs a{};
@@ -680,8 +685,26 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   else hipLaunchKernelGGL((bwd_gemm<kDD, 64>), grid_tiles(I), dim3(256), 0, s, a);
   prof_end(kBwdDown, s);
   prof_begin(kBwdInput, s);
-  if (tall) hipLaunchKernelGGL((bwd_gemm<kDG, 128>), grid_tiles(H), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((bwd_gemm<kDG, 64>), grid_tiles(H), dim3(256), 0, s, a);
+  if (L.large_w) {
+    // dx on the large-group GEMM: W_gate_up transposed to [E][H][2I], 256-row
+    // M-tiles over the same (deterministic) grouping
+    int2* tiles256 = reinterpret_cast<int2*>(b + L.tiles256);
+    int* n_tiles256 = reinterpret_cast<int*>(b + L.n_tiles256);
+    uint16_t* wguT = reinterpret_cast<uint16_t*>(b + L.wguT);
+    err = launch_group_experts(idx, P, E, kLargeBM, const_cast<int*>(a.counts),
+                               const_cast<int*>(a.offsets), tiles256, n_tiles256,
+                               const_cast<int*>(a.perm), row_of, s);
+    if (err == hipSuccess) err = launch_transpose_bf16(wgu, E, 2 * I, H, wguT, s);
+    if (err == hipSuccess)
+      err = launch_dgrad_large(a.dgu, wguT, a.perm, tiles256, n_tiles256, a.counts, a.offsets, H,
+                               2 * I, k, a.dxs, dx, reinterpret_cast<float*>(b + L.partial),
+                               L.max_tiles256, num_cus, s);
+    if (err != hipSuccess) return err;
+  } else if (tall) {
+    hipLaunchKernelGGL((bwd_gemm<kDG, 128>), grid_tiles(H), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_gemm<kDG, 64>), grid_tiles(H), dim3(256), 0, s, a);
+  }
   if (k > 1) hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, a.dxs, row_of, T, H, k, dx);
   prof_end(kBwdInput, s);
   if (L.large_w) {

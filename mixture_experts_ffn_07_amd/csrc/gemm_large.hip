@@ -33,7 +33,7 @@ namespace {
 constexpr int kLBK = 64;                     // K per stage
 constexpr int kLTile = kLargeBM * kLBK;      // elements per operand stage (256 rows x 64)
 constexpr size_t kLLds = 2 * 2 * kLTile * sizeof(uint16_t);   // 128 KB
-enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2, kGateUpSave = 3, kWgradGateUp = 4, kWgradDown = 5 };
+enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2, kGateUpSave = 3, kWgradGateUp = 4, kWgradDown = 5, kDownPlain = 6 };
 
 // Tail split.  One workgroup fills a CU, so n items run in ceil(n / ncu)
 // rounds; when the last round would leave more than half of the CUs idle, its
@@ -114,9 +114,9 @@ __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const 
             p[t] = f32_to_bf16_rne(swiglu(acc[i][j][4 * q + t], acc[i + 2][j][4 * q + t]));
           *reinterpret_cast<uint2*>(hr + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
         }
-    } else if (KIND == kDownFused) {
+    } else if (KIND == kDownFused || KIND == kDownPlain) {
       const int t = perm[rbase + r];        // k = 1: pair id == token
-      const float wt_t = w[t];
+      const float wt_t = KIND == kDownFused ? w[t] : 1.0f;
       uint16_t* orow = out + static_cast<size_t>(t) * H + nb * 256 + wn * 128 + 4 * hi;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -415,9 +415,9 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
 #pragma unroll
     for (int t = 0; t < 4; ++t) p[t] = f32_to_bf16_rne(swiglu(a[t], u[t]));
     *reinterpret_cast<uint2*>(hr) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
-  } else if (KIND == kDownFused) {
+  } else if (KIND == kDownFused || KIND == kDownPlain) {
     const int t = perm[rbase + r];
-    const float wt_t = w[t];
+    const float wt_t = KIND == kDownFused ? w[t] : 1.0f;
     uint16_t* o = out + static_cast<size_t>(t) * H + nb * 256 + wn * 128 + 32 * i + 8 * q + 4 * hi;
     uint32_t p[4];
 #pragma unroll
@@ -911,12 +911,67 @@ hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uin
   return hipGetLastError();
 }
 
+namespace {
+// dst[b][c][r] = src[b][r][c] (BF16; R and C multiples of 64): 64 x 64 LDS tiles,
+// 16-byte loads and stores.
+__global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict__ src, int R, int C,
+                                                      uint16_t* __restrict__ dst) {
+  __shared__ __align__(16) uint16_t tl[64][64 + 8];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const size_t mat = static_cast<size_t>(R) * C * blockIdx.z;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ch = tid + 256 * u, r = ch >> 3, cc = ch & 7;
+    *reinterpret_cast<i32x4*>(&tl[r][cc * 8]) =
+        ld16(src + mat + static_cast<size_t>(r0 + r) * C + c0 + cc * 8);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ch = tid + 256 * u, c = ch >> 3, rc = ch & 7;
+    uint32_t p[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      p[t] = static_cast<uint32_t>(tl[rc * 8 + 2 * t][c]) | (static_cast<uint32_t>(tl[rc * 8 + 2 * t + 1][c]) << 16);
+    *reinterpret_cast<uint4*>(dst + mat + static_cast<size_t>(c0 + c) * R + r0 + rc * 8) =
+        make_uint4(p[0], p[1], p[2], p[3]);
+  }
+}
+}  // namespace
+
+hipError_t launch_transpose_bf16(const uint16_t* src, int B, int R, int C, uint16_t* dst,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(transpose_bf16, dim3(C / 64, R / 64, B), dim3(256), 0, s, src, R, C, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_dgrad_large(const uint16_t* act, const uint16_t* wT, const int* perm,
+                              const int2* tiles, const int* n_tiles, const int* counts,
+                              const int* offsets, int H, int K, int k, float* y, uint16_t* out,
+                              float* partial, int max_tiles, int ncu, hipStream_t s) {
+  const int grid = large_grid(H / 256, max_tiles, ncu);
+#define DGRAD(KD)                                                                             \
+  hipLaunchKernelGGL(gemm_large_bf16<KD>, dim3(grid), dim3(256), kLLds, s, act, wT, perm, tiles, \
+                     n_tiles, counts, offsets, nullptr, H, K, k, nullptr, y, out, partial, ncu,  \
+                     nullptr, 0);                                                                \
+  hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,      \
+                     n_tiles, counts, offsets, nullptr, H, K, nullptr, y, out, partial, ncu,      \
+                     K / kLBK, nullptr)
+  if (k == 1) { DGRAD(kDownPlain); } else { DGRAD(kDownSlots); }
+#undef DGRAD
+  return hipGetLastError();
+}
+
 hipError_t large_set_attributes() {
   const int bytes = static_cast<int>(kLLds);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kGateUp>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kGateUpSave>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kDownPlain>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kWgradGateUp>),

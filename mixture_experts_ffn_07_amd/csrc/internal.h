@@ -80,6 +80,16 @@ hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint
 // per expert): koff [E+1] ints, and transposed operands of wgrad_large_cols(P, E)
 // columns each - xT, doutT [H][cols], dguT [2I][cols], waT [I][cols].
 size_t wgrad_large_cols(int P, int E);
+// dst[b] = src[b]^T for B row-major R x C BF16 matrices (R, C multiples of 64)
+hipError_t launch_transpose_bf16(const uint16_t* src, int B, int R, int C, uint16_t* dst,
+                                 hipStream_t s);
+// Data gradient of a projection on the large-group GEMM: for each grouped row r
+// (256-row M-tiles), D[r][n] = sum_c act[r][c] wT[e][n][c], c < K, n < H; k = 1
+// writes out[perm[r]] = bf16(D), k > 1 writes y[r] = D (FP32).
+hipError_t launch_dgrad_large(const uint16_t* act, const uint16_t* wT, const int* perm,
+                              const int2* tiles, const int* n_tiles, const int* counts,
+                              const int* offsets, int H, int K, int k, float* y, uint16_t* out,
+                              float* partial, int max_tiles, int ncu, hipStream_t s);
 hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uint16_t* dgu,
                               const uint16_t* wa, const int* perm, const int* counts,
                               const int* offsets, int P, int H, int I, int E, int k, int* koff,
@@ -96,7 +106,8 @@ hipError_t launch_group_experts(const int32_t* idx, int P, int E, int BM, int* c
 struct BackwardWs {
   size_t counts, offsets, tiles, n_tiles, perm, row_of, gu, dgu, wa, dwp, dxs, total;
   size_t koff, xT, doutT, dguT, waT;   // large groups: the weight gradients' operands
-  int max_tiles;
+  size_t tiles256, n_tiles256, wguT, partial;   // large groups: dx on the large-group GEMM
+  int max_tiles, max_tiles256;
   bool large_w;                        // weight gradients on the large-group GEMM
 };
 BackwardWs backward_ws_layout(int T, int H, int I, int E, int k);
@@ -105,7 +116,7 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
                            const int32_t* idx, const float* w, const uint16_t* dout,
                            const float* gu_saved, int T, int H, int I, int E, int k,
                            uint16_t* dx, uint16_t* dwgu, uint16_t* dwd, float* dtw,
-                           float* dlogits, void* ws, hipStream_t s);
+                           float* dlogits, void* ws, hipStream_t s, int num_cus);
 
 hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
                            uint8_t* scales, hipStream_t s);
