@@ -46,7 +46,7 @@ CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 # as null until the counters are taken again.
 TRAFFIC = {
     ("decode_gate_up", "qwen3-decode-T32"): (
-        711.0e6, ('decode.hip', 'common.h', 'internal.h'), "0a72dc3f9a36b6e0",
+        711.0e6, ('decode.hip', 'common.h', 'internal.h'), "e84552794ff00e5c",
         "profiles/decode_gate_up_qwen3-decode-T32.md"),
     ("gemm_gate_up", "kimi-bf16-T2048"): (
         23002.0e6, ('batched.hip', 'common.h', 'tiles.h'), "d7acc4ad1d9e06be",

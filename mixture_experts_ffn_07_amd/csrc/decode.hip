@@ -976,10 +976,11 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   // weights); T > 32 the wide one (16-token tiles)
   const int TM8 = T <= 8 ? 1 : (T <= 16 ? 2 : 4);
   // register budget (128 per lane): weights of two tasks + 16*NG accumulators per tile;
-  // one 8-neuron group per item when 16-neuron items would number fewer than two per
-  // CU (T = 1: 8 experts x 48 items): the finer items even out the last round
+  // one 8-neuron group per item when 16-neuron items would number fewer than sixteen
+  // per CU (T <= 10: e.g. T = 8, ~52 touched experts x 48 items): the persistent
+  // workgroups then hold about twice as many items, which evens out the last round
   const long pairs_u = T * k < E ? T * k : E;
-  const int NG = TM8 <= 2 && pairs_u * (I / 16) >= 2L * num_cus ? 2 : 1;
+  const int NG = TM8 <= 2 && pairs_u * (I / 16) >= 16L * num_cus ? 2 : 1;
   const int S = H / 64;                             // a multiple of 4
   // two steps per chunk when every wave's step count is even and registers allow
   const int KC = (S % 16 == 0 && (TM8 == 1 || TM8 == 4)) ? 2 : 1;
