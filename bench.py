@@ -55,7 +55,7 @@ TRAFFIC = {
         13212.0e6, ('batched.hip', 'common.h', 'tiles.h'), "d7acc4ad1d9e06be",
         "profiles/gemm_gate_up_glm-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
-        1958.3e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "ea90c4b366007ff5",
+        2000.8e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "0800648d72b4e025",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
         23710.1e6, ('backward.hip', 'common.h', 'tiles.h'), "63d2f0301b2be2dd",

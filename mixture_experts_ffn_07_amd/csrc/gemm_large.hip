@@ -59,9 +59,11 @@ __device__ __forceinline__ TailPlan tail_plan(int n_real, int ncu, int nk) {
 // of item numbers, 32 at a time.  Numbering N-blocks fastest would make those
 // 32 one or two M-tiles against ~32 different weight blocks (about 34 distinct
 // operand blocks per K stage in the XCD's L2); numbering groups of
-// kLargeGroupM M-tiles with the M-tile fastest makes them 4 M-tiles x 8
+// kLargeGroupM M-tiles with the M-tile fastest makes them 8 M-tiles x 4
 // N-blocks (12 distinct blocks), so each staged block is shared by more CUs.
-constexpr int kLargeGroupM = 4;
+// (Measured over group sizes 2, 4, 6, 8 and 16: 8 is best for MXFP8 and level
+// with 4 for BF16.)
+constexpr int kLargeGroupM = 8;
 __device__ __forceinline__ void large_coords(int item, int nblk, int n_tiles, int& tile, int& nb) {
   const int grp = item / (kLargeGroupM * nblk);
   const int r = item - grp * kLargeGroupM * nblk;
