@@ -583,6 +583,65 @@ __global__ __launch_bounds__(64) void route_bwd(const float* __restrict__ dwp,
   }
 }
 
+// Large groups: dh (FP32, grouped rows, from the large-group GEMM) -> [dg; du]
+// (BF16), w a (BF16) and the partial dots a . dh per 128 columns, with the
+// arithmetic of bwd_gemm's kDD epilogue.  Thread = (row, 8 consecutive columns);
+// 16 rows x 128 columns per workgroup.
+__global__ __launch_bounds__(256) void bwd_dh_finish(BwdArgs a, const float* __restrict__ dh, int P) {
+  const int I = a.I;
+  const int tid = threadIdx.x, sg = tid & 15;
+  const int row = blockIdx.x * 16 + (tid >> 4);
+  const int n0 = blockIdx.y * kNT;
+  if (row >= P) return;                             // whole 16-lane row groups leave together
+  const size_t grow = static_cast<size_t>(row);
+  const int pair = a.perm[grow];
+  const float wt = a.w[pair];
+  const float* gp = (a.gus ? a.gus + static_cast<size_t>(pair) * (2 * I) : a.gu + grow * (2 * I)) +
+                    n0 + 8 * sg;
+  const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp);
+  const f32x4 g1 = *reinterpret_cast<const f32x4*>(gp + 4);
+  const f32x4 u0 = *reinterpret_cast<const f32x4*>(gp + I);
+  const f32x4 u1 = *reinterpret_cast<const f32x4*>(gp + I + 4);
+  const float* hp = dh + grow * I + n0 + 8 * sg;
+  const f32x4 c0 = *reinterpret_cast<const f32x4*>(hp);
+  const f32x4 c1 = *reinterpret_cast<const f32x4*>(hp + 4);
+  float part = 0.0f;
+  uint32_t pg[4], pu[4], pa[4];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float g = q < 4 ? g0[q] : g1[q - 4];
+    const float u = q < 4 ? u0[q] : u1[q - 4];
+    const float d = q < 4 ? c0[q] : c1[q - 4];
+    const float sg_ = sigmoidf_(g);
+    const float si = g * sg_;
+    part = fmaf(si * u, d, part);
+    const float da = wt * d;
+    const uint32_t bg = f32_to_bf16_rne(da * u * (sg_ * (1.0f + g * (1.0f - sg_))));
+    const uint32_t bu = f32_to_bf16_rne(da * si);
+    const uint32_t ba = f32_to_bf16_rne(wt * (si * u));
+    if (q & 1) {
+      pg[q >> 1] |= bg << 16;
+      pu[q >> 1] |= bu << 16;
+      pa[q >> 1] |= ba << 16;
+    } else {
+      pg[q >> 1] = bg;
+      pu[q >> 1] = bu;
+      pa[q >> 1] = ba;
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
+  uint16_t* dst = a.dgu + grow * (2 * I) + n0 + 8 * sg;
+  st16(dst, i32x4{static_cast<int>(pg[0]), static_cast<int>(pg[1]), static_cast<int>(pg[2]),
+                  static_cast<int>(pg[3])});
+  st16(dst + I, i32x4{static_cast<int>(pu[0]), static_cast<int>(pu[1]), static_cast<int>(pu[2]),
+                      static_cast<int>(pu[3])});
+  st16(a.wa + grow * I + n0 + 8 * sg,
+       i32x4{static_cast<int>(pa[0]), static_cast<int>(pa[1]), static_cast<int>(pa[2]),
+             static_cast<int>(pa[3])});
+  if (sg == 0) a.dwp[grow * (I / kNT) + n0 / kNT] = part;
+}
+
 }  // namespace
 
 BackwardWs backward_ws_layout(int T, int H, int I, int E, int k) {
@@ -618,6 +677,8 @@ BackwardWs backward_ws_layout(int T, int H, int I, int E, int k) {
     L.tiles256 = o;   o = align256(o + sizeof(int) * 2 * L.max_tiles256);
     L.wguT = o;       o = align256(o + sizeof(uint16_t) * E * 2 * I * H);
     L.partial = o;    o = align256(o + sizeof(float) * kLargeMaxSlices * kLargeBM * 256);
+    L.wdT = o;        o = align256(o + sizeof(uint16_t) * E * I * H);
+    L.dh = o;         o = align256(o + sizeof(float) * P * I);
   }
   L.total = o;
   return L;
@@ -680,25 +741,43 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
     else hipLaunchKernelGGL((bwd_gemm<kGU, 64>), grid_tiles(2 * I), dim3(256), 0, s, a);
     prof_end(kBwdGateUp, s);
   }
-  prof_begin(kBwdDown, s);
-  if (tall) hipLaunchKernelGGL((bwd_gemm<kDD, 128>), grid_tiles(I), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((bwd_gemm<kDD, 64>), grid_tiles(I), dim3(256), 0, s, a);
-  prof_end(kBwdDown, s);
-  prof_begin(kBwdInput, s);
+  // large groups: 256-row M-tiles over the same (deterministic) grouping for the
+  // large-group GEMMs of dh and dx
+  int2* tiles256 = L.large_w ? reinterpret_cast<int2*>(b + L.tiles256) : nullptr;
+  int* n_tiles256 = L.large_w ? reinterpret_cast<int*>(b + L.n_tiles256) : nullptr;
+  float* partial = L.large_w ? reinterpret_cast<float*>(b + L.partial) : nullptr;
   if (L.large_w) {
-    // dx on the large-group GEMM: W_gate_up transposed to [E][H][2I], 256-row
-    // M-tiles over the same (deterministic) grouping
-    int2* tiles256 = reinterpret_cast<int2*>(b + L.tiles256);
-    int* n_tiles256 = reinterpret_cast<int*>(b + L.n_tiles256);
-    uint16_t* wguT = reinterpret_cast<uint16_t*>(b + L.wguT);
     err = launch_group_experts(idx, P, E, kLargeBM, const_cast<int*>(a.counts),
                                const_cast<int*>(a.offsets), tiles256, n_tiles256,
                                const_cast<int*>(a.perm), row_of, s);
-    if (err == hipSuccess) err = launch_transpose_bf16(wgu, E, 2 * I, H, wguT, s);
+    if (err != hipSuccess) return err;
+  }
+  prof_begin(kBwdDown, s);
+  if (L.large_w) {
+    // dh on the large-group GEMM (W_down transposed to [E][I][H]), then the
+    // SwiGLU backward, w a and the partial dots elementwise
+    uint16_t* wdT = reinterpret_cast<uint16_t*>(b + L.wdT);
+    float* dh = reinterpret_cast<float*>(b + L.dh);
+    err = launch_transpose_bf16(wd, E, H, I, wdT, s);
+    if (err == hipSuccess)
+      err = launch_dh_large(dout, wdT, a.perm, tiles256, n_tiles256, a.counts, a.offsets, H, I, k,
+                            dh, partial, L.max_tiles256, num_cus, s);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(bwd_dh_finish, dim3((P + 15) / 16, I / kNT), dim3(256), 0, s, a, dh, P);
+  } else if (tall) {
+    hipLaunchKernelGGL((bwd_gemm<kDD, 128>), grid_tiles(I), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_gemm<kDD, 64>), grid_tiles(I), dim3(256), 0, s, a);
+  }
+  prof_end(kBwdDown, s);
+  prof_begin(kBwdInput, s);
+  if (L.large_w) {
+    // dx on the large-group GEMM: W_gate_up transposed to [E][H][2I]
+    uint16_t* wguT = reinterpret_cast<uint16_t*>(b + L.wguT);
+    err = launch_transpose_bf16(wgu, E, 2 * I, H, wguT, s);
     if (err == hipSuccess)
       err = launch_dgrad_large(a.dgu, wguT, a.perm, tiles256, n_tiles256, a.counts, a.offsets, H,
-                               2 * I, k, a.dxs, dx, reinterpret_cast<float*>(b + L.partial),
-                               L.max_tiles256, num_cus, s);
+                               2 * I, k, a.dxs, dx, partial, L.max_tiles256, num_cus, s);
     if (err != hipSuccess) return err;
   } else if (tall) {
     hipLaunchKernelGGL((bwd_gemm<kDG, 128>), grid_tiles(H), dim3(256), 0, s, a);

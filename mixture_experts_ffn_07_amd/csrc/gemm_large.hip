@@ -33,7 +33,7 @@ namespace {
 constexpr int kLBK = 64;                     // K per stage
 constexpr int kLTile = kLargeBM * kLBK;      // elements per operand stage (256 rows x 64)
 constexpr size_t kLLds = 2 * 2 * kLTile * sizeof(uint16_t);   // 128 KB
-enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2, kGateUpSave = 3, kWgradGateUp = 4, kWgradDown = 5, kDownPlain = 6 };
+enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2, kGateUpSave = 3, kWgradGateUp = 4, kWgradDown = 5, kDownPlain = 6, kBwdDh = 7 };
 
 // Tail split.  One workgroup fills a CU, so n items run in ceil(n / ncu)
 // rounds; when the last round would leave more than half of the CUs idle, its
@@ -130,7 +130,8 @@ __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const 
           *reinterpret_cast<uint2*>(orow + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
         }
     } else {
-      float* yr = y + static_cast<size_t>(rbase + r) * H + nb * 256 + wn * 128 + 4 * hi;
+      // kDownSlots: y [P, H]; kBwdDh: dh [P, I]
+      float* yr = y + static_cast<size_t>(rbase + r) * (KIND == kBwdDh ? I : H) + nb * 256 + wn * 128 + 4 * hi;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -166,10 +167,11 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
   extern __shared__ __align__(16) uint16_t lds[];   // [stage][A, B][256 x 64]
   constexpr bool kGU = KIND == kGateUp || KIND == kGateUpSave;
   constexpr bool kWG = KIND == kWgradGateUp || KIND == kWgradDown;
-  const int K = kWG ? offsets[E] : (kGU ? H : I);    // row stride of both operands
+  constexpr bool kDH = KIND == kBwdDh;   // backward dh = W_down^T dout: gathered dout rows, K = H
+  const int K = kWG ? offsets[E] : (kGU || kDH ? H : I);    // row stride of both operands
   const int nA = KIND == kWgradGateUp ? H / 256 : I / 256;       // (weight gradients)
   const int nB = KIND == kWgradGateUp ? 2 * I / 256 : H / 256;
-  const int nblk = kGU ? I / 128 : H / 256;
+  const int nblk = kGU ? I / 128 : kDH ? I / 256 : H / 256;
   const int nk = K / kLBK;
   const int L = blockIdx.x;
   int item, kb = 0, ke = nk, slot = -1;
@@ -227,8 +229,9 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     // tile rows 0..127: gate neurons n0.., rows 128..255: up neurons n0..
     ao = static_cast<uint32_t>(((wv < 2 ? n0 + wv * 64 : I + n0 + (wv - 2) * 64) + lrow) * H + lc * 8);
   } else {
+    // down: wt = W_down [E][H][I] (rows h, K = I); kDH: W_down transposed [E][I][H]
     abase = wt + static_cast<size_t>(e) * H * I;
-    ao = static_cast<uint32_t>((nb * 256 + wv * 64 + lrow) * I + lc * 8);
+    ao = static_cast<uint32_t>((nb * 256 + wv * 64 + lrow) * K + lc * 8);
   }
   uint32_t bo[8];
 #pragma unroll
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     const int r = wv * 64 + 8 * j + lrow;
     const int rr = r < mcount ? r : 0;
     bo[j] = kWG ? static_cast<uint32_t>((bb * 256 + r) * K + lc * 8)
-          : kGU ? static_cast<uint32_t>((perm[rbase + rr] / k) * H + lc * 8)
+          : kGU || kDH ? static_cast<uint32_t>((perm[rbase + rr] / k) * H + lc * 8)
                 : static_cast<uint32_t>((rbase + rr) * I + lc * 8);
   }
   // LDS: row r, 16-byte chunk c at r*64 + ((c ^ (r & 7)) * 8); here r & 7 == lrow
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
     const float* __restrict__ partial, int ncu, int nk, float* __restrict__ gu) {
   constexpr bool kGU = KIND == kGateUp || KIND == kGateUpSave;
   constexpr int kPerItem = kGU ? 32 * 256 : 64 * 256;   // threads per tail item
-  const int nblk = kGU ? I / 128 : H / 256;
+  const int nblk = kGU ? I / 128 : KIND == kBwdDh ? I / 256 : H / 256;
   const TailPlan plan = tail_plan(nblk * *n_tiles, ncu, nk);
   const int g = blockIdx.x * 256 + threadIdx.x;
   const int b = g / kPerItem;
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
     for (int t4 = 0; t4 < 4; ++t4) p[t4] = f32_to_bf16_rne(wt_t * a[t4]);
     *reinterpret_cast<uint2*>(o) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
   } else {
-    *reinterpret_cast<f32x4*>(y + static_cast<size_t>(rbase + r) * H + nb * 256 + wn * 128 + 32 * i +
+    *reinterpret_cast<f32x4*>(y + static_cast<size_t>(rbase + r) * (KIND == kBwdDh ? I : H) + nb * 256 + wn * 128 + 32 * i +
                               8 * q + 4 * hi) = a;
   }
 }
@@ -948,6 +951,20 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int B, int R, int C, uint1
   return hipGetLastError();
 }
 
+hipError_t launch_dh_large(const uint16_t* dout, const uint16_t* wdT, const int* perm,
+                           const int2* tiles, const int* n_tiles, const int* counts,
+                           const int* offsets, int H, int I, int k, float* dh, float* partial,
+                           int max_tiles, int ncu, hipStream_t s) {
+  const int grid = large_grid(I / 256, max_tiles, ncu);
+  hipLaunchKernelGGL(gemm_large_bf16<kBwdDh>, dim3(grid), dim3(256), kLLds, s, dout, wdT, perm,
+                     tiles, n_tiles, counts, offsets, nullptr, H, I, k, nullptr, dh, nullptr,
+                     partial, ncu, nullptr, 0);
+  hipLaunchKernelGGL(gemm_large_fixup<kBwdDh>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,
+                     n_tiles, counts, offsets, nullptr, H, I, nullptr, dh, nullptr, partial, ncu,
+                     H / kLBK, nullptr);
+  return hipGetLastError();
+}
+
 hipError_t launch_dgrad_large(const uint16_t* act, const uint16_t* wT, const int* perm,
                               const int2* tiles, const int* n_tiles, const int* counts,
                               const int* offsets, int H, int K, int k, float* y, uint16_t* out,
@@ -971,6 +988,9 @@ hipError_t large_set_attributes() {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kGateUpSave>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kBwdDh>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kDownPlain>),

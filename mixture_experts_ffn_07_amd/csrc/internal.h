@@ -83,6 +83,12 @@ size_t wgrad_large_cols(int P, int E);
 // dst[b] = src[b]^T for B row-major R x C BF16 matrices (R, C multiples of 64)
 hipError_t launch_transpose_bf16(const uint16_t* src, int B, int R, int C, uint16_t* dst,
                                  hipStream_t s);
+// dh[r][i] = sum_h W_down[e][h][i] dout[perm[r] / k][h] for each grouped row r
+// (256-row M-tiles) on the large-group GEMM; wdT = W_down transposed, [E][I][H].
+hipError_t launch_dh_large(const uint16_t* dout, const uint16_t* wdT, const int* perm,
+                           const int2* tiles, const int* n_tiles, const int* counts,
+                           const int* offsets, int H, int I, int k, float* dh, float* partial,
+                           int max_tiles, int ncu, hipStream_t s);
 // Data gradient of a projection on the large-group GEMM: for each grouped row r
 // (256-row M-tiles), D[r][n] = sum_c act[r][c] wT[e][n][c], c < K, n < H; k = 1
 // writes out[perm[r]] = bf16(D), k > 1 writes y[r] = D (FP32).
@@ -107,6 +113,7 @@ struct BackwardWs {
   size_t counts, offsets, tiles, n_tiles, perm, row_of, gu, dgu, wa, dwp, dxs, total;
   size_t koff, xT, doutT, dguT, waT;   // large groups: the weight gradients' operands
   size_t tiles256, n_tiles256, wguT, partial;   // large groups: dx on the large-group GEMM
+  size_t wdT, dh;                                // large groups: dh on the large-group GEMM
   int max_tiles, max_tiles256;
   bool large_w;                        // weight gradients on the large-group GEMM
 };
