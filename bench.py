@@ -512,9 +512,11 @@ def main():
         peak_tf = MFMA_PEAK_TFLOPS[cfg.dtype]
         rows_per_expert = cfg.T * cfg.k / cfg.E
         if rows_per_expert >= 256:       # weight reuse high enough to be MFMA-bound
+            traffic, tprof = traffic_for("gemm_gate_up", cfg.name)
             roof = {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": round(r["kernel_tflops"], 1),
                     "peak": peak_tf, "unit": "TFLOP/s", "frac": round(r["kernel_tflops"] / peak_tf, 4),
-                    "traffic": None, "avg_launch_us": round(r["kernel_avg_us"], 2),
+                    "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": tprof,
+                    "avg_launch_us": round(r["kernel_avg_us"], 2),
                     "launch_us": r["kernel_pct_us"],
                     "algorithmic_flops_per_launch": int(r["kernel_flops_per_launch"]),
                     "hbm_gbs": round(r["kernel_gbs"], 1)}
