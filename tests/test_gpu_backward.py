@@ -161,6 +161,13 @@ def test_backward_large_groups_with_empty_expert(M):
     _check(M, d, "bwd large groups, one empty expert, saved", saved=True)
 
 
+def test_backward_large_groups_padded_grid(M):
+    # E = 3 experts, H = I = 256: 6 dW_gate_up and 3 dW_down blocks of 256 x 256, so the
+    # weight-gradient grids carry idle padding workgroups; k = 1 writes dx directly
+    d = _custom(800, 256, 256, 3, 1, seed=41)
+    _check(M, d, "bwd large groups, E = 3", saved=True)
+
+
 def test_backward_bit_identical_repeats(M):
     d = _custom(600, 512, 256, 12, 4, seed=5)
     dout = W.make_output_grad(d["cfg"], seed=1, device="cuda")
