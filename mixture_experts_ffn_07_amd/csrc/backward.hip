@@ -791,7 +791,7 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
                              reinterpret_cast<int*>(b + L.koff), reinterpret_cast<uint16_t*>(b + L.xT),
                              reinterpret_cast<uint16_t*>(b + L.doutT),
                              reinterpret_cast<uint16_t*>(b + L.dguT),
-                             reinterpret_cast<uint16_t*>(b + L.waT), dwgu, dwd, s);
+                             reinterpret_cast<uint16_t*>(b + L.waT), dwgu, dwd, num_cus, s);
     if (err != hipSuccess) return err;
   } else {
     prof_begin(kBwdWDown, s);

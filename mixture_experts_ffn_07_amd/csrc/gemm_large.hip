@@ -73,6 +73,29 @@ __device__ __forceinline__ void large_coords(int item, int nblk, int n_tiles, in
   tile = t0 + (r - nb * gm);
 }
 
+// Workgroup -> item across XCDs.  One workgroup fills a CU, so the ncu
+// workgroups resident at a time are consecutive; mapping each such round to one
+// contiguous run of items (XCD x, = L mod 8, taking the x-th chunk of it) keeps
+// every CU on the same one or two experts at a time, whose operands then stay in
+// the last-level cache (spreading the XCDs over the whole item range put six
+// experts' weights, 352 MB on the BF16 EP share, in flight at once).  n is a
+// multiple of 8; a last partial round keeps the contiguous-per-XCD split.
+__device__ __forceinline__ int round_item(int L, int n, int ncu) {
+  if (ncu < kXcds || ncu % kXcds) return xcd_item(L, n);
+  const int full = n / ncu * ncu;
+  if (L < full) {
+    const int r = L / ncu, w = L - r * ncu;
+    return r * ncu + (w % kXcds) * (ncu / kXcds) + w / kXcds;
+  }
+  return full + xcd_item(L - full, n - full);
+}
+__device__ __forceinline__ int round_real_item(int L, int nblk, int n_tiles, int ncu) {
+  const int n_real = (nblk * n_tiles + kXcds - 1) / kXcds * kXcds;
+  if (L >= n_real) return -1;
+  const int item = round_item(L, n_real, ncu);
+  return item / nblk < n_tiles ? item : -1;
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -180,7 +203,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     const int per = nA * nB, n_w = E * per;
     const int n_pad = (n_w + kXcds - 1) / kXcds * kXcds;
     if (L >= n_pad) return;
-    item = xcd_item(L, n_pad);
+    item = round_item(L, n_pad, ncu);
     if (item >= n_w) return;
     e = item / per;
     large_coords(item - e * per, nA, nB, bb, nb);
@@ -190,7 +213,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     const int n_real = nblk * *n_tiles;
     const TailPlan plan = tail_plan(n_real, ncu, nk);
     if (plan.S > 1 && L < plan.full) {
-      item = xcd_item(L, plan.full);
+      item = round_item(L, plan.full, ncu);
     } else if (plan.S > 1) {
       const int t = L - plan.full;
       if (t >= plan.rem * plan.S) return;
@@ -200,7 +223,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
       ke = (sl + 1) * nk / plan.S;
       slot = t;
     } else {
-      item = real_item(L, nblk, *n_tiles);
+      item = round_real_item(L, nblk, *n_tiles, ncu);
       if (item < 0) return;
     }
     int tile;
@@ -510,7 +533,7 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
   const int L = blockIdx.x;
   int item, kb = 0, ke = nk, slot = -1;
   if (plan.S > 1 && L < plan.full) {
-    item = xcd_item(L, plan.full);
+    item = round_item(L, plan.full, ncu);
   } else if (plan.S > 1) {
     const int t = L - plan.full;
     if (t >= plan.rem * plan.S) return;
@@ -520,7 +543,7 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
     ke = (sl + 1) * nk / plan.S;
     slot = t;
   } else {
-    item = real_item(L, nblk, *n_tiles);
+    item = round_real_item(L, nblk, *n_tiles, ncu);
     if (item < 0) return;
   }
   int tile, nb;
@@ -889,7 +912,7 @@ hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uin
                               const uint16_t* wa, const int* perm, const int* counts,
                               const int* offsets, int P, int H, int I, int E, int k, int* koff,
                               uint16_t* xT, uint16_t* doutT, uint16_t* dguT, uint16_t* waT,
-                              uint16_t* dwgu, uint16_t* dwd, hipStream_t s) {
+                              uint16_t* dwgu, uint16_t* dwd, int ncu, hipStream_t s) {
   const unsigned gtiles = static_cast<unsigned>((wgrad_large_cols(P, E) + 63) / 64);
   hipLaunchKernelGGL(wgrad_koff, dim3(1), dim3(64), 0, s, counts, E, koff);
   auto grid_w = [&](int nA, int nB) {
@@ -902,7 +925,7 @@ hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uin
                      counts, offsets, koff, E, doutT);
   hipLaunchKernelGGL(gemm_large_bf16<kWgradDown>, grid_w(I / 256, H / 256), dim3(256), kLLds, s,
                      doutT, waT, perm, nullptr, nullptr, counts, koff, nullptr, H, I, k, nullptr,
-                     nullptr, dwd, nullptr, 0, nullptr, E);
+                     nullptr, dwd, nullptr, ncu, nullptr, E);
   prof_end(kBwdWDown, s);
   prof_begin(kBwdWGateUp, s);
   hipLaunchKernelGGL(wgrad_transpose<true>, dim3(gtiles, H / 64), dim3(256), 0, s, x, H, perm, k,
@@ -911,7 +934,7 @@ hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uin
                      perm, k, counts, offsets, koff, E, dguT);
   hipLaunchKernelGGL(gemm_large_bf16<kWgradGateUp>, grid_w(H / 256, 2 * I / 256), dim3(256), kLLds,
                      s, dguT, xT, perm, nullptr, nullptr, counts, koff, nullptr, H, I, k, nullptr,
-                     nullptr, dwgu, nullptr, 0, nullptr, E);
+                     nullptr, dwgu, nullptr, ncu, nullptr, E);
   prof_end(kBwdWGateUp, s);
   return hipGetLastError();
 }

@@ -100,7 +100,7 @@ hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uin
                               const uint16_t* wa, const int* perm, const int* counts,
                               const int* offsets, int P, int H, int I, int E, int k, int* koff,
                               uint16_t* xT, uint16_t* doutT, uint16_t* dguT, uint16_t* waT,
-                              uint16_t* dwgu, uint16_t* dwd, hipStream_t s);
+                              uint16_t* dwgu, uint16_t* dwd, int ncu, hipStream_t s);
 hipError_t large_set_attributes();
 
 // Stable expert grouping of the T*k routed pairs into M-tiles of BM rows
