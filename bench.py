@@ -46,7 +46,7 @@ CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 # as null until the counters are taken again.
 TRAFFIC = {
     ("decode_gate_up", "qwen3-decode-T32"): (
-        711.0e6, ('decode.hip', 'common.h', 'internal.h'), "c47d76b3ca6d6859",
+        711.0e6, ('decode.hip', 'common.h', 'internal.h'), "0b2208813448af41",
         "profiles/decode_gate_up_qwen3-decode-T32.md"),
     ("gemm_gate_up", "kimi-bf16-T2048"): (
         23002.0e6, ('batched.hip', 'common.h', 'tiles.h'), "d7acc4ad1d9e06be",
@@ -55,10 +55,10 @@ TRAFFIC = {
         13212.0e6, ('batched.hip', 'common.h', 'tiles.h'), "d7acc4ad1d9e06be",
         "profiles/gemm_gate_up_glm-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
-        2000.8e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "e2dee5cd2fce5c97",
+        2000.8e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "0af50bb4116dbc85",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
-        23710.0e6, ('backward.hip', 'common.h', 'tiles.h'), "7eeb98b787d506ee",
+        23710.0e6, ('backward.hip', 'common.h', 'tiles.h'), "4f77db38fefb9408",
         "profiles/bwd_wgate_up_kimi-bf16-T2048.md"),
 }
 
