@@ -14,7 +14,7 @@
 //   dlogits[t, m]  = w_m (dw_m - sum_j w_j dw_j) over the selected experts m
 //
 // Launches, all on the caller's stream, in this order:
-//   group_experts   the forward's grouping (64-row M-tiles, stable order)
+//   group_experts   the forward's grouping (64- or 128-row M-tiles, stable order)
 //   kGU   gu[row]  = [W_gate; W_up][e] x[t]                FP32, recomputed when the
 //                   caller has not kept the forward's pre-activations
 //   kDD   dh tile  = W_down[e]^T dout[t]; epilogue: dgu[row] = [dg; du] (BF16), the
@@ -28,6 +28,13 @@
 //
 // Every sum runs in a fixed order (MFMA K order, rows ascending within an
 // expert, slots ascending), so repeated runs are bit-identical.
+//
+// With 256 or more routed rows per expert on average (MFMA-bound) kDD, kDG, kWD
+// and kWG run instead on the 256 x 256 large-group GEMM (gemm_large.hip) over a
+// second, 256-row tiling of the same grouping: W_down and W_gate_up transposed
+// for dh and dx (dh goes through FP32, then bwd_dh_finish applies kDD's
+// epilogue), and x, dout, [dg; du] and w a laid out K-contiguous per expert for
+// the weight gradients.
 //
 // The three activation-gradient GEMMs share one LDS-tiled kernel (bwd_gemm):
 // a workgroup of 4 waves computes a 64-row x 128-column tile in K chunks of

@@ -23,6 +23,12 @@
 // LDS writes are the scarce resource on gfx950 (about a quarter of the read
 // bandwidth), which is why the tile is as large as the register file allows:
 // every staged byte feeds 128 MFMA columns.
+//
+// The same BF16 kernel serves the backward pass of such batches: dx = [dg; du]
+// W_gate_up with W_gate_up transposed (kDownPlain, kDownSlots), dh = W_down^T
+// dout with W_down transposed and the dout rows gathered (kBwdDh), and both
+// weight gradients over transposed, zero-padded operands (kWgradDown,
+// kWgradGateUp); the transposes and the column-offset scan are at the end.
 #include "common.h"
 #include "internal.h"
 #include "tiles.h"
