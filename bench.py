@@ -55,10 +55,10 @@ TRAFFIC = {
         13212.0e6, ('batched.hip', 'common.h', 'tiles.h'), "d7acc4ad1d9e06be",
         "profiles/gemm_gate_up_glm-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
-        2000.8e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "0af50bb4116dbc85",
+        2001.1e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "cffb3d703e47262c",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
-        23710.0e6, ('backward.hip', 'common.h', 'tiles.h'), "4f77db38fefb9408",
+        23710.0e6, ('backward.hip', 'common.h', 'tiles.h'), "70fd8c6cb2280414",
         "profiles/bwd_wgate_up_kimi-bf16-T2048.md"),
 }
 
