@@ -46,7 +46,7 @@ CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 # as null until the counters are taken again.
 TRAFFIC = {
     ("decode_gate_up", "qwen3-decode-T32"): (
-        711.0e6, ('decode.hip', 'common.h', 'internal.h'), "0b2208813448af41",
+        711.0e6, ('decode.hip', 'common.h', 'internal.h'), "6b16bcaf553d155d",
         "profiles/decode_gate_up_qwen3-decode-T32.md"),
     ("gemm_gate_up", "kimi-bf16-T2048"): (
         23002.0e6, ('batched.hip', 'common.h', 'tiles.h'), "d7acc4ad1d9e06be",
@@ -58,7 +58,7 @@ TRAFFIC = {
         2001.1e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "cffb3d703e47262c",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
-        23710.0e6, ('backward.hip', 'common.h', 'tiles.h'), "70fd8c6cb2280414",
+        23710.0e6, ('backward.hip', 'common.h', 'tiles.h'), "61fcc7d088494cab",
         "profiles/bwd_wgate_up_kimi-bf16-T2048.md"),
 }
 

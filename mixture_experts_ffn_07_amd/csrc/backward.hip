@@ -65,6 +65,11 @@ constexpr int kKC = 64;          // K chunk (elements)
 constexpr int kNT = 128;         // output columns per workgroup
 constexpr int kCS32 = kNT + 4;   // FP32 C-tile row stride (elements)
 constexpr int kMB = 8;           // 128-row output blocks per weight-gradient workgroup
+// Weight gradients on the large-group GEMM from this many routed rows per expert
+// on average: below it an expert's reduction is one or two 64-row stages and the
+// per-block fixed costs dominate (measured at 64 rows: 5.9 -> 10.2 ms for the two
+// weight gradients of the GLM-5.2 shape; at 43: 7.3 -> 15.6 ms for Kimi's).
+constexpr int kWgradLargeRows = 256;
 
 inline size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
@@ -668,17 +673,22 @@ BackwardWs backward_ws_layout(int T, int H, int I, int E, int k) {
   L.dwp = o;      o = align256(o + sizeof(float) * P * (I / kNT));
   L.dxs = o;
   if (k > 1) o = align256(o + sizeof(float) * P * H);
-  // >= 256 routed rows per expert on average: the weight gradients run on the
-  // large-group GEMM over transposed operands (32-bit element offsets into them)
+  // >= kWgradLargeRows routed rows per expert on average: the weight gradients
+  // run on the large-group GEMM over transposed operands (32-bit element offsets
+  // into them); >= 256 (MFMA-bound): dh and dx too
   const size_t cols = wgrad_large_cols(static_cast<int>(P), E);
   const size_t rows_max = static_cast<size_t>(H > 2 * I ? H : 2 * I);
-  L.large_w = P >= static_cast<size_t>(256) * E && rows_max * cols < (static_cast<size_t>(1) << 31);
+  L.large_w = P >= static_cast<size_t>(kWgradLargeRows) * E &&
+              rows_max * cols < (static_cast<size_t>(1) << 31);
+  L.large_d = P >= static_cast<size_t>(256) * E;
   if (L.large_w) {
     L.koff = o;   o = align256(o + sizeof(int) * (E + 1));
     L.xT = o;     o = align256(o + sizeof(uint16_t) * H * cols);
     L.doutT = o;  o = align256(o + sizeof(uint16_t) * H * cols);
     L.dguT = o;   o = align256(o + sizeof(uint16_t) * 2 * I * cols);
     L.waT = o;    o = align256(o + sizeof(uint16_t) * I * cols);
+  }
+  if (L.large_d) {
     L.max_tiles256 = static_cast<int>(E + (P + kLargeBM - 1) / kLargeBM);
     L.n_tiles256 = o; o += 256;
     L.tiles256 = o;   o = align256(o + sizeof(int) * 2 * L.max_tiles256);
@@ -750,17 +760,17 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   }
   // large groups: 256-row M-tiles over the same (deterministic) grouping for the
   // large-group GEMMs of dh and dx
-  int2* tiles256 = L.large_w ? reinterpret_cast<int2*>(b + L.tiles256) : nullptr;
-  int* n_tiles256 = L.large_w ? reinterpret_cast<int*>(b + L.n_tiles256) : nullptr;
-  float* partial = L.large_w ? reinterpret_cast<float*>(b + L.partial) : nullptr;
-  if (L.large_w) {
+  int2* tiles256 = L.large_d ? reinterpret_cast<int2*>(b + L.tiles256) : nullptr;
+  int* n_tiles256 = L.large_d ? reinterpret_cast<int*>(b + L.n_tiles256) : nullptr;
+  float* partial = L.large_d ? reinterpret_cast<float*>(b + L.partial) : nullptr;
+  if (L.large_d) {
     err = launch_group_experts(idx, P, E, kLargeBM, const_cast<int*>(a.counts),
                                const_cast<int*>(a.offsets), tiles256, n_tiles256,
                                const_cast<int*>(a.perm), row_of, s);
     if (err != hipSuccess) return err;
   }
   prof_begin(kBwdDown, s);
-  if (L.large_w) {
+  if (L.large_d) {
     // dh on the large-group GEMM (W_down transposed to [E][I][H]), then the
     // SwiGLU backward, w a and the partial dots elementwise
     uint16_t* wdT = reinterpret_cast<uint16_t*>(b + L.wdT);
@@ -778,7 +788,7 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   }
   prof_end(kBwdDown, s);
   prof_begin(kBwdInput, s);
-  if (L.large_w) {
+  if (L.large_d) {
     // dx on the large-group GEMM: W_gate_up transposed to [E][H][2I]
     uint16_t* wguT = reinterpret_cast<uint16_t*>(b + L.wguT);
     err = launch_transpose_bf16(wgu, E, 2 * I, H, wguT, s);

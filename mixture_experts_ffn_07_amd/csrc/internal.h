@@ -116,6 +116,7 @@ struct BackwardWs {
   size_t wdT, dh;                                // large groups: dh on the large-group GEMM
   int max_tiles, max_tiles256;
   bool large_w;                        // weight gradients on the large-group GEMM
+  bool large_d;                        // dh and dx on the large-group GEMM
 };
 BackwardWs backward_ws_layout(int T, int H, int I, int E, int k);
 // gu_saved: NULL (the pre-activations are recomputed) or [T*k, 2I] FP32, slot order
