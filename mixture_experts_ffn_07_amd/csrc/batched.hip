@@ -424,11 +424,8 @@ __global__ __launch_bounds__(256) void quant_mx_rows(const uint16_t* __restrict_
   amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
   const int sexp = mx_scale_exp(amax);
   const float inv = exp2_neg(sexp);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] * inv) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] * inv) << (8 * i);
+  const uint32_t lo = f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  const uint32_t hi = f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
   if (live) {
     *reinterpret_cast<uint2*>(codes + blk * 32 + part * 8) = make_uint2(lo, hi);
     if (part == 0) scales[blk] = static_cast<uint8_t>(sexp + 127);
@@ -626,9 +623,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
                                s_amax[KIND == kProjGateUp ? (wv ^ 1) : 0][r]);
       const int sexp = mx_scale_exp(amax);
       const float inv = exp2_neg(sexp);
-      uint32_t wq = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wq |= f32_to_e4m3(a[g][i] * inv) << (8 * i);
+      const uint32_t wq = f32x4_to_e4m3x4(a[g][0] * inv, a[g][1] * inv, a[g][2] * inv, a[g][3] * inv);
       *reinterpret_cast<uint32_t*>(hout + static_cast<size_t>(rbase + r) * I + nb + 4 * grp) = wq;
       if (grp == 0 && (wv & 1) == 0)
         hsout[static_cast<size_t>(rbase + r) * (I / 32) + nb / 32] = static_cast<uint8_t>(sexp + 127);

@@ -105,4 +105,17 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return sign | mag;
 }
 
+// Four FP32 -> four E4M3 codes, code t in byte t: the hardware conversion
+// (round to nearest even) on inputs clamped to +-448 (exactly representable),
+// which yields the codes of f32_to_e4m3 - checked on every E4M3 value, every
+// midpoint between neighbours and its 1-ulp neighbours, and 2e6 random inputs.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
+  const float lo = -448.0f, hi = 448.0f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi),
+                                          __builtin_amdgcn_fmed3f(b, lo, hi), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, lo, hi),
+                                      __builtin_amdgcn_fmed3f(d, lo, hi), w, true);
+  return static_cast<uint32_t>(w);
+}
+
 }  // namespace moe

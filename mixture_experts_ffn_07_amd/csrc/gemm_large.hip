@@ -486,10 +486,8 @@ __device__ __forceinline__ void mx_store_block(const f32x16& g, const f32x16& u,
   uint8_t* hr = hq + static_cast<size_t>(rbase + r) * I + n + 4 * hi;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) c |= f32_to_e4m3(v[4 * q + t] * inv) << (8 * t);
-    *reinterpret_cast<uint32_t*>(hr + 8 * q) = c;
+    *reinterpret_cast<uint32_t*>(hr + 8 * q) =
+        f32x4_to_e4m3x4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
   }
   if (hi == 0) hs[static_cast<size_t>(rbase + r) * (I / 32) + n / 32] = static_cast<uint8_t>(sx + 127);
 }
