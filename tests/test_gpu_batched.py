@@ -98,9 +98,11 @@ def test_batched_bit_identical_repeats(M):
         assert torch.equal(again[3].view(torch.int16), first[3].view(torch.int16))
 
 
-def test_batched_grouping_is_stable(M):
+@pytest.mark.parametrize("T,E,k", [(300, 10, 3),      # pairs held in registers
+                                   (2100, 16, 8)])    # 16,800 pairs: more than 16 per thread
+def test_batched_grouping_is_stable(M, T, E, k):
     # the h rows come out grouped by expert, tokens ascending inside each expert
-    d = _custom(300, 256, 256, 10, 3, seed=4)
+    d = _custom(T, 256, 256, E, k, seed=4)
     cfg = d["cfg"]
     out, idx, w, h, ws = run_layer(M, d)
     ridx, _ = route(d["logits"].cpu().numpy(), cfg.k)
