@@ -60,9 +60,12 @@ typedef enum {
 } moe_dtype;
 
 /*
- * moe_route_topk -- top-k expert routing with renormalised softmax weights
- * (warp-decode article, "Background": expert routing picks each token's
- * experts; "Key points": the routed experts).
+ * moe_route_topk -- top-k expert routing (warp-decode article, "Background":
+ * expert routing picks each token's experts; "Key points": the routed
+ * experts).  The pages name the step but give no gate function, selection
+ * rule or tie-break; this library reads them as: select on the FP32 logits,
+ * order by (logit descending, index ascending), and weight the k selected
+ * experts by softmax renormalised over them.
  *
  *   logits   [T, E] float32, finite
  *   topk_idx [T, k] int32 out: slot j holds the j-th expert in the order
@@ -92,7 +95,8 @@ int moe_route_topk(const float* logits, int T, int E, int k,
  *   workspace   >= moe_decode_workspace_bytes(T, H, I, E, k) bytes of device
  *               memory, contents ignored on entry and overwritten
  * Limits: 1 <= T <= 64 and I <= 2048 (otherwise MOE_ERR_UNSUPPORTED: use the
- * batched calls), H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024.
+ * batched calls), H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024,
+ * 2*I*H < 2^31 (MOE_ERR_SHAPE otherwise).
  * Only the weights of experts that some token routes to are read.
  */
 int moe_decode_forward(const uint16_t* x, const float* logits,
@@ -140,12 +144,14 @@ int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int K,
  *              writes the expert grouping into it, and moe_down_3d_batched
  *              must be given the same workspace and topk_idx, later on the
  *              same stream
- * Limits: T >= 1, H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024.
+ * Limits: T >= 1, H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024;
+ * T*H, T*k*H, T*k*I and 2*I*H each below 2^31 (the kernels' 32-bit element
+ * offsets).  MOE_ERR_SHAPE otherwise.
  */
 int moe_gate_up_3d_batched(const void* x, const uint8_t* x_scales,
                            const void* w_gate_up, const uint8_t* w_gate_up_scales,
                            const int32_t* topk_idx,
-                           int T, int H, int I, int E, int k, int dtype,
+                           int T, int H, int I, int E, int k, moe_dtype dtype,
                            void* h, uint8_t* h_scales,
                            void* workspace, size_t workspace_bytes, void* stream);
 
@@ -167,11 +173,11 @@ int moe_gate_up_3d_batched(const void* x, const uint8_t* x_scales,
 int moe_down_3d_batched(const void* h, const uint8_t* h_scales,
                         const void* w_down, const uint8_t* w_down_scales,
                         const int32_t* topk_idx, const float* topk_w,
-                        int T, int H, int I, int E, int k, int dtype,
+                        int T, int H, int I, int E, int k, moe_dtype dtype,
                         uint16_t* out,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-size_t moe_workspace_bytes(int T, int H, int I, int E, int k, int dtype);
+size_t moe_workspace_bytes(int T, int H, int I, int E, int k, moe_dtype dtype);
 
 /*
  * moe_gate_up_3d_batched_train -- moe_gate_up_3d_batched (BF16) that also keeps

@@ -88,15 +88,43 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)   # 16-bit patterns read as BF16
+
+
 def _u16(t: torch.Tensor) -> torch.Tensor:
-    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+    if t.dtype not in _BF16:
         raise TypeError(f"expected BF16 bits, got {t.dtype}")
     return t
+
+
+def _need(t: Optional[torch.Tensor], name: str, shape, dtypes, optional: bool = False) -> None:
+    """Check a tensor argument's shape and element type before any pointer is
+    handed to the library (a wrong size would become an out-of-bounds device
+    access; a wrong dtype, e.g. int64 indices, would be misread)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _need_ws(ws: torch.Tensor, nbytes: int) -> None:
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise TypeError("workspace must be a 1-D uint8 tensor")
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {nbytes} required")
 
 
 def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: torch.Tensor = None,
                    topk_w: torch.Tensor = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """logits [T, E] float32 -> (topk_idx [T, k] int32, topk_w [T, k] float32)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [T, E]")
     T, E = logits.shape
     if logits.dtype != torch.float32:
         raise TypeError("logits must be float32")
@@ -104,6 +132,8 @@ def moe_route_topk(logits: torch.Tensor, k: int, topk_idx: torch.Tensor = None,
         topk_idx = torch.empty(T, k, dtype=torch.int32, device=logits.device)
     if topk_w is None:
         topk_w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _need(topk_idx, "topk_idx", (T, k), torch.int32)
+    _need(topk_w, "topk_w", (T, k), torch.float32)
     _check("moe_route_topk", lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx),
                                                 _ptr(topk_w), _stream(stream)))
     return topk_idx, topk_w
@@ -133,11 +163,16 @@ def moe_decode_forward(x: torch.Tensor, logits: torch.Tensor, w_gate_up: torch.T
     if logits.shape != (T, E) or H2 != H or tuple(w_down.shape) != (E, H, I):
         raise ValueError("inconsistent shapes")
     _u16(x), _u16(w_gate_up), _u16(w_down)
+    _need(logits, "logits", (T, E), torch.float32)
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", (T, H), _BF16)
+    _need(topk_idx, "topk_idx", (T, k), torch.int32, optional=True)
+    _need(topk_w, "topk_w", (T, k), torch.float32, optional=True)
     need = moe_decode_workspace_bytes(T, H, I, E, k)
     if ws is None:
         ws = workspace(need, x.device)
+    _need_ws(ws, need)
     _check("moe_decode_forward", lib.moe_decode_forward(
         _ptr(x), _ptr(logits), _ptr(w_gate_up), _ptr(w_down), T, H, I, E, k, _ptr(out),
         _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)))
@@ -153,6 +188,8 @@ def moe_quantize_mxfp8(src: torch.Tensor, codes: torch.Tensor = None, scales: to
         codes = torch.empty(rows, K, dtype=torch.uint8, device=src.device)
     if scales is None:
         scales = torch.empty(rows, K // 32, dtype=torch.uint8, device=src.device)
+    _need(codes, "codes", (rows, K), torch.uint8)
+    _need(scales, "scales", (rows, K // 32), torch.uint8)
     _check("moe_quantize_mxfp8", lib.moe_quantize_mxfp8(_ptr(src), rows, K, _ptr(codes),
                                                         _ptr(scales), _stream(stream)))
     return codes, scales
@@ -162,15 +199,30 @@ def moe_gate_up_3d_batched(x, w_gate_up, topk_idx, k: int, dtype: int = MOE_BF16
                            w_gate_up_scales=None, h=None, h_scales=None, ws=None, stream=None):
     """Grouped gate/up projection + SwiGLU; returns (h, h_scales, ws)."""
     T, H = x.shape
-    E, I2, _ = w_gate_up.shape
+    E, I2, H2 = w_gate_up.shape
     I = I2 // 2
+    if H2 != H:
+        raise ValueError("w_gate_up must be [E, 2I, H] with the H of x")
+    mx = dtype == MOE_MXFP8
+    edt = torch.uint8 if mx else _BF16
+    _need(x, "x", (T, H), edt)
+    _need(w_gate_up, "w_gate_up", (E, I2, H), edt)
+    _need(topk_idx, "topk_idx", (T, k), torch.int32)
+    if mx:
+        _need(x_scales, "x_scales", (T, H // 32), torch.uint8)
+        _need(w_gate_up_scales, "w_gate_up_scales", (E, I2, H // 32), torch.uint8)
     if h is None:
         h = torch.empty(T * k, I, dtype=torch.bfloat16 if dtype == MOE_BF16 else torch.uint8,
                         device=x.device)
-    if dtype == MOE_MXFP8 and h_scales is None:
+    if mx and h_scales is None:
         h_scales = torch.empty(T * k, I // 32, dtype=torch.uint8, device=x.device)
+    _need(h, "h", (T * k, I), edt)
+    if mx:
+        _need(h_scales, "h_scales", (T * k, I // 32), torch.uint8)
+    need = moe_workspace_bytes(T, H, I, E, k, dtype)
     if ws is None:
-        ws = workspace(moe_workspace_bytes(T, H, I, E, k, dtype), x.device)
+        ws = workspace(need, x.device)
+    _need_ws(ws, need)
     _check("moe_gate_up_3d_batched", lib.moe_gate_up_3d_batched(
         _ptr(x), _ptr(x_scales), _ptr(w_gate_up), _ptr(w_gate_up_scales), _ptr(topk_idx),
         T, H, I, E, k, dtype, _ptr(h), _ptr(h_scales), _ptr(ws), ws.numel(), _stream(stream)))
@@ -182,8 +234,19 @@ def moe_down_3d_batched(h, w_down, topk_idx, topk_w, ws, k: int, dtype: int = MO
     """Grouped down projection + fixed-order weighted combine -> out [T, H] BF16."""
     T = topk_idx.shape[0]
     E, H, I = w_down.shape
+    mx = dtype == MOE_MXFP8
+    edt = torch.uint8 if mx else _BF16
+    _need(topk_idx, "topk_idx", (T, k), torch.int32)
+    _need(topk_w, "topk_w", (T, k), torch.float32)
+    _need(h, "h", (T * k, I), edt)
+    _need(w_down, "w_down", (E, H, I), edt)
+    if mx:
+        _need(h_scales, "h_scales", (T * k, I // 32), torch.uint8)
+        _need(w_down_scales, "w_down_scales", (E, H, I // 32), torch.uint8)
     if out is None:
         out = torch.empty(T, H, dtype=torch.bfloat16, device=h.device)
+    _need(out, "out", (T, H), _BF16)
+    _need_ws(ws, moe_workspace_bytes(T, H, I, E, k, dtype))
     _check("moe_down_3d_batched", lib.moe_down_3d_batched(
         _ptr(h), _ptr(h_scales), _ptr(w_down), _ptr(w_down_scales), _ptr(topk_idx),
         _ptr(topk_w), T, H, I, E, k, dtype, _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
@@ -201,12 +264,19 @@ def moe_gate_up_3d_batched_train(x, w_gate_up, topk_idx, k: int, h=None, gu=None
     T, H = x.shape
     E, I2, _ = w_gate_up.shape
     I = I2 // 2
+    _need(x, "x", (T, H), _BF16)
+    _need(w_gate_up, "w_gate_up", (E, I2, H), _BF16)
+    _need(topk_idx, "topk_idx", (T, k), torch.int32)
     if h is None:
         h = torch.empty(T * k, I, dtype=torch.bfloat16, device=x.device)
     if gu is None:
         gu = torch.empty(T * k, I2, dtype=torch.float32, device=x.device)
+    _need(h, "h", (T * k, I), _BF16)
+    _need(gu, "gu", (T * k, I2), torch.float32)
+    need = moe_workspace_bytes(T, H, I, E, k, MOE_BF16)
     if ws is None:
-        ws = workspace(moe_workspace_bytes(T, H, I, E, k, MOE_BF16), x.device)
+        ws = workspace(need, x.device)
+    _need_ws(ws, need)
     _check("moe_gate_up_3d_batched_train", lib.moe_gate_up_3d_batched_train(
         _ptr(x), _ptr(w_gate_up), _ptr(topk_idx), T, H, I, E, k, _ptr(h), _ptr(gu), _ptr(ws),
         ws.numel(), _stream(stream)))
@@ -221,6 +291,13 @@ def moe_backward_batched(x, w_gate_up, w_down, topk_idx, topk_w, dout, k: int, g
     E, I2, _ = w_gate_up.shape
     I = I2 // 2
     dev = x.device
+    _need(x, "x", (T, H), _BF16)
+    _need(w_gate_up, "w_gate_up", (E, I2, H), _BF16)
+    _need(w_down, "w_down", (E, H, I), _BF16)
+    _need(topk_idx, "topk_idx", (T, k), torch.int32)
+    _need(topk_w, "topk_w", (T, k), torch.float32)
+    _need(dout, "dout", (T, H), _BF16)
+    _need(gu_saved, "gu_saved", (T * k, I2), torch.float32, optional=True)
     if dx is None:
         dx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     if dw_gate_up is None:
@@ -231,8 +308,15 @@ def moe_backward_batched(x, w_gate_up, w_down, topk_idx, topk_w, dout, k: int, g
         d_topk_w = torch.empty(T, k, dtype=torch.float32, device=dev)
     if dlogits is None:
         dlogits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    _need(dx, "dx", (T, H), _BF16)
+    _need(dw_gate_up, "dw_gate_up", (E, I2, H), _BF16)
+    _need(dw_down, "dw_down", (E, H, I), _BF16)
+    _need(d_topk_w, "d_topk_w", (T, k), torch.float32)
+    _need(dlogits, "dlogits", (T, E), torch.float32)
+    need = moe_backward_workspace_bytes(T, H, I, E, k)
     if ws is None:
-        ws = workspace(moe_backward_workspace_bytes(T, H, I, E, k), dev)
+        ws = workspace(need, dev)
+    _need_ws(ws, need)
     _check("moe_backward_batched", lib.moe_backward_batched(
         _ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(topk_idx), _ptr(topk_w), _ptr(dout),
         _ptr(gu_saved), T, H, I, E, k, _ptr(dx), _ptr(dw_gate_up), _ptr(dw_down), _ptr(d_topk_w), _ptr(dlogits),

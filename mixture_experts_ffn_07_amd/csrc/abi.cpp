@@ -88,6 +88,18 @@ int check_common(int T, int H, int I, int E, int k, int hmul, int imul) {
   return MOE_OK;
 }
 
+// Element offsets the kernels form in 32-bit arithmetic: rows of x (T*H), of
+// the routed-pair buffers h and y (T*k*I, T*k*H) and of one expert's weights
+// (2I*H).  Each must stay below 2^31.
+int check_offsets(int T, int H, int I, int k) {
+  const long long lim = 1LL << 31;
+  if (static_cast<long long>(T) * H >= lim) return fail(MOE_ERR_SHAPE, "T*H reaches 2^31");
+  if (static_cast<long long>(T) * k * H >= lim) return fail(MOE_ERR_SHAPE, "T*k*H reaches 2^31");
+  if (static_cast<long long>(T) * k * I >= lim) return fail(MOE_ERR_SHAPE, "T*k*I reaches 2^31");
+  if (2LL * I * H >= lim) return fail(MOE_ERR_SHAPE, "2*I*H reaches 2^31");
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,6 +156,7 @@ int moe_decode_forward(const uint16_t* x, const float* logits, const uint16_t* w
   if (T == 0) return fail(MOE_ERR_SHAPE, "T=0: nothing to decode");
   if (T > 64) return fail(MOE_ERR_UNSUPPORTED, "T=%d > 64: use the batched calls", T);
   if (I > 2048) return fail(MOE_ERR_UNSUPPORTED, "I=%d > 2048: use the batched calls", I);
+  if (int st = check_offsets(T, H, I, k)) return st;
   if (!x || !logits || !w_gate_up || !w_down || !out)
     return fail(MOE_ERR_NULL, "x, logits, w_gate_up, w_down and out are required");
   if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
@@ -161,7 +174,7 @@ int moe_decode_forward(const uint16_t* x, const float* logits, const uint16_t* w
                     "moe_decode_forward launch");
 }
 
-size_t moe_workspace_bytes(int T, int H, int I, int E, int k, int dtype) {
+size_t moe_workspace_bytes(int T, int H, int I, int E, int k, moe_dtype dtype) {
   if (T < 1 || H <= 0 || I <= 0 || E < 1 || k < 1 || (dtype != MOE_BF16 && dtype != MOE_MXFP8))
     return 0;
   return moe::batched_ws_layout(T, H, I, E, k, dtype).total;
@@ -182,12 +195,14 @@ int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
                     "moe_quantize_mxfp8 launch");
 }
 
-static int check_batched(int T, int H, int I, int E, int k, int dtype, const void* ws,
+static int check_batched(int T, int H, int I, int E, int k, moe_dtype dtype, const void* ws,
                          size_t ws_bytes) {
   if (int st = check_common(T, H, I, E, k, 256, 256)) return st;
   if (T < 1) return fail(MOE_ERR_SHAPE, "T=%d < 1", T);
   if (dtype != MOE_BF16 && dtype != MOE_MXFP8) return fail(MOE_ERR_SHAPE, "dtype=%d", dtype);
   if (static_cast<long long>(T) * k > (1LL << 30)) return fail(MOE_ERR_SHAPE, "T*k too large");
+  // the kernels form 32-bit element offsets into x, h, y and one expert's weights
+  if (int st = check_offsets(T, H, I, k)) return st;
   if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
   const size_t need = moe::batched_ws_layout(T, H, I, E, k, dtype).total;
   if (ws_bytes < need)
@@ -198,7 +213,7 @@ static int check_batched(int T, int H, int I, int E, int k, int dtype, const voi
 
 int moe_gate_up_3d_batched(const void* x, const uint8_t* x_scales, const void* w_gate_up,
                            const uint8_t* w_gate_up_scales, const int32_t* topk_idx, int T, int H,
-                           int I, int E, int k, int dtype, void* h, uint8_t* h_scales,
+                           int I, int E, int k, moe_dtype dtype, void* h, uint8_t* h_scales,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (int st = check_batched(T, H, I, E, k, dtype, workspace, workspace_bytes)) return st;
   if (!x || !w_gate_up || !topk_idx || !h)
@@ -219,7 +234,7 @@ int moe_gate_up_3d_batched(const void* x, const uint8_t* x_scales, const void* w
 
 int moe_down_3d_batched(const void* h, const uint8_t* h_scales, const void* w_down,
                         const uint8_t* w_down_scales, const int32_t* topk_idx,
-                        const float* topk_w, int T, int H, int I, int E, int k, int dtype,
+                        const float* topk_w, int T, int H, int I, int E, int k, moe_dtype dtype,
                         uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (int st = check_batched(T, H, I, E, k, dtype, workspace, workspace_bytes)) return st;
   if (!h || !w_down || !topk_idx || !topk_w || !out)

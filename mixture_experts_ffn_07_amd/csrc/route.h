@@ -1,8 +1,11 @@
 // Top-k routing of one token by one 64-lane wave.
 //
-// Expert routing (warp-decode article, "Background"): experts are ordered by
-// logit descending, then expert index ascending, and the first k are kept; the weights are the softmax of the k selected logits
-// (softmax over all E renormalised over the selection).
+// Expert routing picks each token's experts (warp-decode article,
+// "Background"); the pages give neither the selection rule nor the gate
+// function, so both are readings: experts are ordered by FP32 logit
+// descending, then expert index ascending, and the first k are kept; the
+// weights are the softmax of the k selected logits (softmax over all E
+// renormalised over the selection).
 //
 // Each logit becomes a 32-bit key: its FP32 bits mapped to an unsigned order
 // (-0 folded onto +0; every finite logit maps above 0, which marks "taken").

@@ -171,3 +171,79 @@ def test_train_forward_validation(m):
     # T*k*2I must stay below 2^31 (pair-row offsets of gu are 32-bit)
     huge = m.lib.moe_workspace_bytes(1 << 20, 256, 1024, 8, 1, 0)
     assert call(T=1 << 20, I=1024, k=1, wsb=huge) == m.MOE_ERR_SHAPE
+
+
+def test_batched_offset_limits(m):
+    # the kernels form 32-bit element offsets: T*H, T*k*H, T*k*I and 2I*H must stay
+    # below 2^31 (checked before the workspace, so any size passes here)
+    g = m.lib.moe_gate_up_3d_batched
+    d = m.lib.moe_down_3d_batched
+    big = 1 << 60
+
+    def gate_up(T, H, I, E, k):
+        return g(FAKE, None, FAKE, None, FAKE, T, H, I, E, k, 0, FAKE, None, FAKE, big, None)
+
+    def down(T, H, I, E, k):
+        return d(FAKE, None, FAKE, None, FAKE, FAKE, T, H, I, E, k, 0, FAKE, FAKE, big, None)
+    for call in (gate_up, down):
+        assert call(300000, 7168, 256, 8, 1) == m.MOE_ERR_SHAPE            # T*H
+        assert b"T*H" in m.lib.moe_last_error()
+        assert call(1 << 18, 1024, 256, 8, 8) == m.MOE_ERR_SHAPE           # T*k*H = 2^31
+        assert b"T*k*H" in m.lib.moe_last_error()
+        assert call(1 << 18, 256, 1024, 8, 8) == m.MOE_ERR_SHAPE           # T*k*I = 2^31
+        assert b"T*k*I" in m.lib.moe_last_error()
+        assert call(4, 1 << 16, 1 << 14, 8, 2) == m.MOE_ERR_SHAPE          # 2*I*H = 2^31
+        assert b"2*I*H" in m.lib.moe_last_error()
+    # just below the limits the shape checks pass (here a misaligned h is next)
+    assert g(FAKE, None, FAKE, None, FAKE, 4, 1 << 16, (1 << 14) - 256, 8, 2, 0, FAKE + 4, None,
+             FAKE, big, None) == m.MOE_ERR_ALIGN
+    assert g(FAKE, None, FAKE, None, FAKE, (1 << 18) - 1, 1024, 256, 8, 8, 0, FAKE + 4, None,
+             FAKE, big, None) == m.MOE_ERR_ALIGN
+    # decode: one expert's weights, 2*I*H, must stay below 2^31
+    assert _dec(m, H=1 << 19, I=2048, wsb=big) == m.MOE_ERR_SHAPE
+    assert b"2*I*H" in m.lib.moe_last_error()
+
+
+def test_binding_validates_tensor_arguments(m):
+    # the Python wrappers check shapes and dtypes before any pointer reaches the
+    # library (CPU tensors of the right shape fail only at the device check)
+    import torch
+    T, H, I, E, k = 4, 256, 256, 8, 2
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    wgu = torch.zeros(E, 2 * I, H, dtype=torch.bfloat16)
+    wd = torch.zeros(E, H, I, dtype=torch.bfloat16)
+    logits = torch.zeros(T, E)
+    idx = torch.zeros(T, k, dtype=torch.int32)
+    tw = torch.zeros(T, k)
+    with pytest.raises(TypeError, match="topk_idx"):
+        m.moe_route_topk(logits, k, topk_idx=torch.zeros(T, k, dtype=torch.int64))
+    with pytest.raises(ValueError, match="topk_w"):
+        m.moe_route_topk(logits, k, topk_w=torch.zeros(T, k + 1))
+    with pytest.raises(ValueError, match="GPU"):
+        m.moe_route_topk(logits, k, topk_idx=idx, topk_w=tw)
+    with pytest.raises(TypeError, match="topk_idx"):
+        m.moe_gate_up_3d_batched(x, wgu, idx.long(), k, h=torch.zeros(T * k, I, dtype=torch.bfloat16),
+                                 ws=torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="h: shape"):
+        m.moe_gate_up_3d_batched(x, wgu, idx, k, h=torch.zeros(T * k - 1, I, dtype=torch.bfloat16),
+                                 ws=torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="x_scales"):
+        m.moe_gate_up_3d_batched(x.view(torch.uint8)[:, :H], wgu.view(torch.uint8)[..., :H], idx, k,
+                                 m.MOE_MXFP8, x_scales=torch.zeros(T, H // 16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="workspace"):
+        m.moe_gate_up_3d_batched(x, wgu, idx, k, h=torch.zeros(T * k, I, dtype=torch.bfloat16),
+                                 ws=torch.zeros(16, dtype=torch.uint8))
+    ws = torch.zeros(m.moe_workspace_bytes(T, H, I, E, k, m.MOE_BF16), dtype=torch.uint8)
+    h = torch.zeros(T * k, I, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out: shape"):
+        m.moe_down_3d_batched(h, wd, idx, tw, ws, k, out=torch.zeros(T, H + 1, dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="topk_w"):
+        m.moe_down_3d_batched(h, wd, idx, tw.double(), ws, k)
+    with pytest.raises(ValueError, match="GPU"):
+        m.moe_down_3d_batched(h, wd, idx, tw, ws, k)
+    with pytest.raises(ValueError, match="codes"):
+        m.moe_quantize_mxfp8(x, codes=torch.zeros(T, H - 32, dtype=torch.uint8))
+    with pytest.raises(TypeError, match="topk_idx"):
+        m.moe_decode_forward(x, logits, wgu, wd, k, topk_idx=tw)
+    with pytest.raises(ValueError, match="gu_saved"):
+        m.moe_backward_batched(x, wgu, wd, idx, tw, x, k, gu_saved=torch.zeros(T * k, I))

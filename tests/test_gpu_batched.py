@@ -98,8 +98,8 @@ def test_batched_bit_identical_repeats(M):
         assert torch.equal(again[3].view(torch.int16), first[3].view(torch.int16))
 
 
-@pytest.mark.parametrize("T,E,k", [(300, 10, 3),      # pairs held in registers
-                                   (2100, 16, 8)])    # 16,800 pairs: more than 16 per thread
+@pytest.mark.parametrize("T,E,k", [(300, 10, 3),      # 900 pairs: one pass of the 1,024 threads
+                                   (2100, 16, 8)])    # 16,800 pairs: several 1,024-pair passes
 def test_batched_grouping_is_stable(M, T, E, k):
     # the h rows come out grouped by expert, tokens ascending inside each expert
     d = _custom(T, 256, 256, E, k, seed=4)

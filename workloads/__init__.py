@@ -122,29 +122,38 @@ def _normal(shape, std, device, seed, tag, index=0) -> torch.Tensor:
 
 
 def _to_mxfp8(w: torch.Tensor):
-    """Store float32 weights [R, K] as E4M3 codes + E8M0 scale codes (blocks of
-    32 along K).  Scale: smallest s with 448 * 2^s >= block max |w|, decided
-    exactly from the binary exponent of the max (no logarithms)."""
-    R, K = w.shape
-    blocks = w.view(R, K // 32, 32)
+    """Store float32 weights [..., K] as E4M3 codes + E8M0 scale codes (blocks
+    of 32 along K), all leading rows at once.  Scale: smallest s with
+    448 * 2^s >= block max |w|, decided exactly from the binary exponent of the
+    max (no logarithms)."""
+    K = w.shape[-1]
+    lead = w.shape[:-1]
+    blocks = w.reshape(-1, K // 32, 32)
     amax = blocks.abs().amax(dim=-1)
     mant, expo = torch.frexp(amax)            # amax = mant * 2^expo, mant in [0.5, 1)
     # 448 * 2^(expo-9) = 0.875 * 2^expo  >= amax  <=>  mant <= 0.875
     s = torch.where(mant <= 0.875, expo - 9, expo - 8)
     s = torch.where(amax == 0, torch.full_like(s, -127), s).clamp(-127, 127)
     scaled = blocks * torch.pow(2.0, -s.to(torch.float32)).unsqueeze(-1)
-    codes = scaled.to(torch.float8_e4m3fn).view(torch.uint8).view(R, K)
-    scales = (s + 127).to(torch.uint8)
+    codes = scaled.to(torch.float8_e4m3fn).view(torch.uint8).reshape(*lead, K)
+    scales = (s + 127).to(torch.uint8).reshape(*lead, K // 32)
     return codes.contiguous(), scales.contiguous()
+
+
+# float32 elements drawn before one vectorised MX quantization (1 GiB)
+_MX_CHUNK_ELEMS = 1 << 28
 
 
 def make_weights(cfg: Config, seed: int = 0, device="cpu", experts=None) -> Dict[str, torch.Tensor]:
     """Expert weights: w_gate_up [E, 2I, H] (gate rows [0, I), up rows [I, 2I)),
     w_down [E, H, I]; K (the reduction dim) contiguous.  BF16 tensors, or uint8
     E4M3 codes plus uint8 E8M0 scale codes [.., K/32] for MXFP8 workloads.
-    ``experts`` restricts generation to a subset (others left zero)."""
+    ``experts`` restricts generation to a subset (others left zero).
+    Each expert's values come from its own seeded stream; MXFP8 experts are
+    drawn into a float32 chunk of several experts that is quantized in one
+    pass, so the number of device operations does not grow with E."""
     E, H, I = cfg.E, cfg.H, cfg.I
-    ids = range(E) if experts is None else experts
+    ids = list(range(E)) if experts is None else [int(e) for e in experts]
     out: Dict[str, torch.Tensor] = {}
     for name, (R, K) in (("w_gate_up", (2 * I, H)), ("w_down", (H, I))):
         if cfg.dtype == "bf16":
@@ -155,10 +164,21 @@ def make_weights(cfg: Config, seed: int = 0, device="cpu", experts=None) -> Dict
         elif cfg.dtype == "mxfp8":
             codes = torch.zeros(E, R, K, dtype=torch.uint8, device=device)
             scales = torch.zeros(E, R, K // 32, dtype=torch.uint8, device=device)
-            for e in ids:
-                c, s = _to_mxfp8(_normal((R, K), cfg.w_std, device, seed, name, e))
-                codes[e].copy_(c)
-                scales[e].copy_(s)
+            per = max(1, _MX_CHUNK_ELEMS // (R * K))
+            stage = torch.empty(min(per, max(len(ids), 1)), R, K, dtype=torch.float32,
+                                device=device)
+            for c0 in range(0, len(ids), per):
+                chunk = ids[c0:c0 + per]
+                for i, e in enumerate(chunk):
+                    torch.randn((R, K), generator=_gen(device, seed, name, e), out=stage[i])
+                f = stage[:len(chunk)]
+                if cfg.w_std != 1.0:
+                    f.mul_(cfg.w_std)
+                c, s = _to_mxfp8(f)
+                sel = torch.as_tensor(chunk, device=device)
+                codes.index_copy_(0, sel, c)
+                scales.index_copy_(0, sel, s)
+                del c, s
             out[name] = codes
             out[name + "_scales"] = scales
         else:
