@@ -56,7 +56,12 @@ typedef enum {
 
 typedef enum {
   MOE_BF16 = 0,   /* BF16 activations and weights                         */
-  MOE_MXFP8 = 1   /* E4M3 codes with one E8M0 scale per 32 along K          */
+  MOE_MXFP8 = 1,  /* E4M3 codes with one E8M0 scale per 32 along K          */
+  /* not element types: they make the enum span every int, so that an unknown
+   * value passed by a caller is a valid value of the type that the library
+   * rejects (MOE_ERR_SHAPE) rather than undefined behaviour in C++ */
+  MOE_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  MOE_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
 } moe_dtype;
 
 /*

@@ -42,9 +42,10 @@ def bf16_round(v) -> np.ndarray:
     return np.rint(v / q) * q                     # exact: q is a power of two
 
 
-def e4m3_decode(codes) -> np.ndarray:
-    """uint8 E4M3 codes -> float64 (exact); 0x7F / 0xFF decode to NaN."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _e4m3_value(c: np.ndarray) -> np.ndarray:
+    """The E4M3 definition, code by code: sign, 4-bit exponent (bias 7; 0 =
+    subnormal, m * 2^-9), 3-bit mantissa; S.1111.111 is NaN."""
+    c = np.asarray(c, dtype=np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     ex = (c >> 3) & 0xF
     man = (c & 0x7).astype(np.float64)
@@ -52,6 +53,16 @@ def e4m3_decode(codes) -> np.ndarray:
                    (1.0 + man / 8.0) * np.exp2((ex - 7).astype(np.float64)))
     mag = np.where((ex == 15) & (c & 0x7 == 7), np.nan, mag)
     return sign * mag
+
+
+# the value of every one of the 256 codes, from the definition above
+_E4M3_VALUES = _e4m3_value(np.arange(256))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """uint8 E4M3 codes -> float64 (exact); 0x7F / 0xFF decode to NaN.  Each
+    code is looked up among the 256 values the definition gives."""
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 def e8m0_decode(codes) -> np.ndarray:

@@ -21,6 +21,14 @@ def m():
     if not os.path.exists(B.LIB):
         B.build()
     import mixture_experts_ffn_07_amd as M
+    alt = os.environ.get("MOE_ABI_TEST_LIB")
+    if alt:     # a sanitizer build of the host code (tests/test_abi_sanitized.py)
+        lib = ctypes.CDLL(alt)
+        for name, (res, args) in M._SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        M.lib = lib
     return M
 
 

@@ -16,9 +16,8 @@ import pytest
 import torch
 
 import workloads as W
-from oracle import moe_backward
 from oracle.moe import rel_l2
-from tests._gpu import Fetch, bits, check_bf16, to_f64
+from tests._gpu import check_bf16, oracle_backward, sample_tokens, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -58,12 +57,16 @@ def _check(M, d, what, tokens=None, experts=None, seed=0, saved=False):
           flush=True)
     dout = W.make_output_grad(cfg, seed=seed, device="cuda")
     (dx, dwgu, dwd, dtw, dl), idx = run_bwd(M, d, dout, saved=saved)
-    if experts == "sample":                           # experts that some token routes to
-        used = np.unique(idx.cpu().numpy())
+    if isinstance(experts, int):                      # that many experts some token routes to:
+        ii = idx.cpu().numpy()                        # the most- and least-loaded, then random
+        used = np.unique(ii)
+        cnt = np.bincount(ii.ravel(), minlength=cfg.E)
         rng = np.random.default_rng(7)
-        experts = np.sort(rng.choice(used, size=min(3, used.size), replace=False))
-    ref = moe_backward(bits(d["x"]), d["logits"].cpu().numpy(), Fetch(d["w_gate_up"]),
-                       Fetch(d["w_down"]), bits(dout), cfg.k, tokens=tokens, experts=experts)
+        ext = [int(used[np.argmax(cnt[used])]), int(used[np.argmin(cnt[used])])]
+        rest = [int(e) for e in rng.permutation(used) if e not in ext]
+        experts = np.array(sorted(set(ext + rest[:max(0, experts - 2)])), dtype=np.int64)
+        print(f"[backward] experts {experts.tolist()} with {cnt[experts].tolist()} rows", flush=True)
+    ref = oracle_backward(d, dout, tokens=tokens, experts=experts)
     ts = slice(None) if tokens is None else torch.as_tensor(tokens, device="cuda")
     es = slice(None) if experts is None else torch.as_tensor(experts, device="cuda")
     check_bf16(dx[ts], ref["dx"], what + " dx")
@@ -180,20 +183,18 @@ def test_backward_bit_identical_repeats(M):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
-def _sample(T, n, seed):
-    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
-
-
 @pytest.mark.parametrize("saved", [False, True])
 def test_backward_kimi_full_size(M, saved):
     d = W.make("kimi-bf16-T2048", seed=0, device="cuda")
-    _check(M, d, "kimi-bf16-T2048 (8 tokens, 3 experts)", tokens=_sample(2048, 8, 2),
-           experts="sample", saved=saved)
+    cfg = d["cfg"]
+    toks, _ = sample_tokens(d["logits"].cpu().numpy(), cfg.k, 32, 2, n_focus=2)
+    _check(M, d, f"kimi-bf16-T2048 ({toks.size} tokens, 8 experts)", tokens=toks, experts=8,
+           saved=saved)
 
 
 def test_backward_ep64_share_full_size(M):
     # ~2,700 rows per expert: long K loops in the weight gradients
     d = W.make("kimi-bf16-ep64share", seed=0, device="cuda")
     cfg = d["cfg"]
-    _check(M, d, "kimi-bf16-ep64share (8 tokens, 1 expert)", tokens=_sample(cfg.T, 8, 3),
-           experts=np.array([2]))
+    toks, _ = sample_tokens(d["logits"].cpu().numpy(), cfg.k, 32, 3, n_focus=2)
+    _check(M, d, f"kimi-bf16-ep64share ({toks.size} tokens, 3 experts)", tokens=toks, experts=3)

@@ -10,7 +10,7 @@ import torch
 
 import workloads as W
 from oracle import route
-from tests._gpu import W_ABS, check_bf16, oracle
+from tests._gpu import W_ABS, check_bf16, oracle, sample_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -70,23 +70,27 @@ def test_batched_skewed_routing(M):
     _check(M, d, "all tokens on two experts")
 
 
-def _sample(T, n, seed):
-    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
+def _full_size(M, name, seed, n=64):
+    # at least n tokens: the first and last tokens of the most- and least-loaded
+    # experts and of six others, and of each one's ragged last M-tile, plus random ones
+    d = W.make(name, seed=0, device="cuda")
+    cfg = d["cfg"]
+    toks, info = sample_tokens(d["logits"].cpu().numpy(), cfg.k, n, seed)
+    c = info["counts"]
+    _check(M, d, f"{name} ({toks.size} sampled tokens; heaviest expert {c[info['heavy']]} rows, "
+                 f"lightest {c[info['light']]})", tokens=toks)
 
 
 def test_batched_kimi_full_size(M):
-    d = W.make("kimi-bf16-T2048", seed=0, device="cuda")
-    _check(M, d, "kimi-bf16-T2048 (8 sampled tokens)", tokens=_sample(2048, 8, 0))
+    _full_size(M, "kimi-bf16-T2048", 0)
 
 
 def test_batched_glm_full_size(M):
-    d = W.make("glm-bf16-T2048", seed=0, device="cuda")
-    _check(M, d, "glm-bf16-T2048 (8 sampled tokens)", tokens=_sample(2048, 8, 4))
+    _full_size(M, "glm-bf16-T2048", 4)
 
 
 def test_batched_kimi_ep64_share(M):
-    d = W.make("kimi-bf16-ep64share", seed=0, device="cuda")
-    _check(M, d, "kimi-bf16-ep64share (48 sampled tokens)", tokens=_sample(16384, 48, 1))
+    _full_size(M, "kimi-bf16-ep64share", 1)
 
 
 def test_batched_bit_identical_repeats(M):
@@ -108,10 +112,13 @@ def test_batched_grouping_is_stable(M, T, E, k):
     ridx, _ = route(d["logits"].cpu().numpy(), cfg.k)
     pairs = [(int(ridx[t, j]), t, j) for t in range(cfg.T) for j in range(cfg.k)]
     pairs.sort()
-    # recompute h for sorted row r from the oracle's activations and compare
+    # row r of h must be the activation of the r-th pair in (expert, token) order:
+    # checked row by row, so a swapped or shifted row fails even when the tensor
+    # as a whole is close
     _, inter = oracle(d, return_intermediates=True)
     a = inter["a"]
     want = np.stack([a[t, j] for (_, t, j) in pairs])
     got = h.float().cpu().double().numpy()
-    rel = np.linalg.norm(got - want) / np.linalg.norm(want)
-    assert rel < 5e-3, rel
+    row_err = np.linalg.norm(got - want, axis=1) / np.linalg.norm(want, axis=1)
+    bad = np.nonzero(row_err >= 1e-2)[0]
+    assert bad.size == 0, f"{bad.size} rows off, first {bad[0]} (pair {pairs[bad[0]]}): {row_err[bad[0]]:.3e}"

@@ -9,7 +9,7 @@ import workloads as W
 from oracle import formats as F
 from oracle import route
 from oracle.moe import rel_l2
-from tests._gpu import MXFP8_REL_L2, W_ABS, bits, oracle, to_f64
+from tests._gpu import MXFP8_REL_L2, W_ABS, bits, oracle, sample_tokens, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -106,18 +106,23 @@ def test_mx_shapes(M, T, H, I, E, k):
     _check(M, _custom(T, H, I, E, k, seed=T + 1), f"mx shape T={T} H={H} I={I} E={E} k={k}")
 
 
-def _sample(T, n, seed):
-    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
+def _full_size(M, name, seed, n=64):
+    # at least n tokens: the first and last tokens of the most- and least-loaded
+    # experts and of six others, and of each one's ragged last M-tile, plus random ones
+    d = W.make(name, seed=0, device="cuda")
+    cfg = d["cfg"]
+    toks, info = sample_tokens(d["logits"].cpu().numpy(), cfg.k, n, seed)
+    c = info["counts"]
+    _check(M, d, f"{name} ({toks.size} sampled tokens; heaviest expert {c[info['heavy']]} rows, "
+                 f"lightest {c[info['light']]})", tokens=toks)
 
 
 def test_mx_dsv4_full_size(M):
-    d = W.make("dsv4-mxfp8-T2048", seed=0, device="cuda")
-    _check(M, d, "dsv4-mxfp8-T2048 (6 sampled tokens)", tokens=_sample(2048, 6, 2))
+    _full_size(M, "dsv4-mxfp8-T2048", 2)
 
 
 def test_mx_dsv4_ep64_share(M):
-    d = W.make("dsv4-mxfp8-ep64share", seed=0, device="cuda")
-    _check(M, d, "dsv4-mxfp8-ep64share (48 sampled tokens)", tokens=_sample(16384, 48, 3))
+    _full_size(M, "dsv4-mxfp8-ep64share", 3)
 
 
 def test_mx_bit_identical_repeats(M):
