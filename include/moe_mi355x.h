@@ -113,6 +113,28 @@ int moe_decode_forward(const uint16_t* x, const float* logits,
 size_t moe_decode_workspace_bytes(int T, int H, int I, int E, int k);
 
 /*
+ * moe_decode_forward_noalloc -- moe_decode_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * and harnesses that forbid hipMalloc.  Same arguments, results and bytes as
+ * moe_decode_forward, without the workspace: the kernels use a scratch array
+ * the library owns, MOE_STATIC_SCRATCH_BYTES on every GPU it runs on (held
+ * until the process ends).  This call allocates nothing.
+ *
+ * Limit: moe_decode_workspace_bytes(T, H, I, E, k) <= MOE_STATIC_SCRATCH_BYTES
+ * (about T*k*I <= 2^21; MOE_ERR_UNSUPPORTED otherwise), besides the limits of
+ * moe_decode_forward.
+ * All calls on one GPU share its scratch array, which keeps the last call's
+ * contents (every byte a call reads there, it has written first): calls that
+ * can overlap on one GPU (on different streams, or from different threads)
+ * race and must be ordered by the caller.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (4u << 20)
+int moe_decode_forward_noalloc(const uint16_t* x, const float* logits,
+                               const uint16_t* w_gate_up, const uint16_t* w_down,
+                               int T, int H, int I, int E, int k,
+                               uint16_t* out, int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
  * moe_quantize_mxfp8 -- MX block quantization of a BF16 matrix along its
  * last dimension (the "MXFP8" forward of the Mixture-of-Kittens summary,
  * "What is 2.37x measured against"; block rule of OCP Microscaling v1.0).

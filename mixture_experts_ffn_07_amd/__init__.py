@@ -31,6 +31,7 @@ _SIGS = {
     "moe_route_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_decode_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "moe_decode_forward_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
     "moe_quantize_mxfp8": (_I, [_P, ctypes.c_int64, _I, _P, _P, _P]),
     "moe_gate_up_3d_batched": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "moe_down_3d_batched": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
@@ -176,6 +177,31 @@ def moe_decode_forward(x: torch.Tensor, logits: torch.Tensor, w_gate_up: torch.T
     _check("moe_decode_forward", lib.moe_decode_forward(
         _ptr(x), _ptr(logits), _ptr(w_gate_up), _ptr(w_down), T, H, I, E, k, _ptr(out),
         _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+STATIC_SCRATCH_BYTES = 4 << 20      # MOE_STATIC_SCRATCH_BYTES
+
+
+def moe_decode_forward_noalloc(x: torch.Tensor, logits: torch.Tensor, w_gate_up: torch.Tensor,
+                               w_down: torch.Tensor, k: int, out: torch.Tensor,
+                               topk_idx: torch.Tensor = None, topk_w: torch.Tensor = None,
+                               stream=None) -> torch.Tensor:
+    """moe_decode_forward without a workspace (the library's own scratch); the
+    caller passes every output, so this call allocates nothing."""
+    T, H = x.shape
+    E, I2, H2 = w_gate_up.shape
+    I = I2 // 2
+    if logits.shape != (T, E) or H2 != H or tuple(w_down.shape) != (E, H, I):
+        raise ValueError("inconsistent shapes")
+    _u16(x), _u16(w_gate_up), _u16(w_down)
+    _need(logits, "logits", (T, E), torch.float32)
+    _need(out, "out", (T, H), _BF16)
+    _need(topk_idx, "topk_idx", (T, k), torch.int32, optional=True)
+    _need(topk_w, "topk_w", (T, k), torch.float32, optional=True)
+    _check("moe_decode_forward_noalloc", lib.moe_decode_forward_noalloc(
+        _ptr(x), _ptr(logits), _ptr(w_gate_up), _ptr(w_down), T, H, I, E, k, _ptr(out),
+        _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
     return out
 
 
@@ -331,6 +357,7 @@ def moe_profile_kernel(kernel, start_event: Optional[int], stop_event: Optional[
 
 
 __all__ = ["lib", "LIB_PATH", "MoeError", "moe_route_topk", "moe_decode_forward",
+           "moe_decode_forward_noalloc", "STATIC_SCRATCH_BYTES",
            "moe_decode_workspace_bytes", "moe_workspace_bytes", "moe_quantize_mxfp8",
            "moe_gate_up_3d_batched", "moe_down_3d_batched", "moe_gate_up_3d_batched_train",
            "moe_backward_batched",

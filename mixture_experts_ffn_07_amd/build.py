@@ -21,7 +21,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(OUT_DIR, "libmoe_mi355x.so")
-SOURCES = ["abi.cpp", "route.hip", "decode.hip", "batched.hip", "gemm_large.hip", "backward.hip"]
+SOURCES = ["abi.cpp", "route.hip", "decode.hip", "batched.hip", "gemm_large.hip", "backward.hip",
+           "scratch.hip"]
 
 
 def hipcc() -> str:

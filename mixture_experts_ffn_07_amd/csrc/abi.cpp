@@ -21,6 +21,9 @@ ProfileHook& profile_hook() {
 }
 }  // namespace moe
 
+static_assert(MOE_STATIC_SCRATCH_BYTES == moe::kStaticScratchBytes,
+              "the header's scratch size must match the array's");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -46,15 +49,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct DeviceInfo {
   int num_cus = 0;
   bool ready = false;
+  void* scratch = nullptr;   // this device's copy of the library-owned scratch array
 };
 std::mutex g_mu;
-DeviceInfo g_dev[64];
+DeviceInfo g_dev[moe::kMaxDevices];
 
-int device_info(int* num_cus) {
+int device_info(int* num_cus, void** scratch = nullptr) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
-  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device ordinal %d", dev);
+  if (dev < 0 || dev >= moe::kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device ordinal %d", dev);
   std::lock_guard<std::mutex> lock(g_mu);
   DeviceInfo& d = g_dev[dev];
   if (!d.ready) {
@@ -67,10 +71,14 @@ int device_info(int* num_cus) {
     e = moe::decode_set_attributes();
     if (e == hipSuccess) e = moe::batched_set_attributes();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
+    // the device address of this device's scratch array (the device is current)
+    e = moe::static_scratch(dev, &d.scratch);
+    if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetSymbolAddress: %s", hipGetErrorString(e));
     d.num_cus = prop.multiProcessorCount;
     d.ready = true;
   }
   *num_cus = d.num_cus;
+  if (scratch) *scratch = d.scratch;
   return MOE_OK;
 }
 
@@ -172,6 +180,33 @@ int moe_decode_forward(const uint16_t* x, const float* logits, const uint16_t* w
   return hip_status(moe::launch_decode(x, logits, w_gate_up, w_down, T, H, I, E, k, out, topk_idx,
                                        topk_w, workspace, static_cast<hipStream_t>(stream), cus),
                     "moe_decode_forward launch");
+}
+
+int moe_decode_forward_noalloc(const uint16_t* x, const float* logits, const uint16_t* w_gate_up,
+                               const uint16_t* w_down, int T, int H, int I, int E, int k,
+                               uint16_t* out, int32_t* topk_idx, float* topk_w, void* stream) {
+  if (int st = check_common(T, H, I, E, k, 256, 256)) return st;
+  if (T == 0) return fail(MOE_ERR_SHAPE, "T=0: nothing to decode");
+  if (T > 64) return fail(MOE_ERR_UNSUPPORTED, "T=%d > 64: use the batched calls", T);
+  if (I > 2048) return fail(MOE_ERR_UNSUPPORTED, "I=%d > 2048: use the batched calls", I);
+  if (int st = check_offsets(T, H, I, k)) return st;
+  const size_t need = moe::decode_ws_layout(T, H, I, E, k).total;
+  if (need > moe::kStaticScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "workspace of %zu bytes exceeds the library's %zu-byte scratch (T*k*I too "
+                "large): use moe_decode_forward with a caller workspace",
+                need, moe::kStaticScratchBytes);
+  if (!x || !logits || !w_gate_up || !w_down || !out)
+    return fail(MOE_ERR_NULL, "x, logits, w_gate_up, w_down and out are required");
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(out) ||
+      !aligned16(logits) || (topk_idx && !aligned16(topk_idx)) || (topk_w && !aligned16(topk_w)))
+    return fail(MOE_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  int cus = 0;
+  void* ws = nullptr;
+  if (int st = device_info(&cus, &ws)) return st;
+  return hip_status(moe::launch_decode(x, logits, w_gate_up, w_down, T, H, I, E, k, out, topk_idx,
+                                       topk_w, ws, static_cast<hipStream_t>(stream), cus),
+                    "moe_decode_forward_noalloc launch");
 }
 
 size_t moe_workspace_bytes(int T, int H, int I, int E, int k, moe_dtype dtype) {

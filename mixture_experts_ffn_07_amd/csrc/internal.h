@@ -28,6 +28,14 @@ enum KernelId { kRoute = 1, kDecGateUp = 2, kDecDown = 3, kGroup = 4, kQuant = 5
                 kGemmGateUp = 6, kGemmDown = 7, kCombine = 8, kBwdGateUp = 9, kBwdDown = 10,
                 kBwdInput = 11, kBwdWDown = 12, kBwdWGateUp = 13, kKernelCount = 14 };
 
+// Library-owned device scratch (scratch.hip): kStaticScratchBytes per GPU for
+// the entry points that allocate nothing.  static_scratch(dev) gives its device
+// address on device `dev`, which must be the current device; the address is
+// taken with hipGetSymbolAddress on the first call for that device.
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(int dev, void** ptr);
+
 // Byte layout of the decode workspace.
 struct DecodeWs {
   size_t plan_u, plan_e, plan_off, plan_pr, idx, w, hw, total;
