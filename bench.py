@@ -1,28 +1,37 @@
 #!/usr/bin/env python3
 """Benchmark of the routed MoE FFN layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1] [--pass backward]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--lines A,B|none]
+                    [--gpus 1] [--pass backward|train]
 
-One step = one full pass of the layer (routing, gate/up + SwiGLU, down +
-weighted combine) over one batch of synthetic tokens.  Default workload: the
-Qwen3-style decode layer (H=2048, E=128, k=8, I=768) at T=32 tokens.
+One step = one full pass of the layer (routing, [MX quantization of x,]
+gate/up + SwiGLU, down + weighted combine) over one batch of synthetic tokens,
+with every input resident in HBM before the timed region starts.
 
-Decode steps cycle through `--layers` independent weight sets (like the
-layers of a model), so each step streams weights that the previous steps did
-not leave in the 256 MB last-level cache, and every step routes a fresh batch
-of tokens.  All inputs are resident in HBM before the timed region starts.
+Default headline: the Kimi-K2.7-Code-shaped batched layer at the pages'
+2,048 tokens per GPU (H 7168, E 384 all resident, k 8, I 2048, BF16; the
+largest shape, HBM-bound at ~43 routed rows per expert).  The same JSON line
+carries, under "lines", the pages' other shapes measured in the same run: the
+DeepSeek-V4-Pro-shaped MXFP8 layer, both one-GPU expert-parallel shares
+(MFMA-bound), the Qwen3-style decode layer at T = 1, 8 and 32, and the
+Qwen3.5-shaped Zipf-skewed decode at T = 64.  Decode steps cycle through
+independent weight sets (like the layers of a model), so each step streams
+weights the 256 MB last-level cache does not hold, and every step routes a
+fresh batch of tokens.
 
 With --pass backward (batched BF16 workloads) a step is routing plus the
 layer's backward pass instead (dx, both weight gradients, the routing-weight
 and logit gradients for a seeded output gradient).
 
 Prints ONE JSON line.  Besides the throughput it carries
-  roofline:     the dominant kernel's algorithmic HBM bytes per launch divided
-                by its average launch time, taken with HIP events recorded
-                around that kernel on the library's stream during the timed
-                steps, against the 8 TB/s HBM peak;
+  roofline:     the dominant kernel's algorithmic HBM bytes (or MFMA flops)
+                per launch divided by its average launch time, taken with HIP
+                events recorded around that kernel on the library's stream
+                during the timed steps, against the 8 TB/s HBM peak (or the
+                dense MFMA peak of the dtype);
   cpu_baseline: the FP64 CPU oracle, timed on this host on a bounded sample
-                of the same workload.
+                of the same workload, with the cores, CPU model and thread
+                settings it ran with.
 """
 from __future__ import annotations
 
@@ -31,6 +40,10 @@ import json
 import os
 import sys
 import time
+
+# the CPU oracle's BLAS threads: every core this process may use, unless set
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
+    os.environ.setdefault(_v, str(len(os.sched_getaffinity(0))))
 
 import hashlib
 
@@ -54,6 +67,12 @@ TRAFFIC = {
     ("gemm_gate_up", "glm-bf16-T2048"): (
         13213.0e6, ('batched.hip', 'common.h', 'tiles.h'), "b363ba1a1057f3d8",
         "profiles/gemm_gate_up_glm-bf16-T2048.md"),
+    ("gemm_gate_up", "dsv4-mxfp8-T2048"): (
+        18180.0e6, ('batched.hip', 'common.h', 'tiles.h'), "b363ba1a1057f3d8",
+        "profiles/gemm_gate_up_dsv4-mxfp8-T2048.md"),
+    ("gemm_gate_up", "qwen3-mxfp8-decode-T32"): (
+        377.89e6, ('batched.hip', 'common.h', 'tiles.h'), "b363ba1a1057f3d8",
+        "profiles/gemm_gate_up_qwen3-mxfp8-decode-T32.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
         2002.6e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "980972c221bc04b2",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
@@ -86,15 +105,19 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}   # dense, MI355X
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="qwen3-decode-T32")
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=None,
+                   help="one workload (default: kimi-bf16-T2048 with the other shapes "
+                        "reported under 'lines')")
+    p.add_argument("--lines", default=None,
+                   help="comma-separated workloads reported beside the headline in the same "
+                        "JSON line ('none' for none; default: the pages' other shapes when the "
+                        "headline is the default workload)")
     p.add_argument("--layers", type=int, default=8, help="independent weight sets to cycle")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time for the oracle baseline (0 = skip)")
-    p.add_argument("--extra", action="store_true",
-                   help="also time decode at T=1 and T=8 (reported under 'extra')")
     p.add_argument("--pass", dest="pass_", choices=("forward", "backward", "train"),
                    default="forward",
                    help="backward: the layer's backward pass; train: forward + backward "
@@ -107,7 +130,12 @@ def parse():
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="only run a plain device copy of this many MiB three times (the "
                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
-    return p.parse_args()
+    a = p.parse_args()
+    if a.lines is None:
+        a.lines = DEFAULT_LINES if (a.workload is None and a.pass_ == "forward") else "none"
+    if a.workload is None:
+        a.workload = "kimi-bf16-T2048"
+    return a
 
 
 def log(*a):
@@ -130,12 +158,19 @@ def launch_percentiles(durs_ms):
     return {"p10": round(q(0.1), 2), "median": round(q(0.5), 2), "p90": round(q(0.9), 2)}
 
 
-def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="decode_gate_up"):
+def decode_weight_sets(W, cfg, layers, seed, dev="cuda"):
+    log(f"generating {layers} weight sets of {cfg.name} ({layers * W.expert_bytes(cfg) * cfg.E / 1e9:.1f} GB)")
+    return [W.make_weights(cfg, seed=seed + 1000 * l, device=dev) for l in range(layers)]
+
+
+def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="decode_gate_up",
+               weights=None):
     from mixture_experts_ffn_07_amd.hip_events import HipEvent
     dev = "cuda"
     n_batches = steps + warmup
-    log(f"generating {layers} weight sets of {cfg.name} ({layers * W.expert_bytes(cfg) * cfg.E / 1e9:.1f} GB)")
-    weights = [W.make_weights(cfg, seed=seed + 1000 * l, device=dev) for l in range(layers)]
+    if weights is None:
+        weights = decode_weight_sets(W, cfg, layers, seed, dev)
+    layers = len(weights)
     acts = [W.make_activations(cfg, seed=seed + 7919 * (b + 1), device=dev) for b in range(n_batches)]
     T, k = cfg.T, cfg.k
     out = torch.empty(T, cfg.H, dtype=torch.bfloat16, device=dev)
@@ -381,34 +416,65 @@ def run_backward(M, W, torch, cfg, steps, warmup, seed, n_batches=2, recompute=F
             "layer_gbs": tot_bytes / elapsed / 1e9, "avg_touched_experts": sum(U) / steps}
 
 
-def cpu_baseline(W, cfg, act, weights, seconds):
-    """Time the FP64 oracle on this host (bounded sample of the same workload)."""
-    import numpy as np
-    from oracle import moe_forward
+def host_info():
+    """Cores this process may use, the CPU model and the thread settings the
+    oracle's BLAS runs with."""
+    cores = len(os.sched_getaffinity(0))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        blas = None
+    env = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                         "MKL_NUM_THREADS")}
+    return cores, model, blas, env
+
+
+def cpu_baseline(W, cfg, act, weights, seconds, n_tokens=None):
+    """Time the FP64 oracle on this host on a bounded sample of the same
+    workload: the first n_tokens tokens of one batch (all of it by default),
+    with the routed experts' weights copied to host memory first (outside the
+    timing).  Passes repeat until `seconds` have gone by."""
+    import numpy as np
+    from oracle import moe_forward, route
     import torch
-    x = act["x"].cpu().view(torch.int16).numpy().view(np.uint16)
-    logits = act["logits"].cpu().numpy()
-    # copy only the experts this batch routes to; the copy is outside the timing
-    from oracle import route
+    T = cfg.T if n_tokens is None else min(n_tokens, cfg.T)
+    x = act["x"][:T].cpu().view(torch.int16).numpy().view(np.uint16)
+    logits = act["logits"][:T].cpu().numpy()
     ids = np.unique(route(logits, cfg.k)[0])
-    wgu = {int(e): weights["w_gate_up"][int(e)].cpu().view(torch.int16).numpy().view(np.uint16) for e in ids}
-    wd = {int(e): weights["w_down"][int(e)].cpu().view(torch.int16).numpy().view(np.uint16) for e in ids}
+
+    def host(name):
+        t = weights[name]
+        if t.dtype == torch.bfloat16:
+            return {int(e): t[int(e)].cpu().view(torch.int16).numpy().view(np.uint16) for e in ids}
+        return {int(e): t[int(e)].cpu().numpy() for e in ids}
+    wgu, wd = host("w_gate_up"), host("w_down")
+    kw = {}
+    if cfg.dtype == "mxfp8":
+        sg, sd = host("w_gate_up_scales"), host("w_down_scales")
+        kw = dict(w_gate_up_scales=sg.__getitem__, w_down_scales=sd.__getitem__)
     n, t0 = 0, time.perf_counter()
     while True:
-        moe_forward(x, logits, wgu.__getitem__, wd.__getitem__, cfg.k)
+        moe_forward(x, logits, wgu.__getitem__, wd.__getitem__, cfg.k, dtype=cfg.dtype, **kw)
         n += 1
         if time.perf_counter() - t0 >= seconds:
             break
     el = time.perf_counter() - t0
-    return {"value": n * cfg.T / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} pass(es) of the FP64 oracle over one {cfg.T}-token batch of "
-                      f"{cfg.name} ({len(ids)} routed experts), weights already in host memory, "
-                      f"{el:.1f} s"}
+    cores, model, blas, env = host_info()
+    return {"value": n * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "blas_threads": blas, "cpu_model": model, "thread_env": env,
+            "sample": f"{n} pass(es) of the FP64 oracle over the first {T} token(s) of one "
+                      f"{cfg.T}-token batch of {cfg.name} ({len(ids)} routed experts), weights "
+                      f"already in host memory, {el:.1f} s"}
 
 
 def main():
@@ -499,38 +565,9 @@ def main():
         return
     if cfg.path == "decode":
         r = run_decode(M, W, torch, cfg, args.steps, args.warmup, args.layers, args.seed)
-        traffic, tprof = traffic_for("decode_gate_up", cfg.name)
-        roof = {"bound": "hbm", "kernel": "decode_gate_up", "achieved": round(r["kernel_gbs"], 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(r["kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "traffic_unit": "bytes per launch", "traffic_source": tprof,
-                "avg_launch_us": round(r["kernel_avg_us"], 2),
-                "launch_us": r["kernel_pct_us"],
-                "algorithmic_bytes_per_launch": int(r["kernel_bytes_per_launch"])}
     else:
         r = run_batched(M, W, torch, cfg, args.steps, args.warmup, args.seed, layers=args.layers)
-        peak_tf = MFMA_PEAK_TFLOPS[cfg.dtype]
-        rows_per_expert = cfg.T * cfg.k / cfg.E
-        if rows_per_expert >= 256:       # weight reuse high enough to be MFMA-bound
-            traffic, tprof = traffic_for("gemm_gate_up", cfg.name)
-            roof = {"bound": "mfma", "kernel": "gemm_gate_up", "achieved": round(r["kernel_tflops"], 1),
-                    "peak": peak_tf, "unit": "TFLOP/s", "frac": round(r["kernel_tflops"] / peak_tf, 4),
-                    "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": tprof,
-                    "avg_launch_us": round(r["kernel_avg_us"], 2),
-                    "launch_us": r["kernel_pct_us"],
-                    "algorithmic_flops_per_launch": int(r["kernel_flops_per_launch"]),
-                    "hbm_gbs": round(r["kernel_gbs"], 1)}
-        else:
-            traffic, tprof = traffic_for("gemm_gate_up", cfg.name)
-            roof = {"bound": "hbm", "kernel": "gemm_gate_up", "achieved": round(r["kernel_gbs"], 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(r["kernel_gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "traffic_unit": "bytes per launch", "traffic_source": tprof,
-                    "avg_launch_us": round(r["kernel_avg_us"], 2),
-                    "launch_us": r["kernel_pct_us"],
-                    "algorithmic_bytes_per_launch": int(r["kernel_bytes_per_launch"]),
-                    "mfma_tflops": round(r["kernel_tflops"], 1),
-                    "mfma_frac": round(r["kernel_tflops"] / peak_tf, 4)}
+    roof, layer = forward_roofline(cfg, r)
     line = {
         "metric": METRIC, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
@@ -541,11 +578,7 @@ def main():
                    "I": cfg.I, "weight_sets": r.get("weight_sets", args.layers),
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
-        "layer": {"hbm_gbs": round(r["layer_gbs"], 1),
-                  **({"mfma_tflops": round(r["layer_tflops"], 1)} if "layer_tflops" in r else {}),
-                  "hbm_frac": round(r["layer_gbs"] / HBM_PEAK_GBS, 4),
-                  "avg_touched_experts": round(r["avg_touched_experts"], 2),
-                  "latency_us": round(1e3 * r["ms_per_step"], 2)},
+        "layer": layer,
     }
     if cfg.path == "decode" and args.layers > 1:
         # the headline cycles weight sets, so each step streams weights no recent step
@@ -556,24 +589,103 @@ def main():
                         "tokens_per_s": round(rw["tokens_per_s"], 1),
                         "gate_up_gbs": round(rw["kernel_gbs"], 1),
                         "gate_up_launch_us": rw["kernel_pct_us"]}
-    if args.extra and cfg.path == "decode":
-        ex = {}
-        for T in (1, 8):
-            c2 = W.get(f"qwen3-decode-T{T}")
-            r2 = run_decode(M, W, torch, c2, args.steps, args.warmup, args.layers, args.seed)
-            ex[c2.name] = {"tokens_per_s": round(r2["tokens_per_s"], 1),
-                           "latency_us": round(1e3 * r2["ms_per_step"], 2),
-                           "gate_up_us": round(r2["kernel_avg_us"], 2),
-                           "gate_up_gbs": round(r2["kernel_gbs"], 1),
-                           "layer_gbs": round(r2["layer_gbs"], 1)}
-        line["extra"] = ex
-    if args.cpu_seconds > 0 and cfg.path == "decode":
+    if args.cpu_seconds > 0:
         log("timing the CPU oracle baseline")
-        line["cpu_baseline"] = cpu_baseline(W, cfg, r["first_batch"], r["first_weights"],
-                                            args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(
+            W, cfg, r["first_batch"], r["first_weights"], args.cpu_seconds,
+            n_tokens=None if cfg.path == "decode" else 2)
     else:
         line["cpu_baseline"] = None
+    first_w = r.pop("first_weights")
+    del first_w, r
+    lines = [] if args.lines in ("", "none") else args.lines.split(",")
+    if lines:
+        line["lines"] = run_lines(M, W, torch, lines, args)
     print(json.dumps(line), flush=True)
+
+
+def forward_roofline(cfg, r):
+    """The dominant kernel's roofline (decode: decode_gate_up against HBM;
+    batched: the gate_up GEMM, against HBM or, at 256+ rows per expert, the
+    MFMA peak of its dtype) and the whole layer's figures."""
+    peak_tf = MFMA_PEAK_TFLOPS[cfg.dtype]
+    if cfg.path == "decode":
+        kern = "decode_gate_up"
+        mfma_bound = False
+    else:
+        kern = "gemm_gate_up"
+        mfma_bound = cfg.T * cfg.k / cfg.E >= 256      # weight reuse high enough
+    traffic, tprof = traffic_for(kern, cfg.name)
+    common = {"kernel": kern, "traffic": traffic, "traffic_unit": "bytes per launch",
+              "traffic_source": tprof, "avg_launch_us": round(r["kernel_avg_us"], 2),
+              "launch_us": r["kernel_pct_us"]}
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(r["kernel_tflops"], 1), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(r["kernel_tflops"] / peak_tf, 4), **common,
+                "algorithmic_flops_per_launch": int(r["kernel_flops_per_launch"]),
+                "hbm_gbs": round(r["kernel_gbs"], 1)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(r["kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(r["kernel_gbs"] / HBM_PEAK_GBS, 4), **common,
+                "algorithmic_bytes_per_launch": int(r["kernel_bytes_per_launch"])}
+        if "kernel_tflops" in r:
+            roof["mfma_tflops"] = round(r["kernel_tflops"], 1)
+            roof["mfma_frac"] = round(r["kernel_tflops"] / peak_tf, 4)
+    layer = {"hbm_gbs": round(r["layer_gbs"], 1), "hbm_frac": round(r["layer_gbs"] / HBM_PEAK_GBS, 4),
+             "avg_touched_experts": round(r["avg_touched_experts"], 2),
+             "latency_us": round(1e3 * r["ms_per_step"], 2)}
+    if "layer_tflops" in r:
+        layer["mfma_tflops"] = round(r["layer_tflops"], 1)
+        layer["mfma_frac"] = round(r["layer_tflops"] / peak_tf, 4)
+    return roof, layer
+
+
+# the pages' other shapes, reported beside the headline in the same JSON line
+DEFAULT_LINES = ("dsv4-mxfp8-T2048,kimi-bf16-ep64share,dsv4-mxfp8-ep64share,"
+                 "qwen3-decode-T1,qwen3-decode-T8,qwen3-decode-T32,q35-zipf-T64")
+
+
+def run_lines(M, W, torch, names, args):
+    """Each workload in turn (its tensors freed before the next): batched lines
+    time `--steps` steps, decode lines max(--steps, 100) steps cycling weight
+    sets (8 for the Qwen3-style shape, shared by its three batch sizes; 2 for the
+    Qwen3.5-shaped one, 25.8 GB)."""
+    out = []
+    qwen_sets = None
+    for name in names:
+        cfg = W.get(name)
+        t0 = time.perf_counter()
+        if cfg.path == "decode":
+            steps = max(args.steps, 100)
+            if name.startswith("qwen3-decode"):
+                if qwen_sets is None:
+                    qwen_sets = decode_weight_sets(W, cfg, 8, args.seed)
+                sets = qwen_sets
+            else:
+                sets = decode_weight_sets(W, cfg, 2, args.seed)
+            r = run_decode(M, W, torch, cfg, steps, args.warmup, len(sets), args.seed,
+                           weights=sets)
+            del sets
+        else:
+            steps = args.steps
+            r = run_batched(M, W, torch, cfg, steps, args.warmup, args.seed, layers=1)
+        r.pop("first_weights", None)
+        r.pop("first_batch", None)
+        roof, layer = forward_roofline(cfg, r)
+        out.append({"workload": name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                    "dtype": cfg.dtype, "steps": steps, "weight_sets": r.get("weight_sets"),
+                    "ms_per_step": round(r["ms_per_step"], 5),
+                    "tokens_per_s": round(r["tokens_per_s"], 1),
+                    "roofline": {k_: roof[k_] for k_ in ("bound", "kernel", "achieved", "peak",
+                                                         "unit", "frac", "avg_launch_us",
+                                                         "traffic", "traffic_source")},
+                    "layer": layer})
+        del r
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        log(f"{name}: {out[-1]['ms_per_step']:.4f} ms/step, frac {roof['frac']} "
+            f"({time.perf_counter() - t0:.1f} s)")
+    return out
 
 
 if __name__ == "__main__":
