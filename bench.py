@@ -99,6 +99,7 @@ def traffic_for(kernel, workload):
         return None, None
     return nbytes, prof
 HBM_PEAK_GBS = 8000.0
+DECODE_FUSED = [False]      # --decode-fused: the single-launch decode at T <= 16
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}   # dense, MI355X
 
 
@@ -125,6 +126,9 @@ def parse():
     p.add_argument("--recompute", action="store_true",
                    help="backward recomputes the gate/up pre-activations instead of reading "
                         "those the training forward kept")
+    p.add_argument("--decode-fused", action="store_true",
+                   help="decode at T <= 16 as one launch (routing, gate_up, device-wide wait, "
+                        "down) instead of two")
     p.add_argument("--calibrate-fill-mib", type=int, default=0,
                    help="only time a plain device fill of this many MiB (HBM write rate)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -163,7 +167,7 @@ def decode_weight_sets(W, cfg, layers, seed, dev="cuda"):
     return [W.make_weights(cfg, seed=seed + 1000 * l, device=dev) for l in range(layers)]
 
 
-def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="decode_gate_up",
+def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="auto",
                weights=None):
     from mixture_experts_ffn_07_amd.hip_events import HipEvent
     dev = "cuda"
@@ -191,6 +195,8 @@ def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="decod
     evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if hook_kernel == "auto":
+        hook_kernel = "decode_fused" if (T <= 16 and DECODE_FUSED[0]) else "decode_gate_up"
     for s in range(steps):
         M.moe_profile_kernel(hook_kernel, evs[s][0].handle, evs[s][1].handle)
         step(warmup + s)
@@ -200,7 +206,10 @@ def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="decod
     durs = [a.elapsed_ms(b) for a, b in evs]
     U = [int(torch.unique(idx[warmup + s]).numel()) for s in range(steps)]
     bytes_ = [decode_algorithmic_bytes(cfg, u) for u in U]
-    kern_bytes = sum(b["gate_up"] for b in bytes_)
+    if hook_kernel == "decode_fused":                 # one launch: the whole layer
+        kern_bytes = sum(sum(b.values()) for b in bytes_)
+    else:
+        kern_bytes = sum(b["gate_up"] for b in bytes_)
     layer_bytes = sum(sum(b.values()) for b in bytes_)
     elapsed = t1 - t0
     res = {
@@ -212,6 +221,7 @@ def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="decod
         "kernel_gbs": kern_bytes / (sum(durs) * 1e-3) / 1e9,
         "kernel_bytes_per_launch": kern_bytes / steps,
         "layer_gbs": layer_bytes / elapsed / 1e9,
+        "kernel": hook_kernel,
         "avg_touched_experts": sum(U) / steps,
         "first_batch": acts[warmup], "first_weights": weights[warmup % layers],
     }
@@ -518,6 +528,9 @@ def main():
         return
     cfg = W.get(args.workload)
     log(f"device {torch.cuda.get_device_name(0)}; workload {cfg.name}")
+    if args.decode_fused:
+        M.moe_set_debug_options(M.MOE_DEBUG_DECODE_FUSED, 0)
+        DECODE_FUSED[0] = True
     if args.pass_ in ("backward", "train"):
         if cfg.path != "batched" or cfg.dtype != "bf16":
             print(f"--pass {args.pass_} needs a batched BF16 workload, not {cfg.name}",
@@ -610,7 +623,7 @@ def forward_roofline(cfg, r):
     MFMA peak of its dtype) and the whole layer's figures."""
     peak_tf = MFMA_PEAK_TFLOPS[cfg.dtype]
     if cfg.path == "decode":
-        kern = "decode_gate_up"
+        kern = r.get("kernel", "decode_gate_up")   # decode_fused: the single-launch layer
         mfma_bound = False
     else:
         kern = "gemm_gate_up"

@@ -88,7 +88,14 @@ int moe_route_topk(const float* logits, int T, int E, int k,
  * moe_decode_forward -- the whole layer for a small decode batch
  * (warp-decode article, "Key points": two kernels, gate_up and down, each
  * output-centric, routed experts' contributions summed directly into FP32
- * accumulators, no per-expert output buffer and no activation-gather buffer).
+ * accumulators, no per-expert output buffer and no activation-gather buffer;
+ * Mixture-of-Kittens summary, "One kernel swallowed the layer's comm+compute":
+ * no kernel-launch boundaries inside the layer).  At T <= 16 routing runs
+ * inside gate_up (two launches); at larger T routing, gate_up and down are three
+ * launches.  A single-launch form (routing, gate_up, a bounded device-wide wait
+ * on per-workgroup ready flags, down) is available through
+ * moe_set_debug_options(MOE_DEBUG_DECODE_FUSED) for T <= 16 and I/64 a power of
+ * two times 3 or 4; it is not the default because it measured no faster.
  *
  *   x           [T, H] BF16
  *   logits      [T, E] float32
@@ -299,10 +306,27 @@ typedef enum {
   MOE_KERNEL_BWD_INPUT = 11,     /* backward: dx (and the slot sum)              */
   MOE_KERNEL_BWD_WDOWN = 12,     /* backward: dw_down                            */
   MOE_KERNEL_BWD_WGATE_UP = 13,  /* backward: dw_gate_up                         */
-  MOE_KERNEL_COUNT = 14
+  MOE_KERNEL_DECODE_FUSED = 14,  /* single-launch decode (T <= 16): the whole layer */
+  MOE_KERNEL_COUNT = 15
 } moe_kernel_id;
 
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event);
+
+/*
+ * Test and debugging options (not on any page), for the calling thread's later
+ * calls until changed:
+ *   MOE_DEBUG_PERMUTE_ORDER  every grouped and decode kernel visits its work
+ *                            items in an order permuted by `seed` (a different
+ *                            workgroup -> item assignment); results must not change
+ *   MOE_DEBUG_DECODE_FUSED   moe_decode_forward at T <= 16 runs as one launch
+ *                            (routing, gate_up, a device-wide wait, down) instead
+ *                            of two
+ * flags = 0 restores the defaults.  Returns MOE_OK, or MOE_ERR_SHAPE for
+ * unknown bits.
+ */
+#define MOE_DEBUG_PERMUTE_ORDER 1u
+#define MOE_DEBUG_DECODE_FUSED 2u
+int moe_set_debug_options(unsigned flags, uint32_t seed);
 
 /* Static text for a moe_status value. */
 const char* moe_status_string(int status);

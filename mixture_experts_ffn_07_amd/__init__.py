@@ -22,7 +22,9 @@ MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = -4, -5, -6
 MOE_BF16, MOE_MXFP8 = 0, 1
 KERNELS = {"none": 0, "route": 1, "decode_gate_up": 2, "decode_down": 3, "group": 4,
            "quant": 5, "gemm_gate_up": 6, "gemm_down": 7, "combine": 8, "bwd_gate_up": 9,
-           "bwd_down": 10, "bwd_input": 11, "bwd_wdown": 12, "bwd_wgate_up": 13}
+           "bwd_down": 10, "bwd_input": 11, "bwd_wdown": 12, "bwd_wgate_up": 13,
+           "decode_fused": 14}
+MOE_DEBUG_PERMUTE_ORDER, MOE_DEBUG_DECODE_FUSED = 1, 2
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -41,6 +43,7 @@ _SIGS = {
     "moe_gate_up_3d_batched_train": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "moe_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_profile_kernel": (_I, [_I, _P, _P]),
+    "moe_set_debug_options": (_I, [ctypes.c_uint, ctypes.c_uint32]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
@@ -350,6 +353,12 @@ def moe_backward_batched(x, w_gate_up, w_down, topk_idx, topk_w, dout, k: int, g
     return dx, dw_gate_up, dw_down, d_topk_w, dlogits
 
 
+def moe_set_debug_options(flags: int = 0, seed: int = 0) -> None:
+    """Test options for this thread's later calls: MOE_DEBUG_PERMUTE_ORDER (permuted
+    workgroup -> work-item order, seeded) and MOE_DEBUG_DECODE_FUSED (two-launch decode)."""
+    _check("moe_set_debug_options", lib.moe_set_debug_options(int(flags), int(seed) & 0xFFFFFFFF))
+
+
 def moe_profile_kernel(kernel, start_event: Optional[int], stop_event: Optional[int]) -> None:
     """Bracket the named kernel's launches with the given hipEvent_t handles."""
     kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
@@ -362,4 +371,5 @@ __all__ = ["lib", "LIB_PATH", "MoeError", "moe_route_topk", "moe_decode_forward"
            "moe_gate_up_3d_batched", "moe_down_3d_batched", "moe_gate_up_3d_batched_train",
            "moe_backward_batched",
            "moe_backward_workspace_bytes", "moe_profile_kernel", "workspace",
+           "moe_set_debug_options", "MOE_DEBUG_PERMUTE_ORDER", "MOE_DEBUG_DECODE_FUSED",
            "MOE_BF16", "MOE_MXFP8", "KERNELS"]

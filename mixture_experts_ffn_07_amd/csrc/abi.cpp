@@ -19,10 +19,18 @@ ProfileHook& profile_hook() {
   thread_local ProfileHook hook;
   return hook;
 }
+
+DebugOptions& debug_options() {
+  thread_local DebugOptions opts;
+  return opts;
+}
 }  // namespace moe
 
 static_assert(MOE_STATIC_SCRATCH_BYTES == moe::kStaticScratchBytes,
               "the header's scratch size must match the array's");
+static_assert(MOE_DEBUG_PERMUTE_ORDER == moe::kDebugPermute &&
+              MOE_DEBUG_DECODE_FUSED == moe::kDebugDecodeFused, "debug option bits");
+static_assert(MOE_KERNEL_COUNT == moe::kKernelCount, "kernel ids");
 
 namespace {
 
@@ -134,6 +142,15 @@ int moe_profile_kernel(int kernel, void* start_event, void* stop_event) {
   h.kernel = (start_event && stop_event) ? kernel : 0;
   h.start = static_cast<hipEvent_t>(start_event);
   h.stop = static_cast<hipEvent_t>(stop_event);
+  return ok();
+}
+
+int moe_set_debug_options(unsigned flags, uint32_t seed) {
+  if (flags & ~(MOE_DEBUG_PERMUTE_ORDER | MOE_DEBUG_DECODE_FUSED))
+    return fail(MOE_ERR_SHAPE, "unknown debug option bits 0x%x", flags);
+  moe::DebugOptions& o = moe::debug_options();
+  o.flags = flags;
+  o.seed = seed;
   return ok();
 }
 

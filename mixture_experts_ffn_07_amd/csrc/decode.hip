@@ -21,6 +21,12 @@
 // Determinism: expert order (ascending id), token order, the MFMA sequence
 // and the cross-wave sum order are all fixed; nothing accumulates through
 // atomics (the only atomic is an integer OR that builds expert token masks).
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <random>
+#include <utility>
+
 #include "common.h"
 #include "internal.h"
 #include "route.h"
@@ -46,6 +52,7 @@ DecodeWs decode_ws_layout(int T, int H, int I, int E, int k) {
   L.idx = o;         o = align256(o + sizeof(int32_t) * pairs);
   L.w = o;           o = align256(o + sizeof(float) * pairs);
   L.hw = o;          o = align256(o + 2 * pairs * I);
+  L.flags = o;       o = align256(o + sizeof(uint64_t) * kMaxDecodeGrid);
   L.total = o;
   return L;
 }
@@ -152,6 +159,282 @@ __device__ void publish_plan(int U, int P, const int* s_e, const int* s_off, con
   }
 }
 
+// down: workgroup = 8*NR output dimensions of every touched expert (NR = 1 or
+// 2 groups of 8; H/(8*NR) workgroups, enough to occupy every CU without
+// splitting the expert sum across workgroups).  The 16x16x32 MFMA is used as
+// two 8x8 products side by side: rows 0..7 and 8..15 both carry the 8
+// dimensions of a group, rows 0..7 with the first 32 of each 64 K positions
+// and rows 8..15 with the second, and columns 0..7 / 8..15 carry the same
+// tokens' matching K halves.  The two diagonal 8x8 blocks of D are the wanted
+// partial sums (the off-diagonal blocks are discarded), so every lane's weight
+// load is useful: per step a wave reads 8 rows x 128 contiguous bytes per
+// group.  The tokens are those routed to the current expert (compacted plan
+// columns).  A dense load (64 lanes, 16 bytes each) brings the wave's K range
+// of several tokens at once into a small wave-private LDS tile, from which
+// the lanes read the MFMA layout; with two groups one activation load serves
+// both (the activations are re-read by every workgroup, so wider workgroups
+// halve that traffic where H leaves enough of them).  Each wave adds an
+// expert's results into its own FP32 accumulator rows in LDS ([token][8*NR
+// dims]), in ascending expert order, first the half-0 block then the half-1
+// block; the 16 waves' accumulators are added in wave order at the end, so the
+// sum order is fixed.  The 16 waves form EGW expert groups x KSW K-slices:
+// wave (eg, ks) takes experts u = eg, eg + EGW, ... and the K range
+// [ks*I/KSW, (ks+1)*I/KSW) of each (64*KD positions), loading the next
+// expert's weights and first activations while it multiplies the current one.
+constexpr int kDownRows = 8;
+constexpr int kDownWaves = 16;
+constexpr int kDownThreads = kDownWaves * kWave;
+
+// per-KD geometry of the activation staging tile
+template <int KD>
+struct DownGeom {
+  static constexpr int kCh = 8 * KD;                // 16-byte chunks of one token's K range
+  static constexpr int kPerLoad = kWave / kCh;      // tokens one dense load covers
+  static constexpr int kTW = 2 * kPerLoad < 8 ? 2 * kPerLoad : 8;   // tokens per MFMA tile
+  static constexpr int kRow = kCh + 1;              // padded tile row (chunks): no bank conflicts
+  static constexpr int kStage = kTW * kRow;         // chunks per wave
+};
+
+// The down phase of one workgroup for output dimensions [d0, d0 + 8*NR): the
+// plan (touched experts ascending, their routed pairs in token order) is in
+// LDS; `accl` is the dynamic LDS of down_lds_bytes().  NWD waves form EGW
+// expert groups x KSW K-slices.  With PRE the weights of each wave's first two
+// tasks are loaded before `wait()` returns and the activations only after it:
+// the single-launch decode waits there for every workgroup's activations.
+template <int KD, int NR, int NWD, bool PRE, typename PE, typename PO, class Wait>
+__device__ __forceinline__ void down_phase(
+    const uint16_t* __restrict__ wd, int U, const PE* s_e, const PO* s_off,
+    const uint16_t* s_pr, const uint8_t* s_tk, const uint16_t* __restrict__ hw, int T, int H,
+    int I, int KSW, int d0, float* accl, uint16_t* __restrict__ out, Wait wait) {
+  using G = DownGeom<KD>;
+  constexpr int RW = kDownRows * NR;                // output dimensions per workgroup
+  constexpr int NTD = NWD * kWave;
+  for (int i = threadIdx.x; i < NWD * T * RW; i += NTD) accl[i] = 0.f;
+  __syncthreads();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
+  const int col = ln & 15, grp = ln >> 4;
+  const int hf = col >> 3, c8 = col & 7;            // K half and row / token within it
+  const int EGW = NWD / KSW;
+  const int ks = wv % KSW, eg = wv / KSW;
+  const int kw = I / KSW;                           // = 64 * KD
+  // weights: lane (row c8, half hf, group grp), step s -> K offset 64s + 32hf + 8grp;
+  // dimension group r adds 8r rows
+  const uint32_t woff = static_cast<uint32_t>((d0 + c8) * I + ks * kw + hf * 32 + grp * 8);
+  float* myacc = accl + wv * T * RW;
+  i32x4* stage = reinterpret_cast<i32x4*>(accl + NWD * T * RW) + wv * G::kStage;
+  // dense activation loads: lane = token slot dc, chunk dq of the wave's K range
+  const int dc = ln / G::kCh, dq = ln - dc * G::kCh;
+  const bool ld_lane = dc < G::kPerLoad;
+  const uint32_t kd = static_cast<uint32_t>(ks * kw + dq * 8);
+  i32x4* st0 = stage + dc * G::kRow + dq;           // this lane's slot for the first load
+  i32x4* st1 = st0 + G::kPerLoad * G::kRow;         // and for the second
+  // MFMA B lane (token c8, half hf, group grp): chunk 8s + 4hf + grp; tokens past the
+  // tile read a valid row whose columns are discarded
+  const i32x4* bsrc = stage + (c8 < G::kTW ? c8 : G::kTW - 1) * G::kRow + 4 * hf + grp;
+  // D: lane (column col, group grp) holds rows 4grp..4grp+3; the wanted block is
+  // group half == column half, token c8, dims 4*(grp&1)..+3
+  const bool d_lane = (grp >> 1) == hf;
+  const int dofs = 4 * (grp & 1);
+  const int ntask = U > eg ? (U - 1 - eg) / EGW + 1 : 0;
+
+  bf16x8 aA[NR][KD], aB[NR][KD];
+  i32x4 hA0 = {}, hA1 = {}, hB0 = {}, hB1 = {};
+  // activations of tokens [c0, c0 + kPerLoad) of the plan entries at `base` (nt of
+  // them): every lane loads (lanes past the tokens repeat the last valid one), so
+  // the load count is fixed
+  auto load_at = [&](int base, int c0, int nt) {
+    const int last = nt - 1;
+    const int slot = ld_lane && c0 + dc <= last ? c0 + dc : (c0 < last ? c0 : last);
+    const uint16_t* p = hw + static_cast<uint32_t>(s_pr[base + slot] * I + kd);
+    if constexpr (PRE) {        // written by other workgroups of this launch: device-coherent
+      const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+      const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return i32x4{static_cast<int>(lo), static_cast<int>(lo >> 32), static_cast<int>(hi),
+                   static_cast<int>(hi >> 32)};
+    }
+    return ld16(p);
+  };
+  auto task_plan = [&](int tsk, int& base, int& nt, int& e) {
+    const int u = eg + tsk * EGW;
+    base = __builtin_amdgcn_readfirstlane(static_cast<int>(s_off[u]));
+    nt = __builtin_amdgcn_readfirstlane(static_cast<int>(s_off[u + 1])) - base;
+    e = __builtin_amdgcn_readfirstlane(static_cast<int>(s_e[u]));
+  };
+  auto issue_w = [&](int tsk, bf16x8 (&A)[NR][KD]) {
+    int base, nt, e;
+    task_plan(tsk, base, nt, e);
+    const uint16_t* pe = wd + static_cast<size_t>(e) * H * I;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int s = 0; s < KD; ++s)
+        A[r][s] = as_bf16x8(ld16_stream(pe + woff + r * kDownRows * I + s * 64));
+  };
+  auto issue_h = [&](int tsk, i32x4& h0, i32x4& h1) {
+    int base, nt, e;
+    task_plan(tsk, base, nt, e);
+    h0 = load_at(base, 0, nt);
+    if (G::kTW > G::kPerLoad && nt > G::kPerLoad) h1 = load_at(base, G::kPerLoad, nt);
+  };
+  // loads of one task in a fixed order: first activations, weights, optional activations
+  auto issue = [&](int tsk, bf16x8 (&A)[NR][KD], i32x4& h0, i32x4& h1) {
+    int base, nt, e;
+    task_plan(tsk, base, nt, e);
+    h0 = load_at(base, 0, nt);
+    const uint16_t* pe = wd + static_cast<size_t>(e) * H * I;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int s = 0; s < KD; ++s)
+        A[r][s] = as_bf16x8(ld16_stream(pe + woff + r * kDownRows * I + s * 64));
+    if (G::kTW > G::kPerLoad && nt > G::kPerLoad) h1 = load_at(base, G::kPerLoad, nt);
+  };
+  // stage tokens [c0, c0 + kTW) (already loaded into h0, h1), multiply, accumulate
+  auto tile = [&](const bf16x8 (&A)[NR][KD], int base, int c0, int nt, const i32x4& h0,
+                  const i32x4& h1) {
+    if (ld_lane) {
+      *st0 = h0;
+      if (G::kTW > G::kPerLoad) *st1 = h1;
+    }
+    __builtin_amdgcn_wave_barrier();
+    bf16x8 b[KD];
+#pragma unroll
+    for (int s = 0; s < KD; ++s) b[s] = as_bf16x8(bsrc[8 * s]);
+    const bool on = d_lane && c8 < G::kTW && c0 + c8 < nt;
+    const int t = on ? s_tk[base + c0 + c8] : 0;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KD; ++s) d = mfma16x16x32(A[r][s], b[s], d);
+      f32x4* acc = reinterpret_cast<f32x4*>(myacc + t * RW + r * kDownRows + dofs);
+      if (on && hf == 0) *acc = *acc + d;           // half-0 block, then half-1 block
+      __builtin_amdgcn_wave_barrier();
+      if (on && hf == 1) *acc = *acc + d;
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+  auto run = [&](int tsk, const bf16x8 (&A)[NR][KD], const i32x4& h0, const i32x4& h1) {
+    int base, nt, e;
+    task_plan(tsk, base, nt, e);
+    tile(A, base, 0, nt, h0, h1);                   // every touched expert has a token
+    if (nt > G::kTW) {                              // experts with more than kTW tokens:
+      // the next tile's loads are issued before the current tile waits (fixed count,
+      // clamped rows), so their latency overlaps
+      i32x4 r0 = load_at(base, G::kTW, nt);
+      i32x4 r1 = G::kTW > G::kPerLoad ? load_at(base, G::kTW + G::kPerLoad, nt) : r0;
+      for (int c0 = G::kTW; c0 < nt; c0 += G::kTW) {
+        const i32x4 n0 = load_at(base, c0 + G::kTW, nt);
+        const i32x4 n1 = G::kTW > G::kPerLoad ? load_at(base, c0 + G::kTW + G::kPerLoad, nt) : n0;
+        tile(A, base, c0, nt, r0, r1);
+        r0 = n0;
+        r1 = n1;
+      }
+    }
+  };
+  // one task ahead: the loads of task t+1 are in flight while task t multiplies
+  int t = 0;
+  if (PRE) {
+    // the first two tasks' weights before the wait, their activations after it
+    if (ntask > 0) issue_w(0, aA);
+    if (ntask > 1) issue_w(1, aB);
+    wait();
+    if (ntask > 0) issue_h(0, hA0, hA1);
+    if (ntask > 1) {
+      issue_h(1, hB0, hB1);
+      run(0, aA, hA0, hA1);
+      if (ntask > 2) issue(2, aA, hA0, hA1);
+      run(1, aB, hB0, hB1);
+      t = 2;
+    }
+  } else if (ntask > 0) {
+    issue(0, aA, hA0, hA1);
+  }
+  if (t < ntask) {
+    for (; t + 2 < ntask; t += 2) {
+      issue(t + 1, aB, hB0, hB1);
+      run(t, aA, hA0, hA1);
+      issue(t + 2, aA, hA0, hA1);
+      run(t + 1, aB, hB0, hB1);
+    }
+    if (t + 1 < ntask) {
+      issue(t + 1, aB, hB0, hB1);
+      run(t, aA, hA0, hA1);
+      run(t + 1, aB, hB0, hB1);
+    } else {
+      run(t, aA, hA0, hA1);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * RW; i += NTD) {
+    float v = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NWD; ++w2) v += accl[w2 * T * RW + i];
+    const int tt = i / RW, mm = i - tt * RW;
+    out[static_cast<size_t>(tt) * H + d0 + mm] = static_cast<uint16_t>(f32_to_bf16_rne(v));
+  }
+}
+
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
+// Wait of the single-launch decode: every workgroup of the grid has published
+// flag == epoch (a 64-bit value unique to the launch, so flags left by earlier
+// launches never match).  Wave 0 polls the flags with device-scope loads,
+// bounded by kGridWaitPolls rounds.  The activations behind the flags were
+// written with device-scope stores that had completed before each flag was
+// written, and the down phase reads them with device-scope loads, so no cache
+// needs flushing here.  *fail = 1 if the bound was reached.
+constexpr int kGridWaitPolls = 1 << 20;
+struct GridWait {
+  const uint64_t* flags;
+  uint64_t epoch;
+  int n;
+  int* fail;
+  __device__ void operator()() const {
+    if (wave_id() == 0) {
+      bool ok = false;
+      for (int it = 0; it < kGridWaitPolls; ++it) {
+        bool mine = true;
+        for (int i = lane_id(); i < n; i += kWave)
+          mine = mine && __hip_atomic_load(flags + i, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == epoch;
+        ok = __all(mine);
+        if (ok) break;
+        __builtin_amdgcn_s_sleep(4);
+      }
+      if (lane_id() == 0) *fail = ok ? 0 : 1;
+    }
+    __syncthreads();
+  }
+};
+
+template <int KD, int NR>
+__global__ __launch_bounds__(kDownThreads) void decode_down(
+    const uint16_t* __restrict__ wd, const int* __restrict__ plan_u,
+    const int32_t* __restrict__ plan_e, const int32_t* __restrict__ plan_off,
+    const uint16_t* __restrict__ plan_pr, const uint16_t* __restrict__ hw, int T, int H, int I,
+    int k, int KSW, uint16_t* __restrict__ out) {
+  // dynamic LDS: [16 waves][T][RW dims] FP32 accumulators, then [16 waves][kStage] chunks
+  extern __shared__ float accl[];
+  __shared__ uint16_t s_e[kMaxPlan];                // E <= 1024
+  __shared__ uint16_t s_off[kMaxPlan + 1];          // <= T*k <= 2048
+  __shared__ uint16_t s_pr[kMaxPairs];
+  __shared__ uint8_t s_tk[kMaxPairs];               // token of each plan entry (T <= 64)
+  const int U = *plan_u;
+  for (int i = threadIdx.x; i < U; i += kDownThreads) s_e[i] = static_cast<uint16_t>(plan_e[i]);
+  for (int i = threadIdx.x; i <= U; i += kDownThreads) s_off[i] = static_cast<uint16_t>(plan_off[i]);
+  for (int i = threadIdx.x; i < T * k; i += kDownThreads) {
+    const int pr = plan_pr[i];
+    s_pr[i] = static_cast<uint16_t>(pr);
+    s_tk[i] = static_cast<uint8_t>(pr / k);
+  }
+  down_phase<KD, NR, kDownWaves, false>(wd, U, s_e, s_off, s_pr, s_tk, hw, T, H, I, KSW,
+                                         blockIdx.x * kDownRows * NR, accl, out, NoWait());
+}
+
 // gate_up: work item = (touched expert u, block of NB = 8*NG neurons);
 // workgroups stride over items.  The K dimension H is cut into steps of 64
 // positions and the eight waves share them (wave wv takes steps
@@ -176,13 +459,29 @@ __device__ void publish_plan(int U, int P, const int* s_e, const int* s_off, con
 // result is bit-identical) into LDS past the plan scratch, and workgroup 0
 // writes topk_idx / topk_w out.  Otherwise the routing launch has written them
 // and each workgroup copies them into the same LDS area.
-template <int TM8, int NG, int KC>   // TM8 <= 4: T <= 32
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_gate_up(
+//
+// FUSED (the single-launch decode, T <= 16): after its last item every
+// workgroup publishes a flag (its activations written and made visible at
+// device scope), and then runs the down phase for output dimensions
+// [8*dg, 8*dg + 8), dg = blockIdx.x, blockIdx.x + gridDim.x, ...: the weights of
+// each wave's first two down tasks are loaded while it waits for every
+// workgroup's flag (they do not depend on the activations), and the rest as in
+// decode_down.  The grid is sized from the occupancy query so that every
+// workgroup is resident at once on the device; a workgroup that is not yet
+// resident (other work holding CUs) is placed as that work retires, since
+// nothing it waits for depends on this kernel.  The wait is bounded all the
+// same (kGridWaitPolls polls), and a workgroup that gives up writes NaN into
+// its outputs.
+template <int TM8, int NG, int KC, int NW = kDecWaves, bool FUSED = false, int KD = 3>   // TM8 <= 4: T <= 32
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_gate_up(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
     const float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ wts,
     int T, int E, int* __restrict__ plan_u, int32_t* __restrict__ plan_e,
     int32_t* __restrict__ plan_off, uint16_t* __restrict__ plan_pr, int H, int I, int k,
-    uint16_t* __restrict__ hw, int route_off, int route) {
+    uint16_t* __restrict__ hw, int route_off, int route, const uint16_t* __restrict__ wd,
+    uint16_t* __restrict__ out, uint64_t* __restrict__ flags, uint64_t epoch, int KSW) {
+  constexpr int kDecWaves = NW;                     // this instantiation's waves
+  constexpr int kDecThreads = NW * kWave;
   constexpr int NB = 8 * NG;                        // neurons per item
   // dynamic LDS: two buffers (alternate items) of [8 waves][TM8 tiles][NG groups]
   // [gate/up][4 regs][16 lanes] FP32 per-wave sums, which the plan scratch (E masks,
@@ -197,11 +496,12 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   if (route) {
     // wave w routes tokens w and w + 8 (T <= 16)
     const int w0 = wave_id();
-    if (E <= 64) route_tokens_wave<1, 2>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
-    else if (E <= 128) route_tokens_wave<2, 2>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
-    else if (E <= 256) route_tokens_wave<4, 2>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
-    else if (E <= 512) route_tokens_wave<8, 2>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
-    else route_tokens_wave<16, 2>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
+    constexpr int NTW = (16 + NW - 1) / NW;          // tokens per wave (T <= 16)
+    if (E <= 64) route_tokens_wave<1, NTW>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
+    else if (E <= 128) route_tokens_wave<2, NTW>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
+    else if (E <= 256) route_tokens_wave<4, NTW>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
+    else if (E <= 512) route_tokens_wave<8, NTW>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
+    else route_tokens_wave<16, NTW>(logits, T, E, k, w0, kDecWaves, r_idx, r_w);
     __syncthreads();
     if (blockIdx.x == 0) {
       for (int i = threadIdx.x; i < T * k; i += kDecThreads) {
@@ -230,13 +530,16 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   const int S = H / 64;                             // steps of 64 positions
   const int s0 = wv * S / kDecWaves, s1 = (wv + 1) * S / kDecWaves;
   const int nch = (s1 - s0) / KC;                   // chunks per item (KC divides s1 - s0)
-  const int my_items = blockIdx.x < items ? (items - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  // FUSED: workgroups take gate_up items from the top of the grid down, so the
+  // low-numbered ones, which also do the down phase, hold the fewest items
+  const int gb = FUSED ? static_cast<int>(gridDim.x - 1 - blockIdx.x) : static_cast<int>(blockIdx.x);
+  const int my_items = gb < items ? (items - 1 - gb) / gridDim.x + 1 : 0;
   // lane's K offset within a step: half hf, 16-byte group grp
   const uint32_t kl = static_cast<uint32_t>(s0 * 64 + hf * 32 + grp * 8);
   const size_t up_off = static_cast<size_t>(I) * H;
 
   auto item_of = [&](int j, int& u, int& rb) {
-    const int item = blockIdx.x + j * gridDim.x;
+    const int item = gb + j * gridDim.x;
     u = item / nrb;
     rb = item - u * nrb;
   };
@@ -334,7 +637,12 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
       if (p < nt) {
         const int pr = s_pr[b0 + p];                 // pair t*k + j of this token and expert
         const float hv = s_w[b0 + p] * swiglu(gs, us);
-        hw[static_cast<size_t>(pr) * I + rb * NB + m] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+        const uint16_t hb = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+        uint16_t* hp = hw + static_cast<size_t>(pr) * I + rb * NB + m;
+        if constexpr (FUSED)    // device-coherent: read by other workgroups in this launch
+          __hip_atomic_store(hp, hb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *hp = hb;
       }
     }
   };
@@ -387,7 +695,6 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
   if (nch == 0) {                                   // no K steps for this wave (H < 512)
     for (int j = 0; j < my_items; ++j) epilogue(j, false);
-    return;
   }
   // one task ahead: the loads of task t+1 are in flight while task t multiplies.
   // The steady-state loop issues unconditionally, so the compiler's waits leave
@@ -408,6 +715,37 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
       run_task(gB, uB, xB, t + 1);
     } else {
       run_task(gA, uA, xA, t);
+    }
+  }
+  if constexpr (FUSED) {
+    // publish: every wave waits until its device-coherent activation stores are
+    // complete, then one thread writes the flag (no L2-wide writeback needed)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_store(flags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int groups = H / kDownRows;
+    if (static_cast<int>(blockIdx.x) >= groups) return;      // no output dimensions here
+    __shared__ uint8_t s_tk[kMaxPairs];
+    __shared__ int s_fail;
+    for (int i = threadIdx.x; i < T * k; i += kDecThreads) s_tk[i] = static_cast<uint8_t>(s_pr[i] / k);
+    GridWait gw{flags, epoch, static_cast<int>(gridDim.x), &s_fail};
+    bool first = true;
+    for (int dg = blockIdx.x; dg < groups; dg += gridDim.x) {
+      __syncthreads();                              // the reduction buffer becomes accl
+      if (first) {
+        down_phase<KD, 1, NW, true>(wd, U, s_e, s_off, s_pr, s_tk, hw, T, H, I, KSW,
+                                    dg * kDownRows, red, out, gw);
+      } else {
+        down_phase<KD, 1, NW, false>(wd, U, s_e, s_off, s_pr, s_tk, hw, T, H, I, KSW,
+                                     dg * kDownRows, red, out, NoWait());
+      }
+      first = false;
+      if (s_fail) {                                 // the wait gave up: no silent result
+        for (int i = threadIdx.x; i < T * kDownRows; i += kDecThreads)
+          out[static_cast<size_t>(i / kDownRows) * H + dg * kDownRows + i % kDownRows] = 0x7FC0;
+      }
     }
   }
 }
@@ -751,193 +1089,6 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   }
 }
 
-// down: workgroup = 8*NR output dimensions of every touched expert (NR = 1 or
-// 2 groups of 8; H/(8*NR) workgroups, enough to occupy every CU without
-// splitting the expert sum across workgroups).  The 16x16x32 MFMA is used as
-// two 8x8 products side by side: rows 0..7 and 8..15 both carry the 8
-// dimensions of a group, rows 0..7 with the first 32 of each 64 K positions
-// and rows 8..15 with the second, and columns 0..7 / 8..15 carry the same
-// tokens' matching K halves.  The two diagonal 8x8 blocks of D are the wanted
-// partial sums (the off-diagonal blocks are discarded), so every lane's weight
-// load is useful: per step a wave reads 8 rows x 128 contiguous bytes per
-// group.  The tokens are those routed to the current expert (compacted plan
-// columns).  A dense load (64 lanes, 16 bytes each) brings the wave's K range
-// of several tokens at once into a small wave-private LDS tile, from which
-// the lanes read the MFMA layout; with two groups one activation load serves
-// both (the activations are re-read by every workgroup, so wider workgroups
-// halve that traffic where H leaves enough of them).  Each wave adds an
-// expert's results into its own FP32 accumulator rows in LDS ([token][8*NR
-// dims]), in ascending expert order, first the half-0 block then the half-1
-// block; the 16 waves' accumulators are added in wave order at the end, so the
-// sum order is fixed.  The 16 waves form EGW expert groups x KSW K-slices:
-// wave (eg, ks) takes experts u = eg, eg + EGW, ... and the K range
-// [ks*I/KSW, (ks+1)*I/KSW) of each (64*KD positions), loading the next
-// expert's weights and first activations while it multiplies the current one.
-constexpr int kDownRows = 8;
-constexpr int kDownWaves = 16;
-constexpr int kDownThreads = kDownWaves * kWave;
-
-// per-KD geometry of the activation staging tile
-template <int KD>
-struct DownGeom {
-  static constexpr int kCh = 8 * KD;                // 16-byte chunks of one token's K range
-  static constexpr int kPerLoad = kWave / kCh;      // tokens one dense load covers
-  static constexpr int kTW = 2 * kPerLoad < 8 ? 2 * kPerLoad : 8;   // tokens per MFMA tile
-  static constexpr int kRow = kCh + 1;              // padded tile row (chunks): no bank conflicts
-  static constexpr int kStage = kTW * kRow;         // chunks per wave
-};
-
-template <int KD, int NR>
-__global__ __launch_bounds__(kDownThreads) void decode_down(
-    const uint16_t* __restrict__ wd, const int* __restrict__ plan_u,
-    const int32_t* __restrict__ plan_e, const int32_t* __restrict__ plan_off,
-    const uint16_t* __restrict__ plan_pr, const uint16_t* __restrict__ hw, int T, int H, int I,
-    int k, int KSW, uint16_t* __restrict__ out) {
-  using G = DownGeom<KD>;
-  constexpr int RW = kDownRows * NR;                // output dimensions per workgroup
-  // dynamic LDS: [16 waves][T][RW dims] FP32 accumulators, then [16 waves][kStage] chunks
-  extern __shared__ float accl[];
-  __shared__ uint16_t s_e[kMaxPlan];                // E <= 1024
-  __shared__ uint16_t s_off[kMaxPlan + 1];          // <= T*k <= 2048
-  __shared__ uint16_t s_pr[kMaxPairs];
-  __shared__ uint8_t s_tk[kMaxPairs];               // token of each plan entry (T <= 64)
-  const int U = *plan_u;
-  for (int i = threadIdx.x; i < U; i += kDownThreads) s_e[i] = static_cast<uint16_t>(plan_e[i]);
-  for (int i = threadIdx.x; i <= U; i += kDownThreads) s_off[i] = static_cast<uint16_t>(plan_off[i]);
-  for (int i = threadIdx.x; i < T * k; i += kDownThreads) {
-    const int pr = plan_pr[i];
-    s_pr[i] = static_cast<uint16_t>(pr);
-    s_tk[i] = static_cast<uint8_t>(pr / k);
-  }
-  for (int i = threadIdx.x; i < kDownWaves * T * RW; i += kDownThreads) accl[i] = 0.f;
-  __syncthreads();
-  const int wv = __builtin_amdgcn_readfirstlane(wave_id()), ln = lane_id();
-  const int col = ln & 15, grp = ln >> 4;
-  const int hf = col >> 3, c8 = col & 7;            // K half and row / token within it
-  const int EGW = kDownWaves / KSW;
-  const int ks = wv % KSW, eg = wv / KSW;
-  const int d0 = blockIdx.x * RW;
-  const int kw = I / KSW;                           // = 64 * KD
-  // weights: lane (row c8, half hf, group grp), step s -> K offset 64s + 32hf + 8grp;
-  // dimension group r adds 8r rows
-  const uint32_t woff = static_cast<uint32_t>((d0 + c8) * I + ks * kw + hf * 32 + grp * 8);
-  float* myacc = accl + wv * T * RW;
-  i32x4* stage = reinterpret_cast<i32x4*>(accl + kDownWaves * T * RW) + wv * G::kStage;
-  // dense activation loads: lane = token slot dc, chunk dq of the wave's K range
-  const int dc = ln / G::kCh, dq = ln - dc * G::kCh;
-  const bool ld_lane = dc < G::kPerLoad;
-  const uint32_t kd = static_cast<uint32_t>(ks * kw + dq * 8);
-  i32x4* st0 = stage + dc * G::kRow + dq;           // this lane's slot for the first load
-  i32x4* st1 = st0 + G::kPerLoad * G::kRow;         // and for the second
-  // MFMA B lane (token c8, half hf, group grp): chunk 8s + 4hf + grp; tokens past the
-  // tile read a valid row whose columns are discarded
-  const i32x4* bsrc = stage + (c8 < G::kTW ? c8 : G::kTW - 1) * G::kRow + 4 * hf + grp;
-  // D: lane (column col, group grp) holds rows 4grp..4grp+3; the wanted block is
-  // group half == column half, token c8, dims 4*(grp&1)..+3
-  const bool d_lane = (grp >> 1) == hf;
-  const int dofs = 4 * (grp & 1);
-  const int ntask = U > eg ? (U - 1 - eg) / EGW + 1 : 0;
-
-  bf16x8 aA[NR][KD], aB[NR][KD];
-  i32x4 hA0 = {}, hA1 = {}, hB0 = {}, hB1 = {};
-  // activations of tokens [c0, c0 + kPerLoad) of the plan entries at `base` (nt of
-  // them): every lane loads (lanes past the tokens repeat the last valid one), so
-  // the load count is fixed
-  auto load_at = [&](int base, int c0, int nt) {
-    const int last = nt - 1;
-    const int slot = ld_lane && c0 + dc <= last ? c0 + dc : (c0 < last ? c0 : last);
-    return ld16(hw + static_cast<uint32_t>(s_pr[base + slot] * I + kd));
-  };
-  auto task_plan = [&](int tsk, int& base, int& nt, int& e) {
-    const int u = eg + tsk * EGW;
-    base = __builtin_amdgcn_readfirstlane(s_off[u]);
-    nt = __builtin_amdgcn_readfirstlane(s_off[u + 1]) - base;
-    e = __builtin_amdgcn_readfirstlane(s_e[u]);
-  };
-  // loads of one task in a fixed order: first activations, weights, optional activations
-  auto issue = [&](int tsk, bf16x8 (&A)[NR][KD], i32x4& h0, i32x4& h1) {
-    int base, nt, e;
-    task_plan(tsk, base, nt, e);
-    h0 = load_at(base, 0, nt);
-    const uint16_t* pe = wd + static_cast<size_t>(e) * H * I;
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int s = 0; s < KD; ++s)
-        A[r][s] = as_bf16x8(ld16_stream(pe + woff + r * kDownRows * I + s * 64));
-    if (G::kTW > G::kPerLoad && nt > G::kPerLoad) h1 = load_at(base, G::kPerLoad, nt);
-  };
-  // stage tokens [c0, c0 + kTW) (already loaded into h0, h1), multiply, accumulate
-  auto tile = [&](const bf16x8 (&A)[NR][KD], int base, int c0, int nt, const i32x4& h0,
-                  const i32x4& h1) {
-    if (ld_lane) {
-      *st0 = h0;
-      if (G::kTW > G::kPerLoad) *st1 = h1;
-    }
-    __builtin_amdgcn_wave_barrier();
-    bf16x8 b[KD];
-#pragma unroll
-    for (int s = 0; s < KD; ++s) b[s] = as_bf16x8(bsrc[8 * s]);
-    const bool on = d_lane && c8 < G::kTW && c0 + c8 < nt;
-    const int t = on ? s_tk[base + c0 + c8] : 0;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KD; ++s) d = mfma16x16x32(A[r][s], b[s], d);
-      f32x4* acc = reinterpret_cast<f32x4*>(myacc + t * RW + r * kDownRows + dofs);
-      if (on && hf == 0) *acc = *acc + d;           // half-0 block, then half-1 block
-      __builtin_amdgcn_wave_barrier();
-      if (on && hf == 1) *acc = *acc + d;
-      __builtin_amdgcn_wave_barrier();
-    }
-  };
-  auto run = [&](int tsk, const bf16x8 (&A)[NR][KD], const i32x4& h0, const i32x4& h1) {
-    int base, nt, e;
-    task_plan(tsk, base, nt, e);
-    tile(A, base, 0, nt, h0, h1);                   // every touched expert has a token
-    if (nt > G::kTW) {                              // experts with more than kTW tokens:
-      // the next tile's loads are issued before the current tile waits (fixed count,
-      // clamped rows), so their latency overlaps
-      i32x4 r0 = load_at(base, G::kTW, nt);
-      i32x4 r1 = G::kTW > G::kPerLoad ? load_at(base, G::kTW + G::kPerLoad, nt) : r0;
-      for (int c0 = G::kTW; c0 < nt; c0 += G::kTW) {
-        const i32x4 n0 = load_at(base, c0 + G::kTW, nt);
-        const i32x4 n1 = G::kTW > G::kPerLoad ? load_at(base, c0 + G::kTW + G::kPerLoad, nt) : n0;
-        tile(A, base, c0, nt, r0, r1);
-        r0 = n0;
-        r1 = n1;
-      }
-    }
-  };
-  // one task ahead: the loads of task t+1 are in flight while task t multiplies
-  if (ntask > 0) {
-    issue(0, aA, hA0, hA1);
-    int t = 0;
-    for (; t + 2 < ntask; t += 2) {
-      issue(t + 1, aB, hB0, hB1);
-      run(t, aA, hA0, hA1);
-      issue(t + 2, aA, hA0, hA1);
-      run(t + 1, aB, hB0, hB1);
-    }
-    if (t + 1 < ntask) {
-      issue(t + 1, aB, hB0, hB1);
-      run(t, aA, hA0, hA1);
-      run(t + 1, aB, hB0, hB1);
-    } else {
-      run(t, aA, hA0, hA1);
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < T * RW; i += kDownThreads) {
-    float v = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < kDownWaves; ++w2) v += accl[w2 * T * RW + i];
-    const int t = i / RW, mm = i - t * RW;
-    out[static_cast<size_t>(t) * H + d0 + mm] = static_cast<uint16_t>(f32_to_bf16_rne(v));
-  }
-}
-
 // dynamic LDS of decode_down<KD, NR>
 inline size_t down_lds_bytes(int T, int KD, int NR) {
   const int stage = KD == 3 ? DownGeom<3>::kStage
@@ -949,6 +1100,63 @@ inline size_t down_lds_bytes(int T, int KD, int NR) {
 // dynamic LDS of decode_gate_up<TM8, NG, KC>: two buffers of per-wave reduction sums
 inline size_t gate_up_lds_bytes(int TM8, int NG) {
   return 2 * sizeof(float) * kDecWaves * TM8 * NG * 2 * 4 * 16;
+}
+
+// dynamic LDS of the down phase with nw waves
+inline size_t down_lds_bytes_w(int T, int KD, int NR, int nw) {
+  const int stage = KD == 3 ? DownGeom<3>::kStage
+                  : KD == 4 ? DownGeom<4>::kStage
+                  : KD == 5 ? DownGeom<5>::kStage : DownGeom<7>::kStage;
+  return sizeof(float) * nw * T * kDownRows * NR + sizeof(i32x4) * nw * stage;
+}
+
+// The single-launch decode kernel for a configuration (T <= 16: TM8 <= 2; down
+// slices of KD = 3 or 4 steps, i.e. I/64 = 3 or 4 times a power of two up to 8:
+// the 5- and 7-step slices do not fit the registers beside the gate_up phase).
+const void* fused_kernel(int TM8, int NG, int KC, int KD) {
+#define FK(TMV, NGV, KCV, KDV) \
+  reinterpret_cast<const void*>(decode_gate_up<TMV, NGV, KCV, kDecWaves, true, KDV>)
+#define FK_KD(TMV, NGV, KCV) (KD == 3 ? FK(TMV, NGV, KCV, 3) : FK(TMV, NGV, KCV, 4))
+  if (TM8 == 1 && NG == 2) return KC == 2 ? FK_KD(1, 2, 2) : FK_KD(1, 2, 1);
+  if (TM8 == 1) return KC == 2 ? FK_KD(1, 1, 2) : FK_KD(1, 1, 1);
+  if (NG == 2) return FK_KD(2, 2, 1);
+  return FK_KD(2, 1, 1);
+#undef FK_KD
+#undef FK
+}
+
+// Resident workgroups per CU of a kernel (cached per kernel and LDS size; also
+// raises the kernel's dynamic LDS limit when it needs more than the default).
+hipError_t fused_occupancy(const void* fn, size_t lds, int* bpc) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, size_t>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(fn, lds);
+  auto it = cache.find(key);
+  if (it != cache.end()) {
+    *bpc = it->second;
+    return hipSuccess;
+  }
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  int n = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kDecThreads, lds);
+  if (e != hipSuccess) return e;
+  cache[key] = n;
+  *bpc = n;
+  return hipSuccess;
+}
+
+// A 64-bit value unique to each single-launch decode of this process: the
+// workgroups' ready flags carry it, so flags of an earlier launch (or whatever
+// a fresh workspace holds, short of a 2^-64 coincidence) never read as ready.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> ctr{[] {
+    std::random_device rd;
+    return ((static_cast<uint64_t>(rd()) << 32) ^ rd()) | 1u;
+  }()};
+  return ctr.fetch_add(1, std::memory_order_relaxed);
 }
 
 hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t* wgu,
@@ -1010,11 +1218,40 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   // (the 5- and 7-step slices keep one group: two would not fit 128 registers)
   const int NR = H / (2 * kDownRows) >= num_cus && KD <= 4 ? 2 : 1;
   const size_t lds_dn = down_lds_bytes(T, KD, NR);
+  if (fuse_route && !wide && (KD == 3 || KD == 4) &&
+      (debug_options().flags & kDebugDecodeFused)) {
+    // single launch: routing, gate_up and down in one grid of resident workgroups
+    uint64_t* flags = reinterpret_cast<uint64_t*>(base + L.flags);
+    const size_t lds_f = std::max(lds_gu, down_lds_bytes_w(T, KD, 1, kDecWaves));
+    const void* fn = fused_kernel(TM8, NG, KC, KD);
+    int bpc = 0;
+    hipError_t err = fused_occupancy(fn, lds_f, &bpc);
+    if (err != hipSuccess) return err;
+    if (bpc >= 1) {
+      const int per_cu = bpc < 2 ? bpc : 2;
+      int grid = per_cu * num_cus;
+      if (grid > kMaxDecodeGrid) grid = kMaxDecodeGrid;
+      uint64_t epoch = next_epoch();
+      int KSWv = KSW;
+      const uint16_t* wd_p = wd;
+      void* args[] = {const_cast<uint16_t**>(&x), const_cast<uint16_t**>(&wgu),
+                      const_cast<float**>(&logits), &idx_p, &w_p, &T, &E, &plan_u, &plan_e,
+                      &plan_off, &plan_pr, &H, &I, &k, &hw, const_cast<int*>(&route_off),
+                      const_cast<int*>(&fuse_route), const_cast<uint16_t**>(&wd_p), &out, &flags,
+                      &epoch, &KSWv};
+      prof_begin(kDecFused, s);
+      err = hipLaunchKernel(fn, dim3(grid), dim3(kDecThreads), args, static_cast<unsigned>(lds_f), s);
+      prof_end(kDecFused, s);
+      if (err != hipSuccess) return err;
+      return hipGetLastError();
+    }
+    // (no residency for the fused kernel: the two-launch path below)
+  }
   prof_begin(kDecGateUp, s);
 #define GU_LAUNCH(TMV, NGV, KCV)                                                               \
   hipLaunchKernelGGL((decode_gate_up<TMV, NGV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, \
                      x, wgu, logits, idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, \
-                     k, hw, route_off, fuse_route)
+                     k, hw, route_off, fuse_route, nullptr, nullptr, nullptr, uint64_t{0}, 0)
 #define GU_WIDE(KCV)                                                                            \
   hipLaunchKernelGGL((decode_gate_up_wide<KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x, wgu, \
                      idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw)

@@ -16,6 +16,20 @@ struct ProfileHook {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 ProfileHook& profile_hook();
+
+// Test and debugging options set by moe_set_debug_options (per calling thread).
+struct DebugOptions {
+  unsigned flags = 0;      // kDebugPermute | kDebugDecodeFused
+  uint32_t seed = 0;       // permutation of the workgroup -> work-item order
+};
+constexpr unsigned kDebugPermute = 1u;
+constexpr unsigned kDebugDecodeFused = 2u;
+DebugOptions& debug_options();
+// The work-item permutation key of the calling thread's launches (0: none).
+inline uint32_t order_key() {
+  const DebugOptions& o = debug_options();
+  return (o.flags & kDebugPermute) ? ((o.seed * 2654435761u) | 1u) : 0u;
+}
 inline void prof_begin(int id, hipStream_t s) {
   const ProfileHook& h = profile_hook();
   if (h.kernel == id && h.start) (void)hipEventRecord(h.start, s);
@@ -26,7 +40,8 @@ inline void prof_end(int id, hipStream_t s) {
 }
 enum KernelId { kRoute = 1, kDecGateUp = 2, kDecDown = 3, kGroup = 4, kQuant = 5,
                 kGemmGateUp = 6, kGemmDown = 7, kCombine = 8, kBwdGateUp = 9, kBwdDown = 10,
-                kBwdInput = 11, kBwdWDown = 12, kBwdWGateUp = 13, kKernelCount = 14 };
+                kBwdInput = 11, kBwdWDown = 12, kBwdWGateUp = 13, kDecFused = 14,
+                kKernelCount = 15 };
 
 // Library-owned device scratch (scratch.hip): kStaticScratchBytes per GPU for
 // the entry points that allocate nothing.  static_scratch(dev) gives its device
@@ -37,8 +52,10 @@ constexpr int kMaxDevices = 64;
 hipError_t static_scratch(int dev, void** ptr);
 
 // Byte layout of the decode workspace.
+// flags: one 64-bit ready flag per workgroup of the single-launch decode.
+constexpr int kMaxDecodeGrid = 4096;
 struct DecodeWs {
-  size_t plan_u, plan_e, plan_off, plan_pr, idx, w, hw, total;
+  size_t plan_u, plan_e, plan_off, plan_pr, idx, w, hw, flags, total;
 };
 DecodeWs decode_ws_layout(int T, int H, int I, int E, int k);
 

@@ -255,3 +255,11 @@ def test_binding_validates_tensor_arguments(m):
         m.moe_decode_forward(x, logits, wgu, wd, k, topk_idx=tw)
     with pytest.raises(ValueError, match="gu_saved"):
         m.moe_backward_batched(x, wgu, wd, idx, tw, x, k, gu_saved=torch.zeros(T * k, I))
+
+
+def test_debug_options_validation(m):
+    assert m.lib.moe_set_debug_options(0, 0) == m.MOE_OK
+    assert m.lib.moe_set_debug_options(m.MOE_DEBUG_PERMUTE_ORDER | m.MOE_DEBUG_DECODE_FUSED, 7) == m.MOE_OK
+    assert m.lib.moe_set_debug_options(4, 0) == m.MOE_ERR_SHAPE
+    assert b"unknown" in m.lib.moe_last_error()
+    assert m.lib.moe_set_debug_options(0, 0) == m.MOE_OK

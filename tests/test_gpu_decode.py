@@ -140,3 +140,41 @@ def test_decode_accuracy_study(M):
           f"{d_fp8:.3e}; FP8 / GPU = {d_fp8 / d_gpu:.2f}", flush=True)
     assert d_gpu < 1.2 * d_bf16
     assert d_fp8 > 3 * d_gpu
+
+
+def _run_opts(M, d, flags):
+    M.moe_set_debug_options(flags, 0)
+    try:
+        return _run(M, d)
+    finally:
+        M.moe_set_debug_options(0, 0)
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (1, 2048, 768, 128, 8),     # the Qwen3-style shape at T = 1 (one down task per wave)
+    (8, 2048, 768, 128, 8),     # T = 8: ~52 touched experts, tasks beyond the prefetched two
+    (16, 2048, 768, 128, 8),    # T = 16: two token tiles, 16-neuron items
+    (2, 7168, 512, 16, 2),      # 896 output groups: workgroups take several groups
+    (4, 256, 256, 8, 2),        # 32 output groups: most workgroups have none
+    (3, 512, 1536, 10, 3),      # I = 1536: eight K-slices of three steps
+    (5, 1024, 2048, 16, 3),     # I = 2048: eight K-slices of four steps
+])
+def test_decode_single_launch_matches_two_launches(M, T, H, I, E, k):
+    # T <= 16 runs as two launches by default; the debug option runs routing,
+    # gate_up and down as one launch.  Both meet the oracle's bars, and agree
+    # closely (the single launch's down phase sums its waves' partials in a
+    # different fixed grouping)
+    d = _custom(T, H, I, E, k, seed=100 + T)
+    what = f"T={T} H={H} I={I} E={E} k={k}"
+    print(f"[decode] single launch vs two launches {what}", flush=True)
+    one, idx1, w1 = _run_opts(M, d, M.MOE_DEBUG_DECODE_FUSED)
+    two, idx2, w2 = _run(M, d)
+    assert torch.equal(idx1, idx2) and torch.equal(w1.view(torch.int32), w2.view(torch.int32))
+    ref = oracle(d)
+    check_bf16(one, ref, f"single launch {what}")
+    check_bf16(two, ref, f"two launches {what}")
+    from oracle.moe import rel_l2
+    assert rel_l2(one.double().cpu().numpy(), two.double().cpu().numpy()) < 2e-3
+    for _ in range(9):                                # ten byte-equal runs of the single launch
+        again, _, _ = _run_opts(M, d, M.MOE_DEBUG_DECODE_FUSED)
+        assert torch.equal(again.view(torch.int16), one.view(torch.int16))
