@@ -112,7 +112,7 @@ __device__ __forceinline__ void pack_pairs(const i32x4& v0, const i32x4& v1, uin
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 template <int KIND, int MT>   // kGU, kDD, kDG; MT = routed rows per M-tile (64 or 128)
-__global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
   constexpr int MI = MT / 32;                         // 16-row A blocks per wave
   constexpr int AROW_U = MT * 8 / 256;                // "rows" A units per thread
   constexpr int BROW_U = kNT * 8 / 256;               // "rows" B units per thread (kGU)
@@ -127,8 +127,9 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
   // ---- work item: (M-tile of MT routed rows, 128 output columns) ----
   const int N = KIND == kGU ? 2 * I : (KIND == kDD ? I : H);
   const int nblk = N / kNT;
-  const int item = real_item(blockIdx.x, nblk, *a.n_tiles);
-  if (item < 0) return;
+  const int item0 = real_item(blockIdx.x, nblk, *a.n_tiles);
+  if (item0 < 0) return;
+  const int item = permute_item(item0, nblk * *a.n_tiles, okey);
   const int tile = item / nblk;
   const int n0 = (item - tile * nblk) * kNT;
   const int2 te = a.tiles[tile];
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a) {
 // neighbouring lanes trade halves (64 contiguous bytes per row per store).
 template <int KIND>   // kWD, kWG (at most 256 registers: two workgroups per CU)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_wgrad(
-    BwdArgs a) {
+    BwdArgs a, uint32_t okey) {
   __shared__ __align__(16) uint16_t lds[4 * 128 * kKC];
   uint16_t* const As = lds;                           // [2][128 rows][64 K]
   uint16_t* const Bs = lds + 2 * 128 * kKC;           // [2][128 columns][64 K]
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int H = a.H, I = a.I, k = a.k;
   const int M = KIND == kWD ? H : 2 * I, N = KIND == kWD ? I : H;
   const int mb = M / 128, nb = N / kNT, mgs = (mb + kMB - 1) / kMB;
-  const int item = xcd_item(blockIdx.x, gridDim.x);
+  const int item = permute_item(xcd_item(blockIdx.x, gridDim.x), gridDim.x, okey);
   if (item >= a.E * nb * mgs) return;
   const int e = item / (nb * mgs);
   const int rem = item - e * (nb * mgs);
@@ -542,8 +543,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // dx[t] = sum_j dxs[row of (t, j)] in slot order (FP32), rounded once to BF16.
 __global__ __launch_bounds__(256) void sum_pairs(const float* __restrict__ dxs,
                                                  const int* __restrict__ row_of, int T, int H, int k,
-                                                 uint16_t* __restrict__ dx) {
-  const int t = blockIdx.x;
+                                                 uint16_t* __restrict__ dx, uint32_t okey) {
+  const int t = permute_item(blockIdx.x, gridDim.x, okey);
   const int P = T * k;
   for (int c = threadIdx.x; c < H / 4; c += blockDim.x) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -568,10 +569,10 @@ __global__ __launch_bounds__(64) void route_bwd(const float* __restrict__ dwp,
                                                 const int32_t* __restrict__ idx,
                                                 const float* __restrict__ w, int T, int E, int k,
                                                 int nI, float* __restrict__ dtw,
-                                                float* __restrict__ dl) {
+                                                float* __restrict__ dl, uint32_t okey) {
   __shared__ int s_idx[32];
   __shared__ float s_val[32];
-  const int t = blockIdx.x, j = threadIdx.x;
+  const int t = permute_item(blockIdx.x, gridDim.x, okey), j = threadIdx.x;
   const int P = T * k;
   float dw = 0.0f, wj = 0.0f;
   if (j < k) {
@@ -599,10 +600,10 @@ __global__ __launch_bounds__(64) void route_bwd(const float* __restrict__ dwp,
 // (BF16), w a (BF16) and the partial dots a . dh per 128 columns, with the
 // arithmetic of bwd_gemm's kDD epilogue.  Thread = (row, 8 consecutive columns);
 // 16 rows x 128 columns per workgroup.
-__global__ __launch_bounds__(256) void bwd_dh_finish(BwdArgs a, const float* __restrict__ dh, int P) {
+__global__ __launch_bounds__(256) void bwd_dh_finish(BwdArgs a, const float* __restrict__ dh, int P, uint32_t okey) {
   const int I = a.I;
   const int tid = threadIdx.x, sg = tid & 15;
-  const int row = blockIdx.x * 16 + (tid >> 4);
+  const int row = permute_item(blockIdx.x, gridDim.x, okey) * 16 + (tid >> 4);
   const int n0 = blockIdx.y * kNT;
   if (row >= P) return;                             // whole 16-lane row groups leave together
   const size_t grow = static_cast<size_t>(row);
@@ -754,8 +755,8 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   };
   if (!gu_saved) {
     prof_begin(kBwdGateUp, s);
-    if (tall) hipLaunchKernelGGL((bwd_gemm<kGU, 128>), grid_tiles(2 * I), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((bwd_gemm<kGU, 64>), grid_tiles(2 * I), dim3(256), 0, s, a);
+    if (tall) hipLaunchKernelGGL((bwd_gemm<kGU, 128>), grid_tiles(2 * I), dim3(256), 0, s, a, order_key());
+    else hipLaunchKernelGGL((bwd_gemm<kGU, 64>), grid_tiles(2 * I), dim3(256), 0, s, a, order_key());
     prof_end(kBwdGateUp, s);
   }
   // large groups: 256-row M-tiles over the same (deterministic) grouping for the
@@ -780,11 +781,11 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
       err = launch_dh_large(dout, wdT, a.perm, tiles256, n_tiles256, a.counts, a.offsets, H, I, k,
                             dh, partial, L.max_tiles256, num_cus, s);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(bwd_dh_finish, dim3((P + 15) / 16, I / kNT), dim3(256), 0, s, a, dh, P);
+    hipLaunchKernelGGL(bwd_dh_finish, dim3((P + 15) / 16, I / kNT), dim3(256), 0, s, a, dh, P, order_key());
   } else if (tall) {
-    hipLaunchKernelGGL((bwd_gemm<kDD, 128>), grid_tiles(I), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_gemm<kDD, 128>), grid_tiles(I), dim3(256), 0, s, a, order_key());
   } else {
-    hipLaunchKernelGGL((bwd_gemm<kDD, 64>), grid_tiles(I), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_gemm<kDD, 64>), grid_tiles(I), dim3(256), 0, s, a, order_key());
   }
   prof_end(kBwdDown, s);
   prof_begin(kBwdInput, s);
@@ -797,11 +798,11 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
                                2 * I, k, a.dxs, dx, partial, L.max_tiles256, num_cus, s);
     if (err != hipSuccess) return err;
   } else if (tall) {
-    hipLaunchKernelGGL((bwd_gemm<kDG, 128>), grid_tiles(H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_gemm<kDG, 128>), grid_tiles(H), dim3(256), 0, s, a, order_key());
   } else {
-    hipLaunchKernelGGL((bwd_gemm<kDG, 64>), grid_tiles(H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_gemm<kDG, 64>), grid_tiles(H), dim3(256), 0, s, a, order_key());
   }
-  if (k > 1) hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, a.dxs, row_of, T, H, k, dx);
+  if (k > 1) hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, a.dxs, row_of, T, H, k, dx, order_key());
   prof_end(kBwdInput, s);
   if (L.large_w) {
     err = launch_wgrad_large(x, dout, a.dgu, a.wa, a.perm, a.counts, a.offsets, P, H, I, E, k,
@@ -812,14 +813,14 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
     if (err != hipSuccess) return err;
   } else {
     prof_begin(kBwdWDown, s);
-    hipLaunchKernelGGL(bwd_wgrad<kWD>, grid_w(H, I), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_wgrad<kWD>, grid_w(H, I), dim3(256), 0, s, a, order_key());
     prof_end(kBwdWDown, s);
     prof_begin(kBwdWGateUp, s);
-    hipLaunchKernelGGL(bwd_wgrad<kWG>, grid_w(2 * I, H), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_wgrad<kWG>, grid_w(2 * I, H), dim3(256), 0, s, a, order_key());
     prof_end(kBwdWGateUp, s);
   }
   hipLaunchKernelGGL(route_bwd, dim3(T), dim3(64), 0, s, a.dwp, row_of, idx, w, T, E, k, I / kNT,
-                     dtw, dlogits);
+                     dtw, dlogits, order_key());
   return hipGetLastError();
 }
 

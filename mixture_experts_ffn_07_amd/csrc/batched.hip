@@ -74,12 +74,12 @@ BatchedWs batched_ws_layout(int T, int H, int I, int E, int k, int dtype) {
 __global__ __launch_bounds__(1024) void group_experts(
     const int32_t* __restrict__ idx, int P, int E, int BM, int* __restrict__ counts,
     int* __restrict__ offsets, int2* __restrict__ tiles, int* __restrict__ n_tiles,
-    int* __restrict__ perm, int* __restrict__ row_of) {
+    int* __restrict__ perm, int* __restrict__ row_of, uint32_t okey) {
   __shared__ int hist[1024];
   __shared__ int s_red[2][16];
   __shared__ int s_wcnt[16];
   const int tid = threadIdx.x, wv = wave_id(), lane = lane_id();
-  const int e = blockIdx.x;
+  const int e = permute_item(blockIdx.x, gridDim.x, okey);
   for (int i = tid; i < E; i += blockDim.x) hist[i] = 0;
   __syncthreads();
   for (int i = tid; i < P; i += blockDim.x) {
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint16_t* __restrict__ hout, float* __restrict__ y,
-    uint16_t* __restrict__ out, float* __restrict__ gu) {
+    uint16_t* __restrict__ out, float* __restrict__ gu, uint32_t okey) {
   constexpr bool GU = KIND == kProjGateUp || KIND == kProjGateUpSave;
   constexpr bool ONE = NGW == 1;         // one 16-row weight group per wave
   constexpr int NT = NW * 64;
@@ -191,8 +191,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
   const int K = GU ? H : I;              // reduction length
   const int N = GU ? I : H;              // outputs
   const int nblk = N / (NW * RPW);
-  const int item = real_item(blockIdx.x, nblk, *n_tiles);
-  if (item < 0) return;
+  const int item0 = real_item(blockIdx.x, nblk, *n_tiles);
+  if (item0 < 0) return;
+  const int item = permute_item(item0, nblk * *n_tiles, okey);
   const int tile = item / nblk, nb_i = item - tile * nblk;
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
@@ -372,8 +373,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
 __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y,
                                                      const int* __restrict__ row_of,
                                                      const float* __restrict__ w, int T, int H,
-                                                     int k, uint16_t* __restrict__ out) {
-  const int t = blockIdx.x;
+                                                     int k, uint16_t* __restrict__ out, uint32_t okey) {
+  const int t = permute_item(blockIdx.x, gridDim.x, okey);
   const int P = T * k;
   for (int c = threadIdx.x; c < H / 4; c += blockDim.x) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -403,8 +404,9 @@ __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y
 // moe_quantize_mxfp8: four lanes per block of 32 (8 BF16 values each).
 __global__ __launch_bounds__(256) void quant_mx_rows(const uint16_t* __restrict__ src,
                                                      int64_t n_blocks, uint8_t* __restrict__ codes,
-                                                     uint8_t* __restrict__ scales) {
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+                                                     uint8_t* __restrict__ scales, uint32_t okey) {
+  const int64_t tid = static_cast<int64_t>(permute_item(blockIdx.x, gridDim.x, okey)) * blockDim.x +
+                      threadIdx.x;
   const int64_t blk = tid >> 2;
   const int part = static_cast<int>(tid & 3);
   const bool live = blk < n_blocks;
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint8_t* __restrict__ hout, uint8_t* __restrict__ hsout,
-    float* __restrict__ y, uint16_t* __restrict__ out) {
+    float* __restrict__ y, uint16_t* __restrict__ out, uint32_t okey) {
   constexpr int NT = NW * 64;
   constexpr int RPW = KIND == kProjGateUp ? 16 : 32;      // outputs per wave
   constexpr int LPT = kBM * kMCH / NT;                    // 16-byte code loads per thread
@@ -469,8 +471,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const int N = KIND == kProjGateUp ? I : H;              // outputs
   const int KB = K / 32;                                  // scale bytes per row
   const int nblk = N / (NW * RPW);
-  const int item = real_item(blockIdx.x, nblk, *n_tiles);
-  if (item < 0) return;
+  const int item0 = real_item(blockIdx.x, nblk, *n_tiles);
+  if (item0 < 0) return;
+  const int item = permute_item(item0, nblk * *n_tiles, okey);
   const int tile = item / nblk, nb_i = item - tile * nblk;
   const int2 te = tiles[tile];
   const int e = te.x, m0 = te.y;
@@ -686,7 +689,7 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
   const int P = T * k;
   prof_begin(kGroup, s);
   hipLaunchKernelGGL(group_experts, dim3(E), dim3(1024), 0, s, idx, P, E, L.bm, p.counts,
-                     p.offsets, p.tiles, p.n_tiles, p.perm, p.row_of);
+                     p.offsets, p.tiles, p.n_tiles, p.perm, p.row_of, order_key());
   prof_end(kGroup, s);
   if (L.bm == kLargeBM) {
     prof_begin(kGemmGateUp, s);
@@ -713,12 +716,12 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
       hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 8, kTallBM>), dim3(n_tall), dim3(512), 0, s,
                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                          p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                         static_cast<uint16_t*>(h), nullptr, nullptr, gu);
+                         static_cast<uint16_t*>(h), nullptr, nullptr, gu, order_key());
     else
       hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 8, kTallBM>), dim3(n_tall), dim3(512), 0, s,
                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                          p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                         static_cast<uint16_t*>(h), nullptr, nullptr, nullptr);
+                         static_cast<uint16_t*>(h), nullptr, nullptr, nullptr, order_key());
     prof_end(kGemmGateUp, s);
     return hipGetLastError();
   }
@@ -732,32 +735,32 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 8>), dim3(n_items8), dim3(512), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint16_t*>(h), nullptr, nullptr, gu);
+                       static_cast<uint16_t*>(h), nullptr, nullptr, gu, order_key());
   else if (narrow && dtype == 0)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 8>), dim3(n_items8), dim3(512), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint16_t*>(h), nullptr, nullptr, nullptr);
+                       static_cast<uint16_t*>(h), nullptr, nullptr, nullptr, order_key());
   else if (narrow)
     hipLaunchKernelGGL((gemm_mx_s<kProjGateUp, 8>), dim3(n_items8), dim3(512), 0, s,
                        static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
                        p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint8_t*>(h), hs, nullptr, nullptr);
+                       static_cast<uint8_t*>(h), hs, nullptr, nullptr, order_key());
   else if (dtype == 0 && gu)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint16_t*>(h), nullptr, nullptr, gu);
+                       static_cast<uint16_t*>(h), nullptr, nullptr, gu, order_key());
   else if (dtype == 0)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint16_t*>(h), nullptr, nullptr, nullptr);
+                       static_cast<uint16_t*>(h), nullptr, nullptr, nullptr, order_key());
   else
     hipLaunchKernelGGL((gemm_mx_s<kProjGateUp, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
                        p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint8_t*>(h), hs, nullptr, nullptr);
+                       static_cast<uint8_t*>(h), hs, nullptr, nullptr, order_key());
   prof_end(kGemmGateUp, s);
   return hipGetLastError();
 }
@@ -784,7 +787,7 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
     prof_end(kGemmDown, s);
     if (e == hipSuccess && k > 1) {
       prof_begin(kCombine, s);
-      hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out);
+      hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out, order_key());
       prof_end(kCombine, s);
       e = hipGetLastError();
     }
@@ -803,12 +806,12 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   hipLaunchKernelGGL((gemm_bf16s<KINDV, NWV>), grid, block, 0, s,                          \
                      static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),       \
                      p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr,   \
-                     p.y, out, nullptr)
+                     p.y, out, nullptr, order_key())
 #define DOWN_MX(KINDV, NWV)                                                                 \
   hipLaunchKernelGGL((gemm_mx_s<KINDV, NWV>), grid, block, 0, s,                           \
                      static_cast<const uint8_t*>(h), hs, static_cast<const uint8_t*>(wd), wds, \
                      p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr,   \
-                     nullptr, p.y, out)
+                     nullptr, p.y, out, order_key())
   prof_begin(kGemmDown, s);
   if (L.bm == kTallBM) {
     // 8 waves x 32 dimensions = 256 output dimensions per workgroup, 128-row tiles
@@ -817,7 +820,7 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
     hipLaunchKernelGGL((gemm_bf16s<KINDV, 8, kTallBM>), grid_t, block_t, 0, s,              \
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),     \
                        p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr, \
-                       p.y, out, nullptr)
+                       p.y, out, nullptr, order_key())
     if (k == 1) DOWN_TALL(kProjDownFused);
     else DOWN_TALL(kProjDown);
 #undef DOWN_TALL
@@ -833,7 +836,7 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   prof_end(kGemmDown, s);
   if (k > 1) {
     prof_begin(kCombine, s);
-    hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out);
+    hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out, order_key());
     prof_end(kCombine, s);
   }
   return hipGetLastError();
@@ -843,7 +846,7 @@ hipError_t launch_group_experts(const int32_t* idx, int P, int E, int BM, int* c
                                 int2* tiles, int* n_tiles, int* perm, int* row_of, hipStream_t s) {
   prof_begin(kGroup, s);
   hipLaunchKernelGGL(group_experts, dim3(E), dim3(1024), 0, s, idx, P, E, BM, counts, offsets,
-                     tiles, n_tiles, perm, row_of);
+                     tiles, n_tiles, perm, row_of, order_key());
   prof_end(kGroup, s);
   return hipGetLastError();
 }
@@ -855,7 +858,7 @@ hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* co
   const int64_t grid = (threads + 255) / 256;
   prof_begin(kQuant, s);
   hipLaunchKernelGGL(quant_mx_rows, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, src,
-                     n_blocks, codes, scales);
+                     n_blocks, codes, scales, order_key());
   prof_end(kQuant, s);
   return hipGetLastError();
 }

@@ -30,6 +30,7 @@
 #include "common.h"
 #include "internal.h"
 #include "route.h"
+#include "tiles.h"
 
 namespace moe {
 
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     const uint16_t* __restrict__ wd, const int* __restrict__ plan_u,
     const int32_t* __restrict__ plan_e, const int32_t* __restrict__ plan_off,
     const uint16_t* __restrict__ plan_pr, const uint16_t* __restrict__ hw, int T, int H, int I,
-    int k, int KSW, uint16_t* __restrict__ out) {
+    int k, int KSW, uint16_t* __restrict__ out, uint32_t okey) {
   // dynamic LDS: [16 waves][T][RW dims] FP32 accumulators, then [16 waves][kStage] chunks
   extern __shared__ float accl[];
   __shared__ uint16_t s_e[kMaxPlan];                // E <= 1024
@@ -432,7 +433,8 @@ __global__ __launch_bounds__(kDownThreads) void decode_down(
     s_tk[i] = static_cast<uint8_t>(pr / k);
   }
   down_phase<KD, NR, kDownWaves, false>(wd, U, s_e, s_off, s_pr, s_tk, hw, T, H, I, KSW,
-                                         blockIdx.x * kDownRows * NR, accl, out, NoWait());
+                                         permute_item(blockIdx.x, gridDim.x, okey) * kDownRows * NR,
+                                         accl, out, NoWait());
 }
 
 // gate_up: work item = (touched expert u, block of NB = 8*NG neurons);
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4, 8
     int T, int E, int* __restrict__ plan_u, int32_t* __restrict__ plan_e,
     int32_t* __restrict__ plan_off, uint16_t* __restrict__ plan_pr, int H, int I, int k,
     uint16_t* __restrict__ hw, int route_off, int route, const uint16_t* __restrict__ wd,
-    uint16_t* __restrict__ out, uint64_t* __restrict__ flags, uint64_t epoch, int KSW) {
+    uint16_t* __restrict__ out, uint64_t* __restrict__ flags, uint64_t epoch, int KSW, uint32_t okey) {
   constexpr int kDecWaves = NW;                     // this instantiation's waves
   constexpr int kDecThreads = NW * kWave;
   constexpr int NB = 8 * NG;                        // neurons per item
@@ -539,7 +541,7 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4, 8
   const size_t up_off = static_cast<size_t>(I) * H;
 
   auto item_of = [&](int j, int& u, int& rb) {
-    const int item = gb + j * gridDim.x;
+    const int item = permute_item(gb + j * gridDim.x, items, okey);
     u = item / nrb;
     rb = item - u * nrb;
   };
@@ -732,7 +734,8 @@ __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(4, 8
     for (int i = threadIdx.x; i < T * k; i += kDecThreads) s_tk[i] = static_cast<uint8_t>(s_pr[i] / k);
     GridWait gw{flags, epoch, static_cast<int>(gridDim.x), &s_fail};
     bool first = true;
-    for (int dg = blockIdx.x; dg < groups; dg += gridDim.x) {
+    for (int dg0 = blockIdx.x; dg0 < groups; dg0 += gridDim.x) {
+      const int dg = permute_item(dg0, groups, okey);
       __syncthreads();                              // the reduction buffer becomes accl
       if (first) {
         down_phase<KD, 1, NW, true>(wd, U, s_e, s_off, s_pr, s_tk, hw, T, H, I, KSW,
@@ -763,7 +766,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
     const int32_t* __restrict__ idx, const float* __restrict__ wts, int T, int E,
     int* __restrict__ plan_u, int32_t* __restrict__ plan_e, int32_t* __restrict__ plan_off,
-    uint16_t* __restrict__ plan_pr, int H, int I, int k, uint16_t* __restrict__ hw) {
+    uint16_t* __restrict__ plan_pr, int H, int I, int k, uint16_t* __restrict__ hw, uint32_t okey) {
   constexpr int TM = 4;                             // 16-token tiles (T <= 64)
   extern __shared__ float red[];                    // [8 waves][TM][gate/up][4][64]
   __shared__ int s_e[kMaxPlan];
@@ -785,7 +788,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
   auto task_w = [&](int t) -> const uint16_t* {
     const int j = t / nch, c = t - j * nch;
-    const int item = blockIdx.x + j * gridDim.x;
+    const int item = permute_item(blockIdx.x + j * gridDim.x, items, okey);
     const int u = item / nrb, rb = item - u * nrb;
     const int e = __builtin_amdgcn_readfirstlane(s_e[u]);
     return wgu + (static_cast<size_t>(e) * 2 * I + rb * 16 + col) * H + kb + c * KC * 32;
@@ -807,7 +810,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
   auto run_task = [&](const bf16x8 (&G)[KC], const bf16x8 (&UU)[KC], int t) {
     const int j = t / nch, c = t - j * nch;
-    const int item = blockIdx.x + j * gridDim.x;
+    const int item = permute_item(blockIdx.x + j * gridDim.x, items, okey);
     const int u = item / nrb, rb = item - u * nrb;
     const int base = __builtin_amdgcn_readfirstlane(s_off[u]);
     if (c == 0) {
@@ -906,7 +909,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wgu,
     const int32_t* __restrict__ idx, const float* __restrict__ wts, int T, int E,
     int* __restrict__ plan_u, int32_t* __restrict__ plan_e, int32_t* __restrict__ plan_off,
-    uint16_t* __restrict__ plan_pr, int H, int I, int k, uint16_t* __restrict__ hw) {
+    uint16_t* __restrict__ plan_pr, int H, int I, int k, uint16_t* __restrict__ hw, uint32_t okey) {
   constexpr int TM = 4;                             // 16-token tiles (T <= 64)
   constexpr int kSlice = TM * 2 * 4 * 64;           // floats per wave in the reduction buffer
   extern __shared__ float red[];                    // [8 waves][TM][gate/up][4][64]
@@ -940,7 +943,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   // weights of task t
   auto issue = [&](int t, i32x4 (&W)[4]) {
     const int j = t / nch, c = t - j * nch;
-    const int item = blockIdx.x + j * gridDim.x;
+    const int item = permute_item(blockIdx.x + j * gridDim.x, items, okey);
     const int u = item / nrb, rb = item - u * nrb;
     const int e = __builtin_amdgcn_readfirstlane(s_e[u]);
     const uint16_t* pw = wgu + (static_cast<size_t>(e) * 2 * I + rb * 16) * H + wl_off + c * 64;
@@ -957,7 +960,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
   auto load_x0 = [&](int t, bf16x8 (&XT)[2]) {
     const int j = t / nch, c = t - j * nch;
     if (c == 0) {
-      const int item = blockIdx.x + j * gridDim.x;
+      const int item = permute_item(blockIdx.x + j * gridDim.x, items, okey);
       const int u = item / nrb;
       const int b = __builtin_amdgcn_readfirstlane(s_off[u]);
       const int n = __builtin_amdgcn_readfirstlane(s_off[u + 1]) - b;
@@ -980,7 +983,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 
 
   auto run_task = [&](const i32x4 (&W)[4], const bf16x8 (&XT)[2], int t) {
     const int j = t / nch, c = t - j * nch;
-    const int item = blockIdx.x + j * gridDim.x;
+    const int item = permute_item(blockIdx.x + j * gridDim.x, items, okey);
     const int u = item / nrb, rb = item - u * nrb;
     const int base = __builtin_amdgcn_readfirstlane(s_off[u]);
     if (c == 0) {
@@ -1234,11 +1237,12 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
       uint64_t epoch = next_epoch();
       int KSWv = KSW;
       const uint16_t* wd_p = wd;
+      uint32_t okey = order_key();
       void* args[] = {const_cast<uint16_t**>(&x), const_cast<uint16_t**>(&wgu),
                       const_cast<float**>(&logits), &idx_p, &w_p, &T, &E, &plan_u, &plan_e,
                       &plan_off, &plan_pr, &H, &I, &k, &hw, const_cast<int*>(&route_off),
                       const_cast<int*>(&fuse_route), const_cast<uint16_t**>(&wd_p), &out, &flags,
-                      &epoch, &KSWv};
+                      &epoch, &KSWv, &okey};
       prof_begin(kDecFused, s);
       err = hipLaunchKernel(fn, dim3(grid), dim3(kDecThreads), args, static_cast<unsigned>(lds_f), s);
       prof_end(kDecFused, s);
@@ -1251,13 +1255,13 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
 #define GU_LAUNCH(TMV, NGV, KCV)                                                               \
   hipLaunchKernelGGL((decode_gate_up<TMV, NGV, KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, \
                      x, wgu, logits, idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, \
-                     k, hw, route_off, fuse_route, nullptr, nullptr, nullptr, uint64_t{0}, 0)
+                     k, hw, route_off, fuse_route, nullptr, nullptr, nullptr, uint64_t{0}, 0, order_key())
 #define GU_WIDE(KCV)                                                                            \
   hipLaunchKernelGGL((decode_gate_up_wide<KCV>), dim3(grid1), dim3(kDecThreads), lds_gu, s, x, wgu, \
-                     idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw)
+                     idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw, order_key())
   if (wide && H % 512 == 0) {
     hipLaunchKernelGGL(decode_gate_up_wide_stream, dim3(grid1), dim3(kDecThreads), lds_gu, s, x, wgu,
-                       idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw);
+                       idx_p, w_p, T, E, plan_u, plan_e, plan_off, plan_pr, H, I, k, hw, order_key());
   } else if (wide) {
     if (KCW == 2) GU_WIDE(2); else GU_WIDE(1);
   } else if (TM8 == 1 && NG == 2) {
@@ -1277,7 +1281,7 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   prof_begin(kDecDown, s);
 #define DN_LAUNCH(KDV, NRV)                                                                    \
   hipLaunchKernelGGL((decode_down<KDV, NRV>), dim3(H / (kDownRows * NRV)), dim3(kDownThreads),    \
-                     lds_dn, s, wd, plan_u, plan_e, plan_off, plan_pr, hw, T, H, I, k, KSW, out)
+                     lds_dn, s, wd, plan_u, plan_e, plan_off, plan_pr, hw, T, H, I, k, KSW, out, order_key())
 #define DN_NR(KDV) \
   if (NR == 2) DN_LAUNCH(KDV, 2); else DN_LAUNCH(KDV, 1);
   switch (KD) {

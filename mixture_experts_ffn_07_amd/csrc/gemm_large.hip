@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint16_t* __restrict__ hout, float* __restrict__ y,
     uint16_t* __restrict__ out, float* __restrict__ partial, int ncu, float* __restrict__ gu,
-    int E) {
+    int E, uint32_t okey) {
   extern __shared__ __align__(16) uint16_t lds[];   // [stage][A, B][256 x 64]
   constexpr bool kGU = KIND == kGateUp || KIND == kGateUpSave;
   constexpr bool kWG = KIND == kWgradGateUp || KIND == kWgradDown;
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     const int per = nA * nB, n_w = E * per;
     const int n_pad = (n_w + kXcds - 1) / kXcds * kXcds;
     if (L >= n_pad) return;
-    item = round_item(L, n_pad, ncu);
+    item = permute_item(round_item(L, n_pad, ncu), n_pad, okey);
     if (item >= n_w) return;
     e = item / per;
     large_coords(item - e * per, nA, nB, bb, nb);
@@ -219,10 +219,11 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     const int n_real = nblk * *n_tiles;
     const TailPlan plan = tail_plan(n_real, ncu, nk);
     if (plan.S > 1 && L < plan.full) {
-      item = round_item(L, plan.full, ncu);
+      item = permute_item(round_item(L, plan.full, ncu), plan.full, okey);
     } else if (plan.S > 1) {
-      const int t = L - plan.full;
-      if (t >= plan.rem * plan.S) return;
+      const int t0 = L - plan.full;
+      if (t0 >= plan.rem * plan.S) return;
+      const int t = permute_item(t0, plan.rem * plan.S, okey);
       item = plan.full + t % plan.rem;
       const int sl = t / plan.rem;
       kb = sl * nk / plan.S;
@@ -231,6 +232,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     } else {
       item = round_real_item(L, nblk, *n_tiles, ncu);
       if (item < 0) return;
+      item = permute_item(item, nblk * *n_tiles, okey);
     }
     int tile;
     large_coords(item, nblk, *n_tiles, tile, nb);
@@ -408,12 +410,12 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, uint16_t* __restrict__ hout, float* __restrict__ y, uint16_t* __restrict__ out,
-    const float* __restrict__ partial, int ncu, int nk, float* __restrict__ gu) {
+    const float* __restrict__ partial, int ncu, int nk, float* __restrict__ gu, uint32_t okey) {
   constexpr bool kGU = KIND == kGateUp || KIND == kGateUpSave;
   constexpr int kPerItem = kGU ? 32 * 256 : 64 * 256;   // threads per tail item
   const int nblk = kGU ? I / 128 : KIND == kBwdDh ? I / 256 : H / 256;
   const TailPlan plan = tail_plan(nblk * *n_tiles, ncu, nk);
-  const int g = blockIdx.x * 256 + threadIdx.x;
+  const int g = permute_item(blockIdx.x, gridDim.x, okey) * 256 + threadIdx.x;
   const int b = g / kPerItem;
   if (plan.S == 1 || b >= plan.rem) return;
   const int f = g - b * kPerItem;            // f32x4 index within the tile (gate half for gate_up)
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
-    float* __restrict__ y, uint16_t* __restrict__ out, float* __restrict__ partial, int ncu) {
+    float* __restrict__ y, uint16_t* __restrict__ out, float* __restrict__ partial, int ncu, uint32_t okey) {
   extern __shared__ __align__(16) uint8_t ldm[];   // [stage][A, B][256 x 128] then [stage][A, B][256] dwords
   uint32_t* lsc = reinterpret_cast<uint32_t*>(ldm + 2 * 2 * kMTile);
   constexpr bool kGU = KIND == kGateUp;
@@ -537,10 +539,11 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
   const int L = blockIdx.x;
   int item, kb = 0, ke = nk, slot = -1;
   if (plan.S > 1 && L < plan.full) {
-    item = round_item(L, plan.full, ncu);
+    item = permute_item(round_item(L, plan.full, ncu), plan.full, okey);
   } else if (plan.S > 1) {
-    const int t = L - plan.full;
-    if (t >= plan.rem * plan.S) return;
+    const int t0 = L - plan.full;
+    if (t0 >= plan.rem * plan.S) return;
+    const int t = permute_item(t0, plan.rem * plan.S, okey);
     item = plan.full + t % plan.rem;
     const int sl = t / plan.rem;
     kb = sl * nk / plan.S;
@@ -549,6 +552,7 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
   } else {
     item = round_real_item(L, nblk, *n_tiles, ncu);
     if (item < 0) return;
+    item = permute_item(item, nblk * *n_tiles, okey);
   }
   int tile, nb;
   large_coords(item, nblk, *n_tiles, tile, nb);
@@ -730,10 +734,11 @@ __global__ __launch_bounds__(256) void gemm_large_mx_fixup_gate_up(
     const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, int H, int I,
     uint8_t* __restrict__ hq, uint8_t* __restrict__ hs, const float* __restrict__ partial, int ncu,
-    int nk) {
+    int nk, uint32_t okey) {
   const int nblk = I / 128;
   const TailPlan plan = tail_plan(nblk * *n_tiles, ncu, nk);
-  const int b = blockIdx.x >> 3, i = (blockIdx.x >> 2) & 1, j = blockIdx.x & 3;
+  const int pb = permute_item(blockIdx.x, gridDim.x, okey);
+  const int b = pb >> 3, i = (pb >> 2) & 1, j = pb & 3;
   if (plan.S == 1 || b >= plan.rem) return;
   const int item = plan.full + b;
   int tile, nb;
@@ -778,10 +783,10 @@ hipError_t launch_gate_up_large_bf16(const uint16_t* x, const uint16_t* wgu, con
 #define LARGE_GU(KG)                                                                          \
   hipLaunchKernelGGL(gemm_large_bf16<KG>, dim3(grid), dim3(256), kLLds, s, x, wgu, perm,       \
                      tiles, n_tiles, counts, offsets, nullptr, H, I, k, h, nullptr, nullptr,  \
-                     partial, ncu, gu, 0);                                                    \
+                     partial, ncu, gu, 0, order_key());                                                    \
   hipLaunchKernelGGL(gemm_large_fixup<KG>, dim3(ncu / 2 * 32), dim3(256), 0, s, perm, tiles,   \
                      n_tiles, counts, offsets, nullptr, H, I, h, nullptr, nullptr, partial, ncu, \
-                     H / kLBK, gu)
+                     H / kLBK, gu, order_key())
   if (gu) { LARGE_GU(kGateUpSave); } else { LARGE_GU(kGateUp); }
 #undef LARGE_GU
   return hipGetLastError();
@@ -796,10 +801,10 @@ hipError_t launch_down_large_bf16(const uint16_t* h, const uint16_t* wd, const i
 #define LARGE_DOWN(KD)                                                                        \
   hipLaunchKernelGGL(gemm_large_bf16<KD>, dim3(grid), dim3(256), kLLds, s, h, wd, perm, tiles, \
                      n_tiles, counts, offsets, w, H, I, k, nullptr, y, out, partial, ncu,     \
-                     nullptr, 0);                                                             \
+                     nullptr, 0, order_key());                                                             \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
                      n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kLBK, \
-                     nullptr)
+                     nullptr, order_key())
   if (k == 1) { LARGE_DOWN(kDownFused); } else { LARGE_DOWN(kDownSlots); }
 #undef LARGE_DOWN
   return hipGetLastError();
@@ -813,9 +818,9 @@ hipError_t launch_gate_up_large_mx(const uint8_t* x, const uint8_t* xs, const ui
   const int grid = large_grid(I / 128, max_tiles, ncu);
   hipLaunchKernelGGL(gemm_large_mx<kGateUp>, dim3(grid), dim3(256), kMLds, s, x, xs, wgu, wgus,
                      perm, tiles, n_tiles, counts, offsets, nullptr, H, I, k, hq, hs, nullptr,
-                     nullptr, partial, ncu);
+                     nullptr, partial, ncu, order_key());
   hipLaunchKernelGGL(gemm_large_mx_fixup_gate_up, dim3(ncu / 2 * 8), dim3(256), 0, s, tiles,
-                     n_tiles, counts, offsets, H, I, hq, hs, partial, ncu, H / kMBK);
+                     n_tiles, counts, offsets, H, I, hq, hs, partial, ncu, H / kMBK, order_key());
   return hipGetLastError();
 }
 
@@ -828,10 +833,10 @@ hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint
 #define LARGE_DOWN_MX(KD)                                                                     \
   hipLaunchKernelGGL(gemm_large_mx<KD>, dim3(grid), dim3(256), kMLds, s, hq, hs, wd, wds,      \
                      perm, tiles, n_tiles, counts, offsets, w, H, I, k, nullptr, nullptr, y,  \
-                     out, partial, ncu);                                                      \
+                     out, partial, ncu, order_key());                                                      \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
                      n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kMBK, \
-                     nullptr)
+                     nullptr, order_key())
   if (k == 1) { LARGE_DOWN_MX(kDownFused); } else { LARGE_DOWN_MX(kDownSlots); }
 #undef LARGE_DOWN_MX
   return hipGetLastError();
@@ -870,10 +875,10 @@ template <bool TOKEN>
 __global__ __launch_bounds__(256) void wgrad_transpose(
     const uint16_t* __restrict__ src, int C, const int* __restrict__ perm, int k,
     const int* __restrict__ counts, const int* __restrict__ offsets,
-    const int* __restrict__ koff, int E, uint16_t* __restrict__ dst) {
+    const int* __restrict__ koff, int E, uint16_t* __restrict__ dst, uint32_t okey) {
   __shared__ __align__(16) uint16_t tl[64][64 + 8];
   const int KPT = koff[E];
-  const int g0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int g0 = permute_item(blockIdx.x, gridDim.x, okey) * 64, c0 = blockIdx.y * 64;
   if (g0 >= KPT) return;
   int lo = 0, hi = E - 1;                         // last e with koff[e] <= g0 (ranges non-empty)
   while (lo < hi) {
@@ -924,21 +929,21 @@ hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uin
   };
   prof_begin(kBwdWDown, s);
   hipLaunchKernelGGL(wgrad_transpose<false>, dim3(gtiles, I / 64), dim3(256), 0, s, wa, I, perm, k,
-                     counts, offsets, koff, E, waT);
+                     counts, offsets, koff, E, waT, order_key());
   hipLaunchKernelGGL(wgrad_transpose<true>, dim3(gtiles, H / 64), dim3(256), 0, s, dout, H, perm, k,
-                     counts, offsets, koff, E, doutT);
+                     counts, offsets, koff, E, doutT, order_key());
   hipLaunchKernelGGL(gemm_large_bf16<kWgradDown>, grid_w(I / 256, H / 256), dim3(256), kLLds, s,
                      doutT, waT, perm, nullptr, nullptr, counts, koff, nullptr, H, I, k, nullptr,
-                     nullptr, dwd, nullptr, ncu, nullptr, E);
+                     nullptr, dwd, nullptr, ncu, nullptr, E, order_key());
   prof_end(kBwdWDown, s);
   prof_begin(kBwdWGateUp, s);
   hipLaunchKernelGGL(wgrad_transpose<true>, dim3(gtiles, H / 64), dim3(256), 0, s, x, H, perm, k,
-                     counts, offsets, koff, E, xT);
+                     counts, offsets, koff, E, xT, order_key());
   hipLaunchKernelGGL(wgrad_transpose<false>, dim3(gtiles, 2 * I / 64), dim3(256), 0, s, dgu, 2 * I,
-                     perm, k, counts, offsets, koff, E, dguT);
+                     perm, k, counts, offsets, koff, E, dguT, order_key());
   hipLaunchKernelGGL(gemm_large_bf16<kWgradGateUp>, grid_w(H / 256, 2 * I / 256), dim3(256), kLLds,
                      s, dguT, xT, perm, nullptr, nullptr, counts, koff, nullptr, H, I, k, nullptr,
-                     nullptr, dwgu, nullptr, ncu, nullptr, E);
+                     nullptr, dwgu, nullptr, ncu, nullptr, E, order_key());
   prof_end(kBwdWGateUp, s);
   return hipGetLastError();
 }
@@ -985,10 +990,10 @@ hipError_t launch_dh_large(const uint16_t* dout, const uint16_t* wdT, const int*
   const int grid = large_grid(I / 256, max_tiles, ncu);
   hipLaunchKernelGGL(gemm_large_bf16<kBwdDh>, dim3(grid), dim3(256), kLLds, s, dout, wdT, perm,
                      tiles, n_tiles, counts, offsets, nullptr, H, I, k, nullptr, dh, nullptr,
-                     partial, ncu, nullptr, 0);
+                     partial, ncu, nullptr, 0, order_key());
   hipLaunchKernelGGL(gemm_large_fixup<kBwdDh>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,
                      n_tiles, counts, offsets, nullptr, H, I, nullptr, dh, nullptr, partial, ncu,
-                     H / kLBK, nullptr);
+                     H / kLBK, nullptr, order_key());
   return hipGetLastError();
 }
 
@@ -1000,10 +1005,10 @@ hipError_t launch_dgrad_large(const uint16_t* act, const uint16_t* wT, const int
 #define DGRAD(KD)                                                                             \
   hipLaunchKernelGGL(gemm_large_bf16<KD>, dim3(grid), dim3(256), kLLds, s, act, wT, perm, tiles, \
                      n_tiles, counts, offsets, nullptr, H, K, k, nullptr, y, out, partial, ncu,  \
-                     nullptr, 0);                                                                \
+                     nullptr, 0, order_key());                                                                \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,      \
                      n_tiles, counts, offsets, nullptr, H, K, nullptr, y, out, partial, ncu,      \
-                     K / kLBK, nullptr)
+                     K / kLBK, nullptr, order_key())
   if (k == 1) { DGRAD(kDownPlain); } else { DGRAD(kDownSlots); }
 #undef DGRAD
   return hipGetLastError();
