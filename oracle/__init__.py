@@ -24,4 +24,4 @@ routines, never against itself.
 from .formats import (bf16_decode, e4m3_decode, e4m3_encode, e8m0_decode,  # noqa: F401
                       mx_quantize, mx_dequantize, E4M3_MAX)
 from .moe import route, silu, moe_forward  # noqa: F401
-from .backward import moe_backward, silu_grad  # noqa: F401
+from .backward import moe_backward, moe_backward_mxfp8, silu_grad  # noqa: F401
