@@ -283,6 +283,45 @@ int moe_backward_batched(const uint16_t* x, const uint16_t* w_gate_up, const uin
 size_t moe_backward_workspace_bytes(int T, int H, int I, int E, int k);
 
 /*
+ * moe_backward_batched_mxfp8 -- backward pass of the MXFP8 layer
+ * (Mixture-of-Kittens summary, "What is 2.37x measured against": the MoE
+ * layer's backward in MXFP8, beside the BF16 one).  The gradients are those of
+ * moe_backward_batched for the MXFP8 layer (pre-activations g, u = W_gate_up x
+ * from the E4M3 weights and x MX-quantized along H), with every matrix product
+ * taking both operands MX-quantized (blocks of 32, the moe_quantize_mxfp8 rule)
+ * along its own reduction axis - a reading of the page, which gives the
+ * backward's speed only:
+ *   dh = W_down^T dout          dout and W_down's columns along H
+ *   dx = W_gate_up^T [dg; du]   [dg; du] and W_gate_up's columns along 2I
+ *   dw_down, dw_gate_up         both operands along the expert's routed pairs
+ *                               (token order, blocks of 32 from its first pair)
+ * from the decoded weights, the BF16 x and dout, and the FP32 a = silu(g) u and
+ * [dg; du]; d_topk_w = a . (W_down^T dout).  Sums accumulate in FP32 in a fixed
+ * order; dx and both weight gradients are rounded once to BF16.
+ *
+ *   x, dout [T, H] BF16; w_gate_up [E, 2I, H] and w_down [E, H, I] E4M3 codes
+ *   with E8M0 scales [E, 2I, H/32] and [E, H, I/32], as for the MXFP8 forward;
+ *   topk_idx, topk_w, dx, dw_gate_up, dw_down, d_topk_w, dlogits as for
+ *   moe_backward_batched (the weight gradients BF16)
+ *   workspace  >= moe_backward_mxfp8_workspace_bytes(T, H, I, E, k): the
+ *              grouping, x and dout encoded along H, both weights re-encoded
+ *              along their output axis (transposed copies, ~1.03 x the weight
+ *              bytes), FP32 pre-activations, dh, a and [dg; du] per routed pair,
+ *              the pair-axis operands and a 64 MiB K-split buffer
+ * Limits: as for moe_backward_batched, and max(H, 2I) * (T*k + 128*E) < 2^31.
+ */
+int moe_backward_batched_mxfp8(const uint16_t* x, const uint8_t* w_gate_up,
+                               const uint8_t* w_gate_up_scales, const uint8_t* w_down,
+                               const uint8_t* w_down_scales, const int32_t* topk_idx,
+                               const float* topk_w, const uint16_t* dout,
+                               int T, int H, int I, int E, int k,
+                               uint16_t* dx, uint16_t* dw_gate_up, uint16_t* dw_down,
+                               float* d_topk_w, float* dlogits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+size_t moe_backward_mxfp8_workspace_bytes(int T, int H, int I, int E, int k);
+
+/*
  * Kernel timing hook for benchmarks and profilers (not on any page).
  * moe_profile_kernel(kernel, start, stop): from now on, the calling thread's
  * launches of `kernel` are bracketed by hipEventRecord(start) and

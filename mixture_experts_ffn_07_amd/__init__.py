@@ -42,6 +42,9 @@ _SIGS = {
                                   _P, _P, _SZ, _P]),
     "moe_gate_up_3d_batched_train": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "moe_backward_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "moe_backward_batched_mxfp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P,
+                                        _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_backward_mxfp8_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "moe_profile_kernel": (_I, [_I, _P, _P]),
     "moe_set_debug_options": (_I, [ctypes.c_uint, ctypes.c_uint32]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
@@ -359,6 +362,52 @@ def moe_set_debug_options(flags: int = 0, seed: int = 0) -> None:
     _check("moe_set_debug_options", lib.moe_set_debug_options(int(flags), int(seed) & 0xFFFFFFFF))
 
 
+def moe_backward_mxfp8_workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    return int(lib.moe_backward_mxfp8_workspace_bytes(T, H, I, E, k))
+
+
+def moe_backward_batched_mxfp8(x, w_gate_up, w_gate_up_scales, w_down, w_down_scales, topk_idx,
+                               topk_w, dout, k: int, dx=None, dw_gate_up=None, dw_down=None,
+                               d_topk_w=None, dlogits=None, ws=None, stream=None):
+    """Backward pass of the MXFP8 layer; returns (dx, dw_gate_up, dw_down, d_topk_w, dlogits)."""
+    T, H = x.shape
+    E, I2, _ = w_gate_up.shape
+    I = I2 // 2
+    dev = x.device
+    _need(x, "x", (T, H), _BF16)
+    _need(w_gate_up, "w_gate_up", (E, I2, H), torch.uint8)
+    _need(w_gate_up_scales, "w_gate_up_scales", (E, I2, H // 32), torch.uint8)
+    _need(w_down, "w_down", (E, H, I), torch.uint8)
+    _need(w_down_scales, "w_down_scales", (E, H, I // 32), torch.uint8)
+    _need(topk_idx, "topk_idx", (T, k), torch.int32)
+    _need(topk_w, "topk_w", (T, k), torch.float32)
+    _need(dout, "dout", (T, H), _BF16)
+    if dx is None:
+        dx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    if dw_gate_up is None:
+        dw_gate_up = torch.empty(E, I2, H, dtype=torch.bfloat16, device=dev)
+    if dw_down is None:
+        dw_down = torch.empty(E, H, I, dtype=torch.bfloat16, device=dev)
+    if d_topk_w is None:
+        d_topk_w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    if dlogits is None:
+        dlogits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    _need(dx, "dx", (T, H), _BF16)
+    _need(dw_gate_up, "dw_gate_up", (E, I2, H), _BF16)
+    _need(dw_down, "dw_down", (E, H, I), _BF16)
+    _need(d_topk_w, "d_topk_w", (T, k), torch.float32)
+    _need(dlogits, "dlogits", (T, E), torch.float32)
+    need = moe_backward_mxfp8_workspace_bytes(T, H, I, E, k)
+    if ws is None:
+        ws = workspace(need, dev)
+    _need_ws(ws, need)
+    _check("moe_backward_batched_mxfp8", lib.moe_backward_batched_mxfp8(
+        _ptr(x), _ptr(w_gate_up), _ptr(w_gate_up_scales), _ptr(w_down), _ptr(w_down_scales),
+        _ptr(topk_idx), _ptr(topk_w), _ptr(dout), T, H, I, E, k, _ptr(dx), _ptr(dw_gate_up),
+        _ptr(dw_down), _ptr(d_topk_w), _ptr(dlogits), _ptr(ws), ws.numel(), _stream(stream)))
+    return dx, dw_gate_up, dw_down, d_topk_w, dlogits
+
+
 def moe_profile_kernel(kernel, start_event: Optional[int], stop_event: Optional[int]) -> None:
     """Bracket the named kernel's launches with the given hipEvent_t handles."""
     kid = KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
@@ -370,6 +419,7 @@ __all__ = ["lib", "LIB_PATH", "MoeError", "moe_route_topk", "moe_decode_forward"
            "moe_decode_workspace_bytes", "moe_workspace_bytes", "moe_quantize_mxfp8",
            "moe_gate_up_3d_batched", "moe_down_3d_batched", "moe_gate_up_3d_batched_train",
            "moe_backward_batched",
-           "moe_backward_workspace_bytes", "moe_profile_kernel", "workspace",
+           "moe_backward_workspace_bytes", "moe_backward_batched_mxfp8",
+           "moe_backward_mxfp8_workspace_bytes", "moe_profile_kernel", "workspace",
            "moe_set_debug_options", "MOE_DEBUG_PERMUTE_ORDER", "MOE_DEBUG_DECODE_FUSED",
            "MOE_BF16", "MOE_MXFP8", "KERNELS"]

@@ -343,6 +343,53 @@ int moe_backward_batched(const uint16_t* x, const uint16_t* w_gate_up, const uin
                     "moe_backward_batched launch");
 }
 
+size_t moe_backward_mxfp8_workspace_bytes(int T, int H, int I, int E, int k) {
+  if (T < 1 || H <= 0 || I <= 0 || E < 1 || k < 1) return 0;
+  return moe::mx_backward_ws_layout(T, H, I, E, k).total;
+}
+
+int moe_backward_batched_mxfp8(const uint16_t* x, const uint8_t* w_gate_up,
+                               const uint8_t* w_gate_up_scales, const uint8_t* w_down,
+                               const uint8_t* w_down_scales, const int32_t* topk_idx,
+                               const float* topk_w, const uint16_t* dout, int T, int H, int I,
+                               int E, int k, uint16_t* dx, uint16_t* dw_gate_up, uint16_t* dw_down,
+                               float* d_topk_w, float* dlogits, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (int st = check_common(T, H, I, E, k, 256, 256)) return st;
+  if (T < 1) return fail(MOE_ERR_SHAPE, "T=%d < 1", T);
+  if (static_cast<long long>(T) * k > (1LL << 24))
+    return fail(MOE_ERR_SHAPE, "T*k=%lld > 2^24", static_cast<long long>(T) * k);
+  if (int st = check_offsets(T, H, I, k)) return st;
+  if (static_cast<long long>(T) * k * 2 * I >= (1LL << 31))
+    return fail(MOE_ERR_SHAPE, "T*k*2I reaches 2^31");
+  // pair-axis operands: rows x (routed pairs, each expert padded to 128) below 2^31
+  {
+    const size_t cols = static_cast<size_t>(T) * k + static_cast<size_t>(128) * E;
+    const size_t rows = static_cast<size_t>(H > 2 * I ? H : 2 * I);
+    if (rows * cols >= (static_cast<size_t>(1) << 31))
+      return fail(MOE_ERR_SHAPE, "max(H, 2I) * (T*k + 128*E) reaches 2^31");
+  }
+  if (!x || !w_gate_up || !w_gate_up_scales || !w_down || !w_down_scales || !topk_idx ||
+      !topk_w || !dout || !dx || !dw_gate_up || !dw_down || !d_topk_w || !dlogits)
+    return fail(MOE_ERR_NULL, "every input and output pointer is required");
+  if (!workspace) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+  const size_t need = moe::mx_backward_ws_layout(T, H, I, E, k).total;
+  if (workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_gate_up_scales) ||
+      !aligned16(w_down) || !aligned16(w_down_scales) || !aligned16(topk_idx) ||
+      !aligned16(topk_w) || !aligned16(dout) || !aligned16(dx) || !aligned16(dw_gate_up) ||
+      !aligned16(dw_down) || !aligned16(d_topk_w) || !aligned16(dlogits) || !aligned16(workspace))
+    return fail(MOE_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  int cus = 0;
+  if (int st = device_info(&cus)) return st;
+  return hip_status(moe::launch_backward_mx(x, w_gate_up, w_gate_up_scales, w_down, w_down_scales,
+                                            topk_idx, topk_w, dout, T, H, I, E, k, dx, dw_gate_up,
+                                            dw_down, d_topk_w, dlogits, workspace,
+                                            static_cast<hipStream_t>(stream), cus),
+                    "moe_backward_batched_mxfp8 launch");
+}
+
 int moe_gate_up_3d_batched_train(const uint16_t* x, const uint16_t* w_gate_up,
                                  const int32_t* topk_idx, int T, int H, int I, int E, int k,
                                  uint16_t* h, float* gu, void* workspace, size_t workspace_bytes,

@@ -824,4 +824,329 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   return hipGetLastError();
 }
 
+// ===========================================================================
+// MXFP8 backward.  Every product takes both operands MX-quantized along its own
+// reduction axis (blocks of 32): dh = W_down^T dout along H, dx = W_gate_up^T
+// [dg; du] along 2I, both weight gradients along the expert's routed pairs.  All
+// five products run on the large-tile MXFP8 GEMM (gemm_large.hip) over one
+// 256-row tiling of the grouping; the kernels here re-quantize the weights
+// along their other axis, finish dh into [dg; du], and lay out the pair-axis
+// operands.
+namespace {
+
+// E4M3 code -> FP32 (exact): sign, 4-bit exponent with bias 7 (0: subnormal
+// m * 2^-9), 3-bit mantissa.  Codes come from MX encoders, so never NaN.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
+                    : static_cast<float>(m) * 0.001953125f;
+  return (c & 0x80u) ? -v : v;
+}
+
+// Eight values of one MX block row (the block spans the four lanes xor 1, 2 of
+// a lane quad): amax over the quad, scale, eight E4M3 codes; returns the scale
+// code.
+__device__ __forceinline__ uint32_t mx_quad_encode(const float (&v)[8], uint32_t& lo, uint32_t& hi) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  const int sx = mx_scale_exp(amax);
+  const float inv = exp2_neg(sx);
+  lo = f32x4_to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  hi = f32x4_to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+  return static_cast<uint32_t>(sx + 127);
+}
+
+// dst[b] = the MX encoding along R of src[b]^T: src codes [B][R][C] with scales
+// [B][R][C/32] (blocks along C) are decoded exactly and re-encoded as dst codes
+// [B][C][R] with scales [B][C][R/32] (blocks along R).  64 x 64 tiles.
+__global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ src,
+                                                    const uint8_t* __restrict__ src_s, int R, int C,
+                                                    uint8_t* __restrict__ dst,
+                                                    uint8_t* __restrict__ dst_s, uint32_t okey) {
+  __shared__ float tl[64][64 + 1];                  // [c][r]
+  const int c0 = permute_item(blockIdx.x, gridDim.x, okey) * 64, r0 = blockIdx.y * 64;
+  const size_t b = blockIdx.z;
+  const int tid = threadIdx.x;
+  {
+    const int r = tid >> 2, q = tid & 3;            // row r, 16 codes at columns 16q
+    const size_t row = b * R + r0 + r;
+    const i32x4 v = ld16(src + row * C + c0 + 16 * q);
+    const int sc = src_s[row * (C / 32) + (c0 + 16 * q) / 32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t code = (static_cast<uint32_t>(v[i >> 2]) >> (8 * (i & 3))) & 0xFFu;
+      tl[16 * q + i][r] = ldexpf(e4m3_value(code), sc - 127);
+    }
+  }
+  __syncthreads();
+  const int c = tid >> 2, q = tid & 3;              // out row c, 16 values at r = 16q
+  float v0[8], v1[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v0[i] = tl[c][16 * q + i];
+    v1[i] = tl[c][16 * q + 8 + i];
+  }
+  // a block of 32 along R = lanes 2 apart in q: pair (q, q ^ 1) holds 32 values
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fmaxf(fabsf(v0[i]), fabsf(v1[i])));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  const int sx = mx_scale_exp(amax);
+  const float inv = exp2_neg(sx);
+  const size_t orow = b * C + c0 + c;
+  st16(dst + orow * R + r0 + 16 * q,
+       i32x4{static_cast<int>(f32x4_to_e4m3x4(v0[0] * inv, v0[1] * inv, v0[2] * inv, v0[3] * inv)),
+             static_cast<int>(f32x4_to_e4m3x4(v0[4] * inv, v0[5] * inv, v0[6] * inv, v0[7] * inv)),
+             static_cast<int>(f32x4_to_e4m3x4(v1[0] * inv, v1[1] * inv, v1[2] * inv, v1[3] * inv)),
+             static_cast<int>(f32x4_to_e4m3x4(v1[4] * inv, v1[5] * inv, v1[6] * inv, v1[7] * inv))});
+  if ((q & 1) == 0) dst_s[orow * (R / 32) + (r0 + 16 * q) / 32] = static_cast<uint8_t>(sx + 127);
+}
+
+// The MXFP8 backward's dh finish, per grouped row r (thread = 8 columns, 16
+// rows x 128 columns per workgroup): from g, u (FP32, grouped rows [P][2I]) and
+// dh = W_down^T dout (FP32 [P][I]): a = silu(g) u and da = w dh, dg = da u
+// silu'(g), du = da silu(g); writes a and [dg; du] in FP32 (the pair-axis
+// operands of the weight gradients), [dg; du] MX-encoded along 2I (dx's
+// operand), and the partial dots a . dh per 128 columns (d topk_w).
+__global__ __launch_bounds__(256) void mx_dh_finish(const float* __restrict__ gu,
+                                                    const float* __restrict__ dh,
+                                                    const int* __restrict__ perm,
+                                                    const float* __restrict__ w, int P, int I,
+                                                    float* __restrict__ aout,
+                                                    float* __restrict__ dgu,
+                                                    uint8_t* __restrict__ dguq,
+                                                    uint8_t* __restrict__ dgus,
+                                                    float* __restrict__ dwp, uint32_t okey) {
+  const int tid = threadIdx.x, sg = tid & 15;
+  const int row = permute_item(blockIdx.x, gridDim.x, okey) * 16 + (tid >> 4);
+  const int n0 = blockIdx.y * kNT;
+  if (row >= P) return;                             // whole 16-lane row groups leave together
+  const size_t grow = static_cast<size_t>(row);
+  const float wt = w[perm[grow]];
+  const float* gp = gu + grow * (2 * I) + n0 + 8 * sg;
+  const float* hp = dh + grow * I + n0 + 8 * sg;
+  float dg[8], du[8], av[8];
+  float part = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float g = gp[q], u = gp[I + q], d = hp[q];
+    const float sgm = sigmoidf_(g);
+    const float si = g * sgm;
+    av[q] = si * u;
+    part = fmaf(av[q], d, part);
+    const float da = wt * d;
+    dg[q] = da * u * (sgm * (1.0f + g * (1.0f - sgm)));
+    du[q] = da * si;
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
+  float* ap = aout + grow * I + n0 + 8 * sg;
+  float* dp = dgu + grow * (2 * I) + n0 + 8 * sg;
+#pragma unroll
+  for (int q = 0; q < 8; q += 4) {
+    *reinterpret_cast<f32x4*>(ap + q) = f32x4{av[q], av[q + 1], av[q + 2], av[q + 3]};
+    *reinterpret_cast<f32x4*>(dp + q) = f32x4{dg[q], dg[q + 1], dg[q + 2], dg[q + 3]};
+    *reinterpret_cast<f32x4*>(dp + I + q) = f32x4{du[q], du[q + 1], du[q + 2], du[q + 3]};
+  }
+  uint32_t lo, hi;
+  const uint32_t sgc = mx_quad_encode(dg, lo, hi);
+  *reinterpret_cast<uint2*>(dguq + grow * (2 * I) + n0 + 8 * sg) = make_uint2(lo, hi);
+  const uint32_t suc = mx_quad_encode(du, lo, hi);
+  *reinterpret_cast<uint2*>(dguq + grow * (2 * I) + I + n0 + 8 * sg) = make_uint2(lo, hi);
+  if ((sg & 3) == 0) {
+    dgus[grow * (2 * I / 32) + (n0 + 8 * sg) / 32] = static_cast<uint8_t>(sgc);
+    dgus[grow * (2 * I / 32) + (I + n0 + 8 * sg) / 32] = static_cast<uint8_t>(suc);
+  }
+  if (sg == 0) dwp[grow * (I / kNT) + n0 / kNT] = part;
+}
+
+// Pair-axis operand of a weight gradient: dst[c][koff[e] + r] = the MX encoding,
+// along the routed pairs of expert e (blocks of 32 from koff[e], padding zero),
+// of element c of the expert's r-th routed row.  SRC 0: x[token] (BF16); 1:
+// w * dout[token] (BF16 dout, FP32 routing weight); 2: grouped FP32 rows
+// (src32, row stride ld).  Workgroup = 32 columns (one block) x 64 rows c.
+template <int SRC>
+__global__ __launch_bounds__(256) void mx_pair_t(const uint16_t* __restrict__ src16,
+                                                 const float* __restrict__ src32, int ld,
+                                                 const int* __restrict__ perm,
+                                                 const float* __restrict__ w, int k,
+                                                 const int* __restrict__ counts,
+                                                 const int* __restrict__ offsets,
+                                                 const int* __restrict__ koff, int E,
+                                                 uint8_t* __restrict__ dst,
+                                                 uint8_t* __restrict__ dst_s, uint32_t okey) {
+  __shared__ float tl[64][32 + 1];                  // [c][pair]
+  const int KPT = koff[E];
+  const int g0 = permute_item(blockIdx.x, gridDim.x, okey) * 32, c0 = blockIdx.y * 64;
+  if (g0 >= KPT) return;
+  int lo = 0, hi = E - 1;                           // last e with koff[e] <= g0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (koff[mid] <= g0) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int cnt = counts[e], base = offsets[e], r0 = g0 - koff[e];
+  const int tid = threadIdx.x;
+  if (SRC < 2) {
+    const int p = tid >> 3, ch = tid & 7;           // pair p, 8 values at 8ch
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (r0 + p < cnt) {
+      const int pr = perm[base + r0 + p];
+      const i32x4 raw = ld16(src16 + static_cast<size_t>(pr / k) * ld + c0 + 8 * ch);
+      const float sc = SRC == 1 ? w[pr] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u = static_cast<uint32_t>(raw[i]);
+        v[2 * i] = sc * bf16_to_f32(u & 0xFFFFu);
+        v[2 * i + 1] = sc * bf16_to_f32(u >> 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tl[8 * ch + i][p] = v[i];
+  } else {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int idx = tid + 256 * h2;
+      const int p = idx >> 4, ch = idx & 15;        // pair p, 4 values at 4ch
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (r0 + p < cnt)
+        v = *reinterpret_cast<const f32x4*>(src32 + static_cast<size_t>(base + r0 + p) * ld + c0 + 4 * ch);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tl[4 * ch + i][p] = v[i];
+    }
+  }
+  __syncthreads();
+  const int c = tid >> 2, q = tid & 3;              // out row c, pairs 8q .. 8q + 7
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = tl[c][8 * q + i];
+  uint32_t clo, chi;
+  const uint32_t scode = mx_quad_encode(v, clo, chi);
+  const size_t orow = static_cast<size_t>(c0 + c);
+  *reinterpret_cast<uint2*>(dst + orow * KPT + g0 + 8 * q) = make_uint2(clo, chi);
+  if (q == 0) dst_s[orow * (KPT / 32) + g0 / 32] = static_cast<uint8_t>(scode);
+}
+
+inline size_t a256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+MxBackwardWs mx_backward_ws_layout(int T, int H, int I, int E, int k) {
+  MxBackwardWs L{};
+  const size_t P = static_cast<size_t>(T) * k;
+  L.max_tiles = static_cast<int>(E + (P + kLargeBM - 1) / kLargeBM);
+  L.kpt_max = (P + static_cast<size_t>(E) * 127 + 127) / 128 * 128;
+  size_t o = 0;
+  L.n_tiles = o;  o += 256;
+  L.counts = o;   o = a256(o + sizeof(int) * E);
+  L.offsets = o;  o = a256(o + sizeof(int) * (E + 1));
+  L.tiles = o;    o = a256(o + sizeof(int) * 2 * L.max_tiles);
+  L.perm = o;     o = a256(o + sizeof(int) * P);
+  L.row_of = o;   o = a256(o + sizeof(int) * P);
+  L.koff = o;     o = a256(o + sizeof(int) * (E + 1));
+  L.xq = o;       o = a256(o + static_cast<size_t>(T) * H);
+  L.xs = o;       o = a256(o + static_cast<size_t>(T) * H / 32);
+  L.dq = o;       o = a256(o + static_cast<size_t>(T) * H);
+  L.ds = o;       o = a256(o + static_cast<size_t>(T) * H / 32);
+  L.wdT = o;      o = a256(o + static_cast<size_t>(E) * I * H);
+  L.wdTs = o;     o = a256(o + static_cast<size_t>(E) * I * H / 32);
+  L.wguT = o;     o = a256(o + static_cast<size_t>(E) * H * 2 * I);
+  L.wguTs = o;    o = a256(o + static_cast<size_t>(E) * H * 2 * I / 32);
+  L.gu = o;       o = a256(o + sizeof(float) * P * 2 * I);
+  L.dh = o;       o = a256(o + sizeof(float) * P * I);
+  L.a = o;        o = a256(o + sizeof(float) * P * I);
+  L.dgu = o;      o = a256(o + sizeof(float) * P * 2 * I);
+  L.dguq = o;     o = a256(o + P * 2 * I);
+  L.dgus = o;     o = a256(o + P * 2 * I / 32);
+  L.dwp = o;      o = a256(o + sizeof(float) * P * (I / kNT));
+  L.dxs = o;
+  if (k > 1) o = a256(o + sizeof(float) * P * H);
+  L.partial = o;  o = a256(o + sizeof(float) * kLargeMaxSlices * kLargeBM * 256);
+  L.aT = o;       o = a256(o + static_cast<size_t>(I) * L.kpt_max);
+  L.aTs = o;      o = a256(o + static_cast<size_t>(I) * L.kpt_max / 32);
+  L.dyT = o;      o = a256(o + static_cast<size_t>(H) * L.kpt_max);
+  L.dyTs = o;     o = a256(o + static_cast<size_t>(H) * L.kpt_max / 32);
+  L.xT = o;       o = a256(o + static_cast<size_t>(H) * L.kpt_max);
+  L.xTs = o;      o = a256(o + static_cast<size_t>(H) * L.kpt_max / 32);
+  L.dguT = o;     o = a256(o + static_cast<size_t>(2 * I) * L.kpt_max);
+  L.dguTs = o;    o = a256(o + static_cast<size_t>(2 * I) * L.kpt_max / 32);
+  L.total = o;
+  return L;
+}
+
+hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8_t* wgus,
+                              const uint8_t* wd, const uint8_t* wds, const int32_t* idx,
+                              const float* w, const uint16_t* dout, int T, int H, int I, int E,
+                              int k, uint16_t* dx, uint16_t* dwgu, uint16_t* dwd, float* dtw,
+                              float* dlogits, void* ws, hipStream_t s, int num_cus) {
+  const MxBackwardWs L = mx_backward_ws_layout(T, H, I, E, k);
+  char* b = static_cast<char*>(ws);
+  auto P8 = [&](size_t off) { return reinterpret_cast<uint8_t*>(b + off); };
+  auto PF = [&](size_t off) { return reinterpret_cast<float*>(b + off); };
+  int* counts = reinterpret_cast<int*>(b + L.counts);
+  int* offsets = reinterpret_cast<int*>(b + L.offsets);
+  int2* tiles = reinterpret_cast<int2*>(b + L.tiles);
+  int* n_tiles = reinterpret_cast<int*>(b + L.n_tiles);
+  int* perm = reinterpret_cast<int*>(b + L.perm);
+  int* row_of = reinterpret_cast<int*>(b + L.row_of);
+  int* koff = reinterpret_cast<int*>(b + L.koff);
+  float* partial = PF(L.partial);
+  const int P = T * k;
+  hipError_t err = launch_group_experts(idx, P, E, kLargeBM, counts, offsets, tiles, n_tiles, perm,
+                                        row_of, s);
+  // x and dout along H; the weights re-encoded along their output axes
+  if (err == hipSuccess) err = launch_quant_mx(x, T, H, P8(L.xq), P8(L.xs), s);
+  if (err == hipSuccess) err = launch_quant_mx(dout, T, H, P8(L.dq), P8(L.ds), s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(mx_requant_t, dim3(I / 64, H / 64, E), dim3(256), 0, s, wd, wds, H, I, P8(L.wdT),
+                     P8(L.wdTs), order_key());
+  hipLaunchKernelGGL(mx_requant_t, dim3(H / 64, 2 * I / 64, E), dim3(256), 0, s, wgu, wgus, 2 * I, H,
+                     P8(L.wguT), P8(L.wguTs), order_key());
+  // the forward's pre-activations, then dh and its finish
+  prof_begin(kBwdGateUp, s);
+  err = launch_gate_up_raw_large_mx(P8(L.xq), P8(L.xs), wgu, wgus, perm, tiles, n_tiles, counts,
+                                    offsets, H, I, k, PF(L.gu), partial, L.max_tiles, num_cus, s);
+  prof_end(kBwdGateUp, s);
+  if (err != hipSuccess) return err;
+  prof_begin(kBwdDown, s);
+  err = launch_dh_large_mx(P8(L.dq), P8(L.ds), P8(L.wdT), P8(L.wdTs), perm, tiles, n_tiles, counts,
+                           offsets, H, I, k, PF(L.dh), partial, L.max_tiles, num_cus, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(mx_dh_finish, dim3((P + 15) / 16, I / kNT), dim3(256), 0, s, PF(L.gu), PF(L.dh),
+                     perm, w, P, I, PF(L.a), PF(L.dgu), P8(L.dguq), P8(L.dgus), PF(L.dwp),
+                     order_key());
+  prof_end(kBwdDown, s);
+  // dx
+  prof_begin(kBwdInput, s);
+  err = launch_dgrad_large_mx(P8(L.dguq), P8(L.dgus), P8(L.wguT), P8(L.wguTs), perm, tiles, n_tiles,
+                              counts, offsets, H, 2 * I, k, PF(L.dxs), dx, partial, L.max_tiles,
+                              num_cus, s);
+  if (err != hipSuccess) return err;
+  if (k > 1) hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, PF(L.dxs), row_of, T, H, k, dx, order_key());
+  prof_end(kBwdInput, s);
+  // weight gradients over pair-axis operands
+  prof_begin(kBwdWGateUp, s);
+  err = launch_koff_mx(counts, E, koff, s);
+  if (err != hipSuccess) return err;
+  const unsigned gb = static_cast<unsigned>(L.kpt_max / 32);
+  hipLaunchKernelGGL(mx_pair_t<1>, dim3(gb, H / 64), dim3(256), 0, s, dout, nullptr, H, perm, w, k,
+                     counts, offsets, koff, E, P8(L.dyT), P8(L.dyTs), order_key());
+  hipLaunchKernelGGL(mx_pair_t<2>, dim3(gb, I / 64), dim3(256), 0, s, nullptr, PF(L.a), I, perm, w, k,
+                     counts, offsets, koff, E, P8(L.aT), P8(L.aTs), order_key());
+  hipLaunchKernelGGL(mx_pair_t<0>, dim3(gb, H / 64), dim3(256), 0, s, x, nullptr, H, perm, w, k,
+                     counts, offsets, koff, E, P8(L.xT), P8(L.xTs), order_key());
+  hipLaunchKernelGGL(mx_pair_t<2>, dim3(gb, 2 * I / 64), dim3(256), 0, s, nullptr, PF(L.dgu), 2 * I,
+                     perm, w, k, counts, offsets, koff, E, P8(L.dguT), P8(L.dguTs), order_key());
+  err = launch_wgrad_large_mx(P8(L.aT), P8(L.aTs), P8(L.dyT), P8(L.dyTs), P8(L.xT), P8(L.xTs),
+                              P8(L.dguT), P8(L.dguTs), koff, H, I, E, dwgu, dwd, num_cus, s);
+  prof_end(kBwdWGateUp, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_bwd, dim3(T), dim3(64), 0, s, PF(L.dwp), row_of, idx, w, T, E, k, I / kNT,
+                     dtw, dlogits, order_key());
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -39,7 +39,8 @@ namespace {
 constexpr int kLBK = 64;                     // K per stage
 constexpr int kLTile = kLargeBM * kLBK;      // elements per operand stage (256 rows x 64)
 constexpr size_t kLLds = 2 * 2 * kLTile * sizeof(uint16_t);   // 128 KB
-enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2, kGateUpSave = 3, kWgradGateUp = 4, kWgradDown = 5, kDownPlain = 6, kBwdDh = 7 };
+enum { kGateUp = 0, kDownFused = 1, kDownSlots = 2, kGateUpSave = 3, kWgradGateUp = 4, kWgradDown = 5, kDownPlain = 6, kBwdDh = 7,
+       kGateUpRaw = 8 };   // kGateUpRaw: FP32 g and u per grouped row (no activation)
 
 // Tail split.  One workgroup fills a CU, so n items run in ceil(n / ncu)
 // rounds; when the last round would leave more than half of the CUs idle, its
@@ -120,10 +121,11 @@ __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const 
   for (int j = 0; j < 4; ++j) {
     const int r = wm * 128 + 32 * j + l32;
     if (r >= mcount) continue;
-    if (KIND == kGateUp || KIND == kGateUpSave) {
-      uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb * 128 + wn * 64 + 4 * hi;
-      if (KIND == kGateUpSave) {                 // FP32 g and u of the pair, slot order
-        float* gp = gu + static_cast<size_t>(perm[rbase + r]) * (2 * I) + nb * 128 + wn * 64 + 4 * hi;
+    if (KIND == kGateUp || KIND == kGateUpSave || KIND == kGateUpRaw) {
+      if (KIND == kGateUpSave || KIND == kGateUpRaw) {   // FP32 g and u: slot order / grouped rows
+        const size_t grow = KIND == kGateUpSave ? static_cast<size_t>(perm[rbase + r])
+                                                : static_cast<size_t>(rbase + r);
+        float* gp = gu + grow * (2 * I) + nb * 128 + wn * 64 + 4 * hi;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -135,6 +137,8 @@ __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const 
                       acc[i + 2][j][4 * q + 3]};
           }
       }
+      if (KIND == kGateUpRaw) continue;
+      uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb * 128 + wn * 64 + 4 * hi;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, uint16_t* __restrict__ hout, float* __restrict__ y, uint16_t* __restrict__ out,
     const float* __restrict__ partial, int ncu, int nk, float* __restrict__ gu, uint32_t okey) {
-  constexpr bool kGU = KIND == kGateUp || KIND == kGateUpSave;
+  constexpr bool kGU = KIND == kGateUp || KIND == kGateUpSave || KIND == kGateUpRaw;
   constexpr int kPerItem = kGU ? 32 * 256 : 64 * 256;   // threads per tail item
   const int nblk = kGU ? I / 128 : KIND == kBwdDh ? I / 256 : H / 256;
   const TailPlan plan = tail_plan(nblk * *n_tiles, ncu, nk);
@@ -440,13 +444,15 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
     if (kGU) u += pp[base + 2 * 16 * 256];   // up block i + 2
   }
   if (kGU) {
-    uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb * 128 + wn * 64 + 32 * i + 8 * q + 4 * hi;
-    if (KIND == kGateUpSave) {                   // FP32 g and u of the pair, slot order
-      float* gp = gu + static_cast<size_t>(perm[rbase + r]) * (2 * I) + nb * 128 + wn * 64 + 32 * i +
-                  8 * q + 4 * hi;
+    if (KIND == kGateUpSave || KIND == kGateUpRaw) {   // FP32 g and u: slot order / grouped rows
+      const size_t grow = KIND == kGateUpSave ? static_cast<size_t>(perm[rbase + r])
+                                              : static_cast<size_t>(rbase + r);
+      float* gp = gu + grow * (2 * I) + nb * 128 + wn * 64 + 32 * i + 8 * q + 4 * hi;
       *reinterpret_cast<f32x4*>(gp) = a;
       *reinterpret_cast<f32x4*>(gp + I) = u;
     }
+    if (KIND == kGateUpRaw) return;
+    uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb * 128 + wn * 64 + 32 * i + 8 * q + 4 * hi;
     uint32_t p[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) p[t] = f32_to_bf16_rne(swiglu(a[t], u[t]));
@@ -518,7 +524,19 @@ __device__ __forceinline__ f32x16 mfma_mx32(i32x8 a, i32x8 b, int sa, int sb, f3
 // KIND kGateUp:  act = x codes [T,H] + scales [T,H/32]; wt = W_gate_up codes [E,2I,H] +
 //                scales [E,2I,H/32]; writes h codes [P,I] + scales [P,I/32] (sorted rows),
 //                quantized from the FP32 SwiGLU values.
-// KIND kDown*:   act = h codes + scales; wt = W_down codes [E,H,I] + scales [E,H,I/32].
+// KIND kGateUpRaw: the same product; writes the FP32 g and u of each grouped row to
+//                y [P, 2I] (the backward's pre-activations).
+// KIND kDown*:   act = h codes + scales; wt = W_down codes [E,H,I] + scales [E,H,I/32]
+//                (the backward's dx: act = [dg; du] codes [P, 2I], wt = W_gate_up
+//                re-quantized along 2I and transposed, [E, H, 2I], with I passed as 2I).
+// KIND kBwdDh:   act = dout codes [T, H] gathered by token; wt = W_down re-quantized
+//                along H and transposed, [E, I, H]; writes FP32 dh [P, I] (grouped rows).
+// KIND kWgradDown / kWgradGateUp: weight gradients over pair-axis operands [rows][KPT]
+//                (codes + scales [rows][KPT/32], expert e's routed pairs in columns
+//                offsets[e] .. offsets[e+1], zero-padded to multiples of 128; KPT =
+//                offsets[E]): kWgradDown A = a^T (rows i), B = (w dout)^T (rows h),
+//                writes dW_down[e][h][i]; kWgradGateUp A = x^T (rows h), B = [dg; du]^T
+//                (rows c), writes dW_gate_up[e][c][h]; BF16, no K split.
 template <int KIND>
 __global__ __launch_bounds__(256) void gemm_large_mx(
     const uint8_t* __restrict__ act, const uint8_t* __restrict__ act_s,
@@ -526,40 +544,60 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
-    float* __restrict__ y, uint16_t* __restrict__ out, float* __restrict__ partial, int ncu, uint32_t okey) {
+    float* __restrict__ y, uint16_t* __restrict__ out, float* __restrict__ partial, int ncu,
+    int E, uint32_t okey) {
   extern __shared__ __align__(16) uint8_t ldm[];   // [stage][A, B][256 x 128] then [stage][A, B][256] dwords
   uint32_t* lsc = reinterpret_cast<uint32_t*>(ldm + 2 * 2 * kMTile);
-  constexpr bool kGU = KIND == kGateUp;
-  const int K = kGU ? H : I;
+  constexpr bool kGU = KIND == kGateUp || KIND == kGateUpRaw;   // gate/up rows, gathered x
+  constexpr bool kWG = KIND == kWgradGateUp || KIND == kWgradDown;
+  constexpr bool kDH = KIND == kBwdDh;               // gathered dout rows, W_down^T rows
+  constexpr bool kGather = kGU || kDH;
+  const int K = kWG ? offsets[E] : (kGather ? H : I);
   const int KSB = K / 32;                          // scale bytes per row
-  const int nblk = kGU ? I / 128 : H / 256;
+  const int nA = KIND == kWgradGateUp ? H / 256 : I / 256;       // (weight gradients)
+  const int nB = KIND == kWgradGateUp ? 2 * I / 256 : H / 256;
+  const int nblk = kGU ? I / 128 : kDH ? I / 256 : H / 256;
   const int nk = K / kMBK;
-  const int n_real = nblk * *n_tiles;
-  const TailPlan plan = tail_plan(n_real, ncu, nk);
   const int L = blockIdx.x;
   int item, kb = 0, ke = nk, slot = -1;
-  if (plan.S > 1 && L < plan.full) {
-    item = permute_item(round_item(L, plan.full, ncu), plan.full, okey);
-  } else if (plan.S > 1) {
-    const int t0 = L - plan.full;
-    if (t0 >= plan.rem * plan.S) return;
-    const int t = permute_item(t0, plan.rem * plan.S, okey);
-    item = plan.full + t % plan.rem;
-    const int sl = t / plan.rem;
-    kb = sl * nk / plan.S;
-    ke = (sl + 1) * nk / plan.S;
-    slot = t;
+  int e, nb, bb = 0, mcount = kLargeBM, rbase = 0;
+  if (kWG) {
+    const int per = nA * nB, n_w = E * per;
+    const int n_pad = (n_w + kXcds - 1) / kXcds * kXcds;
+    if (L >= n_pad) return;
+    item = permute_item(round_item(L, n_pad, ncu), n_pad, okey);
+    if (item >= n_w) return;
+    e = item / per;
+    large_coords(item - e * per, nA, nB, bb, nb);
+    kb = offsets[e] / kMBK;
+    ke = offsets[e + 1] / kMBK;
   } else {
-    item = round_real_item(L, nblk, *n_tiles, ncu);
-    if (item < 0) return;
-    item = permute_item(item, nblk * *n_tiles, okey);
+    const int n_real = nblk * *n_tiles;
+    const TailPlan plan = tail_plan(n_real, ncu, nk);
+    if (plan.S > 1 && L < plan.full) {
+      item = permute_item(round_item(L, plan.full, ncu), plan.full, okey);
+    } else if (plan.S > 1) {
+      const int t0 = L - plan.full;
+      if (t0 >= plan.rem * plan.S) return;
+      const int t = permute_item(t0, plan.rem * plan.S, okey);
+      item = plan.full + t % plan.rem;
+      const int sl = t / plan.rem;
+      kb = sl * nk / plan.S;
+      ke = (sl + 1) * nk / plan.S;
+      slot = t;
+    } else {
+      item = round_real_item(L, nblk, *n_tiles, ncu);
+      if (item < 0) return;
+      item = permute_item(item, nblk * *n_tiles, okey);
+    }
+    int tile;
+    large_coords(item, nblk, *n_tiles, tile, nb);
+    const int2 te = tiles[tile];
+    e = te.x;
+    const int m0 = te.y;
+    mcount = min(kLargeBM, counts[e] - m0);
+    rbase = offsets[e] + m0;
   }
-  int tile, nb;
-  large_coords(item, nblk, *n_tiles, tile, nb);
-  const int2 te = tiles[tile];
-  const int e = te.x, m0 = te.y;
-  const int mcount = min(kLargeBM, counts[e] - m0);
-  const int rbase = offsets[e] + m0;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, l32 = ln & 31, hi = ln >> 5;
   const int wm = wv & 1, wn = wv >> 1;
 
@@ -569,15 +607,21 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
   const uint8_t* __restrict__ asb;
   uint32_t ao, so_a, so_b;
   const int n0 = nb * 128;
-  if (kGU) {
+  if (kWG) {
+    abase = wt;
+    asb = wt_s;
+    ao = static_cast<uint32_t>((nb * 256 + wv * 64 + lrow) * K + lc * 16);
+    so_a = static_cast<uint32_t>((nb * 256 + tid) * KSB);
+  } else if (kGU) {
     abase = wt + static_cast<size_t>(e) * 2 * I * H;
     asb = wt_s + static_cast<size_t>(e) * 2 * I * KSB;
     ao = static_cast<uint32_t>(((wv < 2 ? n0 + wv * 64 : I + n0 + (wv - 2) * 64) + lrow) * H + lc * 16);
     so_a = static_cast<uint32_t>((tid < 128 ? n0 + tid : I + n0 + tid - 128) * KSB);
   } else {
+    // down: [E][H][K = I] rows h; kDH: [E][I][K = H] rows i
     abase = wt + static_cast<size_t>(e) * H * I;
-    asb = wt_s + static_cast<size_t>(e) * H * KSB;
-    ao = static_cast<uint32_t>((nb * 256 + wv * 64 + lrow) * I + lc * 16);
+    asb = wt_s + static_cast<size_t>(e) * (kDH ? I : H) * KSB;
+    ao = static_cast<uint32_t>((nb * 256 + wv * 64 + lrow) * K + lc * 16);
     so_a = static_cast<uint32_t>((nb * 256 + tid) * KSB);
   }
   uint32_t bo[8];
@@ -585,12 +629,14 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
   for (int j = 0; j < 8; ++j) {
     const int r = wv * 64 + 8 * j + lrow;
     const int rr = r < mcount ? r : 0;
-    bo[j] = kGU ? static_cast<uint32_t>((perm[rbase + rr] / k) * H + lc * 16)
-                : static_cast<uint32_t>((rbase + rr) * I + lc * 16);
+    bo[j] = kWG ? static_cast<uint32_t>((bb * 256 + r) * K + lc * 16)
+          : kGather ? static_cast<uint32_t>((perm[rbase + rr] / k) * H + lc * 16)
+                    : static_cast<uint32_t>((rbase + rr) * I + lc * 16);
   }
   {
     const int rr = tid < mcount ? tid : 0;         // scale loader: thread = tile row
-    so_b = static_cast<uint32_t>((kGU ? perm[rbase + rr] / k : rbase + rr) * KSB);
+    so_b = static_cast<uint32_t>((kWG ? bb * 256 + tid : kGather ? perm[rbase + rr] / k : rbase + rr) *
+                                 KSB);
   }
   const int lw = (wv * 64 + lrow) * kMBK + ((lc ^ lrow) * 16);
   int fa[4];
@@ -649,7 +695,9 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
   // (chunks 0..7) and the first of stage s (chunks 8..15 and the scales), as in
   // the BF16 kernel.  Prologue: stage kb and chunks 0..7 of stage kb+1 in LDS;
   // registers holding chunks 8..15 and the scales of stage kb+1 and chunks 0..7
-  // of stage kb+2.
+  // of stage kb+2.  (A weight-gradient expert with no rows has an empty range:
+  // its block is zero.)
+  if (ke > kb) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) GLOAD(q, kb);
   SLOAD(kb);
@@ -697,12 +745,35 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
 #pragma unroll
     for (int q = 0; q < 8; ++q) sc[q] = scn[q];
   }
+  }
 #undef GLOAD
 #undef SLOAD
 #undef LWRITE
 #undef SWRITE
 #undef RDP
 #undef RDS
+
+  if (kWG) {
+    // dW[e][B row][A row], BF16: lane (l32, hi) holds A rows 32i + 8q + 4hi + t of
+    // the wave's 128 and B row 32j + l32 of its 128
+    const int colsA = nA * 256;
+    uint16_t* base = out + static_cast<size_t>(e) * (nB * 256) * colsA;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint16_t* orow = base + static_cast<size_t>(bb * 256 + wm * 128 + 32 * j + l32) * colsA +
+                       nb * 256 + wn * 128 + 4 * hi;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t p[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) p[t] = f32_to_bf16_rne(acc[i][j][4 * q + t]);
+          *reinterpret_cast<uint2*>(orow + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+        }
+    }
+    return;
+  }
 
   if (slot >= 0) {
     f32x4* pp = reinterpret_cast<f32x4*>(partial) + static_cast<size_t>(slot) * 64 * 256 + tid;
@@ -716,12 +787,14 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
               f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     return;
   }
-  if (kGU) {
+  if (KIND == kGateUp) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 2; ++i) mx_store_block(acc[i][j], acc[i + 2][j], wm * 128 + 32 * j + l32, mcount,
                                                  rbase, n0 + wn * 64 + 32 * i, hi, I, hq, hs);
+  } else if (KIND == kGateUpRaw) {
+    large_epilogue<KIND>(acc, perm, w, H, I, rbase, mcount, nb, wm, wn, l32, hi, nullptr, nullptr, out, y);
   } else {
     large_epilogue<KIND>(acc, perm, w, H, I, rbase, mcount, nb, wm, wn, l32, hi, nullptr, y, out, nullptr);
   }
@@ -818,7 +891,7 @@ hipError_t launch_gate_up_large_mx(const uint8_t* x, const uint8_t* xs, const ui
   const int grid = large_grid(I / 128, max_tiles, ncu);
   hipLaunchKernelGGL(gemm_large_mx<kGateUp>, dim3(grid), dim3(256), kMLds, s, x, xs, wgu, wgus,
                      perm, tiles, n_tiles, counts, offsets, nullptr, H, I, k, hq, hs, nullptr,
-                     nullptr, partial, ncu, order_key());
+                     nullptr, partial, ncu, 0, order_key());
   hipLaunchKernelGGL(gemm_large_mx_fixup_gate_up, dim3(ncu / 2 * 8), dim3(256), 0, s, tiles,
                      n_tiles, counts, offsets, H, I, hq, hs, partial, ncu, H / kMBK, order_key());
   return hipGetLastError();
@@ -833,7 +906,7 @@ hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint
 #define LARGE_DOWN_MX(KD)                                                                     \
   hipLaunchKernelGGL(gemm_large_mx<KD>, dim3(grid), dim3(256), kMLds, s, hq, hs, wd, wds,      \
                      perm, tiles, n_tiles, counts, offsets, w, H, I, k, nullptr, nullptr, y,  \
-                     out, partial, ncu, order_key());                                                      \
+                     out, partial, ncu, 0, order_key());                                                   \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
                      n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kMBK, \
                      nullptr, order_key())
@@ -842,16 +915,82 @@ hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint
   return hipGetLastError();
 }
 
+// ---- MXFP8 backward on the large-tile GEMM (launched from backward.hip) ----
+
+hipError_t launch_gate_up_raw_large_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* wgu,
+                                       const uint8_t* wgus, const int* perm, const int2* tiles,
+                                       const int* n_tiles, const int* counts, const int* offsets,
+                                       int H, int I, int k, float* gu, float* partial,
+                                       int max_tiles, int ncu, hipStream_t s) {
+  const int grid = large_grid(I / 128, max_tiles, ncu);
+  hipLaunchKernelGGL(gemm_large_mx<kGateUpRaw>, dim3(grid), dim3(256), kMLds, s, xq, xs, wgu, wgus,
+                     perm, tiles, n_tiles, counts, offsets, nullptr, H, I, k, nullptr, nullptr, gu,
+                     nullptr, partial, ncu, 0, order_key());
+  hipLaunchKernelGGL(gemm_large_fixup<kGateUpRaw>, dim3(ncu / 2 * 32), dim3(256), 0, s, perm, tiles,
+                     n_tiles, counts, offsets, nullptr, H, I, nullptr, nullptr, nullptr, partial,
+                     ncu, H / kMBK, gu, order_key());
+  return hipGetLastError();
+}
+
+hipError_t launch_dh_large_mx(const uint8_t* dq, const uint8_t* ds, const uint8_t* wdT,
+                              const uint8_t* wdTs, const int* perm, const int2* tiles,
+                              const int* n_tiles, const int* counts, const int* offsets, int H,
+                              int I, int k, float* dh, float* partial, int max_tiles, int ncu,
+                              hipStream_t s) {
+  const int grid = large_grid(I / 256, max_tiles, ncu);
+  hipLaunchKernelGGL(gemm_large_mx<kBwdDh>, dim3(grid), dim3(256), kMLds, s, dq, ds, wdT, wdTs, perm,
+                     tiles, n_tiles, counts, offsets, nullptr, H, I, k, nullptr, nullptr, dh,
+                     nullptr, partial, ncu, 0, order_key());
+  hipLaunchKernelGGL(gemm_large_fixup<kBwdDh>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,
+                     n_tiles, counts, offsets, nullptr, H, I, nullptr, dh, nullptr, partial, ncu,
+                     H / kMBK, nullptr, order_key());
+  return hipGetLastError();
+}
+
+hipError_t launch_dgrad_large_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* wT,
+                                 const uint8_t* wTs, const int* perm, const int2* tiles,
+                                 const int* n_tiles, const int* counts, const int* offsets, int H,
+                                 int K, int k, float* y, uint16_t* out, float* partial,
+                                 int max_tiles, int ncu, hipStream_t s) {
+  const int grid = large_grid(H / 256, max_tiles, ncu);
+#define DGRAD_MX(KD)                                                                          \
+  hipLaunchKernelGGL(gemm_large_mx<KD>, dim3(grid), dim3(256), kMLds, s, aq, as, wT, wTs, perm, \
+                     tiles, n_tiles, counts, offsets, nullptr, H, K, k, nullptr, nullptr, y,  \
+                     out, partial, ncu, 0, order_key());                                     \
+  hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
+                     n_tiles, counts, offsets, nullptr, H, K, nullptr, y, out, partial, ncu,   \
+                     K / kMBK, nullptr, order_key())
+  if (k == 1) { DGRAD_MX(kDownPlain); } else { DGRAD_MX(kDownSlots); }
+#undef DGRAD_MX
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_large_mx(const uint8_t* aT, const uint8_t* aTs, const uint8_t* dyT,
+                                 const uint8_t* dyTs, const uint8_t* xT, const uint8_t* xTs,
+                                 const uint8_t* dguT, const uint8_t* dguTs, const int* koff,
+                                 int H, int I, int E, uint16_t* dwgu, uint16_t* dwd, int ncu,
+                                 hipStream_t s) {
+  const int nd = (E * (I / 256) * (H / 256) + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(gemm_large_mx<kWgradDown>, dim3(nd), dim3(256), kMLds, s, dyT, dyTs, aT, aTs,
+                     nullptr, nullptr, nullptr, nullptr, koff, nullptr, H, I, 1, nullptr, nullptr,
+                     nullptr, dwd, nullptr, ncu, E, order_key());
+  const int ng = (E * (H / 256) * (2 * I / 256) + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL(gemm_large_mx<kWgradGateUp>, dim3(ng), dim3(256), kMLds, s, dguT, dguTs, xT,
+                     xTs, nullptr, nullptr, nullptr, nullptr, koff, nullptr, H, I, 1, nullptr,
+                     nullptr, nullptr, dwgu, nullptr, ncu, E, order_key());
+  return hipGetLastError();
+}
+
 namespace {
 // Column offsets of the weight-gradient operands: koff[e] = sum over e' < e of
 // counts[e'] rounded up to 64, koff[E] = KPT.  One wave: each lane sums a run of
 // experts, then an exclusive scan over the lanes.
 __global__ __launch_bounds__(64) void wgrad_koff(const int* __restrict__ counts, int E,
-                                                 int* __restrict__ koff) {
+                                                 int* __restrict__ koff, int pad) {
   const int ln = threadIdx.x;
   const int per = (E + 63) / 64, e0 = ln * per, e1 = min(E, e0 + per);
   int sum = 0;
-  for (int e = e0; e < e1; ++e) sum += (counts[e] + kLBK - 1) / kLBK * kLBK;
+  for (int e = e0; e < e1; ++e) sum += (counts[e] + pad - 1) / pad * pad;
   int incl = sum;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -861,7 +1000,7 @@ __global__ __launch_bounds__(64) void wgrad_koff(const int* __restrict__ counts,
   int run = incl - sum;
   for (int e = e0; e < e1; ++e) {
     koff[e] = run;
-    run += (counts[e] + kLBK - 1) / kLBK * kLBK;
+    run += (counts[e] + pad - 1) / pad * pad;
   }
   if (ln == 63) koff[E] = incl;
 }
@@ -923,7 +1062,7 @@ hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uin
                               uint16_t* xT, uint16_t* doutT, uint16_t* dguT, uint16_t* waT,
                               uint16_t* dwgu, uint16_t* dwd, int ncu, hipStream_t s) {
   const unsigned gtiles = static_cast<unsigned>((wgrad_large_cols(P, E) + 63) / 64);
-  hipLaunchKernelGGL(wgrad_koff, dim3(1), dim3(64), 0, s, counts, E, koff);
+  hipLaunchKernelGGL(wgrad_koff, dim3(1), dim3(64), 0, s, counts, E, koff, kLBK);
   auto grid_w = [&](int nA, int nB) {
     return dim3(static_cast<unsigned>((E * nA * nB + kXcds - 1) / kXcds * kXcds));
   };
@@ -1014,6 +1153,12 @@ hipError_t launch_dgrad_large(const uint16_t* act, const uint16_t* wT, const int
   return hipGetLastError();
 }
 
+// Column offsets of the pair-axis operands padded to 128 (the MX stage).
+hipError_t launch_koff_mx(const int* counts, int E, int* koff, hipStream_t s) {
+  hipLaunchKernelGGL(wgrad_koff, dim3(1), dim3(64), 0, s, counts, E, koff, kMBK);
+  return hipGetLastError();
+}
+
 hipError_t large_set_attributes() {
   const int bytes = static_cast<int>(kLLds);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kGateUp>),
@@ -1049,6 +1194,13 @@ hipError_t large_set_attributes() {
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_mx<kDownSlots>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
+  const void* mx_bwd[] = {reinterpret_cast<const void*>(gemm_large_mx<kGateUpRaw>),
+                          reinterpret_cast<const void*>(gemm_large_mx<kBwdDh>),
+                          reinterpret_cast<const void*>(gemm_large_mx<kDownPlain>),
+                          reinterpret_cast<const void*>(gemm_large_mx<kWgradDown>),
+                          reinterpret_cast<const void*>(gemm_large_mx<kWgradGateUp>)};
+  for (const void* f : mx_bwd)
+    if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
   return e;
 }
 

@@ -154,6 +154,44 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
 hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
                            uint8_t* scales, hipStream_t s);
 
+// MXFP8 backward (backward.hip): workspace layout and launch.  kpt_max bounds the
+// pair-axis operands' columns (routed pairs, each expert padded to 128).
+struct MxBackwardWs {
+  size_t n_tiles, counts, offsets, tiles, perm, row_of, koff, xq, xs, dq, ds, wdT, wdTs, wguT,
+      wguTs, gu, dh, a, dgu, dguq, dgus, dwp, dxs, partial, aT, aTs, dyT, dyTs, xT, xTs, dguT,
+      dguTs, total;
+  size_t kpt_max;
+  int max_tiles;
+};
+MxBackwardWs mx_backward_ws_layout(int T, int H, int I, int E, int k);
+hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8_t* wgus,
+                              const uint8_t* wd, const uint8_t* wds, const int32_t* idx,
+                              const float* w, const uint16_t* dout, int T, int H, int I, int E,
+                              int k, uint16_t* dx, uint16_t* dwgu, uint16_t* dwd, float* dtw,
+                              float* dlogits, void* ws, hipStream_t s, int num_cus);
+// The large-tile MXFP8 GEMM's backward products (gemm_large.hip).
+hipError_t launch_gate_up_raw_large_mx(const uint8_t* xq, const uint8_t* xs, const uint8_t* wgu,
+                                       const uint8_t* wgus, const int* perm, const int2* tiles,
+                                       const int* n_tiles, const int* counts, const int* offsets,
+                                       int H, int I, int k, float* gu, float* partial,
+                                       int max_tiles, int ncu, hipStream_t s);
+hipError_t launch_dh_large_mx(const uint8_t* dq, const uint8_t* ds, const uint8_t* wdT,
+                              const uint8_t* wdTs, const int* perm, const int2* tiles,
+                              const int* n_tiles, const int* counts, const int* offsets, int H,
+                              int I, int k, float* dh, float* partial, int max_tiles, int ncu,
+                              hipStream_t s);
+hipError_t launch_dgrad_large_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* wT,
+                                 const uint8_t* wTs, const int* perm, const int2* tiles,
+                                 const int* n_tiles, const int* counts, const int* offsets, int H,
+                                 int K, int k, float* y, uint16_t* out, float* partial,
+                                 int max_tiles, int ncu, hipStream_t s);
+hipError_t launch_wgrad_large_mx(const uint8_t* aT, const uint8_t* aTs, const uint8_t* dyT,
+                                 const uint8_t* dyTs, const uint8_t* xT, const uint8_t* xTs,
+                                 const uint8_t* dguT, const uint8_t* dguTs, const int* koff,
+                                 int H, int I, int E, uint16_t* dwgu, uint16_t* dwd, int ncu,
+                                 hipStream_t s);
+hipError_t launch_koff_mx(const int* counts, int E, int* koff, hipStream_t s);
+
 // gu: NULL, or (BF16, small groups only) [T*k, 2I] FP32 pre-activations out, slot order
 hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* wgu,
                                   const uint8_t* wgus, const int32_t* idx, int T, int H, int I,

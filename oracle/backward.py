@@ -189,8 +189,6 @@ def moe_backward_mxfp8(x, logits, w_gate_up, w_gate_up_scales, w_down, w_down_sc
         raise ValueError("dout must be [T, H]")
     idx, w = route(logits, k)
     E = np.asarray(logits).shape[1]
-    xq = q(xb)                                   # the forward's x (along H)
-    dq = q(dof)                                  # dout along H, for dh
 
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     exps = np.arange(E) if experts is None else np.asarray(experts, dtype=np.int64)
@@ -217,11 +215,12 @@ def moe_backward_mxfp8(x, logits, w_gate_up, w_gate_up_scales, w_down, w_down_sc
         if not want_e[e]:                        # only the pairs of the asked tokens
             keep = tpos[rows] >= 0
             rows, slots = rows[keep], slots[keep]
-        g = xq[rows] @ wgu[:I].T
-        u = xq[rows] @ wgu[I:].T
+        xq = q(xb[rows])                         # the forward's x, along H (row by row)
+        g = xq @ wgu[:I].T
+        u = xq @ wgu[I:].T
         a = silu(g) * u
         wp = w[rows, slots][:, None]
-        dh = dq[rows] @ q(wd.T).T                # [n_e, I], reduction over H
+        dh = q(dof[rows]) @ q(wd.T).T            # [n_e, I], reduction over H
         da = wp * dh
         dgu = np.concatenate([da * u * silu_grad(g), da * silu(g)], axis=1)   # [n_e, 2I]
         dtw_pair = np.sum(a * dh, axis=1)

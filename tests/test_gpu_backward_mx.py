@@ -1,0 +1,133 @@
+"""GPU parity of the MXFP8 backward (moe_route_topk -> moe_backward_batched_mxfp8)
+against the FP64 oracle's MXFP8 backward (oracle/backward.py:
+moe_backward_mxfp8), which quantizes each product's operands along the same axes.
+
+dx and the weight gradients are BF16 results: relative L2 <= 3e-2 (the MXFP8
+bar) and <= 1e-2 as a tripwire (expected ~2e-3: the BF16 output rounding; both
+sides quantize the same values, the GPU from FP32 and the oracle from FP64).
+d_topk_w and dlogits stay FP32 over the same quantized products: 1e-4 and 1e-3
+relative L2 as for the BF16 backward.  Small shapes are checked in full, the
+full-size shapes on a few tokens and experts (the oracle re-encodes every
+touched expert's weights along a second axis, seconds per expert)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import moe_backward_mxfp8, route
+from oracle.moe import rel_l2
+from tests._gpu import Fetch, bits, to_f64
+
+pytestmark = pytest.mark.gpu
+
+MX_BAR = 3e-2
+MX_TRIPWIRE = 1e-2
+DTW_REL_L2 = 1e-4
+DLOGITS_REL_L2 = 1e-3
+
+
+@pytest.fixture(scope="module")
+def M():
+    import mixture_experts_ffn_07_amd as M
+    return M
+
+
+def run_bwd(M, d, dout):
+    cfg = d["cfg"]
+    idx, w = M.moe_route_topk(d["logits"], cfg.k)
+    res = M.moe_backward_batched_mxfp8(d["x"], d["w_gate_up"], d["w_gate_up_scales"], d["w_down"],
+                                       d["w_down_scales"], idx, w, dout, cfg.k)
+    torch.cuda.synchronize()
+    return res, idx
+
+
+def _cmp(got, ref, bound, what, tripwire=None):
+    g = to_f64(got)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite"
+    rl = rel_l2(g, ref) if np.any(ref != 0) else float(np.max(np.abs(g)))
+    print(f"[parity] {what}: rel_l2={rl:.3e}", flush=True)
+    assert rl <= bound, f"{what}: {rl:.3e} > {bound}"
+    if tripwire is not None:
+        assert rl <= tripwire, f"{what}: {rl:.3e} above the expected level {tripwire}"
+
+
+def _check(M, d, what, tokens=None, experts=None, seed=0):
+    cfg = d["cfg"]
+    print(f"[backward mxfp8] {what}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}", flush=True)
+    dout = W.make_output_grad(cfg, seed=seed, device="cuda")
+    (dx, dwgu, dwd, dtw, dl), idx = run_bwd(M, d, dout)
+    ref = moe_backward_mxfp8(bits(d["x"]), d["logits"].cpu().numpy(), Fetch(d["w_gate_up"]),
+                             Fetch(d["w_gate_up_scales"]), Fetch(d["w_down"]),
+                             Fetch(d["w_down_scales"]), bits(dout), cfg.k, tokens=tokens,
+                             experts=experts)
+    ts = slice(None) if tokens is None else torch.as_tensor(tokens, device="cuda")
+    es = slice(None) if experts is None else torch.as_tensor(experts, device="cuda")
+    _cmp(dx[ts], ref["dx"], MX_BAR, what + " dx", MX_TRIPWIRE)
+    _cmp(dwgu[es], ref["dw_gate_up"], MX_BAR, what + " dw_gate_up", MX_TRIPWIRE)
+    _cmp(dwd[es], ref["dw_down"], MX_BAR, what + " dw_down", MX_TRIPWIRE)
+    _cmp(dtw[ts], ref["d_topk_w"], DTW_REL_L2, what + " d_topk_w")
+    _cmp(dl[ts], ref["dlogits"], DLOGITS_REL_L2, what + " dlogits")
+    gl = to_f64(dl[ts])
+    assert np.all(gl[ref["dlogits"] == 0.0] == 0.0) or cfg.k == 1
+    if experts is None:                               # unrouted experts: zero weight gradients
+        unused = sorted(set(range(cfg.E)) - set(np.unique(idx.cpu().numpy()).tolist()))
+        for e in unused:
+            assert not torch.any(dwgu[e].view(torch.int16)) and not torch.any(dwd[e].view(torch.int16))
+
+
+def _custom(T, H, I, E, k, seed=0):
+    cfg = W.Config(name=f"bwdmx-T{T}-H{H}-I{I}-E{E}-k{k}", T=T, H=H, E=E, k=k, I=I, dtype="mxfp8",
+                   path="batched")
+    return W.make(cfg, seed=seed, device="cuda")
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (1, 256, 256, 4, 2),        # one token, two experts with one routed pair each
+    (100, 512, 256, 8, 2),      # ~25 pairs per expert: one ragged 256-row tile each
+    (300, 256, 512, 6, 3),      # ~150 pairs per expert, pair blocks of 32 with a ragged last one
+    (257, 768, 256, 40, 8),     # many small experts, some empty
+    (200, 512, 256, 5, 1),      # k = 1: dx written directly
+    (64, 256, 256, 16, 16),     # k = E
+    (1100, 512, 256, 4, 1),     # ~275 pairs per expert: K-split tails of the last round
+    (600, 256, 512, 2, 2),      # k = 2, two experts, several tiles each
+])
+def test_backward_mx_shapes(M, T, H, I, E, k):
+    _check(M, _custom(T, H, I, E, k, seed=T + E), f"mx bwd T={T} k={k}")
+
+
+def test_backward_mx_empty_expert(M):
+    d = _custom(800, 256, 256, 4, 2, seed=31)
+    lg = d["logits"].clone()
+    lg[:, 3] = -30.0
+    d["logits"] = lg.contiguous()
+    _check(M, d, "mx bwd, one empty expert")
+
+
+def _pick(d, n_experts, n_tokens, seed):
+    """The most- and least-loaded experts (and random others), and tokens routed to them."""
+    cfg = d["cfg"]
+    idx, _ = route(d["logits"].cpu().numpy(), cfg.k)
+    cnt = np.bincount(idx.ravel(), minlength=cfg.E)
+    used = np.nonzero(cnt)[0]
+    rng = np.random.default_rng(seed)
+    ex = [int(used[np.argmax(cnt[used])]), int(used[np.argmin(cnt[used])])]
+    ex += [int(e) for e in rng.permutation(used) if e not in ex][:max(0, n_experts - 2)]
+    ex = np.array(sorted(set(ex)), dtype=np.int64)
+    mine = np.nonzero(np.isin(idx, ex).any(axis=1))[0]
+    toks = np.sort(rng.choice(mine, size=min(n_tokens, mine.size), replace=False))
+    print(f"[backward mxfp8] experts {ex.tolist()} ({cnt[ex].tolist()} pairs), {toks.size} tokens",
+          flush=True)
+    return toks, ex
+
+
+def test_backward_mx_ep64_share_full_size(M):
+    # one GPU's expert-parallel share: ~2,700 pairs on each of 6 experts
+    d = W.make("dsv4-mxfp8-ep64share", seed=0, device="cuda")
+    toks, ex = _pick(d, 3, 24, seed=5)
+    _check(M, d, "dsv4-mxfp8-ep64share", tokens=toks, experts=ex)
+
+
+def test_backward_mx_dsv4_full_size(M):
+    d = W.make("dsv4-mxfp8-T2048", seed=0, device="cuda")
+    toks, ex = _pick(d, 2, 2, seed=6)
+    _check(M, d, "dsv4-mxfp8-T2048", tokens=toks, experts=ex)

@@ -147,3 +147,18 @@ def test_backward(M, T, H, I, E, k):
                                      gu_saved=gu)
         return (gu,) + tuple(res)
     _check(M, run, f"backward T={T} E={E} k={k}")
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (300, 256, 512, 6, 3),       # small groups, k > 1
+    (1100, 512, 256, 4, 1),      # large groups, K-split tails
+])
+def test_backward_mxfp8(M, T, H, I, E, k):
+    d = W.make(_cfg(T, H, I, E, k, dtype="mxfp8"), seed=10, device="cuda")
+    dout = W.make_output_grad(d["cfg"], seed=2, device="cuda")
+
+    def run():
+        idx, w = M.moe_route_topk(d["logits"], k)
+        return M.moe_backward_batched_mxfp8(d["x"], d["w_gate_up"], d["w_gate_up_scales"],
+                                            d["w_down"], d["w_down_scales"], idx, w, dout, k)
+    _check(M, run, f"backward MXFP8 T={T} E={E} k={k}")
