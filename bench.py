@@ -17,11 +17,14 @@ DeepSeek-V4-Pro-shaped MXFP8 layer, both one-GPU expert-parallel shares
 Qwen3.5-shaped Zipf-skewed decode at T = 64.  Decode steps cycle through
 independent weight sets (like the layers of a model), so each step streams
 weights the 256 MB last-level cache does not hold, and every step routes a
-fresh batch of tokens.
+fresh batch of tokens.  Lines named "<workload>:backward" time the
+layer's backward pass on that shape (BF16 reading the pre-activations the
+training forward kept; MXFP8 recomputing them), segment by segment.
 
-With --pass backward (batched BF16 workloads) a step is routing plus the
-layer's backward pass instead (dx, both weight gradients, the routing-weight
-and logit gradients for a seeded output gradient).
+With --pass backward (batched workloads, BF16 or MXFP8) a step is routing plus
+the layer's backward pass instead (dx, both weight gradients, the routing-weight
+and logit gradients for a seeded output gradient); --pass train adds the
+forward before it.
 
 Prints ONE JSON line.  Besides the throughput it carries
   roofline:     the dominant kernel's algorithmic HBM bytes (or MFMA flops)
@@ -335,6 +338,52 @@ def backward_algorithmic(cfg, U):
     }
 
 
+MX_BWD_KERNELS = ("bwd_requant", "bwd_gate_up", "bwd_down", "bwd_input", "bwd_wgate_up")
+
+
+def mx_backward_algorithmic(cfg, U):
+    """The MXFP8 backward's timed segments: bytes they must at least move and their
+    MFMA flops.  bwd_requant encodes x and dout along H and the touched experts'
+    weights along their output axes; bwd_down is the dh product with its SwiGLU
+    finish; bwd_wgate_up covers the pair-axis encodings and both weight gradients."""
+    T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
+    P = T * k
+    q = 1.0 + 1.0 / 32                                   # an MX code and its share of a scale
+    w_mx = U * 3 * I * H * q                             # both weights, MX
+    return {
+        "bwd_requant": (2 * T * H * 2 + 2 * T * H * q + 2 * w_mx, 0.0),
+        "bwd_gate_up": (U * 2 * I * H * q + T * H * q + P * 2 * I * 4, 2.0 * P * 2 * I * H),
+        "bwd_down": (U * H * I * q + T * H * q + P * 2 * I * 4 + P * I * 4 + P * 2 * I * (4 + q),
+                     2.0 * P * H * I),
+        "bwd_input": (U * 2 * I * H * q + P * 2 * I * q
+                      + ((P * H * 4 * 2 + T * H * 2) if k > 1 else T * H * 2), 2.0 * P * 2 * I * H),
+        "bwd_wgate_up": (2 * T * H * 2 + P * 3 * I * 4 + U * 3 * I * H * 2,
+                         2.0 * P * H * I + 2.0 * P * 2 * I * H),
+    }
+
+
+def backward_roofline(cfg, r):
+    """Roofline of the backward's longest timed segment: MFMA-bound where each
+    expert's weights meet >= 256 routed rows, HBM-bound otherwise."""
+    name, k = max(r["per_kernel"].items(), key=lambda kv: kv[1]["avg_us"])
+    traffic, tprof = traffic_for(name, cfg.name)
+    peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    if cfg.T * cfg.k / cfg.E >= 256 and k["flops_per_launch"] > 0:   # MFMA-bound reuse
+        roof = {"bound": "mfma", "kernel": name, "achieved": round(k["tflops"], 1),
+                "peak": peak, "unit": "TFLOP/s",
+                "frac": round(k["tflops"] / peak, 4),
+                "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": tprof,
+                "avg_launch_us": round(k["avg_us"], 2),
+                "algorithmic_flops_per_launch": int(k["flops_per_launch"])}
+    else:
+        roof = {"bound": "hbm", "kernel": name, "achieved": round(k["gbs"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k["gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": tprof,
+                "avg_launch_us": round(k["avg_us"], 2),
+                "algorithmic_bytes_per_launch": int(k["bytes_per_launch"])}
+    return roof
+
+
 def run_backward(M, W, torch, cfg, steps, warmup, seed, n_batches=2, recompute=False,
                  train=False):
     """One step = routing + the backward pass of one batch (train: routing, the
@@ -351,6 +400,9 @@ def run_backward(M, W, torch, cfg, steps, warmup, seed, n_batches=2, recompute=F
              for b in range(n_batches)]
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     stream = torch.cuda.current_stream()
+    mx = cfg.dtype == "mxfp8"
+    if mx:
+        return run_backward_mx(M, torch, cfg, steps, warmup, wts, acts, douts, train)
     ws = M.workspace(M.moe_backward_workspace_bytes(T, H, I, E, k), dev)
     idx = torch.empty(n_batches, T, k, dtype=torch.int32, device=dev)
     tw = torch.empty(n_batches, T, k, dtype=torch.float32, device=dev)
@@ -406,6 +458,90 @@ def run_backward(M, W, torch, cfg, steps, warmup, seed, n_batches=2, recompute=F
         if train:
             f = batched_algorithmic(cfg, u)
             d["gemm_gate_up"] = (f["gate_up"] + T * k * 2 * I * 4, f["flops_gate_up"])
+            d["gemm_down"] = (f["down"], f["flops_down"])
+        return d
+    per = {}
+    for q, name in enumerate(kernels):
+        ss = [s for s in range(steps) if s % len(kernels) == q]
+        if not ss:
+            continue
+        dur = sum(evs[s][0].elapsed_ms(evs[s][1]) for s in ss) * 1e-3
+        nbytes = sum(alg(U[s])[name][0] for s in ss)
+        flops = sum(alg(U[s])[name][1] for s in ss)
+        per[name] = {"avg_us": 1e6 * dur / len(ss), "gbs": nbytes / dur / 1e9,
+                     "tflops": flops / dur / 1e12, "bytes_per_launch": nbytes / len(ss),
+                     "flops_per_launch": flops / len(ss)}
+    elapsed = t1 - t0
+    tot_bytes = sum(sum(v[0] for v in alg(u).values()) for u in U)
+    return {"elapsed_s": elapsed, "ms_per_step": 1e3 * elapsed / steps,
+            "tokens_per_s": T * steps / elapsed, "per_kernel": per,
+            "layer_gbs": tot_bytes / elapsed / 1e9, "avg_touched_experts": sum(U) / steps}
+
+
+def run_backward_mx(M, torch, cfg, steps, warmup, wts, acts, douts, train):
+    """The MXFP8 backward (moe_backward_batched_mxfp8, which always recomputes the
+    pre-activations from the E4M3 weights); train: routing, the MXFP8 forward
+    (x quantized, gate_up, down) and the backward.  Segments are timed in turn."""
+    from mixture_experts_ffn_07_amd.hip_events import HipEvent
+    dev = "cuda"
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    n_batches = len(acts)
+    stream = torch.cuda.current_stream()
+    ws = M.workspace(M.moe_backward_mxfp8_workspace_bytes(T, H, I, E, k), dev)
+    idx = torch.empty(n_batches, T, k, dtype=torch.int32, device=dev)
+    tw = torch.empty(n_batches, T, k, dtype=torch.float32, device=dev)
+    dx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    dwgu = torch.empty(E, 2 * I, H, dtype=torch.bfloat16, device=dev)
+    dwd = torch.empty(E, H, I, dtype=torch.bfloat16, device=dev)
+    dtw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    dl = torch.empty(T, E, dtype=torch.float32, device=dev)
+    if train:
+        fws = M.workspace(M.moe_workspace_bytes(T, H, I, E, k, M.MOE_MXFP8), dev)
+        h = torch.empty(T * k, I, dtype=torch.uint8, device=dev)
+        hs = torch.empty(T * k, I // 32, dtype=torch.uint8, device=dev)
+        xc = torch.empty(T, H, dtype=torch.uint8, device=dev)
+        xs = torch.empty(T, H // 32, dtype=torch.uint8, device=dev)
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        b = i % n_batches
+        a = acts[b]
+        M.moe_route_topk(a["logits"], k, topk_idx=idx[b], topk_w=tw[b], stream=stream)
+        if train:
+            M.moe_quantize_mxfp8(a["x"], codes=xc, scales=xs, stream=stream)
+            M.moe_gate_up_3d_batched(xc, wts["w_gate_up"], idx[b], k, M.MOE_MXFP8, x_scales=xs,
+                                     w_gate_up_scales=wts["w_gate_up_scales"], h=h, h_scales=hs,
+                                     ws=fws, stream=stream)
+            M.moe_down_3d_batched(h, wts["w_down"], idx[b], tw[b], fws, k, M.MOE_MXFP8,
+                                  h_scales=hs, w_down_scales=wts["w_down_scales"], out=out,
+                                  stream=stream)
+        M.moe_backward_batched_mxfp8(a["x"], wts["w_gate_up"], wts["w_gate_up_scales"],
+                                     wts["w_down"], wts["w_down_scales"], idx[b], tw[b], douts[b],
+                                     k, dx=dx, dw_gate_up=dwgu, dw_down=dwd, d_topk_w=dtw,
+                                     dlogits=dl, ws=ws, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(HipEvent(), HipEvent()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    kernels = list(MX_BWD_KERNELS)
+    if train:
+        kernels = ["gemm_gate_up", "gemm_down"] + kernels
+    t0 = time.perf_counter()
+    for s in range(steps):
+        M.moe_profile_kernel(kernels[s % len(kernels)], evs[s][0].handle, evs[s][1].handle)
+        step(warmup + s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    M.moe_profile_kernel("none", None, None)
+    U = [int(torch.unique(idx[(warmup + s) % n_batches]).numel()) for s in range(steps)]
+
+    def alg(u):
+        d = dict(mx_backward_algorithmic(cfg, u))
+        if train:
+            f = batched_algorithmic(cfg, u)
+            d["gemm_gate_up"] = (f["gate_up"], f["flops_gate_up"])
             d["gemm_down"] = (f["down"], f["flops_down"])
         return d
     per = {}
@@ -532,35 +668,24 @@ def main():
         M.moe_set_debug_options(M.MOE_DEBUG_DECODE_FUSED, 0)
         DECODE_FUSED[0] = True
     if args.pass_ in ("backward", "train"):
-        if cfg.path != "batched" or cfg.dtype != "bf16":
-            print(f"--pass {args.pass_} needs a batched BF16 workload, not {cfg.name}",
+        if cfg.path != "batched":
+            print(f"--pass {args.pass_} needs a batched workload, not {cfg.name}",
                   file=sys.stderr)
             sys.exit(2)
-        recompute = args.recompute
+        recompute = args.recompute or cfg.dtype == "mxfp8"
         r = run_backward(M, W, torch, cfg, args.steps, args.warmup, args.seed,
                          recompute=recompute, train=args.pass_ == "train")
-        name, k = max(r["per_kernel"].items(), key=lambda kv: kv[1]["avg_us"])
-        traffic, tprof = traffic_for(name, cfg.name)
-        if cfg.T * cfg.k / cfg.E >= 256:    # weight reuse high enough to be MFMA-bound
-            roof = {"bound": "mfma", "kernel": name, "achieved": round(k["tflops"], 1),
-                    "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                    "frac": round(k["tflops"] / MFMA_PEAK_TFLOPS["bf16"], 4),
-                    "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": tprof,
-                    "avg_launch_us": round(k["avg_us"], 2),
-                    "algorithmic_flops_per_launch": int(k["flops_per_launch"])}
-        else:
-            roof = {"bound": "hbm", "kernel": name, "achieved": round(k["gbs"], 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k["gbs"] / HBM_PEAK_GBS, 4),
-                    "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": tprof,
-                    "avg_launch_us": round(k["avg_us"], 2),
-                    "algorithmic_bytes_per_launch": int(k["bytes_per_launch"])}
+        roof = backward_roofline(cfg, r)
         line = {
             "metric": ("MoE layer backward tokens/s" if args.pass_ == "backward"
                        else "MoE layer forward+backward tokens/s"),
             "value": round(r["tokens_per_s"], 1),
             "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(r["ms_per_step"], 5), "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "scaling": "weak", "vs_baseline": None,
+            "dtype": ("bf16" if cfg.dtype == "bf16"
+                      else "mxfp8 (e4m3 + e8m0) operands, fp32 accumulate, bf16 gradients"),
+            "data": "synthetic",
             "config": {"workload": f"{cfg.name} {args.pass_}", "T": cfg.T, "H": cfg.H,
                        "E": cfg.E, "k": cfg.k, "I": cfg.I,
                        "preactivations": "recomputed" if recompute else "kept by the forward",
@@ -655,7 +780,9 @@ def forward_roofline(cfg, r):
 
 # the pages' other shapes, reported beside the headline in the same JSON line
 DEFAULT_LINES = ("dsv4-mxfp8-T2048,kimi-bf16-ep64share,dsv4-mxfp8-ep64share,"
-                 "qwen3-decode-T1,qwen3-decode-T8,qwen3-decode-T32,q35-zipf-T64")
+                 "qwen3-decode-T1,qwen3-decode-T8,qwen3-decode-T32,q35-zipf-T64,"
+                 "kimi-bf16-T2048:backward,kimi-bf16-ep64share:backward,"
+                 "dsv4-mxfp8-T2048:backward,dsv4-mxfp8-ep64share:backward")
 
 
 def run_lines(M, W, torch, names, args):
@@ -666,8 +793,30 @@ def run_lines(M, W, torch, names, args):
     out = []
     qwen_sets = None
     for name in names:
+        name, _, pass_ = name.partition(":")
         cfg = W.get(name)
         t0 = time.perf_counter()
+        if pass_ == "backward":
+            r = run_backward(M, W, torch, cfg, args.steps, args.warmup, args.seed,
+                             recompute=cfg.dtype == "mxfp8")
+            roof = backward_roofline(cfg, r)
+            out.append({"workload": name, "pass": "backward", "T": cfg.T, "H": cfg.H, "E": cfg.E,
+                        "k": cfg.k, "I": cfg.I, "dtype": cfg.dtype, "steps": args.steps,
+                        "preactivations": ("recomputed" if cfg.dtype == "mxfp8"
+                                           else "kept by the forward"),
+                        "ms_per_step": round(r["ms_per_step"], 5),
+                        "tokens_per_s": round(r["tokens_per_s"], 1),
+                        "roofline": {k_: roof[k_] for k_ in ("bound", "kernel", "achieved", "peak",
+                                                             "unit", "frac", "avg_launch_us",
+                                                             "traffic", "traffic_source")},
+                        "segments_us": {n: round(v["avg_us"], 1)
+                                        for n, v in r["per_kernel"].items()}})
+            del r
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            log(f"{name} backward: {out[-1]['ms_per_step']:.4f} ms/step, frac {roof['frac']} "
+                f"({time.perf_counter() - t0:.1f} s)")
+            continue
         if cfg.path == "decode":
             steps = max(args.steps, 100)
             if name.startswith("qwen3-decode"):

@@ -346,7 +346,9 @@ typedef enum {
   MOE_KERNEL_BWD_WDOWN = 12,     /* backward: dw_down                            */
   MOE_KERNEL_BWD_WGATE_UP = 13,  /* backward: dw_gate_up                         */
   MOE_KERNEL_DECODE_FUSED = 14,  /* single-launch decode (T <= 16): the whole layer */
-  MOE_KERNEL_COUNT = 15
+  MOE_KERNEL_BWD_REQUANT = 15,   /* MXFP8 backward: x, dout and both weights encoded
+                                    along the backward's reduction axes           */
+  MOE_KERNEL_COUNT = 16
 } moe_kernel_id;
 
 int moe_profile_kernel(int kernel, void* start_event, void* stop_event);

@@ -23,7 +23,7 @@ MOE_BF16, MOE_MXFP8 = 0, 1
 KERNELS = {"none": 0, "route": 1, "decode_gate_up": 2, "decode_down": 3, "group": 4,
            "quant": 5, "gemm_gate_up": 6, "gemm_down": 7, "combine": 8, "bwd_gate_up": 9,
            "bwd_down": 10, "bwd_input": 11, "bwd_wdown": 12, "bwd_wgate_up": 13,
-           "decode_fused": 14}
+           "decode_fused": 14, "bwd_requant": 15}
 MOE_DEBUG_PERMUTE_ORDER, MOE_DEBUG_DECODE_FUSED = 1, 2
 
 _P = ctypes.c_void_p

@@ -861,14 +861,17 @@ __device__ __forceinline__ uint32_t mx_quad_encode(const float (&v)[8], uint32_t
 
 // dst[b] = the MX encoding along R of src[b]^T: src codes [B][R][C] with scales
 // [B][R][C/32] (blocks along C) are decoded exactly and re-encoded as dst codes
-// [B][C][R] with scales [B][C][R/32] (blocks along R).  64 x 64 tiles.
+// [B][C][R] with scales [B][C][R/32] (blocks along R).  64 x 64 tiles.  With
+// counts, matrices b with counts[b] == 0 are skipped (their copy is left as is).
 __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ src,
                                                     const uint8_t* __restrict__ src_s, int R, int C,
                                                     uint8_t* __restrict__ dst,
-                                                    uint8_t* __restrict__ dst_s, uint32_t okey) {
+                                                    uint8_t* __restrict__ dst_s,
+                                                    const int* __restrict__ counts, uint32_t okey) {
   __shared__ float tl[64][64 + 1];                  // [c][r]
   const int c0 = permute_item(blockIdx.x, gridDim.x, okey) * 64, r0 = blockIdx.y * 64;
   const size_t b = blockIdx.z;
+  if (counts && counts[b] == 0) return;             // no pair reads this expert's copy
   const int tid = threadIdx.x;
   {
     const int r = tid >> 2, q = tid & 3;            // row r, 16 codes at columns 16q
@@ -1098,13 +1101,16 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
   hipError_t err = launch_group_experts(idx, P, E, kLargeBM, counts, offsets, tiles, n_tiles, perm,
                                         row_of, s);
   // x and dout along H; the weights re-encoded along their output axes
-  if (err == hipSuccess) err = launch_quant_mx(x, T, H, P8(L.xq), P8(L.xs), s);
+  if (err != hipSuccess) return err;
+  prof_begin(kBwdRequant, s);
+  err = launch_quant_mx(x, T, H, P8(L.xq), P8(L.xs), s);
   if (err == hipSuccess) err = launch_quant_mx(dout, T, H, P8(L.dq), P8(L.ds), s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(mx_requant_t, dim3(I / 64, H / 64, E), dim3(256), 0, s, wd, wds, H, I, P8(L.wdT),
-                     P8(L.wdTs), order_key());
+                     P8(L.wdTs), counts, order_key());
   hipLaunchKernelGGL(mx_requant_t, dim3(H / 64, 2 * I / 64, E), dim3(256), 0, s, wgu, wgus, 2 * I, H,
-                     P8(L.wguT), P8(L.wguTs), order_key());
+                     P8(L.wguT), P8(L.wguTs), counts, order_key());
+  prof_end(kBwdRequant, s);
   // the forward's pre-activations, then dh and its finish
   prof_begin(kBwdGateUp, s);
   err = launch_gate_up_raw_large_mx(P8(L.xq), P8(L.xs), wgu, wgus, perm, tiles, n_tiles, counts,
@@ -1127,7 +1133,8 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
   if (err != hipSuccess) return err;
   if (k > 1) hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, PF(L.dxs), row_of, T, H, k, dx, order_key());
   prof_end(kBwdInput, s);
-  // weight gradients over pair-axis operands
+  // weight gradients over pair-axis operands (the segment timed as dw_gate_up
+  // covers the pair-axis encodings and both weight gradients' single launch)
   prof_begin(kBwdWGateUp, s);
   err = launch_koff_mx(counts, E, koff, s);
   if (err != hipSuccess) return err;

@@ -41,7 +41,8 @@ inline void prof_end(int id, hipStream_t s) {
 enum KernelId { kRoute = 1, kDecGateUp = 2, kDecDown = 3, kGroup = 4, kQuant = 5,
                 kGemmGateUp = 6, kGemmDown = 7, kCombine = 8, kBwdGateUp = 9, kBwdDown = 10,
                 kBwdInput = 11, kBwdWDown = 12, kBwdWGateUp = 13, kDecFused = 14,
-                kKernelCount = 15 };
+                kBwdRequant = 15,
+                kKernelCount = 16 };
 
 // Library-owned device scratch (scratch.hip): kStaticScratchBytes per GPU for
 // the entry points that allocate nothing.  static_scratch(dev) gives its device

@@ -165,6 +165,38 @@ def test_backward_validation(m):
     assert need >= 64 * 2 * 2 * 256 * (4 + 2)
 
 
+def test_backward_mxfp8_validation(m):
+    b = m.lib.moe_backward_batched_mxfp8
+    need = m.lib.moe_backward_mxfp8_workspace_bytes(64, 256, 256, 8, 2)
+    assert need > 0
+    assert m.lib.moe_backward_mxfp8_workspace_bytes(0, 256, 256, 8, 2) == 0
+
+    def call(x=FAKE, wgus=FAKE, wds=FAKE, dout=FAKE, dx=FAKE, dl=FAKE, ws=FAKE, wsb=need, T=64,
+             H=256, I=256, E=8, k=2):
+        return b(x, FAKE, wgus, FAKE, wds, FAKE, FAKE, dout, T, H, I, E, k, dx, FAKE, FAKE, FAKE,
+                 dl, ws, wsb, None)
+    assert call(x=None) == m.MOE_ERR_NULL
+    assert call(wgus=None) == m.MOE_ERR_NULL
+    assert call(wds=None) == m.MOE_ERR_NULL
+    assert call(dout=None) == m.MOE_ERR_NULL
+    assert call(dl=None) == m.MOE_ERR_NULL
+    assert call(H=384) == m.MOE_ERR_SHAPE
+    assert call(I=128) == m.MOE_ERR_SHAPE
+    assert call(T=0) == m.MOE_ERR_SHAPE
+    assert call(k=9) == m.MOE_ERR_SHAPE
+    assert call(ws=None) == m.MOE_ERR_WORKSPACE
+    assert call(wsb=need - 1) == m.MOE_ERR_WORKSPACE
+    assert call(dx=FAKE + 2) == m.MOE_ERR_ALIGN
+    assert call(wgus=FAKE + 8) == m.MOE_ERR_ALIGN
+    # pair-axis operands: max(H, 2I) * (T*k + 128*E) must stay below 2^31
+    big = 1 << 60
+    assert call(T=149500, H=7168, I=256, k=2, wsb=big) == m.MOE_ERR_SHAPE   # T*k*H < 2^31
+    assert b"max(H, 2I)" in m.lib.moe_last_error()
+    # the workspace holds both weights re-encoded along their output axis
+    wbytes = 8 * (2 * 256 * 256 + 256 * 256)
+    assert need >= wbytes + wbytes // 32
+
+
 def test_train_forward_validation(m):
     g = m.lib.moe_gate_up_3d_batched_train
     need = m.lib.moe_workspace_bytes(64, 256, 256, 8, 2, 0)
