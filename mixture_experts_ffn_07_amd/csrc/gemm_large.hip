@@ -299,10 +299,11 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     else *reinterpret_cast<i32x4*>(&st_[kLTile + lw + ((Q) - 8) * 8 * kLBK]) = stg[Q];  \
   } while (0)
 #define RDF(PTR) as_bf16x8(*reinterpret_cast<const i32x4*>(PTR))
-  // One MFMA K step on fragments (A, B): 8 groups of 2 MFMAs; group g then
-  // reads fragment g of the next K step (stage RKT, step RKS) and, for g < NQ,
-  // writes staged chunk Q0+g of stage WKT to LDS and reloads that chunk from
-  // stage WKT+1.  sched_barrier keeps this order.
+  // One MFMA K step on fragments (A, B): 8 groups of 2 MFMAs; groups 0..3 then
+  // read fragments A g and B g of the next K step (stage RKT, step RKS: all of
+  // them in the first half, so they have landed when the next step starts)
+  // and, for g < NQ, write staged chunk Q0+g of stage WKT to LDS and reload that
+  // chunk from stage WKT+1.  sched_barrier keeps this order.
 #define PHASE(A, B, NA, NB, RKT, RKS, WKT, Q0, NQ) do {                                 \
     const uint16_t* at_ = lds + ((RKT) & 1) * 2 * kLTile;                               \
     const uint16_t* bt_ = at_ + kLTile;                                                 \
@@ -312,8 +313,10 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
       acc[i_][j0_] = mfma32x32x16(A[i_], B[j0_], acc[i_][j0_]);                         \
       acc[i_][j0_ + 1] = mfma32x32x16(A[i_], B[j0_ + 1], acc[i_][j0_ + 1]);             \
       __builtin_amdgcn_sched_barrier(0);                                                \
-      if (g < 4) NA[g] = RDF(&at_[fa[g] + so_]);                                        \
-      else NB[g - 4] = RDF(&bt_[fb + 32 * (g - 4) * kLBK + so_]);                       \
+      if (g < 4) {                                                                      \
+        NA[g] = RDF(&at_[fa[g] + so_]);                                                 \
+        NB[g] = RDF(&bt_[fb + 32 * g * kLBK + so_]);                                    \
+      }                                                                                 \
       if (g < (NQ)) { LWRITE((Q0) + g, WKT); GLOAD((Q0) + g, (WKT) + 1); }              \
       __builtin_amdgcn_sched_barrier(0);                                                \
     }                                                                                   \
@@ -716,14 +719,15 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
   for (int p = 0; p < 16; ++p) RDP(f0, p, kb, 0);
   RDS(sc, kb);
   for (int kt = kb; kt < ke; ++kt) {
-    // K step 0: MFMAs on f0; read K step 1 into f1; chunks 8..15 and scales of
-    // stage kt+1 to LDS, each chunk reloaded from stage kt+2
+    // K step 0: MFMAs on f0; read K step 1 into f1 (two pieces per MFMA over the
+    // first half); chunks 8..15 and scales of stage kt+1 to LDS, each chunk
+    // reloaded from stage kt+2
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       const int i = g >> 2, j = g & 3;
       acc[i][j] = mfma_mx32<0>(f0[i], f0[4 + j], static_cast<int>(sc[i]), static_cast<int>(sc[4 + j]), acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
-      RDP(f1, g, kt, 1);
+      if (g < 8) { RDP(f1, 2 * g, kt, 1); RDP(f1, 2 * g + 1, kt, 1); }
       if (g & 1) { LWRITE(8 + (g >> 1), kt + 1); GLOAD(8 + (g >> 1), kt + 2); }
       if (g == 14) { SWRITE(kt + 1); SLOAD(kt + 2); }
       __builtin_amdgcn_sched_barrier(0);
@@ -737,7 +741,7 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
       const int i = g >> 2, j = g & 3;
       acc[i][j] = mfma_mx32<2>(f1[i], f1[4 + j], static_cast<int>(sc[i]), static_cast<int>(sc[4 + j]), acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
-      RDP(f0, g, kt + 1, 0);
+      if (g < 8) { RDP(f0, 2 * g, kt + 1, 0); RDP(f0, 2 * g + 1, kt + 1, 0); }
       if (g == 0) RDS(scn, kt + 1);
       if (g & 1) { LWRITE(g >> 1, kt + 2); GLOAD(g >> 1, kt + 3); }
       __builtin_amdgcn_sched_barrier(0);
