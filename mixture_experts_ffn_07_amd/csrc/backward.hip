@@ -861,51 +861,78 @@ __device__ __forceinline__ uint32_t mx_quad_encode(const float (&v)[8], uint32_t
 
 // dst[b] = the MX encoding along R of src[b]^T: src codes [B][R][C] with scales
 // [B][R][C/32] (blocks along C) are decoded exactly and re-encoded as dst codes
-// [B][C][R] with scales [B][C][R/32] (blocks along R).  64 x 64 tiles.  With
-// counts, matrices b with counts[b] == 0 are skipped (their copy is left as is).
+// [B][C][R] with scales [B][C][R/32] (blocks along R).  A workgroup takes 128
+// columns x 256 rows (C a multiple of 128, R of 256) as four 64-row tiles
+// through LDS: every load covers whole 128-byte lines of source rows (the four
+// tiles' loads in flight together), every store 32 bytes of an output row, and
+// each output row's 8 scale bytes leave in one 8-byte store.  With counts,
+// matrices b with counts[b] == 0 are skipped (their copy is left as is).
 __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ src,
                                                     const uint8_t* __restrict__ src_s, int R, int C,
                                                     uint8_t* __restrict__ dst,
                                                     uint8_t* __restrict__ dst_s,
                                                     const int* __restrict__ counts, uint32_t okey) {
-  __shared__ float tl[64][64 + 1];                  // [c][r]
-  const int c0 = permute_item(blockIdx.x, gridDim.x, okey) * 64, r0 = blockIdx.y * 64;
+  constexpr int U = 4;                              // 64-row tiles per workgroup
+  __shared__ float tl[128][64 + 1];                 // [c][r]
+  __shared__ __align__(8) uint8_t ssc[128][2 * U];  // [c][block of 32 rows]
+  const int c0 = permute_item(blockIdx.x, gridDim.x, okey) * 128, r0 = blockIdx.y * 64 * U;
   const size_t b = blockIdx.z;
   if (counts && counts[b] == 0) return;             // no pair reads this expert's copy
   const int tid = threadIdx.x;
-  {
-    const int r = tid >> 2, q = tid & 3;            // row r, 16 codes at columns 16q
-    const size_t row = b * R + r0 + r;
-    const i32x4 v = ld16(src + row * C + c0 + 16 * q);
-    const int sc = src_s[row * (C / 32) + (c0 + 16 * q) / 32];
+  const int q = tid & 7, rl = tid >> 3;             // load: rows rl and rl + 32 of a tile, 16 codes at 16q
+  i32x4 v[U][2];
+  int sc[U][2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t code = (static_cast<uint32_t>(v[i >> 2]) >> (8 * (i & 3))) & 0xFFu;
-      tl[16 * q + i][r] = ldexpf(e4m3_value(code), sc - 127);
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const size_t row = b * R + r0 + 64 * u + 32 * h + rl;
+      v[u][h] = ld16(src + row * C + c0 + 16 * q);
+      sc[u][h] = src_s[row * (C / 32) + (c0 + 16 * q) / 32];
     }
+  const int c = tid >> 1, hb = tid & 1;             // encode: out row c, block hb of the tile's 64 rows
+  const size_t orow = b * C + c0 + c;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u) __syncthreads();                         // the previous tile is read out
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // decode: the hardware E4M3 pair conversion (exact), times 2^(scale - 127)
+      const float scl = ldexpf(1.0f, sc[u][h] - 127);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(v[u][h][d], false);   // bytes 0, 1
+        const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8(v[u][h][d], true);    // bytes 2, 3
+        tl[16 * q + 4 * d][32 * h + rl] = f0.x * scl;
+        tl[16 * q + 4 * d + 1][32 * h + rl] = f0.y * scl;
+        tl[16 * q + 4 * d + 2][32 * h + rl] = f1.x * scl;
+        tl[16 * q + 4 * d + 3][32 * h + rl] = f1.y * scl;
+      }
+    }
+    __syncthreads();
+    float val[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) val[i] = tl[c][32 * hb + i];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(val[i]));
+    const int sx = mx_scale_exp(amax);
+    const float inv = exp2_neg(sx);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float* w = val + 16 * g;
+      st16(dst + orow * R + r0 + 64 * u + 32 * hb + 16 * g,
+           i32x4{static_cast<int>(f32x4_to_e4m3x4(w[0] * inv, w[1] * inv, w[2] * inv, w[3] * inv)),
+                 static_cast<int>(f32x4_to_e4m3x4(w[4] * inv, w[5] * inv, w[6] * inv, w[7] * inv)),
+                 static_cast<int>(f32x4_to_e4m3x4(w[8] * inv, w[9] * inv, w[10] * inv, w[11] * inv)),
+                 static_cast<int>(f32x4_to_e4m3x4(w[12] * inv, w[13] * inv, w[14] * inv, w[15] * inv))});
+    }
+    ssc[c][2 * u + hb] = static_cast<uint8_t>(sx + 127);
   }
   __syncthreads();
-  const int c = tid >> 2, q = tid & 3;              // out row c, 16 values at r = 16q
-  float v0[8], v1[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v0[i] = tl[c][16 * q + i];
-    v1[i] = tl[c][16 * q + 8 + i];
-  }
-  // a block of 32 along R = lanes 2 apart in q: pair (q, q ^ 1) holds 32 values
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fmaxf(fabsf(v0[i]), fabsf(v1[i])));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-  const int sx = mx_scale_exp(amax);
-  const float inv = exp2_neg(sx);
-  const size_t orow = b * C + c0 + c;
-  st16(dst + orow * R + r0 + 16 * q,
-       i32x4{static_cast<int>(f32x4_to_e4m3x4(v0[0] * inv, v0[1] * inv, v0[2] * inv, v0[3] * inv)),
-             static_cast<int>(f32x4_to_e4m3x4(v0[4] * inv, v0[5] * inv, v0[6] * inv, v0[7] * inv)),
-             static_cast<int>(f32x4_to_e4m3x4(v1[0] * inv, v1[1] * inv, v1[2] * inv, v1[3] * inv)),
-             static_cast<int>(f32x4_to_e4m3x4(v1[4] * inv, v1[5] * inv, v1[6] * inv, v1[7] * inv))});
-  if ((q & 1) == 0) dst_s[orow * (R / 32) + (r0 + 16 * q) / 32] = static_cast<uint8_t>(sx + 127);
+  if (tid < 128)
+    *reinterpret_cast<uint2*>(dst_s + (b * C + c0 + tid) * (R / 32) + r0 / 32) =
+        *reinterpret_cast<const uint2*>(&ssc[tid][0]);
 }
 
 // The MXFP8 backward's dh finish, per grouped row r (thread = 8 columns, 16
@@ -970,7 +997,9 @@ __global__ __launch_bounds__(256) void mx_dh_finish(const float* __restrict__ gu
 // along the routed pairs of expert e (blocks of 32 from koff[e], padding zero),
 // of element c of the expert's r-th routed row.  SRC 0: x[token] (BF16); 1:
 // w * dout[token] (BF16 dout, FP32 routing weight); 2: grouped FP32 rows
-// (src32, row stride ld).  Workgroup = 32 columns (one block) x 64 rows c.
+// (src32, row stride ld).  Workgroup = 128 pairs (four blocks, all of one
+// expert: koff is padded to 128) x 64 rows c, so each row c gets a whole
+// 128-byte line of codes and one 4-byte store of its four scales.
 template <int SRC>
 __global__ __launch_bounds__(256) void mx_pair_t(const uint16_t* __restrict__ src16,
                                                  const float* __restrict__ src32, int ld,
@@ -981,9 +1010,9 @@ __global__ __launch_bounds__(256) void mx_pair_t(const uint16_t* __restrict__ sr
                                                  const int* __restrict__ koff, int E,
                                                  uint8_t* __restrict__ dst,
                                                  uint8_t* __restrict__ dst_s, uint32_t okey) {
-  __shared__ float tl[64][32 + 1];                  // [c][pair]
+  __shared__ float tl[64][128 + 1];                 // [c][pair]
   const int KPT = koff[E];
-  const int g0 = permute_item(blockIdx.x, gridDim.x, okey) * 32, c0 = blockIdx.y * 64;
+  const int g0 = permute_item(blockIdx.x, gridDim.x, okey) * 128, c0 = blockIdx.y * 64;
   if (g0 >= KPT) return;
   int lo = 0, hi = E - 1;                           // last e with koff[e] <= g0
   while (lo < hi) {
@@ -994,26 +1023,33 @@ __global__ __launch_bounds__(256) void mx_pair_t(const uint16_t* __restrict__ sr
   const int cnt = counts[e], base = offsets[e], r0 = g0 - koff[e];
   const int tid = threadIdx.x;
   if (SRC < 2) {
-    const int p = tid >> 3, ch = tid & 7;           // pair p, 8 values at 8ch
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (r0 + p < cnt) {
-      const int pr = perm[base + r0 + p];
-      const i32x4 raw = ld16(src16 + static_cast<size_t>(pr / k) * ld + c0 + 8 * ch);
-      const float sc = SRC == 1 ? w[pr] : 1.0f;
+    i32x4 raw[4];
+    float sc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t u = static_cast<uint32_t>(raw[i]);
-        v[2 * i] = sc * bf16_to_f32(u & 0xFFFFu);
-        v[2 * i + 1] = sc * bf16_to_f32(u >> 16);
+    for (int u = 0; u < 4; ++u) {                   // pair p, 8 values at 8ch
+      const int idx = tid + 256 * u, p = idx >> 3, ch = idx & 7;
+      raw[u] = i32x4{0, 0, 0, 0};
+      sc[u] = 0.f;
+      if (r0 + p < cnt) {
+        const int pr = perm[base + r0 + p];
+        raw[u] = ld16(src16 + static_cast<size_t>(pr / k) * ld + c0 + 8 * ch);
+        sc[u] = SRC == 1 ? w[pr] : 1.0f;
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tl[8 * ch + i][p] = v[i];
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + 256 * u, p = idx >> 3, ch = idx & 7;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t v = static_cast<uint32_t>(raw[u][i]);
+        tl[8 * ch + 2 * i][p] = sc[u] * bf16_to_f32(v & 0xFFFFu);
+        tl[8 * ch + 2 * i + 1][p] = sc[u] * bf16_to_f32(v >> 16);
+      }
+    }
   } else {
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int idx = tid + 256 * h2;
-      const int p = idx >> 4, ch = idx & 15;        // pair p, 4 values at 4ch
+    for (int u = 0; u < 8; ++u) {                   // pair p, 4 values at 4ch
+      const int idx = tid + 256 * u, p = idx >> 4, ch = idx & 15;
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
       if (r0 + p < cnt)
         v = *reinterpret_cast<const f32x4*>(src32 + static_cast<size_t>(base + r0 + p) * ld + c0 + 4 * ch);
@@ -1022,15 +1058,19 @@ __global__ __launch_bounds__(256) void mx_pair_t(const uint16_t* __restrict__ sr
     }
   }
   __syncthreads();
-  const int c = tid >> 2, q = tid & 3;              // out row c, pairs 8q .. 8q + 7
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = tl[c][8 * q + i];
-  uint32_t clo, chi;
-  const uint32_t scode = mx_quad_encode(v, clo, chi);
+  const int c = tid >> 2, q = tid & 3;              // out row c; block b: pairs 32b + 8q .. + 7
   const size_t orow = static_cast<size_t>(c0 + c);
-  *reinterpret_cast<uint2*>(dst + orow * KPT + g0 + 8 * q) = make_uint2(clo, chi);
-  if (q == 0) dst_s[orow * (KPT / 32) + g0 / 32] = static_cast<uint8_t>(scode);
+  uint32_t scodes = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = tl[c][32 * b + 8 * q + i];
+    uint32_t clo, chi;
+    scodes |= mx_quad_encode(v, clo, chi) << (8 * b);
+    *reinterpret_cast<uint2*>(dst + orow * KPT + g0 + 32 * b + 8 * q) = make_uint2(clo, chi);
+  }
+  if (q == 0) *reinterpret_cast<uint32_t*>(dst_s + orow * (KPT / 32) + g0 / 32) = scodes;
 }
 
 inline size_t a256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -1106,9 +1146,9 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
   err = launch_quant_mx(x, T, H, P8(L.xq), P8(L.xs), s);
   if (err == hipSuccess) err = launch_quant_mx(dout, T, H, P8(L.dq), P8(L.ds), s);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(mx_requant_t, dim3(I / 64, H / 64, E), dim3(256), 0, s, wd, wds, H, I, P8(L.wdT),
+  hipLaunchKernelGGL(mx_requant_t, dim3(I / 128, H / 256, E), dim3(256), 0, s, wd, wds, H, I, P8(L.wdT),
                      P8(L.wdTs), counts, order_key());
-  hipLaunchKernelGGL(mx_requant_t, dim3(H / 64, 2 * I / 64, E), dim3(256), 0, s, wgu, wgus, 2 * I, H,
+  hipLaunchKernelGGL(mx_requant_t, dim3(H / 128, 2 * I / 256, E), dim3(256), 0, s, wgu, wgus, 2 * I, H,
                      P8(L.wguT), P8(L.wguTs), counts, order_key());
   prof_end(kBwdRequant, s);
   // the forward's pre-activations, then dh and its finish
@@ -1138,7 +1178,7 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
   prof_begin(kBwdWGateUp, s);
   err = launch_koff_mx(counts, E, koff, s);
   if (err != hipSuccess) return err;
-  const unsigned gb = static_cast<unsigned>(L.kpt_max / 32);
+  const unsigned gb = static_cast<unsigned>(L.kpt_max / 128);
   hipLaunchKernelGGL(mx_pair_t<1>, dim3(gb, H / 64), dim3(256), 0, s, dout, nullptr, H, perm, w, k,
                      counts, offsets, koff, E, P8(L.dyT), P8(L.dyTs), order_key());
   hipLaunchKernelGGL(mx_pair_t<2>, dim3(gb, I / 64), dim3(256), 0, s, nullptr, PF(L.a), I, perm, w, k,

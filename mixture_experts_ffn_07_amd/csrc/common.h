@@ -8,6 +8,7 @@ namespace moe {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef float f32x2 __attribute__((ext_vector_type(2)));   // hardware FP8 pair conversions
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;

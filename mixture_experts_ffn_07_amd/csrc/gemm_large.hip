@@ -110,6 +110,43 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 }  // namespace
 
+// Weight-gradient epilogue: the wave's 128 (B rows) x 128 (A columns) block of
+// dW, BF16, through LDS so that global stores are 16 bytes per lane along dW
+// rows (a wave stores 4 rows x 256 bytes at a time).  Lane (l32, hi) holds A
+// column 32i + 8q + 4hi + t and B row 32j + l32 of the block (register 4q + t of
+// acc[i][j]).  Two passes of 64 rows through the wave's own 17 KB of LDS; the
+// caller has made the LDS free (no wave still reads its K stages).
+constexpr int kWgStage = 272;                  // bytes per staged row: 256 + 16
+constexpr int kWgLds = 4 * 64 * kWgStage;      // 68 KB for the workgroup
+__device__ __forceinline__ void wgrad_store(const f32x16 (&acc)[4][4], uint8_t* lds,
+                                            uint16_t* __restrict__ dw, int cols, int row0,
+                                            int col0, int wv, int ln) {
+  uint8_t* st = lds + wv * 64 * kWgStage;
+  const int l32 = ln & 31, hi = ln >> 5;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& a = acc[i][2 * half + jj];
+          const uint32_t p0 = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
+          const uint32_t p1 = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
+          *reinterpret_cast<uint2*>(st + (32 * jj + l32) * kWgStage + (32 * i + 8 * q + 4 * hi) * 2) =
+              make_uint2(p0, p1);
+        }
+    // one wave's LDS operations complete in order: the reads see the writes above
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int r = 4 * u + (ln >> 4), c = ln & 15;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(st + r * kWgStage + c * 16);
+      *reinterpret_cast<i32x4*>(dw + static_cast<size_t>(row0 + 64 * half + r) * cols + col0 + c * 8) = v;
+    }
+  }
+}
+
 // Epilogue of a 256 x 256 tile (see gemm_large_bf16 for the register layout).
 template <int KIND>
 __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const int* __restrict__ perm,
@@ -371,24 +408,11 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
 #undef PHASE
 
   if (kWG) {
-    // dW[e][B row][A row], BF16: lane (l32, hi) holds A rows 32i + 8q + 4hi + t of
-    // the wave's 128 and B row 32j + l32 of its 128
+    // dW[e][B row][A row], BF16
     const int colsA = nA * 256;
-    uint16_t* base = out + static_cast<size_t>(e) * (nB * 256) * colsA;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint16_t* orow = base + static_cast<size_t>(bb * 256 + wm * 128 + 32 * j + l32) * colsA +
-                       nb * 256 + wn * 128 + 4 * hi;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t p[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) p[t] = f32_to_bf16_rne(acc[i][j][4 * q + t]);
-          *reinterpret_cast<uint2*>(orow + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
-        }
-    }
+    __syncthreads();                               // every wave is done with the K stages
+    wgrad_store(acc, reinterpret_cast<uint8_t*>(lds), out + static_cast<size_t>(e) * (nB * 256) * colsA,
+                colsA, bb * 256 + wm * 128, nb * 256 + wn * 128, wv, ln);
     return;
   }
   if (slot >= 0) {
@@ -517,6 +541,7 @@ namespace {
 constexpr int kMBK = 128;                                  // K per stage
 constexpr int kMTile = kLargeBM * kMBK;                    // bytes per operand stage
 constexpr size_t kMLds = 2 * 2 * kMTile + 2 * 2 * kLargeBM * 4;   // data + scales: 132 KB
+static_assert(kWgLds <= kMLds && kWgLds <= kLLds, "weight-gradient staging fits the K stages' LDS");
 
 template <int OPSEL>
 __device__ __forceinline__ f32x16 mfma_mx32(i32x8 a, i32x8 b, int sa, int sb, f32x16 c) {
@@ -758,24 +783,11 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
 #undef RDS
 
   if (kWG) {
-    // dW[e][B row][A row], BF16: lane (l32, hi) holds A rows 32i + 8q + 4hi + t of
-    // the wave's 128 and B row 32j + l32 of its 128
+    // dW[e][B row][A row], BF16
     const int colsA = nA * 256;
-    uint16_t* base = out + static_cast<size_t>(e) * (nB * 256) * colsA;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint16_t* orow = base + static_cast<size_t>(bb * 256 + wm * 128 + 32 * j + l32) * colsA +
-                       nb * 256 + wn * 128 + 4 * hi;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t p[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) p[t] = f32_to_bf16_rne(acc[i][j][4 * q + t]);
-          *reinterpret_cast<uint2*>(orow + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
-        }
-    }
+    __syncthreads();                               // every wave is done with the K stages
+    wgrad_store(acc, ldm, out + static_cast<size_t>(e) * (nB * 256) * colsA,
+                colsA, bb * 256 + wm * 128, nb * 256 + wn * 128, wv, ln);
     return;
   }
 
