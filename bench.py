@@ -17,7 +17,9 @@ DeepSeek-V4-Pro-shaped MXFP8 layer, both one-GPU expert-parallel shares
 Qwen3.5-shaped Zipf-skewed decode at T = 64.  Decode steps cycle through
 independent weight sets (like the layers of a model), so each step streams
 weights the 256 MB last-level cache does not hold, and every step routes a
-fresh batch of tokens.  Lines named "<workload>:backward" time the
+fresh batch of tokens; their throughput is that of the same steps replayed from a
+HIP graph (8 captured steps per replay, as a serving loop would issue them; the
+eager per-call figures are kept under "issue").  Lines named "<workload>:backward" time the
 layer's backward pass on that shape (BF16 reading the pre-activations the
 training forward kept; MXFP8 recomputing them), segment by segment.
 
@@ -171,7 +173,7 @@ def decode_weight_sets(W, cfg, layers, seed, dev="cuda"):
 
 
 def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="auto",
-               weights=None):
+               weights=None, use_graph=True):
     from mixture_experts_ffn_07_amd.hip_events import HipEvent
     dev = "cuda"
     n_batches = steps + warmup
@@ -209,6 +211,7 @@ def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="auto"
     durs = [a.elapsed_ms(b) for a, b in evs]
     U = [int(torch.unique(idx[warmup + s]).numel()) for s in range(steps)]
     bytes_ = [decode_algorithmic_bytes(cfg, u) for u in U]
+    graph = graph_decode(M, torch, cfg, weights, acts, steps, ws) if use_graph else None
     if hook_kernel == "decode_fused":                 # one launch: the whole layer
         kern_bytes = sum(sum(b.values()) for b in bytes_)
     else:
@@ -228,7 +231,63 @@ def run_decode(M, W, torch, cfg, steps, warmup, layers, seed, hook_kernel="auto"
         "avg_touched_experts": sum(U) / steps,
         "first_batch": acts[warmup], "first_weights": weights[warmup % layers],
     }
+    if graph is not None:
+        # the line's throughput: the same steps replayed from a HIP graph (one host
+        # call per captured cycle), the eager figures kept beside it
+        res["eager"] = {"ms_per_step": round(res["ms_per_step"], 5),
+                        "tokens_per_s": round(res["tokens_per_s"], 1),
+                        "layer_gbs": round(layer_bytes / elapsed / 1e9, 1)}
+        res["ms_per_step"] = graph["ms_per_step"]
+        res["tokens_per_s"] = graph["tokens_per_s"]
+        res["layer_gbs"] = graph["layer_bytes_per_step"] / (graph["ms_per_step"] * 1e-3) / 1e9
+        res["graph"] = {k_: graph[k_] for k_ in ("captured_steps", "replays", "steps")}
     return res
+
+
+def graph_decode(M, torch, cfg, weights, acts, steps, ws):
+    """Decode steps replayed from a HIP graph: G consecutive steps (each with its
+    own activation batch, weight sets cycling as in the eager loop) are captured
+    once on a side stream, then the graph is replayed until at least `steps`
+    steps have run.  A serving loop issues decode this way: the host's per-call
+    work (argument checks, launches) leaves the critical path."""
+    T, k = cfg.T, cfg.k
+    G = min(len(acts), max(len(weights), 8))
+    out = torch.empty(G, T, cfg.H, dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty(G, T, k, dtype=torch.int32, device="cuda")
+    wts = torch.empty(G, T, k, dtype=torch.float32, device="cuda")
+
+    def step(j, stream):
+        wl = weights[j % len(weights)]
+        a = acts[j]
+        M.moe_decode_forward(a["x"], a["logits"], wl["w_gate_up"], wl["w_down"], k, out=out[j],
+                             topk_idx=idx[j], topk_w=wts[j], ws=ws, stream=stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for j in range(G):
+            step(j, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream()
+        for j in range(G):
+            step(j, cs)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // G))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    U = [int(torch.unique(idx[j]).numel()) for j in range(G)]
+    lb = sum(sum(decode_algorithmic_bytes(cfg, u).values()) for u in U) / G
+    n = reps * G
+    return {"captured_steps": G, "replays": reps, "steps": n,
+            "ms_per_step": 1e3 * (t1 - t0) / n, "tokens_per_s": T * n / (t1 - t0),
+            "layer_bytes_per_step": lb}
 
 
 def batched_algorithmic(cfg, U):
@@ -718,6 +777,8 @@ def main():
         "roofline": roof,
         "layer": layer,
     }
+    if "graph" in r:
+        line["issue"] = {"mode": "hip graph replay", **r["graph"], "eager": r["eager"]}
     if cfg.path == "decode" and args.layers > 1:
         # the headline cycles weight sets, so each step streams weights no recent step
         # left in the 256 MB last-level cache; this reruns one weight set back to back
@@ -842,6 +903,8 @@ def run_lines(M, W, torch, names, args):
                                                          "unit", "frac", "avg_launch_us",
                                                          "traffic", "traffic_source")},
                     "layer": layer})
+        if "graph" in r:
+            out[-1]["issue"] = {"mode": "hip graph replay", **r["graph"], "eager": r["eager"]}
         del r
         torch.cuda.synchronize()
         torch.cuda.empty_cache()

@@ -361,7 +361,9 @@ int moe_profile_kernel(int kernel, void* start_event, void* stop_event);
  *                            workgroup -> item assignment); results must not change
  *   MOE_DEBUG_DECODE_FUSED   moe_decode_forward at T <= 16 runs as one launch
  *                            (routing, gate_up, a device-wide wait, down) instead
- *                            of two
+ *                            of two; not on a capturing stream (its wait keys on a
+ *                            per-launch value that a graph would replay): there the
+ *                            two launches run
  * flags = 0 restores the defaults.  Returns MOE_OK, or MOE_ERR_SHAPE for
  * unknown bits.
  */

@@ -1221,7 +1221,13 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
   // (the 5- and 7-step slices keep one group: two would not fit 128 registers)
   const int NR = H / (2 * kDownRows) >= num_cus && KD <= 4 ? 2 : 1;
   const size_t lds_dn = down_lds_bytes(T, KD, NR);
-  if (fuse_route && !wide && (KD == 3 || KD == 4) &&
+  // The single launch waits on flags compared with a per-launch epoch passed as a
+  // kernel argument; a captured graph would replay one epoch, and the flags of
+  // the previous replay would already match.  Under stream capture the two
+  // launches run instead.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &capture) != hipSuccess) capture = hipStreamCaptureStatusActive;
+  if (fuse_route && !wide && (KD == 3 || KD == 4) && capture == hipStreamCaptureStatusNone &&
       (debug_options().flags & kDebugDecodeFused)) {
     // single launch: routing, gate_up and down in one grid of resident workgroups
     uint64_t* flags = reinterpret_cast<uint64_t*>(base + L.flags);
