@@ -63,27 +63,36 @@ CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 # the sources change the figure no longer describes the kernel and is reported
 # as null until the counters are taken again.
 TRAFFIC = {
-    ("decode_gate_up", "qwen3-decode-T32"): (
-        711.0e6, ('decode.hip', 'common.h', 'internal.h'), "8db2fd3db7545b55",
-        "profiles/decode_gate_up_qwen3-decode-T32.md"),
     ("gemm_gate_up", "kimi-bf16-T2048"): (
-        22999.0e6, ('batched.hip', 'common.h', 'tiles.h'), "b363ba1a1057f3d8",
+        22993.8e6, ('batched.hip', 'common.h', 'tiles.h'), "1ba6d324e0fe981f",
         "profiles/gemm_gate_up_kimi-bf16-T2048.md"),
-    ("gemm_gate_up", "glm-bf16-T2048"): (
-        13213.0e6, ('batched.hip', 'common.h', 'tiles.h'), "b363ba1a1057f3d8",
-        "profiles/gemm_gate_up_glm-bf16-T2048.md"),
     ("gemm_gate_up", "dsv4-mxfp8-T2048"): (
-        18180.0e6, ('batched.hip', 'common.h', 'tiles.h'), "b363ba1a1057f3d8",
+        18177.5e6, ('batched.hip', 'common.h', 'tiles.h'), "1ba6d324e0fe981f",
         "profiles/gemm_gate_up_dsv4-mxfp8-T2048.md"),
-    ("gemm_gate_up", "qwen3-mxfp8-decode-T32"): (
-        377.89e6, ('batched.hip', 'common.h', 'tiles.h'), "b363ba1a1057f3d8",
-        "profiles/gemm_gate_up_qwen3-mxfp8-decode-T32.md"),
+    ("gemm_gate_up", "glm-bf16-T2048"): (
+        13213.6e6, ('batched.hip', 'common.h', 'tiles.h'), "1ba6d324e0fe981f",
+        "profiles/gemm_gate_up_glm-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
-        2002.6e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "980972c221bc04b2",
+        1996.4e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "a51b8ceece66bc59",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
+    ("gemm_gate_up", "dsv4-mxfp8-ep64share"): (
+        1739.4e6, ('gemm_large.hip', 'common.h', 'tiles.h'), "a51b8ceece66bc59",
+        "profiles/gemm_gate_up_dsv4-mxfp8-ep64share.md"),
+    ("decode_gate_up", "qwen3-decode-T32"): (
+        700.8e6, ('decode.hip', 'common.h', 'internal.h'), "5936b53c4e39f8a2",
+        "profiles/decode_gate_up_qwen3-decode-T32.md"),
+    ("gemm_gate_up", "qwen3-mxfp8-decode-T32"): (
+        378.9e6, ('batched.hip', 'common.h', 'tiles.h'), "1ba6d324e0fe981f",
+        "profiles/gemm_gate_up_qwen3-mxfp8-decode-T32.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
-        23713.0e6, ('backward.hip', 'common.h', 'tiles.h'), "e0d455ec1a50e34e",
+        23710.2e6, ('backward.hip', 'common.h', 'tiles.h'), "71e64c4d128f515c",
         "profiles/bwd_wgate_up_kimi-bf16-T2048.md"),
+    ("bwd_wgate_up", "dsv4-mxfp8-T2048"): (
+        63562.8e6, ('backward.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "20d0297b9a425358",
+        "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
+    ("bwd_wgate_up", "dsv4-mxfp8-ep64share"): (
+        4179.7e6, ('backward.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "20d0297b9a425358",
+        "profiles/bwd_mxfp8_dsv4-mxfp8-ep64share.md"),
 }
 
 
