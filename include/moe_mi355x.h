@@ -265,12 +265,11 @@ int moe_gate_up_3d_batched_train(const uint16_t* x, const uint16_t* w_gate_up,
  *   dlogits    [T, E] FP32 out
  *   workspace  >= moe_backward_workspace_bytes(T, H, I, E, k) bytes.  With 256 or
  *              more routed rows per expert on average (the expert-parallel
- *              share of a large batch) it also holds transposed copies of
- *              w_gate_up and w_down and K-contiguous copies of x, dout and the
- *              intermediate gradients, an FP32 copy of W_down^T dout and a
- *              64 MiB K-split buffer (about 2*(3*E*H*I + T*k*(2H + 3I)) +
+ *              share of a large batch) it also holds K-contiguous copies of x,
+ *              dout and the intermediate gradients, an FP32 copy of W_down^T
+ *              dout and a 64 MiB K-split buffer (about 2*T*k*(2H + 3I) +
  *              4*T*k*I bytes + 64 MiB), which the large-tile GEMMs of that case
- *              read.
+ *              read (the weights are read in place).
  * Limits: T >= 1, H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024.
  */
 int moe_backward_batched(const uint16_t* x, const uint16_t* w_gate_up, const uint16_t* w_down,

@@ -31,10 +31,10 @@
 //
 // With 256 or more routed rows per expert on average (MFMA-bound) kDD, kDG, kWD
 // and kWG run instead on the 256 x 256 large-group GEMM (gemm_large.hip) over a
-// second, 256-row tiling of the same grouping: W_down and W_gate_up transposed
-// for dh and dx (dh goes through FP32, then bwd_dh_finish applies kDD's
-// epilogue), and x, dout, [dg; du] and w a laid out K-contiguous per expert for
-// the weight gradients.
+// second, 256-row tiling of the same grouping: W_down and W_gate_up read as
+// stored and transposed in the GEMM's loader for dh and dx (dh goes through
+// FP32, then bwd_dh_finish applies kDD's epilogue), and x, dout, [dg; du] and
+// w a laid out K-contiguous per expert for the weight gradients.
 //
 // The three activation-gradient GEMMs share one LDS-tiled kernel (bwd_gemm):
 // a workgroup of 4 waves computes a 64-row x 128-column tile in K chunks of
@@ -693,9 +693,7 @@ BackwardWs backward_ws_layout(int T, int H, int I, int E, int k) {
     L.max_tiles256 = static_cast<int>(E + (P + kLargeBM - 1) / kLargeBM);
     L.n_tiles256 = o; o += 256;
     L.tiles256 = o;   o = align256(o + sizeof(int) * 2 * L.max_tiles256);
-    L.wguT = o;       o = align256(o + sizeof(uint16_t) * E * 2 * I * H);
     L.partial = o;    o = align256(o + sizeof(float) * kLargeMaxSlices * kLargeBM * 256);
-    L.wdT = o;        o = align256(o + sizeof(uint16_t) * E * I * H);
     L.dh = o;         o = align256(o + sizeof(float) * P * I);
   }
   L.total = o;
@@ -772,14 +770,11 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   }
   prof_begin(kBwdDown, s);
   if (L.large_d) {
-    // dh on the large-group GEMM (W_down transposed to [E][I][H]), then the
-    // SwiGLU backward, w a and the partial dots elementwise
-    uint16_t* wdT = reinterpret_cast<uint16_t*>(b + L.wdT);
+    // dh on the large-group GEMM (W_down [E][H][I] read in place, transposed in
+    // the loader), then the SwiGLU backward, w a and the partial dots elementwise
     float* dh = reinterpret_cast<float*>(b + L.dh);
-    err = launch_transpose_bf16(wd, E, H, I, wdT, s);
-    if (err == hipSuccess)
-      err = launch_dh_large(dout, wdT, a.perm, tiles256, n_tiles256, a.counts, a.offsets, H, I, k,
-                            dh, partial, L.max_tiles256, num_cus, s);
+    err = launch_dh_large(dout, wd, a.perm, tiles256, n_tiles256, a.counts, a.offsets, H, I, k,
+                          dh, partial, L.max_tiles256, num_cus, s);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(bwd_dh_finish, dim3((P + 15) / 16, I / kNT), dim3(256), 0, s, a, dh, P, order_key());
   } else if (tall) {
@@ -790,12 +785,9 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   prof_end(kBwdDown, s);
   prof_begin(kBwdInput, s);
   if (L.large_d) {
-    // dx on the large-group GEMM: W_gate_up transposed to [E][H][2I]
-    uint16_t* wguT = reinterpret_cast<uint16_t*>(b + L.wguT);
-    err = launch_transpose_bf16(wgu, E, 2 * I, H, wguT, s);
-    if (err == hipSuccess)
-      err = launch_dgrad_large(a.dgu, wguT, a.perm, tiles256, n_tiles256, a.counts, a.offsets, H,
-                               2 * I, k, a.dxs, dx, partial, L.max_tiles256, num_cus, s);
+    // dx on the large-group GEMM: W_gate_up [E][2I][H] read in place
+    err = launch_dgrad_large(a.dgu, wgu, a.perm, tiles256, n_tiles256, a.counts, a.offsets, H,
+                             2 * I, k, a.dxs, dx, partial, L.max_tiles256, num_cus, s);
     if (err != hipSuccess) return err;
   } else if (tall) {
     hipLaunchKernelGGL((bwd_gemm<kDG, 128>), grid_tiles(H), dim3(256), 0, s, a, order_key());

@@ -212,6 +212,27 @@ __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const 
   }
 }
 
+// 8 x 8 transpose of BF16 values held in registers: t[i] (i < 8) holds 8 values
+// of row i of a block (two per dword, the lower index in the low half); after
+// the call t[j] holds column j (row 2p in the low and 2p+1 in the high half of
+// dword p).  One byte permute per dword swaps the 16-bit halves between row
+// pairs; the rest is dword renaming.
+__device__ __forceinline__ void transpose8x8_bf16(i32x4 (&t)[16]) {
+  uint32_t s[8][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t a = static_cast<uint32_t>(t[2 * p][m]), b = static_cast<uint32_t>(t[2 * p + 1][m]);
+      s[2 * p][m] = __builtin_amdgcn_perm(b, a, 0x05040100u);       // low halves of a, b
+      s[2 * p + 1][m] = __builtin_amdgcn_perm(b, a, 0x07060302u);   // high halves of a, b
+    }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t[j][q] = static_cast<int>(s[2 * q + (j & 1)][j >> 1]);
+}
+
 // KIND kGateUp:    act = x [T,H], wt = W_gate_up [E,2I,H]; writes h [P,I] (sorted rows, BF16).
 // KIND kDown*:     act = h [P,I] (sorted rows), wt = W_down [E,H,I]; kDownFused (k = 1)
 //                  writes out[t] = bf16(w[t] * y), kDownSlots writes y [P,H] FP32 (sorted rows).
@@ -226,7 +247,14 @@ __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const 
 // dW_gate_up[e][c][h]; kWgradDown A = (w a)^T (rows i), B = dout^T (rows h),
 // writes dW_down[e][h][i].  A workgroup takes expert e, 256 A rows and 256 B rows
 // and reduces over the expert's columns only (no K split).
-template <int KIND>
+// AT: the A operand is stored transposed, [E][K][N] with the output dimension N
+// contiguous (the backward's dh reads W_down [E][H][I] and its dx W_gate_up
+// [E][2I][H] in place).  A thread then loads an 8 (K) x 8 (output) block of each
+// stage as eight 16-byte row pieces (a half-wave covers 512 contiguous bytes of a
+// K row), transposes it in registers and writes 8 output rows' 16-byte K chunks;
+// those rows share their low 3 bits, so the A tile's chunk swizzle also XORs in
+// row bits 3..5 (slot = chunk ^ (row & 7) ^ ((row >> 3) & 7)).
+template <int KIND, bool AT = false>
 __global__ __launch_bounds__(256) void gemm_large_bf16(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ wt,
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
@@ -300,11 +328,19 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     abase = wt + static_cast<size_t>(e) * 2 * I * H;
     // tile rows 0..127: gate neurons n0.., rows 128..255: up neurons n0..
     ao = static_cast<uint32_t>(((wv < 2 ? n0 + wv * 64 : I + n0 + (wv - 2) * 64) + lrow) * H + lc * 8);
+  } else if (AT) {
+    // stored [K][ldw]: thread = K rows 8*kb8 .. +7 of the stage, outputs 8*ob8 .. +7
+    abase = wt + static_cast<size_t>(e) * H * I;
+    ao = static_cast<uint32_t>(8 * (2 * wv + (ln >> 5)) * (kDH ? I : H) + nb * 256 + 8 * (ln & 31));
   } else {
     // down: wt = W_down [E][H][I] (rows h, K = I); kDH: W_down transposed [E][I][H]
     abase = wt + static_cast<size_t>(e) * H * I;
     ao = static_cast<uint32_t>((nb * 256 + wv * 64 + lrow) * K + lc * 8);
   }
+  const int ldw = kDH ? I : H;                    // (AT) row stride of the stored A
+  // (AT) LDS element offsets of this thread's 8 output rows' K chunk: row 8*ob8 + j,
+  // chunk kb8 at slot kb8 ^ j ^ (ob8 & 7)
+  const int at_row0 = 8 * (ln & 31) * kLBK, at_kb = 2 * wv + (ln >> 5), at_hs = (ln & 31) & 7;
   uint32_t bo[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -323,16 +359,24 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     fa[i] = ((kGU ? (i >> 1) * 128 + wn * 64 + (i & 1) * 32 : wn * 128 + 32 * i) + l32) * kLBK;
   const int fb = (wm * 128 + l32) * kLBK;
   const int swz = l32 & 7;
+  int swa[4];                                     // A fragment swizzles (AT: + row bits 3..5)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) swa[i] = AT ? swz ^ ((4 * i + (l32 >> 3)) & 7) : swz;
 
   i32x4 stg[16];   // [0..7] weight rows, [8..15] activation rows
 #define GLOAD(Q, KT) do {                                                               \
     const uint32_t kk_ = static_cast<uint32_t>(min((KT), ke - 1) * kLBK);               \
-    if ((Q) < 8) stg[Q] = ld16(abase + ao + static_cast<uint32_t>((Q) * 8) * K + kk_);  \
+    if ((Q) < 8 && AT) stg[Q] = ld16(abase + ao + (kk_ + (Q)) * static_cast<uint32_t>(ldw)); \
+    else if ((Q) < 8) stg[Q] = ld16(abase + ao + static_cast<uint32_t>((Q) * 8) * K + kk_); \
     else stg[Q] = ld16(act + bo[(Q) - 8] + kk_);                                        \
   } while (0)
+  // (AT: the first A chunk of a stage transposes all eight in place)
 #define LWRITE(Q, KT) do {                                                              \
     uint16_t* st_ = lds + ((KT) & 1) * 2 * kLTile;                                      \
-    if ((Q) < 8) *reinterpret_cast<i32x4*>(&st_[lw + (Q) * 8 * kLBK]) = stg[Q];         \
+    if ((Q) < 8 && AT) {                                                                \
+      if ((Q) == 0) transpose8x8_bf16(stg);                                             \
+      *reinterpret_cast<i32x4*>(&st_[at_row0 + (Q) * kLBK + ((at_kb ^ (Q) ^ at_hs) * 8)]) = stg[Q]; \
+    } else if ((Q) < 8) *reinterpret_cast<i32x4*>(&st_[lw + (Q) * 8 * kLBK]) = stg[Q]; \
     else *reinterpret_cast<i32x4*>(&st_[kLTile + lw + ((Q) - 8) * 8 * kLBK]) = stg[Q];  \
   } while (0)
 #define RDF(PTR) as_bf16x8(*reinterpret_cast<const i32x4*>(PTR))
@@ -345,13 +389,14 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     const uint16_t* at_ = lds + ((RKT) & 1) * 2 * kLTile;                               \
     const uint16_t* bt_ = at_ + kLTile;                                                 \
     const int so_ = (((2 * (RKS) + hi) ^ swz) * 8);                                     \
+    const int ka_ = 2 * (RKS) + hi;                                                     \
     _Pragma("unroll") for (int g = 0; g < 8; ++g) {                                     \
       const int i_ = g >> 1, j0_ = (g & 1) * 2;                                         \
       acc[i_][j0_] = mfma32x32x16(A[i_], B[j0_], acc[i_][j0_]);                         \
       acc[i_][j0_ + 1] = mfma32x32x16(A[i_], B[j0_ + 1], acc[i_][j0_ + 1]);             \
       __builtin_amdgcn_sched_barrier(0);                                                \
       if (g < 4) {                                                                      \
-        NA[g] = RDF(&at_[fa[g] + so_]);                                                 \
+        NA[g] = RDF(&at_[fa[g] + ((ka_ ^ swa[g]) * 8)]);                                \
         NB[g] = RDF(&bt_[fb + 32 * g * kLBK + so_]);                                    \
       }                                                                                 \
       if (g < (NQ)) { LWRITE((Q0) + g, WKT); GLOAD((Q0) + g, (WKT) + 1); }              \
@@ -388,7 +433,7 @@ __global__ __launch_bounds__(256) void gemm_large_bf16(
     const uint16_t* at = lds + (kb & 1) * 2 * kLTile;
     const int so = (hi ^ swz) * 8;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) a0[g] = RDF(&at[fa[g] + so]);
+    for (int g = 0; g < 4; ++g) a0[g] = RDF(&at[fa[g] + ((hi ^ swa[g]) * 8)]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) b0[g] = RDF(&at[kLTile + fb + 32 * g * kLBK + so]);
   }
@@ -1103,47 +1148,12 @@ hipError_t launch_wgrad_large(const uint16_t* x, const uint16_t* dout, const uin
   return hipGetLastError();
 }
 
-namespace {
-// dst[b][c][r] = src[b][r][c] (BF16; R and C multiples of 64): 64 x 64 LDS tiles,
-// 16-byte loads and stores.
-__global__ __launch_bounds__(256) void transpose_bf16(const uint16_t* __restrict__ src, int R, int C,
-                                                      uint16_t* __restrict__ dst) {
-  __shared__ __align__(16) uint16_t tl[64][64 + 8];
-  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  const size_t mat = static_cast<size_t>(R) * C * blockIdx.z;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int ch = tid + 256 * u, r = ch >> 3, cc = ch & 7;
-    *reinterpret_cast<i32x4*>(&tl[r][cc * 8]) =
-        ld16(src + mat + static_cast<size_t>(r0 + r) * C + c0 + cc * 8);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int ch = tid + 256 * u, c = ch >> 3, rc = ch & 7;
-    uint32_t p[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      p[t] = static_cast<uint32_t>(tl[rc * 8 + 2 * t][c]) | (static_cast<uint32_t>(tl[rc * 8 + 2 * t + 1][c]) << 16);
-    *reinterpret_cast<uint4*>(dst + mat + static_cast<size_t>(c0 + c) * R + r0 + rc * 8) =
-        make_uint4(p[0], p[1], p[2], p[3]);
-  }
-}
-}  // namespace
-
-hipError_t launch_transpose_bf16(const uint16_t* src, int B, int R, int C, uint16_t* dst,
-                                 hipStream_t s) {
-  hipLaunchKernelGGL(transpose_bf16, dim3(C / 64, R / 64, B), dim3(256), 0, s, src, R, C, dst);
-  return hipGetLastError();
-}
-
-hipError_t launch_dh_large(const uint16_t* dout, const uint16_t* wdT, const int* perm,
+hipError_t launch_dh_large(const uint16_t* dout, const uint16_t* wd, const int* perm,
                            const int2* tiles, const int* n_tiles, const int* counts,
                            const int* offsets, int H, int I, int k, float* dh, float* partial,
                            int max_tiles, int ncu, hipStream_t s) {
   const int grid = large_grid(I / 256, max_tiles, ncu);
-  hipLaunchKernelGGL(gemm_large_bf16<kBwdDh>, dim3(grid), dim3(256), kLLds, s, dout, wdT, perm,
+  hipLaunchKernelGGL((gemm_large_bf16<kBwdDh, true>), dim3(grid), dim3(256), kLLds, s, dout, wd, perm,
                      tiles, n_tiles, counts, offsets, nullptr, H, I, k, nullptr, dh, nullptr,
                      partial, ncu, nullptr, 0, order_key());
   hipLaunchKernelGGL(gemm_large_fixup<kBwdDh>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,
@@ -1152,13 +1162,13 @@ hipError_t launch_dh_large(const uint16_t* dout, const uint16_t* wdT, const int*
   return hipGetLastError();
 }
 
-hipError_t launch_dgrad_large(const uint16_t* act, const uint16_t* wT, const int* perm,
+hipError_t launch_dgrad_large(const uint16_t* act, const uint16_t* w_in, const int* perm,
                               const int2* tiles, const int* n_tiles, const int* counts,
                               const int* offsets, int H, int K, int k, float* y, uint16_t* out,
                               float* partial, int max_tiles, int ncu, hipStream_t s) {
   const int grid = large_grid(H / 256, max_tiles, ncu);
 #define DGRAD(KD)                                                                             \
-  hipLaunchKernelGGL(gemm_large_bf16<KD>, dim3(grid), dim3(256), kLLds, s, act, wT, perm, tiles, \
+  hipLaunchKernelGGL((gemm_large_bf16<KD, true>), dim3(grid), dim3(256), kLLds, s, act, w_in, perm, tiles, \
                      n_tiles, counts, offsets, nullptr, H, K, k, nullptr, y, out, partial, ncu,  \
                      nullptr, 0, order_key());                                                                \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,      \
@@ -1183,10 +1193,13 @@ hipError_t large_set_attributes() {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kGateUpSave>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kBwdDh>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kBwdDh, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kDownPlain>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kDownPlain, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kDownSlots, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_bf16<kWgradGateUp>),

@@ -106,19 +106,18 @@ hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint
 // per expert): koff [E+1] ints, and transposed operands of wgrad_large_cols(P, E)
 // columns each - xT, doutT [H][cols], dguT [2I][cols], waT [I][cols].
 size_t wgrad_large_cols(int P, int E);
-// dst[b] = src[b]^T for B row-major R x C BF16 matrices (R, C multiples of 64)
-hipError_t launch_transpose_bf16(const uint16_t* src, int B, int R, int C, uint16_t* dst,
-                                 hipStream_t s);
 // dh[r][i] = sum_h W_down[e][h][i] dout[perm[r] / k][h] for each grouped row r
-// (256-row M-tiles) on the large-group GEMM; wdT = W_down transposed, [E][I][H].
-hipError_t launch_dh_large(const uint16_t* dout, const uint16_t* wdT, const int* perm,
+// (256-row M-tiles) on the large-group GEMM; wd = W_down [E][H][I] as stored
+// (the loader transposes it).
+hipError_t launch_dh_large(const uint16_t* dout, const uint16_t* wd, const int* perm,
                            const int2* tiles, const int* n_tiles, const int* counts,
                            const int* offsets, int H, int I, int k, float* dh, float* partial,
                            int max_tiles, int ncu, hipStream_t s);
 // Data gradient of a projection on the large-group GEMM: for each grouped row r
-// (256-row M-tiles), D[r][n] = sum_c act[r][c] wT[e][n][c], c < K, n < H; k = 1
-// writes out[perm[r]] = bf16(D), k > 1 writes y[r] = D (FP32).
-hipError_t launch_dgrad_large(const uint16_t* act, const uint16_t* wT, const int* perm,
+// (256-row M-tiles), D[r][n] = sum_c act[r][c] w_in[e][c][n], c < K, n < H
+// (w_in [E][K][H] as stored: W_gate_up with K = 2I); k = 1 writes
+// out[perm[r]] = bf16(D), k > 1 writes y[r] = D (FP32).
+hipError_t launch_dgrad_large(const uint16_t* act, const uint16_t* w_in, const int* perm,
                               const int2* tiles, const int* n_tiles, const int* counts,
                               const int* offsets, int H, int K, int k, float* y, uint16_t* out,
                               float* partial, int max_tiles, int ncu, hipStream_t s);
@@ -138,8 +137,8 @@ hipError_t launch_group_experts(const int32_t* idx, int P, int E, int BM, int* c
 struct BackwardWs {
   size_t counts, offsets, tiles, n_tiles, perm, row_of, gu, dgu, wa, dwp, dxs, total;
   size_t koff, xT, doutT, dguT, waT;   // large groups: the weight gradients' operands
-  size_t tiles256, n_tiles256, wguT, partial;   // large groups: dx on the large-group GEMM
-  size_t wdT, dh;                                // large groups: dh on the large-group GEMM
+  size_t tiles256, n_tiles256, partial;         // large groups: dx on the large-group GEMM
+  size_t dh;                                     // large groups: dh on the large-group GEMM
   int max_tiles, max_tiles256;
   bool large_w;                        // weight gradients on the large-group GEMM
   bool large_d;                        // dh and dx on the large-group GEMM
