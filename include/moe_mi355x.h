@@ -337,8 +337,9 @@ typedef enum {
   MOE_KERNEL_GROUP = 4,          /* expert grouping of the batched path        */
   MOE_KERNEL_QUANT = 5,          /* moe_quantize_mxfp8                         */
   MOE_KERNEL_GEMM_GATE_UP = 6,
-  MOE_KERNEL_GEMM_DOWN = 7,
-  MOE_KERNEL_COMBINE = 8,
+  MOE_KERNEL_GEMM_DOWN = 7,      /* batched down projection and the weighted combine
+                                    (which runs interleaved with it in column parts) */
+  MOE_KERNEL_COMBINE = 8,        /* reserved: the combine is timed within GEMM_DOWN */
   MOE_KERNEL_BWD_GATE_UP = 9,    /* backward: recomputed gate/up pre-activations */
   MOE_KERNEL_BWD_DOWN = 10,      /* backward: W_down^T dout and the SwiGLU step  */
   MOE_KERNEL_BWD_INPUT = 11,     /* backward: dx (and the slot sum)              */

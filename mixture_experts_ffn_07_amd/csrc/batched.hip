@@ -163,6 +163,9 @@ __global__ __launch_bounds__(1024) void group_experts(
 // Epilogues: KIND 0 SwiGLU -> h (BF16); KIND 3 the same, and also the FP32
 // pre-activations g and u of each pair in slot order (for the backward pass);
 // KIND 1 FP32 y per slot; KIND 2 (k = 1) out[t] = bf16(w[t] * y) with t = perm[row].
+// A launch covers the output column blocks [cb0, cb0 + ncb) of NW * RPW outputs
+// each (ncb 0: all of them); KIND 1 writes y with row stride ldy, its column 0
+// being output column cb0 * NW * RPW.
 constexpr int kSXC = 128;                // K chunk of the staged activations
 constexpr int kSXRS = kSXC + 8;          // padded LDS row stride (elements)
 enum { kProjGateUp = 0, kProjDown = 1, kProjDownFused = 2, kProjGateUpSave = 3 };
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint16_t* __restrict__ hout, float* __restrict__ y,
-    uint16_t* __restrict__ out, float* __restrict__ gu, uint32_t okey) {
+    uint16_t* __restrict__ out, float* __restrict__ gu, uint32_t okey, int cb0, int ncb, int ldy) {
   constexpr bool GU = KIND == kProjGateUp || KIND == kProjGateUpSave;
   constexpr bool ONE = NGW == 1;         // one 16-row weight group per wave
   constexpr int NT = NW * 64;
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
   __shared__ __align__(16) i32x4 wtl[NW][16 * 8];         // per wave: [16 rows][8 chunks]
   const int K = GU ? H : I;              // reduction length
   const int N = GU ? I : H;              // outputs
-  const int nblk = N / (NW * RPW);
+  const int nblk = ncb ? ncb : N / (NW * RPW);
   const int item0 = real_item(blockIdx.x, nblk, *n_tiles);
   if (item0 < 0) return;
   const int item = permute_item(item0, nblk * *n_tiles, okey);
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
   const int rbase = offsets[e] + m0;
   const int tid = threadIdx.x, ln = tid & 63, col = ln & 15, grp = ln >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nb = nb_i * NW * RPW + wv * RPW;              // the wave's first output
+  const int nb = (cb0 + nb_i) * NW * RPW + wv * RPW;      // the wave's first output
   // the wave's 16-row weight groups (BM 64: two; BM 128: one, rows 0-7 from row0
   // and rows 8-15 from row1)
   const int row0 = nb, row1 = GU ? I + nb : nb + (ONE ? 8 : 16);
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
         *reinterpret_cast<uint2*>(orow + 16 * m) = v;
       }
     } else {
-      float* yr = y + static_cast<size_t>(rbase + r) * H + nb + 4 * grp;
+      float* yr = y + static_cast<size_t>(rbase + r) * ldy + (nb - cb0 * NW * RPW) + 4 * grp;
       *reinterpret_cast<f32x4*>(yr) = acc0[g];
       if (!ONE) *reinterpret_cast<f32x4*>(yr + 16) = up;
     }
@@ -369,20 +372,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
 }
 
 // combine: out[t] = sum_j w[t,j] * y[row_of[t*k+j]] in slot order (FP32 FMA
-// chain starting from 0), rounded once to BF16.  One workgroup per token.
+// chain starting from 0), rounded once to BF16.  One workgroup per token; a
+// launch covers the output columns [col0, col0 + cols), y holding them with row
+// stride ldy from its column 0.
 __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y,
                                                      const int* __restrict__ row_of,
                                                      const float* __restrict__ w, int T, int H,
-                                                     int k, uint16_t* __restrict__ out, uint32_t okey) {
+                                                     int k, uint16_t* __restrict__ out, uint32_t okey,
+                                                     int col0, int cols, int ldy) {
   const int t = permute_item(blockIdx.x, gridDim.x, okey);
   const int P = T * k;
-  for (int c = threadIdx.x; c < H / 4; c += blockDim.x) {
+  out += col0;
+  for (int c = threadIdx.x; c < cols / 4; c += blockDim.x) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int row = row_of[t * k + j];
       if (static_cast<unsigned>(row) >= static_cast<unsigned>(P)) continue;
       const float wj = w[t * k + j];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(y + static_cast<size_t>(row) * H + 4 * c);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(y + static_cast<size_t>(row) * ldy + 4 * c);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
     }
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
     const int* __restrict__ perm, const int2* __restrict__ tiles, const int* __restrict__ n_tiles,
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint8_t* __restrict__ hout, uint8_t* __restrict__ hsout,
-    float* __restrict__ y, uint16_t* __restrict__ out, uint32_t okey) {
+    float* __restrict__ y, uint16_t* __restrict__ out, uint32_t okey, int cb0, int ncb, int ldy) {
   constexpr int NT = NW * 64;
   constexpr int RPW = KIND == kProjGateUp ? 16 : 32;      // outputs per wave
   constexpr int LPT = kBM * kMCH / NT;                    // 16-byte code loads per thread
@@ -470,7 +477,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const int K = KIND == kProjGateUp ? H : I;              // reduction length
   const int N = KIND == kProjGateUp ? I : H;              // outputs
   const int KB = K / 32;                                  // scale bytes per row
-  const int nblk = N / (NW * RPW);
+  const int nblk = ncb ? ncb : N / (NW * RPW);
   const int item0 = real_item(blockIdx.x, nblk, *n_tiles);
   if (item0 < 0) return;
   const int item = permute_item(item0, nblk * *n_tiles, okey);
@@ -481,7 +488,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const int rbase = offsets[e] + m0;
   const int tid = threadIdx.x, ln = tid & 63, col = ln & 15, grp = ln >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nb = nb_i * NW * RPW + wv * RPW;              // the wave's first output
+  const int nb = (cb0 + nb_i) * NW * RPW + wv * RPW;      // the wave's first output
   const int row0 = nb, row1 = KIND == kProjGateUp ? I + nb : nb + 16;
   const size_t wrows = KIND == kProjGateUp ? 2 * static_cast<size_t>(I) : H;
 
@@ -649,7 +656,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
           *reinterpret_cast<uint2*>(orow + 16 * m) = v;
         }
       } else {
-        float* yr = y + static_cast<size_t>(rbase + r) * H + nb + 4 * grp;
+        float* yr = y + static_cast<size_t>(rbase + r) * ldy + (nb - cb0 * NW * RPW) + 4 * grp;
         *reinterpret_cast<f32x4*>(yr) = acc0[g];
         *reinterpret_cast<f32x4*>(yr + 16) = acc1[g];
       }
@@ -716,12 +723,12 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
       hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 8, kTallBM>), dim3(n_tall), dim3(512), 0, s,
                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                          p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                         static_cast<uint16_t*>(h), nullptr, nullptr, gu, order_key());
+                         static_cast<uint16_t*>(h), nullptr, nullptr, gu, order_key(), 0, 0, 0);
     else
       hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 8, kTallBM>), dim3(n_tall), dim3(512), 0, s,
                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                          p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                         static_cast<uint16_t*>(h), nullptr, nullptr, nullptr, order_key());
+                         static_cast<uint16_t*>(h), nullptr, nullptr, nullptr, order_key(), 0, 0, 0);
     prof_end(kGemmGateUp, s);
     return hipGetLastError();
   }
@@ -735,34 +742,61 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 8>), dim3(n_items8), dim3(512), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint16_t*>(h), nullptr, nullptr, gu, order_key());
+                       static_cast<uint16_t*>(h), nullptr, nullptr, gu, order_key(), 0, 0, 0);
   else if (narrow && dtype == 0)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 8>), dim3(n_items8), dim3(512), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint16_t*>(h), nullptr, nullptr, nullptr, order_key());
+                       static_cast<uint16_t*>(h), nullptr, nullptr, nullptr, order_key(), 0, 0, 0);
   else if (narrow)
     hipLaunchKernelGGL((gemm_mx_s<kProjGateUp, 8>), dim3(n_items8), dim3(512), 0, s,
                        static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
                        p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint8_t*>(h), hs, nullptr, nullptr, order_key());
+                       static_cast<uint8_t*>(h), hs, nullptr, nullptr, order_key(), 0, 0, 0);
   else if (dtype == 0 && gu)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUpSave, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint16_t*>(h), nullptr, nullptr, gu, order_key());
+                       static_cast<uint16_t*>(h), nullptr, nullptr, gu, order_key(), 0, 0, 0);
   else if (dtype == 0)
     hipLaunchKernelGGL((gemm_bf16s<kProjGateUp, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wgu), p.perm,
                        p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint16_t*>(h), nullptr, nullptr, nullptr, order_key());
+                       static_cast<uint16_t*>(h), nullptr, nullptr, nullptr, order_key(), 0, 0, 0);
   else
     hipLaunchKernelGGL((gemm_mx_s<kProjGateUp, 16>), dim3(n_items), dim3(1024), 0, s,
                        static_cast<const uint8_t*>(x), xs, static_cast<const uint8_t*>(wgu), wgus,
                        p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, nullptr, H, I, k,
-                       static_cast<uint8_t*>(h), hs, nullptr, nullptr, order_key());
+                       static_cast<uint8_t*>(h), hs, nullptr, nullptr, order_key(), 0, 0, 0);
   prof_end(kGemmGateUp, s);
   return hipGetLastError();
+}
+
+// The small-tile down projection and the combine run in column parts when k > 1:
+// part q's down launch writes the FP32 slot values of its H / parts output
+// columns into the head of the slot buffer (row stride H / parts), and the
+// combine of those columns reads them right after; the next part overwrites the
+// same bytes.  A part of at most kYPartBytes stays in the 256 MB last-level
+// cache between its write and its read, instead of mixing ~470 MB of slot
+// writes (T 2048, k 8, H 7168) into the weight stream.  Each part is a launch of
+// its own with its own tail, so parts keep at least four rounds of workgroups
+// (by the tile bound max_tiles).  Measured down + combine, T 2048, k 8: H 7168
+// E 384 BF16 2,245 -> 2,128 us (7 parts; 4: 2,180; 14: 2,137; 28: 2,400), whole
+// forward step 5.74 -> 5.65 ms; H 6144 E 256 BF16 128-row tiles 1,390 -> 1,360 us
+// (4 parts; 3: 1,345; 6: 1,460).  The MXFP8 down (16-wave workgroups, one per
+// CU) stays whole: at H 7168 I 3072 its 7-part form, faster alone (1,713 ->
+// 1,650 us), made the whole step slower (4.64 -> 4.68 ms; 2 parts 4.72).
+constexpr size_t kYPartBytes = size_t(72) << 20;
+static int down_parts(size_t P, int H, int cw, int max_tiles, int min_items) {
+  const int nblk = H / cw;
+  int parts = 1;
+  for (int q = 1; q <= nblk; ++q) {
+    if (nblk % q) continue;
+    if (static_cast<int64_t>(nblk / q) * max_tiles < min_items) break;
+    parts = q;
+    if (P * static_cast<size_t>(H / q) * sizeof(float) <= kYPartBytes) break;
+  }
+  return parts;
 }
 
 hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
@@ -772,8 +806,8 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   (void)idx;
   const BatchedWs L = batched_ws_layout(T, H, I, E, k, dtype);
   const BatchedPtrs p = batched_ptrs(ws, L);
+  prof_begin(kGemmDown, s);
   if (L.bm == kLargeBM) {
-    prof_begin(kGemmDown, s);
     hipError_t e =
         dtype == 0
             ? launch_down_large_bf16(static_cast<const uint16_t*>(h),
@@ -784,61 +818,57 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
                                    static_cast<const uint8_t*>(wd), wds, p.perm, p.tiles,
                                    p.n_tiles, p.counts, p.offsets, w, H, I, k, p.y, out,
                                    p.partial, L.max_tiles, num_cus, s);
-    prof_end(kGemmDown, s);
     if (e == hipSuccess && k > 1) {
-      prof_begin(kCombine, s);
-      hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out, order_key());
-      prof_end(kCombine, s);
+      hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out,
+                         order_key(), 0, H, H);
       e = hipGetLastError();
     }
+    prof_end(kGemmDown, s);
     return e;
   }
   // output dims per workgroup: BF16 8 waves x 32, two workgroups per CU (a CU stays
   // busy while one of them starts its next item: measured ~4% faster than one
   // 16-wave workgroup); MXFP8 16 waves x 32, where the 8-wave form measured slower
   // on large batches (8 x 32 when H is not a multiple of 512, or when 16-wave
-  // items would leave fewer than four workgroups per CU)
+  // items would leave fewer than four workgroups per CU); BF16 128-row tiles 8 x 32
   const bool wide = dtype == 1 && H % 512 == 0 && (H / 512) * L.max_tiles >= 4 * num_cus;
   const int dims = wide ? 512 : 256;
-  const int n_items = round_up((H / dims) * L.max_tiles, kXcds);
-  const dim3 grid(n_items), block(2 * dims);
-#define DOWN_BF16(KINDV, NWV)                                                               \
-  hipLaunchKernelGGL((gemm_bf16s<KINDV, NWV>), grid, block, 0, s,                          \
-                     static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),       \
-                     p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr,   \
-                     p.y, out, nullptr, order_key())
-#define DOWN_MX(KINDV, NWV)                                                                 \
-  hipLaunchKernelGGL((gemm_mx_s<KINDV, NWV>), grid, block, 0, s,                           \
-                     static_cast<const uint8_t*>(h), hs, static_cast<const uint8_t*>(wd), wds, \
-                     p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr,   \
-                     nullptr, p.y, out, order_key())
-  prof_begin(kGemmDown, s);
-  if (L.bm == kTallBM) {
-    // 8 waves x 32 dimensions = 256 output dimensions per workgroup, 128-row tiles
-    const dim3 grid_t(round_up((H / 256) * L.max_tiles, kXcds)), block_t(512);
-#define DOWN_TALL(KINDV)                                                                    \
-    hipLaunchKernelGGL((gemm_bf16s<KINDV, 8, kTallBM>), grid_t, block_t, 0, s,              \
-                       static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(wd),     \
-                       p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr, \
-                       p.y, out, nullptr, order_key())
-    if (k == 1) DOWN_TALL(kProjDownFused);
-    else DOWN_TALL(kProjDown);
-#undef DOWN_TALL
-  } else if (dtype == 0) {
-    if (k == 1) DOWN_BF16(kProjDownFused, 8);
-    else DOWN_BF16(kProjDown, 8);
-  } else {
-    if (k == 1) { if (wide) DOWN_MX(kProjDownFused, 16); else DOWN_MX(kProjDownFused, 8); }
-    else { if (wide) DOWN_MX(kProjDown, 16); else DOWN_MX(kProjDown, 8); }
+  // BF16 (two 8-wave workgroups per CU): four rounds are 8 * num_cus items
+  const int parts = k > 1 && dtype == 0
+                        ? down_parts(static_cast<size_t>(T) * k, H, dims, L.max_tiles, 8 * num_cus)
+                        : 1;
+  const int hq = H / parts, ncb = hq / dims;
+  const dim3 grid(round_up(ncb * L.max_tiles, kXcds)), block(2 * dims);
+  const uint16_t* hb = static_cast<const uint16_t*>(h);
+  const uint16_t* wb = static_cast<const uint16_t*>(wd);
+  const uint8_t* hm = static_cast<const uint8_t*>(h);
+  const uint8_t* wm = static_cast<const uint8_t*>(wd);
+  for (int q = 0; q < parts; ++q) {
+    const int cb0 = q * ncb;
+#define DOWN_ARGS_B p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr, p.y, out, \
+                    nullptr, order_key(), cb0, ncb, hq
+#define DOWN_ARGS_M p.perm, p.tiles, p.n_tiles, p.counts, p.offsets, w, H, I, k, nullptr, nullptr, \
+                    p.y, out, order_key(), cb0, ncb, hq
+    if (L.bm == kTallBM) {
+      if (k == 1) hipLaunchKernelGGL((gemm_bf16s<kProjDownFused, 8, kTallBM>), grid, block, 0, s, hb, wb, DOWN_ARGS_B);
+      else hipLaunchKernelGGL((gemm_bf16s<kProjDown, 8, kTallBM>), grid, block, 0, s, hb, wb, DOWN_ARGS_B);
+    } else if (dtype == 0) {
+      if (k == 1) hipLaunchKernelGGL((gemm_bf16s<kProjDownFused, 8>), grid, block, 0, s, hb, wb, DOWN_ARGS_B);
+      else hipLaunchKernelGGL((gemm_bf16s<kProjDown, 8>), grid, block, 0, s, hb, wb, DOWN_ARGS_B);
+    } else if (wide) {
+      if (k == 1) hipLaunchKernelGGL((gemm_mx_s<kProjDownFused, 16>), grid, block, 0, s, hm, hs, wm, wds, DOWN_ARGS_M);
+      else hipLaunchKernelGGL((gemm_mx_s<kProjDown, 16>), grid, block, 0, s, hm, hs, wm, wds, DOWN_ARGS_M);
+    } else {
+      if (k == 1) hipLaunchKernelGGL((gemm_mx_s<kProjDownFused, 8>), grid, block, 0, s, hm, hs, wm, wds, DOWN_ARGS_M);
+      else hipLaunchKernelGGL((gemm_mx_s<kProjDown, 8>), grid, block, 0, s, hm, hs, wm, wds, DOWN_ARGS_M);
+    }
+#undef DOWN_ARGS_B
+#undef DOWN_ARGS_M
+    if (k > 1)
+      hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out,
+                         order_key(), q * hq, hq, hq);
   }
-#undef DOWN_BF16
-#undef DOWN_MX
   prof_end(kGemmDown, s);
-  if (k > 1) {
-    prof_begin(kCombine, s);
-    hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out, order_key());
-    prof_end(kCombine, s);
-  }
   return hipGetLastError();
 }
 
