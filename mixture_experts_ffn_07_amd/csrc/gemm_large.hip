@@ -769,8 +769,34 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
   // the BF16 kernel.  Prologue: stage kb and chunks 0..7 of stage kb+1 in LDS;
   // registers holding chunks 8..15 and the scales of stage kb+1 and chunks 0..7
   // of stage kb+2.  (A weight-gradient expert with no rows has an empty range:
-  // its block is zero.)
-  if (ke > kb) {
+  // its block is zero.)  A weight-gradient item of a single stage (an expert
+  // with at most 128 routed pairs) loads it once and multiplies: the pipelined
+  // form would wait on three load round trips of that same stage (its loads of
+  // the next stages are clamped to the last one).
+  if (kWG && ke - kb == 1) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) GLOAD(q, kb);
+    SLOAD(kb);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) LWRITE(q, kb);
+    SWRITE(kb);
+    __syncthreads();
+    i32x8 f0[8], f1[8];
+    uint32_t sc[8];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) RDP(f0, p, kb, 0);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) RDP(f1, p, kb, 1);
+    RDS(sc, kb);
+#pragma unroll
+    for (int g = 0; g < 16; ++g)
+      acc[g >> 2][g & 3] = mfma_mx32<0>(f0[g >> 2], f0[4 + (g & 3)], static_cast<int>(sc[g >> 2]),
+                                        static_cast<int>(sc[4 + (g & 3)]), acc[g >> 2][g & 3]);
+#pragma unroll
+    for (int g = 0; g < 16; ++g)
+      acc[g >> 2][g & 3] = mfma_mx32<2>(f1[g >> 2], f1[4 + (g & 3)], static_cast<int>(sc[g >> 2]),
+                                        static_cast<int>(sc[4 + (g & 3)]), acc[g >> 2][g & 3]);
+  } else if (ke > kb) {
 #pragma unroll
   for (int q = 0; q < 16; ++q) GLOAD(q, kb);
   SLOAD(kb);
