@@ -352,10 +352,10 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
           } else {
             const int t = a.perm[grow];               // k = 1: pair id == token
             i32x4 o;
-            o[0] = static_cast<int>(f32_to_bf16_rne(c0[0]) | (f32_to_bf16_rne(c0[1]) << 16));
-            o[1] = static_cast<int>(f32_to_bf16_rne(c0[2]) | (f32_to_bf16_rne(c0[3]) << 16));
-            o[2] = static_cast<int>(f32_to_bf16_rne(c1[0]) | (f32_to_bf16_rne(c1[1]) << 16));
-            o[3] = static_cast<int>(f32_to_bf16_rne(c1[2]) | (f32_to_bf16_rne(c1[3]) << 16));
+            o[0] = static_cast<int>(pack_bf16x2(c0[0], c0[1]));
+            o[1] = static_cast<int>(pack_bf16x2(c0[2], c0[3]));
+            o[2] = static_cast<int>(pack_bf16x2(c1[0], c1[1]));
+            o[3] = static_cast<int>(pack_bf16x2(c1[2], c1[3]));
             st16(a.dx + static_cast<size_t>(t) * H + n0 + 8 * sg, o);
           }
         }
@@ -475,10 +475,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int j = 0; j < 4; j += 2) {
         uint32_t lo[2], hi[2];
-        lo[0] = f32_to_bf16_rne(acc[i][j][0]) | (f32_to_bf16_rne(acc[i][j][1]) << 16);
-        lo[1] = f32_to_bf16_rne(acc[i][j][2]) | (f32_to_bf16_rne(acc[i][j][3]) << 16);
-        hi[0] = f32_to_bf16_rne(acc[i][j + 1][0]) | (f32_to_bf16_rne(acc[i][j + 1][1]) << 16);
-        hi[1] = f32_to_bf16_rne(acc[i][j + 1][2]) | (f32_to_bf16_rne(acc[i][j + 1][3]) << 16);
+        lo[0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        lo[1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        hi[0] = pack_bf16x2(acc[i][j + 1][0], acc[i][j + 1][1]);
+        hi[1] = pack_bf16x2(acc[i][j + 1][2], acc[i][j + 1][3]);
         const uint32_t s0 = odd ? lo[0] : hi[0], s1 = odd ? lo[1] : hi[1];
         const uint32_t r0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(s0), 16, kWave));
         const uint32_t r1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(s1), 16, kWave));
@@ -556,8 +556,8 @@ __global__ __launch_bounds__(256) void sum_pairs(const float* __restrict__ dxs,
       for (int i = 0; i < 4; ++i) acc[i] += v[i];
     }
     uint2 o;
-    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
     *reinterpret_cast<uint2*>(dx + static_cast<size_t>(t) * H + 4 * c) = o;
   }
 }

@@ -339,12 +339,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
     if (r >= mcount || (ONE && GU && grp >= 2)) continue;
     if (GU) {
       uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb + 4 * grp;
-      uint32_t p[4];
+      float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = f32_to_bf16_rne(swiglu(acc0[g][i], up[i]));
+      for (int i = 0; i < 4; ++i) p[i] = swiglu(acc0[g][i], up[i]);
       uint2 v;
-      v.x = p[0] | (p[1] << 16);
-      v.y = p[2] | (p[3] << 16);
+      v.x = pack_bf16x2(p[0], p[1]);
+      v.y = pack_bf16x2(p[2], p[3]);
       *reinterpret_cast<uint2*>(hr) = v;
       if (KIND == kProjGateUpSave) {                      // FP32 g and u of the pair, slot order
         float* gp = gu + static_cast<size_t>(perm[rbase + r]) * (2 * I) + nb + 4 * grp;
@@ -359,8 +359,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
       for (int m = 0; m < NGW; ++m) {
         const f32x4 a = m == 0 ? acc0[g] : up;
         uint2 v;
-        v.x = f32_to_bf16_rne(wt_ * a[0]) | (f32_to_bf16_rne(wt_ * a[1]) << 16);
-        v.y = f32_to_bf16_rne(wt_ * a[2]) | (f32_to_bf16_rne(wt_ * a[3]) << 16);
+        v.x = pack_bf16x2(wt_ * a[0], wt_ * a[1]);
+        v.y = pack_bf16x2(wt_ * a[2], wt_ * a[3]);
         *reinterpret_cast<uint2*>(orow + 16 * m) = v;
       }
     } else {
@@ -394,8 +394,8 @@ __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
     }
     uint2 o;
-    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
     *reinterpret_cast<uint2*>(out + static_cast<size_t>(t) * H + 4 * c) = o;
   }
 }
@@ -651,8 +651,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
         for (int m = 0; m < 2; ++m) {
           const f32x4 a = m == 0 ? acc0[g] : acc1[g];
           uint2 v;
-          v.x = f32_to_bf16_rne(wt_ * a[0]) | (f32_to_bf16_rne(wt_ * a[1]) << 16);
-          v.y = f32_to_bf16_rne(wt_ * a[2]) | (f32_to_bf16_rne(wt_ * a[3]) << 16);
+          v.x = pack_bf16x2(wt_ * a[0], wt_ * a[1]);
+          v.y = pack_bf16x2(wt_ * a[2], wt_ * a[3]);
           *reinterpret_cast<uint2*>(orow + 16 * m) = v;
         }
       } else {

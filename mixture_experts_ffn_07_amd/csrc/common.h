@@ -32,12 +32,15 @@ __device__ __forceinline__ i32x4 ld16_stream(const void* p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// FP32 -> BF16 bits, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// FP32 -> BF16, round to nearest, ties to even, on gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32, two values per instruction): pack_bf16x2
+// returns a's bits in the low half and b's in the high half; f32_to_bf16_rne
+// one value's bits.
+typedef __bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_cvt));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // silu(z) * u in FP32.  For z -> -inf, exp(-z) overflows to +inf and

@@ -132,8 +132,8 @@ __device__ __forceinline__ void wgrad_store(const f32x16 (&acc)[4][4], uint8_t* 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x16& a = acc[i][2 * half + jj];
-          const uint32_t p0 = f32_to_bf16_rne(a[4 * q]) | (f32_to_bf16_rne(a[4 * q + 1]) << 16);
-          const uint32_t p1 = f32_to_bf16_rne(a[4 * q + 2]) | (f32_to_bf16_rne(a[4 * q + 3]) << 16);
+          const uint32_t p0 = pack_bf16x2(a[4 * q], a[4 * q + 1]);
+          const uint32_t p1 = pack_bf16x2(a[4 * q + 2], a[4 * q + 3]);
           *reinterpret_cast<uint2*>(st + (32 * jj + l32) * kWgStage + (32 * i + 8 * q + 4 * hi) * 2) =
               make_uint2(p0, p1);
         }
@@ -180,11 +180,10 @@ __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const 
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint32_t p[4];
+          float p[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            p[t] = f32_to_bf16_rne(swiglu(acc[i][j][4 * q + t], acc[i + 2][j][4 * q + t]));
-          *reinterpret_cast<uint2*>(hr + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+          for (int t = 0; t < 4; ++t) p[t] = swiglu(acc[i][j][4 * q + t], acc[i + 2][j][4 * q + t]);
+          *reinterpret_cast<uint2*>(hr + 32 * i + 8 * q) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
         }
     } else if (KIND == kDownFused || KIND == kDownPlain) {
       const int t = perm[rbase + r];        // k = 1: pair id == token
@@ -194,10 +193,10 @@ __device__ __forceinline__ void large_epilogue(const f32x16 (&acc)[4][4], const 
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint32_t p[4];
+          float p[4];
 #pragma unroll
-          for (int t4 = 0; t4 < 4; ++t4) p[t4] = f32_to_bf16_rne(wt_t * acc[i][j][4 * q + t4]);
-          *reinterpret_cast<uint2*>(orow + 32 * i + 8 * q) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+          for (int t4 = 0; t4 < 4; ++t4) p[t4] = wt_t * acc[i][j][4 * q + t4];
+          *reinterpret_cast<uint2*>(orow + 32 * i + 8 * q) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
         }
     } else {
       // kDownSlots: y [P, H]; kBwdDh: dh [P, I]
@@ -525,18 +524,18 @@ __global__ __launch_bounds__(256) void gemm_large_fixup(
     }
     if (KIND == kGateUpRaw) return;
     uint16_t* hr = hout + static_cast<size_t>(rbase + r) * I + nb * 128 + wn * 64 + 32 * i + 8 * q + 4 * hi;
-    uint32_t p[4];
+    float p[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) p[t] = f32_to_bf16_rne(swiglu(a[t], u[t]));
-    *reinterpret_cast<uint2*>(hr) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+    for (int t = 0; t < 4; ++t) p[t] = swiglu(a[t], u[t]);
+    *reinterpret_cast<uint2*>(hr) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
   } else if (KIND == kDownFused || KIND == kDownPlain) {
     const int t = perm[rbase + r];
     const float wt_t = KIND == kDownFused ? w[t] : 1.0f;
     uint16_t* o = out + static_cast<size_t>(t) * H + nb * 256 + wn * 128 + 32 * i + 8 * q + 4 * hi;
-    uint32_t p[4];
+    float p[4];
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) p[t4] = f32_to_bf16_rne(wt_t * a[t4]);
-    *reinterpret_cast<uint2*>(o) = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+    for (int t4 = 0; t4 < 4; ++t4) p[t4] = wt_t * a[t4];
+    *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
   } else {
     *reinterpret_cast<f32x4*>(y + static_cast<size_t>(rbase + r) * (KIND == kBwdDh ? I : H) + nb * 256 + wn * 128 + 32 * i +
                               8 * q + 4 * hi) = a;
