@@ -856,16 +856,19 @@ __device__ __forceinline__ uint32_t mx_quad_encode(const float (&v)[8], uint32_t
 // [B][C][R] with scales [B][C][R/32] (blocks along R).  A workgroup takes 128
 // columns x 256 rows (C a multiple of 128, R of 256) as four 64-row tiles
 // through LDS: every load covers whole 128-byte lines of source rows (the four
-// tiles' loads in flight together), every store 32 bytes of an output row, and
-// each output row's 8 scale bytes leave in one 8-byte store.  With counts,
-// matrices b with counts[b] == 0 are skipped (their copy is left as is).
+// tiles' loads in flight together); the codes of the 128 output rows collect in
+// LDS and leave as whole 128-byte lines (eight lanes per line), and each output
+// row's 8 scale bytes in one 8-byte store.  With counts, matrices b with
+// counts[b] == 0 are skipped (their copy is left as is).
 __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ src,
                                                     const uint8_t* __restrict__ src_s, int R, int C,
                                                     uint8_t* __restrict__ dst,
                                                     uint8_t* __restrict__ dst_s,
                                                     const int* __restrict__ counts, uint32_t okey) {
   constexpr int U = 4;                              // 64-row tiles per workgroup
+  constexpr int kOt = 64 * U + 16;                  // bytes per staged output row (+16: banks)
   __shared__ float tl[128][64 + 1];                 // [c][r]
+  __shared__ __align__(16) uint8_t ot[128 * kOt];   // [c][256 codes]
   __shared__ __align__(8) uint8_t ssc[128][2 * U];  // [c][block of 32 rows]
   const int c0 = permute_item(blockIdx.x, gridDim.x, okey) * 128, r0 = blockIdx.y * 64 * U;
   const size_t b = blockIdx.z;
@@ -883,7 +886,6 @@ __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ 
       sc[u][h] = src_s[row * (C / 32) + (c0 + 16 * q) / 32];
     }
   const int c = tid >> 1, hb = tid & 1;             // encode: out row c, block hb of the tile's 64 rows
-  const size_t orow = b * C + c0 + c;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (u) __syncthreads();                         // the previous tile is read out
@@ -913,15 +915,26 @@ __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ 
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const float* w = val + 16 * g;
-      st16(dst + orow * R + r0 + 64 * u + 32 * hb + 16 * g,
+      *reinterpret_cast<i32x4*>(&ot[c * kOt + 64 * u + 32 * hb + 16 * g]) =
            i32x4{static_cast<int>(f32x4_to_e4m3x4(w[0] * inv, w[1] * inv, w[2] * inv, w[3] * inv)),
                  static_cast<int>(f32x4_to_e4m3x4(w[4] * inv, w[5] * inv, w[6] * inv, w[7] * inv)),
                  static_cast<int>(f32x4_to_e4m3x4(w[8] * inv, w[9] * inv, w[10] * inv, w[11] * inv)),
-                 static_cast<int>(f32x4_to_e4m3x4(w[12] * inv, w[13] * inv, w[14] * inv, w[15] * inv))});
+                 static_cast<int>(f32x4_to_e4m3x4(w[12] * inv, w[13] * inv, w[14] * inv, w[15] * inv))};
     }
     ssc[c][2 * u + hb] = static_cast<uint8_t>(sx + 127);
   }
   __syncthreads();
+  // 128 rows x 256 bytes: lane ln of wave wv stores bytes [16 (ln & 15), +16) of row
+  // 32 wv + 4 s + (ln >> 4), so each store instruction writes four rows' whole lines
+  {
+    const int wv = tid >> 6, ln = tid & 63;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int row = 32 * wv + 4 * s + (ln >> 4), off = 16 * (ln & 15);
+      st16(dst + (b * C + c0 + row) * static_cast<size_t>(R) + r0 + off,
+           *reinterpret_cast<const i32x4*>(&ot[row * kOt + off]));
+    }
+  }
   if (tid < 128)
     *reinterpret_cast<uint2*>(dst_s + (b * C + c0 + tid) * (R / 32) + r0 / 32) =
         *reinterpret_cast<const uint2*>(&ssc[tid][0]);
