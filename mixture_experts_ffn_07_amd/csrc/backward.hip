@@ -377,12 +377,16 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
 // rows per expert) the B tiles are staged during the first row block and stay
 // in LDS (one slot per chunk) for every later row block;
 // each row block's A tile is loaded while the previous block multiplies, and
-// the finished block is written from the accumulators, 16 bytes per lane after
-// neighbouring lanes trade halves (64 contiguous bytes per row per store).
+// the finished block leaves through a small per-wave LDS tile: each store
+// instruction writes eight whole 128-byte row segments (storing straight from
+// the accumulators wrote 64-byte half lines, which the memory system handles
+// at a markedly lower rate).
 template <int KIND>   // kWD, kWG (at most 256 registers: two workgroups per CU)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_wgrad(
     BwdArgs a, uint32_t okey) {
   __shared__ __align__(16) uint16_t lds[4 * 128 * kKC];
+  constexpr int kWs = 128 + 16;                       // bytes per staged output row (+16: banks)
+  __shared__ __align__(16) uint8_t wst[4][16 * kWs];  // per wave: 16 rows x 64 columns, BF16
   uint16_t* const As = lds;                           // [2][128 rows][64 K]
   uint16_t* const Bs = lds + 2 * 128 * kKC;           // [2][128 columns][64 K]
   const int tid = threadIdx.x, ln = tid & 63;
@@ -465,29 +469,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // lane: output row mi*128 + wm*64 + 16i + fr, columns n0 + wn*64 + 16j + 4fg .. +3.
-  // Lanes fg and fg^1 (lane ^ 16) trade halves so that each stores 8 consecutive
-  // columns: the even one those of block j, the odd one those of block j+1.
+  // Per 16-row group i the wave writes its 16 x 64 block into its LDS tile and
+  // reads it back as rows 8s + (ln >> 3), 16-byte chunk ln & 7 (a wave's LDS
+  // operations complete in order, so each read sees the writes before it and
+  // the next group's writes follow the reads).
   auto store_tile = [&](int mi) {
-    const bool odd = fg & 1;
+    uint8_t* st = wst[wv];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint16_t* orow = out + static_cast<size_t>(mi * 128 + wm * 64 + 16 * i + fr) * N + n0 + wn * 64;
 #pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        uint32_t lo[2], hi[2];
-        lo[0] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-        lo[1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-        hi[0] = pack_bf16x2(acc[i][j + 1][0], acc[i][j + 1][1]);
-        hi[1] = pack_bf16x2(acc[i][j + 1][2], acc[i][j + 1][3]);
-        const uint32_t s0 = odd ? lo[0] : hi[0], s1 = odd ? lo[1] : hi[1];
-        const uint32_t r0 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(s0), 16, kWave));
-        const uint32_t r1 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(s1), 16, kWave));
-        const i32x4 v = odd ? i32x4{static_cast<int>(r0), static_cast<int>(r1), static_cast<int>(hi[0]),
-                                    static_cast<int>(hi[1])}
-                            : i32x4{static_cast<int>(lo[0]), static_cast<int>(lo[1]),
-                                    static_cast<int>(r0), static_cast<int>(r1)};
-        const int col = odd ? 16 * (j + 1) + 4 * (fg - 1) : 16 * j + 4 * fg;
-        st16(orow + col, v);
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint2*>(st + fr * kWs + (16 * j + 4 * fg) * 2) =
+            make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int r = 8 * s + (ln >> 3), c = ln & 7;
+        st16(out + static_cast<size_t>(mi * 128 + wm * 64 + 16 * i + r) * N + n0 + wn * 64 + 8 * c,
+             *reinterpret_cast<const i32x4*>(st + r * kWs + 16 * c));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
