@@ -94,6 +94,8 @@ struct BwdArgs {
   uint16_t* dwgu;           // [E, 2I, H]
   uint16_t* dwd;            // [E, H, I]
   int H, I, E, k;
+  int cb0, ncb, ldx;        // kDG with k > 1: column blocks [cb0, cb0 + ncb) of kNT (ncb 0:
+                            // all), written to dxs with row stride ldx from column cb0 * kNT
 };
 
 // Element offset of 16-byte chunk c of LDS row r (rows of kKC elements).
@@ -126,12 +128,13 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
 
   // ---- work item: (M-tile of MT routed rows, 128 output columns) ----
   const int N = KIND == kGU ? 2 * I : (KIND == kDD ? I : H);
-  const int nblk = N / kNT;
+  const int cb0 = KIND == kDG ? a.cb0 : 0;
+  const int nblk = KIND == kDG && a.ncb ? a.ncb : N / kNT;
   const int item0 = real_item(blockIdx.x, nblk, *a.n_tiles);
   if (item0 < 0) return;
   const int item = permute_item(item0, nblk * *a.n_tiles, okey);
   const int tile = item / nblk;
-  const int n0 = (item - tile * nblk) * kNT;
+  const int n0 = (cb0 + item - tile * nblk) * kNT;
   const int2 te = a.tiles[tile];
   const int e = te.x;
   const int mcount = min(MT, a.counts[e] - te.y);
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
       } else {   // kDG
         if (live) {
           if (k > 1) {
-            float* dst = a.dxs + grow * H + n0 + 8 * sg;
+            float* dst = a.dxs + grow * a.ldx + (n0 - cb0 * kNT) + 8 * sg;
             *reinterpret_cast<f32x4*>(dst) = c0;
             *reinterpret_cast<f32x4*>(dst + 4) = c1;
           } else {
@@ -538,18 +541,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// dx[t] = sum_j dxs[row of (t, j)] in slot order (FP32), rounded once to BF16.
+// dx[t] = sum_j dxs[row of (t, j)] in slot order (FP32), rounded once to BF16;
+// a launch covers dx columns [col0, col0 + cols), dxs holding them with row
+// stride ldx from its column 0.
 __global__ __launch_bounds__(256) void sum_pairs(const float* __restrict__ dxs,
                                                  const int* __restrict__ row_of, int T, int H, int k,
-                                                 uint16_t* __restrict__ dx, uint32_t okey) {
+                                                 uint16_t* __restrict__ dx, uint32_t okey, int col0,
+                                                 int cols, int ldx) {
   const int t = permute_item(blockIdx.x, gridDim.x, okey);
   const int P = T * k;
-  for (int c = threadIdx.x; c < H / 4; c += blockDim.x) {
+  dx += col0;
+  for (int c = threadIdx.x; c < cols / 4; c += blockDim.x) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int row = row_of[t * k + j];
       if (static_cast<unsigned>(row) >= static_cast<unsigned>(P)) continue;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(dxs + static_cast<size_t>(row) * H + 4 * c);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(dxs + static_cast<size_t>(row) * ldx + 4 * c);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] += v[i];
     }
@@ -787,12 +794,30 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
     err = launch_dgrad_large(a.dgu, wgu, a.perm, tiles256, n_tiles256, a.counts, a.offsets, H,
                              2 * I, k, a.dxs, dx, partial, L.max_tiles256, num_cus, s);
     if (err != hipSuccess) return err;
-  } else if (tall) {
-    hipLaunchKernelGGL((bwd_gemm<kDG, 128>), grid_tiles(H), dim3(256), 0, s, a, order_key());
   } else {
-    hipLaunchKernelGGL((bwd_gemm<kDG, 64>), grid_tiles(H), dim3(256), 0, s, a, order_key());
+    // column parts (column_parts): each part's FP32 per-pair slice is summed right
+    // after its launch, while it is still in the last-level cache (T 2048, k 8,
+    // H 7168: 7 parts; 64-row tiles run three workgroups per CU, 128-row tiles two)
+    const int parts = k > 1 ? column_parts(static_cast<size_t>(P), H, kNT, L.max_tiles,
+                                           (tall ? 8 : 12) * num_cus)
+                            : 1;
+    const int hq = H / parts;
+    for (int q = 0; q < parts; ++q) {
+      BwdArgs ap = a;
+      ap.cb0 = q * (hq / kNT);
+      ap.ncb = hq / kNT;
+      ap.ldx = hq;
+      const dim3 g(static_cast<unsigned>((hq / kNT * L.max_tiles + kXcds - 1) / kXcds * kXcds));
+      if (tall) hipLaunchKernelGGL((bwd_gemm<kDG, 128>), g, dim3(256), 0, s, ap, order_key());
+      else hipLaunchKernelGGL((bwd_gemm<kDG, 64>), g, dim3(256), 0, s, ap, order_key());
+      if (k > 1)
+        hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, a.dxs, row_of, T, H, k, dx,
+                           order_key(), q * hq, hq, hq);
+    }
   }
-  if (k > 1) hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, a.dxs, row_of, T, H, k, dx, order_key());
+  if (L.large_d && k > 1)
+    hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, a.dxs, row_of, T, H, k, dx, order_key(),
+                       0, H, H);
   prof_end(kBwdInput, s);
   if (L.large_w) {
     err = launch_wgrad_large(x, dout, a.dgu, a.wa, a.perm, a.counts, a.offsets, P, H, I, E, k,
@@ -1174,7 +1199,9 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
                               counts, offsets, H, 2 * I, k, PF(L.dxs), dx, partial, L.max_tiles,
                               num_cus, s);
   if (err != hipSuccess) return err;
-  if (k > 1) hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, PF(L.dxs), row_of, T, H, k, dx, order_key());
+  if (k > 1)
+    hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, PF(L.dxs), row_of, T, H, k, dx, order_key(),
+                       0, H, H);
   prof_end(kBwdInput, s);
   // weight gradients over pair-axis operands (the segment timed as dw_gate_up
   // covers the pair-axis encodings and both weight gradients' single launch)

@@ -772,32 +772,17 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
   return hipGetLastError();
 }
 
-// The small-tile down projection and the combine run in column parts when k > 1:
-// part q's down launch writes the FP32 slot values of its H / parts output
-// columns into the head of the slot buffer (row stride H / parts), and the
-// combine of those columns reads them right after; the next part overwrites the
-// same bytes.  A part of at most kYPartBytes stays in the 256 MB last-level
-// cache between its write and its read, instead of mixing ~470 MB of slot
-// writes (T 2048, k 8, H 7168) into the weight stream.  Each part is a launch of
-// its own with its own tail, so parts keep at least four rounds of workgroups
-// (by the tile bound max_tiles).  Measured down + combine, T 2048, k 8: H 7168
-// E 384 BF16 2,245 -> 2,128 us (7 parts; 4: 2,180; 14: 2,137; 28: 2,400), whole
-// forward step 5.74 -> 5.65 ms; H 6144 E 256 BF16 128-row tiles 1,390 -> 1,360 us
-// (4 parts; 3: 1,345; 6: 1,460).  The MXFP8 down (16-wave workgroups, one per
-// CU) stays whole: at H 7168 I 3072 its 7-part form, faster alone (1,713 ->
-// 1,650 us), made the whole step slower (4.64 -> 4.68 ms; 2 parts 4.72).
-constexpr size_t kYPartBytes = size_t(72) << 20;
-static int down_parts(size_t P, int H, int cw, int max_tiles, int min_items) {
-  const int nblk = H / cw;
-  int parts = 1;
-  for (int q = 1; q <= nblk; ++q) {
-    if (nblk % q) continue;
-    if (static_cast<int64_t>(nblk / q) * max_tiles < min_items) break;
-    parts = q;
-    if (P * static_cast<size_t>(H / q) * sizeof(float) <= kYPartBytes) break;
-  }
-  return parts;
-}
+// The small-tile down projection and the combine run in column parts when k > 1
+// (column_parts): part q's down launch writes the FP32 slot values of its
+// H / parts output columns into the head of the slot buffer (row stride
+// H / parts), and the combine of those columns reads them right after.
+// Measured down + combine, T 2048, k 8: H 7168 E 384 BF16 2,245 -> 2,128 us (7
+// parts; 4: 2,180; 14: 2,137; 28: 2,400, the per-launch tails taking over),
+// whole forward step 5.74 -> 5.65 ms; H 6144 E 256 BF16 128-row tiles
+// 1,390 -> 1,360 us (4 parts; 3: 1,345; 6: 1,460).  The MXFP8 down (16-wave
+// workgroups, one per CU) stays whole: at H 7168 I 3072 its 7-part form, faster
+// alone (1,713 -> 1,650 us), made the whole step slower (4.64 -> 4.68 ms; 2
+// parts 4.72).
 
 hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
                                const uint8_t* wds, const int32_t* idx, const float* w, int T,
@@ -835,7 +820,7 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   const int dims = wide ? 512 : 256;
   // BF16 (two 8-wave workgroups per CU): four rounds are 8 * num_cus items
   const int parts = k > 1 && dtype == 0
-                        ? down_parts(static_cast<size_t>(T) * k, H, dims, L.max_tiles, 8 * num_cus)
+                        ? column_parts(static_cast<size_t>(T) * k, H, dims, L.max_tiles, 8 * num_cus)
                         : 1;
   const int hq = H / parts, ncb = hq / dims;
   const dim3 grid(round_up(ncb * L.max_tiles, kXcds)), block(2 * dims);

@@ -38,6 +38,27 @@ inline void prof_end(int id, hipStream_t s) {
   const ProfileHook& h = profile_hook();
   if (h.kernel == id && h.stop) (void)hipEventRecord(h.stop, s);
 }
+// Column parts of a grouped GEMM that writes FP32 per-pair rows (rows x cols)
+// for a fixed-order slot sum that reads them right after: the sum runs after
+// each part's launch, and a part's slice (at most kYPartBytes, rewritten in
+// place by the next part) stays in the 256 MB last-level cache between its
+// write and its read instead of mixing the whole buffer's writes into the
+// weight stream.  Each part is a launch of its own with its own tail, so parts
+// keep at least min_items workgroups (cw: columns per workgroup item; max_tiles
+// bounds the M-tiles).  Returns the part count (1: one launch).
+constexpr size_t kYPartBytes = size_t(72) << 20;
+inline int column_parts(size_t rows, int cols, int cw, int max_tiles, int min_items) {
+  const int nblk = cols / cw;
+  int parts = 1;
+  for (int q = 1; q <= nblk; ++q) {
+    if (nblk % q) continue;
+    if (static_cast<int64_t>(nblk / q) * max_tiles < min_items) break;
+    parts = q;
+    if (rows * static_cast<size_t>(cols / q) * sizeof(float) <= kYPartBytes) break;
+  }
+  return parts;
+}
+
 enum KernelId { kRoute = 1, kDecGateUp = 2, kDecDown = 3, kGroup = 4, kQuant = 5,
                 kGemmGateUp = 6, kGemmDown = 7, kCombine = 8, kBwdGateUp = 9, kBwdDown = 10,
                 kBwdInput = 11, kBwdWDown = 12, kBwdWGateUp = 13, kDecFused = 14,
