@@ -1217,8 +1217,11 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
                      counts, offsets, koff, E, P8(L.xT), P8(L.xTs), order_key());
   hipLaunchKernelGGL(mx_pair_t<2>, dim3(gb, 2 * I / 64), dim3(256), 0, s, nullptr, PF(L.dgu), 2 * I,
                      perm, w, k, counts, offsets, koff, E, P8(L.dguT), P8(L.dguTs), order_key());
+  // experts averaging at most one 128-pair K stage: 128 x 128 tiles, several workgroups
+  // per CU; longer pair runs keep the 256 x 256 tile and its pipelined K loop
+  const bool small = static_cast<int64_t>(T) * k <= 128LL * E;
   err = launch_wgrad_large_mx(P8(L.aT), P8(L.aTs), P8(L.dyT), P8(L.dyTs), P8(L.xT), P8(L.xTs),
-                              P8(L.dguT), P8(L.dguTs), koff, H, I, E, dwgu, dwd, num_cus, s);
+                              P8(L.dguT), P8(L.dguTs), koff, H, I, E, dwgu, dwd, small, num_cus, s);
   prof_end(kBwdWGateUp, s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_bwd, dim3(T), dim3(64), 0, s, PF(L.dwp), row_of, idx, w, T, E, k, I / kNT,

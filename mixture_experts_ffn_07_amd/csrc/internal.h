@@ -209,8 +209,8 @@ hipError_t launch_dgrad_large_mx(const uint8_t* aq, const uint8_t* as, const uin
 hipError_t launch_wgrad_large_mx(const uint8_t* aT, const uint8_t* aTs, const uint8_t* dyT,
                                  const uint8_t* dyTs, const uint8_t* xT, const uint8_t* xTs,
                                  const uint8_t* dguT, const uint8_t* dguTs, const int* koff,
-                                 int H, int I, int E, uint16_t* dwgu, uint16_t* dwd, int ncu,
-                                 hipStream_t s);
+                                 int H, int I, int E, uint16_t* dwgu, uint16_t* dwd, bool small,
+                                 int ncu, hipStream_t s);
 hipError_t launch_koff_mx(const int* counts, int E, int* koff, hipStream_t s);
 
 // gu: NULL, or (BF16, small groups only) [T*k, 2I] FP32 pre-activations out, slot order
