@@ -928,87 +928,98 @@ __global__ __launch_bounds__(256) void gemm_large_mx_fixup_gate_up(
 
 // Weight gradients of experts averaging at most 128 routed pairs (the MXFP8
 // backward at T 2048, k 8, E 384: one K stage per expert): 128 x 128 dW tiles,
-// four waves of 64 x 64, so that four workgroups share a CU (64 accumulator
-// registers per lane, 36 KB of LDS) and one workgroup's loads, products and dW
-// stores overlap the others' - the 256 x 256 tile of gemm_large_mx runs one
-// workgroup per CU, which waits for its loads and drains its stores with
-// nothing else to do.  Operands and products as gemm_large_mx's weight-gradient
-// kinds (`bm`: its act, B rows = dW rows; `am`: its wt, A rows = dW columns; the
-// same block-scaled 32x32x64 MFMA on the same fragments), so the result is
-// bit-identical; experts with more than one stage take them one at a time.
-// The finished 64 x 64 block of a wave leaves through LDS as eight whole
-// 128-byte row segments per store instruction.
+// four waves of 64 x 64 (64 accumulator registers per lane, so two workgroups
+// share a CU - the 256 x 256 tile of gemm_large_mx runs one per CU, which waits
+// for its loads and drains its stores with nothing else to do).  A workgroup
+// takes one 128-row block of B (dW rows) and kW1Run consecutive 128-row blocks
+// of A (dW columns): for a single-stage expert the B block stays in LDS, and the
+// next A block's loads fly while the current block multiplies and its dW block
+// is stored.  Operands and products as gemm_large_mx's weight-gradient kinds
+// (`bm`: its act, B rows = dW rows; `am`: its wt, A rows = dW columns; the same
+// block-scaled 32x32x64 MFMA on the same fragments, K steps in the same order),
+// so the result is bit-identical; experts with more than one stage take each A
+// block's stages one at a time.  A wave's finished 64 x 64 block leaves through
+// its own LDS region as eight whole 128-byte row segments per store instruction.
+constexpr int kW1Run = 4;                                  // A blocks per workgroup
 constexpr int kW1Tile = 128 * kMBK;                        // bytes per operand stage
 constexpr int kW1Row = 128 + 16;                           // bytes per staged dW row (+16: banks)
-constexpr int kW1Lds = 4 * 64 * kW1Row > 2 * kW1Tile + 2 * 128 * 4 ? 4 * 64 * kW1Row
-                                                                    : 2 * kW1Tile + 2 * 128 * 4;
+constexpr int kW1Stage = 2 * kW1Tile + 2 * 128 * 4;        // A, B codes and their scale dwords
+constexpr int kW1Lds = kW1Stage + 4 * 64 * kW1Row;         // + dW staging: 69 KB
 template <int KIND>
 __global__ __launch_bounds__(256) void wgrad_mx_t128(
     const uint8_t* __restrict__ bm, const uint8_t* __restrict__ bms, const uint8_t* __restrict__ am,
     const uint8_t* __restrict__ ams, const int* __restrict__ offsets, int H, int I, int E,
     uint16_t* __restrict__ out, uint32_t okey) {
   static_assert(KIND == kWgradGateUp || KIND == kWgradDown, "weight-gradient kinds");
-  __shared__ __align__(16) uint8_t ldm[kW1Lds];     // [A, B][128 x 128], [A, B][128] dwords; dW staging
+  extern __shared__ __align__(16) uint8_t ldm[];    // [A, B][128 x 128], [A, B][128] dwords; dW staging
   uint32_t* lsc = reinterpret_cast<uint32_t*>(ldm + 2 * kW1Tile);
   const int K = offsets[E];                          // row stride of both operands
   const int KSB = K / 32;
-  const int nA = KIND == kWgradGateUp ? H / 128 : I / 128;
+  const int nA = KIND == kWgradGateUp ? H / 128 : I / 128;   // a multiple of kW1Run
   const int nB = KIND == kWgradGateUp ? 2 * I / 128 : H / 128;
-  const int per = nA * nB, n_w = E * per;
+  const int nG = nA / kW1Run;
+  const int per = nG * nB, n_w = E * per;
   const int n_pad = (n_w + kXcds - 1) / kXcds * kXcds;
   const int L = blockIdx.x;
   if (L >= n_pad) return;
   const int item = permute_item(xcd_item(L, n_pad), n_pad, okey);
   if (item >= n_w) return;
   const int e = item / per;
-  int bb, nb;
-  large_coords(item - e * per, nA, nB, bb, nb);
+  int bb, ng;
+  large_coords(item - e * per, nG, nB, bb, ng);
   const int kb = offsets[e] / kMBK, ke = offsets[e + 1] / kMBK;
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, l32 = ln & 31, hi = ln >> 5;
   const int wm = wv & 1, wn = wv >> 1;               // B rows 64 wm .., A rows 64 wn ..
-  // loader: chunk u = tid + 256 i of each operand -> row u >> 3, 16-byte chunk u & 7,
-  // LDS slot (u & 7) ^ (row & 7)
-  uint32_t ao[4], bo[4];
+  // loader: chunk u = tid + 256 i of an operand block -> row u >> 3, 16-byte chunk
+  // u & 7, LDS slot (u & 7) ^ (row & 7); scale dwords: thread tid < 128 the A
+  // block's row tid, the others the B block's row tid - 128
+  uint32_t ro[4];
   int lw[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = tid + 256 * i, r = u >> 3, c = u & 7;
-    ao[i] = static_cast<uint32_t>((nb * 128 + r) * K + c * 16);
-    bo[i] = static_cast<uint32_t>((bb * 128 + r) * K + c * 16);
+    ro[i] = static_cast<uint32_t>(r * K + c * 16);
     lw[i] = r * kMBK + ((c ^ (r & 7)) * 16);
   }
-  const uint32_t so = static_cast<uint32_t>((tid < 128 ? nb * 128 + tid : bb * 128 + tid - 128) * KSB);
-  const uint8_t* ssrc = tid < 128 ? ams : bms;
-  i32x4 sa[4], sb[4];
-  uint32_t ss;
-  auto load = [&](int kt) {
-    const uint32_t kk = static_cast<uint32_t>(kt * kMBK);
+  const bool sa_lane = tid < 128;
+  const uint32_t b_off = static_cast<uint32_t>(bb * 128 * K);
+  i32x4 ra[4], rb[4];
+  uint32_t rs;
+  auto load_a = [&](int nb, int kt) {               // A block nb, stage kt (and, tid < 128, its scales)
+    const uint8_t* p = am + static_cast<uint32_t>(nb * 128 * K) + static_cast<uint32_t>(kt * kMBK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = ld16(am + ao[i] + kk);
+    for (int i = 0; i < 4; ++i) ra[i] = ld16(p + ro[i]);
+    if (sa_lane) rs = *reinterpret_cast<const uint32_t*>(ams + static_cast<uint32_t>((nb * 128 + tid) * KSB + kt * 4));
+  };
+  auto load_b = [&](int kt) {                       // B block, stage kt (and, tid >= 128, its scales)
+    const uint8_t* p = bm + b_off + static_cast<uint32_t>(kt * kMBK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sb[i] = ld16(bm + bo[i] + kk);
-    ss = *reinterpret_cast<const uint32_t*>(ssrc + so + static_cast<uint32_t>(kt * 4));
+    for (int i = 0; i < 4; ++i) rb[i] = ld16(p + ro[i]);
+    if (!sa_lane) rs = *reinterpret_cast<const uint32_t*>(bms + static_cast<uint32_t>((bb * 128 + tid - 128) * KSB + kt * 4));
+  };
+  auto put_a = [&] {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(&ldm[lw[i]]) = ra[i];
+    if (sa_lane) lsc[tid] = rs;
+  };
+  auto put_b = [&] {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(&ldm[kW1Tile + lw[i]]) = rb[i];
+    if (!sa_lane) lsc[tid] = rs;
   };
   f32x16 acc[2][2];
+  auto zero = [&] {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  };
   // fragments: A rows 64 wn + 32 i + l32, B rows 64 wm + 32 j + l32 (gemm_large_mx's
-  // A / B pieces: at K step ks lane hi takes chunks 4 ks + hi and 4 ks + 2 + hi)
+  // pieces: at K step ks lane hi takes chunks 4 ks + hi and 4 ks + 2 + hi)
   const int swz = l32 & 7;
-  if (ke > kb) load(kb);
-  for (int kt = kb; kt < ke; ++kt) {
-    if (kt > kb) __syncthreads();                   // every wave is done reading stage kt - 1
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(&ldm[lw[i]]) = sa[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(&ldm[kW1Tile + lw[i]]) = sb[i];
-    lsc[tid] = ss;                                  // [A 128][B 128] scale dwords
-    if (kt + 1 < ke) load(kt + 1);
-    __syncthreads();
+  auto multiply = [&] {
     uint32_t sc[4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) sc[i] = lsc[64 * wn + 32 * i + l32] >> (8 * hi);
@@ -1035,28 +1046,67 @@ __global__ __launch_bounds__(256) void wgrad_mx_t128(
           acc[i][j] = mfma_mx32<2>(f[i], f[2 + j], static_cast<int>(sc[i]), static_cast<int>(sc[2 + j]), acc[i][j]);
       }
     }
-  }
+  };
   // dW[e][B row][A row], BF16: lane (l32, hi) holds A row (dW column) 32 i + 8 q + 4 hi + t
   // and B row (dW row) 32 j + l32 of the wave's block (register 4 q + t of acc[i][j])
-  __syncthreads();                                  // every wave is done with the stage
-  uint8_t* st = ldm + wv * 64 * kW1Row;
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint2*>(st + (32 * j + l32) * kW1Row + (32 * i + 8 * q + 4 * hi) * 2) =
-            make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                       pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-  // a wave's LDS operations complete in order: the reads see the writes above
   const int cols = nA * 128;
-  uint16_t* dw = out + static_cast<size_t>(e) * (nB * 128) * cols;
+  uint16_t* dw = out + static_cast<size_t>(e) * (nB * 128) * cols + static_cast<size_t>(bb * 128 + 64 * wm) * cols;
+  uint8_t* st = ldm + kW1Stage + wv * 64 * kW1Row;
+  auto store = [&](int nb) {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int r = 8 * s + (ln >> 3), c = ln & 7;
-    st16(dw + static_cast<size_t>(bb * 128 + 64 * wm + r) * cols + nb * 128 + 64 * wn + 8 * c,
-         *reinterpret_cast<const i32x4*>(st + r * kW1Row + 16 * c));
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(st + (32 * j + l32) * kW1Row + (32 * i + 8 * q + 4 * hi) * 2) =
+              make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                         pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+    // a wave's LDS operations complete in order: the reads see the writes above
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int r = 8 * s + (ln >> 3), c = ln & 7;
+      st16(dw + static_cast<size_t>(r) * cols + nb * 128 + 64 * wn + 8 * c,
+           *reinterpret_cast<const i32x4*>(st + r * kW1Row + 16 * c));
+    }
+  };
+
+  const int nb0 = ng * kW1Run;
+  zero();
+  if (ke - kb == 1) {
+    // the B block stays in LDS; A block m + 1 is loaded while block m multiplies
+    // and is stored
+    load_b(kb);
+    put_b();
+    load_a(nb0, kb);
+    put_a();
+    load_a(nb0 + 1, kb);
+    __syncthreads();
+    for (int m = 0; m < kW1Run; ++m) {
+      multiply();
+      __syncthreads();                              // every wave is done reading A block m
+      if (m + 1 < kW1Run) {
+        put_a();
+        if (m + 2 < kW1Run) load_a(nb0 + m + 2, kb);
+      }
+      store(nb0 + m);
+      zero();
+      __syncthreads();                              // A block m + 1 is in LDS
+    }
+  } else {
+    for (int m = 0; m < kW1Run; ++m) {
+      for (int kt = kb; kt < ke; ++kt) {
+        load_b(kt);
+        load_a(nb0 + m, kt);
+        __syncthreads();                            // every wave is done reading the last stage
+        put_b();
+        put_a();
+        __syncthreads();
+        multiply();
+      }
+      store(nb0 + m);                               // (an expert with no pairs: zeros)
+      zero();
+    }
   }
 }
 
@@ -1190,13 +1240,14 @@ hipError_t launch_wgrad_large_mx(const uint8_t* aT, const uint8_t* aTs, const ui
                                  const uint8_t* dguT, const uint8_t* dguTs, const int* koff,
                                  int H, int I, int E, uint16_t* dwgu, uint16_t* dwd, bool small,
                                  int ncu, hipStream_t s) {
-  if (small) {                                     // 128 x 128 tiles, four workgroups per CU
-    const int nd1 = (E * (I / 128) * (H / 128) + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL(wgrad_mx_t128<kWgradDown>, dim3(nd1), dim3(256), 0, s, dyT, dyTs, aT, aTs,
-                       koff, H, I, E, dwd, order_key());
-    const int ng1 = (E * (H / 128) * (2 * I / 128) + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL(wgrad_mx_t128<kWgradGateUp>, dim3(ng1), dim3(256), 0, s, dguT, dguTs, xT,
-                       xTs, koff, H, I, E, dwgu, order_key());
+  // 128 x 128 tiles, two workgroups per CU (runs of kW1Run A blocks: H and I multiples of 512)
+  if (small && (I / 128) % kW1Run == 0 && (H / 128) % kW1Run == 0) {
+    const int nd1 = (E * (I / 128 / kW1Run) * (H / 128) + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL(wgrad_mx_t128<kWgradDown>, dim3(nd1), dim3(256), kW1Lds, s, dyT, dyTs, aT,
+                       aTs, koff, H, I, E, dwd, order_key());
+    const int ng1 = (E * (H / 128 / kW1Run) * (2 * I / 128) + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL(wgrad_mx_t128<kWgradGateUp>, dim3(ng1), dim3(256), kW1Lds, s, dguT, dguTs,
+                       xT, xTs, koff, H, I, E, dwgu, order_key());
     return hipGetLastError();
   }
   const int nd = (E * (I / 256) * (H / 256) + kXcds - 1) / kXcds * kXcds;
@@ -1398,6 +1449,10 @@ hipError_t large_set_attributes() {
                           reinterpret_cast<const void*>(gemm_large_mx<kWgradGateUp>)};
   for (const void* f : mx_bwd)
     if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
+  const void* t128[] = {reinterpret_cast<const void*>(wgrad_mx_t128<kWgradDown>),
+                        reinterpret_cast<const void*>(wgrad_mx_t128<kWgradGateUp>)};
+  for (const void* f : t128)
+    if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kW1Lds);
   return e;
 }
 

@@ -95,6 +95,29 @@ def test_backward_mx_shapes(M, T, H, I, E, k):
     _check(M, _custom(T, H, I, E, k, seed=T + E), f"mx bwd T={T} k={k}")
 
 
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (200, 512, 512, 8, 2),      # ~50 pairs per expert, H and I multiples of 512: the weight
+    (160, 1024, 512, 16, 4),    # gradients on 128 x 128 tiles in runs of four column blocks
+])
+def test_backward_mx_small_pair_tiles(M, T, H, I, E, k):
+    _check(M, _custom(T, H, I, E, k, seed=T + 7 * E), f"mx bwd small-pair tiles T={T} E={E}")
+
+
+def test_backward_mx_small_pair_tiles_long_expert(M):
+    # ~75 pairs per expert on average, but one expert holds (nearly) every token (~300
+    # pairs: three K stages of 128, taken one at a time by the 128 x 128 weight-gradient
+    # kernel).  The bias keeps its routing weight well below 1: at w = 1 - 1e-13 (a
+    # logit of 30) FP32 rounds w to exactly 1 and the FP64 oracle does not, so block
+    # amax values that are powers of two (BF16 dout) flip their E8M0 scale.
+    d = _custom(300, 512, 512, 8, 2, seed=41)
+    lg = d["logits"].clone()
+    lg[:, 5] += 6.0
+    d["logits"] = lg.contiguous()
+    idx, _ = route(d["logits"].cpu().numpy(), 2)
+    assert np.count_nonzero(idx == 5) > 256 and idx.size <= 128 * 8   # 3 stages; average <= 128
+    _check(M, d, "mx bwd small-pair tiles, one expert with 300 pairs")
+
+
 def test_backward_mx_empty_expert(M):
     d = _custom(800, 256, 256, 4, 2, seed=31)
     lg = d["logits"].clone()
