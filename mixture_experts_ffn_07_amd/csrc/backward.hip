@@ -1144,6 +1144,9 @@ MxBackwardWs mx_backward_ws_layout(int T, int H, int I, int E, int k) {
   L.xTs = o;      o = a256(o + static_cast<size_t>(H) * L.kpt_max / 32);
   L.dguT = o;     o = a256(o + static_cast<size_t>(2 * I) * L.kpt_max);
   L.dguTs = o;    o = a256(o + static_cast<size_t>(2 * I) * L.kpt_max / 32);
+  L.max_tiles64 = static_cast<int>(E + (P + 63) / 64);
+  L.n_tiles64 = o; o += 256;
+  L.tiles64 = o;  o = a256(o + sizeof(int) * 2 * L.max_tiles64);
   L.total = o;
   return L;
 }
@@ -1193,11 +1196,24 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
                      perm, w, P, I, PF(L.a), PF(L.dgu), P8(L.dguq), P8(L.dgus), PF(L.dwp),
                      order_key());
   prof_end(kBwdDown, s);
-  // dx
+  // dx.  Experts averaging fewer than 256 routed pairs (k > 1): the batched down kernel on
+  // 64-row tiles streams W_gate_up^T with whole-line loads, FP32 per grouped row into dxs
+  // (T 2048, k 8, E 384: the whole backward 32.6 -> 32.0 ms; the 256-row tile spends most of
+  // its rows on padding)
   prof_begin(kBwdInput, s);
-  err = launch_dgrad_large_mx(P8(L.dguq), P8(L.dgus), P8(L.wguT), P8(L.wguTs), perm, tiles, n_tiles,
-                              counts, offsets, H, 2 * I, k, PF(L.dxs), dx, partial, L.max_tiles,
-                              num_cus, s);
+  if (k > 1 && static_cast<int64_t>(P) < static_cast<int64_t>(kLargeBM) * E) {
+    int2* tiles64 = reinterpret_cast<int2*>(b + L.tiles64);
+    int* n_tiles64 = reinterpret_cast<int*>(b + L.n_tiles64);
+    err = launch_group_experts(idx, P, E, 64, counts, offsets, tiles64, n_tiles64, perm, row_of, s);
+    if (err == hipSuccess)
+      err = launch_mx_rows_down(P8(L.dguq), P8(L.dgus), P8(L.wguT), P8(L.wguTs), perm, tiles64,
+                                n_tiles64, L.max_tiles64, counts, offsets, H, 2 * I, k, PF(L.dxs), s,
+                                num_cus);
+  } else {
+    err = launch_dgrad_large_mx(P8(L.dguq), P8(L.dgus), P8(L.wguT), P8(L.wguTs), perm, tiles, n_tiles,
+                                counts, offsets, H, 2 * I, k, PF(L.dxs), dx, partial, L.max_tiles,
+                                num_cus, s);
+  }
   if (err != hipSuccess) return err;
   if (k > 1)
     hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, PF(L.dxs), row_of, T, H, k, dx, order_key(),

@@ -857,6 +857,26 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
   return hipGetLastError();
 }
 
+hipError_t launch_mx_rows_down(const uint8_t* act, const uint8_t* acts, const uint8_t* wt,
+                               const uint8_t* wts, const int* perm, const int2* tiles,
+                               const int* n_tiles, int max_tiles, const int* counts,
+                               const int* offsets, int N, int K, int k, float* y, hipStream_t s,
+                               int num_cus) {
+  // as the MXFP8 down projection of launch_down_batched (N plays H, K plays I)
+  const bool wide = N % 512 == 0 && (N / 512) * max_tiles >= 4 * num_cus;
+  const int dims = wide ? 512 : 256;
+  const dim3 grid(round_up((N / dims) * max_tiles, kXcds)), block(2 * dims);
+  if (wide)
+    hipLaunchKernelGGL((gemm_mx_s<kProjDown, 16>), grid, block, 0, s, act, acts, wt, wts, perm, tiles,
+                       n_tiles, counts, offsets, nullptr, N, K, k, nullptr, nullptr, y, nullptr,
+                       order_key(), 0, N / dims, N);
+  else
+    hipLaunchKernelGGL((gemm_mx_s<kProjDown, 8>), grid, block, 0, s, act, acts, wt, wts, perm, tiles,
+                       n_tiles, counts, offsets, nullptr, N, K, k, nullptr, nullptr, y, nullptr,
+                       order_key(), 0, N / dims, N);
+  return hipGetLastError();
+}
+
 hipError_t launch_group_experts(const int32_t* idx, int P, int E, int BM, int* counts, int* offsets,
                                 int2* tiles, int* n_tiles, int* perm, int* row_of, hipStream_t s) {
   prof_begin(kGroup, s);

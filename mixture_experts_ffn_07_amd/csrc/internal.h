@@ -180,9 +180,9 @@ hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* co
 struct MxBackwardWs {
   size_t n_tiles, counts, offsets, tiles, perm, row_of, koff, xq, xs, dq, ds, wdT, wdTs, wguT,
       wguTs, gu, dh, a, dgu, dguq, dgus, dwp, dxs, partial, aT, aTs, dyT, dyTs, xT, xTs, dguT,
-      dguTs, total;
+      dguTs, n_tiles64, tiles64, total;
   size_t kpt_max;
-  int max_tiles;
+  int max_tiles, max_tiles64;
 };
 MxBackwardWs mx_backward_ws_layout(int T, int H, int I, int E, int k);
 hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8_t* wgus,
@@ -219,6 +219,14 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
                                   int E, int k, int dtype, void* h, uint8_t* hs, void* ws,
                                   hipStream_t s, int num_cus, float* gu = nullptr);
 
+// MXFP8 grouped rows x weights^T with FP32 per-row output (the batched down kernel
+// on 64-row tiles): y[row][n] = sum_k act[row][k] wt[e][n][k] for the grouped rows
+// of each expert, act [P][K] codes + scales [P][K/32], wt [E][N][K] + [E][N][K/32].
+hipError_t launch_mx_rows_down(const uint8_t* act, const uint8_t* acts, const uint8_t* wt,
+                               const uint8_t* wts, const int* perm, const int2* tiles,
+                               const int* n_tiles, int max_tiles, const int* counts,
+                               const int* offsets, int N, int K, int k, float* y, hipStream_t s,
+                               int num_cus);
 hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
                                const uint8_t* wds, const int32_t* idx, const float* w, int T,
                                int H, int I, int E, int k, int dtype, uint16_t* out, void* ws,
