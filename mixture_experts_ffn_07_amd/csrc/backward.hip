@@ -1188,27 +1188,34 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
                                     offsets, H, I, k, PF(L.gu), partial, L.max_tiles, num_cus, s);
   prof_end(kBwdGateUp, s);
   if (err != hipSuccess) return err;
+  // Experts averaging fewer than 256 routed pairs: dh and dx on the batched MXFP8 kernel's
+  // 64-row tiles (whole-line weight streams; the 256-row tile spends most of its rows on
+  // padding there), over a second tiling of the same grouping
+  const bool rows64 = static_cast<int64_t>(P) < static_cast<int64_t>(kLargeBM) * E;
+  int2* tiles64 = reinterpret_cast<int2*>(b + L.tiles64);
+  int* n_tiles64 = reinterpret_cast<int*>(b + L.n_tiles64);
   prof_begin(kBwdDown, s);
-  err = launch_dh_large_mx(P8(L.dq), P8(L.ds), P8(L.wdT), P8(L.wdTs), perm, tiles, n_tiles, counts,
-                           offsets, H, I, k, PF(L.dh), partial, L.max_tiles, num_cus, s);
+  if (rows64) {
+    err = launch_group_experts(idx, P, E, 64, counts, offsets, tiles64, n_tiles64, perm, row_of, s);
+    if (err == hipSuccess)
+      err = launch_mx_rows_gather(P8(L.dq), P8(L.ds), P8(L.wdT), P8(L.wdTs), perm, tiles64, n_tiles64,
+                                  L.max_tiles64, counts, offsets, H, I, k, PF(L.dh), s, num_cus);
+  } else {
+    err = launch_dh_large_mx(P8(L.dq), P8(L.ds), P8(L.wdT), P8(L.wdTs), perm, tiles, n_tiles, counts,
+                             offsets, H, I, k, PF(L.dh), partial, L.max_tiles, num_cus, s);
+  }
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(mx_dh_finish, dim3((P + 15) / 16, I / kNT), dim3(256), 0, s, PF(L.gu), PF(L.dh),
                      perm, w, P, I, PF(L.a), PF(L.dgu), P8(L.dguq), P8(L.dgus), PF(L.dwp),
                      order_key());
   prof_end(kBwdDown, s);
-  // dx.  Experts averaging fewer than 256 routed pairs (k > 1): the batched down kernel on
-  // 64-row tiles streams W_gate_up^T with whole-line loads, FP32 per grouped row into dxs
-  // (T 2048, k 8, E 384: the whole backward 32.6 -> 32.0 ms; the 256-row tile spends most of
-  // its rows on padding)
+  // dx (rows64, k > 1: FP32 per grouped row into dxs, then the slot sum; T 2048, k 8, E 384:
+  // the whole backward 32.6 -> 32.0 ms)
   prof_begin(kBwdInput, s);
-  if (k > 1 && static_cast<int64_t>(P) < static_cast<int64_t>(kLargeBM) * E) {
-    int2* tiles64 = reinterpret_cast<int2*>(b + L.tiles64);
-    int* n_tiles64 = reinterpret_cast<int*>(b + L.n_tiles64);
-    err = launch_group_experts(idx, P, E, 64, counts, offsets, tiles64, n_tiles64, perm, row_of, s);
-    if (err == hipSuccess)
-      err = launch_mx_rows_down(P8(L.dguq), P8(L.dgus), P8(L.wguT), P8(L.wguTs), perm, tiles64,
-                                n_tiles64, L.max_tiles64, counts, offsets, H, 2 * I, k, PF(L.dxs), s,
-                                num_cus);
+  if (rows64 && k > 1) {
+    err = launch_mx_rows_down(P8(L.dguq), P8(L.dgus), P8(L.wguT), P8(L.wguTs), perm, tiles64,
+                              n_tiles64, L.max_tiles64, counts, offsets, H, 2 * I, k, PF(L.dxs), s,
+                              num_cus);
   } else {
     err = launch_dgrad_large_mx(P8(L.dguq), P8(L.dgus), P8(L.wguT), P8(L.wguTs), perm, tiles, n_tiles,
                                 counts, offsets, H, 2 * I, k, PF(L.dxs), dx, partial, L.max_tiles,

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(1024) void group_experts(
 // being output column cb0 * NW * RPW.
 constexpr int kSXC = 128;                // K chunk of the staged activations
 constexpr int kSXRS = kSXC + 8;          // padded LDS row stride (elements)
-enum { kProjGateUp = 0, kProjDown = 1, kProjDownFused = 2, kProjGateUpSave = 3 };
+enum { kProjGateUp = 0, kProjDown = 1, kProjDownFused = 2, kProjGateUpSave = 3, kProjGatherRows = 4 };
 
 // BM = 128 (experts averaging 48 routed rows or more, where 64-row tiles would
 // stream about half the experts' weights twice): the tile's 128 rows in eight
@@ -474,8 +474,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   __shared__ __align__(16) uint8_t sl[2][kBM * kMSC];
   __shared__ __align__(16) i32x4 wtl[NW][16 * 8];         // per wave: [16 rows][8 chunks]
   __shared__ float s_amax[KIND == kProjGateUp ? NW : 1][kBM];
-  const int K = KIND == kProjGateUp ? H : I;              // reduction length
-  const int N = KIND == kProjGateUp ? I : H;              // outputs
+  // kProjGatherRows (the backward's dh = W_down^T dout): activation rows gathered by
+  // token as gate_up's (K = H), one weight matrix [E][I][H] as down's (outputs I),
+  // FP32 per grouped row as down's slot output (row stride ldy)
+  constexpr bool GATHER = KIND == kProjGateUp || KIND == kProjGatherRows;
+  const int K = GATHER ? H : I;                           // reduction length
+  const int N = GATHER ? I : H;                           // outputs
   const int KB = K / 32;                                  // scale bytes per row
   const int nblk = ncb ? ncb : N / (NW * RPW);
   const int item0 = real_item(blockIdx.x, nblk, *n_tiles);
@@ -490,7 +494,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = (cb0 + nb_i) * NW * RPW + wv * RPW;      // the wave's first output
   const int row0 = nb, row1 = KIND == kProjGateUp ? I + nb : nb + 16;
-  const size_t wrows = KIND == kProjGateUp ? 2 * static_cast<size_t>(I) : H;
+  const size_t wrows = KIND == kProjGateUp ? 2 * static_cast<size_t>(I) : static_cast<size_t>(N);
 
   // whole-line loads: lane = (row lr of an 8-row group, 16-byte chunk lc)
   const int lr = ln >> 3, lc = ln & 7;
@@ -516,13 +520,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   for (int i = 0; i < LPT; ++i) {
     const int c = tid + i * NT, r = c / kMCH, rr = r < mcount ? r : 0;
     lrow[i] = r * kMRS + (c % kMCH) * 16;
-    const int arow = KIND == kProjGateUp ? perm[rbase + rr] / k : rbase + rr;
+    const int arow = GATHER ? perm[rbase + rr] / k : rbase + rr;
     oxl[i] = static_cast<uint32_t>(arow * K + (c % kMCH) * 16);
   }
   const bool sload = tid < kBM;
   const int srow = tid < mcount ? tid : 0;
   const uint32_t osl =
-      sload ? static_cast<uint32_t>((KIND == kProjGateUp ? perm[rbase + srow] / k : rbase + srow) * KB)
+      sload ? static_cast<uint32_t>((GATHER ? perm[rbase + srow] / k : rbase + srow) * KB)
             : 0u;
   i32x4 xr[LPT];
   uint2 sr = make_uint2(0u, 0u);
@@ -873,6 +877,26 @@ hipError_t launch_mx_rows_down(const uint8_t* act, const uint8_t* acts, const ui
   else
     hipLaunchKernelGGL((gemm_mx_s<kProjDown, 8>), grid, block, 0, s, act, acts, wt, wts, perm, tiles,
                        n_tiles, counts, offsets, nullptr, N, K, k, nullptr, nullptr, y, nullptr,
+                       order_key(), 0, N / dims, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_rows_gather(const uint8_t* act, const uint8_t* acts, const uint8_t* wt,
+                                 const uint8_t* wts, const int* perm, const int2* tiles,
+                                 const int* n_tiles, int max_tiles, const int* counts,
+                                 const int* offsets, int K, int N, int k, float* y, hipStream_t s,
+                                 int num_cus) {
+  // act rows gathered by token (perm / k), y [P][N]; the kernel's (H, I) are (K, N)
+  const bool wide = N % 512 == 0 && (N / 512) * max_tiles >= 4 * num_cus;
+  const int dims = wide ? 512 : 256;
+  const dim3 grid(round_up((N / dims) * max_tiles, kXcds)), block(2 * dims);
+  if (wide)
+    hipLaunchKernelGGL((gemm_mx_s<kProjGatherRows, 16>), grid, block, 0, s, act, acts, wt, wts, perm,
+                       tiles, n_tiles, counts, offsets, nullptr, K, N, k, nullptr, nullptr, y, nullptr,
+                       order_key(), 0, N / dims, N);
+  else
+    hipLaunchKernelGGL((gemm_mx_s<kProjGatherRows, 8>), grid, block, 0, s, act, acts, wt, wts, perm,
+                       tiles, n_tiles, counts, offsets, nullptr, K, N, k, nullptr, nullptr, y, nullptr,
                        order_key(), 0, N / dims, N);
   return hipGetLastError();
 }

@@ -227,6 +227,13 @@ hipError_t launch_mx_rows_down(const uint8_t* act, const uint8_t* acts, const ui
                                const int* n_tiles, int max_tiles, const int* counts,
                                const int* offsets, int N, int K, int k, float* y, hipStream_t s,
                                int num_cus);
+// The same with activation rows gathered by token (perm / k): y[row][n] = sum_k
+// act[perm[row] / k][k] wt[e][n][k], act [T][K].
+hipError_t launch_mx_rows_gather(const uint8_t* act, const uint8_t* acts, const uint8_t* wt,
+                                 const uint8_t* wts, const int* perm, const int2* tiles,
+                                 const int* n_tiles, int max_tiles, const int* counts,
+                                 const int* offsets, int K, int N, int k, float* y, hipStream_t s,
+                                 int num_cus);
 hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
                                const uint8_t* wds, const int32_t* idx, const float* w, int T,
                                int H, int I, int E, int k, int dtype, uint16_t* out, void* ws,
