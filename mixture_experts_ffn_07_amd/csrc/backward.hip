@@ -1182,24 +1182,30 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
   hipLaunchKernelGGL(mx_requant_t, dim3(H / 128, 2 * I / 256, E), dim3(256), 0, s, wgu, wgus, 2 * I, H,
                      P8(L.wguT), P8(L.wguTs), counts, order_key());
   prof_end(kBwdRequant, s);
-  // the forward's pre-activations, then dh and its finish
-  prof_begin(kBwdGateUp, s);
-  err = launch_gate_up_raw_large_mx(P8(L.xq), P8(L.xs), wgu, wgus, perm, tiles, n_tiles, counts,
-                                    offsets, H, I, k, PF(L.gu), partial, L.max_tiles, num_cus, s);
-  prof_end(kBwdGateUp, s);
-  if (err != hipSuccess) return err;
-  // Experts averaging fewer than 256 routed pairs: dh and dx on the batched MXFP8 kernel's
-  // 64-row tiles (whole-line weight streams; the 256-row tile spends most of its rows on
-  // padding there), over a second tiling of the same grouping
+  // Experts averaging fewer than 256 routed pairs: the pre-activations, dh and dx on the
+  // batched MXFP8 kernel's 64-row tiles (whole-line weight streams; the 256-row tile spends
+  // most of its rows on padding there), over a second tiling of the same grouping
   const bool rows64 = static_cast<int64_t>(P) < static_cast<int64_t>(kLargeBM) * E;
   int2* tiles64 = reinterpret_cast<int2*>(b + L.tiles64);
   int* n_tiles64 = reinterpret_cast<int*>(b + L.n_tiles64);
-  prof_begin(kBwdDown, s);
   if (rows64) {
     err = launch_group_experts(idx, P, E, 64, counts, offsets, tiles64, n_tiles64, perm, row_of, s);
-    if (err == hipSuccess)
-      err = launch_mx_rows_gather(P8(L.dq), P8(L.ds), P8(L.wdT), P8(L.wdTs), perm, tiles64, n_tiles64,
-                                  L.max_tiles64, counts, offsets, H, I, k, PF(L.dh), s, num_cus);
+    if (err != hipSuccess) return err;
+  }
+  // the forward's pre-activations, then dh and its finish
+  prof_begin(kBwdGateUp, s);
+  if (rows64)
+    err = launch_mx_gate_up_raw_rows(P8(L.xq), P8(L.xs), wgu, wgus, perm, tiles64, n_tiles64,
+                                     L.max_tiles64, counts, offsets, H, I, k, PF(L.gu), s, num_cus);
+  else
+    err = launch_gate_up_raw_large_mx(P8(L.xq), P8(L.xs), wgu, wgus, perm, tiles, n_tiles, counts,
+                                      offsets, H, I, k, PF(L.gu), partial, L.max_tiles, num_cus, s);
+  prof_end(kBwdGateUp, s);
+  if (err != hipSuccess) return err;
+  prof_begin(kBwdDown, s);
+  if (rows64) {
+    err = launch_mx_rows_gather(P8(L.dq), P8(L.ds), P8(L.wdT), P8(L.wdTs), perm, tiles64, n_tiles64,
+                                L.max_tiles64, counts, offsets, H, I, k, PF(L.dh), s, num_cus);
   } else {
     err = launch_dh_large_mx(P8(L.dq), P8(L.ds), P8(L.wdT), P8(L.wdTs), perm, tiles, n_tiles, counts,
                              offsets, H, I, k, PF(L.dh), partial, L.max_tiles, num_cus, s);

@@ -168,7 +168,8 @@ __global__ __launch_bounds__(1024) void group_experts(
 // being output column cb0 * NW * RPW.
 constexpr int kSXC = 128;                // K chunk of the staged activations
 constexpr int kSXRS = kSXC + 8;          // padded LDS row stride (elements)
-enum { kProjGateUp = 0, kProjDown = 1, kProjDownFused = 2, kProjGateUpSave = 3, kProjGatherRows = 4 };
+enum { kProjGateUp = 0, kProjDown = 1, kProjDownFused = 2, kProjGateUpSave = 3, kProjGatherRows = 4,
+       kProjGateUpRaw = 5 };
 
 // BM = 128 (experts averaging 48 routed rows or more, where 64-row tiles would
 // stream about half the experts' weights twice): the tile's 128 rows in eight
@@ -468,7 +469,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
     int H, int I, int k, uint8_t* __restrict__ hout, uint8_t* __restrict__ hsout,
     float* __restrict__ y, uint16_t* __restrict__ out, uint32_t okey, int cb0, int ncb, int ldy) {
   constexpr int NT = NW * 64;
-  constexpr int RPW = KIND == kProjGateUp ? 16 : 32;      // outputs per wave
+  constexpr bool GU = KIND == kProjGateUp || KIND == kProjGateUpRaw;   // gate and up rows
+  constexpr int RPW = GU ? 16 : 32;                       // outputs per wave
   constexpr int LPT = kBM * kMCH / NT;                    // 16-byte code loads per thread
   __shared__ __align__(16) uint8_t xl[2][kBM * kMRS];
   __shared__ __align__(16) uint8_t sl[2][kBM * kMSC];
@@ -477,7 +479,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   // kProjGatherRows (the backward's dh = W_down^T dout): activation rows gathered by
   // token as gate_up's (K = H), one weight matrix [E][I][H] as down's (outputs I),
   // FP32 per grouped row as down's slot output (row stride ldy)
-  constexpr bool GATHER = KIND == kProjGateUp || KIND == kProjGatherRows;
+  // kProjGateUpRaw (the backward's pre-activations): gate_up's product, FP32 g and u of
+  // each grouped row into y [P][2I] instead of h
+  constexpr bool GATHER = GU || KIND == kProjGatherRows;
   const int K = GATHER ? H : I;                           // reduction length
   const int N = GATHER ? I : H;                           // outputs
   const int KB = K / 32;                                  // scale bytes per row
@@ -493,8 +497,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   const int tid = threadIdx.x, ln = tid & 63, col = ln & 15, grp = ln >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = (cb0 + nb_i) * NW * RPW + wv * RPW;      // the wave's first output
-  const int row0 = nb, row1 = KIND == kProjGateUp ? I + nb : nb + 16;
-  const size_t wrows = KIND == kProjGateUp ? 2 * static_cast<size_t>(I) : static_cast<size_t>(N);
+  const int row0 = nb, row1 = GU ? I + nb : nb + 16;
+  const size_t wrows = GU ? 2 * static_cast<size_t>(I) : static_cast<size_t>(N);
 
   // whole-line loads: lane = (row lr of an 8-row group, 16-byte chunk lc)
   const int lr = ln >> 3, lc = ln & 7;
@@ -641,6 +645,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
       *reinterpret_cast<uint32_t*>(hout + static_cast<size_t>(rbase + r) * I + nb + 4 * grp) = wq;
       if (grp == 0 && (wv & 1) == 0)
         hsout[static_cast<size_t>(rbase + r) * (I / 32) + nb / 32] = static_cast<uint8_t>(sexp + 127);
+    }
+  } else if (KIND == kProjGateUpRaw) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r = 16 * g + col;
+      if (r >= mcount) continue;
+      float* gp = y + static_cast<size_t>(rbase + r) * (2 * I) + nb + 4 * grp;
+      *reinterpret_cast<f32x4*>(gp) = acc0[g];
+      *reinterpret_cast<f32x4*>(gp + I) = acc1[g];
     }
   } else {
 #pragma unroll
@@ -898,6 +911,26 @@ hipError_t launch_mx_rows_gather(const uint8_t* act, const uint8_t* acts, const 
     hipLaunchKernelGGL((gemm_mx_s<kProjGatherRows, 8>), grid, block, 0, s, act, acts, wt, wts, perm,
                        tiles, n_tiles, counts, offsets, nullptr, K, N, k, nullptr, nullptr, y, nullptr,
                        order_key(), 0, N / dims, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gate_up_raw_rows(const uint8_t* x, const uint8_t* xs, const uint8_t* wgu,
+                                     const uint8_t* wgus, const int* perm, const int2* tiles,
+                                     const int* n_tiles, int max_tiles, const int* counts,
+                                     const int* offsets, int H, int I, int k, float* gu,
+                                     hipStream_t s, int num_cus) {
+  // as the MXFP8 gate_up of launch_gate_up_batched: 16 or 8 waves of 16 neurons
+  const int n16 = round_up((I / 256) * max_tiles, kXcds);
+  if ((I / 256) * max_tiles >= 4 * num_cus) {
+    hipLaunchKernelGGL((gemm_mx_s<kProjGateUpRaw, 16>), dim3(n16), dim3(1024), 0, s, x, xs, wgu, wgus,
+                       perm, tiles, n_tiles, counts, offsets, nullptr, H, I, k, nullptr, nullptr, gu,
+                       nullptr, order_key(), 0, 0, 0);
+  } else {
+    const int n8 = round_up((I / 128) * max_tiles, kXcds);
+    hipLaunchKernelGGL((gemm_mx_s<kProjGateUpRaw, 8>), dim3(n8), dim3(512), 0, s, x, xs, wgu, wgus,
+                       perm, tiles, n_tiles, counts, offsets, nullptr, H, I, k, nullptr, nullptr, gu,
+                       nullptr, order_key(), 0, 0, 0);
+  }
   return hipGetLastError();
 }
 

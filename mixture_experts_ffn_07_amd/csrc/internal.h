@@ -234,6 +234,13 @@ hipError_t launch_mx_rows_gather(const uint8_t* act, const uint8_t* acts, const 
                                  const int* n_tiles, int max_tiles, const int* counts,
                                  const int* offsets, int K, int N, int k, float* y, hipStream_t s,
                                  int num_cus);
+// MXFP8 gate_up product of grouped rows (x gathered by token), FP32 g and u per grouped
+// row into gu [P][2I] (the backward's pre-activations), on 64-row tiles.
+hipError_t launch_mx_gate_up_raw_rows(const uint8_t* x, const uint8_t* xs, const uint8_t* wgu,
+                                     const uint8_t* wgus, const int* perm, const int2* tiles,
+                                     const int* n_tiles, int max_tiles, const int* counts,
+                                     const int* offsets, int H, int I, int k, float* gu,
+                                     hipStream_t s, int num_cus);
 hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
                                const uint8_t* wds, const int32_t* idx, const float* w, int T,
                                int H, int I, int E, int k, int dtype, uint16_t* out, void* ws,
