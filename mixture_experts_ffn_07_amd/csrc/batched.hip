@@ -346,11 +346,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
       uint2 v;
       v.x = pack_bf16x2(p[0], p[1]);
       v.y = pack_bf16x2(p[2], p[3]);
-      *reinterpret_cast<uint2*>(hr) = v;
+      st8_stream(hr, v);
       if (KIND == kProjGateUpSave) {                      // FP32 g and u of the pair, slot order
         float* gp = gu + static_cast<size_t>(perm[rbase + r]) * (2 * I) + nb + 4 * grp;
-        *reinterpret_cast<f32x4*>(gp) = acc0[g];
-        *reinterpret_cast<f32x4*>(gp + I) = up;
+        st16_stream(gp, acc0[g]);
+        st16_stream(gp + I, up);
       }
     } else if (KIND == kProjDownFused) {
       const int t = perm[rbase + r];                      // k = 1: pair id == token
