@@ -1027,7 +1027,9 @@ __global__ __launch_bounds__(256) void mx_dh_finish(const float* __restrict__ gu
 // w * dout[token] (BF16 dout, FP32 routing weight); 2: grouped FP32 rows
 // (src32, row stride ld).  Workgroup = 128 pairs (four blocks, all of one
 // expert: koff is padded to 128) x 64 rows c, so each row c gets a whole
-// 128-byte line of codes and one 4-byte store of its four scales.
+// 128-byte line of codes and one 4-byte store of its four scales; the scales
+// go out transposed ([KPT/128][rows] dwords: the workgroup's 64 dwords are
+// consecutive).
 template <int SRC>
 __global__ __launch_bounds__(256) void mx_pair_t(const uint16_t* __restrict__ src16,
                                                  const float* __restrict__ src32, int ld,
@@ -1098,7 +1100,9 @@ __global__ __launch_bounds__(256) void mx_pair_t(const uint16_t* __restrict__ sr
     scodes |= mx_quad_encode(v, clo, chi) << (8 * b);
     *reinterpret_cast<uint2*>(dst + orow * KPT + g0 + 32 * b + 8 * q) = make_uint2(clo, chi);
   }
-  if (q == 0) *reinterpret_cast<uint32_t*>(dst_s + orow * (KPT / 32) + g0 / 32) = scodes;
+  // scale dwords transposed, [KPT/128][rows]: a stage's dwords of consecutive rows are
+  // consecutive for the weight-gradient GEMMs' loaders
+  if (q == 0) reinterpret_cast<uint32_t*>(dst_s)[static_cast<size_t>(g0 / 128) * (gridDim.y * 64) + orow] = scodes;
 }
 
 inline size_t a256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
@@ -1147,6 +1151,14 @@ MxBackwardWs mx_backward_ws_layout(int T, int H, int I, int E, int k) {
   L.max_tiles64 = static_cast<int>(E + (P + 63) / 64);
   L.n_tiles64 = o; o += 256;
   L.tiles64 = o;  o = a256(o + sizeof(int) * 2 * L.max_tiles64);
+  // transposed scale dwords for the 256-row large-tile projections (the recompute, dh
+  // and dx when experts average >= 256 routed pairs; dx also at k = 1)
+  L.sct = o;
+  if (P >= static_cast<size_t>(kLargeBM) * E || k == 1) {
+    const size_t gu = static_cast<size_t>(E) * 2 * I * (H / 32) + P * (H / 32);
+    const size_t dx = static_cast<size_t>(E) * H * (2 * I / 32) + P * (2 * I / 32);
+    o = a256(o + (gu > dx ? gu : dx));
+  }
   L.total = o;
   return L;
 }
@@ -1168,6 +1180,7 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
   int* row_of = reinterpret_cast<int*>(b + L.row_of);
   int* koff = reinterpret_cast<int*>(b + L.koff);
   float* partial = PF(L.partial);
+  uint32_t* sct = reinterpret_cast<uint32_t*>(b + L.sct);
   const int P = T * k;
   hipError_t err = launch_group_experts(idx, P, E, kLargeBM, counts, offsets, tiles, n_tiles, perm,
                                         row_of, s);
@@ -1199,7 +1212,8 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
                                      L.max_tiles64, counts, offsets, H, I, k, PF(L.gu), s, num_cus);
   else
     err = launch_gate_up_raw_large_mx(P8(L.xq), P8(L.xs), wgu, wgus, perm, tiles, n_tiles, counts,
-                                      offsets, H, I, k, PF(L.gu), partial, L.max_tiles, num_cus, s);
+                                      offsets, H, I, k, PF(L.gu), partial, L.max_tiles, num_cus, s,
+                                      T, E, sct);
   prof_end(kBwdGateUp, s);
   if (err != hipSuccess) return err;
   prof_begin(kBwdDown, s);
@@ -1208,7 +1222,7 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
                                 L.max_tiles64, counts, offsets, H, I, k, PF(L.dh), s, num_cus);
   } else {
     err = launch_dh_large_mx(P8(L.dq), P8(L.ds), P8(L.wdT), P8(L.wdTs), perm, tiles, n_tiles, counts,
-                             offsets, H, I, k, PF(L.dh), partial, L.max_tiles, num_cus, s);
+                             offsets, H, I, k, PF(L.dh), partial, L.max_tiles, num_cus, s, T, E, sct);
   }
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(mx_dh_finish, dim3((P + 15) / 16, I / kNT), dim3(256), 0, s, PF(L.gu), PF(L.dh),
@@ -1225,7 +1239,7 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
   } else {
     err = launch_dgrad_large_mx(P8(L.dguq), P8(L.dgus), P8(L.wguT), P8(L.wguTs), perm, tiles, n_tiles,
                                 counts, offsets, H, 2 * I, k, PF(L.dxs), dx, partial, L.max_tiles,
-                                num_cus, s);
+                                num_cus, s, T, E, sct);
   }
   if (err != hipSuccess) return err;
   if (k > 1)

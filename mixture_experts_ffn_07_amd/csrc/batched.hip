@@ -60,6 +60,8 @@ BatchedWs batched_ws_layout(int T, int H, int I, int E, int k, int dtype) {
   if (k > 1) o = align256(o + sizeof(float) * P * H);
   L.partial = o;
   if (L.bm == kLargeBM) o = align256(o + sizeof(float) * kLargeMaxSlices * kLargeBM * 256);
+  L.sct = o;                 // MXFP8 large tiles: transposed scale dwords
+  if (L.bm == kLargeBM && dtype == 1) o = align256(o + mx_scales_t_bytes(static_cast<int>(P), H, I, E));
   L.total = o;
   return L;
 }
@@ -508,7 +510,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     ow[i] = static_cast<uint32_t>(((i < 2 ? row0 : row1) + 8 * (i & 1) + lr) * K + lc * 16);
-  // scale bytes: lane (row col, group grp) of each 16-row group
+  // weight scale bytes: lane (row col, group grp) of each 16-row group.  16 waves
+  // (large batches) load them four stages at a time: the lane takes the 8 bytes of
+  // stage 4w + grp of its row, so the four lanes of a row read one 32-byte piece
+  // and a row's line is touched once per four stages, and the stage's bytes reach
+  // the other lanes of the row by lane shuffles (every lane reading the stage's 8
+  // bytes, stage by stage, made the scale lines ~5% of the DeepSeek-shaped
+  // gate_up's time).  8 waves (small batches, where the shuffles' latency showed
+  // and the line traffic did not) keep the stage-by-stage loads.
+  constexpr bool kPieces = NW == 16;
   const uint32_t osw0 = static_cast<uint32_t>((row0 + col) * KB);
   const uint32_t osw1 = static_cast<uint32_t>((row1 + col) * KB);
   i32x4* tw = wtl[wv];
@@ -546,11 +556,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   for (int g = 0; g < 4; ++g) acc0[g] = acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nchunk = K / 128;
   i32x4 wA[4], wB[4];
-  uint2 scA0, scA1;                                       // this stage's scale bytes, groups 0 / 1
+  uint2 scA0, scA1;                                       // scale bytes of groups 0 / 1
 #pragma unroll
   for (int i = 0; i < 4; ++i) wA[i] = ld16_stream(wb + ow[i]);
-  scA0 = *reinterpret_cast<const uint2*>(wsb + osw0);
-  scA1 = *reinterpret_cast<const uint2*>(wsb + osw1);
+  const int nstage = K / kMXC;
+  {
+    const uint32_t s0 = kPieces ? static_cast<uint32_t>(min(grp, nstage - 1) * kMSC) : 0u;
+    scA0 = *reinterpret_cast<const uint2*>(wsb + osw0 + s0);
+    scA1 = *reinterpret_cast<const uint2*>(wsb + osw1 + s0);
+  }
   __syncthreads();
 
   // one 128-position chunk cc (0 or 1) of stage buffer buf: weights W, block scales
@@ -583,7 +597,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
       }
     }
   };
-  const int nstage = K / kMXC;
   for (int st = 0; st < nstage; ++st) {
     const int buf = st & 1;
     const bool more = st + 1 < nstage;
@@ -596,17 +609,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
     // first (clamped to the last chunk / stage, a harmless repeat: fixed load count)
     const uint32_t k1 = static_cast<uint32_t>((2 * st + 1) * 128);
     const uint32_t k2 = static_cast<uint32_t>(min(2 * st + 2, nchunk - 1) * 128);
-    const uint32_t s2 = static_cast<uint32_t>(min(st + 1, nstage - 1) * kMSC);
 #pragma unroll
     for (int i = 0; i < 4; ++i) wB[i] = ld16_stream(wb + ow[i] + k1);
-    const int b1_0 = static_cast<int>((scA0.y >> (8 * grp)) & 0xFFu);   // chunk 1's scale bytes
-    const int b1_1 = static_cast<int>((scA1.y >> (8 * grp)) & 0xFFu);
-    chunk(wA, buf, 0, static_cast<int>((scA0.x >> (8 * grp)) & 0xFFu),
-          static_cast<int>((scA1.x >> (8 * grp)) & 0xFFu));
+    // this stage's 8 scale bytes of the lane's rows (kPieces: from lane (col, st & 3))
+    uint32_t c0x = scA0.x, c0y = scA0.y, c1x = scA1.x, c1y = scA1.y;
+    if (kPieces) {
+      const int src = col + 16 * (st & 3);
+      c0x = static_cast<uint32_t>(__shfl(static_cast<int>(c0x), src, kWave));
+      c0y = static_cast<uint32_t>(__shfl(static_cast<int>(c0y), src, kWave));
+      c1x = static_cast<uint32_t>(__shfl(static_cast<int>(c1x), src, kWave));
+      c1y = static_cast<uint32_t>(__shfl(static_cast<int>(c1y), src, kWave));
+    }
+    const int b1_0 = static_cast<int>((c0y >> (8 * grp)) & 0xFFu);   // chunk 1's scale bytes
+    const int b1_1 = static_cast<int>((c1y >> (8 * grp)) & 0xFFu);
+    chunk(wA, buf, 0, static_cast<int>((c0x >> (8 * grp)) & 0xFFu),
+          static_cast<int>((c1x >> (8 * grp)) & 0xFFu));
 #pragma unroll
     for (int i = 0; i < 4; ++i) wA[i] = ld16_stream(wb + ow[i] + k2);
-    scA0 = *reinterpret_cast<const uint2*>(wsb + osw0 + s2);
-    scA1 = *reinterpret_cast<const uint2*>(wsb + osw1 + s2);
+    if (!kPieces || (st & 3) == 3) {                      // the next stage's bytes / four stages' pieces
+      const uint32_t s2 = static_cast<uint32_t>(min(st + 1 + (kPieces ? grp : 0), nstage - 1) * kMSC);
+      scA0 = *reinterpret_cast<const uint2*>(wsb + osw0 + s2);
+      scA1 = *reinterpret_cast<const uint2*>(wsb + osw1 + s2);
+    }
     chunk(wB, buf, 1, b1_0, b1_1);
     if (more) {
 #pragma unroll
@@ -687,6 +711,7 @@ struct BatchedPtrs {
   int *n_tiles, *counts, *offsets, *perm, *row_of;
   int2* tiles;
   float *y, *partial;
+  uint32_t* sct;
 };
 BatchedPtrs batched_ptrs(void* ws, const BatchedWs& L) {
   char* b = static_cast<char*>(ws);
@@ -699,6 +724,7 @@ BatchedPtrs batched_ptrs(void* ws, const BatchedWs& L) {
   p.row_of = reinterpret_cast<int*>(b + L.row_of);
   p.y = reinterpret_cast<float*>(b + L.y);
   p.partial = reinterpret_cast<float*>(b + L.partial);
+  p.sct = reinterpret_cast<uint32_t*>(b + L.sct);
   return p;
 }
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
@@ -728,7 +754,7 @@ hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* 
                                       static_cast<const uint8_t*>(wgu), wgus, p.perm, p.tiles,
                                       p.n_tiles, p.counts, p.offsets, H, I, k,
                                       static_cast<uint8_t*>(h), hs, p.partial, L.max_tiles,
-                                      num_cus, s);
+                                      num_cus, s, T, E, p.sct);
     prof_end(kGemmGateUp, s);
     return e;
   }
@@ -819,7 +845,7 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
             : launch_down_large_mx(static_cast<const uint8_t*>(h), hs,
                                    static_cast<const uint8_t*>(wd), wds, p.perm, p.tiles,
                                    p.n_tiles, p.counts, p.offsets, w, H, I, k, p.y, out,
-                                   p.partial, L.max_tiles, num_cus, s);
+                                   p.partial, L.max_tiles, num_cus, s, T, E, p.sct);
     if (e == hipSuccess && k > 1) {
       hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out,
                          order_key(), 0, H, H);

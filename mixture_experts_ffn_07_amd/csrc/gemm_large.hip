@@ -604,12 +604,19 @@ __device__ __forceinline__ f32x16 mfma_mx32(i32x8 a, i32x8 b, int sa, int sb, f3
 // KIND kBwdDh:   act = dout codes [T, H] gathered by token; wt = W_down re-quantized
 //                along H and transposed, [E, I, H]; writes FP32 dh [P, I] (grouped rows).
 // KIND kWgradDown / kWgradGateUp: weight gradients over pair-axis operands [rows][KPT]
-//                (codes + scales [rows][KPT/32], expert e's routed pairs in columns
+//                (codes [rows][KPT] + scale dwords [KPT/128][rows], expert e's routed pairs in columns
 //                offsets[e] .. offsets[e+1], zero-padded to multiples of 128; KPT =
 //                offsets[E]): kWgradDown A = a^T (rows i), B = (w dout)^T (rows h),
 //                writes dW_down[e][h][i]; kWgradGateUp A = x^T (rows h), B = [dg; du]^T
 //                (rows c), writes dW_gate_up[e][c][h]; BF16, no K split.
-template <int KIND>
+// TS: the scale dwords (4 bytes per row and 128-wide K stage) transposed, so a
+// stage's 256 dwords of an operand are consecutive (1 KB) instead of one per
+// row, 4 bytes out of each row's scale line (with row-major scales the scale
+// lines took ~10% of the MFMA-bound gate_up's time).  Projections: wt_s
+// [E][K/128][rows of A] and act_s [K/128][ldsc] by grouped row, made by
+// mx_scales_t; weight gradients: both [KPT/128][rows] as the pair-axis encoder
+// writes them (ldsc = rows of B).
+template <int KIND, bool TS = false>
 __global__ __launch_bounds__(256) void gemm_large_mx(
     const uint8_t* __restrict__ act, const uint8_t* __restrict__ act_s,
     const uint8_t* __restrict__ wt, const uint8_t* __restrict__ wt_s,
@@ -617,7 +624,7 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
     const int* __restrict__ counts, const int* __restrict__ offsets, const float* __restrict__ w,
     int H, int I, int k, uint8_t* __restrict__ hq, uint8_t* __restrict__ hs,
     float* __restrict__ y, uint16_t* __restrict__ out, float* __restrict__ partial, int ncu,
-    int E, uint32_t okey) {
+    int E, uint32_t okey, int ldsc) {
   extern __shared__ __align__(16) uint8_t ldm[];   // [stage][A, B][256 x 128] then [stage][A, B][256] dwords
   uint32_t* lsc = reinterpret_cast<uint32_t*>(ldm + 2 * 2 * kMTile);
   constexpr bool kGU = KIND == kGateUp || KIND == kGateUpRaw;   // gate/up rows, gathered x
@@ -683,18 +690,18 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
     abase = wt;
     asb = wt_s;
     ao = static_cast<uint32_t>((nb * 256 + wv * 64 + lrow) * K + lc * 16);
-    so_a = static_cast<uint32_t>((nb * 256 + tid) * KSB);
+    so_a = static_cast<uint32_t>((nb * 256 + tid) * (TS ? 1 : KSB));
   } else if (kGU) {
     abase = wt + static_cast<size_t>(e) * 2 * I * H;
-    asb = wt_s + static_cast<size_t>(e) * 2 * I * KSB;
+    asb = wt_s + static_cast<size_t>(e) * 2 * I * KSB;       // (TS: [nk][2I] dwords of expert e)
     ao = static_cast<uint32_t>(((wv < 2 ? n0 + wv * 64 : I + n0 + (wv - 2) * 64) + lrow) * H + lc * 16);
-    so_a = static_cast<uint32_t>((tid < 128 ? n0 + tid : I + n0 + tid - 128) * KSB);
+    so_a = static_cast<uint32_t>((tid < 128 ? n0 + tid : I + n0 + tid - 128) * (TS ? 1 : KSB));
   } else {
     // down: [E][H][K = I] rows h; kDH: [E][I][K = H] rows i
     abase = wt + static_cast<size_t>(e) * H * I;
     asb = wt_s + static_cast<size_t>(e) * (kDH ? I : H) * KSB;
     ao = static_cast<uint32_t>((nb * 256 + wv * 64 + lrow) * K + lc * 16);
-    so_a = static_cast<uint32_t>((nb * 256 + tid) * KSB);
+    so_a = static_cast<uint32_t>((nb * 256 + tid) * (TS ? 1 : KSB));
   }
   uint32_t bo[8];
 #pragma unroll
@@ -707,8 +714,9 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
   }
   {
     const int rr = tid < mcount ? tid : 0;         // scale loader: thread = tile row
-    so_b = static_cast<uint32_t>((kWG ? bb * 256 + tid : kGather ? perm[rbase + rr] / k : rbase + rr) *
-                                 KSB);
+    so_b = TS ? static_cast<uint32_t>(kWG ? bb * 256 + tid : rbase + rr)   // (TS: row of act_s's columns)
+              : static_cast<uint32_t>((kWG ? bb * 256 + tid : kGather ? perm[rbase + rr] / k : rbase + rr) *
+                                      KSB);
   }
   const int lw = (wv * 64 + lrow) * kMBK + ((lc ^ lrow) * 16);
   int fa[4];
@@ -719,15 +727,24 @@ __global__ __launch_bounds__(256) void gemm_large_mx(
 
   i32x4 stg[16];
   uint32_t sst[2];
+  // (TS) rows of A's transposed scales: W_gate_up 2I, W_down H, W_down^T I; weight
+  // gradients x^T H, (w a)^T I
+  const uint32_t ra_rows = static_cast<uint32_t>(
+      kWG ? (KIND == kWgradGateUp ? H : I) : kGU ? 2 * I : kDH ? I : H);
 #define GLOAD(Q, KT) do {                                                               \
     const uint32_t kk_ = static_cast<uint32_t>(min((KT), ke - 1) * kMBK);               \
     if ((Q) < 8) stg[Q] = ld16(abase + ao + static_cast<uint32_t>((Q) * 8) * K + kk_);  \
     else stg[Q] = ld16(act + bo[(Q) - 8] + kk_);                                        \
   } while (0)
 #define SLOAD(KT) do {                                                                  \
-    const uint32_t ks_ = static_cast<uint32_t>(min((KT), ke - 1) * 4);                 \
-    sst[0] = *reinterpret_cast<const uint32_t*>(asb + so_a + ks_);                      \
-    sst[1] = *reinterpret_cast<const uint32_t*>(act_s + so_b + ks_);                    \
+    const uint32_t ks_ = static_cast<uint32_t>(min((KT), ke - 1));                     \
+    if (TS) {                                                                           \
+      sst[0] = reinterpret_cast<const uint32_t*>(asb)[ks_ * ra_rows + so_a];                \
+      sst[1] = reinterpret_cast<const uint32_t*>(act_s)[ks_ * static_cast<uint32_t>(ldsc) + so_b]; \
+    } else {                                                                            \
+      sst[0] = *reinterpret_cast<const uint32_t*>(asb + so_a + 4 * ks_);                \
+      sst[1] = *reinterpret_cast<const uint32_t*>(act_s + so_b + 4 * ks_);              \
+    }                                                                                   \
   } while (0)
 #define LWRITE(Q, KT) do {                                                              \
     uint8_t* st_ = ldm + ((KT) & 1) * 2 * kMTile;                                       \
@@ -953,8 +970,7 @@ __global__ __launch_bounds__(256) void wgrad_mx_t128(
   static_assert(KIND == kWgradGateUp || KIND == kWgradDown, "weight-gradient kinds");
   extern __shared__ __align__(16) uint8_t ldm[];    // [A, B][128 x 128], [A, B][128] dwords; dW staging
   uint32_t* lsc = reinterpret_cast<uint32_t*>(ldm + 2 * kW1Tile);
-  const int K = offsets[E];                          // row stride of both operands
-  const int KSB = K / 32;
+  const int K = offsets[E];                          // row stride of both operands' codes
   const int nA = KIND == kWgradGateUp ? H / 128 : I / 128;   // a multiple of kW1Run
   const int nB = KIND == kWgradGateUp ? 2 * I / 128 : H / 128;
   const int nG = nA / kW1Run;
@@ -971,8 +987,9 @@ __global__ __launch_bounds__(256) void wgrad_mx_t128(
   const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63, l32 = ln & 31, hi = ln >> 5;
   const int wm = wv & 1, wn = wv >> 1;               // B rows 64 wm .., A rows 64 wn ..
   // loader: chunk u = tid + 256 i of an operand block -> row u >> 3, 16-byte chunk
-  // u & 7, LDS slot (u & 7) ^ (row & 7); scale dwords: thread tid < 128 the A
-  // block's row tid, the others the B block's row tid - 128
+  // u & 7, LDS slot (u & 7) ^ (row & 7); scale dwords ([K/128][rows] per operand,
+  // as the pair-axis encoder writes them): thread tid < 128 the A block's row tid,
+  // the others the B block's row tid - 128
   uint32_t ro[4];
   int lw[4];
 #pragma unroll
@@ -989,13 +1006,13 @@ __global__ __launch_bounds__(256) void wgrad_mx_t128(
     const uint8_t* p = am + static_cast<uint32_t>(nb * 128 * K) + static_cast<uint32_t>(kt * kMBK);
 #pragma unroll
     for (int i = 0; i < 4; ++i) ra[i] = ld16(p + ro[i]);
-    if (sa_lane) rs = *reinterpret_cast<const uint32_t*>(ams + static_cast<uint32_t>((nb * 128 + tid) * KSB + kt * 4));
+    if (sa_lane) rs = reinterpret_cast<const uint32_t*>(ams)[static_cast<uint32_t>(kt * (nA * 128) + nb * 128 + tid)];
   };
   auto load_b = [&](int kt) {                       // B block, stage kt (and, tid >= 128, its scales)
     const uint8_t* p = bm + b_off + static_cast<uint32_t>(kt * kMBK);
 #pragma unroll
     for (int i = 0; i < 4; ++i) rb[i] = ld16(p + ro[i]);
-    if (!sa_lane) rs = *reinterpret_cast<const uint32_t*>(bms + static_cast<uint32_t>((bb * 128 + tid - 128) * KSB + kt * 4));
+    if (!sa_lane) rs = reinterpret_cast<const uint32_t*>(bms)[static_cast<uint32_t>(kt * (nB * 128) + bb * 128 + tid - 128)];
   };
   auto put_a = [&] {
 #pragma unroll
@@ -1110,7 +1127,66 @@ __global__ __launch_bounds__(256) void wgrad_mx_t128(
   }
 }
 
+// Scale dwords (the 4 E8M0 bytes of one 128-wide K stage) transposed for the
+// large-tile MXFP8 GEMM, weights and activations in one launch:
+//   wout[e][kt][r] = win[e][r][kt]                    (r < wrows, E experts)
+//   aout[kt][r]    = ain[perm ? perm[r] / k : r][kt]  (r < P; with perm - the
+//                    activation rows gathered into grouped order - only the
+//                    routed pairs r < offsets[E], the rest left alone)
+// Tiles of 64 rows x 32 stages through LDS, reads and writes along rows of
+// their own layout; the first E * (weight tiles per expert) workgroups take the
+// weights.
+__global__ __launch_bounds__(256) void mx_scales_t(const uint32_t* __restrict__ win, int wrows,
+                                                   int E, const uint32_t* __restrict__ ain, int P,
+                                                   int nk, const int* __restrict__ perm, int k,
+                                                   const int* __restrict__ offsets,
+                                                   uint32_t* __restrict__ wout,
+                                                   uint32_t* __restrict__ aout) {
+  __shared__ uint32_t t[64][33];
+  const int tk = (nk + 31) / 32, twr = (wrows + 63) / 64;
+  const int nwt = E * twr * tk;
+  const bool wpart = static_cast<int>(blockIdx.x) < nwt;
+  const int b = wpart ? blockIdx.x : blockIdx.x - nwt;
+  const int per = wpart ? twr * tk : 0;
+  const int e = wpart ? b / per : 0;
+  const int rem = wpart ? b - e * per : b;
+  const int r0 = (rem / tk) * 64, k0 = (rem % tk) * 32;
+  const int rows = wpart ? wrows : P;
+  const int nrows = wpart || !perm ? rows : min(P, offsets[E]);
+  const uint32_t* __restrict__ ib = wpart ? win + static_cast<size_t>(e) * wrows * nk : ain;
+  uint32_t* __restrict__ ob = wpart ? wout + static_cast<size_t>(e) * nk * wrows : aout;
+  for (int i = threadIdx.x; i < 64 * 32; i += 256) {
+    const int rr = i >> 5, kk = i & 31, r = r0 + rr, kt = k0 + kk;
+    if (r < nrows && kt < nk) {
+      const int src = !wpart && perm ? perm[r] / k : r;
+      t[rr][kk] = ib[static_cast<size_t>(src) * nk + kt];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 32; i += 256) {
+    const int kk = i >> 6, rr = i & 63, r = r0 + rr, kt = k0 + kk;
+    if (r < nrows && kt < nk) ob[static_cast<size_t>(kt) * rows + r] = t[rr][kk];
+  }
+}
+
+size_t mx_scales_t_bytes(int P, int H, int I, int E) {
+  const size_t gu = static_cast<size_t>(E) * 2 * I * (H / 32) + static_cast<size_t>(P) * (H / 32);
+  const size_t dn = static_cast<size_t>(E) * H * (I / 32) + static_cast<size_t>(P) * (I / 32);
+  return gu > dn ? gu : dn;
+}
+
 namespace {
+// transposed weight scales [E][K/128][rows] at sct, activation scales [K/128][P] after them
+void transpose_scales(const uint8_t* ws_, int rows, int K, const uint8_t* as_, int P,
+                      const int* perm, int k, const int* offsets, int E, uint32_t* sct,
+                      hipStream_t s) {
+  const int nk = K / 128, tk = (nk + 31) / 32;
+  const int nblk = E * ((rows + 63) / 64) * tk + ((P + 63) / 64) * tk;
+  hipLaunchKernelGGL(mx_scales_t, dim3(nblk), dim3(256), 0, s, reinterpret_cast<const uint32_t*>(ws_),
+                     rows, E, reinterpret_cast<const uint32_t*>(as_), P, nk, perm, k, offsets, sct,
+                     sct + static_cast<size_t>(E) * nk * rows);
+}
+
 // grid: every item whole, plus room for the tail slices (rem * S - rem < ncu)
 int large_grid(int nblk, int max_tiles, int ncu) {
   return (nblk * max_tiles + ncu + kXcds - 1) / kXcds * kXcds;
@@ -1157,11 +1233,16 @@ hipError_t launch_gate_up_large_mx(const uint8_t* x, const uint8_t* xs, const ui
                                    const uint8_t* wgus, const int* perm, const int2* tiles,
                                    const int* n_tiles, const int* counts, const int* offsets, int H,
                                    int I, int k, uint8_t* hq, uint8_t* hs, float* partial,
-                                   int max_tiles, int ncu, hipStream_t s) {
+                                   int max_tiles, int ncu, hipStream_t s, int T, int E,
+                                   uint32_t* sct) {
   const int grid = large_grid(I / 128, max_tiles, ncu);
-  hipLaunchKernelGGL(gemm_large_mx<kGateUp>, dim3(grid), dim3(256), kMLds, s, x, xs, wgu, wgus,
+  const int P = T * k;
+  transpose_scales(wgus, 2 * I, H, xs, P, perm, k, offsets, E, sct, s);
+  const uint8_t* wst = reinterpret_cast<const uint8_t*>(sct);
+  const uint8_t* xst = reinterpret_cast<const uint8_t*>(sct + static_cast<size_t>(E) * (H / 128) * 2 * I);
+  hipLaunchKernelGGL((gemm_large_mx<kGateUp, true>), dim3(grid), dim3(256), kMLds, s, x, xst, wgu, wst,
                      perm, tiles, n_tiles, counts, offsets, nullptr, H, I, k, hq, hs, nullptr,
-                     nullptr, partial, ncu, 0, order_key());
+                     nullptr, partial, ncu, 0, order_key(), P);
   hipLaunchKernelGGL(gemm_large_mx_fixup_gate_up, dim3(ncu / 2 * 8), dim3(256), 0, s, tiles,
                      n_tiles, counts, offsets, H, I, hq, hs, partial, ncu, H / kMBK, order_key());
   return hipGetLastError();
@@ -1171,12 +1252,18 @@ hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint
                                 const uint8_t* wds, const int* perm, const int2* tiles,
                                 const int* n_tiles, const int* counts, const int* offsets,
                                 const float* w, int H, int I, int k, float* y, uint16_t* out,
-                                float* partial, int max_tiles, int ncu, hipStream_t s) {
+                                float* partial, int max_tiles, int ncu, hipStream_t s, int T,
+                                int E, uint32_t* sct) {
   const int grid = large_grid(H / 256, max_tiles, ncu);
+  const int P = T * k;
+  // h's rows are already grouped: its scales transpose without a gather
+  transpose_scales(wds, H, I, hs, P, nullptr, 1, offsets, E, sct, s);
+  const uint8_t* wst = reinterpret_cast<const uint8_t*>(sct);
+  const uint8_t* hst = reinterpret_cast<const uint8_t*>(sct + static_cast<size_t>(E) * (I / 128) * H);
 #define LARGE_DOWN_MX(KD)                                                                     \
-  hipLaunchKernelGGL(gemm_large_mx<KD>, dim3(grid), dim3(256), kMLds, s, hq, hs, wd, wds,      \
+  hipLaunchKernelGGL((gemm_large_mx<KD, true>), dim3(grid), dim3(256), kMLds, s, hq, hst, wd, wst, \
                      perm, tiles, n_tiles, counts, offsets, w, H, I, k, nullptr, nullptr, y,  \
-                     out, partial, ncu, 0, order_key());                                                   \
+                     out, partial, ncu, 0, order_key(), P);                                   \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
                      n_tiles, counts, offsets, w, H, I, nullptr, y, out, partial, ncu, I / kMBK, \
                      nullptr, order_key())
@@ -1191,11 +1278,16 @@ hipError_t launch_gate_up_raw_large_mx(const uint8_t* xq, const uint8_t* xs, con
                                        const uint8_t* wgus, const int* perm, const int2* tiles,
                                        const int* n_tiles, const int* counts, const int* offsets,
                                        int H, int I, int k, float* gu, float* partial,
-                                       int max_tiles, int ncu, hipStream_t s) {
+                                       int max_tiles, int ncu, hipStream_t s, int T, int E,
+                                       uint32_t* sct) {
   const int grid = large_grid(I / 128, max_tiles, ncu);
-  hipLaunchKernelGGL(gemm_large_mx<kGateUpRaw>, dim3(grid), dim3(256), kMLds, s, xq, xs, wgu, wgus,
+  const int P = T * k;
+  transpose_scales(wgus, 2 * I, H, xs, P, perm, k, offsets, E, sct, s);
+  const uint8_t* wst = reinterpret_cast<const uint8_t*>(sct);
+  const uint8_t* xst = reinterpret_cast<const uint8_t*>(sct + static_cast<size_t>(E) * (H / 128) * 2 * I);
+  hipLaunchKernelGGL((gemm_large_mx<kGateUpRaw, true>), dim3(grid), dim3(256), kMLds, s, xq, xst, wgu, wst,
                      perm, tiles, n_tiles, counts, offsets, nullptr, H, I, k, nullptr, nullptr, gu,
-                     nullptr, partial, ncu, 0, order_key());
+                     nullptr, partial, ncu, 0, order_key(), P);
   hipLaunchKernelGGL(gemm_large_fixup<kGateUpRaw>, dim3(ncu / 2 * 32), dim3(256), 0, s, perm, tiles,
                      n_tiles, counts, offsets, nullptr, H, I, nullptr, nullptr, nullptr, partial,
                      ncu, H / kMBK, gu, order_key());
@@ -1206,11 +1298,15 @@ hipError_t launch_dh_large_mx(const uint8_t* dq, const uint8_t* ds, const uint8_
                               const uint8_t* wdTs, const int* perm, const int2* tiles,
                               const int* n_tiles, const int* counts, const int* offsets, int H,
                               int I, int k, float* dh, float* partial, int max_tiles, int ncu,
-                              hipStream_t s) {
+                              hipStream_t s, int T, int E, uint32_t* sct) {
   const int grid = large_grid(I / 256, max_tiles, ncu);
-  hipLaunchKernelGGL(gemm_large_mx<kBwdDh>, dim3(grid), dim3(256), kMLds, s, dq, ds, wdT, wdTs, perm,
+  const int P = T * k;
+  transpose_scales(wdTs, I, H, ds, P, perm, k, offsets, E, sct, s);
+  const uint8_t* wst = reinterpret_cast<const uint8_t*>(sct);
+  const uint8_t* dst_ = reinterpret_cast<const uint8_t*>(sct + static_cast<size_t>(E) * (H / 128) * I);
+  hipLaunchKernelGGL((gemm_large_mx<kBwdDh, true>), dim3(grid), dim3(256), kMLds, s, dq, dst_, wdT, wst, perm,
                      tiles, n_tiles, counts, offsets, nullptr, H, I, k, nullptr, nullptr, dh,
-                     nullptr, partial, ncu, 0, order_key());
+                     nullptr, partial, ncu, 0, order_key(), P);
   hipLaunchKernelGGL(gemm_large_fixup<kBwdDh>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,
                      n_tiles, counts, offsets, nullptr, H, I, nullptr, dh, nullptr, partial, ncu,
                      H / kMBK, nullptr, order_key());
@@ -1221,12 +1317,17 @@ hipError_t launch_dgrad_large_mx(const uint8_t* aq, const uint8_t* as, const uin
                                  const uint8_t* wTs, const int* perm, const int2* tiles,
                                  const int* n_tiles, const int* counts, const int* offsets, int H,
                                  int K, int k, float* y, uint16_t* out, float* partial,
-                                 int max_tiles, int ncu, hipStream_t s) {
+                                 int max_tiles, int ncu, hipStream_t s, int T, int E,
+                                 uint32_t* sct) {
   const int grid = large_grid(H / 256, max_tiles, ncu);
+  const int P = T * k;
+  transpose_scales(wTs, H, K, as, P, nullptr, 1, offsets, E, sct, s);   // rows grouped already
+  const uint8_t* wst = reinterpret_cast<const uint8_t*>(sct);
+  const uint8_t* ast = reinterpret_cast<const uint8_t*>(sct + static_cast<size_t>(E) * (K / 128) * H);
 #define DGRAD_MX(KD)                                                                          \
-  hipLaunchKernelGGL(gemm_large_mx<KD>, dim3(grid), dim3(256), kMLds, s, aq, as, wT, wTs, perm, \
+  hipLaunchKernelGGL((gemm_large_mx<KD, true>), dim3(grid), dim3(256), kMLds, s, aq, ast, wT, wst, perm, \
                      tiles, n_tiles, counts, offsets, nullptr, H, K, k, nullptr, nullptr, y,  \
-                     out, partial, ncu, 0, order_key());                                     \
+                     out, partial, ncu, 0, order_key(), P);                                     \
   hipLaunchKernelGGL(gemm_large_fixup<KD>, dim3(ncu / 2 * 64), dim3(256), 0, s, perm, tiles,   \
                      n_tiles, counts, offsets, nullptr, H, K, nullptr, y, out, partial, ncu,   \
                      K / kMBK, nullptr, order_key())
@@ -1251,13 +1352,13 @@ hipError_t launch_wgrad_large_mx(const uint8_t* aT, const uint8_t* aTs, const ui
     return hipGetLastError();
   }
   const int nd = (E * (I / 256) * (H / 256) + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(gemm_large_mx<kWgradDown>, dim3(nd), dim3(256), kMLds, s, dyT, dyTs, aT, aTs,
+  hipLaunchKernelGGL((gemm_large_mx<kWgradDown, true>), dim3(nd), dim3(256), kMLds, s, dyT, dyTs, aT, aTs,
                      nullptr, nullptr, nullptr, nullptr, koff, nullptr, H, I, 1, nullptr, nullptr,
-                     nullptr, dwd, nullptr, ncu, E, order_key());
+                     nullptr, dwd, nullptr, ncu, E, order_key(), H);
   const int ng = (E * (H / 256) * (2 * I / 256) + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(gemm_large_mx<kWgradGateUp>, dim3(ng), dim3(256), kMLds, s, dguT, dguTs, xT,
+  hipLaunchKernelGGL((gemm_large_mx<kWgradGateUp, true>), dim3(ng), dim3(256), kMLds, s, dguT, dguTs, xT,
                      xTs, nullptr, nullptr, nullptr, nullptr, koff, nullptr, H, I, 1, nullptr,
-                     nullptr, nullptr, dwgu, nullptr, ncu, E, order_key());
+                     nullptr, nullptr, dwgu, nullptr, ncu, E, order_key(), 2 * I);
   return hipGetLastError();
 }
 
@@ -1434,19 +1535,19 @@ hipError_t large_set_attributes() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   const int mbytes = static_cast<int>(kMLds);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_mx<kGateUp>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_mx<kGateUp, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_mx<kDownFused>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_mx<kDownFused, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_mx<kDownSlots>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_large_mx<kDownSlots, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
-  const void* mx_bwd[] = {reinterpret_cast<const void*>(gemm_large_mx<kGateUpRaw>),
-                          reinterpret_cast<const void*>(gemm_large_mx<kBwdDh>),
-                          reinterpret_cast<const void*>(gemm_large_mx<kDownPlain>),
-                          reinterpret_cast<const void*>(gemm_large_mx<kWgradDown>),
-                          reinterpret_cast<const void*>(gemm_large_mx<kWgradGateUp>)};
+  const void* mx_bwd[] = {reinterpret_cast<const void*>(gemm_large_mx<kGateUpRaw, true>),
+                          reinterpret_cast<const void*>(gemm_large_mx<kBwdDh, true>),
+                          reinterpret_cast<const void*>(gemm_large_mx<kDownPlain, true>),
+                          reinterpret_cast<const void*>(gemm_large_mx<kWgradDown, true>),
+                          reinterpret_cast<const void*>(gemm_large_mx<kWgradGateUp, true>)};
   for (const void* f : mx_bwd)
     if (e == hipSuccess) e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mbytes);
   const void* t128[] = {reinterpret_cast<const void*>(wgrad_mx_t128<kWgradDown>),

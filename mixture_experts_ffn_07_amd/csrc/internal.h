@@ -91,7 +91,7 @@ hipError_t launch_decode(const uint16_t* x, const float* logits, const uint16_t*
 // Byte layout of the batched workspace.  bm = rows per M-tile (64, or
 // kLargeBM when the large-group GEMMs run).
 struct BatchedWs {
-  size_t counts, offsets, perm, row_of, tiles, n_tiles, y, partial, total;
+  size_t counts, offsets, perm, row_of, tiles, n_tiles, y, partial, sct, total;
   int max_tiles, bm;
 };
 BatchedWs batched_ws_layout(int T, int H, int I, int E, int k, int dtype);
@@ -113,16 +113,21 @@ hipError_t launch_down_large_bf16(const uint16_t* h, const uint16_t* wd, const i
                                   const int* offsets, const float* w, int H, int I, int k,
                                   float* y, uint16_t* out, float* partial, int max_tiles, int ncu,
                                   hipStream_t s);
+// The MXFP8 launchers first transpose the weights' and the activations' scale
+// dwords into sct (mx_scales_t_bytes(T*k, H, I, E) bytes of workspace).
+size_t mx_scales_t_bytes(int P, int H, int I, int E);
 hipError_t launch_gate_up_large_mx(const uint8_t* x, const uint8_t* xs, const uint8_t* wgu,
                                    const uint8_t* wgus, const int* perm, const int2* tiles,
                                    const int* n_tiles, const int* counts, const int* offsets, int H,
                                    int I, int k, uint8_t* hq, uint8_t* hs, float* partial,
-                                   int max_tiles, int ncu, hipStream_t s);
+                                   int max_tiles, int ncu, hipStream_t s, int T, int E,
+                                   uint32_t* sct);
 hipError_t launch_down_large_mx(const uint8_t* hq, const uint8_t* hs, const uint8_t* wd,
                                 const uint8_t* wds, const int* perm, const int2* tiles,
                                 const int* n_tiles, const int* counts, const int* offsets,
                                 const float* w, int H, int I, int k, float* y, uint16_t* out,
-                                float* partial, int max_tiles, int ncu, hipStream_t s);
+                                float* partial, int max_tiles, int ncu, hipStream_t s, int T,
+                                int E, uint32_t* sct);
 // Weight gradients of the backward pass for large groups (>= 256 routed rows
 // per expert): koff [E+1] ints, and transposed operands of wgrad_large_cols(P, E)
 // columns each - xT, doutT [H][cols], dguT [2I][cols], waT [I][cols].
@@ -180,7 +185,7 @@ hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* co
 struct MxBackwardWs {
   size_t n_tiles, counts, offsets, tiles, perm, row_of, koff, xq, xs, dq, ds, wdT, wdTs, wguT,
       wguTs, gu, dh, a, dgu, dguq, dgus, dwp, dxs, partial, aT, aTs, dyT, dyTs, xT, xTs, dguT,
-      dguTs, n_tiles64, tiles64, total;
+      dguTs, n_tiles64, tiles64, sct, total;
   size_t kpt_max;
   int max_tiles, max_tiles64;
 };
@@ -195,17 +200,19 @@ hipError_t launch_gate_up_raw_large_mx(const uint8_t* xq, const uint8_t* xs, con
                                        const uint8_t* wgus, const int* perm, const int2* tiles,
                                        const int* n_tiles, const int* counts, const int* offsets,
                                        int H, int I, int k, float* gu, float* partial,
-                                       int max_tiles, int ncu, hipStream_t s);
+                                       int max_tiles, int ncu, hipStream_t s, int T, int E,
+                                       uint32_t* sct);
 hipError_t launch_dh_large_mx(const uint8_t* dq, const uint8_t* ds, const uint8_t* wdT,
                               const uint8_t* wdTs, const int* perm, const int2* tiles,
                               const int* n_tiles, const int* counts, const int* offsets, int H,
                               int I, int k, float* dh, float* partial, int max_tiles, int ncu,
-                              hipStream_t s);
+                              hipStream_t s, int T, int E, uint32_t* sct);
 hipError_t launch_dgrad_large_mx(const uint8_t* aq, const uint8_t* as, const uint8_t* wT,
                                  const uint8_t* wTs, const int* perm, const int2* tiles,
                                  const int* n_tiles, const int* counts, const int* offsets, int H,
                                  int K, int k, float* y, uint16_t* out, float* partial,
-                                 int max_tiles, int ncu, hipStream_t s);
+                                 int max_tiles, int ncu, hipStream_t s, int T, int E,
+                                 uint32_t* sct);
 hipError_t launch_wgrad_large_mx(const uint8_t* aT, const uint8_t* aTs, const uint8_t* dyT,
                                  const uint8_t* dyTs, const uint8_t* xT, const uint8_t* xTs,
                                  const uint8_t* dguT, const uint8_t* dguTs, const int* koff,
