@@ -101,6 +101,9 @@ def _custom(T, H, I, E, k, seed=0):
     (257, 768, 256, 40, 8),     # many small experts, some empty; 8-wave down
     (500, 512, 512, 6, 1),      # k = 1: fused output
     (200, 768, 512, 5, 1),      # k = 1 with the 8-wave down
+    (640, 768, 2048, 64, 8),    # 16-wave gate_up (scale bytes four stages per load) over 3 stages
+    (1100, 512, 512, 4, 1),     # >= 256 pairs per expert: 256-row tiles, transposed scales, K-split tails
+    (600, 256, 512, 2, 2),      # 256-row tiles, k = 2: slot output and combine
 ])
 def test_mx_shapes(M, T, H, I, E, k):
     _check(M, _custom(T, H, I, E, k, seed=T + 1), f"mx shape T={T} H={H} I={I} E={E} k={k}")
