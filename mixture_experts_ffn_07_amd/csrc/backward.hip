@@ -487,8 +487,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int r = 8 * s + (ln >> 3), c = ln & 7;
-        st16(out + static_cast<size_t>(mi * 128 + wm * 64 + 16 * i + r) * N + n0 + wn * 64 + 8 * c,
-             *reinterpret_cast<const i32x4*>(st + r * kWs + 16 * c));
+        st16_stream(out + static_cast<size_t>(mi * 128 + wm * 64 + 16 * i + r) * N + n0 + wn * 64 + 8 * c,
+                    *reinterpret_cast<const i32x4*>(st + r * kWs + 16 * c));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -954,8 +954,8 @@ __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ 
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int row = 32 * wv + 4 * s + (ln >> 4), off = 16 * (ln & 15);
-      st16(dst + (b * C + c0 + row) * static_cast<size_t>(R) + r0 + off,
-           *reinterpret_cast<const i32x4*>(&ot[row * kOt + off]));
+      st16_stream(dst + (b * C + c0 + row) * static_cast<size_t>(R) + r0 + off,
+                  *reinterpret_cast<const i32x4*>(&ot[row * kOt + off]));
     }
   }
   if (tid < 128)

@@ -44,6 +44,12 @@ __device__ __forceinline__ void st8_stream(void* p, uint2 v) {
 __device__ __forceinline__ void st16_stream(void* p, f32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
 }
+// The same for the write-bound kernels' whole-line stores (weight gradients, the
+// MXFP8 weight re-encoding): ~1-2% on those segments, and the caches they would
+// have filled stay with the next kernel's operands.
+__device__ __forceinline__ void st16_stream(void* p, i32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(p));
+}
 
 // FP32 -> BF16, round to nearest, ties to even, on gfx950's conversion
 // instruction (v_cvt_pk_bf16_f32, two values per instruction): pack_bf16x2

@@ -1083,8 +1083,8 @@ __global__ __launch_bounds__(256) void wgrad_mx_t128(
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int r = 8 * s + (ln >> 3), c = ln & 7;
-      st16(dw + static_cast<size_t>(r) * cols + nb * 128 + 64 * wn + 8 * c,
-           *reinterpret_cast<const i32x4*>(st + r * kW1Row + 16 * c));
+      st16_stream(dw + static_cast<size_t>(r) * cols + nb * 128 + 64 * wn + 8 * c,
+                  *reinterpret_cast<const i32x4*>(st + r * kW1Row + 16 * c));
     }
   };
 
