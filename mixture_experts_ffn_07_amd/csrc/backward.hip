@@ -337,11 +337,11 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
         for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
         if (live) {
           uint16_t* dst = a.dgu + grow * (2 * I) + n0 + 8 * sg;
-          st16(dst, i32x4{static_cast<int>(pg[0]), static_cast<int>(pg[1]), static_cast<int>(pg[2]),
-                          static_cast<int>(pg[3])});
-          st16(dst + I, i32x4{static_cast<int>(pu[0]), static_cast<int>(pu[1]),
-                              static_cast<int>(pu[2]), static_cast<int>(pu[3])});
-          st16(a.wa + grow * I + n0 + 8 * sg,
+          st16_stream(dst, i32x4{static_cast<int>(pg[0]), static_cast<int>(pg[1]),
+                                 static_cast<int>(pg[2]), static_cast<int>(pg[3])});
+          st16_stream(dst + I, i32x4{static_cast<int>(pu[0]), static_cast<int>(pu[1]),
+                                     static_cast<int>(pu[2]), static_cast<int>(pu[3])});
+          st16_stream(a.wa + grow * I + n0 + 8 * sg,
                i32x4{static_cast<int>(pa[0]), static_cast<int>(pa[1]), static_cast<int>(pa[2]),
                      static_cast<int>(pa[3])});
           if (sg == 0) a.dwp[grow * (I / kNT) + n0 / kNT] = part;
@@ -350,8 +350,8 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
         if (live) {
           if (k > 1) {
             float* dst = a.dxs + grow * a.ldx + (n0 - cb0 * kNT) + 8 * sg;
-            *reinterpret_cast<f32x4*>(dst) = c0;
-            *reinterpret_cast<f32x4*>(dst + 4) = c1;
+            st16_stream(dst, c0);
+            st16_stream(dst + 4, c1);
           } else {
             const int t = a.perm[grow];               // k = 1: pair id == token
             i32x4 o;

@@ -368,8 +368,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
       }
     } else {
       float* yr = y + static_cast<size_t>(rbase + r) * ldy + (nb - cb0 * NW * RPW) + 4 * grp;
-      *reinterpret_cast<f32x4*>(yr) = acc0[g];
-      if (!ONE) *reinterpret_cast<f32x4*>(yr + 16) = up;
+      st16_stream(yr, acc0[g]);
+      if (!ONE) st16_stream(yr + 16, up);
     }
   }
 }
