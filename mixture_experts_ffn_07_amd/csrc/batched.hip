@@ -676,8 +676,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
       const int r = 16 * g + col;
       if (r >= mcount) continue;
       float* gp = y + static_cast<size_t>(rbase + r) * (2 * I) + nb + 4 * grp;
-      *reinterpret_cast<f32x4*>(gp) = acc0[g];
-      *reinterpret_cast<f32x4*>(gp + I) = acc1[g];
+      st16_stream(gp, acc0[g]);
+      st16_stream(gp + I, acc1[g]);
     }
   } else {
 #pragma unroll
@@ -698,8 +698,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
         }
       } else {
         float* yr = y + static_cast<size_t>(rbase + r) * ldy + (nb - cb0 * NW * RPW) + 4 * grp;
-        *reinterpret_cast<f32x4*>(yr) = acc0[g];
-        *reinterpret_cast<f32x4*>(yr + 16) = acc1[g];
+        st16_stream(yr, acc0[g]);
+        st16_stream(yr + 16, acc1[g]);
       }
     }
   }

@@ -37,8 +37,9 @@ __device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast
 // stream, cost the Kimi-shaped batched gate_up 6% for 0.3% of its bytes (67 MB of
 // h), the streaming form about half of that; the BF16 down projection's FP32 slot
 // slices (read back by the combine right after) 3-7% faster, the backward's dh
-// epilogue and dx slices 2-3% (the MXFP8 gate_up's 4-byte code stores measured
-// 2% slower that way, and keep plain stores).
+// epilogue and dx slices 2-3%, the MXFP8 kernel's FP32 outputs (slot slices,
+// pre-activations, dh) 4-8% (its 4-byte code stores measured 2% slower that way,
+// and keep plain stores).
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void st8_stream(void* p, uint2 v) {
   __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
