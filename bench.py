@@ -64,55 +64,55 @@ CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 # as null until the counters are taken again.
 TRAFFIC = {
     ("gemm_gate_up", "kimi-bf16-T2048"): (
-        23012.7e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "5b45f83804dd96ee",
+        23013.0e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "09fca070836ee3ef",
         "profiles/gemm_gate_up_kimi-bf16-T2048.md"),
     ("gemm_gate_up", "dsv4-mxfp8-T2048"): (
-        18173.7e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "5b45f83804dd96ee",
+        18187.3e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "09fca070836ee3ef",
         "profiles/gemm_gate_up_dsv4-mxfp8-T2048.md"),
     ("gemm_gate_up", "glm-bf16-T2048"): (
-        13238.9e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "5b45f83804dd96ee",
+        13239.1e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "09fca070836ee3ef",
         "profiles/gemm_gate_up_glm-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
-        1996.3e6, ('gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "a06a754983f61921",
+        2055.4e6, ('gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "d632fb8a73731959",
         "profiles/gemm_gate_up_kimi-bf16-ep64share.md"),
     ("gemm_gate_up", "dsv4-mxfp8-ep64share"): (
-        1804.2e6, ('gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "a06a754983f61921",
+        1671.8e6, ('gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "d632fb8a73731959",
         "profiles/gemm_gate_up_dsv4-mxfp8-ep64share.md"),
     ("decode_gate_up", "qwen3-decode-T32"): (
-        700.8e6, ('decode.hip', 'common.h', 'internal.h', 'route.h', 'tiles.h'), "d03c957b01fa5ae2",
+        700.8e6, ('decode.hip', 'common.h', 'internal.h', 'route.h', 'tiles.h'), "fd2144a70db086dc",
         "profiles/decode_gate_up_qwen3-decode-T32.md"),
     ("decode_gate_up", "qwen3-decode-T1"): (
-        50.9e6, ('decode.hip', 'common.h', 'internal.h', 'route.h', 'tiles.h'), "d03c957b01fa5ae2",
+        50.9e6, ('decode.hip', 'common.h', 'internal.h', 'route.h', 'tiles.h'), "fd2144a70db086dc",
         "profiles/decode_gate_up_qwen3-decode-T1.md"),
     ("decode_gate_up", "qwen3-decode-T8"): (
-        317.1e6, ('decode.hip', 'common.h', 'internal.h', 'route.h', 'tiles.h'), "d03c957b01fa5ae2",
+        317.1e6, ('decode.hip', 'common.h', 'internal.h', 'route.h', 'tiles.h'), "fd2144a70db086dc",
         "profiles/decode_gate_up_qwen3-decode-T8.md"),
     ("decode_gate_up", "q35-zipf-T64"): (
-        1114.8e6, ('decode.hip', 'common.h', 'internal.h', 'route.h', 'tiles.h'), "d03c957b01fa5ae2",
+        1114.8e6, ('decode.hip', 'common.h', 'internal.h', 'route.h', 'tiles.h'), "fd2144a70db086dc",
         "profiles/decode_gate_up_q35-zipf-T64.md"),
     ("gemm_gate_up", "qwen3-mxfp8-decode-T32"): (
-        378.8e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "5b45f83804dd96ee",
+        378.8e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "09fca070836ee3ef",
         "profiles/gemm_gate_up_qwen3-mxfp8-decode-T32.md"),
     ("bwd_input", "kimi-bf16-T2048"): (
-        24534.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "420fe50376a45741",
+        24682.7e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
         "profiles/bwd_kimi-bf16-T2048.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
-        23623.7e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "420fe50376a45741",
+        22916.3e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
         "profiles/bwd_kimi-bf16-T2048.md"),
     ("bwd_input", "kimi-bf16-ep64share"): (
-        2189.1e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "420fe50376a45741",
+        2188.5e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
         "profiles/bwd_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-ep64share"): (
-        2558.4e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "420fe50376a45741",
+        2559.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
         "profiles/bwd_kimi-bf16-ep64share.md"),
     ("bwd_requant", "dsv4-mxfp8-T2048"): (
-        58057.0e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "420fe50376a45741",
+        58126.7e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
         "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
     ("bwd_wgate_up", "dsv4-mxfp8-T2048"): (
-        61662.9e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "420fe50376a45741",
+        56074.8e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
         "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
     ("bwd_wgate_up", "dsv4-mxfp8-ep64share"): (
-        4201.1e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "420fe50376a45741",
+        4018.4e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
         "profiles/bwd_mxfp8_dsv4-mxfp8-ep64share.md"),
 }
 
