@@ -295,8 +295,8 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
       if constexpr (KIND == kGU) {
         if (live) {
           float* dst = a.gu + grow * (2 * I) + n0 + 8 * sg;
-          *reinterpret_cast<f32x4*>(dst) = c0;
-          *reinterpret_cast<f32x4*>(dst + 4) = c1;
+          st16_stream(dst, c0);
+          st16_stream(dst + 4, c1);
         }
       } else if constexpr (KIND == kDD) {
         // columns n0 + 8sg .. +7 of the intermediate dimension
