@@ -94,8 +94,9 @@ struct BwdArgs {
   uint16_t* dwgu;           // [E, 2I, H]
   uint16_t* dwd;            // [E, H, I]
   int H, I, E, k;
-  int cb0, ncb, ldx;        // kDG with k > 1: column blocks [cb0, cb0 + ncb) of kNT (ncb 0:
-                            // all), written to dxs with row stride ldx from column cb0 * kNT
+  int cb0, ncb, ldx;        // kDG with k > 1: column blocks [cb0, cb0 + ncb) of the kernel's
+                            // width (ncb 0: all), written to dxs with row stride ldx from
+                            // column cb0 * width
 };
 
 // Element offset of 16-byte chunk c of LDS row r (rows of kKC elements).
@@ -113,12 +114,22 @@ __device__ __forceinline__ void pack_pairs(const i32x4& v0, const i32x4& v1, uin
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
-template <int KIND, int MT>   // kGU, kDD, kDG; MT = routed rows per M-tile (64 or 128)
-__global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
+// LDS of bwd_gemm<KIND, MT, WN> (dynamic): both operands' two K-chunk buffers
+constexpr size_t bwd_lds(int MT, int WN) { return static_cast<size_t>(2 * MT * kKC + 2 * 64 * WN * kKC) * 2; }
+
+// WN: waves along the output columns (64 each): 2 (128 columns, 4 waves) or, for kDG,
+// 4 (256 columns, 8 waves), which reads W_gate_up's rows in 512-byte runs instead of
+// 256-byte ones (its K rows are 2I apart by H elements).
+template <int KIND, int MT, int WN = 2>   // kGU, kDD, kDG; MT = routed rows per M-tile (64 or 128)
+__global__ __launch_bounds__(128 * WN) void bwd_gemm(BwdArgs a, uint32_t okey) {
+  static_assert(WN == 2 || KIND == kDG, "wide tiles: dx only");
+  constexpr int NTH = 128 * WN;                       // threads
+  constexpr int NTC = 64 * WN;                        // output columns per workgroup
+  constexpr int CS32 = NTC + 4;                       // FP32 C-tile row stride (elements)
   constexpr int MI = MT / 32;                         // 16-row A blocks per wave
-  constexpr int AROW_U = MT * 8 / 256;                // "rows" A units per thread
-  constexpr int BROW_U = kNT * 8 / 256;               // "rows" B units per thread (kGU)
-  __shared__ __align__(16) uint16_t lds[2 * MT * kKC + 2 * kNT * kKC];
+  constexpr int AROW_U = MT * 8 / NTH;                // "rows" A units per thread
+  constexpr int BROW_U = NTC * 8 / NTH;               // "rows" B units per thread (kGU)
+  extern __shared__ __align__(16) uint16_t lds[];     // [2][MT x kKC] A, [2][NTC x kKC] B
   uint16_t* const As = lds;
   uint16_t* const Bs = lds + 2 * MT * kKC;
 
@@ -126,15 +137,15 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, I = a.I, k = a.k;
 
-  // ---- work item: (M-tile of MT routed rows, 128 output columns) ----
+  // ---- work item: (M-tile of MT routed rows, NTC output columns) ----
   const int N = KIND == kGU ? 2 * I : (KIND == kDD ? I : H);
   const int cb0 = KIND == kDG ? a.cb0 : 0;
-  const int nblk = KIND == kDG && a.ncb ? a.ncb : N / kNT;
+  const int nblk = KIND == kDG && a.ncb ? a.ncb : N / NTC;
   const int item0 = real_item(blockIdx.x, nblk, *a.n_tiles);
   if (item0 < 0) return;
   const int item = permute_item(item0, nblk * *a.n_tiles, okey);
   const int tile = item / nblk;
-  const int n0 = (cb0 + item - tile * nblk) * kNT;
+  const int n0 = (cb0 + item - tile * nblk) * NTC;
   const int2 te = a.tiles[tile];
   const int e = te.x;
   const int mcount = min(MT, a.counts[e] - te.y);
@@ -148,7 +159,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
   uint32_t aoff[AROW_U];
 #pragma unroll
   for (int i = 0; i < AROW_U; ++i) {
-    const int u = tid + 256 * i, r = u >> 3, c = u & 7;
+    const int u = tid + NTH * i, r = u >> 3, c = u & 7;
     const int rr = r < mcount ? r : 0;
     const uint32_t row = KIND == kDG ? static_cast<uint32_t>(rbase + rr) * (2 * I)
                                      : static_cast<uint32_t>(a.perm[rbase + rr] / k) * H;
@@ -162,7 +173,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
     bbase = a.wgu + static_cast<size_t>(e) * 2 * I * H;
 #pragma unroll
     for (int i = 0; i < BROW_U; ++i) {
-      const int u = tid + 256 * i, r = u >> 3, c = u & 7;
+      const int u = tid + NTH * i, r = u >> 3, c = u & 7;
       boff[i] = static_cast<uint32_t>(n0 + r) * H + 8 * c;
     }
   } else if constexpr (KIND == kDD || KIND == kDG) {
@@ -172,8 +183,8 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
     bbase = KIND == kDD ? a.wd + static_cast<size_t>(e) * H * I
                         : a.wgu + static_cast<size_t>(e) * 2 * I * H;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = tid + 256 * i, q = u & 15, p = u >> 4;
+    for (int i = 0; i < 2; ++i) {                    // NTC/8 column groups x 32 K-row pairs
+      const int u = tid + NTH * i, q = u % (NTC / 8), p = u / (NTC / 8);
       boff[i] = static_cast<uint32_t>(2 * p) * bld + n0 + 8 * q;
     }
   }
@@ -200,16 +211,16 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
 
   auto store_chunk = [&](int buf) {
     uint16_t* ab = As + buf * MT * kKC;
-    uint16_t* bb = Bs + buf * kNT * kKC;
+    uint16_t* bb = Bs + buf * NTC * kKC;
 #pragma unroll
     for (int i = 0; i < AROW_U; ++i) {
-      const int u = tid + 256 * i;
+      const int u = tid + NTH * i;
       *reinterpret_cast<i32x4*>(ab + swz(u >> 3, u & 7)) = ra[i];
     }
     if constexpr (KIND == kGU) {
 #pragma unroll
       for (int i = 0; i < BROW_U; ++i) {
-        const int u = tid + 256 * i;
+        const int u = tid + NTH * i;
         *reinterpret_cast<i32x4*>(bb + swz(u >> 3, u & 7)) = rb[i];
       }
     } else {
@@ -217,7 +228,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
       // column 8q+j becomes LDS row 8q+j
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int u = tid + 256 * i, q = u & 15, p = u >> 4;
+        const int u = tid + NTH * i, q = u % (NTC / 8), p = u / (NTC / 8);
         uint32_t wb_[8];
         pack_pairs(rb[2 * i], rb[2 * i + 1], wb_);
 #pragma unroll
@@ -244,7 +255,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
     const bool more = ch + 1 < nchunks;
     if (more) load_chunk(ch + 1);
     const uint16_t* ab = As + buf * MT * kKC;
-    const uint16_t* bb = Bs + buf * kNT * kKC;
+    const uint16_t* bb = Bs + buf * NTC * kKC;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int c = 4 * s + fg;
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
 
   // ---- C tile through LDS, 64 rows at a time (the operand buffers are free after
   // the last barrier); lane: tile row wm*MT/2 + 16i + fr, columns wn*64 + 16j + 4fg .. +3
-  const int sg = tid & 15;
+  const int sg = tid % (NTC / 8);
 #pragma unroll 1
   for (int half = 0; half < MT / 64; ++half) {
     if (MT == 64 || wm == half) {
@@ -278,18 +289,18 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<f32x4*>(Cs + (rl + 16 * i + fr) * kCS32 + wn * 64 + 16 * j + 4 * fg) =
+          *reinterpret_cast<f32x4*>(Cs + (rl + 16 * i + fr) * CS32 + wn * 64 + 16 * j + 4 * fg) =
               acc[i][j];
     }
     __syncthreads();
   // ---- epilogue: thread = (tile row r, 8 consecutive columns 8*sg) ----
 #pragma unroll 1
-  for (int rc = tid >> 4; rc < 64; rc += 16) {
+  for (int rc = tid / (NTC / 8); rc < 64; rc += NTH / (NTC / 8)) {
     const int r = half * 64 + rc;
     {
       const float* Cs = reinterpret_cast<const float*>(lds);
-      const f32x4 c0 = *reinterpret_cast<const f32x4*>(Cs + rc * kCS32 + 8 * sg);
-      const f32x4 c1 = *reinterpret_cast<const f32x4*>(Cs + rc * kCS32 + 8 * sg + 4);
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(Cs + rc * CS32 + 8 * sg);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(Cs + rc * CS32 + 8 * sg + 4);
       const bool live = r < mcount;
       const size_t grow = static_cast<size_t>(rbase + (live ? r : 0));
       if constexpr (KIND == kGU) {
@@ -349,7 +360,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(BwdArgs a, uint32_t okey) {
       } else {   // kDG
         if (live) {
           if (k > 1) {
-            float* dst = a.dxs + grow * a.ldx + (n0 - cb0 * kNT) + 8 * sg;
+            float* dst = a.dxs + grow * a.ldx + (n0 - cb0 * NTC) + 8 * sg;
             st16_stream(dst, c0);
             st16_stream(dst + 4, c1);
           } else {
@@ -758,8 +769,8 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   };
   if (!gu_saved) {
     prof_begin(kBwdGateUp, s);
-    if (tall) hipLaunchKernelGGL((bwd_gemm<kGU, 128>), grid_tiles(2 * I), dim3(256), 0, s, a, order_key());
-    else hipLaunchKernelGGL((bwd_gemm<kGU, 64>), grid_tiles(2 * I), dim3(256), 0, s, a, order_key());
+    if (tall) hipLaunchKernelGGL((bwd_gemm<kGU, 128>), grid_tiles(2 * I), dim3(256), bwd_lds(128, 2), s, a, order_key());
+    else hipLaunchKernelGGL((bwd_gemm<kGU, 64>), grid_tiles(2 * I), dim3(256), bwd_lds(64, 2), s, a, order_key());
     prof_end(kBwdGateUp, s);
   }
   // large groups: 256-row M-tiles over the same (deterministic) grouping for the
@@ -783,9 +794,9 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(bwd_dh_finish, dim3((P + 15) / 16, I / kNT), dim3(256), 0, s, a, dh, P, order_key());
   } else if (tall) {
-    hipLaunchKernelGGL((bwd_gemm<kDD, 128>), grid_tiles(I), dim3(256), 0, s, a, order_key());
+    hipLaunchKernelGGL((bwd_gemm<kDD, 128>), grid_tiles(I), dim3(256), bwd_lds(128, 2), s, a, order_key());
   } else {
-    hipLaunchKernelGGL((bwd_gemm<kDD, 64>), grid_tiles(I), dim3(256), 0, s, a, order_key());
+    hipLaunchKernelGGL((bwd_gemm<kDD, 64>), grid_tiles(I), dim3(256), bwd_lds(64, 2), s, a, order_key());
   }
   prof_end(kBwdDown, s);
   prof_begin(kBwdInput, s);
@@ -797,19 +808,23 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   } else {
     // column parts (column_parts): each part's FP32 per-pair slice is summed right
     // after its launch, while it is still in the last-level cache (T 2048, k 8,
-    // H 7168: 7 parts; 64-row tiles run three workgroups per CU, 128-row tiles two)
-    const int parts = k > 1 ? column_parts(static_cast<size_t>(P), H, kNT, L.max_tiles,
-                                           (tall ? 8 : 12) * num_cus)
+    // H 7168: 7 parts).  64-row tiles: workgroups of 8 waves x 256 columns, two per
+    // CU (W_gate_up's rows read in 512-byte runs: Kimi shape 4.05 -> 3.73 ms); 128-row
+    // tiles keep 4 waves x 128 columns, two per CU (the wide form fits one per CU
+    // there and ran 11% slower on the GLM shape).
+    const int dw = tall ? kNT : 256;
+    const int parts = k > 1 ? column_parts(static_cast<size_t>(P), H, dw, L.max_tiles,
+                                           8 * num_cus)
                             : 1;
     const int hq = H / parts;
     for (int q = 0; q < parts; ++q) {
       BwdArgs ap = a;
-      ap.cb0 = q * (hq / kNT);
-      ap.ncb = hq / kNT;
+      ap.cb0 = q * (hq / dw);
+      ap.ncb = hq / dw;
       ap.ldx = hq;
-      const dim3 g(static_cast<unsigned>((hq / kNT * L.max_tiles + kXcds - 1) / kXcds * kXcds));
-      if (tall) hipLaunchKernelGGL((bwd_gemm<kDG, 128>), g, dim3(256), 0, s, ap, order_key());
-      else hipLaunchKernelGGL((bwd_gemm<kDG, 64>), g, dim3(256), 0, s, ap, order_key());
+      const dim3 g(static_cast<unsigned>((hq / dw * L.max_tiles + kXcds - 1) / kXcds * kXcds));
+      if (tall) hipLaunchKernelGGL((bwd_gemm<kDG, 128>), g, dim3(256), bwd_lds(128, 2), s, ap, order_key());
+      else hipLaunchKernelGGL((bwd_gemm<kDG, 64, 4>), g, dim3(512), bwd_lds(64, 4), s, ap, order_key());
       if (k > 1)
         hipLaunchKernelGGL(sum_pairs, dim3(T), dim3(256), 0, s, a.dxs, row_of, T, H, k, dx,
                            order_key(), q * hq, hq, hq);
@@ -1270,6 +1285,14 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
   hipLaunchKernelGGL(route_bwd, dim3(T), dim3(64), 0, s, PF(L.dwp), row_of, idx, w, T, E, k, I / kNT,
                      dtw, dlogits, order_key());
   return hipGetLastError();
+}
+
+
+hipError_t backward_set_attributes() {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_gemm<kDG, 64, 4>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(bwd_lds(64, 4)));
+  return e;
 }
 
 }  // namespace moe
