@@ -122,7 +122,7 @@ constexpr size_t bwd_lds(int MT, int WN) { return static_cast<size_t>(2 * MT * k
 // 256-byte ones (its K rows are 2I apart by H elements).
 template <int KIND, int MT, int WN = 2>   // kGU, kDD, kDG; MT = routed rows per M-tile (64 or 128)
 __global__ __launch_bounds__(128 * WN) void bwd_gemm(BwdArgs a, uint32_t okey) {
-  static_assert(WN == 2 || KIND == kDG, "wide tiles: dx only");
+  static_assert(WN == 2 || KIND == kDG || KIND == kDD, "wide tiles: dh and dx only");
   constexpr int NTH = 128 * WN;                       // threads
   constexpr int NTC = 64 * WN;                        // output columns per workgroup
   constexpr int CS32 = NTC + 4;                       // FP32 C-tile row stride (elements)
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(128 * WN) void bwd_gemm(BwdArgs a, uint32_t okey) {
             pa[q >> 1] = ba;
           }
         }
-        // partial dot over the 128 columns: the 16 lanes of this row, fixed butterfly
+        // partial dot over each 128 columns: their 16 lanes of this row, fixed butterfly
 #pragma unroll
         for (int m = 8; m >= 1; m >>= 1) part += __shfl_xor(part, m, kWave);
         if (live) {
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(128 * WN) void bwd_gemm(BwdArgs a, uint32_t okey) {
           st16_stream(a.wa + grow * I + n0 + 8 * sg,
                i32x4{static_cast<int>(pa[0]), static_cast<int>(pa[1]), static_cast<int>(pa[2]),
                      static_cast<int>(pa[3])});
-          if (sg == 0) a.dwp[grow * (I / kNT) + n0 / kNT] = part;
+          if ((sg & 15) == 0) a.dwp[grow * (I / kNT) + (n0 + 8 * sg) / kNT] = part;
         }
       } else {   // kDG
         if (live) {
@@ -796,7 +796,9 @@ hipError_t launch_backward(const uint16_t* x, const uint16_t* wgu, const uint16_
   } else if (tall) {
     hipLaunchKernelGGL((bwd_gemm<kDD, 128>), grid_tiles(I), dim3(256), bwd_lds(128, 2), s, a, order_key());
   } else {
-    hipLaunchKernelGGL((bwd_gemm<kDD, 64>), grid_tiles(I), dim3(256), bwd_lds(64, 2), s, a, order_key());
+    // 8 waves x 256 columns: W_down's rows read in 512-byte runs
+    const dim3 g(static_cast<unsigned>((I / 256 * L.max_tiles + kXcds - 1) / kXcds * kXcds));
+    hipLaunchKernelGGL((bwd_gemm<kDD, 64, 4>), g, dim3(512), bwd_lds(64, 4), s, a, order_key());
   }
   prof_end(kBwdDown, s);
   prof_begin(kBwdInput, s);
@@ -1292,6 +1294,10 @@ hipError_t backward_set_attributes() {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_gemm<kDG, 64, 4>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(bwd_lds(64, 4)));
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_gemm<kDD, 64, 4>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(bwd_lds(64, 4)));
   return e;
 }
 
