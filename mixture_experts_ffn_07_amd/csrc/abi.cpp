@@ -14,6 +14,7 @@
 namespace moe {
 hipError_t decode_set_attributes();
 hipError_t batched_set_attributes();
+hipError_t backward_set_attributes();
 
 ProfileHook& profile_hook() {
   thread_local ProfileHook hook;
@@ -78,6 +79,7 @@ int device_info(int* num_cus, void** scratch = nullptr) {
                   prop.gcnArchName);
     e = moe::decode_set_attributes();
     if (e == hipSuccess) e = moe::batched_set_attributes();
+    if (e == hipSuccess) e = moe::backward_set_attributes();
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
     // the device address of this device's scratch array (the device is current)
     e = moe::static_scratch(dev, &d.scratch);

@@ -981,9 +981,6 @@ hipError_t launch_quant_mx(const uint16_t* src, int64_t rows, int K, uint8_t* co
   return hipGetLastError();
 }
 
-hipError_t batched_set_attributes() {
-  hipError_t e = large_set_attributes();
-  return e == hipSuccess ? backward_set_attributes() : e;
-}
+hipError_t batched_set_attributes() { return large_set_attributes(); }
 
 }  // namespace moe

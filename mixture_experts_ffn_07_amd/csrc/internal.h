@@ -190,8 +190,6 @@ struct MxBackwardWs {
   int max_tiles, max_tiles64;
 };
 MxBackwardWs mx_backward_ws_layout(int T, int H, int I, int E, int k);
-// Raises the dynamic LDS limit of the backward kernels that use more than 64 KB.
-hipError_t backward_set_attributes();
 hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8_t* wgus,
                               const uint8_t* wd, const uint8_t* wds, const int32_t* idx,
                               const float* w, const uint16_t* dout, int T, int H, int I, int E,
