@@ -94,25 +94,25 @@ TRAFFIC = {
         378.8e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "09fca070836ee3ef",
         "profiles/gemm_gate_up_qwen3-mxfp8-decode-T32.md"),
     ("bwd_input", "kimi-bf16-T2048"): (
-        24682.7e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
+        24767.8e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
         "profiles/bwd_kimi-bf16-T2048.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
-        22916.3e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
+        22912.9e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
         "profiles/bwd_kimi-bf16-T2048.md"),
     ("bwd_input", "kimi-bf16-ep64share"): (
-        2188.5e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
+        2189.1e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
         "profiles/bwd_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-ep64share"): (
-        2559.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
+        2559.0e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
         "profiles/bwd_kimi-bf16-ep64share.md"),
     ("bwd_requant", "dsv4-mxfp8-T2048"): (
-        58126.7e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
+        58137.9e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
         "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
     ("bwd_wgate_up", "dsv4-mxfp8-T2048"): (
-        56074.8e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
+        56073.9e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
         "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
     ("bwd_wgate_up", "dsv4-mxfp8-ep64share"): (
-        4018.4e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7bd59578f34b9740",
+        4018.3e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
         "profiles/bwd_mxfp8_dsv4-mxfp8-ep64share.md"),
 }
 
