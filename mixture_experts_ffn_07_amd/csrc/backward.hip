@@ -900,12 +900,12 @@ __device__ __forceinline__ uint32_t mx_quad_encode(const float (&v)[8], uint32_t
 // LDS and leave as whole 128-byte lines (eight lanes per line), and each output
 // row's 8 scale bytes in one 8-byte store.  With counts, matrices b with
 // counts[b] == 0 are skipped (their copy is left as is).
+template <int U>                                    // 64-row tiles per workgroup
 __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ src,
                                                     const uint8_t* __restrict__ src_s, int R, int C,
                                                     uint8_t* __restrict__ dst,
                                                     uint8_t* __restrict__ dst_s,
                                                     const int* __restrict__ counts, uint32_t okey) {
-  constexpr int U = 4;                              // 64-row tiles per workgroup
   constexpr int kOt = 64 * U + 16;                  // bytes per staged output row (+16: banks)
   __shared__ float tl[128][64 + 1];                 // [c][r]
   __shared__ __align__(16) uint8_t ot[128 * kOt];   // [c][256 codes]
@@ -964,20 +964,22 @@ __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ 
     ssc[c][2 * u + hb] = static_cast<uint8_t>(sx + 127);
   }
   __syncthreads();
-  // 128 rows x 256 bytes: lane ln of wave wv stores bytes [16 (ln & 15), +16) of row
-  // 32 wv + 4 s + (ln >> 4), so each store instruction writes four rows' whole lines
+  // 128 rows x 64U bytes: lane ln of wave wv stores bytes [16 (ln % 4U), +16) of row
+  // 32 wv + (16 / U) s + ln / 4U, so each store instruction writes whole row lines
   {
     const int wv = tid >> 6, ln = tid & 63;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int row = 32 * wv + 4 * s + (ln >> 4), off = 16 * (ln & 15);
+    for (int s = 0; s < 2 * U; ++s) {
+      const int row = 32 * wv + (16 / U) * s + ln / (4 * U), off = 16 * (ln % (4 * U));
       st16_stream(dst + (b * C + c0 + row) * static_cast<size_t>(R) + r0 + off,
                   *reinterpret_cast<const i32x4*>(&ot[row * kOt + off]));
     }
   }
-  if (tid < 128)
-    *reinterpret_cast<uint2*>(dst_s + (b * C + c0 + tid) * (R / 32) + r0 / 32) =
-        *reinterpret_cast<const uint2*>(&ssc[tid][0]);
+  if (tid < 128) {
+    uint8_t* sp = dst_s + (b * C + c0 + tid) * (R / 32) + r0 / 32;
+    if constexpr (U == 4) *reinterpret_cast<uint2*>(sp) = *reinterpret_cast<const uint2*>(&ssc[tid][0]);
+    else *reinterpret_cast<uint32_t*>(sp) = *reinterpret_cast<const uint32_t*>(&ssc[tid][0]);
+  }
 }
 
 // The MXFP8 backward's dh finish, per grouped row r (thread = 8 columns, 16
@@ -1180,6 +1182,9 @@ MxBackwardWs mx_backward_ws_layout(int T, int H, int I, int E, int k) {
   return L;
 }
 
+// 64-row tiles per re-encoding workgroup (2: 52 KB of LDS, three workgroups per CU)
+constexpr int kRqU = 2;
+
 hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8_t* wgus,
                               const uint8_t* wd, const uint8_t* wds, const int32_t* idx,
                               const float* w, const uint16_t* dout, int T, int H, int I, int E,
@@ -1207,9 +1212,9 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
   err = launch_quant_mx(x, T, H, P8(L.xq), P8(L.xs), s);
   if (err == hipSuccess) err = launch_quant_mx(dout, T, H, P8(L.dq), P8(L.ds), s);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(mx_requant_t, dim3(I / 128, H / 256, E), dim3(256), 0, s, wd, wds, H, I, P8(L.wdT),
+  hipLaunchKernelGGL(mx_requant_t<kRqU>, dim3(I / 128, H / (64 * kRqU), E), dim3(256), 0, s, wd, wds, H, I, P8(L.wdT),
                      P8(L.wdTs), counts, order_key());
-  hipLaunchKernelGGL(mx_requant_t, dim3(H / 128, 2 * I / 256, E), dim3(256), 0, s, wgu, wgus, 2 * I, H,
+  hipLaunchKernelGGL(mx_requant_t<kRqU>, dim3(H / 128, 2 * I / (64 * kRqU), E), dim3(256), 0, s, wgu, wgus, 2 * I, H,
                      P8(L.wguT), P8(L.wguTs), counts, order_key());
   prof_end(kBwdRequant, s);
   // Experts averaging fewer than 256 routed pairs: the pre-activations, dh and dx on the
