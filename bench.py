@@ -94,25 +94,25 @@ TRAFFIC = {
         378.8e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "09fca070836ee3ef",
         "profiles/gemm_gate_up_qwen3-mxfp8-decode-T32.md"),
     ("bwd_input", "kimi-bf16-T2048"): (
-        24767.8e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
+        24767.9e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
         "profiles/bwd_kimi-bf16-T2048.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
-        22912.9e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
+        22915.7e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
         "profiles/bwd_kimi-bf16-T2048.md"),
     ("bwd_input", "kimi-bf16-ep64share"): (
-        2189.1e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
+        2189.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
         "profiles/bwd_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-ep64share"): (
-        2559.0e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
+        2560.4e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
         "profiles/bwd_kimi-bf16-ep64share.md"),
     ("bwd_requant", "dsv4-mxfp8-T2048"): (
-        58137.9e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
+        58054.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
         "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
     ("bwd_wgate_up", "dsv4-mxfp8-T2048"): (
-        56073.9e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
+        56073.1e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
         "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
     ("bwd_wgate_up", "dsv4-mxfp8-ep64share"): (
-        4018.3e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "7ad7821f1ad77b47",
+        4018.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
         "profiles/bwd_mxfp8_dsv4-mxfp8-ep64share.md"),
 }
 
