@@ -375,9 +375,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BM == 1
 }
 
 // combine: out[t] = sum_j w[t,j] * y[row_of[t*k+j]] in slot order (FP32 FMA
-// chain starting from 0), rounded once to BF16.  One workgroup per token; a
-// launch covers the output columns [col0, col0 + cols), y holding them with row
-// stride ldy from its column 0.
+// chain starting from 0), rounded once to BF16.  Workgroup (x, y): token x,
+// column chunk y of gridDim.y (small batches split the columns so that the
+// launch still spreads over the CUs); a launch covers the output columns [col0,
+// col0 + cols), y holding them with row stride ldy from its column 0.
 __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y,
                                                      const int* __restrict__ row_of,
                                                      const float* __restrict__ w, int T, int H,
@@ -386,7 +387,8 @@ __global__ __launch_bounds__(256) void combine_slots(const float* __restrict__ y
   const int t = permute_item(blockIdx.x, gridDim.x, okey);
   const int P = T * k;
   out += col0;
-  for (int c = threadIdx.x; c < cols / 4; c += blockDim.x) {
+  const int c4 = cols / 4, c_lo = blockIdx.y * c4 / gridDim.y, c_hi = (blockIdx.y + 1) * c4 / gridDim.y;
+  for (int c = c_lo + threadIdx.x; c < c_hi; c += blockDim.x) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int row = row_of[t * k + j];
@@ -728,6 +730,14 @@ BatchedPtrs batched_ptrs(void* ws, const BatchedWs& L) {
   return p;
 }
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
+// combine_slots grid: one workgroup per token and, for batches of fewer tokens than
+// two per CU, column chunks of at least 256 columns (T 32, H 2048: 8 chunks, 9.9 ->
+// ~4 us on the decode-sized MXFP8 shape)
+dim3 combine_grid(int T, int cols, int num_cus) {
+  int ch = T > 0 ? (2 * num_cus + T - 1) / T : 1;
+  ch = ch < 1 ? 1 : ch > cols / 256 ? cols / 256 : ch;
+  return dim3(static_cast<unsigned>(T), static_cast<unsigned>(ch < 1 ? 1 : ch));
+}
 }  // namespace
 
 hipError_t launch_gate_up_batched(const void* x, const uint8_t* xs, const void* wgu,
@@ -847,8 +857,8 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
                                    p.n_tiles, p.counts, p.offsets, w, H, I, k, p.y, out,
                                    p.partial, L.max_tiles, num_cus, s, T, E, p.sct);
     if (e == hipSuccess && k > 1) {
-      hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out,
-                         order_key(), 0, H, H);
+      hipLaunchKernelGGL(combine_slots, combine_grid(T, H, num_cus), dim3(256), 0, s, p.y, p.row_of, w, T,
+                         H, k, out, order_key(), 0, H, H);
       e = hipGetLastError();
     }
     prof_end(kGemmDown, s);
@@ -893,8 +903,8 @@ hipError_t launch_down_batched(const void* h, const uint8_t* hs, const void* wd,
 #undef DOWN_ARGS_B
 #undef DOWN_ARGS_M
     if (k > 1)
-      hipLaunchKernelGGL(combine_slots, dim3(T), dim3(256), 0, s, p.y, p.row_of, w, T, H, k, out,
-                         order_key(), q * hq, hq, hq);
+      hipLaunchKernelGGL(combine_slots, combine_grid(T, hq, num_cus), dim3(256), 0, s, p.y, p.row_of, w,
+                         T, H, k, out, order_key(), q * hq, hq, hq);
   }
   prof_end(kGemmDown, s);
   return hipGetLastError();
