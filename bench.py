@@ -64,13 +64,13 @@ CSRC = os.path.join(ROOT, "mixture_experts_ffn_07_amd", "csrc")
 # as null until the counters are taken again.
 TRAFFIC = {
     ("gemm_gate_up", "kimi-bf16-T2048"): (
-        23013.0e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "09fca070836ee3ef",
+        23012.2e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "12e9ae18e929026f",
         "profiles/gemm_gate_up_kimi-bf16-T2048.md"),
     ("gemm_gate_up", "dsv4-mxfp8-T2048"): (
-        18187.3e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "09fca070836ee3ef",
+        18188.0e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "12e9ae18e929026f",
         "profiles/gemm_gate_up_dsv4-mxfp8-T2048.md"),
     ("gemm_gate_up", "glm-bf16-T2048"): (
-        13239.1e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "09fca070836ee3ef",
+        13239.0e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "12e9ae18e929026f",
         "profiles/gemm_gate_up_glm-bf16-T2048.md"),
     ("gemm_gate_up", "kimi-bf16-ep64share"): (
         2055.4e6, ('gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "d632fb8a73731959",
@@ -91,28 +91,28 @@ TRAFFIC = {
         1114.8e6, ('decode.hip', 'common.h', 'internal.h', 'route.h', 'tiles.h'), "fd2144a70db086dc",
         "profiles/decode_gate_up_q35-zipf-T64.md"),
     ("gemm_gate_up", "qwen3-mxfp8-decode-T32"): (
-        378.8e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "09fca070836ee3ef",
+        378.8e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "12e9ae18e929026f",
         "profiles/gemm_gate_up_qwen3-mxfp8-decode-T32.md"),
     ("bwd_input", "kimi-bf16-T2048"): (
-        24767.9e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
+        24767.9e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fa2e1ef566b4d938",
         "profiles/bwd_kimi-bf16-T2048.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
-        22915.7e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
+        22915.7e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fa2e1ef566b4d938",
         "profiles/bwd_kimi-bf16-T2048.md"),
     ("bwd_input", "kimi-bf16-ep64share"): (
-        2189.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
+        2189.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fa2e1ef566b4d938",
         "profiles/bwd_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-ep64share"): (
-        2560.4e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
+        2560.4e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fa2e1ef566b4d938",
         "profiles/bwd_kimi-bf16-ep64share.md"),
     ("bwd_requant", "dsv4-mxfp8-T2048"): (
-        58054.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
+        58054.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fa2e1ef566b4d938",
         "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
     ("bwd_wgate_up", "dsv4-mxfp8-T2048"): (
-        56073.1e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
+        56073.1e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fa2e1ef566b4d938",
         "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
     ("bwd_wgate_up", "dsv4-mxfp8-ep64share"): (
-        4018.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "29eacbf3020e4eb0",
+        4018.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fa2e1ef566b4d938",
         "profiles/bwd_mxfp8_dsv4-mxfp8-ep64share.md"),
 }
 
