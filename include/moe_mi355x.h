@@ -177,7 +177,9 @@ int moe_quantize_mxfp8(const uint16_t* src, int64_t rows, int K,
  *   workspace  >= moe_workspace_bytes(T, H, I, E, k, dtype) bytes; this call
  *              writes the expert grouping into it, and moe_down_3d_batched
  *              must be given the same workspace and topk_idx, later on the
- *              same stream
+ *              same stream (MXFP8 with >= 256 routed pairs per expert on
+ *              average: both calls also keep transposed copies of the weights'
+ *              and the activations' scale bytes there)
  * Limits: T >= 1, H and I multiples of 256, 1 <= k <= min(E, 32), E <= 1024;
  * T*H, T*k*H, T*k*I and 2*I*H each below 2^31 (the kernels' 32-bit element
  * offsets).  MOE_ERR_SHAPE otherwise.
@@ -306,7 +308,9 @@ size_t moe_backward_workspace_bytes(int T, int H, int I, int E, int k);
  *              grouping, x and dout encoded along H, both weights re-encoded
  *              along their output axis (transposed copies, ~1.03 x the weight
  *              bytes), FP32 pre-activations, dh, a and [dg; du] per routed pair,
- *              the pair-axis operands and a 64 MiB K-split buffer
+ *              the pair-axis operands, a 64 MiB K-split buffer and (>= 256
+ *              routed pairs per expert on average, or k = 1) transposed copies
+ *              of the projections' scale bytes
  * Limits: as for moe_backward_batched, and max(H, 2I) * (T*k + 128*E) < 2^31.
  */
 int moe_backward_batched_mxfp8(const uint16_t* x, const uint8_t* w_gate_up,
