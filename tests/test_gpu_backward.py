@@ -96,6 +96,7 @@ def _custom(T, H, I, E, k, seed=0):
     (257, 768, 256, 40, 8),     # many small experts, some empty
     (200, 512, 256, 5, 1),      # k = 1: dx written directly, no logit gradient
     (64, 256, 256, 16, 16),     # k = E
+    (150, 1280, 768, 8, 2),     # 64-row tiles: dh over 3 and dx over 5 blocks of 256 columns
 ])
 def test_backward_shapes(M, T, H, I, E, k):
     _check(M, _custom(T, H, I, E, k, seed=T + E), f"bwd T={T} k={k}")

@@ -58,6 +58,7 @@ def _custom(T, H, I, E, k, seed=0, x_std=1.0):
     (500, 512, 256, 6, 1),      # k = 1, 128-row tiles: down writes the output directly
     (200, 768, 512, 5, 1),      # k = 1 with the 8-wave down
     (64, 256, 256, 16, 16),     # k = E
+    (200, 1280, 256, 8, 2),     # combine split into 3 uneven column chunks (T < 2 per CU)
 ])
 def test_batched_shapes(M, T, H, I, E, k):
     _check(M, _custom(T, H, I, E, k, seed=T + E), f"shape T={T} H={H} I={I} E={E} k={k}")
