@@ -893,14 +893,15 @@ __device__ __forceinline__ uint32_t mx_quad_encode(const float (&v)[8], uint32_t
 
 // dst[b] = the MX encoding along R of src[b]^T: src codes [B][R][C] with scales
 // [B][R][C/32] (blocks along C) are decoded exactly and re-encoded as dst codes
-// [B][C][R] with scales [B][C][R/32] (blocks along R).  A workgroup takes 128
-// columns x 256 rows (C a multiple of 128, R of 256) as four 64-row tiles
-// through LDS: every load covers whole 128-byte lines of source rows (the four
-// tiles' loads in flight together); the codes of the 128 output rows collect in
-// LDS and leave as whole 128-byte lines (eight lanes per line), and each output
-// row's 8 scale bytes in one 8-byte store.  With counts, matrices b with
-// counts[b] == 0 are skipped (their copy is left as is).
-template <int U>                                    // 64-row tiles per workgroup
+// [B][C][R] with scales [B][C][R/32] (blocks along R).  A workgroup takes 64U
+// rows (R a multiple of 64U) and J consecutive blocks of 128 columns (C a multiple
+// of 128J), one block at a time as U 64-row tiles through LDS, with the next
+// block's loads in flight while the current one is converted and stored: every
+// load covers whole 128-byte lines of source rows; the codes of the 128 output
+// rows collect in LDS and leave as whole row lines, and each output row's 2U scale
+// bytes in one store.  With counts, matrices b with counts[b] == 0 are skipped
+// (their copy is left as is).
+template <int U, int J>                             // 64-row tiles, 128-column blocks per workgroup
 __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ src,
                                                     const uint8_t* __restrict__ src_s, int R, int C,
                                                     uint8_t* __restrict__ dst,
@@ -908,77 +909,95 @@ __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ 
                                                     const int* __restrict__ counts, uint32_t okey) {
   constexpr int kOt = 64 * U + 16;                  // bytes per staged output row (+16: banks)
   __shared__ float tl[128][64 + 1];                 // [c][r]
-  __shared__ __align__(16) uint8_t ot[128 * kOt];   // [c][256 codes]
+  __shared__ __align__(16) uint8_t ot[128 * kOt];   // [c][64U codes]
   __shared__ __align__(8) uint8_t ssc[128][2 * U];  // [c][block of 32 rows]
-  const int c0 = permute_item(blockIdx.x, gridDim.x, okey) * 128, r0 = blockIdx.y * 64 * U;
+  const int cb = permute_item(blockIdx.x, gridDim.x, okey) * J, r0 = blockIdx.y * 64 * U;
   const size_t b = blockIdx.z;
   if (counts && counts[b] == 0) return;             // no pair reads this expert's copy
   const int tid = threadIdx.x;
   const int q = tid & 7, rl = tid >> 3;             // load: rows rl and rl + 32 of a tile, 16 codes at 16q
-  i32x4 v[U][2];
-  int sc[U][2];
+  i32x4 v[U][2], vn[U][2];
+  int sc[U][2], sn[U][2];
+  auto load = [&](int c0, i32x4 (&V)[U][2], int (&S)[U][2]) {
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const size_t row = b * R + r0 + 64 * u + 32 * h + rl;
-      v[u][h] = ld16(src + row * C + c0 + 16 * q);
-      sc[u][h] = src_s[row * (C / 32) + (c0 + 16 * q) / 32];
-    }
-  const int c = tid >> 1, hb = tid & 1;             // encode: out row c, block hb of the tile's 64 rows
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (u) __syncthreads();                         // the previous tile is read out
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // decode: the hardware E4M3 pair conversion (exact), times 2^(scale - 127)
-      const float scl = ldexpf(1.0f, sc[u][h] - 127);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(v[u][h][d], false);   // bytes 0, 1
-        const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8(v[u][h][d], true);    // bytes 2, 3
-        tl[16 * q + 4 * d][32 * h + rl] = f0.x * scl;
-        tl[16 * q + 4 * d + 1][32 * h + rl] = f0.y * scl;
-        tl[16 * q + 4 * d + 2][32 * h + rl] = f1.x * scl;
-        tl[16 * q + 4 * d + 3][32 * h + rl] = f1.y * scl;
+      for (int h = 0; h < 2; ++h) {
+        const size_t row = b * R + r0 + 64 * u + 32 * h + rl;
+        V[u][h] = ld16(src + row * C + c0 + 16 * q);
+        S[u][h] = src_s[row * (C / 32) + (c0 + 16 * q) / 32];
       }
+  };
+  load(cb * 128, v, sc);
+  const int c = tid >> 1, hb = tid & 1;             // encode: out row c, block hb of the tile's 64 rows
+#pragma unroll 1
+  for (int jj = 0; jj < J; ++jj) {
+    const int c0 = (cb + jj) * 128;
+    if (jj + 1 < J) load(c0 + 128, vn, sn);         // the next block's codes in flight
+    if (jj) __syncthreads();                        // the previous block's rows are stored
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u) __syncthreads();                       // the previous tile is read out
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // decode: the hardware E4M3 pair conversion (exact), times 2^(scale - 127)
+        const float scl = ldexpf(1.0f, sc[u][h] - 127);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(v[u][h][d], false);   // bytes 0, 1
+          const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8(v[u][h][d], true);    // bytes 2, 3
+          tl[16 * q + 4 * d][32 * h + rl] = f0.x * scl;
+          tl[16 * q + 4 * d + 1][32 * h + rl] = f0.y * scl;
+          tl[16 * q + 4 * d + 2][32 * h + rl] = f1.x * scl;
+          tl[16 * q + 4 * d + 3][32 * h + rl] = f1.y * scl;
+        }
+      }
+      __syncthreads();
+      float val[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) val[i] = tl[c][32 * hb + i];
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(val[i]));
+      const int sx = mx_scale_exp(amax);
+      const float inv = exp2_neg(sx);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float* w = val + 16 * g;
+        *reinterpret_cast<i32x4*>(&ot[c * kOt + 64 * u + 32 * hb + 16 * g]) =
+             i32x4{static_cast<int>(f32x4_to_e4m3x4(w[0] * inv, w[1] * inv, w[2] * inv, w[3] * inv)),
+                   static_cast<int>(f32x4_to_e4m3x4(w[4] * inv, w[5] * inv, w[6] * inv, w[7] * inv)),
+                   static_cast<int>(f32x4_to_e4m3x4(w[8] * inv, w[9] * inv, w[10] * inv, w[11] * inv)),
+                   static_cast<int>(f32x4_to_e4m3x4(w[12] * inv, w[13] * inv, w[14] * inv, w[15] * inv))};
+      }
+      ssc[c][2 * u + hb] = static_cast<uint8_t>(sx + 127);
     }
     __syncthreads();
-    float val[32];
+    // 128 rows x 64U bytes: lane ln of wave wv stores bytes [16 (ln % 4U), +16) of row
+    // 32 wv + (16 / U) s + ln / 4U, so each store instruction writes whole row lines
+    {
+      const int wv = tid >> 6, ln = tid & 63;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) val[i] = tl[c][32 * hb + i];
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(val[i]));
-    const int sx = mx_scale_exp(amax);
-    const float inv = exp2_neg(sx);
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const float* w = val + 16 * g;
-      *reinterpret_cast<i32x4*>(&ot[c * kOt + 64 * u + 32 * hb + 16 * g]) =
-           i32x4{static_cast<int>(f32x4_to_e4m3x4(w[0] * inv, w[1] * inv, w[2] * inv, w[3] * inv)),
-                 static_cast<int>(f32x4_to_e4m3x4(w[4] * inv, w[5] * inv, w[6] * inv, w[7] * inv)),
-                 static_cast<int>(f32x4_to_e4m3x4(w[8] * inv, w[9] * inv, w[10] * inv, w[11] * inv)),
-                 static_cast<int>(f32x4_to_e4m3x4(w[12] * inv, w[13] * inv, w[14] * inv, w[15] * inv))};
+      for (int s = 0; s < 2 * U; ++s) {
+        const int row = 32 * wv + (16 / U) * s + ln / (4 * U), off = 16 * (ln % (4 * U));
+        st16_stream(dst + (b * C + c0 + row) * static_cast<size_t>(R) + r0 + off,
+                    *reinterpret_cast<const i32x4*>(&ot[row * kOt + off]));
+      }
     }
-    ssc[c][2 * u + hb] = static_cast<uint8_t>(sx + 127);
-  }
-  __syncthreads();
-  // 128 rows x 64U bytes: lane ln of wave wv stores bytes [16 (ln % 4U), +16) of row
-  // 32 wv + (16 / U) s + ln / 4U, so each store instruction writes whole row lines
-  {
-    const int wv = tid >> 6, ln = tid & 63;
-#pragma unroll
-    for (int s = 0; s < 2 * U; ++s) {
-      const int row = 32 * wv + (16 / U) * s + ln / (4 * U), off = 16 * (ln % (4 * U));
-      st16_stream(dst + (b * C + c0 + row) * static_cast<size_t>(R) + r0 + off,
-                  *reinterpret_cast<const i32x4*>(&ot[row * kOt + off]));
+    if (tid < 128) {
+      uint8_t* sp = dst_s + (b * C + c0 + tid) * (R / 32) + r0 / 32;
+      if constexpr (U == 4) *reinterpret_cast<uint2*>(sp) = *reinterpret_cast<const uint2*>(&ssc[tid][0]);
+      else *reinterpret_cast<uint32_t*>(sp) = *reinterpret_cast<const uint32_t*>(&ssc[tid][0]);
     }
-  }
-  if (tid < 128) {
-    uint8_t* sp = dst_s + (b * C + c0 + tid) * (R / 32) + r0 / 32;
-    if constexpr (U == 4) *reinterpret_cast<uint2*>(sp) = *reinterpret_cast<const uint2*>(&ssc[tid][0]);
-    else *reinterpret_cast<uint32_t*>(sp) = *reinterpret_cast<const uint32_t*>(&ssc[tid][0]);
+    if (jj + 1 < J) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          v[u][h] = vn[u][h];
+          sc[u][h] = sn[u][h];
+        }
+    }
   }
 }
 
@@ -1183,7 +1202,10 @@ MxBackwardWs mx_backward_ws_layout(int T, int H, int I, int E, int k) {
 }
 
 // 64-row tiles per re-encoding workgroup (2: 52 KB of LDS, three workgroups per CU)
+// and its 128-column blocks (the next one's loads in flight meanwhile; I and H are
+// multiples of 256, so 2 divides both block counts)
 constexpr int kRqU = 2;
+constexpr int kRqJ = 2;
 
 hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8_t* wgus,
                               const uint8_t* wd, const uint8_t* wds, const int32_t* idx,
@@ -1212,9 +1234,9 @@ hipError_t launch_backward_mx(const uint16_t* x, const uint8_t* wgu, const uint8
   err = launch_quant_mx(x, T, H, P8(L.xq), P8(L.xs), s);
   if (err == hipSuccess) err = launch_quant_mx(dout, T, H, P8(L.dq), P8(L.ds), s);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(mx_requant_t<kRqU>, dim3(I / 128, H / (64 * kRqU), E), dim3(256), 0, s, wd, wds, H, I, P8(L.wdT),
+  hipLaunchKernelGGL((mx_requant_t<kRqU, kRqJ>), dim3(I / (128 * kRqJ), H / (64 * kRqU), E), dim3(256), 0, s, wd, wds, H, I, P8(L.wdT),
                      P8(L.wdTs), counts, order_key());
-  hipLaunchKernelGGL(mx_requant_t<kRqU>, dim3(H / 128, 2 * I / (64 * kRqU), E), dim3(256), 0, s, wgu, wgus, 2 * I, H,
+  hipLaunchKernelGGL((mx_requant_t<kRqU, kRqJ>), dim3(H / (128 * kRqJ), 2 * I / (64 * kRqU), E), dim3(256), 0, s, wgu, wgus, 2 * I, H,
                      P8(L.wguT), P8(L.wguTs), counts, order_key());
   prof_end(kBwdRequant, s);
   // Experts averaging fewer than 256 routed pairs: the pre-activations, dh and dx on the
