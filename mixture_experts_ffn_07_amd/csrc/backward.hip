@@ -907,6 +907,8 @@ __global__ __launch_bounds__(256) void mx_requant_t(const uint8_t* __restrict__ 
                                                     uint8_t* __restrict__ dst,
                                                     uint8_t* __restrict__ dst_s,
                                                     const int* __restrict__ counts, uint32_t okey) {
+  // the scale store below writes a row's 2U scale bytes as one 4- or 8-byte word
+  static_assert(U == 2 || U == 4, "64U-row workgroups with U = 2 or 4");
   constexpr int kOt = 64 * U + 16;                  // bytes per staged output row (+16: banks)
   __shared__ float tl[128][64 + 1];                 // [c][r]
   __shared__ __align__(16) uint8_t ot[128 * kOt];   // [c][64U codes]
