@@ -94,25 +94,25 @@ TRAFFIC = {
         378.8e6, ('batched.hip', 'common.h', 'tiles.h', 'internal.h'), "12e9ae18e929026f",
         "profiles/gemm_gate_up_qwen3-mxfp8-decode-T32.md"),
     ("bwd_input", "kimi-bf16-T2048"): (
-        24771.1e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fef0030a943fd8db",
+        24773.4e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "2bf00baff9e035ff",
         "profiles/bwd_kimi-bf16-T2048.md"),
     ("bwd_wgate_up", "kimi-bf16-T2048"): (
-        22908.3e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fef0030a943fd8db",
+        22916.5e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "2bf00baff9e035ff",
         "profiles/bwd_kimi-bf16-T2048.md"),
     ("bwd_input", "kimi-bf16-ep64share"): (
-        2188.6e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fef0030a943fd8db",
+        2189.0e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "2bf00baff9e035ff",
         "profiles/bwd_kimi-bf16-ep64share.md"),
     ("bwd_wgate_up", "kimi-bf16-ep64share"): (
-        2560.3e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fef0030a943fd8db",
+        2558.1e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "2bf00baff9e035ff",
         "profiles/bwd_kimi-bf16-ep64share.md"),
     ("bwd_requant", "dsv4-mxfp8-T2048"): (
-        59008.8e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fef0030a943fd8db",
+        59007.7e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "2bf00baff9e035ff",
         "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
     ("bwd_wgate_up", "dsv4-mxfp8-T2048"): (
-        56073.2e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fef0030a943fd8db",
+        56072.7e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "2bf00baff9e035ff",
         "profiles/bwd_mxfp8_dsv4-mxfp8-T2048.md"),
     ("bwd_wgate_up", "dsv4-mxfp8-ep64share"): (
-        4018.3e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "fef0030a943fd8db",
+        4018.3e6, ('backward.hip', 'batched.hip', 'gemm_large.hip', 'common.h', 'tiles.h', 'internal.h'), "2bf00baff9e035ff",
         "profiles/bwd_mxfp8_dsv4-mxfp8-ep64share.md"),
 }
 

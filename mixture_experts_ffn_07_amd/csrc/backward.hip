@@ -64,7 +64,7 @@ constexpr int kBB = 64;          // routed rows per M-tile (128 when experts ave
 constexpr int kKC = 64;          // K chunk (elements)
 constexpr int kNT = 128;         // output columns per workgroup
 constexpr int kCS32 = kNT + 4;   // FP32 C-tile row stride (elements)
-constexpr int kMB = 8;           // 128-row output blocks per weight-gradient workgroup
+constexpr int kMB = 16;          // 128-row output blocks per weight-gradient workgroup
 // Weight gradients on the large-group GEMM from this many routed rows per expert
 // on average: below it an expert's reduction is one or two 64-row stages and the
 // per-block fixed costs dominate (measured at 64 rows: 5.9 -> 10.2 ms for the two
